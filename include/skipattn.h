@@ -1,0 +1,154 @@
+/*
+ * skipattn.h - C ABI of libskipattn: exact tiled softmax attention with the
+ * Skip-Softmax tile-skip rule, for long-context prefill and split-K decode,
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed
+ * ----------------
+ * Blockwise ("Flash") attention: scores, softmax and the value product are
+ * formed one key block at a time and the N x N score matrix is never stored
+ * (TurboAttention talk page, "Technical Deep Dive").
+ *
+ * Skip-Softmax (TensorRT-LLM Skip Softmax summary page, "Key Points" and
+ * "Detailed Analysis"): key blocks are visited in ascending order, and a
+ * block is skipped when its local maximum score lies below the running
+ * maximum minus a user threshold tau. Readings fixed by this library:
+ *   - scores are s = q.k / sqrt(d); tau is in the same (natural-logit) units;
+ *   - the decision tile is 64 query rows x 64 keys; the running maximum is
+ *     per query row, over the tiles kept so far; the tile is skipped iff
+ *     EVERY valid row r has t_r < m_r - tau (strict), t_r = the row's
+ *     maximum score inside the tile;
+ *   - a skipped tile contributes nothing to the output, to the normaliser or
+ *     to the running maximum; its scores are still formed for the test;
+ *   - the first visited tile (running max -inf) is never skipped;
+ *   - tau = +INFINITY gives dense exact attention; tau must be >= 0.
+ * Query head h reads key/value head h / (Hq / Hkv) (grouped-query attention).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers to dense row-major arrays.
+ *   q, k, v are bfloat16 (passed as void*); o and lse are float32.
+ * - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
+ *   null stream) and returns; results are valid once the stream has
+ *   synchronised. The library never allocates, frees or synchronises.
+ *   The caller owns every buffer, including the decode workspace.
+ * - Arguments are validated on the host before anything is launched: a
+ *   nonzero return leaves every output untouched.
+ * - Calls on different streams may overlap; calls that share output or
+ *   workspace buffers must be ordered by the caller.
+ * - Empty work (B == 0, or N / L == 0) is valid and launches nothing.
+ *
+ * Return codes
+ *   SKIPATTN_OK           0
+ *   SKIPATTN_EINVAL       1  NULL q/k/v/o/lse pointer; negative size;
+ *                            Hq or Hkv < 1 or Hq % Hkv != 0; causal not 0/1;
+ *                            tau NaN or < 0; a pointer not 16-byte aligned;
+ *                            an element count beyond 2^40
+ *   SKIPATTN_EUNSUPPORTED 2  d not in {64, 128}; decode with Hq/Hkv > 16
+ *   SKIPATTN_EWORKSPACE   3  decode workspace NULL or smaller than
+ *                            attn_decode_workspace_bytes()
+ *   SKIPATTN_EHIP         4  a kernel launch failed (hipGetLastError)
+ * attn_last_error() returns a description of the last nonzero return on
+ * the calling thread.
+ */
+#ifndef SKIPATTN_H
+#define SKIPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SKIPATTN_OK 0
+#define SKIPATTN_EINVAL 1
+#define SKIPATTN_EUNSUPPORTED 2
+#define SKIPATTN_EWORKSPACE 3
+#define SKIPATTN_EHIP 4
+
+/* Tile edge of the skip decision (queries and keys), and the decode split. */
+#define SKIPATTN_TILE 64
+#define SKIPATTN_SPLIT 4096
+
+/* Mask byte values. */
+#define SKIPATTN_KEPT 0
+#define SKIPATTN_SKIPPED 1
+#define SKIPATTN_NOT_VISITED 2
+
+/*
+ * attn_prefill - causal or full self-attention over N tokens.
+ *
+ *   q    bf16 [B, Hq,  N, d]
+ *   k    bf16 [B, Hkv, N, d]
+ *   v    bf16 [B, Hkv, N, d]
+ *   o    fp32 [B, Hq,  N, d]  out: softmax over the kept keys, times V
+ *   lse  fp32 [B, Hq,  N]     out: natural-log sum of e^s over kept keys
+ *   causal     1: query i attends keys j <= i; tiles wholly above the
+ *              diagonal are not visited. 0: every key.
+ *   tau        skip threshold in logit units, >= 0; +INFINITY = dense.
+ *   skip_mask  NULL, or uint8 [B, Hq, ceil(N/64), ceil(N/64)], written for
+ *              every (query tile, key tile): SKIPATTN_KEPT, SKIPATTN_SKIPPED,
+ *              or SKIPATTN_NOT_VISITED (causal tiles above the diagonal).
+ * N need not be a multiple of 64: missing keys of the last tile are masked
+ * and missing rows of the last query tile take no part in the vote.
+ */
+int attn_prefill(const void* q, const void* k, const void* v, float* o,
+                 float* lse, int B, int Hq, int Hkv, int N, int d, int causal,
+                 float tau, uint8_t* skip_mask, void* stream);
+
+/*
+ * attn_decode_workspace_bytes - bytes of device scratch attn_decode needs:
+ * B * Hq * ceil(L / 4096) * (d + 1) * 4 (per-split partial outputs and
+ * log-sum-exps). Returns 0 for invalid or empty sizes.
+ */
+size_t attn_decode_workspace_bytes(int B, int Hq, int L, int d);
+
+/*
+ * attn_decode - one query token per sequence against a contiguous KV cache,
+ * split-K over fixed 4096-key splits.
+ *
+ *   q    bf16 [B, Hq, d]
+ *   k    bf16 [B, Hkv, L, d]
+ *   v    bf16 [B, Hkv, L, d]
+ *   o    fp32 [B, Hq, d]   out
+ *   lse  fp32 [B, Hq]      out, natural log
+ *   tau        as for attn_prefill. The decision tile is one query x 64 keys,
+ *              per query head. Each split [4096 s, 4096 (s+1)) runs the rule
+ *              over its own tiles with its own running maximum, starting at
+ *              -inf, so the first tile of every split is kept.
+ *   skip_mask  NULL, or uint8 [B, Hq, ceil(L/64)]: SKIPATTN_KEPT or
+ *              SKIPATTN_SKIPPED per (head, key tile).
+ *   workspace  device scratch of at least attn_decode_workspace_bytes();
+ *              its contents on entry do not matter.
+ * The query attends all L cached keys (no mask). The per-split partial
+ * results are merged by log-sum-exp in a second kernel on the same stream.
+ */
+int attn_decode(const void* q, const void* k, const void* v, float* o,
+                float* lse, int B, int Hq, int Hkv, int L, int d, float tau,
+                uint8_t* skip_mask, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/*
+ * attn_prefill_check / attn_decode_check - the host-side argument
+ * validation of the two entry points on its own: the same return code the
+ * entry point would give before launching, with no HIP call at all.
+ */
+int attn_prefill_check(const void* q, const void* k, const void* v,
+                       const float* o, const float* lse, int B, int Hq,
+                       int Hkv, int N, int d, int causal, float tau,
+                       const uint8_t* skip_mask);
+int attn_decode_check(const void* q, const void* k, const void* v,
+                      const float* o, const float* lse, int B, int Hq,
+                      int Hkv, int L, int d, float tau,
+                      const uint8_t* skip_mask, const void* workspace,
+                      size_t workspace_bytes);
+
+/* Text for the last nonzero return on this thread ("" if none). */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKIPATTN_H */

@@ -1,0 +1,12 @@
+"""libskipattn: exact tiled softmax attention with the Skip-Softmax rule on
+MI355X (gfx950). The computation lives in the HIP library built from csrc/;
+this package is its thin Python binding."""
+from ._lib import (OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, TILE, SPLIT,
+                   KEPT, SKIPPED, NOT_VISITED, EXPORTS, LIB_PATH, SkipAttnError,
+                   load, attn_prefill, attn_decode, attn_decode_workspace_bytes,
+                   attn_last_error, prefill, decode)
+
+__all__ = ["OK", "EINVAL", "EUNSUPPORTED", "EWORKSPACE", "EHIP", "TILE", "SPLIT",
+           "KEPT", "SKIPPED", "NOT_VISITED", "EXPORTS", "LIB_PATH", "SkipAttnError",
+           "load", "attn_prefill", "attn_decode", "attn_decode_workspace_bytes",
+           "attn_last_error", "prefill", "decode"]

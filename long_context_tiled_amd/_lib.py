@@ -1,0 +1,178 @@
+"""ctypes binding of libskipattn (include/skipattn.h).
+
+Argument marshalling only: torch tensors are checked for dtype, device,
+contiguity and shape, turned into device pointers, and passed with torch's
+current HIP stream. Every step of the computation runs in the library's HIP
+kernels; there is no fallback path. Loading fails loudly if the library has
+not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libskipattn.so")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
+TILE = 64
+SPLIT = 4096
+KEPT, SKIPPED, NOT_VISITED = 0, 1, 2
+
+EXPORTS = ("attn_prefill", "attn_decode", "attn_decode_workspace_bytes",
+           "attn_prefill_check", "attn_decode_check", "attn_last_error")
+
+_lib = None
+
+
+class SkipAttnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libskipattn error {code}: {msg}")
+        self.code = code
+
+
+def load() -> ctypes.CDLL:
+    """Load libskipattn.so (built in-tree); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} not found: build it with `python -m long_context_tiled_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, f32p, u8p = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+    i, f, sz = ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.attn_prefill.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, i, f, u8p, vp]
+    lib.attn_prefill.restype = i
+    lib.attn_prefill_check.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, i, f, u8p]
+    lib.attn_prefill_check.restype = i
+    lib.attn_decode.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, f, u8p, vp, sz, vp]
+    lib.attn_decode.restype = i
+    lib.attn_decode_check.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, f, u8p, vp, sz]
+    lib.attn_decode_check.restype = i
+    lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i]
+    lib.attn_decode_workspace_bytes.restype = sz
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def attn_last_error() -> str:
+    return load().attn_last_error().decode()
+
+
+def _raise(rc: int):
+    if rc != OK:
+        raise SkipAttnError(rc, attn_last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(t, name, dtype, shape):
+    import torch
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def attn_prefill(q, k, v, o, lse, causal: bool, tau: float, skip_mask=None,
+                 stream=None) -> None:
+    """Enqueue prefill attention: q [B,Hq,N,d], k/v [B,Hkv,N,d] bf16;
+    writes o [B,Hq,N,d] fp32, lse [B,Hq,N] fp32 and, if given, skip_mask
+    [B,Hq,ceil(N/64),ceil(N/64)] uint8."""
+    import torch
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    _check(q, "q", torch.bfloat16, (B, Hq, N, d))
+    _check(k, "k", torch.bfloat16, (B, Hkv, N, d))
+    _check(v, "v", torch.bfloat16, (B, Hkv, N, d))
+    _check(o, "o", torch.float32, (B, Hq, N, d))
+    _check(lse, "lse", torch.float32, (B, Hq, N))
+    if skip_mask is not None:
+        nt = (N + TILE - 1) // TILE
+        _check(skip_mask, "skip_mask", torch.uint8, (B, Hq, nt, nt))
+    rc = load().attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq,
+                             Hkv, N, d, int(bool(causal)), float(tau),
+                             _ptr(skip_mask), _stream(stream))
+    _raise(rc)
+
+
+def attn_decode_workspace_bytes(B: int, Hq: int, L: int, d: int) -> int:
+    return int(load().attn_decode_workspace_bytes(B, Hq, L, d))
+
+
+def attn_decode(q, k, v, o, lse, tau: float, workspace, skip_mask=None,
+                stream=None) -> None:
+    """Enqueue split-K decode: q [B,Hq,d], k/v [B,Hkv,L,d] bf16; writes o
+    [B,Hq,d] fp32, lse [B,Hq] fp32 and, if given, skip_mask [B,Hq,ceil(L/64)]
+    uint8. ``workspace`` is a device tensor of at least
+    attn_decode_workspace_bytes(B, Hq, L, d) bytes."""
+    import torch
+    B, Hq, d = q.shape
+    Hkv, L = k.shape[1], k.shape[2]
+    _check(q, "q", torch.bfloat16, (B, Hq, d))
+    _check(k, "k", torch.bfloat16, (B, Hkv, L, d))
+    _check(v, "v", torch.bfloat16, (B, Hkv, L, d))
+    _check(o, "o", torch.float32, (B, Hq, d))
+    _check(lse, "lse", torch.float32, (B, Hq))
+    if skip_mask is not None:
+        _check(skip_mask, "skip_mask", torch.uint8, (B, Hq, (L + TILE - 1) // TILE))
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = load().attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv,
+                            L, d, float(tau), _ptr(skip_mask), _ptr(workspace), nbytes,
+                            _stream(stream))
+    _raise(rc)
+
+
+# ---- allocation conveniences around the two entry points ----
+
+def prefill(q, k, v, causal: bool, tau: float = math.inf, want_mask: bool = False,
+            stream=None):
+    """Allocate outputs with torch and call attn_prefill. Returns (o, lse, mask)."""
+    import torch
+    B, Hq, N, d = q.shape
+    o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    mask = None
+    if want_mask:
+        nt = (N + TILE - 1) // TILE
+        mask = torch.empty((B, Hq, nt, nt), dtype=torch.uint8, device=q.device)
+    attn_prefill(q, k, v, o, lse, causal, tau, mask, stream)
+    return o, lse, mask
+
+
+def decode(q, k, v, tau: float = math.inf, want_mask: bool = False, workspace=None,
+           stream=None):
+    """Allocate outputs (and the workspace if not given) and call attn_decode.
+    Returns (o, lse, mask)."""
+    import torch
+    B, Hq, d = q.shape
+    L = k.shape[2]
+    o = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    mask = None
+    if want_mask:
+        mask = torch.empty((B, Hq, (L + TILE - 1) // TILE), dtype=torch.uint8,
+                           device=q.device)
+    if workspace is None:
+        nbytes = max(16, attn_decode_workspace_bytes(B, Hq, L, d))
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    attn_decode(q, k, v, o, lse, tau, workspace, mask, stream)
+    return o, lse, mask

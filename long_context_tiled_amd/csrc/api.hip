@@ -1,0 +1,134 @@
+// C ABI of libskipattn: argument validation and kernel launches.
+// The operations and their readings are documented in include/skipattn.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/skipattn.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr long long kMaxElems = 1LL << 40;
+
+int check_tau(float tau) {
+  if (isnan(tau)) return fail(SKIPATTN_EINVAL, "tau is NaN");
+  if (tau < 0.f) return fail(SKIPATTN_EINVAL, "tau must be >= 0 (got %g)", (double)tau);
+  return SKIPATTN_OK;
+}
+
+int check_heads(int Hq, int Hkv) {
+  if (Hq < 1 || Hkv < 1) return fail(SKIPATTN_EINVAL, "Hq and Hkv must be >= 1 (got %d, %d)", Hq, Hkv);
+  if (Hq % Hkv != 0) return fail(SKIPATTN_EINVAL, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  return SKIPATTN_OK;
+}
+
+float tau_raw(float tau, int d) {
+  return isinf(tau) ? INFINITY : (float)((double)tau * sqrt((double)d));
+}
+
+float exp2_scale(int d) { return (float)(1.4426950408889634 / sqrt((double)d)); }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_last_error(void) { return g_err; }
+
+int attn_prefill_check(const void* q, const void* k, const void* v, const float* o,
+                       const float* lse, int B, int Hq, int Hkv, int N, int d,
+                       int causal, float tau, const uint8_t* skip_mask) {
+  (void)skip_mask;
+  g_err[0] = '\0';
+  if (!q || !k || !v || !o || !lse) return fail(SKIPATTN_EINVAL, "NULL tensor pointer");
+  if (B < 0 || N < 0 || d < 0) return fail(SKIPATTN_EINVAL, "negative size (B=%d N=%d d=%d)", B, N, d);
+  if (int e = check_heads(Hq, Hkv)) return e;
+  if (causal != 0 && causal != 1) return fail(SKIPATTN_EINVAL, "causal must be 0 or 1 (got %d)", causal);
+  if (int e = check_tau(tau)) return e;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(SKIPATTN_EINVAL, "q, k, v and o must be 16-byte aligned");
+  if ((long long)B * Hq * N * (long long)(d > 0 ? d : 1) > kMaxElems)
+    return fail(SKIPATTN_EINVAL, "tensor too large");
+  if (d != 64 && d != 128) return fail(SKIPATTN_EUNSUPPORTED, "d must be 64 or 128 (got %d)", d);
+  return SKIPATTN_OK;
+}
+
+int attn_prefill(const void* q, const void* k, const void* v, float* o, float* lse,
+                 int B, int Hq, int Hkv, int N, int d, int causal, float tau,
+                 uint8_t* skip_mask, void* stream) {
+  if (int e = attn_prefill_check(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, tau, skip_mask))
+    return e;
+  if (B == 0 || N == 0) return SKIPATTN_OK;
+  skipattn::PrefillArgs a{q, k, v, o, lse, skip_mask, B, Hq, Hkv, N, d, causal,
+                          tau_raw(tau, d), exp2_scale(d), stream};
+  if (skipattn::launch_prefill(a) != 0) return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(SKIPATTN_EHIP, "prefill launch: %s", hipGetErrorString(err));
+  return SKIPATTN_OK;
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int L, int d) {
+  if (B <= 0 || Hq <= 0 || L <= 0 || d <= 0) return 0;
+  const size_t nsplit = ((size_t)L + SKIPATTN_SPLIT - 1) / SKIPATTN_SPLIT;
+  return (size_t)B * Hq * nsplit * ((size_t)d + 1) * sizeof(float);
+}
+
+int attn_decode_check(const void* q, const void* k, const void* v, const float* o,
+                      const float* lse, int B, int Hq, int Hkv, int L, int d, float tau,
+                      const uint8_t* skip_mask, const void* workspace, size_t workspace_bytes) {
+  (void)skip_mask;
+  g_err[0] = '\0';
+  if (!q || !k || !v || !o || !lse) return fail(SKIPATTN_EINVAL, "NULL tensor pointer");
+  if (B < 0 || L < 0 || d < 0) return fail(SKIPATTN_EINVAL, "negative size (B=%d L=%d d=%d)", B, L, d);
+  if (int e = check_heads(Hq, Hkv)) return e;
+  if (int e = check_tau(tau)) return e;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(SKIPATTN_EINVAL, "q, k, v and o must be 16-byte aligned");
+  if ((long long)B * Hkv * L * (long long)(d > 0 ? d : 1) > kMaxElems)
+    return fail(SKIPATTN_EINVAL, "tensor too large");
+  if (d != 64 && d != 128) return fail(SKIPATTN_EUNSUPPORTED, "d must be 64 or 128 (got %d)", d);
+  if (Hq / Hkv > 16) return fail(SKIPATTN_EUNSUPPORTED, "decode supports at most 16 query heads per KV head (got %d)", Hq / Hkv);
+  if (B == 0 || L == 0) return SKIPATTN_OK;
+  const size_t need = attn_decode_workspace_bytes(B, Hq, L, d);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(SKIPATTN_EWORKSPACE, "decode workspace needs %zu bytes (got %zu)", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (!aligned16(workspace)) return fail(SKIPATTN_EINVAL, "workspace must be 16-byte aligned");
+  return SKIPATTN_OK;
+}
+
+int attn_decode(const void* q, const void* k, const void* v, float* o, float* lse, int B,
+                int Hq, int Hkv, int L, int d, float tau, uint8_t* skip_mask, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  if (int e = attn_decode_check(q, k, v, o, lse, B, Hq, Hkv, L, d, tau, skip_mask, workspace,
+                                workspace_bytes))
+    return e;
+  if (B == 0 || L == 0) return SKIPATTN_OK;
+  const int nsplit = (L + SKIPATTN_SPLIT - 1) / SKIPATTN_SPLIT;
+  float* ws_o = (float*)workspace;
+  float* ws_lse = ws_o + (size_t)B * Hq * nsplit * d;
+  skipattn::DecodeArgs a{q, k, v, o, lse, skip_mask, ws_o, ws_lse, B, Hq, Hkv, L, d, nsplit,
+                         tau_raw(tau, d), exp2_scale(d), stream};
+  if (skipattn::launch_decode(a) != 0) return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(SKIPATTN_EHIP, "decode launch: %s", hipGetErrorString(err));
+  return SKIPATTN_OK;
+}
+
+}  // extern "C"
