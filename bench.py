@@ -1,0 +1,310 @@
+"""Benchmark of libskipattn on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-cpu]
+
+A step is one pass of the whole hot path: a causal GQA prefill at 128K
+context (B=1, Hq=8, Hkv=1, N=131072, d=128) followed by a split-K decode
+over a 128K KV cache (B=16, Hq=64, Hkv=8, L=131072, d=128), both at
+tau = inf, on seeded synthetic bf16 inputs already resident in HBM.
+
+Printed: one JSON line. ``value`` is the prefill's dense-equivalent
+TFLOP/s (4 d x unmasked query-key pairs per call) from HIP events recorded on
+the launch stream around each call inside the timed region; the decode's KV
+GB/s is reported beside it, then a tau sweep (skip fractions, dense and
+executed TFLOP/s, dense and actual GB/s) and the fp64 oracle's throughput on
+the host cores over a bounded sample of the same workloads.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill attn TFLOP/s (dense-equiv) & decode KV GB/s at 128K ctx, per τ"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def _dev(bits, device):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def prefill_dense_flops(B, Hq, N, d, causal=True):
+    pairs = N * (N + 1) // 2 if causal else N * N
+    return 4.0 * d * B * Hq * pairs
+
+
+def prefill_exec_flops(mask, d):
+    """QK^T on every visited tile, PV on kept tiles (full-tile count)."""
+    visited = int((mask != 2).sum())
+    kept = int((mask == 0).sum())
+    return 2.0 * d * 64 * 64 * (visited + kept), visited, kept
+
+
+def decode_bytes(B, Hkv, L, d, mask=None, G=1):
+    """Dense KV bytes, and the bytes the kernel must read at this mask: all of
+    K plus the V tiles that at least one head of the KV group keeps."""
+    dense = 2.0 * B * Hkv * L * d * 2
+    if mask is None:
+        return dense, dense
+    Bm, Hq, nt = mask.shape
+    keep_any = (mask.reshape(Bm, Hkv, G, nt) == 0).any(axis=2)
+    tile_keys = np.full(nt, 64)
+    tile_keys[-1] = L - 64 * (nt - 1)
+    v_bytes = float((keep_any * tile_keys[None, None, :]).sum()) * d * 2
+    return dense, dense / 2 + v_bytes
+
+
+class Timer:
+    """HIP events on the current stream around each call."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def __enter__(self):
+        import torch
+        self.s = torch.cuda.Event(enable_timing=True)
+        self.e = torch.cuda.Event(enable_timing=True)
+        self.s.record()
+        return self
+
+    def __exit__(self, *a):
+        self.e.record()
+        self.pairs.append((self.s, self.e))
+
+    def ms(self):
+        return [s.elapsed_time(e) for s, e in self.pairs]
+
+
+# ---------------------------------------------------------------- CPU baseline
+
+_CPU = {}  # arrays shared with forked oracle workers (inherited, never pickled)
+
+
+def _cpu_prefill_block(qb):
+    from threadpoolctl import threadpool_limits
+    import oracle
+    import synth
+    with threadpool_limits(1):
+        qrows = synth.bf16_bits_to_f64(_CPU["pq"][qb * 64:(qb + 1) * 64])
+        oracle.prefill_blocks(qrows, _CPU["pk"], _CPU["pv"], qb, True, math.inf)
+
+
+def _cpu_decode_head(job):
+    from threadpoolctl import threadpool_limits
+    import oracle
+    import synth
+    i, hh = job
+    with threadpool_limits(1):
+        k, v, q = _CPU["dkv"][i]
+        oracle.decode_head(synth.bf16_bits_to_f64(q[hh]), k, v, math.inf)
+
+
+def cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=64, nkv=8):
+    """The fp64 oracle as it stands, timed on a bounded sample of each
+    workload with one process per host core (fp64 widening of the inputs is
+    done before the clock starts)."""
+    import multiprocessing as mp
+
+    import synth
+    cores = min(16, os.cpu_count() or 1)
+    N, d = pq.shape[2], pq.shape[3]
+    nt = N // 64
+    qbs = [int(x) for x in np.linspace(0, nt - 1, nblocks).astype(int)]
+    _CPU.clear()
+    _CPU.update(pq=pq[0, 0], pk=synth.bf16_bits_to_f64(pk[0, 0]),
+                pv=synth.bf16_bits_to_f64(pv[0, 0]))
+    B, Hq = dq.shape[0], dq.shape[1]
+    Hkv, L = dk.shape[1], dk.shape[2]
+    G = Hq // Hkv
+    picks = [(b, g) for b in range(B) for g in range(Hkv)][:nkv]
+    _CPU["dkv"] = [(synth.bf16_bits_to_f64(dk[b, g]), synth.bf16_bits_to_f64(dv[b, g]),
+                    dq[b, g * G:(g + 1) * G]) for b, g in picks]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores) as pool:
+        t0 = time.perf_counter()
+        pool.map(_cpu_prefill_block, qbs, chunksize=1)
+        pwall = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        pool.map(_cpu_decode_head, [(i, hh) for i in range(len(picks)) for hh in range(G)],
+                 chunksize=1)
+        dwall = time.perf_counter() - t0
+    _CPU.clear()
+    pairs = sum(64 * (qb * 64) + 64 * 65 // 2 for qb in qbs)
+    pre = dict(value=float(4.0 * d * pairs / pwall / 1e12), unit="TFLOP/s", cores=cores,
+               kind="oracle",
+               sample=f"prefill_128k head 0: {nblocks} of {nt} query blocks spread evenly, "
+                      f"tau=inf, fp64 numpy, {pwall:.1f} s wall")
+    kv_bytes = len(picks) * 2.0 * L * d * 2
+    dec = dict(value=float(kv_bytes / dwall / 1e9), unit="GB/s", cores=cores, kind="oracle",
+               sample=f"decode_128k: {len(picks)} KV heads x {G} query heads, tau=inf, "
+                      f"fp64 numpy, {dwall:.1f} s wall")
+    return pre, dec
+
+
+# ---------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--reading", default="S", choices=["S", "P"])
+    ap.add_argument("--only", default="both", choices=["both", "prefill", "decode"],
+                    help="profile one leg only (the JSON line then reports that leg)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: --gpus {args.gpus} is not supported "
+              "(this attention path has no multi-GPU mode)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import long_context_tiled_amd as lib
+    import synth
+
+    lib.load()
+    dev = torch.device("cuda:0")
+    pcfg = synth.workload("prefill_128k")
+    dcfg = synth.workload("decode_128k")
+    t0 = time.perf_counter()
+    pq, pk, pv = synth.make_prefill(pcfg, reading=args.reading)
+    dq, dk, dv = synth.make_decode(dcfg, reading=args.reading)
+    print(f"# inputs generated in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    B, Hq, N, d = pq.shape
+    Hkv = pk.shape[1]
+    tq, tk, tv = _dev(pq, dev), _dev(pk, dev), _dev(pv, dev)
+    po = torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev)
+    plse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    nt = (N + 63) // 64
+    pmask = torch.empty((B, Hq, nt, nt), dtype=torch.uint8, device=dev)
+    DB, DHq, Dd = dq.shape
+    DHkv, L = dk.shape[1], dk.shape[2]
+    uq, uk, uv = _dev(dq, dev), _dev(dk, dev), _dev(dv, dev)
+    do = torch.empty((DB, DHq, Dd), dtype=torch.float32, device=dev)
+    dlse = torch.empty((DB, DHq), dtype=torch.float32, device=dev)
+    dnt = (L + 63) // 64
+    dmask = torch.empty((DB, DHq, dnt), dtype=torch.uint8, device=dev)
+    ws = torch.empty(lib.attn_decode_workspace_bytes(DB, DHq, L, Dd), dtype=torch.uint8,
+                     device=dev)
+    torch.cuda.synchronize()
+
+    run_p = args.only in ("both", "prefill")
+    run_d = args.only in ("both", "decode")
+
+    def prefill(tau):
+        lib.attn_prefill(tq, tk, tv, po, plse, True, tau, pmask)
+
+    def decode(tau):
+        lib.attn_decode(uq, uk, uv, do, dlse, tau, ws, dmask)
+
+    for _ in range(args.warmup):
+        if run_p:
+            prefill(math.inf)
+        if run_d:
+            decode(math.inf)
+    torch.cuda.synchronize()
+
+    tp, td = Timer(), Timer()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for _ in range(args.steps):
+        if run_p:
+            with tp:
+                prefill(math.inf)
+        if run_d:
+            with td:
+                decode(math.inf)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3 / args.steps
+    print(f"# timed {args.steps} steps: {wall_ms:.2f} ms/step", file=sys.stderr, flush=True)
+
+    dense_flops = prefill_dense_flops(B, Hq, N, d)
+    out = dict(metric=METRIC, n_gpus=1, steps=args.steps, warmup=args.warmup,
+               ms_per_step=round(wall_ms, 4), higher_is_better=True, scaling="weak",
+               vs_baseline=None, dtype="bf16", data="synthetic")
+    cfg = dict(workload="prefill_128k + decode_128k, tau=inf",
+               prefill=dict(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, causal=True),
+               decode=dict(B=DB, Hq=DHq, Hkv=DHkv, L=L, d=Dd, split=4096),
+               reading=args.reading, inputs="seeded N(0,1) bf16 + sinks/band/window")
+    out["config"] = cfg
+
+    if run_p:
+        p_ms = float(np.mean(tp.ms()))
+        p_tf = dense_flops / (p_ms * 1e-3) / 1e12
+        out.update(value=round(p_tf, 3), unit="TFLOP/s")
+        out["roofline"] = dict(bound="mfma", achieved=round(p_tf, 3), peak=PEAK_BF16_TFLOPS,
+                               unit="TFLOP/s", frac=round(p_tf / PEAK_BF16_TFLOPS, 4),
+                               traffic=None, kernel="prefill_kernel<128,true,4>",
+                               avg_ms=round(p_ms, 4),
+                               per_launch_flops=dense_flops)
+    if run_d:
+        d_ms = float(np.mean(td.ms()))
+        dense_b, _ = decode_bytes(DB, DHkv, L, Dd)
+        gbs = dense_b / (d_ms * 1e-3) / 1e9
+        dec = dict(value=round(gbs, 2), unit="GB/s", ms=round(d_ms, 4),
+                   frac_of_hbm=round(gbs / PEAK_HBM_GBS, 4),
+                   per_call_kv_bytes=dense_b, kernels="decode_split_kernel<128> + decode_merge_kernel<128>")
+        out["decode"] = dec
+        if not run_p:
+            out.update(value=round(gbs, 2), unit="GB/s")
+            out["roofline"] = dict(bound="hbm", achieved=round(gbs, 2), peak=PEAK_HBM_GBS,
+                                   unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4),
+                                   traffic=None, kernel="decode_split_kernel<128>",
+                                   avg_ms=round(d_ms, 4), per_launch_bytes=dense_b)
+
+    if not args.no_sweep:
+        sweep = []
+        for tau in pcfg["taus"] if run_p else []:
+            t = Timer()
+            for _ in range(3):
+                with t:
+                    prefill(tau)
+            torch.cuda.synchronize()
+            ms = float(np.median(t.ms()))
+            m = pmask.cpu().numpy()
+            ex, vis, kept = prefill_exec_flops(m, d)
+            sweep.append(dict(leg="prefill_128k", tau=str(tau), ms=round(ms, 4),
+                              skip_fraction=round(1 - kept / vis, 4),
+                              tflops_dense=round(dense_flops / ms / 1e9, 3),
+                              tflops_executed=round(ex / ms / 1e9, 3)))
+        for tau in dcfg["taus"] if run_d else []:
+            t = Timer()
+            for _ in range(3):
+                with t:
+                    decode(tau)
+            torch.cuda.synchronize()
+            ms = float(np.median(t.ms()))
+            m = dmask.cpu().numpy()
+            dense_b, act_b = decode_bytes(DB, DHkv, L, Dd, m, DHq // DHkv)
+            sweep.append(dict(leg="decode_128k", tau=str(tau), ms=round(ms, 4),
+                              skip_fraction=round(float((m == 1).mean()), 4),
+                              gbs_dense=round(dense_b / ms / 1e6, 2),
+                              gbs_actual=round(act_b / ms / 1e6, 2)))
+        out["tau_sweep"] = sweep
+
+    if not args.no_cpu:
+        print("# cpu baseline (fp64 oracle on a bounded sample)", file=sys.stderr, flush=True)
+        pre, dec = cpu_baseline(pq, pk, pv, dq, dk, dv)
+        out["cpu_baseline"] = pre if run_p else dec
+        out["cpu_baseline_decode"] = dec
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
