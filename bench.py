@@ -164,6 +164,9 @@ def main():
     ap.add_argument("--reading", default="S", choices=["S", "P"])
     ap.add_argument("--only", default="both", choices=["both", "prefill", "decode"],
                     help="profile one leg only (the JSON line then reports that leg)")
+    ap.add_argument("--copy-ref-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB, a reference "
+                         "dispatch of known traffic for hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: --gpus {args.gpus} is not supported "
@@ -201,6 +204,17 @@ def main():
     ws = torch.empty(lib.attn_decode_workspace_bytes(DB, DHq, L, Dd), dtype=torch.uint8,
                      device=dev)
     torch.cuda.synchronize()
+
+    if args.copy_ref_mib > 0:
+        n = args.copy_ref_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"# copy reference: {args.copy_ref_mib} MiB read + {args.copy_ref_mib} MiB written",
+              file=sys.stderr, flush=True)
+        del src, dst
 
     run_p = args.only in ("both", "prefill")
     run_d = args.only in ("both", "decode")

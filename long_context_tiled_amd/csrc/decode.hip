@@ -27,28 +27,33 @@
 namespace skipattn {
 
 constexpr int kDecodeVStride = kTile * 2 + 16;  // bytes per V^T row (padded)
+constexpr uint32_t kBufferCfg = 0x00020000u;    // raw 32-bit buffer, range-checked
 
 // Position, inside a V^T LDS row, of key j of the tile: within each 32-key
-// group, key 16a + 4g + c sits at 8g + 4a + c.
+// group, key 16a + 4g + c sits at 8g + 4a + c (the order in which the S^T
+// accumulator registers hand keys to the PV MFMA's contraction index).
 __device__ __forceinline__ int dec_vt_pos(int j) {
   const int kap = j & 31;
   return (j & ~31) | (((kap >> 2) & 3) << 3) | (((kap >> 4) & 1) << 2) | (kap & 3);
 }
 
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t rs, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+}
+
 template <int D>
-__global__ __launch_bounds__(256) void decode_split_kernel(
+__global__ __launch_bounds__(256, 2) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ ws_o,
     float* __restrict__ ws_lse, uint8_t* __restrict__ mask, int Hq, int Hkv,
     int L, int nsplit, float tau_raw, float c, int nwork) {
-  constexpr int KS = D / 32;  // k-steps over d (32 each) for S^T
-  constexpr int DB = D / 16;  // 16-row d blocks of O^T
-  constexpr int C8 = D / 8;   // 16-byte chunks per row
+  constexpr int KS = D / 32;        // k-steps over d (32 each) for S^T
+  constexpr int DB = D / 16;        // 16-row d blocks of O^T
   constexpr int VB = (2 * D) / 64;  // 4-key x 8-d V blocks per lane
   __shared__ __attribute__((aligned(16))) char smem[4][D * kDecodeVStride];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int work = blockIdx.x * 4 + wave;
   if (work >= nwork) return;  // whole wave leaves; the kernel has no barrier
   const int sp = work % nsplit;
@@ -61,8 +66,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   char* vs_ = smem[wave];
 
   const size_t kv_off = (size_t)(b * Hkv + g) * L * D;
-  const uint16_t* kbase = k + kv_off;
-  const uint16_t* vbase = v + kv_off;
+  const int head_bytes = L * D * 2;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(k + kv_off), (short)0, head_bytes, kBufferCfg);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(v + kv_off), (short)0, head_bytes, kBufferCfg);
   const int ntile_all = (L + kTile - 1) / kTile;
   const int key_begin = sp * kSplit;
   const int key_end = min(L, key_begin + kSplit);
@@ -79,43 +87,40 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     qf[ks] = as_bf16x8(x);
   }
 
-  f32x4 acc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc[db][r] = 0.f;
-  float m = -INFINITY, lsum = 0.f;
-
-  // K fragments: A[m = key][k = d], key 16 mb + hl, d = 32 ks + 8 grp.
-  u32x4 kcur[4][KS], knext[4][KS];
-  auto kload = [&](int t, u32x4 (&dst)[4][KS]) {
+  // K fragments: A[m = key][k = d], key 16 mb + hl, d = 32 ks + 8 grp; keys
+  // past L read as zero.
+  u32x4 kreg[4][KS];
+  auto kload = [&](int t) {
     const int key0 = key_begin + t * kTile;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int key = key0 + 16 * mb + hl;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (key < L) x = ldg16(kbase + (size_t)key * D + ks * 32 + 8 * grp);
-        dst[mb][ks] = x;
-      }
-    }
-  };
-
-  kload(0, kcur);
-  for (int t = 0; t < ntile; ++t) {
-    if (t + 1 < ntile) kload(t + 1, knext);
-    const int key0 = key_begin + t * kTile;
-
-    // ---- S^T = K . q^T ----
-    f32x4 s[4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s[mb][r] = 0.f;
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kcur[mb][ks]), qf[ks], s[mb], 0, 0, 0);
+        kreg[mb][ks] = bload16(krs, ((key0 + 16 * mb + hl) * D + ks * 32 + 8 * grp) * 2);
+  };
+  // V blocks of 4 keys x 8 d: lane l takes key group (l & 15), d chunk
+  // (l >> 4) + 4 j, so that the transposed LDS writes of one instruction
+  // cover whole V^T rows (no bank conflicts).
+  u32x4 vreg[VB][4];
+  auto vload = [&](int t) {
+    const int key0 = key_begin + t * kTile;
+#pragma unroll
+    for (int j = 0; j < VB; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        vreg[j][i] = bload16(vrs, ((key0 + 4 * hl + i) * D + 8 * (grp + 4 * j)) * 2);
+  };
+
+  // Scores of one tile, masked past L, and the per-head tile maximum.
+  auto scores = [&](int t, f32x4 (&s)[4]) -> float {
+    const int key0 = key_begin + t * kTile;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const f32x4 zero = {};
+      s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kreg[mb][0]), qf[0], zero, 0, 0, 0);
+#pragma unroll
+      for (int ks = 1; ks < KS; ++ks)
+        s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kreg[mb][ks]), qf[ks], s[mb], 0, 0, 0);
     }
     if (key0 + kTile > L) {
 #pragma unroll
@@ -124,55 +129,80 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         for (int r = 0; r < 4; ++r)
           if (key0 + 16 * mb + 4 * grp + r >= L) s[mb][r] = -INFINITY;
     }
-
-    // ---- tile max per head, skip test per head ----
-    float tmax = s[0][0];
+    float x = s[0][0];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, s[mb][r]);
-    tmax = fmaxf(tmax, xor16(tmax));
-    tmax = fmaxf(tmax, xor32(tmax));
-    const bool keep = !(tmax < m - tau_raw);
-    if (mask != nullptr && lane < G)
-      mask[bh * ntile_all + key0 / kTile] = keep ? 0 : 1;
-    const bool any = __ballot(keep && head_ok) != 0ull;
+      for (int r = 0; r < 4; ++r) x = fmaxf(x, s[mb][r]);
+    x = fmaxf(x, xor16(x));
+    return fmaxf(x, xor32(x));
+  };
 
-    if (any) {
-      // ---- V tile -> V^T in this wave's LDS region ----
+  f32x4 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[db][r] = 0.f;
+  float m_run = -INFINITY;  // running max over kept tiles: the skip test's reference
+  float m_ref = -INFINITY;  // reference max of the exponentials accumulated so far
+  float lsum = 0.f;
+
+  // The decision of tile t+1 is taken while tile t's V is still in flight:
+  // scores run one tile ahead of the exp/PV work.
+  auto decide = [&](float tmax, int t, bool& keep) -> bool {
+    keep = !(tmax < m_run - tau_raw);
+    if (keep) m_run = fmaxf(m_run, tmax);
+    if (mask != nullptr && lane < G)
+      mask[bh * ntile_all + (key_begin / kTile + t)] = keep ? 0 : 1;
+    return __ballot(keep && head_ok) != 0ull;
+  };
+
+  kload(0);
+  f32x4 s_cur[4];
+  float t_cur = scores(0, s_cur);
+  bool keep_cur;
+  bool any_cur = decide(t_cur, 0, keep_cur);
+  if (ntile > 1) kload(1);
+  if (any_cur) vload(0);
+
+  for (int t = 0; t < ntile; ++t) {
+    f32x4 s_nx[4];
+    float t_nx = -INFINITY;
+    bool keep_nx = false, any_nx = false;
+    if (t + 1 < ntile) {
+      t_nx = scores(t + 1, s_nx);
+      any_nx = decide(t_nx, t + 1, keep_nx);
+      if (t + 2 < ntile) kload(t + 2);
+    }
+    if (any_cur) {
+      // ---- V tile t -> V^T in this wave's LDS region ----
 #pragma unroll
       for (int j = 0; j < VB; ++j) {
-        const int blk = lane + 64 * j;
-        const int kg = blk / C8, dc = blk % C8;
-        u32x4 rows[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = key0 + 4 * kg + i;
-          u32x4 x = {0u, 0u, 0u, 0u};
-          if (key < L) x = ldg16(vbase + (size_t)key * D + dc * 8);
-          rows[i] = x;
-        }
-        const int pos = dec_vt_pos(4 * kg);
+        const int dc = grp + 4 * j;
+        const int pos = dec_vt_pos(4 * hl);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           *reinterpret_cast<u32x2*>(vs_ + (dc * 8 + e) * kDecodeVStride + pos * 2) =
-              column_of_4x8(rows, e);
+              column_of_4x8(vreg[j], e);
       }
+    }
+    if (any_nx) vload(t + 1);
+    if (any_cur) {
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
       __builtin_amdgcn_wave_barrier();
 
-      // ---- online softmax for the heads that keep the tile ----
-      const float mn = keep ? fmaxf(m, tmax) : m;
-      if (mn > m) {
-        const float alpha = exp2_fast((m - mn) * c);
+      // ---- online softmax for the heads that keep tile t ----
+      const float mn = keep_cur ? fmaxf(m_ref, t_cur) : m_ref;
+      if (mn > m_ref) {
+        const float alpha = exp2_fast((m_ref - mn) * c);
         lsum *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[db][r] *= alpha;
+        m_ref = mn;
       }
-      m = mn;
-      const float nmc = -mn * c;
+      const float nmc = -m_ref * c;
       bf16x8 pf[2];
       float part = 0.f;
 #pragma unroll
@@ -182,9 +212,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         for (int i2 = 0; i2 < 4; ++i2) {
           const int mb = 2 * ks + (i2 >> 1);
           const int r0 = 2 * (i2 & 1);
-          float p0 = exp2_fast(__builtin_fmaf(s[mb][r0], c, nmc));
-          float p1 = exp2_fast(__builtin_fmaf(s[mb][r0 + 1], c, nmc));
-          if (!keep) { p0 = 0.f; p1 = 0.f; }
+          float p0 = exp2_fast(__builtin_fmaf(s_cur[mb][r0], c, nmc));
+          float p1 = exp2_fast(__builtin_fmaf(s_cur[mb][r0 + 1], c, nmc));
+          if (!keep_cur) { p0 = 0.f; p1 = 0.f; }
           part += p0 + p1;
           w[i2] = pack_bf16x2(p0, p1);
         }
@@ -204,11 +234,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
       __builtin_amdgcn_s_waitcnt(0xc07f);
       __builtin_amdgcn_wave_barrier();
     }
-
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kcur[mb][ks] = knext[mb][ks];
+    for (int mb = 0; mb < 4; ++mb) s_cur[mb] = s_nx[mb];
+    t_cur = t_nx;
+    keep_cur = keep_nx;
+    any_cur = any_nx;
   }
 
   // ---- split epilogue: normalised partial output and its LSE ----
@@ -224,7 +254,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
       for (int r = 0; r < 4; ++r) val[r] = acc[db][r] * inv;
       *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * grp) = val;
     }
-    if (grp == 0) ws_lse[bh * nsplit + sp] = (m * c + __log2f(ltot)) * kLn2;
+    if (grp == 0) ws_lse[bh * nsplit + sp] = (m_ref * c + __log2f(ltot)) * kLn2;
   }
 }
 
