@@ -88,44 +88,39 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
 }
 
 // V^T fragments of one 16-key step for MB 32-d blocks: two transpose reads
-// per block (keys +0..3 and +8..11 of each lane half). The reads and the wait
-// for them are one asm block, so no load is left in flight past it and the
-// compiler adds no wait on the tile copies still in flight.
-template <int MB>
-__device__ __forceinline__ void read_vt(bf16x8 (&vf)[MB], uint32_t base, uint32_t a0, uint32_t a1) {
+// per block (keys +0..3 and +8..11 of each lane half) at the per-lane LDS
+// addresses ad[] plus the immediate KOFF. The reads and the wait for them are
+// one asm block, so no load is left in flight past it and the compiler adds
+// no wait on the tile copies still in flight.
+template <int MB, int KOFF>
+__device__ __forceinline__ void read_vt(bf16x8 (&vf)[MB], const uint32_t (&ad)[2 * MB]) {
   typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
   u32x2v r[2 * MB];
-  uint32_t ad[2 * MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    ad[2 * mb] = base + (a0 ^ (64u * mb));
-    ad[2 * mb + 1] = base + (a1 ^ (64u * mb));
-  }
   if constexpr (MB == 4) {
     asm volatile(
-        "ds_read_b64_tr_b16 %0, %8\n\t"
-        "ds_read_b64_tr_b16 %1, %9\n\t"
-        "ds_read_b64_tr_b16 %2, %10\n\t"
-        "ds_read_b64_tr_b16 %3, %11\n\t"
-        "ds_read_b64_tr_b16 %4, %12\n\t"
-        "ds_read_b64_tr_b16 %5, %13\n\t"
-        "ds_read_b64_tr_b16 %6, %14\n\t"
-        "ds_read_b64_tr_b16 %7, %15\n\t"
+        "ds_read_b64_tr_b16 %0, %8 offset:%c16\n\t"
+        "ds_read_b64_tr_b16 %1, %9 offset:%c16\n\t"
+        "ds_read_b64_tr_b16 %2, %10 offset:%c16\n\t"
+        "ds_read_b64_tr_b16 %3, %11 offset:%c16\n\t"
+        "ds_read_b64_tr_b16 %4, %12 offset:%c16\n\t"
+        "ds_read_b64_tr_b16 %5, %13 offset:%c16\n\t"
+        "ds_read_b64_tr_b16 %6, %14 offset:%c16\n\t"
+        "ds_read_b64_tr_b16 %7, %15 offset:%c16\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
           "=&v"(r[6]), "=&v"(r[7])
         : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]),
-          "v"(ad[7])
+          "v"(ad[7]), "i"(KOFF)
         : "memory");
   } else {
     asm volatile(
-        "ds_read_b64_tr_b16 %0, %4\n\t"
-        "ds_read_b64_tr_b16 %1, %5\n\t"
-        "ds_read_b64_tr_b16 %2, %6\n\t"
-        "ds_read_b64_tr_b16 %3, %7\n\t"
+        "ds_read_b64_tr_b16 %0, %4 offset:%c8\n\t"
+        "ds_read_b64_tr_b16 %1, %5 offset:%c8\n\t"
+        "ds_read_b64_tr_b16 %2, %6 offset:%c8\n\t"
+        "ds_read_b64_tr_b16 %3, %7 offset:%c8\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
-        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "i"(KOFF)
         : "memory");
   }
 #pragma unroll
@@ -137,6 +132,162 @@ __device__ __forceinline__ void read_vt(bf16x8 (&vf)[MB], uint32_t base, uint32_
     w[3] = r[2 * mb + 1][1];
     vf[mb] = as_bf16x8(w);
   }
+}
+
+// The O^T accumulators live in fixed AGPRs: block (mb, nb) of the 128-d
+// kernel is a[32 mb + 16 nb : +15] (a[0:63] for d = 64). Every asm statement
+// that touches them names those registers, so the register allocator keeps
+// them there for the whole key loop. (Written as builtins inside the
+// kept-tile branch, the allocator parks them in VGPRs between iterations and
+// copies all of them on every tile.)
+#define SKA_ACC8                                                                   \
+  "+{a[0:15]}"(acc[0][0]), "+{a[16:31]}"(acc[0][1]), "+{a[32:47]}"(acc[1][0]),     \
+      "+{a[48:63]}"(acc[1][1]), "+{a[64:79]}"(acc[2][0]), "+{a[80:95]}"(acc[2][1]), \
+      "+{a[96:111]}"(acc[3][0]), "+{a[112:127]}"(acc[3][1])
+#define SKA_ACC4 \
+  "+{a[0:15]}"(acc[0][0]), "+{a[16:31]}"(acc[0][1]), "+{a[32:47]}"(acc[1][0]), "+{a[48:63]}"(acc[1][1])
+
+// O^T += V^T . P^T for one 16-key step. The leading s_nop covers the
+// VALU-write to MFMA-read wait states of the P and V operands.
+__device__ __forceinline__ void pv_step(f32x16 (&acc)[4][2], const bf16x8 (&vf)[4],
+                                        const bf16x8 (&pf)[2]) {
+  asm volatile(
+      "s_nop 4\n\t"
+      "v_mfma_f32_32x32x16_bf16 a[0:15], %8, %12, a[0:15]\n\t"
+      "v_mfma_f32_32x32x16_bf16 a[16:31], %8, %13, a[16:31]\n\t"
+      "v_mfma_f32_32x32x16_bf16 a[32:47], %9, %12, a[32:47]\n\t"
+      "v_mfma_f32_32x32x16_bf16 a[48:63], %9, %13, a[48:63]\n\t"
+      "v_mfma_f32_32x32x16_bf16 a[64:79], %10, %12, a[64:79]\n\t"
+      "v_mfma_f32_32x32x16_bf16 a[80:95], %10, %13, a[80:95]\n\t"
+      "v_mfma_f32_32x32x16_bf16 a[96:111], %11, %12, a[96:111]\n\t"
+      "v_mfma_f32_32x32x16_bf16 a[112:127], %11, %13, a[112:127]"
+      : SKA_ACC8
+      : "v"(vf[0]), "v"(vf[1]), "v"(vf[2]), "v"(vf[3]), "v"(pf[0]), "v"(pf[1]));
+}
+
+__device__ __forceinline__ void pv_step(f32x16 (&acc)[2][2], const bf16x8 (&vf)[2],
+                                        const bf16x8 (&pf)[2]) {
+  asm volatile(
+      "s_nop 4\n\t"
+      "v_mfma_f32_32x32x16_bf16 a[0:15], %4, %6, a[0:15]\n\t"
+      "v_mfma_f32_32x32x16_bf16 a[16:31], %4, %7, a[16:31]\n\t"
+      "v_mfma_f32_32x32x16_bf16 a[32:47], %5, %6, a[32:47]\n\t"
+      "v_mfma_f32_32x32x16_bf16 a[48:63], %5, %7, a[48:63]"
+      : SKA_ACC4
+      : "v"(vf[0]), "v"(vf[1]), "v"(pf[0]), "v"(pf[1]));
+}
+
+// Wait states after the last accumulating MFMA (16 passes) before its result
+// registers may be read by other instructions.
+__device__ __forceinline__ void drain_mfma() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
+// Zero the pinned accumulators.
+#define SKA_Z4(a, b, c, d)                                                     \
+  "v_accvgpr_write_b32 a" #a ", 0\n\tv_accvgpr_write_b32 a" #b ", 0\n\t"        \
+  "v_accvgpr_write_b32 a" #c ", 0\n\tv_accvgpr_write_b32 a" #d ", 0\n\t"
+
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][2]) {
+  asm volatile(
+      SKA_Z4(0, 1, 2, 3) SKA_Z4(4, 5, 6, 7) SKA_Z4(8, 9, 10, 11) SKA_Z4(12, 13, 14, 15)
+      SKA_Z4(16, 17, 18, 19) SKA_Z4(20, 21, 22, 23) SKA_Z4(24, 25, 26, 27) SKA_Z4(28, 29, 30, 31)
+      SKA_Z4(32, 33, 34, 35) SKA_Z4(36, 37, 38, 39) SKA_Z4(40, 41, 42, 43) SKA_Z4(44, 45, 46, 47)
+      SKA_Z4(48, 49, 50, 51) SKA_Z4(52, 53, 54, 55) SKA_Z4(56, 57, 58, 59) SKA_Z4(60, 61, 62, 63)
+      SKA_Z4(64, 65, 66, 67) SKA_Z4(68, 69, 70, 71) SKA_Z4(72, 73, 74, 75) SKA_Z4(76, 77, 78, 79)
+      SKA_Z4(80, 81, 82, 83) SKA_Z4(84, 85, 86, 87) SKA_Z4(88, 89, 90, 91) SKA_Z4(92, 93, 94, 95)
+      SKA_Z4(96, 97, 98, 99) SKA_Z4(100, 101, 102, 103) SKA_Z4(104, 105, 106, 107)
+      SKA_Z4(108, 109, 110, 111) SKA_Z4(112, 113, 114, 115) SKA_Z4(116, 117, 118, 119)
+      SKA_Z4(120, 121, 122, 123) SKA_Z4(124, 125, 126, 127)
+      "s_nop 1"
+      : "={a[0:15]}"(acc[0][0]), "={a[16:31]}"(acc[0][1]), "={a[32:47]}"(acc[1][0]),
+        "={a[48:63]}"(acc[1][1]), "={a[64:79]}"(acc[2][0]), "={a[80:95]}"(acc[2][1]),
+        "={a[96:111]}"(acc[3][0]), "={a[112:127]}"(acc[3][1]));
+}
+
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[2][2]) {
+  asm volatile(
+      SKA_Z4(0, 1, 2, 3) SKA_Z4(4, 5, 6, 7) SKA_Z4(8, 9, 10, 11) SKA_Z4(12, 13, 14, 15)
+      SKA_Z4(16, 17, 18, 19) SKA_Z4(20, 21, 22, 23) SKA_Z4(24, 25, 26, 27) SKA_Z4(28, 29, 30, 31)
+      SKA_Z4(32, 33, 34, 35) SKA_Z4(36, 37, 38, 39) SKA_Z4(40, 41, 42, 43) SKA_Z4(44, 45, 46, 47)
+      SKA_Z4(48, 49, 50, 51) SKA_Z4(52, 53, 54, 55) SKA_Z4(56, 57, 58, 59) SKA_Z4(60, 61, 62, 63)
+      "s_nop 1"
+      : "={a[0:15]}"(acc[0][0]), "={a[16:31]}"(acc[0][1]), "={a[32:47]}"(acc[1][0]),
+        "={a[48:63]}"(acc[1][1]));
+}
+
+// Copy one pinned accumulator block into 16 VGPR floats.
+#define SKA_RD1(i, n) "v_accvgpr_read_b32 %" #i ", a" #n "\n\t"
+#define SKA_READ16(RANGE, blk, out, n0, n1, n2, n3, n4, n5, n6, n7, n8, n9, n10, n11, n12, n13, \
+                   n14, n15)                                                                   \
+  asm volatile(SKA_RD1(0, n0) SKA_RD1(1, n1) SKA_RD1(2, n2) SKA_RD1(3, n3) SKA_RD1(4, n4)       \
+                   SKA_RD1(5, n5) SKA_RD1(6, n6) SKA_RD1(7, n7) SKA_RD1(8, n8) SKA_RD1(9, n9)   \
+                       SKA_RD1(10, n10) SKA_RD1(11, n11) SKA_RD1(12, n12) SKA_RD1(13, n13)      \
+                           SKA_RD1(14, n14) SKA_RD1(15, n15) "s_nop 1"                          \
+               : "=v"(out[0]), "=v"(out[1]), "=v"(out[2]), "=v"(out[3]), "=v"(out[4]),         \
+                 "=v"(out[5]), "=v"(out[6]), "=v"(out[7]), "=v"(out[8]), "=v"(out[9]),         \
+                 "=v"(out[10]), "=v"(out[11]), "=v"(out[12]), "=v"(out[13]), "=v"(out[14]),    \
+                 "=v"(out[15])                                                                  \
+               : RANGE(blk))
+
+// Block (mb, nb) of the pinned accumulators, as 16 floats in VGPRs.
+template <int MBX>
+__device__ __forceinline__ void read_acc(const f32x16 (&acc)[MBX][2], int mb, int nb, float (&o)[16]) {
+  const int id = 2 * mb + nb;
+  if (id == 0) SKA_READ16("{a[0:15]}", acc[0][0], o, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+  if (id == 1) SKA_READ16("{a[16:31]}", acc[0][1], o, 16, 17, 18, 19, 20, 21, 22, 23, 24, 25, 26, 27, 28, 29, 30, 31);
+  if (id == 2) SKA_READ16("{a[32:47]}", acc[1][0], o, 32, 33, 34, 35, 36, 37, 38, 39, 40, 41, 42, 43, 44, 45, 46, 47);
+  if (id == 3) SKA_READ16("{a[48:63]}", acc[1][1], o, 48, 49, 50, 51, 52, 53, 54, 55, 56, 57, 58, 59, 60, 61, 62, 63);
+  if constexpr (MBX == 4) {
+    if (id == 4) SKA_READ16("{a[64:79]}", acc[2][0], o, 64, 65, 66, 67, 68, 69, 70, 71, 72, 73, 74, 75, 76, 77, 78, 79);
+    if (id == 5) SKA_READ16("{a[80:95]}", acc[2][1], o, 80, 81, 82, 83, 84, 85, 86, 87, 88, 89, 90, 91, 92, 93, 94, 95);
+    if (id == 6) SKA_READ16("{a[96:111]}", acc[3][0], o, 96, 97, 98, 99, 100, 101, 102, 103, 104, 105, 106, 107, 108, 109, 110, 111);
+    if (id == 7) SKA_READ16("{a[112:127]}", acc[3][1], o, 112, 113, 114, 115, 116, 117, 118, 119, 120, 121, 122, 123, 124, 125, 126, 127);
+  }
+}
+
+// acc[.][nb] *= alpha in place, on the pinned AGPRs.
+#define SKA_R1(n)                                                                \
+  "v_accvgpr_read_b32 %[t], a" #n "\n\ts_nop 1\n\tv_mul_f32 %[t], %[t], %[al]\n\t" \
+  "s_nop 1\n\tv_accvgpr_write_b32 a" #n ", %[t]\n\t"
+#define SKA_R4(a, b, c, d) SKA_R1(a) SKA_R1(b) SKA_R1(c) SKA_R1(d)
+#define SKA_R16(a0, a1, a2, a3, a4, a5, a6, a7, a8, a9, a10, a11, a12, a13, a14, a15) \
+  SKA_R4(a0, a1, a2, a3) SKA_R4(a4, a5, a6, a7) SKA_R4(a8, a9, a10, a11) SKA_R4(a12, a13, a14, a15)
+
+__device__ __forceinline__ void rescale_acc(f32x16 (&acc)[4][2], float alpha0, float alpha1) {
+  float t;
+  asm volatile(
+      SKA_R16(0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15)
+      SKA_R16(32, 33, 34, 35, 36, 37, 38, 39, 40, 41, 42, 43, 44, 45, 46, 47)
+      SKA_R16(64, 65, 66, 67, 68, 69, 70, 71, 72, 73, 74, 75, 76, 77, 78, 79)
+      SKA_R16(96, 97, 98, 99, 100, 101, 102, 103, 104, 105, 106, 107, 108, 109, 110, 111)
+      "s_nop 1"
+      : SKA_ACC8, [t] "=&v"(t)
+      : [al] "v"(alpha0));
+  asm volatile(
+      SKA_R16(16, 17, 18, 19, 20, 21, 22, 23, 24, 25, 26, 27, 28, 29, 30, 31)
+      SKA_R16(48, 49, 50, 51, 52, 53, 54, 55, 56, 57, 58, 59, 60, 61, 62, 63)
+      SKA_R16(80, 81, 82, 83, 84, 85, 86, 87, 88, 89, 90, 91, 92, 93, 94, 95)
+      SKA_R16(112, 113, 114, 115, 116, 117, 118, 119, 120, 121, 122, 123, 124, 125, 126, 127)
+      "s_nop 1"
+      : SKA_ACC8, [t] "=&v"(t)
+      : [al] "v"(alpha1));
+}
+
+__device__ __forceinline__ void rescale_acc(f32x16 (&acc)[2][2], float alpha0, float alpha1) {
+  float t;
+  asm volatile(
+      SKA_R16(0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15)
+      SKA_R16(32, 33, 34, 35, 36, 37, 38, 39, 40, 41, 42, 43, 44, 45, 46, 47)
+      "s_nop 1"
+      : SKA_ACC4, [t] "=&v"(t)
+      : [al] "v"(alpha0));
+  asm volatile(
+      SKA_R16(16, 17, 18, 19, 20, 21, 22, 23, 24, 25, 26, 27, 28, 29, 30, 31)
+      SKA_R16(48, 49, 50, 51, 52, 53, 54, 55, 56, 57, 58, 59, 60, 61, 62, 63)
+      "s_nop 1"
+      : SKA_ACC4, [t] "=&v"(t)
+      : [al] "v"(alpha1));
 }
 
 // One 16-byte-per-lane copy from a buffer straight into LDS: lane i writes
@@ -158,7 +309,8 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(
   constexpr int MB = D / 32;     // 32-row d blocks of O^T
   using T = PrefillTile<D>;
   constexpr int STAGE_BYTES = 2 * T::bytes;
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
+  // K/V stages, then one 64-row Q tile per wave.
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES + 4 * T::bytes];
   typedef __attribute__((address_space(3))) char lds_char;
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_char*)smem;  // LDS byte address
 
@@ -195,17 +347,6 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(
 
   // Q^T fragments (B operand of S^T = K . Q^T): query row (l & 31) of each
   // 32-query half, d = 16 ks + 8 (l >> 5) .. + 7. Rows past N read as 0.
-  bf16x8 qf[2][KS];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int row = wave_valid ? qb * kTile + nb * 32 + l32 : N;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const auto x = __builtin_amdgcn_raw_buffer_load_b128(qrs, (row * D + ks * 16 + 8 * hh) * 2, 0, 0);
-      qf[nb][ks] = __builtin_bit_cast(bf16x8, x);
-    }
-  }
-
   // Per-lane load geometry for the direct-to-LDS copies: instruction i of
   // wave w fills LDS bytes [1024 (w * IPW + i), +1024) of the tile.
   constexpr int IPW = T::instrPerWave;
@@ -233,6 +374,20 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(
     }
   };
 
+  // The wave's 64 query rows go to its own swizzled LDS tile once (rows past
+  // N read as zero); Q^T fragments are read from there for every key tile.
+  char* qs_ = smem + STAGES * STAGE_BYTES + wave * T::bytes;
+  if (wave_valid) {
+    constexpr int QI = T::bytes / 1024;  // 1 KB copy instructions per Q tile
+#pragma unroll
+    for (int i = 0; i < QI; ++i) {
+      const int r = i * T::rowsPerInstr + lane / T::chunks;
+      const int slot = lane % T::chunks;
+      const int cc = slot ^ (r & (T::chunks - 1));
+      dma16(qrs, (lds_void*)(qs_ + 1024 * i), (qb * kTile + r) * T::rowBytes + cc * 16);
+    }
+  }
+
   // ds_read_b64_tr_b16 geometry for the V^T operand: lane k of a 16-lane
   // group fetches 4 consecutive d of key row (16 ks + key_base + k / 4); the
   // instruction hands lane i of the group element (i % 4) of the chunks of
@@ -240,23 +395,22 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(
   // block mb, the swizzled address is A ^ (64 mb) with A fixed per lane.
   const int grp16 = lane >> 4;
   const int k16 = lane & 15;
-  uint32_t tr_addr[2];  // rows tr_row and tr_row + 8 of key step 0, mb = 0
+  uint32_t tr_off[2 * MB];  // LDS address (stage 0) of each (mb, 4-key half) read
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const int row = 4 * (grp16 >> 1) + (k16 >> 2) + 8 * half;
     const int d = 16 * (grp16 & 1) + 4 * (k16 & 3);
-    tr_addr[half] = (uint32_t)(swz<D>(row, d >> 3) + 2 * (d & 7));
+    const uint32_t a = (uint32_t)(swz<D>(row, d >> 3) + 2 * (d & 7));
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) tr_off[2 * mb + half] = smem_lds + (a ^ (64u * mb));
   }
 
-  f32x16 acc[MB][2];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
-  float m[2] = {-INFINITY, -INFINITY};
+  f32x16 acc[MB][2];  // O^T accumulators, pinned to AGPRs (see pv_step)
+  zero_acc(acc);
+  float m[2] = {-INFINITY, -INFINITY};     // running max over kept tiles (skip test)
+  float mref[2] = {-INFINITY, -INFINITY};  // reference max of what acc / lsum hold
   float lsum[2] = {0.f, 0.f};
+  const float lazy_raw = 8.0f / c;         // 8 in log2 units, as a raw-score gap
 
   // Prologue: tiles 0 .. STAGES-2 in flight.
 #pragma unroll
@@ -287,11 +441,13 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(
           const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks_ + swz<D>(row, 2 * ks + hh));
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb) {
+            const bf16x8 qf =
+                *reinterpret_cast<const bf16x8*>(qs_ + swz<D>(nb * 32 + l32, 2 * ks + hh));
             if (ks == 0) {
               const f32x16 zero = {};
-              s[a][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[nb][0], zero, 0, 0, 0);
+              s[a][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf, zero, 0, 0, 0);
             } else {
-              s[a][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[nb][ks], s[a][nb], 0, 0, 0);
+              s[a][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf, s[a][nb], 0, 0, 0);
             }
           }
         }
@@ -338,30 +494,33 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(
 
       if (!skip) {
         // ---- online softmax update ----
-        float mn[2];
+        // m is the running max of the skip test. The exponentials use a
+        // reference mref <= m that is only raised (with a rescale of acc and
+        // lsum) once some row's max exceeds it by more than 2^8 in weight,
+        // so the rescale is rare; the final O = acc / l and LSE = mref / sqrt(d)
+        // + ln l do not depend on which reference was used.
         bool grow = false;
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
-          mn[nb] = fmaxf(m[nb], t[nb]);
-          grow |= mn[nb] > m[nb];
+          m[nb] = fmaxf(m[nb], t[nb]);
+          grow |= m[nb] > mref[nb] + lazy_raw;
         }
         if (__ballot(grow) != 0ull) {
+          drain_mfma();
+          float alpha[2];
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb) {
-            const float alpha = exp2_fast((m[nb] - mn[nb]) * c);
-            lsum[nb] *= alpha;
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) acc[mb][nb][r] *= alpha;
+            alpha[nb] = m[nb] > mref[nb] ? exp2_fast((mref[nb] - m[nb]) * c) : 1.0f;
+            lsum[nb] *= alpha[nb];
+            mref[nb] = fmaxf(mref[nb], m[nb]);
           }
+          rescale_acc(acc, alpha[0], alpha[1]);
         }
         bf16x8 pf[4][2];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
-          m[nb] = mn[nb];
-          const float nmc = -mn[nb] * c;
-          float part = 0.f;
+          const float nmc = -mref[nb] * c;
+          float l = lsum[nb];
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks) {
             u32x4 w;
@@ -370,31 +529,34 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(
               const int r0 = 8 * (ks & 1) + 2 * i2;
               const float p0 = exp2_fast(__builtin_fmaf(s[ks >> 1][nb][r0], c, nmc));
               const float p1 = exp2_fast(__builtin_fmaf(s[ks >> 1][nb][r0 + 1], c, nmc));
-              part += p0 + p1;
               w[i2] = pack_bf16x2(p0, p1);
+              l += p0 + p1;  // fp32 row sum of the unrounded weights
             }
             pf[ks][nb] = as_bf16x8(w);
           }
-          lsum[nb] += part;
+          lsum[nb] = l;
         }
 
         // ---- O^T += V^T . P^T ----
-        const uint32_t vbase = smem_lds + (uint32_t)(vs_ - smem);
+        const uint32_t vstage = (uint32_t)(vs_ - smem);
+        uint32_t ad[2 * MB];
+#pragma unroll
+        for (int i = 0; i < 2 * MB; ++i) ad[i] = tr_off[i] + vstage;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           bf16x8 vf[MB];
-          read_vt<MB>(vf, vbase + 16 * ks * T::rowBytes, tr_addr[0], tr_addr[1]);
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[mb], pf[ks][nb], acc[mb][nb], 0, 0, 0);
+          if (ks == 0) read_vt<MB, 0 * 16 * T::rowBytes>(vf, ad);
+          if (ks == 1) read_vt<MB, 1 * 16 * T::rowBytes>(vf, ad);
+          if (ks == 2) read_vt<MB, 2 * 16 * T::rowBytes>(vf, ad);
+          if (ks == 3) read_vt<MB, 3 * 16 * T::rowBytes>(vf, ad);
+          pv_step(acc, vf, pf[ks]);
         }
       }
     }
   }
 
   if (!wave_valid) return;
+  drain_mfma();
 
   // ---- epilogue: O = O^T / l, LSE = m / sqrt(d) + ln l ----
 #pragma unroll
@@ -405,15 +567,18 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(
     if (row < N) {
       float* orow = o + (bh * N + row) * D;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < MB; ++mb) {
+        float ov[16];
+        read_acc<MB>(acc, mb, nb, ov);
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           f32x4 val;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) val[i] = acc[mb][nb][4 * r4 + i] * inv;
+          for (int i = 0; i < 4; ++i) val[i] = ov[4 * r4 + i] * inv;
           *reinterpret_cast<f32x4*>(orow + mb * 32 + 8 * r4 + 4 * hh) = val;
         }
-      if (hh == 0) lse[bh * N + row] = (m[nb] * c + __log2f(ltot)) * kLn2;
+      }
+      if (hh == 0) lse[bh * N + row] = (mref[nb] * c + __log2f(ltot)) * kLn2;
     }
   }
   if (CAUSAL && mask != nullptr) {
