@@ -33,6 +33,33 @@ METRIC = "prefill attn TFLOP/s (dense-equiv) & decode KV GB/s at 128K ctx, per Ï
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
+# HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE,
+# scaled by the same counters on a 1 GiB copy (FETCH x 2.0, WRITE x 1.0).
+# Keyed by the SHA-1 of the kernel's source files: once a kernel changes the
+# figure no longer applies and is reported as null.
+MEASURED_TRAFFIC = {
+    "prefill": {"sources": ("prefill.hip", "common.hpp"),
+                "sha1": "017610a1fcf1bc5a30ab0876ae09e3cd82bad489",
+                "bytes": (3169463.1 * 2.0 + 564678.2) * 1024},
+    "decode": {"sources": ("decode.hip", "common.hpp"),
+               "sha1": "eb18a592b854d20636e2a86f58719610c49806d3",
+               "bytes": (4210048.9 * 2.0 + 94330.1) * 1024},
+}
+
+
+def _source_sha1(names):
+    import hashlib
+    h = hashlib.sha1()
+    for n in names:
+        with open(os.path.join(ROOT, "long_context_tiled_amd", "csrc", n), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(leg):
+    t = MEASURED_TRAFFIC[leg]
+    return t["bytes"] if _source_sha1(t["sources"]) == t["sha1"] else None
+
 
 def _dev(bits, device):
     import torch
@@ -262,7 +289,8 @@ def main():
         out.update(value=round(p_tf, 3), unit="TFLOP/s")
         out["roofline"] = dict(bound="mfma", achieved=round(p_tf, 3), peak=PEAK_BF16_TFLOPS,
                                unit="TFLOP/s", frac=round(p_tf / PEAK_BF16_TFLOPS, 4),
-                               traffic=None, kernel="prefill_kernel<128,true,4>",
+                               traffic=measured_traffic("prefill"),
+                               kernel="prefill_kernel<128,true,4>",
                                avg_ms=round(p_ms, 4),
                                per_launch_flops=dense_flops)
     if run_d:
@@ -270,6 +298,7 @@ def main():
         dense_b, _ = decode_bytes(DB, DHkv, L, Dd)
         gbs = dense_b / (d_ms * 1e-3) / 1e9
         dec = dict(value=round(gbs, 2), unit="GB/s", ms=round(d_ms, 4),
+                   traffic=measured_traffic("decode"),
                    frac_of_hbm=round(gbs / PEAK_HBM_GBS, 4),
                    per_call_kv_bytes=dense_b, kernels="decode_split_kernel<128> + decode_merge_kernel<128>")
         out["decode"] = dec
@@ -277,7 +306,8 @@ def main():
             out.update(value=round(gbs, 2), unit="GB/s")
             out["roofline"] = dict(bound="hbm", achieved=round(gbs, 2), peak=PEAK_HBM_GBS,
                                    unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4),
-                                   traffic=None, kernel="decode_split_kernel<128>",
+                                   traffic=measured_traffic("decode"),
+                                   kernel="decode_split_kernel<128>",
                                    avg_ms=round(d_ms, 4), per_launch_bytes=dense_b)
 
     if not args.no_sweep:
