@@ -3,7 +3,9 @@
     python -m long_context_tiled_amd.build        # or build() from Python
 
 Every HIP source under csrc/ is compiled for gfx950 only and linked into
-long_context_tiled_amd/libskipattn.so.
+long_context_tiled_amd/libskipattn.so. The prefill kernel's hand-scheduled
+tile steps (csrc/prefill_steps.inc) are rewritten from
+csrc/gen_prefill_steps.py first.
 """
 from __future__ import annotations
 
@@ -19,7 +21,7 @@ BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.hip", "prefill.hip", "decode.hip"]
-HEADERS = ["common.hpp", "launch.hpp"]
+HEADERS = ["common.hpp", "launch.hpp", "prefill_steps.inc"]
 
 # Packed fp32 VALU ops are disabled: hipcc otherwise forms them from plain
 # float code.
@@ -37,7 +39,16 @@ def _compile(src: str) -> str:
     return obj
 
 
+def generate() -> None:
+    """Rewrite csrc/prefill_steps.inc from its generator."""
+    r = subprocess.run([sys.executable, os.path.join(CSRC, "gen_prefill_steps.py")],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gen_prefill_steps.py failed:\n{r.stdout}\n{r.stderr}")
+
+
 def build(verbose: bool = False) -> str:
+    generate()
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(len(SOURCES)) as ex:
         objs = list(ex.map(_compile, SOURCES))

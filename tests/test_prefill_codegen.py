@@ -1,0 +1,102 @@
+"""Host-side checks of the prefill kernel's generated instruction blocks.
+
+The per-tile steps are hand-scheduled asm written by
+long_context_tiled_amd/csrc/gen_prefill_steps.py. They name fixed registers
+(O^T and Q^T in AGPRs, two score buffers, fragments and P^T in VGPRs), and the
+kernel limits the compiler to v[0:48) / a[0:48). These tests check that the
+committed blocks are the generator's output, that the compiled kernel keeps
+that contract (no compiler instruction touches a reserved register), and that
+every kernel is launched with the full register file it names."""
+import os
+import re
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "long_context_tiled_amd", "csrc")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+RESERVED_FROM = 48
+
+
+def test_steps_inc_is_generator_output():
+    with tempfile.TemporaryDirectory() as td:
+        out = os.path.join(td, "steps.inc")
+        subprocess.run([sys.executable, os.path.join(CSRC, "gen_prefill_steps.py"), out], check=True)
+        with open(out) as f:
+            fresh = f.read()
+    with open(os.path.join(CSRC, "prefill_steps.inc")) as f:
+        committed = f.read()
+    assert fresh == committed, "prefill_steps.inc is stale: rerun gen_prefill_steps.py"
+
+
+@pytest.fixture(scope="module")
+def device_asm():
+    if not os.path.exists(HIPCC):
+        pytest.skip("hipcc not available")
+    with tempfile.TemporaryDirectory() as td:
+        out = os.path.join(td, "prefill.s")
+        cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature",
+               "-Xclang", "-packed-fp32-ops", "-I" + os.path.join(ROOT, "include"),
+               "--cuda-device-only", "-S", os.path.join(CSRC, "prefill.hip"), "-o", out]
+        subprocess.run(cmd, check=True, capture_output=True)
+        with open(out) as f:
+            return f.read()
+
+
+def _kernels(text):
+    """name -> (list of (in_asm, instruction) lines, descriptor dict)"""
+    out = {}
+    cur = None
+    in_asm = False
+    for line in text.split("\n"):
+        t = line.strip()
+        m = re.match(r"^(_Z\w*prefill_kernel\w*):", t)
+        if m:
+            cur = m.group(1)
+            out[cur] = ([], {})
+            continue
+        if cur is None:
+            continue
+        if t.startswith(".Lfunc_end"):
+            cur = None
+            continue
+        if t.startswith(";;#ASMSTART"):
+            in_asm = True
+            continue
+        if t.startswith(";;#ASMEND"):
+            in_asm = False
+            continue
+        if t and not t.startswith((";", ".")):
+            out[cur][0].append((in_asm, t.split(";")[0]))
+    for m in re.finditer(r"\.amdhsa_kernel (\w+)(.*?)\.end_amdhsa_kernel", text, re.S):
+        if m.group(1) in out:
+            for k, v in re.findall(r"\.amdhsa_(\w+) (\d+)", m.group(2)):
+                out[m.group(1)][1][k] = int(v)
+    return out
+
+
+def test_compiler_keeps_out_of_reserved_registers(device_asm):
+    kernels = _kernels(device_asm)
+    assert len(kernels) == 12
+    for name, (lines, _) in kernels.items():
+        bad = []
+        for in_asm, ins in lines:
+            if in_asm:
+                continue
+            for m in re.finditer(r"\b([va])(\d+)\b|\b([va])\[(\d+):(\d+)\]", ins):
+                hi = int(m.group(2) or m.group(5))
+                if hi >= RESERVED_FROM:
+                    bad.append(ins)
+        assert not bad, f"{name}: compiler code uses reserved registers: {bad[:5]}"
+        assert not any(ins.startswith("scratch_") for _, ins in lines), f"{name} spills"
+
+
+def test_kernels_get_the_register_file_they_name(device_asm):
+    for name, (_, desc) in _kernels(device_asm).items():
+        d128 = "ILi128E" in name
+        assert desc["accum_offset"] == 256, name
+        assert desc["next_free_vgpr"] == (512 if d128 else 416), name
+        assert desc["private_segment_fixed_size"] == 0, name
