@@ -18,8 +18,9 @@ vector ALUs work. Here each step overlaps two tiles:
   over the MFMA issue slots of both phases.
 
 An MFMA takes 32 cycles; vector instructions issued after it run meanwhile.
-Measured issue costs on gfx950 (cycles per wave64 instruction): add / fma /
-max3 4.2, exp 8.2, bf16 pack ~6, plus ~8 cycles per MFMA issue. The
+Measured on gfx950 for one wave per SIMD: every instruction costs about 4
+issue cycles (an s_nop too), v_exp about 8, an MFMA issue about 8; up to six
+plain VALU instructions hide completely behind one 32-cycle MFMA. The
 scheduler below fills each MFMA slot with about BUDGET cycles of vector work.
 
 The step variants:
@@ -38,15 +39,24 @@ Register plan (fixed, so the blocks can name registers directly):
   v[64:95]              K fragments (phase A) / V^T fragments (phase B)
   v[96:127]             P^T operand, key step kp, query half nb at
                         96 + 4 (2 kp + nb)
-  v[56:63]              exp temporaries
-Everything below v56 is left to the compiler.
+  v[48:63]              exp temporaries and LDS read addresses
+  v[40:46)              vote temporaries
+Everything below v40 (and a40) is left to the compiler.
+
+After the row maxima of the new tile, the full and qk steps also take the
+Skip-Softmax vote on it: the per-query maxima of the two lane halves are
+combined (v_permlane32_swap), compared with m - tau, and any valid row that
+does not clear the threshold keeps the tile. A kept tile raises the running
+maxima m (unless the caller flags the tile as needing a mask first), and the
+step reports whether some m now exceeds the reference max by more than the
+lazy-rescale margin.
 
 Hazards are resolved here, not by the compiler (which does not look inside
 asm): every read of a register is checked against its last writer and
 s_nop / s_waitcnt lgkmcnt are inserted as needed:
   MFMA (8 passes) write -> VALU read           12 wait states
   VALU write -> MFMA read                      4 (2 required)
-  transcendental write -> VALU read            2 (1 required)
+  transcendental write -> VALU read            1
   ds_read -> any use                           s_waitcnt lgkmcnt
   MFMA read of a fragment -> ds_read over it   2
 Back-to-back accumulation into the same MFMA destination needs none.
@@ -59,8 +69,9 @@ import sys
 
 NOP_MFMA_VALU = 12
 NOP_VALU_MFMA = 4
-NOP_TRANS_VALU = 2
+NOP_TRANS_VALU = 1
 NOP_MFMA_READ_LOAD = 2
+NOP_VALU_PERM = 2
 
 COST = {"v_exp_f32": 8.2, "v_cvt_pk_bf16_f32": 6.0}
 COST_DEFAULT = 4.2
@@ -71,8 +82,9 @@ PREG = 96     # P^T operand, v[96:127]
 TREG = 48     # exp temporaries, three pairs v[48:53]
 VADR = 54     # V^T read addresses, v[54 : 54 + 2 MB)
 KADR = 62     # K read addresses, v62 / v63 alternating
+VOTE = 40     # vote temporaries, v[40:46)
 OB = 64       # first AGPR of O^T
-COMPILER_VGPRS = 48  # v[0:48) and a[0:48) stay with the compiler
+COMPILER_VGPRS = 40  # v[0:40) and a[0:40) stay with the compiler
 
 
 def expand(r):
@@ -95,7 +107,8 @@ class Ins:
         self.rd = [x for r in rd for x in expand(r)]
         self.tag = tag
         op = text.split()[0]
-        self.cost = COST.get(op, COST_DEFAULT) if kind in ("valu", "trans") else 0.0
+        self.cost = COST.get(op, COST_DEFAULT) if kind in ("valu", "trans", "perm") else (
+            1.0 if kind == "salu" else 0.0)
 
 
 class Step:
@@ -121,8 +134,8 @@ class Step:
     def s_blk(self, buf, a, nb):
         return rng("v", self.s_reg(buf, a, nb), 16)
 
-    def kfrag(self, j, a):
-        return rng("v", KREG + 8 * j + 4 * a, 4)
+    def kfrag(self, j, a=0):
+        return rng("v", KREG + 4 * j, 4)
 
     def vfrag(self, j, mb):
         # V^T fragments of one key step: MB tuples of 4 registers; two buffers
@@ -137,19 +150,19 @@ class Step:
     def oblk(self, mb, nb):
         return rng("a", OB + 16 * (2 * mb + nb), 16)
 
-    def k_loads(self, ks):
-        # fragment address of k-step ks: the tile base XOR 32 ks (the swizzle
-        # only moves address bits 4..7, the tile base has bits 0..9 clear)
+    def k_load(self, a, ks, j):
+        """K fragment (k-step ks, key half a) into fragment buffer j. The
+        fragment address of k-step ks is the tile base XOR 32 ks (the swizzle
+        only moves address bits 4..7; the tile base has bits 0..9 clear)."""
         out = []
         if ks == 0:
             adr = "%[kb0]"
         else:
-            adr = f"v{KADR + (ks & 1)}"
+            adr = f"v{KADR + (j & 1)}"
             out.append(Ins(f"v_xor_b32 {adr}, {32 * ks}, %[kb0]", "valu", wr=[adr]))
-        for a in range(2):
-            dst = self.kfrag(ks & 1, a)
-            off = a * 32 * self.rowBytes
-            out.append(Ins(f"ds_read_b128 {dst}, {adr} offset:{off}", "lds", wr=[dst], rd=[adr]))
+        dst = self.kfrag(j, 0)
+        off = a * 32 * self.rowBytes
+        out.append(Ins(f"ds_read_b128 {dst}, {adr} offset:{off}", "lds", wr=[dst], rd=[adr]))
         return out
 
     def v_addr(self):
@@ -178,9 +191,9 @@ class Step:
                                wr=[dst], rd=[adr]))
         return out
 
-    def qk_mfma(self, ks, a, nb):
+    def qk_mfma(self, ks, a, nb, j):
         s = self.s_blk(self.y, a, nb)
-        kf = self.kfrag(ks & 1, a)
+        kf = self.kfrag(j, 0)
         qf = self.qfrag(ks, nb)
         src_c = "0" if ks == 0 else s
         rd = [kf, qf] + ([] if ks == 0 else [s])
@@ -206,7 +219,7 @@ class Step:
             t0 = f"v{TREG + 2 * (gp % 3)}"
             t1 = f"v{TREG + 2 * (gp % 3) + 1}"
             w = f"v{PREG + 4 * (2 * kp + nb) + i2}"
-            ls = f"%[ls{nb}]"
+            ls = f"%[lo{nb}]"
             nm = f"%[nm{nb}]"
             out += [
                 Ins(f"v_fma_f32 {t0}, {s0}, %[c], {nm}", "valu", wr=[t0], rd=[s0]),
@@ -231,72 +244,113 @@ class Step:
                     s0, s1 = f"v{r0}", f"v{r0 + 1}"
                     tm = f"%[tm{nb}]"
                     if first[nb]:
-                        out.append(Ins(f"v_max_f32 {tm}, {s0}, {s1}", "valu", rd=[s0, s1]))
+                        out.append(Ins(f"v_max_f32 {tm}, {s0}, {s1}", "valu", rd=[s0, s1], tag=("blk", a)))
                         first[nb] = False
                     else:
-                        out.append(Ins(f"v_max3_f32 {tm}, {tm}, {s0}, {s1}", "valu", rd=[s0, s1]))
+                        out.append(Ins(f"v_max3_f32 {tm}, {tm}, {s0}, {s1}", "valu", rd=[s0, s1],
+                                       tag=("blk", a)))
         return out
+
+    def vote_stream(self):
+        v = [f"v{VOTE + i}" for i in range(6)]
+        return [
+            Ins(f"v_mov_b32 {v[0]}, %[tm0]", "valu", wr=[v[0]]),
+            Ins(f"v_mov_b32 {v[1]}, %[tm0]", "valu", wr=[v[1]]),
+            Ins(f"v_mov_b32 {v[2]}, %[tm1]", "valu", wr=[v[2]]),
+            Ins(f"v_mov_b32 {v[3]}, %[tm1]", "valu", wr=[v[3]]),
+            Ins(f"v_subrev_f32 {v[4]}, %[tau], %[mi0]", "valu", wr=[v[4]]),
+            Ins(f"v_subrev_f32 {v[5]}, %[tau], %[mi1]", "valu", wr=[v[5]]),
+            Ins(f"v_permlane32_swap_b32 {v[0]}, {v[1]}", "perm", wr=[v[0], v[1]], rd=[v[0], v[1]]),
+            Ins(f"v_permlane32_swap_b32 {v[2]}, {v[3]}", "perm", wr=[v[2], v[3]], rd=[v[2], v[3]]),
+            Ins(f"v_max_f32 {v[0]}, {v[0]}, {v[1]}", "valu", wr=[v[0]], rd=[v[0], v[1]]),
+            Ins(f"v_max_f32 {v[2]}, {v[2]}, {v[3]}", "valu", wr=[v[2]], rd=[v[2], v[3]]),
+            Ins(f"v_cmp_nlt_f32 %[k0], {v[0]}, {v[4]}", "valu", rd=[v[0], v[4]]),
+            Ins(f"v_cmp_nlt_f32 %[k1], {v[2]}, {v[5]}", "valu", rd=[v[2], v[5]]),
+            Ins("s_and_b64 %[k0], %[k0], %[val0]", "salu"),
+            Ins("s_and_b64 %[k1], %[k1], %[val1]", "salu"),
+            Ins("s_or_b64 %[keep], %[k0], %[k1]", "salu"),
+            Ins("s_cmp_lg_u64 %[keep], 0", "salu"),
+            Ins("s_cselect_b64 %[keep], -1, 0", "salu"),
+            Ins("s_andn2_b64 %[k0], %[keep], %[rare]", "salu"),
+            Ins(f"v_max_f32 {v[1]}, %[mi0], {v[0]}", "valu", wr=[v[1]], rd=[v[0]]),
+            Ins(f"v_max_f32 {v[3]}, %[mi1], {v[2]}", "valu", wr=[v[3]], rd=[v[2]]),
+            Ins(f"v_cndmask_b32 %[mo0], %[mi0], {v[1]}, %[k0]", "valu", rd=[v[1]]),
+            Ins(f"v_cndmask_b32 %[mo1], %[mi1], {v[3]}, %[k0]", "valu", rd=[v[3]]),
+            Ins(f"v_add_f32 {v[4]}, %[lazy], %[mr0]", "valu", wr=[v[4]]),
+            Ins(f"v_add_f32 {v[5]}, %[lazy], %[mr1]", "valu", wr=[v[5]]),
+            Ins(f"v_cmp_gt_f32 %[k0], %[mo0], {v[4]}", "valu", rd=[v[4]]),
+            Ins(f"v_cmp_gt_f32 %[k1], %[mo1], {v[5]}", "valu", rd=[v[5]]),
+            Ins("s_or_b64 %[grow], %[k0], %[k1]", "salu"),
+        ]
 
     # ---- schedule ---------------------------------------------------------
     def build(self):
-        seq = []          # scheduled instructions (before hazard fixing)
+        """Phase A walks key half a = 0 then a = 1, k-steps inside, both
+        query halves per k-step: the S blocks of key half 0 are final at the
+        middle of phase A, so their row maxima start there; key half 1's
+        follow early in phase B, then the vote. Vector work is pulled into
+        the MFMA slots against a cycle budget; a PV key step first forces
+        the exponentials it consumes."""
+        seq = []
         exp_q = self.exp_stream() if self.pv else []
-        max_q = self.max_stream() if self.qk else []
+        max_q = (self.max_stream() + self.vote_stream()) if self.qk else []
         KS, MB = self.KS, self.MB
+        n_slots = (4 * KS if self.qk else 0) + (8 * MB if self.pv else 0)
+        total_valu = sum(i.cost for i in exp_q) + sum(i.cost for i in max_q)
+        budget = max(self.budget, total_valu / max(n_slots, 1))
+        pos = {"exp": 0, "max": 0}
+        done_half = set()   # key halves whose S blocks are final (plus margin)
 
-        # exp pairs needed before PV key step ks: pairs 0 .. 8 ks + 7, i.e.
-        # the pack of chunk kp <= ks; index of the last such pack in exp_q
+        def max_ready(ins):
+            return ins.tag is None or ins.tag[1] in done_half
+
+        def pull(limit, use_max=True):
+            used = 0.0
+            while True:
+                cand = None
+                if pos["exp"] < len(exp_q):
+                    cand = ("exp", exp_q[pos["exp"]])
+                elif use_max and pos["max"] < len(max_q) and max_ready(max_q[pos["max"]]):
+                    cand = ("max", max_q[pos["max"]])
+                if cand is None or used + cand[1].cost > limit + 1e-9:
+                    return used
+                seq.append(cand[1])
+                used += cand[1].cost
+                pos[cand[0]] += 1
+
         def exp_needed(ks):
             last = -1
             for i, ins in enumerate(exp_q):
-                if ins.tag == ("pf", ks) or (ins.tag and ins.tag[0] == "pf" and ins.tag[1] < ks):
+                if ins.tag and ins.tag[0] == "pf" and ins.tag[1] <= ks:
                     last = i
             return last + 1
 
-        exp_pos = 0
-        max_pos = 0
-        n_slots = (4 * KS if self.qk else 0) + (8 * MB if self.pv else 0)
-        total_valu = sum(i.cost for i in exp_q) + sum(i.cost for i in max_q)
-        per_slot = total_valu / max(n_slots, 1)
-        budget = max(self.budget, per_slot)
-
-        def pull_exp(limit_cycles):
-            nonlocal exp_pos
-            used = 0.0
-            while exp_pos < len(exp_q) and used + exp_q[exp_pos].cost <= limit_cycles + 1e-9:
-                seq.append(exp_q[exp_pos])
-                used += exp_q[exp_pos].cost
-                exp_pos += 1
-            return used
-
-        def pull_max(n):
-            nonlocal max_pos
-            used = 0.0
-            for _ in range(n):
-                if max_pos < len(max_q):
-                    seq.append(max_q[max_pos])
-                    used += max_q[max_pos].cost
-                    max_pos += 1
-            return used
-
         if self.pv:
+            seq += [Ins("v_mov_b32 %[lo0], %[li0]", "valu"), Ins("v_mov_b32 %[lo1], %[li1]", "valu")]
             seq += self.v_addr()
         # phase A --------------------------------------------------------
         if self.qk:
-            seq += self.k_loads(0)
-            # vector work that needs no fragment, while the first loads fly
+            order = [(a, ks) for a in range(2) for ks in range(KS)]
+            seq += self.k_load(0, 0, 0)
+            seq += self.k_load(0, 1, 1)
             if self.pv:
-                pull_exp(2 * budget)
-            for ks in range(KS):
-                for blk in range(4):
-                    a, nb = blk >> 1, blk & 1
-                    seq.append(self.qk_mfma(ks, a, nb))
-                    if blk == 0 and ks + 1 < KS:
-                        seq += self.k_loads(ks + 1)
-                    if blk == 0 and self.pv and ks == KS // 2:
+                pull(2 * budget, use_max=False)
+            for n, (a, ks) in enumerate(order):
+                j = n & 3
+                for nb in range(2):
+                    seq.append(self.qk_mfma(ks, a, nb, j))
+                    if nb == 0 and n + 2 < len(order):
+                        seq += self.k_load(*order[n + 2], (n + 2) & 3)
+                    if nb == 0 and self.pv and n == len(order) // 2 + 2:
                         seq += self.v_loads(0)
-                    if self.pv:
-                        pull_exp(budget)
+                    pull(budget)
+                # key half 0 final after its last k-step; its maxima wait two
+                # more k-steps (four MFMAs) to clear the MFMA result latency
+                if a == 0 and ks == KS - 1:
+                    pass
+                if n == KS + 1:
+                    done_half.add(0)
+            done_half.add(1)
         elif self.pv:
             seq += self.v_loads(0)
 
@@ -304,23 +358,22 @@ class Step:
         if self.pv:
             for ks in range(4):
                 need = exp_needed(ks)
-                while exp_pos < need:
-                    seq.append(exp_q[exp_pos])
-                    exp_pos += 1
+                while pos["exp"] < need:
+                    seq.append(exp_q[pos["exp"]])
+                    pos["exp"] += 1
                 for i in range(2 * MB):
                     mb, nb = i >> 1, i & 1
                     seq.append(self.pv_mfma(ks, mb, nb))
                     if i == 0 and ks + 1 < 4:
                         seq += self.v_loads(ks + 1)
-                    used = pull_max(1) if (self.qk and (ks > 0 or i > 1)) else 0.0
-                    pull_exp(budget - used)
+                    pull(budget)
         # leftovers
-        while exp_pos < len(exp_q):
-            seq.append(exp_q[exp_pos])
-            exp_pos += 1
-        while max_pos < len(max_q):
-            seq.append(max_q[max_pos])
-            max_pos += 1
+        while pos["exp"] < len(exp_q):
+            seq.append(exp_q[pos["exp"]])
+            pos["exp"] += 1
+        while pos["max"] < len(max_q):
+            seq.append(max_q[pos["max"]])
+            pos["max"] += 1
         self.seq = seq
         return self
 
@@ -367,8 +420,14 @@ class Step:
                     need = max(need, NOP_MFMA_VALU - slots_since(widx))
                 elif wkind in ("valu", "trans") and ins.kind == "mfma":
                     need = max(need, NOP_VALU_MFMA - slots_since(widx))
-                elif wkind == "trans" and ins.kind in ("valu", "trans"):
+                elif wkind == "trans" and ins.kind in ("valu", "trans", "perm"):
                     need = max(need, NOP_TRANS_VALU - slots_since(widx))
+                elif wkind in ("valu", "perm") and ins.kind == "perm":
+                    need = max(need, NOP_VALU_PERM - slots_since(widx))
+                elif wkind == "perm" and ins.kind in ("valu", "perm"):
+                    need = max(need, 1 - slots_since(widx))
+                if wkind == "mfma" and ins.kind == "perm":
+                    need = max(need, NOP_MFMA_VALU - slots_since(widx))
             while need > 0:
                 n = min(need, 8)
                 emit(f"s_nop {n - 1}", n)
@@ -412,17 +471,24 @@ class Step:
         name = f"step_{self.variant}_{self.x if self.pv else ''}{self.y if self.qk else ''}"
         args, outs, ins_ = [], [], []
         if self.qk:
-            args += ["float (&tm)[2]", "uint32_t kb0"]
-            outs += ['[tm0] "=&v"(tm[0])', '[tm1] "=&v"(tm[1])']
-            ins_ += ['[kb0] "v"(kb0)']
+            args += ["float (&tm)[2]", "uint32_t kb0", "float (&m)[2]", "const float (&mref)[2]",
+                     "float tau", "float lazy", "const uint64_t (&val)[2]", "uint64_t rare",
+                     "uint64_t& keep", "uint64_t& grow"]
+            outs += ['[tm0] "=&v"(tm[0])', '[tm1] "=&v"(tm[1])', '[mo0] "=&v"(mo[0])',
+                     '[mo1] "=&v"(mo[1])', '[keep] "=&s"(keep)', '[grow] "=&s"(grow)',
+                     '[k0] "=&s"(k0)', '[k1] "=&s"(k1)']
+            ins_ += ['[kb0] "v"(kb0)', '[mi0] "v"(m[0])', '[mi1] "v"(m[1])', '[mr0] "v"(mref[0])',
+                     '[mr1] "v"(mref[1])', '[tau] "s"(tau)', '[lazy] "v"(lazy)', '[val0] "s"(val[0])',
+                     '[val1] "s"(val[1])', '[rare] "s"(rare)']
         if self.pv:
             args += ["float (&lsum)[2]", "const float (&nmc)[2]", "float c", "uint32_t vb0",
                      "uint32_t vb1"]
-            outs += ['[ls0] "+v"(lsum[0])', '[ls1] "+v"(lsum[1])']
-            ins_ += ['[nm0] "v"(nmc[0])', '[nm1] "v"(nmc[1])', '[c] "s"(c)', '[vb0] "v"(vb0)',
+            outs += ['[lo0] "=&v"(lo[0])', '[lo1] "=&v"(lo[1])']
+            ins_ += ['[li0] "v"(lsum[0])', '[li1] "v"(lsum[1])', '[nm0] "v"(nmc[0])', '[nm1] "v"(nmc[1])', '[c] "s"(c)', '[vb0] "v"(vb0)',
                      '[vb1] "v"(vb1)']
         clob = [f"v{r}" for r in range(TREG, 128)]
         if self.qk:
+            clob += [f"v{VOTE + i}" for i in range(6)] + ["scc"]
             clob += [f"v{r}" for r in range(SBUF[self.y], SBUF[self.y] + 64)]
         if self.pv:
             clob += [f"a{r}" for r in range(OB, OB + 32 * MB)]
@@ -432,20 +498,32 @@ class Step:
                 "pv": f"exp and PV of the current tile from buffer {self.x}"}[self.variant]
         head = (f"// {self.variant} step, d = {self.d}: {what} "
                 f"({len(self.out)} instructions, ~{self.estimate():.0f} cycles)")
-        return asm_function(head, name, args, self.out, outs, ins_, clob)
+        # m and lsum are read and rewritten: they go in as inputs and come out
+        # through early-clobber outputs, so that no other input (say mref,
+        # which can hold the same value) shares their registers
+        pre, post = [], []
+        if self.qk:
+            pre += ["uint64_t k0, k1;", "float mo[2];"]
+            post += ["m[0] = mo[0];", "m[1] = mo[1];"]
+        if self.pv:
+            pre += ["float lo[2];"]
+            post += ["lsum[0] = lo[0];", "lsum[1] = lo[1];"]
+        return asm_function(head, name, args, self.out, outs, ins_, clob, pre, post)
 
 
-def asm_function(head, name, args, body, outs, ins_, clob):
+def asm_function(head, name, args, body, outs, ins_, clob, pre=(), post=()):
     text = "\n".join(f'      "{t}\\n\\t"' for t in body)
     clob_s = ", ".join(f'"{c}"' for c in clob + ["memory"])
     return "\n".join([
         head,
         f"__device__ __forceinline__ void {name}({', '.join(args)}) {{",
+        *[f"  {p}" for p in pre],
         "  asm volatile(",
         text,
         "      : " + ",\n        ".join(outs),
         "      : " + ",\n        ".join(ins_),
         "      : " + clob_s + ");",
+        *[f"  {p}" for p in post],
         "}"])
 
 
@@ -539,7 +617,7 @@ def main(out_path=None):
              "// Per-key-tile steps of the prefill kernel (see the script's docstring for",
              "// the schedule, the register plan and the hazard rules).",
              "#pragma once", ""]
-    for d, budget in ((128, 22.0), (64, 30.0)):
+    for d, budget in ((128, 20.0), (64, 30.0)):
         parts.append(f"namespace d{d} {{")
         for h in helpers_cxx(d):
             parts.append(h)

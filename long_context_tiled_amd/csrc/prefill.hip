@@ -42,7 +42,7 @@
 // instruction blocks written by gen_prefill_steps.py into prefill_steps.inc,
 // which also fixes the register plan: O^T and Q^T live in AGPRs, the scores
 // of two tiles in v[128:255], fragments and P^T in v[48:127]; the compiler
-// gets v[0:48) for everything else (amdgpu_num_vgpr below), so none of that
+// gets v[0:40) for everything else (amdgpu_num_vgpr below), so none of that
 // state is ever an SSA value it could move or spill.
 //
 // Units: scores stay raw (q.k) in registers. The test compares
@@ -142,7 +142,7 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, lds_void* lds, 
   } while (0)
 
 template <int D, bool CAUSAL, int HPW, int STAGES>
-__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(48))) void prefill_kernel(
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ o,
     float* __restrict__ lse, uint8_t* __restrict__ mask, int Hq, int Hkv,
@@ -257,9 +257,22 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(48))) void p
   const float lazy_raw = 8.0f / c;         // 8 in log2 units, as a raw-score gap
   float tm[2];                             // row maxima of the tile just scored
   bool keep = false;  // the current tile was kept: its exp and PV are pending
+  bool grow = false;  // some running max outgrew the reference by the lazy margin
+  uint64_t row_valid[2];                   // lanes whose query row (per half) is < N
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) row_valid[nb] = __ballot(qb * kTile + nb * 32 + l32 < N);
 
   auto stage_base = [&](int kb) __attribute__((always_inline)) -> uint32_t {
     return smem_lds + (uint32_t)((kb % STAGES) * STAGE_BYTES);
+  };
+
+  auto is_rare = [&](int kbn) __attribute__((always_inline)) -> bool {
+    return (CAUSAL && kbn == qb) || kbn * kTile + kTile > N;
+  };
+  // The same flag as an all-ones / zero 64-bit scalar (an SGPR operand).
+  auto rare_mask = [&](int kbn) __attribute__((always_inline)) -> uint64_t {
+    const uint32_t r = __builtin_amdgcn_readfirstlane(is_rare(kbn) ? ~0u : 0u);
+    return ((uint64_t)r << 32) | r;
   };
 
   // Skip-Softmax vote on tile kbn (scores in buffer A when YA, else B) from
@@ -268,7 +281,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(48))) void p
   // first (their row maxima recomputed).
   auto vote = [&](int kbn, auto ya_tag) __attribute__((always_inline)) -> bool {
     constexpr bool YA = decltype(ya_tag)::value;
-    if ((CAUSAL && kbn == qb) || kbn * kTile + kTile > N) {
+    if (is_rare(kbn)) {
       int lim[2];
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
@@ -294,15 +307,16 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(48))) void p
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) m[nb] = fmaxf(m[nb], t[nb]);
     }
+    bool g = false;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) g |= m[nb] > mref[nb] + lazy_raw;
+    grow = __ballot(g) != 0ull;
     return !skip;
   };
 
   // The rare rescale of O / lsum when a row's max outgrew the reference.
   auto maybe_rescale = [&]() __attribute__((always_inline)) {
-    bool grow = false;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) grow |= m[nb] > mref[nb] + lazy_raw;
-    if (__ballot(grow) != 0ull) {
+    if (grow) {
       drain_mfma();
       float alpha[2];
 #pragma unroll
@@ -312,7 +326,20 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(48))) void p
         mref[nb] = fmaxf(mref[nb], m[nb]);
       }
       SKA_CALL(D, rescale_o, alpha[0], alpha[1]);
+      grow = false;
     }
+  };
+
+  // After a generated step has voted on tile kbn: the causal-diagonal or
+  // ragged tile is masked and voted on again here (the step left m alone
+  // for it); otherwise the step's vote stands.
+  auto finish_vote = [&](int kbn, auto ya_tag, uint64_t keepb, uint64_t growb)
+      __attribute__((always_inline)) -> bool {
+    if (is_rare(kbn)) return vote(kbn, ya_tag);
+    const bool kept = keepb != 0ull;
+    grow = growb != 0ull;
+    if (mask != nullptr && lane == 0) mask[(bh * nqb + qb) * nqb + kbn] = kept ? 0 : 1;
+    return kept;
   };
 
   // One step with tile kb in score buffer X (= A when XA) and tile kb + 1
@@ -326,19 +353,27 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(48))) void p
     }
     if (kb + 1 < nkb_w) {
       const uint32_t kb0 = stage_base(kb + 1) + frag;
+      const uint64_t rare = rare_mask(kb + 1);
+      uint64_t keepb, growb;
       if (keep) {
         maybe_rescale();
         float nmc[2];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) nmc[nb] = -mref[nb] * c;
         const uint32_t vs = stage_base(kb) + (uint32_t)T::bytes;
-        if constexpr (XA) SKA_CALL(D, step_full_AB, tm, kb0, lsum, nmc, c, vs + tr0[0], vs + tr0[1]);
-        else SKA_CALL(D, step_full_BA, tm, kb0, lsum, nmc, c, vs + tr0[0], vs + tr0[1]);
+        if constexpr (XA)
+          SKA_CALL(D, step_full_AB, tm, kb0, m, mref, tau_raw, lazy_raw, row_valid, rare, keepb,
+                   growb, lsum, nmc, c, vs + tr0[0], vs + tr0[1]);
+        else
+          SKA_CALL(D, step_full_BA, tm, kb0, m, mref, tau_raw, lazy_raw, row_valid, rare, keepb,
+                   growb, lsum, nmc, c, vs + tr0[0], vs + tr0[1]);
       } else {
-        if constexpr (XA) SKA_CALL(D, step_qk_B, tm, kb0);
-        else SKA_CALL(D, step_qk_A, tm, kb0);
+        if constexpr (XA)
+          SKA_CALL(D, step_qk_B, tm, kb0, m, mref, tau_raw, lazy_raw, row_valid, rare, keepb, growb);
+        else
+          SKA_CALL(D, step_qk_A, tm, kb0, m, mref, tau_raw, lazy_raw, row_valid, rare, keepb, growb);
       }
-      keep = vote(kb + 1, std::integral_constant<bool, !XA>{});
+      keep = finish_vote(kb + 1, std::integral_constant<bool, !XA>{}, keepb, growb);
     } else if (kb + 1 == nkb_w) {
       // the wave's last tile
       if (keep) {
@@ -367,8 +402,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(48))) void p
   __syncthreads();
   if (0 < nkb_w) {
     SKA_CALL(D, load_q, smem_lds + q_lds + frag);
-    SKA_CALL(D, step_qk_A, tm, stage_base(0) + frag);
-    keep = vote(0, std::true_type{});
+    uint64_t keepb, growb;
+    SKA_CALL(D, step_qk_A, tm, stage_base(0) + frag, m, mref, tau_raw, lazy_raw, row_valid,
+             rare_mask(0), keepb, growb);
+    keep = finish_vote(0, std::true_type{}, keepb, growb);
   }
 
   // Key loop, two tiles per trip (tile kb in buffer A, kb + 1 in buffer B).

@@ -3,7 +3,7 @@
 The per-tile steps are hand-scheduled asm written by
 long_context_tiled_amd/csrc/gen_prefill_steps.py. They name fixed registers
 (O^T and Q^T in AGPRs, two score buffers, fragments and P^T in VGPRs), and the
-kernel limits the compiler to v[0:48) / a[0:48). These tests check that the
+kernel limits the compiler to the low VGPRs / AGPRs (COMPILER_VGPRS). These tests check that the
 committed blocks are the generator's output, that the compiled kernel keeps
 that contract (no compiler instruction touches a reserved register), and that
 every kernel is launched with the full register file it names."""
@@ -18,7 +18,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "long_context_tiled_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-RESERVED_FROM = 48
+sys.path.insert(0, CSRC)
+from gen_prefill_steps import COMPILER_VGPRS as RESERVED_FROM  # noqa: E402
 
 
 def test_steps_inc_is_generator_output():
