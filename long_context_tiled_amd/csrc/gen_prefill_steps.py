@@ -114,7 +114,8 @@ class Ins:
 class Step:
     """One step variant for one head dim and buffer assignment."""
 
-    def __init__(self, d, variant, x, y, budget):
+    def __init__(self, d, variant, x, y, budget, loop=False):
+        self.loop = loop
         self.d = d
         self.MB = d // 32
         self.KS = d // 16
@@ -326,7 +327,9 @@ class Step:
             return last + 1
 
         if self.pv:
-            seq += [Ins("v_mov_b32 %[lo0], %[li0]", "valu"), Ins("v_mov_b32 %[lo1], %[li1]", "valu")]
+            if not self.loop:
+                seq += [Ins("v_mov_b32 %[lo0], %[li0]", "valu"),
+                        Ins("v_mov_b32 %[lo1], %[li1]", "valu")]
             seq += self.v_addr()
         # phase A --------------------------------------------------------
         if self.qk:
@@ -610,6 +613,264 @@ def helpers_cxx(d):
     return parts
 
 
+# ---------------------------------------------------------------------------
+# The whole key loop of one wave as one asm block.
+#
+# Between the generated steps the loop also needs: the workgroup barrier and
+# the K/V tile copies (buffer_load ... lds), the choice of step variant from
+# the vote, the lazy rescale, the masked re-vote of the causal-diagonal or
+# ragged tile, and the skip-mask byte. Written in C++ that glue costs about
+# as much as a quarter of a step (branches and register copies, at ~4 cycles
+# per instruction for a lone wave), so it is emitted here as scalar control
+# flow around the step blocks. Every block below starts with no hazard
+# pending and leaves none behind (each ends with its LDS reads waited and
+# its MFMA results read after the required wait states).
+# ---------------------------------------------------------------------------
+
+def _rename(lines, mapping):
+    out = []
+    for t in lines:
+        for a, b in mapping.items():
+            t = t.replace(a, b)
+        out.append(t)
+    return out
+
+
+def _step_lines(d, variant, x, y, budget):
+    st = Step(d, variant, x, y, budget, loop=True).build().fix_hazards()
+    return _rename(st.out, {"%[mi0]": "%[m0]", "%[mi1]": "%[m1]", "%[mo0]": "%[m0]",
+                            "%[mo1]": "%[m1]", "%[lo0]": "%[ls0]", "%[lo1]": "%[ls1]"})
+
+
+def _vote_again_lines():
+    """The vote once more on masked maxima (tm recomputed), m always updated
+    when kept."""
+    body = []
+    for ins in Step(128, "qk", "A", "A", 0, loop=True).vote_stream():
+        body.append(ins.text.replace("s_andn2_b64 %[k0], %[keep], %[rare]", "s_mov_b64 %[k0], %[keep]"))
+    # vote temporaries: a VALU write feeds v_permlane32_swap after 4 instructions
+    return _rename(body, {"%[mi0]": "%[m0]", "%[mi1]": "%[m1]", "%[mo0]": "%[m0]",
+                          "%[mo1]": "%[m1]"})
+
+
+def _mask_lines(d, y):
+    body = [f"v_mov_b32 v{TREG}, 0xff800000"]
+    for a in range(2):
+        for nb in range(2):
+            for r in range(16):
+                key = 32 * a + 8 * (r >> 2) + (r & 3)
+                reg = SBUF[y] + 16 * (2 * a + nb) + r
+                body.append(f"v_cmp_gt_i32 vcc, {key}, %[lim{nb}]")
+                body.append(f"v_cndmask_b32 v{reg}, v{reg}, v{TREG}, vcc")
+    for nb in range(2):
+        regs = [SBUF[y] + 16 * (2 * a + nb) + r for a in range(2) for r in range(16)]
+        body.append(f"v_max_f32 %[tm{nb}], v{regs[0]}, v{regs[1]}")
+        for i in range(2, 32, 2):
+            body.append(f"v_max3_f32 %[tm{nb}], %[tm{nb}], v{regs[i]}, v{regs[i + 1]}")
+    return body
+
+
+def _rescale_lines(d):
+    """alpha = m > mref ? exp2((mref - m) c) : 1; lsum *= alpha; mref = max;
+    O half nb *= alpha_nb. Drains the MFMAs first."""
+    MB = d // 32
+    al = ["v52", "v53"]
+    body = ["s_nop 7", "s_nop 7", "s_nop 7"]
+    for nb in range(2):
+        body += [f"v_sub_f32 {al[nb]}, %[mr{nb}], %[m{nb}]",
+                 f"v_mul_f32 {al[nb]}, {al[nb]}, %[c]",
+                 f"v_exp_f32 {al[nb]}, {al[nb]}",
+                 f"v_cmp_gt_f32 vcc, %[m{nb}], %[mr{nb}]",
+                 f"v_cndmask_b32 {al[nb]}, 1.0, {al[nb]}, vcc",
+                 f"v_mul_f32 %[ls{nb}], %[ls{nb}], {al[nb]}",
+                 f"v_max_f32 %[mr{nb}], %[mr{nb}], %[m{nb}]"]
+    for nb in range(2):
+        for mb in range(MB):
+            lo = OB + 16 * (2 * mb + nb)
+            for r in range(lo, lo + 16, 4):
+                body += [f"v_accvgpr_read_b32 v{TREG + k}, a{r + k}" for k in range(4)]
+                body.append("s_nop 1")
+                body += [f"v_mul_f32 v{TREG + k}, v{TREG + k}, {al[nb]}" for k in range(4)]
+                body.append("s_nop 1")
+                body += [f"v_accvgpr_write_b32 a{r + k}, v{TREG + k}" for k in range(4)]
+    body += ["s_nop 4", "s_mov_b64 %[grow], 0"]
+    return body
+
+
+LOOP_ARGS = """// Operands of the key loop. Scalars are wave-uniform (SGPRs); krs / vrs are
+// raw buffer descriptors of the K and V head; mask_row is the skip-mask row
+// of this wave's query tile (0 when no mask is written).
+struct LoopArgs {{
+  uint32_t frag, tr0, tr1, gk[{ipw}], gv[{ipw}];
+  int lim_base[2];
+  float lazy;
+  int nkb_wg, nkb_w, qb, N;
+  float tau, c;
+  u32x4 krs, vrs;
+  uint32_t wl, smem;
+  uint64_t mask_row;
+  uint64_t val[2];
+}};
+"""
+
+
+def loop_cxx(d, causal, budget):
+    MB = d // 32
+    row_bytes = 2 * d
+    tile_bytes = 64 * row_bytes
+    stage_bytes = 2 * tile_bytes
+    ipw = 64 // (1024 // row_bytes) // 4
+    L = []
+
+    def lab(name):
+        return f".L{name}_%="
+
+    def kaddr():   # %[kb0] = K fragment base of tile kb + 1 (slot stg1)
+        return [f"s_mul_i32 %[t0], %[stg1], {stage_bytes}", "s_add_u32 %[t0], %[t0], %[smem]",
+                "v_add_u32 %[kb0], %[t0], %[frag]"]
+
+    def vaddr():   # %[vb0/1] = V^T read bases of tile kb (slot stg0)
+        return [f"s_mul_i32 %[t0], %[stg0], {stage_bytes}",
+                f"s_add_u32 %[t0], %[t0], %[smem]", f"s_add_u32 %[t0], %[t0], {tile_bytes}",
+                "v_add_u32 %[vb0], %[t0], %[tr0]", "v_add_u32 %[vb1], %[t0], %[tr1]"]
+
+    def nmc():
+        return ["v_mul_f32 %[nm0], %[mr0], %[c]", "v_mul_f32 %[nm1], %[mr1], %[c]",
+                "v_xor_b32 %[nm0], 0x80000000, %[nm0]", "v_xor_b32 %[nm1], 0x80000000, %[nm1]"]
+
+    def rare(kbn):  # %[rare] = all ones when tile kbn needs the mask
+        out = [f"s_lshl_b32 %[t0], {kbn}, 6", "s_add_u32 %[t0], %[t0], 64",
+               "s_cmp_gt_i32 %[t0], %[N]", "s_cselect_b64 %[rare], -1, 0"]
+        if causal:
+            out += [f"s_cmp_eq_u32 {kbn}, %[qb]", "s_cselect_b64 %[k0], -1, 0",
+                    "s_or_b64 %[rare], %[rare], %[k0]"]
+        return out
+
+    def after_vote(kbn, y, tag):  # masked re-vote if needed, then the mask byte
+        out = ["s_cmp_lg_u64 %[rare], 0", f"s_cbranch_scc0 {lab('nm' + tag)}",
+               f"s_lshl_b32 %[t0], {kbn}, 6",
+               "v_subrev_u32 %[lim0], %[t0], %[L0]", "v_subrev_u32 %[lim1], %[t0], %[L1]"]
+        out += _mask_lines(d, y) + _vote_again_lines()
+        # skip-mask byte of tile kbn (0 kept, 1 skipped), written by lane 0
+        out += [f"{lab('nm' + tag)}:",
+                "s_cmp_lg_u64 %[mptr], 0", f"s_cbranch_scc0 {lab('ns' + tag)}",
+                "s_cmp_lg_u64 %[keep], 0", "s_cselect_b32 %[t0], 0, 1",
+                "v_mov_b32 %[vt], %[t0]", f"v_mov_b32 %[vz], {kbn}",
+                "s_mov_b64 %[sx], exec", "s_mov_b64 exec, 1",
+                "global_store_byte %[vz], %[vt], %[mptr]",
+                "s_mov_b64 exec, %[sx]",
+                f"{lab('ns' + tag)}:"]
+        return out
+
+    def dma():     # copies of tile kb + 2 into slot stg2
+        # The tile offset goes into the VGPR offset: the raw-buffer range
+        # check (zero fill past N) covers voffset, not soffset.
+        out = ["s_add_u32 %[t1], %[kb], 2", f"s_mul_i32 %[t1], %[t1], {tile_bytes}",
+               f"s_mul_i32 %[t2], %[stg2], {stage_bytes}", "s_add_u32 %[t2], %[t2], %[wl]"]
+        n = 0
+        for which, rs, g in (("K", "%[krs]", "gk"), ("V", "%[vrs]", "gv")):
+            for i in range(ipw):
+                off = (tile_bytes if which == "V" else 0) + i * 1024
+                tmp = "%[vt]" if n % 2 == 0 else "%[vz]"
+                n += 1
+                out += [f"v_add_u32 {tmp}, %[t1], %[{g}{i}]", f"s_add_u32 m0, %[t2], {off}",
+                        "s_nop 0", f"buffer_load_dwordx4 {tmp}, {rs}, 0 offen lds"]
+        return out
+
+    # -- init ------------------------------------------------------------
+    L += ["v_mov_b32 %[m0], 0xff800000", "v_mov_b32 %[m1], 0xff800000",
+          "v_mov_b32 %[mr0], 0xff800000", "v_mov_b32 %[mr1], 0xff800000",
+          "v_mov_b32 %[ls0], 0", "v_mov_b32 %[ls1], 0",
+          "s_mov_b32 %[kb], 0", "s_mov_b32 %[stg0], 0", "s_mov_b32 %[stg1], 1",
+          "s_mov_b32 %[stg2], 2", "s_mov_b64 %[keep], 0", "s_mov_b64 %[grow], 0"]
+    # tile 0 scored into buffer A and voted on
+    L += ["s_cmp_gt_i32 %[nkbw], 0", f"s_cbranch_scc0 {lab('loop')}"]
+    L += ["s_mov_b32 %[t0], %[smem]", "v_add_u32 %[kb0], %[t0], %[frag]"]
+    L += rare("0")
+    L += _step_lines(d, "qk", "A", "A", budget)
+    L += after_vote("0", "A", "p0")
+    L += [f"{lab('loop')}:"]
+    for x, y in (("A", "B"), ("B", "A")):
+        t = x + y
+        L += ["s_add_u32 %[t1], %[kb], 1", "s_cmp_lt_i32 %[t1], %[nkbwg]",
+              f"s_cbranch_scc0 {lab('nb' + t)}",
+              "s_waitcnt vmcnt(0)", "s_barrier",
+              "s_add_u32 %[t1], %[kb], 2", "s_cmp_lt_i32 %[t1], %[nkbwg]",
+              f"s_cbranch_scc0 {lab('nb' + t)}"]
+        L += dma()
+        L += [f"{lab('nb' + t)}:",
+              "s_add_u32 %[t1], %[kb], 1", "s_cmp_lt_i32 %[t1], %[nkbw]",
+              f"s_cbranch_scc0 {lab('last' + t)}"]
+        L += kaddr() + rare("%[t1]")
+        L += ["s_cmp_lg_u64 %[keep], 0", f"s_cbranch_scc0 {lab('skip' + t)}",
+              "s_cmp_lg_u64 %[grow], 0", f"s_cbranch_scc0 {lab('nr' + t)}"]
+        L += _rescale_lines(d)
+        L += [f"{lab('nr' + t)}:"] + nmc() + vaddr()
+        L += _step_lines(d, "full", x, y, budget)
+        L += [f"s_branch {lab('voted' + t)}", f"{lab('skip' + t)}:"]
+        L += _step_lines(d, "qk", y, y, budget)
+        L += [f"{lab('voted' + t)}:", "s_add_u32 %[t1], %[kb], 1"]
+        L += after_vote("%[t1]", y, t)
+        L += [f"s_branch {lab('end' + t)}",
+              f"{lab('last' + t)}:", "s_cmp_eq_u32 %[t1], %[nkbw]", f"s_cbranch_scc0 {lab('end' + t)}",
+              "s_cmp_lg_u64 %[keep], 0", f"s_cbranch_scc0 {lab('ld' + t)}",
+              "s_cmp_lg_u64 %[grow], 0", f"s_cbranch_scc0 {lab('nrl' + t)}"]
+        L += _rescale_lines(d)
+        L += [f"{lab('nrl' + t)}:"] + nmc() + vaddr()
+        L += _step_lines(d, "pv", x, x, budget)
+        L += [f"{lab('ld' + t)}:", "s_mov_b64 %[keep], 0",
+              f"{lab('end' + t)}:",
+              # next tile; slots rotate
+              "s_add_u32 %[kb], %[kb], 1",
+              "s_mov_b32 %[t0], %[stg0]", "s_mov_b32 %[stg0], %[stg1]", "s_mov_b32 %[stg1], %[stg2]",
+              "s_mov_b32 %[stg2], %[t0]",
+              "s_cmp_lt_i32 %[kb], %[nkbwg]", f"s_cbranch_scc0 {lab('done')}"]
+    L += [f"s_branch {lab('loop')}", f"{lab('done')}:"]
+
+    outs = ['[m0] "=&v"(m[0])', '[m1] "=&v"(m[1])', '[mr0] "=&v"(mref[0])', '[mr1] "=&v"(mref[1])',
+            '[ls0] "=&v"(lsum[0])', '[ls1] "=&v"(lsum[1])',
+            '[tm0] "=&v"(vtmp[0])', '[tm1] "=&v"(vtmp[1])', '[kb0] "=&v"(vtmp[2])',
+            '[vb0] "=&v"(vtmp[3])', '[vb1] "=&v"(vtmp[4])', '[nm0] "=&v"(vtmp[5])',
+            '[nm1] "=&v"(vtmp[6])', '[lim0] "=&v"(vtmp[7])', '[lim1] "=&v"(vtmp[8])',
+            '[vt] "=&v"(vtmp[9])', '[vz] "=&v"(vtmp[10])',
+            '[kb] "=&s"(s32[0])', '[stg0] "=&s"(s32[1])', '[stg1] "=&s"(s32[2])',
+            '[stg2] "=&s"(s32[3])', '[t0] "=&s"(s32[4])', '[t1] "=&s"(s32[5])',
+            '[t2] "=&s"(s32[6])',
+            '[keep] "=&s"(s64[0])', '[grow] "=&s"(s64[1])', '[k0] "=&s"(s64[2])',
+            '[k1] "=&s"(s64[3])', '[rare] "=&s"(s64[4])', '[sx] "=&s"(s64[5])']
+    ins_ = ['[frag] "v"(a.frag)', '[tr0] "v"(a.tr0)', '[tr1] "v"(a.tr1)',
+            '[L0] "v"(a.lim_base[0])', '[L1] "v"(a.lim_base[1])', '[lazy] "v"(a.lazy)']
+    ins_ += [f'[gk{i}] "v"(a.gk[{i}])' for i in range(ipw)]
+    ins_ += [f'[gv{i}] "v"(a.gv[{i}])' for i in range(ipw)]
+    ins_ += ['[nkbwg] "s"(a.nkb_wg)', '[nkbw] "s"(a.nkb_w)', '[qb] "s"(a.qb)', '[N] "s"(a.N)',
+             '[tau] "s"(a.tau)', '[c] "s"(a.c)', '[krs] "s"(a.krs)', '[vrs] "s"(a.vrs)',
+             '[wl] "s"(a.wl)', '[smem] "s"(a.smem)', '[mptr] "s"(a.mask_row)',
+             '[val0] "s"(a.val[0])', '[val1] "s"(a.val[1])']
+    clob = [f"v{r}" for r in range(VOTE, VOTE + 6)] + [f"v{r}" for r in range(TREG, 256)]
+    clob += [f"a{r}" for r in range(OB, OB + 32 * MB)] + ["vcc", "scc", "m0"]
+    body = []
+    for t in L:
+        body.append(t)
+    # %[mpp] is the 64-bit pair (mp, mp_hi): spelled out below
+    text = "\n".join(f'      "{t}\\n\\t"' for t in body)
+    head = (f"// The key loop of one wave, d = {d}, {'causal' if causal else 'full'} attention "
+            f"({len(body)} lines)")
+    name = f"key_loop_{'causal' if causal else 'full'}"
+    return "\n".join([
+        head,
+        f"__device__ __forceinline__ void {name}(const LoopArgs& a, float (&m)[2], float (&mref)[2], "
+        "float (&lsum)[2]) {",
+        "  float vtmp[11];",
+        "  uint32_t s32[7];",
+        "  uint64_t s64[6];",
+        "  asm volatile(",
+        text,
+        "      : " + ",\n        ".join(outs),
+        "      : " + ",\n        ".join(ins_),
+        "      : " + ", ".join(f'"{c}"' for c in clob + ["memory"]) + ");",
+        "}"])
+
+
 def main(out_path=None):
     here = os.path.dirname(os.path.abspath(__file__))
     parts = ["// Generated by gen_prefill_steps.py; edit that script, not this file.",
@@ -621,6 +882,11 @@ def main(out_path=None):
         parts.append(f"namespace d{d} {{")
         for h in helpers_cxx(d):
             parts.append(h)
+            parts.append("")
+        ipw = 64 // (1024 // (2 * d)) // 4
+        parts.append(LOOP_ARGS.format(ipw=ipw))
+        for causal in (True, False):
+            parts.append(loop_cxx(d, causal, budget))
             parts.append("")
         for variant, pairs in (("full", (("A", "B"), ("B", "A"))), ("qk", (("A", "A"), ("B", "B"))),
                                ("pv", (("A", "A"), ("B", "B")))):

@@ -251,146 +251,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
     tr0[half] = (uint32_t)(row * T::rowBytes + 16 * ((d >> 3) ^ swz_v<D>(row)) + 2 * (d & 7));
   }
 
-  float m[2] = {-INFINITY, -INFINITY};     // running max over kept tiles (skip test)
-  float mref[2] = {-INFINITY, -INFINITY};  // reference max of what O / lsum hold
-  float lsum[2] = {0.f, 0.f};
-  const float lazy_raw = 8.0f / c;         // 8 in log2 units, as a raw-score gap
-  float tm[2];                             // row maxima of the tile just scored
-  bool keep = false;  // the current tile was kept: its exp and PV are pending
-  bool grow = false;  // some running max outgrew the reference by the lazy margin
-  uint64_t row_valid[2];                   // lanes whose query row (per half) is < N
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) row_valid[nb] = __ballot(qb * kTile + nb * 32 + l32 < N);
-
-  auto stage_base = [&](int kb) __attribute__((always_inline)) -> uint32_t {
-    return smem_lds + (uint32_t)((kb % STAGES) * STAGE_BYTES);
-  };
-
-  auto is_rare = [&](int kbn) __attribute__((always_inline)) -> bool {
-    return (CAUSAL && kbn == qb) || kbn * kTile + kTile > N;
-  };
-  // The same flag as an all-ones / zero 64-bit scalar (an SGPR operand).
-  auto rare_mask = [&](int kbn) __attribute__((always_inline)) -> uint64_t {
-    const uint32_t r = __builtin_amdgcn_readfirstlane(is_rare(kbn) ? ~0u : 0u);
-    return ((uint64_t)r << 32) | r;
-  };
-
-  // Skip-Softmax vote on tile kbn (scores in buffer A when YA, else B) from
-  // its row maxima: skip iff every valid row has t < m - tau; a kept tile
-  // raises m. The causal-diagonal tile and a ragged last tile are masked
-  // first (their row maxima recomputed).
-  auto vote = [&](int kbn, auto ya_tag) __attribute__((always_inline)) -> bool {
-    constexpr bool YA = decltype(ya_tag)::value;
-    if (is_rare(kbn)) {
-      int lim[2];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int qrow = qb * kTile + nb * 32 + l32;
-        const int last = CAUSAL ? min(N - 1, qrow) : N - 1;
-        lim[nb] = last - (kbn * kTile + 4 * hh);
-      }
-      if constexpr (YA) SKA_CALL(D, mask_A, lim, tm);
-      else SKA_CALL(D, mask_B, lim, tm);
-    }
-    float t[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) t[nb] = swap_halves_max(tm[nb]);
-    bool blocks = false;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int qrow = qb * kTile + nb * 32 + l32;
-      if (qrow < N && !(t[nb] < m[nb] - tau_raw)) blocks = true;
-    }
-    const bool skip = __ballot(blocks) == 0ull;
-    if (mask != nullptr && lane == 0) mask[(bh * nqb + qb) * nqb + kbn] = skip ? 1 : 0;
-    if (!skip) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) m[nb] = fmaxf(m[nb], t[nb]);
-    }
-    bool g = false;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) g |= m[nb] > mref[nb] + lazy_raw;
-    grow = __ballot(g) != 0ull;
-    return !skip;
-  };
-
-  // The rare rescale of O / lsum when a row's max outgrew the reference.
-  auto maybe_rescale = [&]() __attribute__((always_inline)) {
-    if (grow) {
-      drain_mfma();
-      float alpha[2];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        alpha[nb] = m[nb] > mref[nb] ? exp2_fast((mref[nb] - m[nb]) * c) : 1.0f;
-        lsum[nb] *= alpha[nb];
-        mref[nb] = fmaxf(mref[nb], m[nb]);
-      }
-      SKA_CALL(D, rescale_o, alpha[0], alpha[1]);
-      grow = false;
-    }
-  };
-
-  // After a generated step has voted on tile kbn: the causal-diagonal or
-  // ragged tile is masked and voted on again here (the step left m alone
-  // for it); otherwise the step's vote stands.
-  auto finish_vote = [&](int kbn, auto ya_tag, uint64_t keepb, uint64_t growb)
-      __attribute__((always_inline)) -> bool {
-    if (is_rare(kbn)) return vote(kbn, ya_tag);
-    const bool kept = keepb != 0ull;
-    grow = growb != 0ull;
-    if (mask != nullptr && lane == 0) mask[(bh * nqb + qb) * nqb + kbn] = kept ? 0 : 1;
-    return kept;
-  };
-
-  // One step with tile kb in score buffer X (= A when XA) and tile kb + 1
-  // scored into the other buffer.
-  auto step = [&](auto xa_tag, int kb) __attribute__((always_inline)) {
-    constexpr bool XA = decltype(xa_tag)::value;
-    if (kb + 1 < nkb_wg) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's copies of tile kb + 1 landed
-      __syncthreads();                     // every wave's; tile kb - 1 no longer read
-      if (kb + STAGES - 1 < nkb_wg) issue_tile(kb + STAGES - 1);
-    }
-    if (kb + 1 < nkb_w) {
-      const uint32_t kb0 = stage_base(kb + 1) + frag;
-      const uint64_t rare = rare_mask(kb + 1);
-      uint64_t keepb, growb;
-      if (keep) {
-        maybe_rescale();
-        float nmc[2];
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) nmc[nb] = -mref[nb] * c;
-        const uint32_t vs = stage_base(kb) + (uint32_t)T::bytes;
-        if constexpr (XA)
-          SKA_CALL(D, step_full_AB, tm, kb0, m, mref, tau_raw, lazy_raw, row_valid, rare, keepb,
-                   growb, lsum, nmc, c, vs + tr0[0], vs + tr0[1]);
-        else
-          SKA_CALL(D, step_full_BA, tm, kb0, m, mref, tau_raw, lazy_raw, row_valid, rare, keepb,
-                   growb, lsum, nmc, c, vs + tr0[0], vs + tr0[1]);
-      } else {
-        if constexpr (XA)
-          SKA_CALL(D, step_qk_B, tm, kb0, m, mref, tau_raw, lazy_raw, row_valid, rare, keepb, growb);
-        else
-          SKA_CALL(D, step_qk_A, tm, kb0, m, mref, tau_raw, lazy_raw, row_valid, rare, keepb, growb);
-      }
-      keep = finish_vote(kb + 1, std::integral_constant<bool, !XA>{}, keepb, growb);
-    } else if (kb + 1 == nkb_w) {
-      // the wave's last tile
-      if (keep) {
-        maybe_rescale();
-        float nmc[2];
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) nmc[nb] = -mref[nb] * c;
-        const uint32_t vs = stage_base(kb) + (uint32_t)T::bytes;
-        if constexpr (XA) SKA_CALL(D, step_pv_A, lsum, nmc, c, vs + tr0[0], vs + tr0[1]);
-        else SKA_CALL(D, step_pv_B, lsum, nmc, c, vs + tr0[0], vs + tr0[1]);
-      }
-      keep = false;
-    }
-  };
-
-  // Prologue: tiles 0 .. STAGES-2 in flight; Q^T into AGPRs; tile 0 scored
-  // into buffer A and voted on.
+  // Prologue: tiles 0 .. STAGES-2 in flight; Q^T into AGPRs.
   SKA_CALL(D, zero_o);
 #pragma unroll
   for (int st = 0; st < STAGES - 1; ++st)
@@ -400,19 +261,53 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
   else
     __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  if (0 < nkb_w) {
-    SKA_CALL(D, load_q, smem_lds + q_lds + frag);
-    uint64_t keepb, growb;
-    SKA_CALL(D, step_qk_A, tm, stage_base(0) + frag, m, mref, tau_raw, lazy_raw, row_valid,
-             rare_mask(0), keepb, growb);
-    keep = finish_vote(0, std::true_type{}, keepb, growb);
-  }
+  if (0 < nkb_w) SKA_CALL(D, load_q, smem_lds + q_lds + frag);
 
-  // Key loop, two tiles per trip (tile kb in buffer A, kb + 1 in buffer B).
-  for (int kb = 0; kb < nkb_wg; kb += 2) {
-    step(std::true_type{}, kb);
-    if (kb + 1 < nkb_wg) step(std::false_type{}, kb + 1);
+  // The key loop runs as one generated block (barriers, tile copies, the
+  // pipelined steps, votes, rescales, masks). Its scalar operands must be
+  // wave-uniform.
+  const float lazy_raw = 8.0f / c;  // 8 in log2 units, as a raw-score gap
+  typename std::conditional<D == 128, d128::LoopArgs, d64::LoopArgs>::type la;
+  la.frag = frag;
+  la.tr0 = tr0[0];
+  la.tr1 = tr0[1];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    la.gk[i] = (uint32_t)ld_gk[i];
+    la.gv[i] = (uint32_t)ld_gv[i];
   }
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int qrow = qb * kTile + nb * 32 + l32;
+    const int last = CAUSAL ? min(N - 1, qrow) : N - 1;  // last key this row may see
+    la.lim_base[nb] = last - 4 * hh;
+    la.val[nb] = __ballot(qrow < N);
+  }
+  la.lazy = lazy_raw;
+  la.nkb_wg = nkb_wg;
+  la.nkb_w = __builtin_amdgcn_readfirstlane(nkb_w);
+  la.qb = __builtin_amdgcn_readfirstlane(qb);
+  la.N = N;
+  la.tau = tau_raw;
+  la.c = c;
+  auto rsrc = [&](const uint16_t* p) {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    u32x4 r;
+    r[0] = (uint32_t)a;
+    r[1] = (uint32_t)(a >> 32) & 0xffffu;  // stride 0
+    r[2] = (uint32_t)head_bytes;
+    r[3] = kBufferCfg;
+    return r;
+  };
+  la.krs = rsrc(k + kv_off);
+  la.vrs = rsrc(v + kv_off);
+  la.wl = smem_lds + (uint32_t)(wave * IPW * 1024);
+  la.smem = smem_lds;
+  la.mask_row = mask != nullptr ? (uint64_t)(uintptr_t)(mask + (bh * nqb + qb) * nqb) : 0ull;
+  float m[2], mref[2], lsum[2];
+  if constexpr (CAUSAL) SKA_CALL(D, key_loop_causal, la, m, mref, lsum);
+  else SKA_CALL(D, key_loop_full, la, m, mref, lsum);
+  (void)m;
 
   if (!wave_valid) return;
   drain_mfma();
