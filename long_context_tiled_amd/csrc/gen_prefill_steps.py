@@ -114,8 +114,9 @@ class Ins:
 class Step:
     """One step variant for one head dim and buffer assignment."""
 
-    def __init__(self, d, variant, x, y, budget, loop=False):
+    def __init__(self, d, variant, x, y, budget, loop=False, dma=False):
         self.loop = loop
+        self.dma = dma
         self.d = d
         self.MB = d // 32
         self.KS = d // 16
@@ -191,6 +192,27 @@ class Step:
                 out.append(Ins(f"ds_read_b64_tr_b16 {dst}, {adr} offset:{off}", "lds",
                                wr=[dst], rd=[adr]))
         return out
+
+    def dma_groups(self):
+        """This wave's share of the copies of tile n + 2 (K then V), one group
+        per instruction: the tile offset into the VGPR offset (the raw-buffer
+        range check, which zero-fills keys past N, covers voffset only), the
+        LDS destination into M0. %[t1] is the tile's byte offset, %[t2] this
+        wave's LDS destination base."""
+        ipw = 64 // (1024 // self.rowBytes) // 4
+        tile_bytes = 64 * self.rowBytes
+        groups = []
+        n = 0
+        for which, rs, g in (("K", "%[krs]", "gk"), ("V", "%[vrs]", "gv")):
+            for i in range(ipw):
+                off = (tile_bytes if which == "V" else 0) + i * 1024
+                tmp = "%[vt]" if n % 2 == 0 else "%[vz]"
+                n += 1
+                groups.append([Ins(f"v_add_u32 {tmp}, %[t1], %[{g}{i}]", "valu"),
+                               Ins(f"s_add_u32 m0, %[t2], {off}", "salu"),
+                               Ins("s_nop 0", "salu"),
+                               Ins(f"buffer_load_dwordx4 {tmp}, {rs}, 0 offen lds", "vmem")])
+        return groups
 
     def qk_mfma(self, ks, a, nb, j):
         s = self.s_blk(self.y, a, nb)
@@ -301,6 +323,12 @@ class Step:
         budget = max(self.budget, total_valu / max(n_slots, 1))
         pos = {"exp": 0, "max": 0}
         done_half = set()   # key halves whose S blocks are final (plus margin)
+        dma_q = self.dma_groups() if self.dma else []
+
+        def mfma(ins):      # an MFMA, then the next tile-copy group if any
+            seq.append(ins)
+            if dma_q and len([x for x in seq if x.kind == "mfma"]) >= 2:
+                seq.extend(dma_q.pop(0))
 
         def max_ready(ins):
             return ins.tag is None or ins.tag[1] in done_half
@@ -341,7 +369,7 @@ class Step:
             for n, (a, ks) in enumerate(order):
                 j = n & 3
                 for nb in range(2):
-                    seq.append(self.qk_mfma(ks, a, nb, j))
+                    mfma(self.qk_mfma(ks, a, nb, j))
                     if nb == 0 and n + 2 < len(order):
                         seq += self.k_load(*order[n + 2], (n + 2) & 3)
                     if nb == 0 and self.pv and n == len(order) // 2 + 2:
@@ -366,11 +394,13 @@ class Step:
                     pos["exp"] += 1
                 for i in range(2 * MB):
                     mb, nb = i >> 1, i & 1
-                    seq.append(self.pv_mfma(ks, mb, nb))
+                    mfma(self.pv_mfma(ks, mb, nb))
                     if i == 0 and ks + 1 < 4:
                         seq += self.v_loads(ks + 1)
                     pull(budget)
         # leftovers
+        while dma_q:
+            seq.extend(dma_q.pop(0))
         while pos["exp"] < len(exp_q):
             seq.append(exp_q[pos["exp"]])
             pos["exp"] += 1
@@ -636,8 +666,8 @@ def _rename(lines, mapping):
     return out
 
 
-def _step_lines(d, variant, x, y, budget):
-    st = Step(d, variant, x, y, budget, loop=True).build().fix_hazards()
+def _step_lines(d, variant, x, y, budget, dma=True):
+    st = Step(d, variant, x, y, budget, loop=True, dma=dma).build().fix_hazards()
     return _rename(st.out, {"%[mi0]": "%[m0]", "%[mi1]": "%[m1]", "%[mo0]": "%[m0]",
                             "%[mo1]": "%[m1]", "%[lo0]": "%[ls0]", "%[lo1]": "%[ls1]"})
 
@@ -725,13 +755,20 @@ def loop_cxx(d, causal, budget):
     def lab(name):
         return f".L{name}_%="
 
-    def kaddr():   # %[kb0] = K fragment base of tile kb + 1 (slot stg1)
-        return [f"s_mul_i32 %[t0], %[stg1], {stage_bytes}", "s_add_u32 %[t0], %[t0], %[smem]",
+    # Tile t lives in slot t % 5 (five K/V slots; slots 3-4 stage the Q tiles
+    # before the loop).
+    def slot_base(dst, t_off):
+        return [f"s_add_u32 {dst}, %[kb], {t_off}" if t_off else f"s_mov_b32 {dst}, %[kb]",
+                f"s_mul_hi_u32 %[t3], {dst}, 0xcccccccd", "s_lshr_b32 %[t3], %[t3], 2",
+                "s_mul_i32 %[t3], %[t3], 5", f"s_sub_u32 {dst}, {dst}, %[t3]",
+                f"s_mul_i32 {dst}, {dst}, {stage_bytes}", f"s_add_u32 {dst}, {dst}, %[smem]"]
+
+    def kaddr():   # %[kb0] = K fragment base of tile kb + 1
+        return slot_base("%[t0]", 1) + [
                 "v_add_u32 %[kb0], %[t0], %[frag]"]
 
-    def vaddr():   # %[vb0/1] = V^T read bases of tile kb (slot stg0)
-        return [f"s_mul_i32 %[t0], %[stg0], {stage_bytes}",
-                f"s_add_u32 %[t0], %[t0], %[smem]", f"s_add_u32 %[t0], %[t0], {tile_bytes}",
+    def vaddr():   # %[vb0/1] = V^T read bases of tile kb
+        return slot_base("%[t0]", 0) + [f"s_add_u32 %[t0], %[t0], {tile_bytes}",
                 "v_add_u32 %[vb0], %[t0], %[tr0]", "v_add_u32 %[vb1], %[t0], %[tr1]"]
 
     def nmc():
@@ -739,8 +776,8 @@ def loop_cxx(d, causal, budget):
                 "v_xor_b32 %[nm0], 0x80000000, %[nm0]", "v_xor_b32 %[nm1], 0x80000000, %[nm1]"]
 
     def rare(kbn):  # %[rare] = all ones when tile kbn needs the mask
-        out = [f"s_lshl_b32 %[t0], {kbn}, 6", "s_add_u32 %[t0], %[t0], 64",
-               "s_cmp_gt_i32 %[t0], %[N]", "s_cselect_b64 %[rare], -1, 0"]
+        out = [f"s_lshl_b32 %[t3], {kbn}, 6", "s_add_u32 %[t3], %[t3], 64",
+               "s_cmp_gt_i32 %[t3], %[N]", "s_cselect_b64 %[rare], -1, 0"]
         if causal:
             out += [f"s_cmp_eq_u32 {kbn}, %[qb]", "s_cselect_b64 %[k0], -1, 0",
                     "s_or_b64 %[rare], %[rare], %[k0]"]
@@ -762,46 +799,45 @@ def loop_cxx(d, causal, budget):
                 f"{lab('ns' + tag)}:"]
         return out
 
-    def dma():     # copies of tile kb + 2 into slot stg2
-        # The tile offset goes into the VGPR offset: the raw-buffer range
-        # check (zero fill past N) covers voffset, not soffset.
-        out = ["s_add_u32 %[t1], %[kb], 2", f"s_mul_i32 %[t1], %[t1], {tile_bytes}",
-               f"s_mul_i32 %[t2], %[stg2], {stage_bytes}", "s_add_u32 %[t2], %[t2], %[wl]"]
-        n = 0
-        for which, rs, g in (("K", "%[krs]", "gk"), ("V", "%[vrs]", "gv")):
-            for i in range(ipw):
-                off = (tile_bytes if which == "V" else 0) + i * 1024
-                tmp = "%[vt]" if n % 2 == 0 else "%[vz]"
-                n += 1
-                out += [f"v_add_u32 {tmp}, %[t1], %[{g}{i}]", f"s_add_u32 m0, %[t2], {off}",
-                        "s_nop 0", f"buffer_load_dwordx4 {tmp}, {rs}, 0 offen lds"]
+    def dma_target():
+        # %[t1] = byte offset of tile kb + 3, %[t2] = this wave's LDS base for
+        # it. Its slot held tile kb - 2, which every wave finished before the
+        # barrier at the top of this trip; a tile past the end only wastes
+        # the copy (zero-filled past N).
+        return slot_base("%[t2]", 3) + [
+                "s_sub_u32 %[t2], %[t2], %[smem]", "s_add_u32 %[t2], %[t2], %[wl]",
+                "s_add_u32 %[t1], %[kb], 3", f"s_mul_i32 %[t1], %[t1], {tile_bytes}"]
+
+    def dma_alone():
+        out = []
+        for g in Step(d, "qk", "A", "A", 0, loop=True, dma=True).dma_groups():
+            out += [i.text for i in g]
         return out
 
     # -- init ------------------------------------------------------------
     L += ["v_mov_b32 %[m0], 0xff800000", "v_mov_b32 %[m1], 0xff800000",
           "v_mov_b32 %[mr0], 0xff800000", "v_mov_b32 %[mr1], 0xff800000",
           "v_mov_b32 %[ls0], 0", "v_mov_b32 %[ls1], 0",
-          "s_mov_b32 %[kb], 0", "s_mov_b32 %[stg0], 0", "s_mov_b32 %[stg1], 1",
-          "s_mov_b32 %[stg2], 2", "s_mov_b64 %[keep], 0", "s_mov_b64 %[grow], 0"]
+          "s_mov_b32 %[kb], 0", "s_mov_b64 %[keep], 0", "s_mov_b64 %[grow], 0"]
     # tile 0 scored into buffer A and voted on
     L += ["s_cmp_gt_i32 %[nkbw], 0", f"s_cbranch_scc0 {lab('loop')}"]
     L += ["s_mov_b32 %[t0], %[smem]", "v_add_u32 %[kb0], %[t0], %[frag]"]
     L += rare("0")
-    L += _step_lines(d, "qk", "A", "A", budget)
+    L += _step_lines(d, "qk", "A", "A", budget, dma=False)
     L += after_vote("0", "A", "p0")
     L += [f"{lab('loop')}:"]
     for x, y in (("A", "B"), ("B", "A")):
         t = x + y
-        L += ["s_add_u32 %[t1], %[kb], 1", "s_cmp_lt_i32 %[t1], %[nkbwg]",
-              f"s_cbranch_scc0 {lab('nb' + t)}",
-              "s_waitcnt vmcnt(0)", "s_barrier",
-              "s_add_u32 %[t1], %[kb], 2", "s_cmp_lt_i32 %[t1], %[nkbwg]",
-              f"s_cbranch_scc0 {lab('nb' + t)}"]
-        L += dma()
-        L += [f"{lab('nb' + t)}:",
-              "s_add_u32 %[t1], %[kb], 1", "s_cmp_lt_i32 %[t1], %[nkbw]",
+        # the copies of tile kb + 3 ride inside whichever step this wave runs
+        if x == "A":
+            # top of a trip (two tiles): every copy issued so far has landed
+            # (tiles kb + 1, kb + 2), and every wave is past the previous
+            # trip, so the slots of tiles kb - 2, kb - 1 are free
+            L += ["s_waitcnt vmcnt(0)", "s_barrier"]
+        L += dma_target() + [f"{lab('cp' + t)}:",
+              "s_add_u32 %[t0], %[kb], 1", "s_cmp_lt_i32 %[t0], %[nkbw]",
               f"s_cbranch_scc0 {lab('last' + t)}"]
-        L += kaddr() + rare("%[t1]")
+        L += kaddr() + ["s_add_u32 %[t0], %[kb], 1"] + rare("%[t0]")
         L += ["s_cmp_lg_u64 %[keep], 0", f"s_cbranch_scc0 {lab('skip' + t)}",
               "s_cmp_lg_u64 %[grow], 0", f"s_cbranch_scc0 {lab('nr' + t)}"]
         L += _rescale_lines(d)
@@ -812,20 +848,20 @@ def loop_cxx(d, causal, budget):
         L += [f"{lab('voted' + t)}:", "s_add_u32 %[t1], %[kb], 1"]
         L += after_vote("%[t1]", y, t)
         L += [f"s_branch {lab('end' + t)}",
-              f"{lab('last' + t)}:", "s_cmp_eq_u32 %[t1], %[nkbw]", f"s_cbranch_scc0 {lab('end' + t)}",
-              "s_cmp_lg_u64 %[keep], 0", f"s_cbranch_scc0 {lab('ld' + t)}",
+              f"{lab('last' + t)}:", "s_cmp_eq_u32 %[t0], %[nkbw]", f"s_cbranch_scc0 {lab('idle' + t)}",
+              "s_cmp_lg_u64 %[keep], 0", f"s_cbranch_scc0 {lab('idle' + t)}",
               "s_cmp_lg_u64 %[grow], 0", f"s_cbranch_scc0 {lab('nrl' + t)}"]
         L += _rescale_lines(d)
         L += [f"{lab('nrl' + t)}:"] + nmc() + vaddr()
         L += _step_lines(d, "pv", x, x, budget)
+        L += [f"s_branch {lab('ld' + t)}", f"{lab('idle' + t)}:"]
+        L += dma_alone()
         L += [f"{lab('ld' + t)}:", "s_mov_b64 %[keep], 0",
               f"{lab('end' + t)}:",
-              # next tile; slots rotate
               "s_add_u32 %[kb], %[kb], 1",
-              "s_mov_b32 %[t0], %[stg0]", "s_mov_b32 %[stg0], %[stg1]", "s_mov_b32 %[stg1], %[stg2]",
-              "s_mov_b32 %[stg2], %[t0]",
               "s_cmp_lt_i32 %[kb], %[nkbwg]", f"s_cbranch_scc0 {lab('done')}"]
-    L += [f"s_branch {lab('loop')}", f"{lab('done')}:"]
+    L += [f"s_branch {lab('loop')}", f"{lab('done')}:", "s_waitcnt vmcnt(0)"]
+
 
     outs = ['[m0] "=&v"(m[0])', '[m1] "=&v"(m[1])', '[mr0] "=&v"(mref[0])', '[mr1] "=&v"(mref[1])',
             '[ls0] "=&v"(lsum[0])', '[ls1] "=&v"(lsum[1])',
@@ -833,9 +869,8 @@ def loop_cxx(d, causal, budget):
             '[vb0] "=&v"(vtmp[3])', '[vb1] "=&v"(vtmp[4])', '[nm0] "=&v"(vtmp[5])',
             '[nm1] "=&v"(vtmp[6])', '[lim0] "=&v"(vtmp[7])', '[lim1] "=&v"(vtmp[8])',
             '[vt] "=&v"(vtmp[9])', '[vz] "=&v"(vtmp[10])',
-            '[kb] "=&s"(s32[0])', '[stg0] "=&s"(s32[1])', '[stg1] "=&s"(s32[2])',
-            '[stg2] "=&s"(s32[3])', '[t0] "=&s"(s32[4])', '[t1] "=&s"(s32[5])',
-            '[t2] "=&s"(s32[6])',
+            '[kb] "=&s"(s32[0])', '[t0] "=&s"(s32[4])', '[t1] "=&s"(s32[5])',
+            '[t2] "=&s"(s32[6])', '[t3] "=&s"(s32[7])',
             '[keep] "=&s"(s64[0])', '[grow] "=&s"(s64[1])', '[k0] "=&s"(s64[2])',
             '[k1] "=&s"(s64[3])', '[rare] "=&s"(s64[4])', '[sx] "=&s"(s64[5])']
     ins_ = ['[frag] "v"(a.frag)', '[tr0] "v"(a.tr0)', '[tr1] "v"(a.tr1)',
@@ -861,7 +896,7 @@ def loop_cxx(d, causal, budget):
         f"__device__ __forceinline__ void {name}(const LoopArgs& a, float (&m)[2], float (&mref)[2], "
         "float (&lsum)[2]) {",
         "  float vtmp[11];",
-        "  uint32_t s32[7];",
+        "  uint32_t s32[8];",
         "  uint64_t s64[6];",
         "  asm volatile(",
         text,
@@ -888,12 +923,6 @@ def main(out_path=None):
         for causal in (True, False):
             parts.append(loop_cxx(d, causal, budget))
             parts.append("")
-        for variant, pairs in (("full", (("A", "B"), ("B", "A"))), ("qk", (("A", "A"), ("B", "B"))),
-                               ("pv", (("A", "A"), ("B", "B")))):
-            for x, y in pairs:
-                st = Step(d, variant, x, y, budget).build().fix_hazards()
-                parts.append(st.cxx())
-                parts.append("")
         parts.append(f"}}  // namespace d{d}")
         parts.append("")
     with open(out_path or os.path.join(here, "prefill_steps.inc"), "w") as f:

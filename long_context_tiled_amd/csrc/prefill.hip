@@ -19,9 +19,11 @@
 //   K and V tiles (64 keys x d, bf16) go from HBM/L2 straight into LDS with
 //   buffer_load_dwordx4 ... lds (no VGPR staging). Keys past N read as zero
 //   through the buffer descriptor's range check. Rows are stored unpadded,
-//   with the 16-byte chunk c of row r at slot c ^ (r & (chunks - 1)) so that
-//   the fragment reads below hit distinct LDS banks. STAGES tiles are in
-//   flight; one workgroup barrier per key tile.
+//   with their 16-byte chunks permuted per row (swz_k / swz_v below) so that
+//   the fragment reads hit distinct LDS banks. There are five tile slots
+//   (tile t in slot t % 5); the Q tiles pass through slots 3-4 on their way
+//   to AGPRs. The loop takes one workgroup barrier per two key tiles and
+//   copies tiles three ahead.
 //
 // Per wave and key tile:
 //   S^T (64 keys x 64 queries) = K . Q^T with v_mfma_f32_32x32x16_bf16:
@@ -151,8 +153,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
   constexpr int MB = D / 32;     // 32-row d blocks of O^T
   using T = PrefillTile<D>;
   constexpr int STAGE_BYTES = 2 * T::bytes;
-  // K/V stages, then one 64-row Q tile per wave.
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES + 4 * T::bytes];
+  // STAGES K/V slots, tile t in slot t % STAGES. The four Q tiles are
+  // staged in slots 3-4 before the loop.
+  static_assert(STAGES == 5 && 4 * T::bytes == 2 * STAGE_BYTES, "slot plan");
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
   typedef __attribute__((address_space(3))) char lds_char;
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_char*)smem;  // LDS byte address
 
@@ -216,7 +220,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
 
   // The wave's 64 query rows go to its own swizzled LDS tile once (rows past
   // N read as zero), and from there into AGPRs.
-  const uint32_t q_lds = (uint32_t)(STAGES * STAGE_BYTES + wave * T::bytes);
+  const uint32_t q_lds = (uint32_t)(3 * STAGE_BYTES + wave * T::bytes);
   if (wave_valid) {
     constexpr int QI = T::bytes / 1024;  // 1 KB copy instructions per Q tile
 #pragma unroll
@@ -251,17 +255,14 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
     tr0[half] = (uint32_t)(row * T::rowBytes + 16 * ((d >> 3) ^ swz_v<D>(row)) + 2 * (d & 7));
   }
 
-  // Prologue: tiles 0 .. STAGES-2 in flight; Q^T into AGPRs.
+  // Prologue: Q tiles (slots 3-4) and K/V tiles 0-2 copied; Q^T into AGPRs.
   SKA_CALL(D, zero_o);
-#pragma unroll
-  for (int st = 0; st < STAGES - 1; ++st)
-    if (st < nkb_wg) issue_tile(st);
-  if (STAGES == 3 && 1 < nkb_wg)
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * IPW));  // all but tile 1's copies
-  else
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+  for (int t = 0; t < 3; ++t)
+    if (t < nkb_wg) issue_tile(t);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   if (0 < nkb_w) SKA_CALL(D, load_q, smem_lds + q_lds + frag);
+  __syncthreads();  // slots 3-4 are K/V slots from here on
 
   // The key loop runs as one generated block (barriers, tile copies, the
   // pipelined steps, votes, rescales, masks). Its scalar operands must be
@@ -351,7 +352,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
   }
 }
 
-constexpr int kStages = 3;
+constexpr int kStages = 5;
 
 template <int D, bool CAUSAL, int HPW>
 static int launch_one(const PrefillArgs& a) {
