@@ -12,7 +12,9 @@ TFLOP/s (4 d x unmasked query-key pairs per call) from HIP events recorded on
 the launch stream around each call inside the timed region; the decode's KV
 GB/s is reported beside it, then a tau sweep (skip fractions, dense and
 executed TFLOP/s, dense and actual GB/s) and the fp64 oracle's throughput on
-the host cores over a bounded sample of the same workloads.
+the host cores over a bounded sample of the same workloads. Timed calls
+write no skip mask (an optional output); the sweep reads each tau's mask
+from one extra call outside its timing.
 """
 from __future__ import annotations
 
@@ -38,12 +40,12 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # Keyed by the SHA-1 of the kernel's source files: once a kernel changes the
 # figure no longer applies and is reported as null.
 MEASURED_TRAFFIC = {
-    "prefill": {"sources": ("prefill.hip", "common.hpp"),
-                "sha1": "017610a1fcf1bc5a30ab0876ae09e3cd82bad489",
-                "bytes": (3169463.1 * 2.0 + 564678.2) * 1024},
+    "prefill": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp"),
+                "sha1": "bb8e13ccc508b0fbc4315f4bd92234855ff4a0fa",
+                "bytes": (2892849.2 * 2.0 + 528384.0) * 1024},
     "decode": {"sources": ("decode.hip", "common.hpp"),
                "sha1": "eb18a592b854d20636e2a86f58719610c49806d3",
-               "bytes": (4210048.9 * 2.0 + 94330.1) * 1024},
+               "bytes": (4212979.6 * 2.0 + 17031.2) * 1024},
 }
 
 
@@ -137,7 +139,7 @@ def _cpu_decode_head(job):
         oracle.decode_head(synth.bf16_bits_to_f64(q[hh]), k, v, math.inf)
 
 
-def cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=64, nkv=8):
+def cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=768, nkv=32):
     """The fp64 oracle as it stands, timed on a bounded sample of each
     workload with one process per host core (fp64 widening of the inputs is
     done before the clock starts)."""
@@ -246,11 +248,14 @@ def main():
     run_p = args.only in ("both", "prefill")
     run_d = args.only in ("both", "decode")
 
-    def prefill(tau):
-        lib.attn_prefill(tq, tk, tv, po, plse, True, tau, pmask)
+    # Timed calls pass no skip-mask buffer (the mask is an optional output
+    # for analysis); the tau sweep takes one extra masked call per tau to
+    # count skipped tiles, outside its timed calls.
+    def prefill(tau, mask=None):
+        lib.attn_prefill(tq, tk, tv, po, plse, True, tau, mask)
 
-    def decode(tau):
-        lib.attn_decode(uq, uk, uv, do, dlse, tau, ws, dmask)
+    def decode(tau, mask=None):
+        lib.attn_decode(uq, uk, uv, do, dlse, tau, ws, mask)
 
     for _ in range(args.warmup):
         if run_p:
@@ -319,6 +324,7 @@ def main():
                     prefill(tau)
             torch.cuda.synchronize()
             ms = float(np.median(t.ms()))
+            prefill(tau, pmask)
             m = pmask.cpu().numpy()
             ex, vis, kept = prefill_exec_flops(m, d)
             sweep.append(dict(leg="prefill_128k", tau=str(tau), ms=round(ms, 4),
@@ -332,6 +338,7 @@ def main():
                     decode(tau)
             torch.cuda.synchronize()
             ms = float(np.median(t.ms()))
+            decode(tau, dmask)
             m = dmask.cpu().numpy()
             dense_b, act_b = decode_bytes(DB, DHkv, L, Dd, m, DHq // DHkv)
             sweep.append(dict(leg="decode_128k", tau=str(tau), ms=round(ms, 4),
