@@ -42,10 +42,10 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 MEASURED_TRAFFIC = {
     "prefill": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp"),
                 "sha1": "bb8e13ccc508b0fbc4315f4bd92234855ff4a0fa",
-                "bytes": (2892849.2 * 2.0 + 528384.0) * 1024},
+                "bytes": (2745087.6 * 2.0 + 528384.0) * 1024},
     "decode": {"sources": ("decode.hip", "common.hpp"),
-               "sha1": "eb18a592b854d20636e2a86f58719610c49806d3",
-               "bytes": (4212979.6 * 2.0 + 17031.2) * 1024},
+               "sha1": "4547b90f42cc1cefbe9bf8d39618b34c46dc83fa",
+               "bytes": (4195496.6 * 2.0 + 16641.1) * 1024},
 }
 
 

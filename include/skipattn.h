@@ -44,7 +44,9 @@
  *                            Hq or Hkv < 1 or Hq % Hkv != 0; causal not 0/1;
  *                            tau NaN or < 0; a pointer not 16-byte aligned;
  *                            an element count beyond 2^40
- *   SKIPATTN_EUNSUPPORTED 2  d not in {64, 128}; decode with Hq/Hkv > 16
+ *   SKIPATTN_EUNSUPPORTED 2  d not in {64, 128}; decode with Hq/Hkv > 16;
+ *                            one head of K/V over 2^31 - 2^16 bytes
+ *                            (N * d * 2, L * d * 2)
  *   SKIPATTN_EWORKSPACE   3  decode workspace NULL or smaller than
  *                            attn_decode_workspace_bytes()
  *   SKIPATTN_EHIP         4  a kernel launch failed (hipGetLastError)

@@ -26,6 +26,11 @@ int fail(int code, const char* fmt, ...) {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 constexpr long long kMaxElems = 1LL << 40;
+// The kernels address one (b, head) slice of K, V (and Q) through a buffer
+// resource with a 32-bit byte range and 32-bit offsets, with up to one tile of
+// padding rows past its end and offsets at or above 2^31 reserved for loads
+// that must read nothing; a slice must stay below 2^31 - 2^16 bytes.
+constexpr long long kMaxHeadBytes = (1LL << 31) - (1LL << 16);
 
 int check_tau(float tau) {
   if (isnan(tau)) return fail(SKIPATTN_EINVAL, "tau is NaN");
@@ -66,6 +71,9 @@ int attn_prefill_check(const void* q, const void* k, const void* v, const float*
   if ((long long)B * Hq * N * (long long)(d > 0 ? d : 1) > kMaxElems)
     return fail(SKIPATTN_EINVAL, "tensor too large");
   if (d != 64 && d != 128) return fail(SKIPATTN_EUNSUPPORTED, "d must be 64 or 128 (got %d)", d);
+  if ((long long)N * d * 2 > kMaxHeadBytes)
+    return fail(SKIPATTN_EUNSUPPORTED, "N * d * 2 = %lld bytes per head exceeds %lld", (long long)N * d * 2,
+                kMaxHeadBytes);
   return SKIPATTN_OK;
 }
 
@@ -104,6 +112,9 @@ int attn_decode_check(const void* q, const void* k, const void* v, const float* 
     return fail(SKIPATTN_EINVAL, "tensor too large");
   if (d != 64 && d != 128) return fail(SKIPATTN_EUNSUPPORTED, "d must be 64 or 128 (got %d)", d);
   if (Hq / Hkv > 16) return fail(SKIPATTN_EUNSUPPORTED, "decode supports at most 16 query heads per KV head (got %d)", Hq / Hkv);
+  if ((long long)L * d * 2 > kMaxHeadBytes)
+    return fail(SKIPATTN_EUNSUPPORTED, "L * d * 2 = %lld bytes per head exceeds %lld", (long long)L * d * 2,
+                kMaxHeadBytes);
   if (B == 0 || L == 0) return SKIPATTN_OK;
   const size_t need = attn_decode_workspace_bytes(B, Hq, L, d);
   if (workspace == nullptr || workspace_bytes < need)

@@ -11,13 +11,20 @@
 // Split kernel: one wave per (sequence b, KV head g, split). The G query
 // heads of g ride in the N dimension of v_mfma_f32_16x16x32_bf16 (16 slots):
 //   S^T (16 keys x 16 heads) = K . q^T, K fragments loaded straight from HBM
-//   as 16-byte row segments (K is read exactly once), next tile prefetched.
+//   (K is read exactly once), next tile prefetched.
 //   Lane l owns head (l & 15) and 16 keys of the tile; the tile max per head
 //   is an in-lane max and two lane exchanges.
-//   The V tile is loaded only when at least one head keeps the tile: 16-byte
-//   coalesced row loads, transposed in registers into V^T in the wave's own
-//   LDS region, in the key order that P^T's registers hand to the PV MFMA.
-// The split writes its normalised partial output and LSE to the workspace.
+//   The V tile is read from memory only when at least one head keeps the
+//   tile; it is transposed in registers into V^T in the wave's own LDS
+//   region, in the key order that P^T's registers hand to the PV MFMA.
+//   Every K and V load instruction reads 8 rows x 128 contiguous bytes (whole
+//   128-byte lines) as a streaming (non-temporal) load: the cache keeps no
+//   line that is read once, and no line is split between two instructions.
+//   The fragment layouts above hold only 4 lanes per key row, so each pair of
+//   loads is dealt out to its lanes by one exchange between lanes l and l ^ 8
+//   (pair_fix).
+// The split writes its normalised partial output and LSE to the workspace,
+// and the skip bits of its tiles to the optional mask after its loop.
 //
 // Merge kernel: one wave per (b, query head): LSE = log sum_s e^lse_s and
 // O = sum_s e^(lse_s - LSE) O_s.
@@ -37,8 +44,34 @@ __device__ __forceinline__ int dec_vt_pos(int j) {
   return (j & ~31) | (((kap >> 2) & 3) << 3) | (((kap >> 4) & 1) << 2) | (kap & 3);
 }
 
-__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t rs, int off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+// 16-byte raw buffer load with the non-temporal cache policy (bit 1 of the
+// cache-policy operand): the KV cache is streamed once per call.
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 2));
+}
+// Tile base offset of a load that must read nothing: at or above 2^31, past
+// every head's byte range (the host keeps head slices below 2^31 - 2^16), so
+// the range check returns zeros without a memory access. Every iteration of
+// the tile loop issues the same loads, wanted or not: the wait counts that the
+// compiler derives then hold on every path and never drain loads still needed
+// in flight.
+constexpr uint32_t kNoLoad = 0x80000000u;
+
+// A pair of loads I0, I1 covers 16 rows x 8 chunks (I0 the first 8 rows, I1
+// the last 8). Lane (hl, grp) read chunk grp of its rows if hl < 8 ("lo"),
+// chunk grp + 4 if not. The fragments want row hl with chunk grp in r0 and
+// chunk grp + 4 in r1, so a lo lane keeps I0 as r0 and takes r1 from lane
+// hl + 8's I0, and a hi lane keeps I1 as r1 and takes r0 from lane hl - 8's
+// I1. The exchange is a rotate by 8 lanes within each 16-lane row (DPP
+// row_ror:8, control 0x128).
+__device__ __forceinline__ void pair_fix(u32x4& r0, u32x4& r1, bool lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t y0 = __builtin_amdgcn_mov_dpp((int)r0[e], 0x128, 0xf, 0xf, false);
+    const uint32_t y1 = __builtin_amdgcn_mov_dpp((int)r1[e], 0x128, 0xf, 0xf, false);
+    r0[e] = lo ? r0[e] : y1;
+    r1[e] = lo ? y0 : r1[e];
+  }
 }
 
 template <int D>
@@ -50,6 +83,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   constexpr int KS = D / 32;        // k-steps over d (32 each) for S^T
   constexpr int DB = D / 16;        // 16-row d blocks of O^T
   constexpr int VB = (2 * D) / 64;  // 4-key x 8-d V blocks per lane
+  static_assert(kSplit / kTile <= 64, "the per-lane skip bits hold one split");
   __shared__ __attribute__((aligned(16))) char smem[4][D * kDecodeVStride];
 
   const int lane = threadIdx.x & 63;
@@ -87,33 +121,52 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     qf[ks] = as_bf16x8(x);
   }
 
-  // K fragments: A[m = key][k = d], key 16 mb + hl, d = 32 ks + 8 grp; keys
-  // past L read as zero.
+  const bool lo = hl < 8;
+  const int h7 = hl & 7, hi4 = 4 * (hl >> 3);
+  // K fragments: A[m = key][k = d], key 16 mb + hl, d = 32 ks + 8 grp (chunk
+  // 4 ks + grp); keys past L read as zero. Loaded as pairs (2p, 2p + 1): load
+  // s of the pair reads rows 16 mb + 8 s + (hl & 7), chunk 8 p + grp + 4 (hl >> 3).
   u32x4 kreg[4][KS];
   auto kload = [&](int t) {
-    const int key0 = key_begin + t * kTile;
+    const uint32_t tb = t < ntile ? (uint32_t)(key_begin + t * kTile) * (D * 2) : kNoLoad;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        kreg[mb][ks] = bload16(krs, ((key0 + 16 * mb + hl) * D + ks * 32 + 8 * grp) * 2);
+        kreg[mb][ks] = bload16(
+            krs, tb + ((16 * mb + 8 * (ks & 1) + h7) * D + 8 * (8 * (ks >> 1) + grp + hi4)) * 2);
+  };
+  auto kfix = [&]() {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int p = 0; p < KS / 2; ++p) pair_fix(kreg[mb][2 * p], kreg[mb][2 * p + 1], lo);
   };
   // V blocks of 4 keys x 8 d: lane l takes key group (l & 15), d chunk
   // (l >> 4) + 4 j, so that the transposed LDS writes of one instruction
-  // cover whole V^T rows (no bank conflicts).
+  // cover whole V^T rows (no bank conflicts). Loaded as pairs (2q, 2q + 1):
+  // load j reads key group (hl & 7) + 8 (j & 1), chunk grp + 4 (hl >> 3) + 8 (j >> 1).
   u32x4 vreg[VB][4];
-  auto vload = [&](int t) {
-    const int key0 = key_begin + t * kTile;
+  auto vload = [&](int t, bool want) {
+    const uint32_t tb = want && t < ntile ? (uint32_t)(key_begin + t * kTile) * (D * 2) : kNoLoad;
 #pragma unroll
     for (int j = 0; j < VB; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        vreg[j][i] = bload16(vrs, ((key0 + 4 * hl + i) * D + 8 * (grp + 4 * j)) * 2);
+        vreg[j][i] = bload16(
+            vrs, tb + ((4 * (h7 + 8 * (j & 1)) + i) * D + 8 * (grp + hi4 + 8 * (j >> 1))) * 2);
+  };
+  auto vfix = [&]() {
+#pragma unroll
+    for (int q2 = 0; q2 < VB / 2; ++q2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pair_fix(vreg[2 * q2][i], vreg[2 * q2 + 1][i], lo);
   };
 
   // Scores of one tile, masked past L, and the per-head tile maximum.
   auto scores = [&](int t, f32x4 (&s)[4]) -> float {
     const int key0 = key_begin + t * kTile;
+    kfix();
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const f32x4 zero = {};
@@ -149,11 +202,13 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
 
   // The decision of tile t+1 is taken while tile t's V is still in flight:
   // scores run one tile ahead of the exp/PV work.
+  // Skipped tiles of this lane's head, bit t for tile t of the split (a split
+  // holds at most 64 tiles); written to the mask after the loop.
+  uint64_t skipped = 0;
   auto decide = [&](float tmax, int t, bool& keep) -> bool {
     keep = !(tmax < m_run - tau_raw);
     if (keep) m_run = fmaxf(m_run, tmax);
-    if (mask != nullptr && lane < G)
-      mask[bh * ntile_all + (key_begin / kTile + t)] = keep ? 0 : 1;
+    else skipped |= 1ull << t;
     return __ballot(keep && head_ok) != 0ull;
   };
 
@@ -162,8 +217,12 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   float t_cur = scores(0, s_cur);
   bool keep_cur;
   bool any_cur = decide(t_cur, 0, keep_cur);
-  if (ntile > 1) kload(1);
-  if (any_cur) vload(0);
+  // K of the next tile is always issued before V of the current one (here and
+  // in the loop), and the scheduler may not swap them: the loop's wait for K
+  // then leaves the 16 V loads behind it in flight.
+  kload(1);
+  __builtin_amdgcn_sched_barrier(0);
+  vload(0, any_cur);
 
   for (int t = 0; t < ntile; ++t) {
     f32x4 s_nx[4];
@@ -172,10 +231,12 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     if (t + 1 < ntile) {
       t_nx = scores(t + 1, s_nx);
       any_nx = decide(t_nx, t + 1, keep_nx);
-      if (t + 2 < ntile) kload(t + 2);
     }
+    kload(t + 2);
+    __builtin_amdgcn_sched_barrier(0);
     if (any_cur) {
       // ---- V tile t -> V^T in this wave's LDS region ----
+      vfix();
 #pragma unroll
       for (int j = 0; j < VB; ++j) {
         const int dc = grp + 4 * j;
@@ -186,7 +247,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
               column_of_4x8(vreg[j], e);
       }
     }
-    if (any_nx) vload(t + 1);
+    vload(t + 1, any_nx);
     if (any_cur) {
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
       __builtin_amdgcn_wave_barrier();
@@ -239,6 +300,11 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     t_cur = t_nx;
     keep_cur = keep_nx;
     any_cur = any_nx;
+  }
+
+  if (mask != nullptr && lane < G) {  // lane < G: grp 0, head hl = lane
+    uint8_t* mrow = mask + bh * ntile_all + key_begin / kTile;
+    for (int t = 0; t < ntile; ++t) mrow[t] = (uint8_t)((skipped >> t) & 1u);
   }
 
   // ---- split epilogue: normalised partial output and its LSE ----

@@ -27,6 +27,9 @@ def test_exports_every_declared_symbol():
         assert hasattr(so, n), n
 
 
+HEAD_LIMIT = (1 << 31) - (1 << 16)  # bytes of one (b, head) slice of K or V
+
+
 def _pcheck(**kw):
     a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=8, Hkv=2, N=1024, d=128, causal=1,
              tau=4.0, mask=None)
@@ -44,6 +47,9 @@ def _pcheck(**kw):
     ({"causal": 2}, 1), ({"tau": math.nan}, 1), ({"tau": -1.0}, 1), ({"tau": -INF}, 1),
     ({"q": P + 8}, 1), ({"o": P + 4}, 1), ({"B": 1 << 20, "N": 1 << 20}, 1),
     ({"d": 96}, 2), ({"d": 256}, 2), ({"d": 0}, 2),
+    # one head of K/V must stay below 2^31 - 2^16 bytes (32-bit buffer offsets)
+    ({"N": HEAD_LIMIT // 256}, 0), ({"N": HEAD_LIMIT // 256 + 1}, 2),
+    ({"N": HEAD_LIMIT // 128 + 1, "d": 64}, 2),
 ])
 def test_prefill_validation(kw, code):
     assert _pcheck(**kw) == code
@@ -76,6 +82,8 @@ def _dcheck(**kw):
     ({"q": None}, 1), ({"Hq": 65}, 1), ({"tau": math.nan}, 1), ({"tau": -0.5}, 1),
     ({"L": -1}, 1), ({"ws": P + 4}, 1),
     ({"Hq": 17, "Hkv": 1}, 2), ({"d": 80}, 2),
+    ({"L": HEAD_LIMIT // 256}, 0), ({"L": HEAD_LIMIT // 256 + 1}, 2),
+    ({"L": HEAD_LIMIT // 128 + 1, "d": 64}, 2),
     ({"ws": None}, 3), ({"wsb": 100}, 3),
 ])
 def test_decode_validation(kw, code):
