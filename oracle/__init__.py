@@ -6,6 +6,7 @@ path. It shares no code with the HIP kernels.
 """
 from .attention import (TILE, SPLIT, KEPT, SKIPPED, NOT_VISITED, prefill,
                         prefill_blocks, decode, decode_head)
+from . import kvq4
 
 __all__ = ["TILE", "SPLIT", "KEPT", "SKIPPED", "NOT_VISITED", "prefill",
-           "prefill_blocks", "decode", "decode_head"]
+           "prefill_blocks", "decode", "decode_head", "kvq4"]
