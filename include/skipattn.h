@@ -146,6 +146,59 @@ int attn_decode_check(const void* q, const void* k, const void* v,
                       const uint8_t* skip_mask, const void* workspace,
                       size_t workspace_bytes);
 
+/*
+ * 4-bit asymmetric KV cache (TurboAttention talk page, "Technical Deep Dive"
+ * and its pre-fill / decoding workflow: the cache is stored and moved as
+ * low-bit asymmetric integers with a floating zero point per block and is
+ * turned back into numbers inside the attention kernel). The 4-bit width is
+ * the one the talk calls near-lossless. Readings fixed by this library:
+ *   - a K block is one key's row of d values; a V block is one channel of one
+ *     64-key tile (the keys of that tile that exist);
+ *   - per block: z = minimum; s = (maximum - z) / 15 in fp32, rounded up to
+ *     the next bf16 value; code = clamp(rint((x - z) / s), 0, 15), subtract
+ *     and divide in fp32 rounded to nearest even (0 when s == 0); the value
+ *     the decode attends to is code * s + z, within s / 2 of x;
+ *   - a 32-bit word holds 8 consecutive elements (consecutive d for K,
+ *     consecutive keys for V): elements 0, 2, 4, 6 in nibbles 0..3 and
+ *     elements 1, 3, 5, 7 in nibbles 4..7; a parameter word holds the bf16
+ *     bits of s in its low half and of z in its high half.
+ * Arrays (T = ceil(L / 64)), all 16-byte aligned:
+ *   kq  uint8  [B, Hkv, L, d/2]       K codes, row by row
+ *   kp  uint32 [B, Hkv, L]            K parameter word per key
+ *   vq  uint8  [B, Hkv, T, d, 32]     V codes: per tile and channel, the 64
+ *                                     keys' codes (keys past L: code 0)
+ *   vp  uint32 [B, Hkv, T, d]         V parameter word per (tile, channel)
+ * Inputs must be finite with |x| < 2^127.
+ */
+
+/*
+ * attn_kv_quantize_q4 - K, V bf16 [B, Hkv, L, d] -> kq, kp, vq, vp (every
+ * byte of the outputs is written). Errors as for attn_decode.
+ */
+int attn_kv_quantize_q4(const void* k, const void* v, uint8_t* kq, uint32_t* kp,
+                        uint8_t* vq, uint32_t* vp, int B, int Hkv, int L,
+                        int d, void* stream);
+
+/*
+ * attn_decode_q4 - attn_decode over a 4-bit cache: the same rule, splits,
+ * outputs, mask and workspace (attn_decode_workspace_bytes), with the keys
+ * and values taken as code * s + z from kq/kp and vq/vp (layout above). The
+ * products run in fp16 with fp32 accumulation on the exact codes; q is
+ * rounded to fp16 after a per-head power-of-two scaling that keeps it in
+ * range, and the probabilities are rounded to fp16 for the value product.
+ */
+int attn_decode_q4(const void* q, const uint8_t* kq, const uint32_t* kp,
+                   const uint8_t* vq, const uint32_t* vp, float* o,
+                   float* lse, int B, int Hq, int Hkv, int L, int d,
+                   float tau, uint8_t* skip_mask, void* workspace,
+                   size_t workspace_bytes, void* stream);
+int attn_decode_q4_check(const void* q, const uint8_t* kq, const uint32_t* kp,
+                         const uint8_t* vq, const uint32_t* vp,
+                         const float* o, const float* lse, int B, int Hq,
+                         int Hkv, int L, int d, float tau,
+                         const uint8_t* skip_mask, const void* workspace,
+                         size_t workspace_bytes);
+
 /* Text for the last nonzero return on this thread ("" if none). */
 const char* attn_last_error(void);
 

@@ -4,9 +4,11 @@ this package is its thin Python binding."""
 from ._lib import (OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, TILE, SPLIT,
                    KEPT, SKIPPED, NOT_VISITED, EXPORTS, LIB_PATH, SkipAttnError,
                    load, attn_prefill, attn_decode, attn_decode_workspace_bytes,
-                   attn_last_error, prefill, decode)
+                   attn_last_error, prefill, decode, q4_shapes, attn_kv_quantize_q4,
+                   attn_decode_q4, quantize_q4, decode_q4)
 
 __all__ = ["OK", "EINVAL", "EUNSUPPORTED", "EWORKSPACE", "EHIP", "TILE", "SPLIT",
            "KEPT", "SKIPPED", "NOT_VISITED", "EXPORTS", "LIB_PATH", "SkipAttnError",
            "load", "attn_prefill", "attn_decode", "attn_decode_workspace_bytes",
-           "attn_last_error", "prefill", "decode"]
+           "attn_last_error", "prefill", "decode", "q4_shapes", "attn_kv_quantize_q4",
+           "attn_decode_q4", "quantize_q4", "decode_q4"]

@@ -21,7 +21,8 @@ SPLIT = 4096
 KEPT, SKIPPED, NOT_VISITED = 0, 1, 2
 
 EXPORTS = ("attn_prefill", "attn_decode", "attn_decode_workspace_bytes",
-           "attn_prefill_check", "attn_decode_check", "attn_last_error")
+           "attn_prefill_check", "attn_decode_check", "attn_last_error",
+           "attn_kv_quantize_q4", "attn_decode_q4", "attn_decode_q4_check")
 
 _lib = None
 
@@ -53,6 +54,14 @@ def load() -> ctypes.CDLL:
     lib.attn_decode_check.restype = i
     lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i]
     lib.attn_decode_workspace_bytes.restype = sz
+    lib.attn_kv_quantize_q4.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
+    lib.attn_kv_quantize_q4.restype = i
+    lib.attn_decode_q4.argtypes = [vp, vp, vp, vp, vp, f32p, f32p, i, i, i, i, i, f, u8p, vp,
+                                   sz, vp]
+    lib.attn_decode_q4.restype = i
+    lib.attn_decode_q4_check.argtypes = [vp, vp, vp, vp, vp, f32p, f32p, i, i, i, i, i, f,
+                                         u8p, vp, sz]
+    lib.attn_decode_q4_check.restype = i
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -141,7 +150,92 @@ def attn_decode(q, k, v, o, lse, tau: float, workspace, skip_mask=None,
     _raise(rc)
 
 
-# ---- allocation conveniences around the two entry points ----
+def q4_shapes(B: int, Hkv: int, L: int, d: int) -> dict:
+    """Shapes of the 4-bit cache arrays (kq, kp, vq, vp)."""
+    T = (L + TILE - 1) // TILE
+    return dict(kq=(B, Hkv, L, d // 2), kp=(B, Hkv, L), vq=(B, Hkv, T, d, 32),
+                vp=(B, Hkv, T, d))
+
+
+def _check_q4(cache, B, Hkv, L, d):
+    import torch
+    shp = q4_shapes(B, Hkv, L, d)
+    for name, dt in (("kq", torch.uint8), ("kp", torch.int32), ("vq", torch.uint8),
+                     ("vp", torch.int32)):
+        _check(cache[name], name, dt, shp[name])
+
+
+def attn_kv_quantize_q4(k, v, cache, stream=None) -> None:
+    """Enqueue the 4-bit quantiser: k/v [B,Hkv,L,d] bf16 -> cache dict of
+    kq uint8, kp int32 (parameter words), vq uint8, vp int32 tensors with the
+    shapes of q4_shapes()."""
+    import torch
+    B, Hkv, L, d = k.shape
+    _check(k, "k", torch.bfloat16, (B, Hkv, L, d))
+    _check(v, "v", torch.bfloat16, (B, Hkv, L, d))
+    _check_q4(cache, B, Hkv, L, d)
+    rc = load().attn_kv_quantize_q4(_ptr(k), _ptr(v), _ptr(cache["kq"]), _ptr(cache["kp"]),
+                                    _ptr(cache["vq"]), _ptr(cache["vp"]), B, Hkv, L, d,
+                                    _stream(stream))
+    _raise(rc)
+
+
+def attn_decode_q4(q, cache, L: int, o, lse, tau: float, workspace, skip_mask=None,
+                   stream=None) -> None:
+    """Enqueue split-K decode over a 4-bit cache (dict as for
+    attn_kv_quantize_q4, holding L keys); other arguments as attn_decode."""
+    import torch
+    B, Hq, d = q.shape
+    Hkv = cache["kp"].shape[1]
+    _check(q, "q", torch.bfloat16, (B, Hq, d))
+    _check_q4(cache, B, Hkv, L, d)
+    _check(o, "o", torch.float32, (B, Hq, d))
+    _check(lse, "lse", torch.float32, (B, Hq))
+    if skip_mask is not None:
+        _check(skip_mask, "skip_mask", torch.uint8, (B, Hq, (L + TILE - 1) // TILE))
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = load().attn_decode_q4(_ptr(q), _ptr(cache["kq"]), _ptr(cache["kp"]),
+                               _ptr(cache["vq"]), _ptr(cache["vp"]), _ptr(o), _ptr(lse), B,
+                               Hq, Hkv, L, d, float(tau), _ptr(skip_mask), _ptr(workspace),
+                               nbytes, _stream(stream))
+    _raise(rc)
+
+
+# ---- allocation conveniences around the entry points ----
+
+def quantize_q4(k, v, stream=None) -> dict:
+    """Allocate a 4-bit cache with torch and fill it from bf16 k, v."""
+    import torch
+    B, Hkv, L, d = k.shape
+    shp = q4_shapes(B, Hkv, L, d)
+    cache = {n: torch.empty(shp[n], dtype=torch.uint8 if n in ("kq", "vq") else torch.int32,
+                            device=k.device) for n in shp}
+    attn_kv_quantize_q4(k, v, cache, stream)
+    return cache
+
+
+def decode_q4(q, cache, L: int, tau: float = math.inf, want_mask: bool = False,
+              workspace=None, stream=None):
+    """Allocate outputs (and the workspace if not given) and call
+    attn_decode_q4. Returns (o, lse, mask)."""
+    import torch
+    B, Hq, d = q.shape
+    o = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    mask = None
+    if want_mask:
+        mask = torch.empty((B, Hq, (L + TILE - 1) // TILE), dtype=torch.uint8,
+                           device=q.device)
+    if workspace is None:
+        nbytes = max(16, attn_decode_workspace_bytes(B, Hq, L, d))
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    attn_decode_q4(q, cache, L, o, lse, tau, workspace, mask, stream)
+    return o, lse, mask
+
+
+# ---- allocation conveniences around the two bf16 entry points ----
 
 def prefill(q, k, v, causal: bool, tau: float = math.inf, want_mask: bool = False,
             stream=None):

@@ -142,4 +142,61 @@ int attn_decode(const void* q, const void* k, const void* v, float* o, float* ls
   return SKIPATTN_OK;
 }
 
+int attn_decode_q4_check(const void* q, const uint8_t* kq, const uint32_t* kp,
+                         const uint8_t* vq, const uint32_t* vp, const float* o,
+                         const float* lse, int B, int Hq, int Hkv, int L, int d, float tau,
+                         const uint8_t* skip_mask, const void* workspace,
+                         size_t workspace_bytes) {
+  g_err[0] = '\0';
+  if (!kq || !kp || !vq || !vp) return fail(SKIPATTN_EINVAL, "NULL cache pointer");
+  if (!aligned16(kq) || !aligned16(kp) || !aligned16(vq) || !aligned16(vp))
+    return fail(SKIPATTN_EINVAL, "kq, kp, vq and vp must be 16-byte aligned");
+  // The bf16 checks cover every other argument; kq stands in for k and v.
+  return attn_decode_check(q, kq, kq, o, lse, B, Hq, Hkv, L, d, tau, skip_mask, workspace,
+                           workspace_bytes);
+}
+
+int attn_decode_q4(const void* q, const uint8_t* kq, const uint32_t* kp, const uint8_t* vq,
+                   const uint32_t* vp, float* o, float* lse, int B, int Hq, int Hkv, int L, int d,
+                   float tau, uint8_t* skip_mask, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  if (int e = attn_decode_q4_check(q, kq, kp, vq, vp, o, lse, B, Hq, Hkv, L, d, tau, skip_mask,
+                                   workspace, workspace_bytes))
+    return e;
+  if (B == 0 || L == 0) return SKIPATTN_OK;
+  const int nsplit = (L + SKIPATTN_SPLIT - 1) / SKIPATTN_SPLIT;
+  float* ws_o = (float*)workspace;
+  float* ws_lse = ws_o + (size_t)B * Hq * nsplit * d;
+  skipattn::DecodeQ4Args a{q,         kq,   kp,     vq, vp,     o,  lse,      skip_mask,
+                           ws_o,      ws_lse, B,   Hq, Hkv, L, d, nsplit,
+                           tau_raw(tau, d), exp2_scale(d), stream};
+  if (skipattn::launch_decode_q4(a) != 0) return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(SKIPATTN_EHIP, "decode_q4 launch: %s", hipGetErrorString(err));
+  return SKIPATTN_OK;
+}
+
+int attn_kv_quantize_q4(const void* k, const void* v, uint8_t* kq, uint32_t* kp, uint8_t* vq,
+                        uint32_t* vp, int B, int Hkv, int L, int d, void* stream) {
+  g_err[0] = '\0';
+  if (!k || !v || !kq || !kp || !vq || !vp) return fail(SKIPATTN_EINVAL, "NULL tensor pointer");
+  if (B < 0 || L < 0 || d < 0) return fail(SKIPATTN_EINVAL, "negative size (B=%d L=%d d=%d)", B, L, d);
+  if (Hkv < 1) return fail(SKIPATTN_EINVAL, "Hkv must be >= 1 (got %d)", Hkv);
+  if (!aligned16(k) || !aligned16(v) || !aligned16(kq) || !aligned16(kp) || !aligned16(vq) ||
+      !aligned16(vp))
+    return fail(SKIPATTN_EINVAL, "every pointer must be 16-byte aligned");
+  if ((long long)B * Hkv * L * (long long)(d > 0 ? d : 1) > kMaxElems)
+    return fail(SKIPATTN_EINVAL, "tensor too large");
+  if (d != 64 && d != 128) return fail(SKIPATTN_EUNSUPPORTED, "d must be 64 or 128 (got %d)", d);
+  if ((long long)L * d * 2 > kMaxHeadBytes)
+    return fail(SKIPATTN_EUNSUPPORTED, "L * d * 2 = %lld bytes per head exceeds %lld", (long long)L * d * 2,
+                kMaxHeadBytes);
+  if (B == 0 || L == 0) return SKIPATTN_OK;
+  skipattn::QuantArgs a{k, v, kq, kp, vq, vp, B, Hkv, L, d, stream};
+  if (skipattn::launch_kv_quantize_q4(a) != 0) return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(SKIPATTN_EHIP, "quantize launch: %s", hipGetErrorString(err));
+  return SKIPATTN_OK;
+}
+
 }  // extern "C"

@@ -372,4 +372,16 @@ int launch_decode(const DecodeArgs& a) {
   return a.d == 128 ? launch_d<128>(a) : launch_d<64>(a);
 }
 
+int launch_decode_merge(const float* ws_o, const float* ws_lse, float* o, float* lse, int nbh,
+                        int d, int nsplit, void* stream) {
+  const unsigned g = (unsigned)((nbh + 3) / 4);
+  if (d == 128)
+    hipLaunchKernelGGL((decode_merge_kernel<128>), dim3(g), dim3(256), 0, (hipStream_t)stream,
+                       ws_o, ws_lse, o, lse, nbh, nsplit);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<64>), dim3(g), dim3(256), 0, (hipStream_t)stream,
+                       ws_o, ws_lse, o, lse, nbh, nsplit);
+  return 0;
+}
+
 }  // namespace skipattn

@@ -1,0 +1,487 @@
+// 4-bit asymmetric KV cache: the quantiser (bf16 K, V -> stored format) and
+// the split-K decode that reads the stored format directly.
+//
+// Method: the TurboAttention talk page ("Technical Deep Dive" and the
+// pre-fill / decoding workflow) stores and moves the KV cache as low-bit
+// asymmetric integers with a floating zero point per block, and turns them
+// back into numbers inside the attention kernel, next to the products. The
+// 4-bit width is the one the talk calls near-lossless. Decoding runs the
+// Skip-Softmax rule (TensorRT-LLM Skip Softmax summary page, "Key Points",
+// "Detailed Analysis") per query head over 64-key tiles, each 4096-key split
+// with its own running maximum, exactly as the bf16 decode does.
+//
+// Format (readings where the pages are silent):
+//   K block = one key row of d values; V block = one channel of one 64-key
+//   tile. Each block runs along the contraction index of the product that
+//   consumes it (d for q.K, keys for P.V), so its scale s and zero z factor
+//   out of the matrix product: q.k^ = s (q.c) + z sum(q), and
+//   sum_j p_j v^_jc = s_c (sum_j p_j c_jc) + z_c sum_j p_j.
+//   z = block minimum; s = (max - z) / 15 in fp32, rounded up to bf16;
+//   code = clamp(rint((x - z) / s), 0, 15) in fp32 (0 if s == 0).
+//   A 32-bit word holds 8 consecutive elements, even ones in nibbles 0-3, odd
+//   ones in nibbles 4-7. Parameter word: bf16 s (low half), bf16 z (high).
+//   kq [B,Hkv,L,d/2] u8, kp [B,Hkv,L] u32, vq [B,Hkv,T,d,32] u8 (64 keys of a
+//   channel per tile, keys past L code 0), vp [B,Hkv,T,d] u32, T = ceil(L/64).
+//
+// Decode split kernel: one wave per (sequence, KV head, split), no LDS. The
+// products run on v_mfma_f32_16x16x32_f16 with the codes expanded to exact
+// fp16 integers (0..15), q in fp16 (scaled by a power of two when a head's
+// largest element would not fit) and P in fp16; the affine parts of the
+// dequantisation are applied to the fp32 results.
+//   Key order inside a tile: S^T row 4 grp + r of block mb holds key
+//   16 grp + 4 mb + r, so lane (head, grp) owns keys 16 grp .. 16 grp + 15 and
+//   its P^T fragment for PV k-step ks is keys 16 grp + 8 ks .. + 7, which is
+//   word 2 grp + ks of every V code row. The K fragment row m of block mb is
+//   then key 16 (m >> 2) + 4 mb + (m & 3), and lane group grp reads d range
+//   [grp d/4, (grp + 1) d/4) of it, k-step ks taking word ks of that range.
+//   Every load instruction reads whole 128-byte lines of codes (K: 4 runs of
+//   4 rows; V: 16 rows of 32 bytes) with the non-temporal policy; the small
+//   parameter words use the default policy.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace skipattn {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+namespace {
+
+constexpr uint32_t kCfg = 0x00020000u;     // raw 32-bit buffer, range-checked
+constexpr uint32_t kNoRead = 0x80000000u;  // tile offset of a load that reads nothing
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __builtin_bit_cast(float, bits16 << 16);
+}
+
+// Non-negative finite fp32 rounded up to the bf16 grid.
+__device__ __forceinline__ float bf16_round_up(float x) {
+  uint32_t b = __builtin_bit_cast(uint32_t, x);
+  if (b & 0xffffu) b = (b + 0x10000u) & 0xffff0000u;
+  return __builtin_bit_cast(float, b);
+}
+
+// Block parameters and codes. The fp32 subtract and divide are rounded to
+// nearest even and are not fused with anything: they decide integers.
+__device__ __forceinline__ float block_scale(float lo, float hi) {
+  return bf16_round_up(__fdiv_rn(__fsub_rn(hi, lo), 15.0f));
+}
+__device__ __forceinline__ uint32_t code_of(float x, float s, float z) {
+  if (!(s > 0.f)) return 0u;
+  const float r = rintf(__fdiv_rn(__fsub_rn(x, z), s));
+  return (uint32_t)fminf(fmaxf(r, 0.f), 15.f);
+}
+// Eight codes (element order) -> one storage word.
+__device__ __forceinline__ uint32_t pack_word(const uint32_t (&c)[8]) {
+  const uint32_t lo = c[0] | (c[2] << 4) | (c[4] << 8) | (c[6] << 12);
+  const uint32_t hi = c[1] | (c[3] << 4) | (c[5] << 8) | (c[7] << 12);
+  return lo | (hi << 16);
+}
+__device__ __forceinline__ uint32_t pack_params(float s, float z) {
+  return (__builtin_bit_cast(uint32_t, s) >> 16) | (__builtin_bit_cast(uint32_t, z) & 0xffff0000u);
+}
+
+// ---------------------------------------------------------------- quantiser
+// K: W = D/8 lanes per key row, each lane one word (8 elements, 16 bytes of
+// bf16 in, 4 bytes of codes out); the row's min and max by xor shuffles.
+template <int D>
+__global__ __launch_bounds__(256) void quant_k_kernel(const uint16_t* __restrict__ k,
+                                                      uint8_t* __restrict__ kq,
+                                                      uint32_t* __restrict__ kp,
+                                                      long long rows) {
+  constexpr int W = D / 8;
+  const int lane = threadIdx.x & 63;
+  const long long row = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / W) + lane / W;
+  const int w = lane % W;
+  const bool ok = row < rows;
+  float x[8];
+  if (ok) {
+    const u32x4 r = *reinterpret_cast<const u32x4*>(k + row * D + 8 * w);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16_to_f32(r[i] & 0xffffu);
+      x[2 * i + 1] = bf16_to_f32(r[i] >> 16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = 0.f;
+  }
+  float lo = x[0], hi = x[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) {
+    lo = fminf(lo, x[i]);
+    hi = fmaxf(hi, x[i]);
+  }
+#pragma unroll
+  for (int off = 1; off < W; off <<= 1) {
+    lo = fminf(lo, __shfl_xor(lo, off));
+    hi = fmaxf(hi, __shfl_xor(hi, off));
+  }
+  if (!ok) return;
+  const float s = block_scale(lo, hi);
+  uint32_t c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = code_of(x[i], s, lo);
+  reinterpret_cast<uint32_t*>(kq + row * (D / 2))[w] = pack_word(c);
+  if (w == 0) kp[row] = pack_params(s, lo);
+}
+
+// V: one thread per channel of one 64-key tile (block = one (b, g, tile)).
+template <int D>
+__global__ __launch_bounds__(D) void quant_v_kernel(const uint16_t* __restrict__ v,
+                                                    uint8_t* __restrict__ vq,
+                                                    uint32_t* __restrict__ vp, int L, int T) {
+  const int ch = threadIdx.x;
+  const long long bg = blockIdx.x / T;
+  const int t = blockIdx.x % T;
+  const int n = min(kTile, L - kTile * t);
+  const uint16_t* src = v + (bg * L + (long long)kTile * t) * D + ch;
+  float lo = bf16_to_f32(src[0]), hi = lo;
+  for (int j = 1; j < n; ++j) {
+    const float x = bf16_to_f32(src[(long long)j * D]);
+    lo = fminf(lo, x);
+    hi = fmaxf(hi, x);
+  }
+  const float s = block_scale(lo, hi);
+  const long long blk = (bg * T + t) * D + ch;
+  uint32_t* dst = reinterpret_cast<uint32_t*>(vq + blk * 32);
+#pragma unroll
+  for (int wd = 0; wd < 8; ++wd) {
+    uint32_t c[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = 8 * wd + e;
+      c[e] = j < n ? code_of(bf16_to_f32(src[(long long)j * D]), s, lo) : 0u;
+    }
+    dst[wd] = pack_word(c);
+  }
+  vp[blk] = pack_params(s, lo);
+}
+
+// ------------------------------------------------------------ decode kernel
+constexpr int kNT = 2;  // non-temporal cache policy
+constexpr int kRT = 0;  // default cache policy
+template <int AUX>
+__device__ __forceinline__ u32x4 ld4(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, AUX));
+}
+template <int AUX>
+__device__ __forceinline__ u32x2 ld2(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, AUX));
+}
+
+// One storage word -> its 8 codes as exact fp16 integers, element order.
+// (w & 0x000f000f) | 0x64006400 is the fp16 pair (1024 + e0, 1024 + e1); the
+// 0x00f0 nibbles give 1024 + 16 e, brought back by (x / 16 - 64).
+__device__ __forceinline__ f16x8 expand_word(uint32_t w) {
+  const uint32_t m = 0x64006400u;
+  const uint32_t w8 = w >> 8;
+  const f16x2 x0 = __builtin_bit_cast(f16x2, (w & 0x000f000fu) | m);
+  const f16x2 x1 = __builtin_bit_cast(f16x2, (w & 0x00f000f0u) | m);
+  const f16x2 x2 = __builtin_bit_cast(f16x2, (w8 & 0x000f000fu) | m);
+  const f16x2 x3 = __builtin_bit_cast(f16x2, (w8 & 0x00f000f0u) | m);
+  const f16x2 off = {(_Float16)-1024.f, (_Float16)-1024.f};
+  const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const f16x2 off16 = {(_Float16)-64.f, (_Float16)-64.f};
+  const f16x2 y0 = x0 + off;
+  const f16x2 y1 = __builtin_elementwise_fma(x1, sixteenth, off16);
+  const f16x2 y2 = x2 + off;
+  const f16x2 y3 = __builtin_elementwise_fma(x3, sixteenth, off16);
+  f16x8 r;
+  r[0] = y0[0]; r[1] = y0[1]; r[2] = y1[0]; r[3] = y1[1];
+  r[4] = y2[0]; r[5] = y2[1]; r[6] = y3[0]; r[7] = y3[1];
+  return r;
+}
+
+__device__ __forceinline__ float param_s(uint32_t p) { return __builtin_bit_cast(float, p << 16); }
+__device__ __forceinline__ float param_z(uint32_t p) { return __builtin_bit_cast(float, p & 0xffff0000u); }
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ kq,
+    const uint32_t* __restrict__ kp, const uint8_t* __restrict__ vq,
+    const uint32_t* __restrict__ vp, float* __restrict__ ws_o, float* __restrict__ ws_lse,
+    uint8_t* __restrict__ mask, int Hq, int Hkv, int L, int nsplit, float tau_raw, float c,
+    int nwork) {
+  constexpr int KS = D / 32;  // QK k-steps; words per lane per K row
+  constexpr int DB = D / 16;  // 16-channel blocks of O^T and of V code rows
+  constexpr int RB = D / 2;   // bytes of codes per K row
+  static_assert(kSplit / kTile <= 64, "the per-lane skip bits hold one split");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int work = blockIdx.x * 4 + wave;
+  if (work >= nwork) return;  // whole wave leaves; the kernel has no barrier
+  const int sp = work % nsplit;
+  const int bg = work / nsplit;
+  const int g = bg % Hkv;
+  const int b = bg / Hkv;
+  const int G = Hq / Hkv;
+  const int hl = lane & 15;
+  const int grp = lane >> 4;
+  const int T = (L + kTile - 1) / kTile;
+
+  const size_t head = (size_t)(b * Hkv + g);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(kq + head * L * RB), (short)0, L * RB, kCfg);
+  const __amdgpu_buffer_rsrc_t kprs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(kp + head * L), (short)0, L * 4, kCfg);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(vq + head * T * D * 32), (short)0, T * D * 32, kCfg);
+  const __amdgpu_buffer_rsrc_t vprs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(vp + head * T * D), (short)0, T * D * 4, kCfg);
+
+  const int key_begin = sp * kSplit;
+  const int key_end = min(L, key_begin + kSplit);
+  const int ntile = (key_end - key_begin + kTile - 1) / kTile;
+  const int tile_begin = key_begin / kTile;
+  const bool head_ok = hl < G;
+  const size_t bh = (size_t)b * Hq + g * G + hl;
+
+  // q^T fragments (B operand, n = head): lane group grp holds d range
+  // [grp D/4, (grp + 1) D/4), k-step ks its elements 8 ks .. 8 ks + 7.
+  float qv[KS][8];
+  float qmax = 0.f, qsum = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (head_ok) x = ldg16(q + bh * D + grp * (D / 4) + 8 * ks);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qv[ks][2 * i] = bf16_to_f32(x[i] & 0xffffu);
+      qv[ks][2 * i + 1] = bf16_to_f32(x[i] >> 16);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qmax = fmaxf(qmax, fabsf(qv[ks][e]));
+      qsum += qv[ks][e];
+    }
+  }
+  qmax = fmaxf(qmax, xor16(qmax));
+  qmax = fmaxf(qmax, xor32(qmax));
+  qsum += xor16(qsum);
+  qsum += xor32(qsum);
+  // fp16 holds |x| < 2^16: scale the head by 2^-e with qmax 2^-e < 2^15.
+  const int qe = max(0, __builtin_amdgcn_frexp_expf(qmax) - 15);
+  const float qdown = __builtin_ldexpf(1.f, -qe);
+  const float qup = __builtin_ldexpf(1.f, qe);
+  f16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[ks][e] = (_Float16)(qv[ks][e] * qdown);
+
+  // Per-tile registers: K codes (block mb: KS words of row 16 (hl >> 2) +
+  // 4 mb + (hl & 3)), K parameters (keys 16 grp + 4 j .. + 3), V codes
+  // (block db: words 2 grp, 2 grp + 1 of channel row 16 db + hl) and V
+  // parameters (channels 16 db + 4 grp .. + 3).
+  uint32_t kc[4][KS];
+  u32x4 kpr[4];
+  u32x2 vc[DB];
+  u32x4 vpr[DB];
+  const int krow = 16 * (hl >> 2) + (hl & 3);
+  auto kload = [&](int t) {
+    const uint32_t tb = t < ntile ? (uint32_t)(key_begin + t * kTile) : 0u;
+    const uint32_t no = t < ntile ? 0u : kNoRead;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const uint32_t off = no + (tb + krow + 4 * mb) * RB + grp * (RB / 4);
+      if constexpr (KS == 4) {
+        const u32x4 x = ld4<kNT>(krs, off);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) kc[mb][w] = x[w];
+      } else {
+        const u32x2 x = ld2<kNT>(krs, off);
+#pragma unroll
+        for (int w = 0; w < 2; ++w) kc[mb][w] = x[w];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kpr[j] = ld4<kRT>(kprs, no + (tb + 16 * grp + 4 * j) * 4);
+  };
+  auto vload = [&](int t, bool want) {
+    const bool rd = want && t < ntile;
+    const uint32_t tile = rd ? (uint32_t)(tile_begin + t) : 0u;
+    const uint32_t no = rd ? 0u : kNoRead;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      vc[db] = ld2<kNT>(vrs, no + ((tile * D + 16 * db + hl) * 32 + 8 * grp));
+      vpr[db] = ld4<kRT>(vprs, no + (tile * D + 16 * db + 4 * grp) * 4);
+    }
+  };
+
+  // Scores of one tile (raw q.k^ units), masked past L, and the tile max.
+  auto scores = [&](int t, f32x4 (&s)[4]) -> float {
+    const int key0 = key_begin + t * kTile;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        a = __builtin_amdgcn_mfma_f32_16x16x32_f16(expand_word(kc[mb][ks]), qf[ks], a, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t p = kpr[mb][r];
+        s[mb][r] = __builtin_fmaf(param_s(p), a[r] * qup, param_z(p) * qsum);
+      }
+    }
+    if (key0 + kTile > L) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (key0 + 16 * grp + 4 * mb + r >= L) s[mb][r] = -INFINITY;
+    }
+    float x = s[0][0];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x = fmaxf(x, s[mb][r]);
+    x = fmaxf(x, xor16(x));
+    return fmaxf(x, xor32(x));
+  };
+
+  f32x4 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[db][r] = 0.f;
+  float m_run = -INFINITY;  // running max over kept tiles: the skip test's reference
+  float m_ref = -INFINITY;  // reference max of the exponentials accumulated so far
+  float lsum = 0.f;
+  uint64_t skipped = 0;
+  auto decide = [&](float tmax, int t, bool& keep) -> bool {
+    keep = !(tmax < m_run - tau_raw);
+    if (keep) m_run = fmaxf(m_run, tmax);
+    else skipped |= 1ull << t;
+    return __ballot(keep && head_ok) != 0ull;
+  };
+
+  // As in the bf16 decode: the next tile's K always goes out before this
+  // tile's V, and every iteration issues the same loads (kNoRead for the
+  // unwanted ones), so the compiler's wait counts keep the rest in flight.
+  kload(0);
+  f32x4 s_cur[4];
+  float t_cur = scores(0, s_cur);
+  bool keep_cur;
+  bool any_cur = decide(t_cur, 0, keep_cur);
+  kload(1);
+  __builtin_amdgcn_sched_barrier(0);
+  vload(0, any_cur);
+
+  for (int t = 0; t < ntile; ++t) {
+    f32x4 s_nx[4];
+    float t_nx = -INFINITY;
+    bool keep_nx = false, any_nx = false;
+    if (t + 1 < ntile) {
+      t_nx = scores(t + 1, s_nx);
+      any_nx = decide(t_nx, t + 1, keep_nx);
+    }
+    kload(t + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (any_cur) {
+      const float mn = keep_cur ? fmaxf(m_ref, t_cur) : m_ref;
+      if (mn > m_ref) {
+        const float alpha = exp2_fast((m_ref - mn) * c);
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[db][r] *= alpha;
+        m_ref = mn;
+      }
+      const float nmc = -m_ref * c;
+      f16x8 pf[2];
+      float part = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float p = exp2_fast(__builtin_fmaf(s_cur[2 * ks + (e >> 2)][e & 3], c, nmc));
+          if (!keep_cur) p = 0.f;
+          part += p;
+          pf[ks][e] = (_Float16)p;
+        }
+      lsum += part;
+      float ptile = part + xor16(part);
+      ptile += xor32(ptile);
+      // O^T += s_c (codes^T . P^T) + z_c sum_j p_j
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          u = __builtin_amdgcn_mfma_f32_16x16x32_f16(expand_word(vc[db][ks]), pf[ks], u, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t p = vpr[db][r];
+          acc[db][r] = __builtin_fmaf(param_s(p), u[r], __builtin_fmaf(param_z(p), ptile, acc[db][r]));
+        }
+      }
+    }
+    vload(t + 1, any_nx);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) s_cur[mb] = s_nx[mb];
+    t_cur = t_nx;
+    keep_cur = keep_nx;
+    any_cur = any_nx;
+  }
+
+  if (mask != nullptr && lane < G) {  // lane < G: grp 0, head hl = lane
+    uint8_t* mrow = mask + bh * T + tile_begin;
+    for (int t = 0; t < ntile; ++t) mrow[t] = (uint8_t)((skipped >> t) & 1u);
+  }
+
+  float ltot = lsum + xor16(lsum);
+  ltot += xor32(ltot);
+  if (head_ok) {
+    const float inv = 1.f / ltot;
+    float* dst = ws_o + (bh * nsplit + sp) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      f32x4 val;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) val[r] = acc[db][r] * inv;
+      *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * grp) = val;
+    }
+    if (grp == 0) ws_lse[bh * nsplit + sp] = (m_ref * c + __log2f(ltot)) * kLn2;
+  }
+}
+
+template <int D>
+int launch_q_d(const QuantArgs& a) {
+  const long long rows = (long long)a.B * a.Hkv * a.L;
+  const long long waves = (rows + (64 / (D / 8)) - 1) / (64 / (D / 8));
+  const long long g1 = (waves + 3) / 4;
+  const int T = (a.L + kTile - 1) / kTile;
+  const long long g2 = (long long)a.B * a.Hkv * T;
+  if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return -1;
+  hipLaunchKernelGGL((quant_k_kernel<D>), dim3((unsigned)g1), dim3(256), 0, (hipStream_t)a.stream,
+                     (const uint16_t*)a.k, a.kq, a.kp, rows);
+  hipLaunchKernelGGL((quant_v_kernel<D>), dim3((unsigned)g2), dim3(D), 0, (hipStream_t)a.stream,
+                     (const uint16_t*)a.v, a.vq, a.vp, a.L, T);
+  return 0;
+}
+
+template <int D>
+int launch_dq_d(const DecodeQ4Args& a) {
+  const long long nwork = (long long)a.B * a.Hkv * a.nsplit;
+  if (nwork > 0x7fffffffLL) return -1;
+  const unsigned g1 = (unsigned)((nwork + 3) / 4);
+  hipLaunchKernelGGL((decode_q4_split_kernel<D>), dim3(g1), dim3(256), 0, (hipStream_t)a.stream,
+                     (const uint16_t*)a.q, a.kq, a.kp, a.vq, a.vp, a.ws_o, a.ws_lse, a.mask, a.Hq,
+                     a.Hkv, a.L, a.nsplit, a.tau_raw, a.c, (int)nwork);
+  return launch_decode_merge(a.ws_o, a.ws_lse, a.o, a.lse, a.B * a.Hq, a.d, a.nsplit, a.stream);
+}
+
+}  // namespace
+
+int launch_kv_quantize_q4(const QuantArgs& a) {
+  return a.d == 128 ? launch_q_d<128>(a) : launch_q_d<64>(a);
+}
+
+int launch_decode_q4(const DecodeQ4Args& a) {
+  return a.d == 128 ? launch_dq_d<128>(a) : launch_dq_d<64>(a);
+}
+
+}  // namespace skipattn

@@ -34,9 +34,42 @@ struct DecodeArgs {
   void* stream;
 };
 
+struct QuantArgs {
+  const void* k;  // bf16 [B, Hkv, L, d]
+  const void* v;
+  uint8_t* kq;    // 4-bit codes and parameter words, layout in kvq4.hip
+  uint32_t* kp;
+  uint8_t* vq;
+  uint32_t* vp;
+  int B, Hkv, L, d;
+  void* stream;
+};
+
+struct DecodeQ4Args {
+  const void* q;
+  const uint8_t* kq;
+  const uint32_t* kp;
+  const uint8_t* vq;
+  const uint32_t* vp;
+  float* o;
+  float* lse;
+  uint8_t* mask;
+  float* ws_o;
+  float* ws_lse;
+  int B, Hq, Hkv, L, d, nsplit;
+  float tau_raw;
+  float c;
+  void* stream;
+};
+
 // Each returns 0 when the kernels were enqueued, nonzero if the grid cannot
 // be expressed; launch errors are read back by the caller.
 int launch_prefill(const PrefillArgs& a);
 int launch_decode(const DecodeArgs& a);
+int launch_kv_quantize_q4(const QuantArgs& a);
+int launch_decode_q4(const DecodeQ4Args& a);
+// The log-sum-exp merge of per-split partials (shared by both decodes).
+int launch_decode_merge(const float* ws_o, const float* ws_lse, float* o, float* lse, int nbh,
+                        int d, int nsplit, void* stream);
 
 }  // namespace skipattn

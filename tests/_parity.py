@@ -133,9 +133,16 @@ def check_prefill(q_bits, k_bits, v_bits, causal, tau, o, lse, mask, blocks=None
 
 
 def check_decode(q_bits, k_bits, v_bits, tau, o, lse, mask, heads=None,
-                 split=oracle.SPLIT) -> Report:
+                 split=oracle.SPLIT, kv_for=None, Hkv=None) -> Report:
+    """``kv_for(b, g)`` -> (k, v) fp64 (L, d) replaces the bf16 K/V (then
+    k_bits and v_bits may be None and Hkv must be given): the 4-bit cache
+    is checked against the oracle on its dequantised values."""
     B, Hq, d = q_bits.shape
-    Hkv = k_bits.shape[1]
+    if kv_for is None:
+        Hkv = k_bits.shape[1]
+
+        def kv_for(b, g):
+            return synth.bf16_bits_to_f64(k_bits[b, g]), synth.bf16_bits_to_f64(v_bits[b, g])
     G = Hq // Hkv
     if heads is None:
         heads = [(b, h) for b in range(B) for h in range(Hq)]
@@ -146,8 +153,7 @@ def check_decode(q_bits, k_bits, v_bits, tau, o, lse, mask, heads=None,
         g = h // G
         if (b, g) not in cache:
             cache.clear()
-            cache[(b, g)] = (synth.bf16_bits_to_f64(k_bits[b, g]),
-                             synth.bf16_bits_to_f64(v_bits[b, g]))
+            cache[(b, g)] = kv_for(b, g)
         k, v = cache[(b, g)]
         qv = synth.bf16_bits_to_f64(q_bits[b, h])
         ro, rl, dec, margin = oracle.decode_head(qv, k, v, tau, split)

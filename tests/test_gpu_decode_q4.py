@@ -1,0 +1,172 @@
+"""GPU parity of the 4-bit KV cache: the quantiser against the oracle's
+encoder bit for bit, and attn_decode_q4 against the fp64 decode oracle run
+on the oracle's dequantised cache (same tolerances as the bf16 decode)."""
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import kvq4
+from tests import _parity
+
+pytestmark = pytest.mark.gpu
+INF = math.inf
+
+
+def _dev(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _host(cache):
+    out = {n: t.cpu().numpy() for n, t in cache.items()}
+    out["kp"] = out["kp"].view(np.uint32)
+    out["vp"] = out["vp"].view(np.uint32)
+    return out
+
+
+def _oracle_kv(enc, L):
+    def kv_for(b, g):
+        return (kvq4.decode_k(enc["kq"][b, g], enc["kp"][b, g]),
+                kvq4.decode_v(enc["vq"][b, g], enc["vp"][b, g], L))
+    return kv_for
+
+
+def _assert_same_cache(got, want, where=""):
+    for n in ("kq", "kp", "vq", "vp"):
+        a, b = got[n], want[n]
+        assert a.shape == b.shape, (n, a.shape, b.shape)
+        bad = np.argwhere(a != b)
+        assert bad.size == 0, f"{where} {n}: {len(bad)} differing entries, first {bad[:3].tolist()}"
+
+
+def _rand_kv(B, Hkv, L, d, seed, scale=1.0):
+    rng = np.random.default_rng(seed)
+    x = rng.normal(scale=scale, size=(2, B, Hkv, L, d)).astype(np.float32)
+    bits = synth.f32_to_bf16_bits(x)
+    return bits[0], bits[1]
+
+
+QCASES = [  # (B, Hkv, L, d, seed, scale)
+    (1, 1, 1, 128, 1, 1.0), (1, 2, 63, 64, 2, 1.0), (2, 1, 64, 128, 3, 1.0),
+    (1, 3, 65, 64, 4, 30.0), (2, 2, 4097, 128, 5, 1.0), (1, 1, 1000, 128, 6, 1e-3),
+    (1, 2, 300, 64, 7, 1e4),
+]
+
+
+@pytest.mark.parametrize("B,Hkv,L,d,seed,scale", QCASES)
+def test_quantiser_bit_exact(B, Hkv, L, d, seed, scale):
+    import torch
+    import long_context_tiled_amd as lib
+    k, v = _rand_kv(B, Hkv, L, d, seed, scale)
+    k[0, 0, 0, :] = k[0, 0, 0, 0]                   # a constant K row
+    v[0, 0, : min(L, 64), 0] = v[0, 0, 0, 0]         # a constant V block
+    print(f"[q4] quantise B={B} Hkv={Hkv} L={L} d={d} seed={seed}", flush=True)
+    got = _host(lib.quantize_q4(_dev(k), _dev(v)))
+    torch.cuda.synchronize()
+    want = kvq4.encode(synth.bf16_bits_to_f32(k), synth.bf16_bits_to_f32(v))
+    _assert_same_cache(got, want)
+
+
+def _decode_case(q, k, v, taus, name):
+    import torch
+    import long_context_tiled_amd as lib
+    B, Hq, d = q.shape
+    Hkv, L = k.shape[1], k.shape[2]
+    print(f"[q4] {name}: quantise", flush=True)
+    cache = lib.quantize_q4(_dev(k), _dev(v))
+    enc = kvq4.encode(synth.bf16_bits_to_f32(k), synth.bf16_bits_to_f32(v))
+    _assert_same_cache(_host(cache), enc, name)
+    dq = _dev(q)
+    for tau in taus:
+        print(f"[q4] {name} tau={tau}", flush=True)
+        o, lse, mask = lib.decode_q4(dq, cache, L, tau, want_mask=True)
+        torch.cuda.synchronize()
+        rep = _parity.check_decode(q, None, None, tau, o.cpu().numpy(), lse.cpu().numpy(),
+                                   mask.cpu().numpy(), kv_for=_oracle_kv(enc, L), Hkv=Hkv)
+        print(f"  {rep}", flush=True)
+        assert rep.ok(), str(rep)
+
+
+def _cfg(**kw):
+    base = dict(kind="decode", B=2, Hq=8, Hkv=2, L=10000, d=128, sinks=True, window=True)
+    base.update(kw)
+    return base
+
+
+SMALL = [
+    ("gqa4_ragged_3splits", _cfg(id=60), (INF, 8.0, 4.0, 1.0)),
+    ("g1_d64_one_split", _cfg(B=1, Hq=2, Hkv=2, L=4096, d=64, id=61), (INF, 2.0)),
+    ("g8_split_edge", _cfg(B=1, Hq=8, Hkv=1, L=4097, id=62), (INF, 4.0)),
+    ("g16", _cfg(B=1, Hq=16, Hkv=1, L=9000, id=63), (INF, 3.0)),
+    ("g3_d64", _cfg(B=3, Hq=6, Hkv=2, L=12345, d=64, id=64), (INF, 0.0, 2.0)),
+]
+
+
+@pytest.mark.parametrize("name,cfg,taus", SMALL, ids=[s[0] for s in SMALL])
+def test_decode_q4_small(name, cfg, taus):
+    q, k, v = synth.make_decode(cfg)
+    _decode_case(q, k, v, taus, name)
+
+
+@pytest.mark.parametrize("L", [1, 2, 63, 64, 65, 4095, 4096, 4160, 8193])
+def test_decode_q4_edge_lengths(L):
+    q, k, v = synth.make_decode(_cfg(B=1, Hq=4, Hkv=1, L=L, id=70))
+    _decode_case(q, k, v, (INF, 0.0, 3.0), f"edge L={L}")
+
+
+def test_decode_q4_large_q_is_rescaled():
+    # q elements far outside fp16's range take the per-head power-of-two path
+    q, k, v = synth.make_decode(_cfg(B=1, Hq=4, Hkv=1, L=700, id=71))
+    qf = synth.bf16_bits_to_f32(q) * np.float32(2.0 ** 40)
+    q = synth.f32_to_bf16_bits(qf)
+    kf = synth.bf16_bits_to_f32(k) * np.float32(2.0 ** -40)
+    k = synth.f32_to_bf16_bits(kf)
+    _decode_case(q, k, v, (INF, 4.0), "large q")
+
+
+def test_decode_q4_workload_sampled():
+    import torch
+    import long_context_tiled_amd as lib
+    cfg = synth.workload("decode_128k")
+    print("[q4] generating decode_128k", flush=True)
+    q, k, v = synth.make_decode(cfg)
+    B, Hq, d = q.shape
+    Hkv, L = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    print("[q4] decode_128k: quantise", flush=True)
+    cache = lib.quantize_q4(_dev(k), _dev(v))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    heads = sorted({(int(rng.integers(B)), int(rng.integers(Hq))) for _ in range(8)}
+                   | {(0, 0), (B - 1, Hq - 1)})
+    groups = sorted({(b, h // G) for b, h in heads})
+    enc = {}
+    for b, g in groups:   # the cache of every sampled KV head, bit for bit
+        e = kvq4.encode(synth.bf16_bits_to_f32(k[b, g]), synth.bf16_bits_to_f32(v[b, g]))
+        got = {n: cache[n][b, g].cpu().numpy() for n in cache}
+        got["kp"], got["vp"] = got["kp"].view(np.uint32), got["vp"].view(np.uint32)
+        _assert_same_cache(got, e, f"b={b} g={g}")
+        enc[(b, g)] = e
+
+    def kv_for(b, g):
+        e = enc[(b, g)]
+        return kvq4.decode_k(e["kq"], e["kp"]), kvq4.decode_v(e["vq"], e["vp"], L)
+
+    dq = _dev(q)
+    prev = None
+    for tau in cfg["taus"]:
+        print(f"[q4] decode_128k tau={tau}", flush=True)
+        o, lse, mask = lib.decode_q4(dq, cache, L, tau, want_mask=True)
+        torch.cuda.synchronize()
+        mask_np = mask.cpu().numpy()
+        assert (mask_np[:, :, ::64] == 0).all()
+        if prev is not None:
+            assert ((prev == 1) <= (mask_np == 1)).all()
+        prev = mask_np
+        rep = _parity.check_decode(q, None, None, tau, o.cpu().numpy(), lse.cpu().numpy(),
+                                   mask_np, heads=heads, kv_for=kv_for, Hkv=Hkv)
+        print(f"  skip_fraction={(mask_np == 1).mean():.4f} {rep}", flush=True)
+        assert rep.ok(), str(rep)
+        del o, lse, mask
