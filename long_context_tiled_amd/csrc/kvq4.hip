@@ -23,11 +23,16 @@
 //   kq [B,Hkv,L,d/2] u8, kp [B,Hkv,L] u32, vq [B,Hkv,T,d,32] u8 (64 keys of a
 //   channel per tile, keys past L code 0), vp [B,Hkv,T,d] u32, T = ceil(L/64).
 //
-// Decode split kernel: one wave per (sequence, KV head, split), no LDS. The
-// products run on v_mfma_f32_16x16x32_f16 with the codes expanded to exact
-// fp16 integers (0..15), q in fp16 (scaled by a power of two when a head's
-// largest element would not fit) and P in fp16; the affine parts of the
-// dequantisation are applied to the fp32 results.
+// Decode split kernel: one wave per (sequence, KV head, split), no LDS.
+//   q.K on v_mfma_f32_16x16x32_bf16: q exact in bf16, each code c expanded to
+//   the exact bf16 value 128 + c (bits 0x4300 | c, one and-or per pair of
+//   codes), and the offset folded into the zero point: q.k^ = s (q.(128 + c))
+//   + (z - 128 s) sum(q), with sum(q) from the same MFMA on a row of ones.
+//   P.V on v_mfma_f32_16x16x32_f16: P rounded to fp16, codes expanded to exact
+//   fp16 integers (the 0x6400 | c trick, then the 1024 offset removed by a
+//   packed fp16 add or fma), so the offset never meets P's rounding:
+//   sum_j p_j v^_jc = s_c (P.c) + z_c sum(P), with sum(P) again from an MFMA
+//   over the same fp16 P.
 //   Key order inside a tile: S^T row 4 grp + r of block mb holds key
 //   16 grp + 4 mb + r, so lane (head, grp) owns keys 16 grp .. 16 grp + 15 and
 //   its P^T fragment for PV k-step ks is keys 16 grp + 8 ks .. + 7, which is
@@ -170,16 +175,45 @@ __device__ __forceinline__ u32x2 ld2(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, AUX));
 }
 
+// The two constants of expand_word, held in registers: gfx9 VOP3 encodings
+// take no literal, so with the mask in an SGPR and the magic in a VGPR the
+// compiler can fuse each mask-and-or into one v_and_or_b32 (and it still
+// sees every register it writes, for the MFMA read hazards).
+struct ExpandConsts {
+  uint32_t mask;     // 0x000f000f
+  uint32_t mask4;    // 0x00f000f0
+  uint32_t bmagic;   // 0x43004300: bf16 128 in both halves
+  uint32_t hmagic;   // 0x64006400: fp16 1024 in both halves
+};
+__device__ __forceinline__ ExpandConsts expand_consts() {
+  ExpandConsts k;
+  asm volatile("s_mov_b32 %0, 0x000f000f" : "=s"(k.mask));
+  asm volatile("s_mov_b32 %0, 0x00f000f0" : "=s"(k.mask4));
+  asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(k.bmagic));
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(k.hmagic));
+  return k;
+}
+
+// One storage word -> its 8 codes as bf16 values 128 + c, element order:
+// nibble n of each 16-bit half, moved to bits 0..3 and or-ed into 0x4300.
+__device__ __forceinline__ bf16x8 expand_word_bf16(uint32_t w, const ExpandConsts& k) {
+  u32x4 r;
+  r[0] = (w & k.mask) | k.bmagic;
+  r[1] = ((w >> 4) & k.mask) | k.bmagic;
+  r[2] = ((w >> 8) & k.mask) | k.bmagic;
+  r[3] = ((w >> 12) & k.mask) | k.bmagic;
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 // One storage word -> its 8 codes as exact fp16 integers, element order.
 // (w & 0x000f000f) | 0x64006400 is the fp16 pair (1024 + e0, 1024 + e1); the
 // 0x00f0 nibbles give 1024 + 16 e, brought back by (x / 16 - 64).
-__device__ __forceinline__ f16x8 expand_word(uint32_t w) {
-  const uint32_t m = 0x64006400u;
+__device__ __forceinline__ f16x8 expand_word_f16(uint32_t w, const ExpandConsts& k) {
   const uint32_t w8 = w >> 8;
-  const f16x2 x0 = __builtin_bit_cast(f16x2, (w & 0x000f000fu) | m);
-  const f16x2 x1 = __builtin_bit_cast(f16x2, (w & 0x00f000f0u) | m);
-  const f16x2 x2 = __builtin_bit_cast(f16x2, (w8 & 0x000f000fu) | m);
-  const f16x2 x3 = __builtin_bit_cast(f16x2, (w8 & 0x00f000f0u) | m);
+  const f16x2 x0 = __builtin_bit_cast(f16x2, (w & k.mask) | k.hmagic);
+  const f16x2 x1 = __builtin_bit_cast(f16x2, (w & k.mask4) | k.hmagic);
+  const f16x2 x2 = __builtin_bit_cast(f16x2, (w8 & k.mask) | k.hmagic);
+  const f16x2 x3 = __builtin_bit_cast(f16x2, (w8 & k.mask4) | k.hmagic);
   const f16x2 off = {(_Float16)-1024.f, (_Float16)-1024.f};
   const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
   const f16x2 off16 = {(_Float16)-64.f, (_Float16)-64.f};
@@ -240,47 +274,39 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
 
   // q^T fragments (B operand, n = head): lane group grp holds d range
   // [grp D/4, (grp + 1) D/4), k-step ks its elements 8 ks .. 8 ks + 7.
-  float qv[KS][8];
-  float qmax = 0.f, qsum = 0.f;
+  bf16x8 qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     u32x4 x = {0u, 0u, 0u, 0u};
     if (head_ok) x = ldg16(q + bh * D + grp * (D / 4) + 8 * ks);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      qv[ks][2 * i] = bf16_to_f32(x[i] & 0xffffu);
-      qv[ks][2 * i + 1] = bf16_to_f32(x[i] >> 16);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      qmax = fmaxf(qmax, fabsf(qv[ks][e]));
-      qsum += qv[ks][e];
-    }
+    qf[ks] = as_bf16x8(x);
   }
-  qmax = fmaxf(qmax, xor16(qmax));
-  qmax = fmaxf(qmax, xor32(qmax));
-  qsum += xor16(qsum);
-  qsum += xor32(qsum);
-  // fp16 holds |x| < 2^16: scale the head by 2^-e with qmax 2^-e < 2^15.
-  const int qe = max(0, __builtin_amdgcn_frexp_expf(qmax) - 15);
-  const float qdown = __builtin_ldexpf(1.f, -qe);
-  const float qup = __builtin_ldexpf(1.f, qe);
-  f16x8 qf[KS];
+  const ExpandConsts xk = expand_consts();
+  // sum_d q_d per head, accumulated by the MFMA itself (A = ones)
+  float qsum;
+  {
+    const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qf[ks][e] = (_Float16)(qv[ks][e] * qdown);
+    for (int ks = 0; ks < KS; ++ks)
+      a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ones), qf[ks], a, 0, 0, 0);
+    qsum = a[0];
+  }
+  const u32x4 ones16 = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};  // fp16 1.0
 
   // Per-tile registers: K codes (block mb: KS words of row 16 (hl >> 2) +
   // 4 mb + (hl & 3)), K parameters (keys 16 grp + 4 j .. + 3), V codes
   // (block db: words 2 grp, 2 grp + 1 of channel row 16 db + hl) and V
   // parameters (channels 16 db + 4 grp .. + 3).
-  uint32_t kc[4][KS];
-  u32x4 kpr[4];
+  struct KSet {
+    uint32_t c[4][KS];
+    u32x4 p[4];
+  };
+  KSet ka, kb;  // K of even tiles in ka, of odd tiles in kb
   u32x2 vc[DB];
   u32x4 vpr[DB];
   const int krow = 16 * (hl >> 2) + (hl & 3);
-  auto kload = [&](int t) {
+  auto kload = [&](KSet& ks_, int t) {
     const uint32_t tb = t < ntile ? (uint32_t)(key_begin + t * kTile) : 0u;
     const uint32_t no = t < ntile ? 0u : kNoRead;
 #pragma unroll
@@ -289,15 +315,15 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
       if constexpr (KS == 4) {
         const u32x4 x = ld4<kNT>(krs, off);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) kc[mb][w] = x[w];
+        for (int w = 0; w < 4; ++w) ks_.c[mb][w] = x[w];
       } else {
         const u32x2 x = ld2<kNT>(krs, off);
 #pragma unroll
-        for (int w = 0; w < 2; ++w) kc[mb][w] = x[w];
+        for (int w = 0; w < 2; ++w) ks_.c[mb][w] = x[w];
       }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) kpr[j] = ld4<kRT>(kprs, no + (tb + 16 * grp + 4 * j) * 4);
+    for (int j = 0; j < 4; ++j) ks_.p[j] = ld4<kRT>(kprs, no + (tb + 16 * grp + 4 * j) * 4);
   };
   auto vload = [&](int t, bool want) {
     const bool rd = want && t < ntile;
@@ -311,18 +337,21 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
   };
 
   // Scores of one tile (raw q.k^ units), masked past L, and the tile max.
-  auto scores = [&](int t, f32x4 (&s)[4]) -> float {
+  auto scores = [&](const KSet& ks_, int t, f32x4 (&s)[4]) -> float {
     const int key0 = key_begin + t * kTile;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        a = __builtin_amdgcn_mfma_f32_16x16x32_f16(expand_word(kc[mb][ks]), qf[ks], a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(expand_word_bf16(ks_.c[mb][ks], xk), qf[ks], a,
+                                                    0, 0, 0);
+      // q.k^ = s (q.(128 + c)) + (z - 128 s) sum(q)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const uint32_t p = kpr[mb][r];
-        s[mb][r] = __builtin_fmaf(param_s(p), a[r] * qup, param_z(p) * qsum);
+        const uint32_t p = ks_.p[mb][r];
+        const float sc = param_s(p);
+        s[mb][r] = __builtin_fmaf(sc, a[r], __builtin_fmaf(-128.f, sc, param_z(p)) * qsum);
       }
     }
     if (key0 + kTile > L) {
@@ -357,27 +386,33 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
     return __ballot(keep && head_ok) != 0ull;
   };
 
-  // As in the bf16 decode: the next tile's K always goes out before this
-  // tile's V, and every iteration issues the same loads (kNoRead for the
-  // unwanted ones), so the compiler's wait counts keep the rest in flight.
-  kload(0);
+  // K runs two tiles ahead of the scores and V one tile ahead of the PV; the
+  // K of a later tile always goes out before the V of an earlier one, and
+  // every step issues the same loads (kNoRead for the unwanted ones), so the
+  // compiler's wait counts keep the rest in flight.
+  kload(ka, 0);
+  kload(kb, 1);
+  __builtin_amdgcn_sched_barrier(0);
   f32x4 s_cur[4];
-  float t_cur = scores(0, s_cur);
+  float t_cur = scores(ka, 0, s_cur);
   bool keep_cur;
   bool any_cur = decide(t_cur, 0, keep_cur);
-  kload(1);
+  kload(ka, 2);
   __builtin_amdgcn_sched_barrier(0);
   vload(0, any_cur);
 
-  for (int t = 0; t < ntile; ++t) {
+  // One tile: scores and decision of tile t + 1 (K in kn, which then takes
+  // tile t + 3), exp/PV of tile t, V of tile t + 1. A step past the last tile
+  // issues only loads that read nothing.
+  auto step = [&](int t, KSet& kn) {
     f32x4 s_nx[4];
     float t_nx = -INFINITY;
     bool keep_nx = false, any_nx = false;
     if (t + 1 < ntile) {
-      t_nx = scores(t + 1, s_nx);
+      t_nx = scores(kn, t + 1, s_nx);
       any_nx = decide(t_nx, t + 1, keep_nx);
     }
-    kload(t + 2);
+    kload(kn, t + 3);
     __builtin_amdgcn_sched_barrier(0);
     if (any_cur) {
       const float mn = keep_cur ? fmaxf(m_ref, t_cur) : m_ref;
@@ -403,15 +438,21 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
           pf[ks][e] = (_Float16)p;
         }
       lsum += part;
-      float ptile = part + xor16(part);
-      ptile += xor32(ptile);
+      // sum_j of the fp16 P of this head, from the same MFMA path (A = ones)
+      f32x4 pt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        pt = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, ones16), pf[ks], pt, 0,
+                                                    0, 0);
+      const float ptile = pt[0];
       // O^T += s_c (codes^T . P^T) + z_c sum_j p_j
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         f32x4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-          u = __builtin_amdgcn_mfma_f32_16x16x32_f16(expand_word(vc[db][ks]), pf[ks], u, 0, 0, 0);
+          u = __builtin_amdgcn_mfma_f32_16x16x32_f16(expand_word_f16(vc[db][ks], xk), pf[ks], u, 0,
+                                                     0, 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const uint32_t p = vpr[db][r];
@@ -425,6 +466,10 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
     t_cur = t_nx;
     keep_cur = keep_nx;
     any_cur = any_nx;
+  };
+  for (int t = 0; t < ntile; t += 2) {
+    step(t, kb);
+    step(t + 1, ka);
   }
 
   if (mask != nullptr && lane < G) {  // lane < G: grp 0, head hl = lane

@@ -54,6 +54,13 @@ class Report:
                 f"lse_err={self.lse_err:.3e} {self.notes[:3]}")
 
 
+def max_abs_err(got, want) -> float:
+    """Largest |got - want|; +inf if any entry of either side is not finite
+    (a NaN must fail the tolerance, not vanish in a max)."""
+    d = np.abs(np.asarray(got, np.float64) - np.asarray(want, np.float64))
+    return float(d.max()) if np.all(np.isfinite(d)) else math.inf
+
+
 def _compare_decisions(gpu_dec, ref_dec, margin, visited):
     """Return (forced array or None, n_ambiguous, n_hard) for one block."""
     diff = (gpu_dec != ref_dec) & visited
@@ -112,8 +119,8 @@ class PrefillChecker:
                                                  forced[None, :])
         rep.tiles += int(visited.sum())
         rep.skipped += int((mask_gpu[visited] == 1).sum())
-        rep.o_err = float(np.abs(o_gpu - o).max())
-        rep.lse_err = float(np.abs(lse_gpu - lse).max())
+        rep.o_err = max_abs_err(o_gpu, o)
+        rep.lse_err = max_abs_err(lse_gpu, lse)
         return rep
 
 
@@ -169,8 +176,8 @@ def check_decode(q_bits, k_bits, v_bits, tau, o, lse, mask, heads=None,
         rep.skipped += int((mask[b, h] == 1).sum())
         rep.ambiguous += amb
         rep.hard_mismatch += hard
-        rep.o_err = max(rep.o_err, float(np.abs(o[b, h] - ro).max()))
-        rep.lse_err = max(rep.lse_err, float(abs(lse[b, h] - rl)))
+        rep.o_err = max(rep.o_err, max_abs_err(o[b, h], ro))
+        rep.lse_err = max(rep.lse_err, max_abs_err(lse[b, h], rl))
     return rep
 
 

@@ -388,3 +388,12 @@ def test_margin_sign_matches_decision():
         r = oracle.prefill(q, k, v, True, tau)
         vis = r["mask"] != 2
         assert ((r["margin"][vis] > 0) == (r["mask"][vis] == 1)).all()
+
+
+def test_parity_error_measure_refuses_nan():
+    from tests import _parity
+    assert _parity.max_abs_err([1.0, 2.0], [1.0, 2.5]) == 0.5
+    assert _parity.max_abs_err([1.0, float("nan")], [1.0, 2.0]) == float("inf")
+    assert _parity.max_abs_err([1.0], [float("inf")]) == float("inf")
+    r = _parity.Report(o_err=_parity.max_abs_err([float("nan")], [0.0]))
+    assert not r.ok()
