@@ -15,6 +15,11 @@ executed TFLOP/s, dense and actual GB/s) and the fp64 oracle's throughput on
 the host cores over a bounded sample of the same workloads. Timed calls
 write no skip mask (an optional output); the sweep reads each tau's mask
 from one extra call outside its timing.
+
+Beside the step, the same decode workload is run over the 4-bit asymmetric
+KV cache (attn_kv_quantize_q4 once, then attn_decode_q4 timed like the bf16
+decode): ``decode_q4`` reports GB/s of the 4-bit bytes read, its fraction of
+HBM peak and the bf16-equivalent rate.
 """
 from __future__ import annotations
 
@@ -42,10 +47,13 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 MEASURED_TRAFFIC = {
     "prefill": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp"),
                 "sha1": "bb8e13ccc508b0fbc4315f4bd92234855ff4a0fa",
-                "bytes": (2745087.6 * 2.0 + 528384.0) * 1024},
+                "bytes": (2784622.6 * 2.0 + 528384.0) * 1024},
+    "decode_q4": {"sources": ("kvq4.hip", "decode.hip", "common.hpp"),
+                  "sha1": "63b8d2d4eb8c126158cf04284f84a49cead20eb4",
+                  "bytes": (1148101.7 * 2.0 + 16640.3) * 1024},
     "decode": {"sources": ("decode.hip", "common.hpp"),
-               "sha1": "4547b90f42cc1cefbe9bf8d39618b34c46dc83fa",
-               "bytes": (4195496.6 * 2.0 + 16641.1) * 1024},
+               "sha1": "642a5529eba59c233ecfeeab8f85092e500c5ce1",
+               "bytes": (4195501.2 * 2.0 + 16641.4) * 1024},
 }
 
 
@@ -92,6 +100,20 @@ def decode_bytes(B, Hkv, L, d, mask=None, G=1):
     tile_keys[-1] = L - 64 * (nt - 1)
     v_bytes = float((keep_any * tile_keys[None, None, :]).sum()) * d * 2
     return dense, dense / 2 + v_bytes
+
+
+def q4_bytes(B, Hkv, L, d, mask=None, G=1):
+    """Bytes of the 4-bit cache the decode must read: K codes (d/2 per key)
+    and parameter words (4 per key), and per V tile its codes (32 d) and
+    parameter words (4 d) when at least one head of the KV group keeps it."""
+    T = (L + 63) // 64
+    k_b = float(B * Hkv * L * (d // 2 + 4))
+    v_tile = 36.0 * d
+    if mask is None:
+        return k_b + B * Hkv * T * v_tile
+    Bm, Hq, nt = mask.shape
+    keep_any = (mask.reshape(Bm, Hkv, G, nt) == 0).any(axis=2)
+    return k_b + float(keep_any.sum()) * v_tile
 
 
 class Timer:
@@ -191,8 +213,10 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--reading", default="S", choices=["S", "P"])
-    ap.add_argument("--only", default="both", choices=["both", "prefill", "decode"],
+    ap.add_argument("--only", default="both", choices=["both", "prefill", "decode", "decode_q4"],
                     help="profile one leg only (the JSON line then reports that leg)")
+    ap.add_argument("--no-q4", action="store_true",
+                    help="skip the 4-bit KV-cache decode measured beside the step")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB, a reference "
                          "dispatch of known traffic for hardware byte counters")
@@ -247,6 +271,7 @@ def main():
 
     run_p = args.only in ("both", "prefill")
     run_d = args.only in ("both", "decode")
+    run_q = args.only == "decode_q4" or (args.only == "both" and not args.no_q4)
 
     # Timed calls pass no skip-mask buffer (the mask is an optional output
     # for analysis); the tau sweep takes one extra masked call per tau to
@@ -315,6 +340,44 @@ def main():
                                    kernel="decode_split_kernel<128>",
                                    avg_ms=round(d_ms, 4), per_launch_bytes=dense_b)
 
+    if run_q:
+        # 4-bit KV cache of the same decode workload: quantised once (timed
+        # on its own), then attn_decode_q4 timed like the bf16 decode.
+        tq0 = Timer()
+        with tq0:
+            cache = lib.quantize_q4(uk, uv)
+        torch.cuda.synchronize()
+        q4b = q4_bytes(DB, DHkv, L, Dd)
+
+        def decode_q4(tau, mask=None):
+            lib.attn_decode_q4(uq, cache, L, do, dlse, tau, ws, mask)
+
+        for _ in range(args.warmup):
+            decode_q4(math.inf)
+        tq4 = Timer()
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            with tq4:
+                decode_q4(math.inf)
+        torch.cuda.synchronize()
+        q_ms = float(np.mean(tq4.ms()))
+        dense_b, _ = decode_bytes(DB, DHkv, L, Dd)
+        gbs_q = q4b / (q_ms * 1e-3) / 1e9
+        dq4 = dict(value=round(gbs_q, 2), unit="GB/s", ms=round(q_ms, 4),
+                   frac_of_hbm=round(gbs_q / PEAK_HBM_GBS, 4), per_call_bytes=q4b,
+                   gbs_bf16_equivalent=round(dense_b / (q_ms * 1e-3) / 1e9, 2),
+                   traffic=measured_traffic("decode_q4"),
+                   quantise_ms=round(float(tq0.ms()[0]), 4),
+                   kernels="decode_q4_split_kernel<128> + decode_merge_kernel<128>")
+        out["decode_q4"] = dq4
+        if args.only == "decode_q4":
+            out.update(value=round(gbs_q, 2), unit="GB/s")
+            out["roofline"] = dict(bound="hbm", achieved=round(gbs_q, 2), peak=PEAK_HBM_GBS,
+                                   unit="GB/s", frac=round(gbs_q / PEAK_HBM_GBS, 4),
+                                   traffic=measured_traffic("decode_q4"),
+                                   kernel="decode_q4_split_kernel<128>",
+                                   avg_ms=round(q_ms, 4), per_launch_bytes=q4b)
+
     if not args.no_sweep:
         sweep = []
         for tau in pcfg["taus"] if run_p else []:
@@ -344,6 +407,19 @@ def main():
             sweep.append(dict(leg="decode_128k", tau=str(tau), ms=round(ms, 4),
                               skip_fraction=round(float((m == 1).mean()), 4),
                               gbs_dense=round(dense_b / ms / 1e6, 2),
+                              gbs_actual=round(act_b / ms / 1e6, 2)))
+        for tau in dcfg["taus"] if run_q else []:
+            t = Timer()
+            for _ in range(3):
+                with t:
+                    decode_q4(tau)
+            torch.cuda.synchronize()
+            ms = float(np.median(t.ms()))
+            decode_q4(tau, dmask)
+            m = dmask.cpu().numpy()
+            act_b = q4_bytes(DB, DHkv, L, Dd, m, DHq // DHkv)
+            sweep.append(dict(leg="decode_128k_q4", tau=str(tau), ms=round(ms, 4),
+                              skip_fraction=round(float((m == 1).mean()), 4),
                               gbs_actual=round(act_b / ms / 1e6, 2)))
         out["tau_sweep"] = sweep
 

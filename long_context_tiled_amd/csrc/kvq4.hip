@@ -132,6 +132,9 @@ __global__ __launch_bounds__(256) void quant_k_kernel(const uint16_t* __restrict
 }
 
 // V: one thread per channel of one 64-key tile (block = one (b, g, tile)).
+// One pass: the tile's 64 values of the channel stay in registers (loads of
+// one key row are coalesced across the block's threads), and the channel's
+// 32-byte code row goes out as two 16-byte stores.
 template <int D>
 __global__ __launch_bounds__(D) void quant_v_kernel(const uint16_t* __restrict__ v,
                                                     uint8_t* __restrict__ vq,
@@ -141,25 +144,31 @@ __global__ __launch_bounds__(D) void quant_v_kernel(const uint16_t* __restrict__
   const int t = blockIdx.x % T;
   const int n = min(kTile, L - kTile * t);
   const uint16_t* src = v + (bg * L + (long long)kTile * t) * D + ch;
-  float lo = bf16_to_f32(src[0]), hi = lo;
-  for (int j = 1; j < n; ++j) {
-    const float x = bf16_to_f32(src[(long long)j * D]);
-    lo = fminf(lo, x);
-    hi = fmaxf(hi, x);
+  float x[kTile];
+#pragma unroll
+  for (int j = 0; j < kTile; ++j) x[j] = j < n ? bf16_to_f32(src[(long long)j * D]) : x[0];
+  float lo = x[0], hi = x[0];
+#pragma unroll
+  for (int j = 1; j < kTile; ++j) {
+    lo = fminf(lo, x[j]);
+    hi = fmaxf(hi, x[j]);
   }
   const float s = block_scale(lo, hi);
   const long long blk = (bg * T + t) * D + ch;
-  uint32_t* dst = reinterpret_cast<uint32_t*>(vq + blk * 32);
+  u32x4 out[2];
 #pragma unroll
   for (int wd = 0; wd < 8; ++wd) {
     uint32_t c[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int j = 8 * wd + e;
-      c[e] = j < n ? code_of(bf16_to_f32(src[(long long)j * D]), s, lo) : 0u;
+      c[e] = j < n ? code_of(x[j], s, lo) : 0u;
     }
-    dst[wd] = pack_word(c);
+    out[wd >> 2][wd & 3] = pack_word(c);
   }
+  u32x4* dst = reinterpret_cast<u32x4*>(vq + blk * 32);
+  dst[0] = out[0];
+  dst[1] = out[1];
   vp[blk] = pack_params(s, lo);
 }
 

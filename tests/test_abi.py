@@ -106,3 +106,42 @@ def test_binding_refuses_host_tensors():
     lse = torch.zeros((1, 2, 64), dtype=torch.float32)
     with pytest.raises(ValueError):
         lib.attn_prefill(q, q, q, o, lse, True, 1.0)
+
+
+def _q4check(**kw):
+    a = dict(q=P, kq=P, kp=P, vq=P, vp=P, o=P, lse=P, B=16, Hq=64, Hkv=8, L=131072, d=128,
+             tau=4.0, mask=None, ws=P, wsb=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = lib.attn_decode_workspace_bytes(a["B"], a["Hq"], a["L"], a["d"])
+    return lib.load().attn_decode_q4_check(a["q"], a["kq"], a["kp"], a["vq"], a["vp"], a["o"],
+                                           a["lse"], a["B"], a["Hq"], a["Hkv"], a["L"], a["d"],
+                                           a["tau"], a["mask"], a["ws"], a["wsb"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, 0), ({"tau": INF}, 0), ({"L": 70, "d": 64}, 0), ({"B": 0, "ws": None, "wsb": 0}, 0),
+    ({"kq": None}, 1), ({"kp": None}, 1), ({"vq": None}, 1), ({"vp": None}, 1),
+    ({"kp": P + 4}, 1), ({"vq": P + 8}, 1), ({"q": None}, 1), ({"tau": -1.0}, 1),
+    ({"d": 96}, 2), ({"Hq": 34, "Hkv": 2}, 2), ({"L": HEAD_LIMIT // 256 + 1}, 2),
+    ({"wsb": 64}, 3),
+])
+def test_decode_q4_validation(kw, code):
+    assert _q4check(**kw) == code
+
+
+def test_quantise_q4_rejects_before_any_launch():
+    so = lib.load()
+    # every case returns before any HIP call (B = 0 is empty work)
+    assert so.attn_kv_quantize_q4(P, P, P, P, P, P, 0, 8, 4096, 128, None) == lib.OK
+    assert so.attn_kv_quantize_q4(None, P, P, P, P, P, 1, 8, 4096, 128, None) == lib.EINVAL
+    assert so.attn_kv_quantize_q4(P, P, P, P + 4, P, P, 1, 8, 4096, 128, None) == lib.EINVAL
+    assert so.attn_kv_quantize_q4(P, P, P, P, P, P, 1, 0, 4096, 128, None) == lib.EINVAL
+    assert so.attn_kv_quantize_q4(P, P, P, P, P, P, 1, 8, 4096, 80, None) == lib.EUNSUPPORTED
+    assert so.attn_kv_quantize_q4(P, P, P, P, P, P, 1, 1, HEAD_LIMIT // 256 + 1, 128,
+                                  None) == lib.EUNSUPPORTED
+
+
+def test_q4_shapes():
+    s = lib.q4_shapes(2, 3, 130, 64)
+    assert s == dict(kq=(2, 3, 130, 32), kp=(2, 3, 130), vq=(2, 3, 3, 64, 32), vp=(2, 3, 3, 64))
