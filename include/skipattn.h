@@ -100,6 +100,24 @@ int attn_prefill(const void* q, const void* k, const void* v, float* o,
                  float tau, uint8_t* skip_mask, void* stream);
 
 /*
+ * attn_prefill_chunk - chunked prefill: the last Nq of N positions attend
+ * to the N keys (the rows N - Nq .. N - 1 of attn_prefill over N positions,
+ * with the same decisions and results; attn_prefill is the case Nq == N).
+ *
+ *   q    bf16 [B, Hq,  Nq, d]  the chunk's queries
+ *   k    bf16 [B, Hkv, N,  d]  every key up to the chunk's end
+ *   v    bf16 [B, Hkv, N,  d]
+ *   o    fp32 [B, Hq,  Nq, d]  out
+ *   lse  fp32 [B, Hq,  Nq]     out
+ *   skip_mask  NULL, or uint8 [B, Hq, ceil(Nq/64), ceil(N/64)].
+ * causal == 1 requires N - Nq to be a multiple of 64 (the chunk starts on a
+ * decision-tile boundary; SKIPATTN_EUNSUPPORTED otherwise); 0 <= Nq <= N.
+ */
+int attn_prefill_chunk(const void* q, const void* k, const void* v, float* o,
+                       float* lse, int B, int Hq, int Hkv, int Nq, int N, int d,
+                       int causal, float tau, uint8_t* skip_mask, void* stream);
+
+/*
  * attn_decode_workspace_bytes - bytes of device scratch attn_decode needs:
  * B * Hq * ceil(L / 4096) * (d + 1) * 4 (per-split partial outputs and
  * log-sum-exps). Returns 0 for invalid or empty sizes.
@@ -132,14 +150,18 @@ int attn_decode(const void* q, const void* k, const void* v, float* o,
                 void* stream);
 
 /*
- * attn_prefill_check / attn_decode_check - the host-side argument
- * validation of the two entry points on its own: the same return code the
+ * attn_prefill_check / attn_prefill_chunk_check / attn_decode_check - the
+ * host-side argument validation of those entry points on its own: the same return code the
  * entry point would give before launching, with no HIP call at all.
  */
 int attn_prefill_check(const void* q, const void* k, const void* v,
                        const float* o, const float* lse, int B, int Hq,
                        int Hkv, int N, int d, int causal, float tau,
                        const uint8_t* skip_mask);
+int attn_prefill_chunk_check(const void* q, const void* k, const void* v,
+                             const float* o, const float* lse, int B, int Hq,
+                             int Hkv, int Nq, int N, int d, int causal,
+                             float tau, const uint8_t* skip_mask);
 int attn_decode_check(const void* q, const void* k, const void* v,
                       const float* o, const float* lse, int B, int Hq,
                       int Hkv, int L, int d, float tau,
@@ -178,6 +200,20 @@ int attn_decode_check(const void* q, const void* k, const void* v,
 int attn_kv_quantize_q4(const void* k, const void* v, uint8_t* kq, uint32_t* kp,
                         uint8_t* vq, uint32_t* vp, int B, int Hkv, int L,
                         int d, void* stream);
+
+/*
+ * attn_kv_quantize_q4_range - the same for keys k0 .. k1 - 1 only, into
+ * arrays sized for a cache of L keys (K, V bf16 [B, Hkv, L, d] hold the
+ * cache's bf16 keys and values; rows outside the range are not read).
+ * k0 must be a multiple of 64. Every V tile that holds a key of the range
+ * is written from its keys below k1, so appending a chunk and later
+ * rewriting a partial tile with more keys gives the same bytes as one call
+ * over the whole cache. 0 <= k0 <= k1 <= L.
+ */
+int attn_kv_quantize_q4_range(const void* k, const void* v, uint8_t* kq,
+                              uint32_t* kp, uint8_t* vq, uint32_t* vp, int B,
+                              int Hkv, int L, int d, int k0, int k1,
+                              void* stream);
 
 /*
  * attn_decode_q4 - attn_decode over a 4-bit cache: the same rule, splits,

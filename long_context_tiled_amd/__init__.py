@@ -5,10 +5,12 @@ from ._lib import (OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, TILE, SPLIT,
                    KEPT, SKIPPED, NOT_VISITED, EXPORTS, LIB_PATH, SkipAttnError,
                    load, attn_prefill, attn_decode, attn_decode_workspace_bytes,
                    attn_last_error, prefill, decode, q4_shapes, attn_kv_quantize_q4,
-                   attn_decode_q4, quantize_q4, decode_q4)
+                   attn_decode_q4, quantize_q4, decode_q4, attn_prefill_chunk, prefill_chunk,
+                   empty_q4)
 
 __all__ = ["OK", "EINVAL", "EUNSUPPORTED", "EWORKSPACE", "EHIP", "TILE", "SPLIT",
            "KEPT", "SKIPPED", "NOT_VISITED", "EXPORTS", "LIB_PATH", "SkipAttnError",
            "load", "attn_prefill", "attn_decode", "attn_decode_workspace_bytes",
            "attn_last_error", "prefill", "decode", "q4_shapes", "attn_kv_quantize_q4",
-           "attn_decode_q4", "quantize_q4", "decode_q4"]
+           "attn_decode_q4", "quantize_q4", "decode_q4", "attn_prefill_chunk",
+           "prefill_chunk", "empty_q4"]

@@ -22,7 +22,8 @@ KEPT, SKIPPED, NOT_VISITED = 0, 1, 2
 
 EXPORTS = ("attn_prefill", "attn_decode", "attn_decode_workspace_bytes",
            "attn_prefill_check", "attn_decode_check", "attn_last_error",
-           "attn_kv_quantize_q4", "attn_decode_q4", "attn_decode_q4_check")
+           "attn_kv_quantize_q4", "attn_decode_q4", "attn_decode_q4_check",
+           "attn_prefill_chunk", "attn_prefill_chunk_check", "attn_kv_quantize_q4_range")
 
 _lib = None
 
@@ -48,6 +49,10 @@ def load() -> ctypes.CDLL:
     lib.attn_prefill.restype = i
     lib.attn_prefill_check.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, i, f, u8p]
     lib.attn_prefill_check.restype = i
+    lib.attn_prefill_chunk.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, i, i, f, u8p, vp]
+    lib.attn_prefill_chunk.restype = i
+    lib.attn_prefill_chunk_check.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, i, i, f, u8p]
+    lib.attn_prefill_chunk_check.restype = i
     lib.attn_decode.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, f, u8p, vp, sz, vp]
     lib.attn_decode.restype = i
     lib.attn_decode_check.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, f, u8p, vp, sz]
@@ -56,6 +61,8 @@ def load() -> ctypes.CDLL:
     lib.attn_decode_workspace_bytes.restype = sz
     lib.attn_kv_quantize_q4.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
     lib.attn_kv_quantize_q4.restype = i
+    lib.attn_kv_quantize_q4_range.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+    lib.attn_kv_quantize_q4_range.restype = i
     lib.attn_decode_q4.argtypes = [vp, vp, vp, vp, vp, f32p, f32p, i, i, i, i, i, f, u8p, vp,
                                    sz, vp]
     lib.attn_decode_q4.restype = i
@@ -121,6 +128,28 @@ def attn_prefill(q, k, v, o, lse, causal: bool, tau: float, skip_mask=None,
     _raise(rc)
 
 
+def attn_prefill_chunk(q, k, v, o, lse, causal: bool, tau: float, skip_mask=None,
+                       stream=None) -> None:
+    """Enqueue chunked prefill: q [B,Hq,Nq,d] are the last Nq of the N
+    positions of k/v [B,Hkv,N,d]; writes o [B,Hq,Nq,d], lse [B,Hq,Nq] and, if
+    given, skip_mask [B,Hq,ceil(Nq/64),ceil(N/64)]."""
+    import torch
+    B, Hq, Nq, d = q.shape
+    Hkv, N = k.shape[1], k.shape[2]
+    _check(q, "q", torch.bfloat16, (B, Hq, Nq, d))
+    _check(k, "k", torch.bfloat16, (B, Hkv, N, d))
+    _check(v, "v", torch.bfloat16, (B, Hkv, N, d))
+    _check(o, "o", torch.float32, (B, Hq, Nq, d))
+    _check(lse, "lse", torch.float32, (B, Hq, Nq))
+    if skip_mask is not None:
+        _check(skip_mask, "skip_mask", torch.uint8,
+               (B, Hq, (Nq + TILE - 1) // TILE, (N + TILE - 1) // TILE))
+    rc = load().attn_prefill_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv,
+                                   Nq, N, d, int(bool(causal)), float(tau), _ptr(skip_mask),
+                                   _stream(stream))
+    _raise(rc)
+
+
 def attn_decode_workspace_bytes(B: int, Hq: int, L: int, d: int) -> int:
     return int(load().attn_decode_workspace_bytes(B, Hq, L, d))
 
@@ -165,18 +194,20 @@ def _check_q4(cache, B, Hkv, L, d):
         _check(cache[name], name, dt, shp[name])
 
 
-def attn_kv_quantize_q4(k, v, cache, stream=None) -> None:
+def attn_kv_quantize_q4(k, v, cache, stream=None, key_range=None) -> None:
     """Enqueue the 4-bit quantiser: k/v [B,Hkv,L,d] bf16 -> cache dict of
     kq uint8, kp int32 (parameter words), vq uint8, vp int32 tensors with the
-    shapes of q4_shapes()."""
+    shapes of q4_shapes(). ``key_range=(k0, k1)`` writes only those keys
+    (k0 a multiple of 64), e.g. a chunk appended after a chunked prefill."""
     import torch
     B, Hkv, L, d = k.shape
     _check(k, "k", torch.bfloat16, (B, Hkv, L, d))
     _check(v, "v", torch.bfloat16, (B, Hkv, L, d))
     _check_q4(cache, B, Hkv, L, d)
-    rc = load().attn_kv_quantize_q4(_ptr(k), _ptr(v), _ptr(cache["kq"]), _ptr(cache["kp"]),
-                                    _ptr(cache["vq"]), _ptr(cache["vp"]), B, Hkv, L, d,
-                                    _stream(stream))
+    k0, k1 = (0, L) if key_range is None else key_range
+    rc = load().attn_kv_quantize_q4_range(_ptr(k), _ptr(v), _ptr(cache["kq"]), _ptr(cache["kp"]),
+                                          _ptr(cache["vq"]), _ptr(cache["vp"]), B, Hkv, L, d,
+                                          int(k0), int(k1), _stream(stream))
     _raise(rc)
 
 
@@ -205,13 +236,18 @@ def attn_decode_q4(q, cache, L: int, o, lse, tau: float, workspace, skip_mask=No
 
 # ---- allocation conveniences around the entry points ----
 
+def empty_q4(B: int, Hkv: int, L: int, d: int, device) -> dict:
+    """Allocate (uninitialised) 4-bit cache arrays for L keys."""
+    import torch
+    shp = q4_shapes(B, Hkv, L, d)
+    return {n: torch.empty(shp[n], dtype=torch.uint8 if n in ("kq", "vq") else torch.int32,
+                           device=device) for n in shp}
+
+
 def quantize_q4(k, v, stream=None) -> dict:
     """Allocate a 4-bit cache with torch and fill it from bf16 k, v."""
-    import torch
     B, Hkv, L, d = k.shape
-    shp = q4_shapes(B, Hkv, L, d)
-    cache = {n: torch.empty(shp[n], dtype=torch.uint8 if n in ("kq", "vq") else torch.int32,
-                            device=k.device) for n in shp}
+    cache = empty_q4(B, Hkv, L, d, k.device)
     attn_kv_quantize_q4(k, v, cache, stream)
     return cache
 
@@ -249,6 +285,22 @@ def prefill(q, k, v, causal: bool, tau: float = math.inf, want_mask: bool = Fals
         nt = (N + TILE - 1) // TILE
         mask = torch.empty((B, Hq, nt, nt), dtype=torch.uint8, device=q.device)
     attn_prefill(q, k, v, o, lse, causal, tau, mask, stream)
+    return o, lse, mask
+
+
+def prefill_chunk(q, k, v, causal: bool, tau: float = math.inf, want_mask: bool = False,
+                  stream=None):
+    """Allocate outputs with torch and call attn_prefill_chunk. Returns (o, lse, mask)."""
+    import torch
+    B, Hq, Nq, d = q.shape
+    N = k.shape[2]
+    o = torch.empty((B, Hq, Nq, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    mask = None
+    if want_mask:
+        mask = torch.empty((B, Hq, (Nq + TILE - 1) // TILE, (N + TILE - 1) // TILE),
+                           dtype=torch.uint8, device=q.device)
+    attn_prefill_chunk(q, k, v, o, lse, causal, tau, mask, stream)
     return o, lse, mask
 
 

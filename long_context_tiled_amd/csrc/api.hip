@@ -56,13 +56,15 @@ extern "C" {
 
 const char* attn_last_error(void) { return g_err; }
 
-int attn_prefill_check(const void* q, const void* k, const void* v, const float* o,
-                       const float* lse, int B, int Hq, int Hkv, int N, int d,
-                       int causal, float tau, const uint8_t* skip_mask) {
+int attn_prefill_chunk_check(const void* q, const void* k, const void* v, const float* o,
+                             const float* lse, int B, int Hq, int Hkv, int Nq, int N, int d,
+                             int causal, float tau, const uint8_t* skip_mask) {
   (void)skip_mask;
   g_err[0] = '\0';
   if (!q || !k || !v || !o || !lse) return fail(SKIPATTN_EINVAL, "NULL tensor pointer");
-  if (B < 0 || N < 0 || d < 0) return fail(SKIPATTN_EINVAL, "negative size (B=%d N=%d d=%d)", B, N, d);
+  if (B < 0 || N < 0 || Nq < 0 || d < 0)
+    return fail(SKIPATTN_EINVAL, "negative size (B=%d Nq=%d N=%d d=%d)", B, Nq, N, d);
+  if (Nq > N) return fail(SKIPATTN_EINVAL, "Nq (%d) exceeds N (%d)", Nq, N);
   if (int e = check_heads(Hq, Hkv)) return e;
   if (causal != 0 && causal != 1) return fail(SKIPATTN_EINVAL, "causal must be 0 or 1 (got %d)", causal);
   if (int e = check_tau(tau)) return e;
@@ -74,21 +76,38 @@ int attn_prefill_check(const void* q, const void* k, const void* v, const float*
   if ((long long)N * d * 2 > kMaxHeadBytes)
     return fail(SKIPATTN_EUNSUPPORTED, "N * d * 2 = %lld bytes per head exceeds %lld", (long long)N * d * 2,
                 kMaxHeadBytes);
+  if (causal && (N - Nq) % SKIPATTN_TILE != 0)
+    return fail(SKIPATTN_EUNSUPPORTED, "causal chunk must start on a 64-key boundary (N - Nq = %d)",
+                N - Nq);
+  return SKIPATTN_OK;
+}
+
+int attn_prefill_check(const void* q, const void* k, const void* v, const float* o,
+                       const float* lse, int B, int Hq, int Hkv, int N, int d,
+                       int causal, float tau, const uint8_t* skip_mask) {
+  return attn_prefill_chunk_check(q, k, v, o, lse, B, Hq, Hkv, N, N, d, causal, tau, skip_mask);
+}
+
+int attn_prefill_chunk(const void* q, const void* k, const void* v, float* o, float* lse,
+                       int B, int Hq, int Hkv, int Nq, int N, int d, int causal, float tau,
+                       uint8_t* skip_mask, void* stream) {
+  if (int e = attn_prefill_chunk_check(q, k, v, o, lse, B, Hq, Hkv, Nq, N, d, causal, tau,
+                                       skip_mask))
+    return e;
+  if (B == 0 || Nq == 0) return SKIPATTN_OK;
+  skipattn::PrefillArgs a{q,         k,      v, o, lse, skip_mask, B, Hq, Hkv, N, d, causal,
+                          Nq,        causal ? (N - Nq) / SKIPATTN_TILE : 0,
+                          tau_raw(tau, d), exp2_scale(d), stream};
+  if (skipattn::launch_prefill(a) != 0) return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(SKIPATTN_EHIP, "prefill launch: %s", hipGetErrorString(err));
   return SKIPATTN_OK;
 }
 
 int attn_prefill(const void* q, const void* k, const void* v, float* o, float* lse,
                  int B, int Hq, int Hkv, int N, int d, int causal, float tau,
                  uint8_t* skip_mask, void* stream) {
-  if (int e = attn_prefill_check(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, tau, skip_mask))
-    return e;
-  if (B == 0 || N == 0) return SKIPATTN_OK;
-  skipattn::PrefillArgs a{q, k, v, o, lse, skip_mask, B, Hq, Hkv, N, d, causal,
-                          tau_raw(tau, d), exp2_scale(d), stream};
-  if (skipattn::launch_prefill(a) != 0) return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return fail(SKIPATTN_EHIP, "prefill launch: %s", hipGetErrorString(err));
-  return SKIPATTN_OK;
+  return attn_prefill_chunk(q, k, v, o, lse, B, Hq, Hkv, N, N, d, causal, tau, skip_mask, stream);
 }
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int L, int d) {
@@ -176,12 +195,15 @@ int attn_decode_q4(const void* q, const uint8_t* kq, const uint32_t* kp, const u
   return SKIPATTN_OK;
 }
 
-int attn_kv_quantize_q4(const void* k, const void* v, uint8_t* kq, uint32_t* kp, uint8_t* vq,
-                        uint32_t* vp, int B, int Hkv, int L, int d, void* stream) {
+int attn_kv_quantize_q4_range(const void* k, const void* v, uint8_t* kq, uint32_t* kp,
+                              uint8_t* vq, uint32_t* vp, int B, int Hkv, int L, int d, int k0,
+                              int k1, void* stream) {
   g_err[0] = '\0';
   if (!k || !v || !kq || !kp || !vq || !vp) return fail(SKIPATTN_EINVAL, "NULL tensor pointer");
   if (B < 0 || L < 0 || d < 0) return fail(SKIPATTN_EINVAL, "negative size (B=%d L=%d d=%d)", B, L, d);
   if (Hkv < 1) return fail(SKIPATTN_EINVAL, "Hkv must be >= 1 (got %d)", Hkv);
+  if (k0 < 0 || k1 < k0 || k1 > L)
+    return fail(SKIPATTN_EINVAL, "key range [%d, %d) outside [0, %d]", k0, k1, L);
   if (!aligned16(k) || !aligned16(v) || !aligned16(kq) || !aligned16(kp) || !aligned16(vq) ||
       !aligned16(vp))
     return fail(SKIPATTN_EINVAL, "every pointer must be 16-byte aligned");
@@ -191,12 +213,19 @@ int attn_kv_quantize_q4(const void* k, const void* v, uint8_t* kq, uint32_t* kp,
   if ((long long)L * d * 2 > kMaxHeadBytes)
     return fail(SKIPATTN_EUNSUPPORTED, "L * d * 2 = %lld bytes per head exceeds %lld", (long long)L * d * 2,
                 kMaxHeadBytes);
-  if (B == 0 || L == 0) return SKIPATTN_OK;
-  skipattn::QuantArgs a{k, v, kq, kp, vq, vp, B, Hkv, L, d, stream};
+  if (k0 % SKIPATTN_TILE != 0)
+    return fail(SKIPATTN_EUNSUPPORTED, "k0 (%d) must be a multiple of 64", k0);
+  if (B == 0 || k1 == k0) return SKIPATTN_OK;
+  skipattn::QuantArgs a{k, v, kq, kp, vq, vp, B, Hkv, L, d, k0, k1, stream};
   if (skipattn::launch_kv_quantize_q4(a) != 0) return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(SKIPATTN_EHIP, "quantize launch: %s", hipGetErrorString(err));
   return SKIPATTN_OK;
+}
+
+int attn_kv_quantize_q4(const void* k, const void* v, uint8_t* kq, uint32_t* kp, uint8_t* vq,
+                        uint32_t* vp, int B, int Hkv, int L, int d, void* stream) {
+  return attn_kv_quantize_q4_range(k, v, kq, kp, vq, vp, B, Hkv, L, d, 0, L < 0 ? 0 : L, stream);
 }
 
 }  // extern "C"

@@ -89,16 +89,18 @@ __device__ __forceinline__ uint32_t pack_params(float s, float z) {
 // ---------------------------------------------------------------- quantiser
 // K: W = D/8 lanes per key row, each lane one word (8 elements, 16 bytes of
 // bf16 in, 4 bytes of codes out); the row's min and max by xor shuffles.
+// Rows are the keys k0 .. k1 - 1 of every (b, g) of a cache holding L keys.
 template <int D>
 __global__ __launch_bounds__(256) void quant_k_kernel(const uint16_t* __restrict__ k,
                                                       uint8_t* __restrict__ kq,
                                                       uint32_t* __restrict__ kp,
-                                                      long long rows) {
+                                                      long long rows, int L, int k0, int nk) {
   constexpr int W = D / 8;
   const int lane = threadIdx.x & 63;
-  const long long row = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / W) + lane / W;
+  const long long idx = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / W) + lane / W;
   const int w = lane % W;
-  const bool ok = row < rows;
+  const bool ok = idx < rows;
+  const long long row = ok ? (idx / nk) * L + k0 + idx % nk : 0;  // key row in the cache
   float x[8];
   if (ok) {
     const u32x4 r = *reinterpret_cast<const u32x4*>(k + row * D + 8 * w);
@@ -134,15 +136,17 @@ __global__ __launch_bounds__(256) void quant_k_kernel(const uint16_t* __restrict
 // V: one thread per channel of one 64-key tile (block = one (b, g, tile)).
 // One pass: the tile's 64 values of the channel stay in registers (loads of
 // one key row are coalesced across the block's threads), and the channel's
-// 32-byte code row goes out as two 16-byte stores.
+// 32-byte code row goes out as two 16-byte stores. Tiles t0 .. t0 + nt - 1
+// of a cache of T tiles; a tile holds its keys below k1.
 template <int D>
 __global__ __launch_bounds__(D) void quant_v_kernel(const uint16_t* __restrict__ v,
                                                     uint8_t* __restrict__ vq,
-                                                    uint32_t* __restrict__ vp, int L, int T) {
+                                                    uint32_t* __restrict__ vp, int L, int T,
+                                                    int t0, int nt, int k1) {
   const int ch = threadIdx.x;
-  const long long bg = blockIdx.x / T;
-  const int t = blockIdx.x % T;
-  const int n = min(kTile, L - kTile * t);
+  const long long bg = blockIdx.x / nt;
+  const int t = t0 + blockIdx.x % nt;
+  const int n = min(kTile, k1 - kTile * t);
   const uint16_t* src = v + (bg * L + (long long)kTile * t) * D + ch;
   float x[kTile];
 #pragma unroll
@@ -504,16 +508,19 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
 
 template <int D>
 int launch_q_d(const QuantArgs& a) {
-  const long long rows = (long long)a.B * a.Hkv * a.L;
+  const int nk = a.k1 - a.k0;
+  const long long rows = (long long)a.B * a.Hkv * nk;
   const long long waves = (rows + (64 / (D / 8)) - 1) / (64 / (D / 8));
   const long long g1 = (waves + 3) / 4;
   const int T = (a.L + kTile - 1) / kTile;
-  const long long g2 = (long long)a.B * a.Hkv * T;
+  const int t0 = a.k0 / kTile;
+  const int nt = (a.k1 + kTile - 1) / kTile - t0;
+  const long long g2 = (long long)a.B * a.Hkv * nt;
   if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return -1;
   hipLaunchKernelGGL((quant_k_kernel<D>), dim3((unsigned)g1), dim3(256), 0, (hipStream_t)a.stream,
-                     (const uint16_t*)a.k, a.kq, a.kp, rows);
+                     (const uint16_t*)a.k, a.kq, a.kp, rows, a.L, a.k0, nk);
   hipLaunchKernelGGL((quant_v_kernel<D>), dim3((unsigned)g2), dim3(D), 0, (hipStream_t)a.stream,
-                     (const uint16_t*)a.v, a.vq, a.vp, a.L, T);
+                     (const uint16_t*)a.v, a.vq, a.vp, a.L, T, t0, nt, a.k1);
   return 0;
 }
 

@@ -14,6 +14,8 @@ struct PrefillArgs {
   float* lse;
   uint8_t* mask;
   int B, Hq, Hkv, N, d, causal;
+  int Nq;         // queries: key positions N - Nq .. N - 1 (Nq == N: self-attention)
+  int q0t;        // (N - Nq) / 64
   float tau_raw;  // tau * sqrt(d): threshold in raw q.k units (+inf = dense)
   float c;        // log2(e) / sqrt(d)
   void* stream;
@@ -42,6 +44,7 @@ struct QuantArgs {
   uint8_t* vq;
   uint32_t* vp;
   int B, Hkv, L, d;
+  int k0, k1;     // keys written: k0 .. k1 - 1 (k0 a multiple of 64)
   void* stream;
 };
 

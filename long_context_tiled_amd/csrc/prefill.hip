@@ -148,7 +148,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ o,
     float* __restrict__ lse, uint8_t* __restrict__ mask, int Hq, int Hkv,
-    int N, float tau_raw, float c, int nqg, int ny) {
+    int Nq, int N, int q0t, float tau_raw, float c, int nqg, int ny) {
+  // Nq queries (the chunk) at key positions 64 q0t .. 64 q0t + Nq - 1 of N
+  // keys: query tile qb of the chunk is tile qb + q0t of the key axis.
   constexpr int QPW = 4 / HPW;   // query tiles per workgroup
   constexpr int MB = D / 32;     // 32-row d blocks of O^T
   using T = PrefillTile<D>;
@@ -175,11 +177,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
   const int rem = y % (Hkv * gper);
   const int g = rem / gper;
   const int h = g * G + (rem % gper) * HPW + (wave % HPW);
-  const int qb = qg * QPW + wave / HPW;
-  const int nqb = (N + kTile - 1) / kTile;
+  const int qb = qg * QPW + wave / HPW;   // query tile within the chunk
+  const int qbg = qb + q0t;               // the same tile on the key axis
+  const int nqb = (Nq + kTile - 1) / kTile;
+  const int nkb = (N + kTile - 1) / kTile;
   const bool wave_valid = qb < nqb;
-  const int nkb_wg = CAUSAL ? min(nqb, qg * QPW + QPW) : nqb;
-  const int nkb_w = wave_valid ? (CAUSAL ? qb + 1 : nqb) : 0;
+  const int nkb_wg = CAUSAL ? min(nkb, qg * QPW + QPW + q0t) : nkb;
+  const int nkb_w = wave_valid ? (CAUSAL ? qbg + 1 : nkb) : 0;
 
   const int head_bytes = N * D * 2;
   const size_t kv_off = (size_t)(b * Hkv + g) * N * D;
@@ -189,7 +193,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
       __builtin_amdgcn_make_buffer_rsrc((void*)(v + kv_off), (short)0, head_bytes, kBufferCfg);
   const size_t bh = (size_t)b * Hq + h;
   const __amdgpu_buffer_rsrc_t qrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(q + bh * N * D), (short)0, head_bytes, kBufferCfg);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(q + bh * Nq * D), (short)0, Nq * D * 2, kBufferCfg);
 
   // Per-lane load geometry for the direct-to-LDS copies: instruction i of
   // wave w fills LDS bytes [1024 (w * IPW + i), +1024) of the tile.
@@ -279,15 +283,16 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
   }
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const int qrow = qb * kTile + nb * 32 + l32;
-    const int last = CAUSAL ? min(N - 1, qrow) : N - 1;  // last key this row may see
+    const int qrow = qb * kTile + nb * 32 + l32;  // row within the chunk
+    const int qpos = qbg * kTile + nb * 32 + l32; // its key position
+    const int last = CAUSAL ? min(N - 1, qpos) : N - 1;  // last key this row may see
     la.lim_base[nb] = last - 4 * hh;
-    la.val[nb] = __ballot(qrow < N);
+    la.val[nb] = __ballot(qrow < Nq);
   }
   la.lazy = lazy_raw;
   la.nkb_wg = nkb_wg;
   la.nkb_w = __builtin_amdgcn_readfirstlane(nkb_w);
-  la.qb = __builtin_amdgcn_readfirstlane(qb);
+  la.qb = __builtin_amdgcn_readfirstlane(qbg);  // the diagonal tile
   la.N = N;
   la.tau = tau_raw;
   la.c = c;
@@ -304,7 +309,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
   la.vrs = rsrc(v + kv_off);
   la.wl = smem_lds + (uint32_t)(wave * IPW * 1024);
   la.smem = smem_lds;
-  la.mask_row = mask != nullptr ? (uint64_t)(uintptr_t)(mask + (bh * nqb + qb) * nqb) : 0ull;
+  la.mask_row = mask != nullptr ? (uint64_t)(uintptr_t)(mask + (bh * nqb + qb) * nkb) : 0ull;
   float m[2], mref[2], lsum[2];
   if constexpr (CAUSAL) SKA_CALL(D, key_loop_causal, la, m, mref, lsum);
   else SKA_CALL(D, key_loop_full, la, m, mref, lsum);
@@ -333,8 +338,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
         if (id == 6) d128::read_o_30(ov);
         if (id == 7) d128::read_o_31(ov);
       }
-      if (row < N) {
-        float* orow = o + (bh * N + row) * D;
+      if (row < Nq) {
+        float* orow = o + (bh * Nq + row) * D;
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           f32x4 val;
@@ -344,11 +349,11 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
         }
       }
     }
-    if (row < N && hh == 0) lse[bh * N + row] = (mref[nb] * c + __log2f(ltot)) * kLn2;
+    if (row < Nq && hh == 0) lse[bh * Nq + row] = (mref[nb] * c + __log2f(ltot)) * kLn2;
   }
   if (CAUSAL && mask != nullptr) {
-    for (int kb = qb + 1 + lane; kb < nqb; kb += 64)
-      mask[(bh * nqb + qb) * nqb + kb] = 2;
+    for (int kb = qbg + 1 + lane; kb < nkb; kb += 64)
+      mask[(bh * nqb + qb) * nkb + kb] = 2;
   }
 }
 
@@ -356,7 +361,7 @@ constexpr int kStages = 5;
 
 template <int D, bool CAUSAL, int HPW>
 static int launch_one(const PrefillArgs& a) {
-  const int nqb = (a.N + kTile - 1) / kTile;
+  const int nqb = (a.Nq + kTile - 1) / kTile;
   constexpr int QPW = 4 / HPW;
   const int nqg = (nqb + QPW - 1) / QPW;
   const int G = a.Hq / a.Hkv;
@@ -365,7 +370,7 @@ static int launch_one(const PrefillArgs& a) {
   if (blocks > 0x7fffffffLL) return -1;
   hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, HPW, kStages>), dim3((unsigned)blocks), dim3(256),
                      0, (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                     (const uint16_t*)a.v, a.o, a.lse, a.mask, a.Hq, a.Hkv, a.N,
+                     (const uint16_t*)a.v, a.o, a.lse, a.mask, a.Hq, a.Hkv, a.Nq, a.N, a.q0t,
                      a.tau_raw, a.c, nqg, ny);
   return 0;
 }

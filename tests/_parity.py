@@ -76,7 +76,9 @@ def _compare_decisions(gpu_dec, ref_dec, margin, visited):
 class PrefillChecker:
     """Caches fp64 copies of K/V per (b, kv head) for repeated block checks."""
 
-    def __init__(self, q_bits, k_bits, v_bits, causal: bool):
+    def __init__(self, q_bits, k_bits, v_bits, causal: bool, q0: int = 0):
+        """q_bits may be a chunk: its row r sits at key position q0 + r
+        (q0 a multiple of 64 when causal)."""
         self.q, self.k, self.v = q_bits, k_bits, v_bits
         self.causal = causal
         B, Hq, N, d = q_bits.shape
@@ -84,6 +86,7 @@ class PrefillChecker:
         self.Hkv = k_bits.shape[1]
         self.G = Hq // self.Hkv
         self.nt = (N + 63) // 64
+        self.q0t = q0 // 64
         self._kv = {}
 
     def kv(self, b, g):
@@ -101,7 +104,7 @@ class PrefillChecker:
         k, v = self.kv(b, h // self.G)
         r0, r1 = qb * 64, min(self.N, qb * 64 + 64)
         qrows = synth.bf16_bits_to_f64(self.q[b, h, r0:r1])
-        o, lse, dec, margin = oracle.prefill_blocks(qrows, k, v, qb, self.causal, tau)
+        o, lse, dec, margin = oracle.prefill_blocks(qrows, k, v, qb + self.q0t, self.causal, tau)
         dec, margin = dec[0], margin[0]
         visited = dec != oracle.NOT_VISITED
         if not np.array_equal(mask_gpu[~visited], dec[~visited]):
@@ -115,7 +118,7 @@ class PrefillChecker:
             bad = np.nonzero((mask_gpu != dec) & visited)[0][:4]
             rep.notes.append(f"b={b} h={h} qb={qb} kb={bad.tolist()} margin={margin[bad].tolist()}")
         if forced is not None:
-            o, lse, _, _ = oracle.prefill_blocks(qrows, k, v, qb, self.causal, tau,
+            o, lse, _, _ = oracle.prefill_blocks(qrows, k, v, qb + self.q0t, self.causal, tau,
                                                  forced[None, :])
         rep.tiles += int(visited.sum())
         rep.skipped += int((mask_gpu[visited] == 1).sum())
@@ -124,9 +127,11 @@ class PrefillChecker:
         return rep
 
 
-def check_prefill(q_bits, k_bits, v_bits, causal, tau, o, lse, mask, blocks=None) -> Report:
-    """Compare full GPU outputs (numpy) over the given (b, h, qb) blocks."""
-    chk = PrefillChecker(q_bits, k_bits, v_bits, causal)
+def check_prefill(q_bits, k_bits, v_bits, causal, tau, o, lse, mask, blocks=None,
+                  q0: int = 0) -> Report:
+    """Compare full GPU outputs (numpy) over the given (b, h, qb) blocks
+    (q_bits and the outputs may be a chunk starting at key position q0)."""
+    chk = PrefillChecker(q_bits, k_bits, v_bits, causal, q0)
     if blocks is None:
         blocks = [(b, h, qb) for b in range(chk.B) for h in range(chk.Hq)
                   for qb in range(chk.nt)]

@@ -145,3 +145,32 @@ def test_quantise_q4_rejects_before_any_launch():
 def test_q4_shapes():
     s = lib.q4_shapes(2, 3, 130, 64)
     assert s == dict(kq=(2, 3, 130, 32), kp=(2, 3, 130), vq=(2, 3, 3, 64, 32), vp=(2, 3, 3, 64))
+
+
+def _ccheck(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=8, Hkv=2, Nq=512, N=4096, d=128, causal=1,
+             tau=4.0, mask=None)
+    a.update(kw)
+    return lib.load().attn_prefill_chunk_check(a["q"], a["k"], a["v"], a["o"], a["lse"],
+                                               a["B"], a["Hq"], a["Hkv"], a["Nq"], a["N"],
+                                               a["d"], a["causal"], a["tau"], a["mask"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, 0), ({"Nq": 4096}, 0), ({"Nq": 0}, 0), ({"Nq": 64, "N": 4160}, 0),
+    ({"Nq": 100, "N": 164}, 0), ({"Nq": 100, "N": 4096, "causal": 0}, 0),
+    ({"Nq": 4097}, 1), ({"Nq": -1}, 1), ({"q": None}, 1), ({"causal": 3}, 1),
+    ({"Nq": 100, "N": 4096}, 2), ({"Nq": 1, "N": 4096}, 2), ({"d": 96}, 2),
+])
+def test_prefill_chunk_validation(kw, code):
+    assert _ccheck(**kw) == code
+
+
+def test_quantise_q4_range_rejects_before_any_launch():
+    so = lib.load()
+    r = so.attn_kv_quantize_q4_range
+    assert r(P, P, P, P, P, P, 1, 8, 4096, 128, 64, 64, None) == lib.OK       # empty range
+    assert r(P, P, P, P, P, P, 1, 8, 4096, 128, 10, 100, None) == lib.EUNSUPPORTED
+    assert r(P, P, P, P, P, P, 1, 8, 4096, 128, 128, 64, None) == lib.EINVAL
+    assert r(P, P, P, P, P, P, 1, 8, 4096, 128, 0, 4097, None) == lib.EINVAL
+    assert r(P, P, P, P, P, P, 1, 8, 4096, 128, -64, 64, None) == lib.EINVAL

@@ -170,3 +170,30 @@ def test_decode_q4_workload_sampled():
         print(f"  skip_fraction={(mask_np == 1).mean():.4f} {rep}", flush=True)
         assert rep.ok(), str(rep)
         del o, lse, mask
+
+
+def test_quantiser_key_ranges_compose():
+    # chunk by chunk (k0 on tile boundaries, a partial tile rewritten later)
+    # gives the same bytes as one call; the state after a prefix equals the
+    # oracle's encoding of that prefix
+    import torch
+    import long_context_tiled_amd as lib
+    k, v = _rand_kv(2, 2, 1000, 128, 21)
+    dk, dv = _dev(k), _dev(v)
+    whole = _host(lib.quantize_q4(dk, dv))
+    for ranges in (((0, 512), (512, 1000)), ((0, 700), (640, 1000)), ((0, 64), (64, 65), (64, 1000))):
+        print(f"[q4] ranges {ranges}", flush=True)
+        cache = lib.empty_q4(2, 2, 1000, 128, dk.device)
+        for i, (k0, k1) in enumerate(ranges):
+            lib.attn_kv_quantize_q4(dk, dv, cache, key_range=(k0, k1))
+            if i == 0:
+                torch.cuda.synchronize()
+                part = _host(cache)
+                want = kvq4.encode(synth.bf16_bits_to_f32(k[:, :, :k1]),
+                                   synth.bf16_bits_to_f32(v[:, :, :k1]))
+                T1 = (k1 + 63) // 64
+                got = dict(kq=part["kq"][:, :, :k1], kp=part["kp"][:, :, :k1],
+                           vq=part["vq"][:, :, :T1], vp=part["vp"][:, :, :T1])
+                _assert_same_cache(got, want, f"prefix {k1}")
+        torch.cuda.synchronize()
+        _assert_same_cache(_host(cache), whole, str(ranges))
