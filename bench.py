@@ -46,14 +46,14 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # figure no longer applies and is reported as null.
 MEASURED_TRAFFIC = {
     "prefill": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp"),
-                "sha1": "bb8e13ccc508b0fbc4315f4bd92234855ff4a0fa",
-                "bytes": (2784622.6 * 2.0 + 528384.0) * 1024},
+                "sha1": "a1e0b55fc23192d5c213c22fef57275f2dda1810",
+                "bytes": (3216218.7 * 2.0 + 528384.0) * 1024},
     "decode_q4": {"sources": ("kvq4.hip", "decode.hip", "common.hpp"),
-                  "sha1": "63b8d2d4eb8c126158cf04284f84a49cead20eb4",
-                  "bytes": (1148101.7 * 2.0 + 16640.3) * 1024},
+                  "sha1": "0fb1c7f54a42426359088c3578c9cca80deaa744",
+                  "bytes": (1148100.4 * 2.0 + 16640.1) * 1024},
     "decode": {"sources": ("decode.hip", "common.hpp"),
                "sha1": "642a5529eba59c233ecfeeab8f85092e500c5ce1",
-               "bytes": (4195501.2 * 2.0 + 16641.4) * 1024},
+               "bytes": (4195500.0 * 2.0 + 16642.0) * 1024},
 }
 
 
@@ -161,7 +161,20 @@ def _cpu_decode_head(job):
         oracle.decode_head(synth.bf16_bits_to_f64(q[hh]), k, v, math.inf)
 
 
-def cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=768, nkv=32):
+def _cpu_decode_q4_head(i):
+    from threadpoolctl import threadpool_limits
+    import oracle
+    import synth
+    from oracle import kvq4
+    with threadpool_limits(1):
+        e, q, L = _CPU["dq4"][i]
+        k = kvq4.decode_k(e["kq"], e["kp"])
+        v = kvq4.decode_v(e["vq"], e["vp"], L)
+        for hh in range(q.shape[0]):
+            oracle.decode_head(synth.bf16_bits_to_f64(q[hh]), k, v, math.inf)
+
+
+def cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=768, nkv=32, nkv_q4=16):
     """The fp64 oracle as it stands, timed on a bounded sample of each
     workload with one process per host core (fp64 widening of the inputs is
     done before the clock starts)."""
@@ -181,6 +194,10 @@ def cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=768, nkv=32):
     picks = [(b, g) for b in range(B) for g in range(Hkv)][:nkv]
     _CPU["dkv"] = [(synth.bf16_bits_to_f64(dk[b, g]), synth.bf16_bits_to_f64(dv[b, g]),
                     dq[b, g * G:(g + 1) * G]) for b, g in picks]
+    from oracle import kvq4
+    picks4 = picks[:nkv_q4]
+    _CPU["dq4"] = [(kvq4.encode(synth.bf16_bits_to_f32(dk[b, g]), synth.bf16_bits_to_f32(dv[b, g])),
+                    dq[b, g * G:(g + 1) * G], L) for b, g in picks4]
     ctx = mp.get_context("fork")
     with ctx.Pool(cores) as pool:
         t0 = time.perf_counter()
@@ -190,6 +207,9 @@ def cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=768, nkv=32):
         pool.map(_cpu_decode_head, [(i, hh) for i in range(len(picks)) for hh in range(G)],
                  chunksize=1)
         dwall = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        pool.map(_cpu_decode_q4_head, list(range(len(picks4))), chunksize=1)
+        qwall = time.perf_counter() - t0
     _CPU.clear()
     pairs = sum(64 * (qb * 64) + 64 * 65 // 2 for qb in qbs)
     pre = dict(value=float(4.0 * d * pairs / pwall / 1e12), unit="TFLOP/s", cores=cores,
@@ -200,7 +220,11 @@ def cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=768, nkv=32):
     dec = dict(value=float(kv_bytes / dwall / 1e9), unit="GB/s", cores=cores, kind="oracle",
                sample=f"decode_128k: {len(picks)} KV heads x {G} query heads, tau=inf, "
                       f"fp64 numpy, {dwall:.1f} s wall")
-    return pre, dec
+    q4b = len(picks4) * float(L * (d // 2 + 4) + ((L + 63) // 64) * 36 * d)
+    dq4 = dict(value=float(q4b / qwall / 1e9), unit="GB/s", cores=cores, kind="oracle",
+               sample=f"decode_128k over the 4-bit cache: {len(picks4)} KV heads x {G} query "
+                      f"heads, dequantise + fp64 decode oracle, tau=inf, {qwall:.1f} s wall")
+    return pre, dec, dq4
 
 
 # ---------------------------------------------------------------------- main
@@ -425,9 +449,10 @@ def main():
 
     if not args.no_cpu:
         print("# cpu baseline (fp64 oracle on a bounded sample)", file=sys.stderr, flush=True)
-        pre, dec = cpu_baseline(pq, pk, pv, dq, dk, dv)
-        out["cpu_baseline"] = pre if run_p else dec
+        pre, dec, dq4 = cpu_baseline(pq, pk, pv, dq, dk, dv)
+        out["cpu_baseline"] = pre if run_p else (dec if run_d else dq4)
         out["cpu_baseline_decode"] = dec
+        out["cpu_baseline_decode_q4"] = dq4
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
