@@ -83,6 +83,7 @@ TREG = 48     # exp temporaries, three pairs v[48:53]
 VADR = 54     # V^T read addresses, v[54 : 54 + 2 MB)
 KADR = 62     # K read addresses, v62 / v63 alternating
 VOTE = 40     # vote temporaries, v[40:46)
+PSUM = 46     # this tile's partial row sums, v46 (query half 0) and v47 (half 1)
 OB = 64       # first AGPR of O^T
 COMPILER_VGPRS = 40  # v[0:40) and a[0:40) stay with the compiler
 
@@ -230,8 +231,13 @@ class Step:
                    tag=("pv", ks))
 
     def exp_stream(self):
-        """Per score pair: scale-and-shift, exp2, row-sum, pack to bf16."""
+        """Per score pair: scale-and-shift, exp2, pack to bf16, pair sum into
+        this tile's partial row sum; at the end each partial sum joins the
+        running row sum once. (Adding every exponential straight into the
+        running sum loses the small terms once that sum is large: over
+        millions of keys the row sum, and so the LSE, came out low.)"""
         out = []
+        first = {0: True, 1: True}
         for gp in range(32):
             ch, i2 = gp >> 2, gp & 3
             kp, nb = ch >> 1, ch & 1
@@ -242,18 +248,25 @@ class Step:
             t0 = f"v{TREG + 2 * (gp % 3)}"
             t1 = f"v{TREG + 2 * (gp % 3) + 1}"
             w = f"v{PREG + 4 * (2 * kp + nb) + i2}"
-            ls = f"%[lo{nb}]"
+            ps = f"v{PSUM + nb}"
             nm = f"%[nm{nb}]"
             out += [
                 Ins(f"v_fma_f32 {t0}, {s0}, %[c], {nm}", "valu", wr=[t0], rd=[s0]),
                 Ins(f"v_fma_f32 {t1}, {s1}, %[c], {nm}", "valu", wr=[t1], rd=[s1]),
                 Ins(f"v_exp_f32 {t0}, {t0}", "trans", wr=[t0], rd=[t0]),
                 Ins(f"v_exp_f32 {t1}, {t1}", "trans", wr=[t1], rd=[t1]),
-                Ins(f"v_add_f32 {ls}, {ls}, {t0}", "valu", rd=[t0]),
                 Ins(f"v_cvt_pk_bf16_f32 {w}, {t0}, {t1}", "valu", wr=[w], rd=[t0, t1],
                     tag=("pf", kp)),
-                Ins(f"v_add_f32 {ls}, {ls}, {t1}", "valu", rd=[t1]),
             ]
+            if first[nb]:
+                out.append(Ins(f"v_add_f32 {ps}, {t0}, {t1}", "valu", wr=[ps], rd=[t0, t1]))
+                first[nb] = False
+            else:
+                out += [Ins(f"v_add_f32 {t0}, {t0}, {t1}", "valu", wr=[t0], rd=[t0, t1]),
+                        Ins(f"v_add_f32 {ps}, {ps}, {t0}", "valu", wr=[ps], rd=[ps, t0])]
+        for nb in range(2):
+            out.append(Ins(f"v_add_f32 %[lo{nb}], %[lo{nb}], v{PSUM + nb}", "valu",
+                           rd=[f"v{PSUM + nb}"]))
         return out
 
     def max_stream(self):
@@ -519,7 +532,7 @@ class Step:
             outs += ['[lo0] "=&v"(lo[0])', '[lo1] "=&v"(lo[1])']
             ins_ += ['[li0] "v"(lsum[0])', '[li1] "v"(lsum[1])', '[nm0] "v"(nmc[0])', '[nm1] "v"(nmc[1])', '[c] "s"(c)', '[vb0] "v"(vb0)',
                      '[vb1] "v"(vb1)']
-        clob = [f"v{r}" for r in range(TREG, 128)]
+        clob = [f"v{r}" for r in range(PSUM, 128)]
         if self.qk:
             clob += [f"v{VOTE + i}" for i in range(6)] + ["scc"]
             clob += [f"v{r}" for r in range(SBUF[self.y], SBUF[self.y] + 64)]
@@ -881,7 +894,7 @@ def loop_cxx(d, causal, budget):
              '[tau] "s"(a.tau)', '[c] "s"(a.c)', '[krs] "s"(a.krs)', '[vrs] "s"(a.vrs)',
              '[wl] "s"(a.wl)', '[smem] "s"(a.smem)', '[mptr] "s"(a.mask_row)',
              '[val0] "s"(a.val[0])', '[val1] "s"(a.val[1])']
-    clob = [f"v{r}" for r in range(VOTE, VOTE + 6)] + [f"v{r}" for r in range(TREG, 256)]
+    clob = [f"v{r}" for r in range(VOTE, 256)]
     clob += [f"a{r}" for r in range(OB, OB + 32 * MB)] + ["vcc", "scc", "m0"]
     body = []
     for t in L:
