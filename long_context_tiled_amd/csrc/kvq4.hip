@@ -32,10 +32,12 @@
 //   fp16 integers (the 0x6400 | c trick, then the 1024 offset removed by a
 //   packed fp16 add or fma), so the offset never meets P's rounding:
 //   sum_j p_j v^_jc = s_c (P.c) + z_c sum(P), with sum(P) again from an MFMA
-//   over the same fp16 P.
+//   over the same fp16 P. P is that product's A operand and the codes its B
+//   operand, so O comes out head-major and each lane needs the parameter of
+//   one channel per 16-channel block.
 //   Key order inside a tile: S^T row 4 grp + r of block mb holds key
 //   16 grp + 4 mb + r, so lane (head, grp) owns keys 16 grp .. 16 grp + 15 and
-//   its P^T fragment for PV k-step ks is keys 16 grp + 8 ks .. + 7, which is
+//   its P fragment for PV k-step ks is keys 16 grp + 8 ks .. + 7, which is
 //   word 2 grp + ks of every V code row. The K fragment row m of block mb is
 //   then key 16 (m >> 2) + 4 mb + (m & 3), and lane group grp reads d range
 //   [grp d/4, (grp + 1) d/4) of it, k-step ks taking word ks of that range.
@@ -184,6 +186,10 @@ __device__ __forceinline__ u32x4 ld4(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, AUX));
 }
 template <int AUX>
+__device__ __forceinline__ uint32_t ld1(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(rs, (int)off, 0, AUX);
+}
+template <int AUX>
 __device__ __forceinline__ u32x2 ld2(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, AUX));
 }
@@ -309,15 +315,19 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
 
   // Per-tile registers: K codes (block mb: KS words of row 16 (hl >> 2) +
   // 4 mb + (hl & 3)), K parameters (keys 16 grp + 4 j .. + 3), V codes
-  // (block db: words 2 grp, 2 grp + 1 of channel row 16 db + hl) and V
-  // parameters (channels 16 db + 4 grp .. + 3).
+  // (block db: words 2 grp, 2 grp + 1 of channel row 16 db + hl) and the V
+  // parameter of channel 16 db + hl. V has two register sets, so the V of
+  // tile t + 1 is in flight while the PV of tile t waits for its own.
   struct KSet {
     uint32_t c[4][KS];
     u32x4 p[4];
   };
+  struct VSet {
+    u32x2 c[DB];
+    uint32_t p[DB];
+  };
   KSet ka, kb;  // K of even tiles in ka, of odd tiles in kb
-  u32x2 vc[DB];
-  u32x4 vpr[DB];
+  VSet va, vb;  // V of even tiles in va, of odd tiles in vb
   const int krow = 16 * (hl >> 2) + (hl & 3);
   auto kload = [&](KSet& ks_, int t) {
     const uint32_t tb = t < ntile ? (uint32_t)(key_begin + t * kTile) : 0u;
@@ -338,15 +348,15 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) ks_.p[j] = ld4<kRT>(kprs, no + (tb + 16 * grp + 4 * j) * 4);
   };
-  auto vload = [&](int t, bool want) {
+  auto vload = [&](VSet& vs, int t, bool want) {
     const bool rd = want && t < ntile;
     const uint32_t tile = rd ? (uint32_t)(tile_begin + t) : 0u;
     const uint32_t no = rd ? 0u : kNoRead;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      vc[db] = ld2<kNT>(vrs, no + ((tile * D + 16 * db + hl) * 32 + 8 * grp));
-      vpr[db] = ld4<kRT>(vprs, no + (tile * D + 16 * db + 4 * grp) * 4);
-    }
+    for (int db = 0; db < DB; ++db)
+      vs.c[db] = ld2<kNT>(vrs, no + ((tile * D + 16 * db + hl) * 32 + 8 * grp));
+#pragma unroll
+    for (int db = 0; db < DB; ++db) vs.p[db] = ld1<kRT>(vprs, no + (tile * D + 16 * db + hl) * 4);
   };
 
   // Scores of one tile (raw q.k^ units), masked past L, and the tile max.
@@ -383,6 +393,9 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
     return fmaxf(x, xor32(x));
   };
 
+  // O accumulator: acc[db][r] = O[head 4 grp + r][channel 16 db + hl]
+  // (P is the A operand of the PV product, the V codes the B operand). The
+  // running max, the row sum and the skip state stay per head hl.
   f32x4 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -398,11 +411,18 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
     else skipped |= 1ull << t;
     return __ballot(keep && head_ok) != 0ull;
   };
+  // value of head 4 grp + r, from the lane of grp 0 that holds it per head
+  const int hsrc = 16 * grp;  // byte address of lane 4 grp, for ds_bpermute
+  auto of_head = [&](float x, int r) -> float {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                         hsrc + 4 * r, __builtin_bit_cast(int, x)));
+  };
 
-  // K runs two tiles ahead of the scores and V one tile ahead of the PV; the
-  // K of a later tile always goes out before the V of an earlier one, and
-  // every step issues the same loads (kNoRead for the unwanted ones), so the
-  // compiler's wait counts keep the rest in flight.
+  // K runs two tiles ahead of the scores and V one tile ahead of the PV; in
+  // every step the V of tile t + 1 and the K of tile t + 3 go out before the
+  // PV of tile t waits for its V, and every step issues the same loads
+  // (kNoRead for the unwanted ones), so the compiler's wait counts keep the
+  // later loads in flight.
   kload(ka, 0);
   kload(kb, 1);
   __builtin_amdgcn_sched_barrier(0);
@@ -410,14 +430,15 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
   float t_cur = scores(ka, 0, s_cur);
   bool keep_cur;
   bool any_cur = decide(t_cur, 0, keep_cur);
+  vload(va, 0, any_cur);
+  __builtin_amdgcn_sched_barrier(0);
   kload(ka, 2);
   __builtin_amdgcn_sched_barrier(0);
-  vload(0, any_cur);
 
   // One tile: scores and decision of tile t + 1 (K in kn, which then takes
-  // tile t + 3), exp/PV of tile t, V of tile t + 1. A step past the last tile
-  // issues only loads that read nothing.
-  auto step = [&](int t, KSet& kn) {
+  // tile t + 3, V into vn), exp/PV of tile t (V in vc). A step past the last
+  // tile issues only loads that read nothing.
+  auto step = [&](int t, KSet& kn, const VSet& vc, VSet& vn) {
     f32x4 s_nx[4];
     float t_nx = -INFINITY;
     bool keep_nx = false, any_nx = false;
@@ -425,18 +446,22 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
       t_nx = scores(kn, t + 1, s_nx);
       any_nx = decide(t_nx, t + 1, keep_nx);
     }
+    vload(vn, t + 1, any_nx);
+    __builtin_amdgcn_sched_barrier(0);
     kload(kn, t + 3);
     __builtin_amdgcn_sched_barrier(0);
     if (any_cur) {
       const float mn = keep_cur ? fmaxf(m_ref, t_cur) : m_ref;
-      if (mn > m_ref) {
-        const float alpha = exp2_fast((m_ref - mn) * c);
+      if (__ballot(mn > m_ref) != 0ull) {
+        const float alpha = mn > m_ref ? exp2_fast((m_ref - mn) * c) : 1.f;
         lsum *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[db][r] *= alpha;
         m_ref = mn;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float ar = of_head(alpha, r);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[db][r] *= ar;
+        }
       }
       const float nmc = -m_ref * c;
       f16x8 pf[2];
@@ -451,29 +476,26 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
           pf[ks][e] = (_Float16)p;
         }
       lsum += part;
-      // sum_j of the fp16 P of this head, from the same MFMA path (A = ones)
+      // sum_j of the fp16 P of head 4 grp + r in pt[r], from the same MFMA
+      // path (B = ones)
       f32x4 pt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
-        pt = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, ones16), pf[ks], pt, 0,
+        pt = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[ks], __builtin_bit_cast(f16x8, ones16), pt, 0,
                                                     0, 0);
-      const float ptile = pt[0];
-      // O^T += s_c (codes^T . P^T) + z_c sum_j p_j
+      // O += s_c (P . codes) + z_c sum_j p_j
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         f32x4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-          u = __builtin_amdgcn_mfma_f32_16x16x32_f16(expand_word_f16(vc[db][ks], xk), pf[ks], u, 0,
+          u = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[ks], expand_word_f16(vc.c[db][ks], xk), u, 0,
                                                      0, 0);
+        const float sc = param_s(vc.p[db]), zc = param_z(vc.p[db]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint32_t p = vpr[db][r];
-          acc[db][r] = __builtin_fmaf(param_s(p), u[r], __builtin_fmaf(param_z(p), ptile, acc[db][r]));
-        }
+        for (int r = 0; r < 4; ++r) acc[db][r] = __builtin_fmaf(sc, u[r], __builtin_fmaf(zc, pt[r], acc[db][r]));
       }
     }
-    vload(t + 1, any_nx);
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) s_cur[mb] = s_nx[mb];
     t_cur = t_nx;
@@ -481,8 +503,8 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
     any_cur = any_nx;
   };
   for (int t = 0; t < ntile; t += 2) {
-    step(t, kb);
-    step(t + 1, ka);
+    step(t, kb, va, vb);
+    step(t + 1, ka, vb, va);
   }
 
   if (mask != nullptr && lane < G) {  // lane < G: grp 0, head hl = lane
@@ -492,17 +514,18 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
 
   float ltot = lsum + xor16(lsum);
   ltot += xor32(ltot);
-  if (head_ok) {
-    const float inv = 1.f / ltot;
-    float* dst = ws_o + (bh * nsplit + sp) * D;
+  if (head_ok && grp == 0) ws_lse[bh * nsplit + sp] = (m_ref * c + __log2f(ltot)) * kLn2;
+  const float inv = 1.f / ltot;
+  const size_t bh0 = (size_t)b * Hq + g * G;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      f32x4 val;
+  for (int r = 0; r < 4; ++r) {
+    const float ir = of_head(inv, r);
+    const int h = 4 * grp + r;
+    if (h < G) {
+      float* dst = ws_o + ((bh0 + h) * nsplit + sp) * D + hl;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) val[r] = acc[db][r] * inv;
-      *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * grp) = val;
+      for (int db = 0; db < DB; ++db) dst[16 * db] = acc[db][r] * ir;
     }
-    if (grp == 0) ws_lse[bh * nsplit + sp] = (m_ref * c + __log2f(ltot)) * kLn2;
   }
 }
 
