@@ -28,11 +28,11 @@
 //   the exact bf16 value 128 + c (bits 0x4300 | c, one and-or per pair of
 //   codes), and the offset folded into the zero point: q.k^ = s (q.(128 + c))
 //   + (z - 128 s) sum(q), with sum(q) from the same MFMA on a row of ones.
-//   P.V on v_mfma_f32_16x16x32_f16: P rounded to fp16, codes expanded to exact
-//   fp16 integers (the 0x6400 | c trick, then the 1024 offset removed by a
-//   packed fp16 add or fma), so the offset never meets P's rounding:
-//   sum_j p_j v^_jc = s_c (P.c) + z_c sum(P), with sum(P) again from an MFMA
-//   over the same fp16 P. P is that product's A operand and the codes its B
+//   P.V on v_mfma_f32_16x16x32_f16: P rounded to fp16, codes expanded to the
+//   exact fp16 values 1024 + c (bits 0x6400 | c), the offset again folded into
+//   the zero point: sum_j p_j v^_jc = s_c (P.(1024 + c)) + (z_c - 1024 s_c)
+//   sum(P), with sum(P) from an MFMA over the same fp16 P, so the offset
+//   cancels up to fp32 rounding. P is that product's A operand and the codes its B
 //   operand, so O comes out head-major and each lane needs the parameter of
 //   one channel per 16-channel block.
 //   Key order inside a tile: S^T row 4 grp + r of block mb holds key
@@ -50,7 +50,6 @@
 namespace skipattn {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 namespace {
 
@@ -194,20 +193,18 @@ __device__ __forceinline__ u32x2 ld2(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, AUX));
 }
 
-// The two constants of expand_word, held in registers: gfx9 VOP3 encodings
+// The constants of the expand_word functions, held in registers: gfx9 VOP3 encodings
 // take no literal, so with the mask in an SGPR and the magic in a VGPR the
 // compiler can fuse each mask-and-or into one v_and_or_b32 (and it still
 // sees every register it writes, for the MFMA read hazards).
 struct ExpandConsts {
   uint32_t mask;     // 0x000f000f
-  uint32_t mask4;    // 0x00f000f0
   uint32_t bmagic;   // 0x43004300: bf16 128 in both halves
   uint32_t hmagic;   // 0x64006400: fp16 1024 in both halves
 };
 __device__ __forceinline__ ExpandConsts expand_consts() {
   ExpandConsts k;
   asm volatile("s_mov_b32 %0, 0x000f000f" : "=s"(k.mask));
-  asm volatile("s_mov_b32 %0, 0x00f000f0" : "=s"(k.mask4));
   asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(k.bmagic));
   asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(k.hmagic));
   return k;
@@ -224,26 +221,16 @@ __device__ __forceinline__ bf16x8 expand_word_bf16(uint32_t w, const ExpandConst
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// One storage word -> its 8 codes as exact fp16 integers, element order.
-// (w & 0x000f000f) | 0x64006400 is the fp16 pair (1024 + e0, 1024 + e1); the
-// 0x00f0 nibbles give 1024 + 16 e, brought back by (x / 16 - 64).
+// One storage word -> its 8 codes as the exact fp16 values 1024 + c, element
+// order: nibble n of each 16-bit half, moved to bits 0..3 and or-ed into
+// 0x6400 (fp16 1024, whose unit in the last place is 1).
 __device__ __forceinline__ f16x8 expand_word_f16(uint32_t w, const ExpandConsts& k) {
-  const uint32_t w8 = w >> 8;
-  const f16x2 x0 = __builtin_bit_cast(f16x2, (w & k.mask) | k.hmagic);
-  const f16x2 x1 = __builtin_bit_cast(f16x2, (w & k.mask4) | k.hmagic);
-  const f16x2 x2 = __builtin_bit_cast(f16x2, (w8 & k.mask) | k.hmagic);
-  const f16x2 x3 = __builtin_bit_cast(f16x2, (w8 & k.mask4) | k.hmagic);
-  const f16x2 off = {(_Float16)-1024.f, (_Float16)-1024.f};
-  const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-  const f16x2 off16 = {(_Float16)-64.f, (_Float16)-64.f};
-  const f16x2 y0 = x0 + off;
-  const f16x2 y1 = __builtin_elementwise_fma(x1, sixteenth, off16);
-  const f16x2 y2 = x2 + off;
-  const f16x2 y3 = __builtin_elementwise_fma(x3, sixteenth, off16);
-  f16x8 r;
-  r[0] = y0[0]; r[1] = y0[1]; r[2] = y1[0]; r[3] = y1[1];
-  r[4] = y2[0]; r[5] = y2[1]; r[6] = y3[0]; r[7] = y3[1];
-  return r;
+  u32x4 r;
+  r[0] = (w & k.mask) | k.hmagic;
+  r[1] = ((w >> 4) & k.mask) | k.hmagic;
+  r[2] = ((w >> 8) & k.mask) | k.hmagic;
+  r[3] = ((w >> 12) & k.mask) | k.hmagic;
+  return __builtin_bit_cast(f16x8, r);
 }
 
 __device__ __forceinline__ float param_s(uint32_t p) { return __builtin_bit_cast(float, p << 16); }
@@ -463,15 +450,15 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
           for (int db = 0; db < DB; ++db) acc[db][r] *= ar;
         }
       }
-      const float nmc = -m_ref * c;
+      // a skipped head's exponentials are exp2(-inf) = 0
+      const float nmc = keep_cur ? -m_ref * c : -INFINITY;
       f16x8 pf[2];
       float part = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          float p = exp2_fast(__builtin_fmaf(s_cur[2 * ks + (e >> 2)][e & 3], c, nmc));
-          if (!keep_cur) p = 0.f;
+          const float p = exp2_fast(__builtin_fmaf(s_cur[2 * ks + (e >> 2)][e & 3], c, nmc));
           part += p;
           pf[ks][e] = (_Float16)p;
         }
@@ -483,7 +470,7 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
       for (int ks = 0; ks < 2; ++ks)
         pt = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[ks], __builtin_bit_cast(f16x8, ones16), pt, 0,
                                                     0, 0);
-      // O += s_c (P . codes) + z_c sum_j p_j
+      // O += s_c (P . (1024 + codes)) + (z_c - 1024 s_c) sum_j p_j
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         f32x4 u = {0.f, 0.f, 0.f, 0.f};
@@ -491,7 +478,8 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
         for (int ks = 0; ks < 2; ++ks)
           u = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[ks], expand_word_f16(vc.c[db][ks], xk), u, 0,
                                                      0, 0);
-        const float sc = param_s(vc.p[db]), zc = param_z(vc.p[db]);
+        const float sc = param_s(vc.p[db]);
+        const float zc = __builtin_fmaf(-1024.f, sc, param_z(vc.p[db]));
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[db][r] = __builtin_fmaf(sc, u[r], __builtin_fmaf(zc, pt[r], acc[db][r]));
       }
