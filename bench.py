@@ -46,14 +46,14 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # figure no longer applies and is reported as null.
 MEASURED_TRAFFIC = {
     "prefill": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp"),
-                "sha1": "a1e0b55fc23192d5c213c22fef57275f2dda1810",
-                "bytes": (3216218.7 * 2.0 + 528384.0) * 1024},
+                "sha1": "283e872ac435cb2fce3d1e020a23f4d9532e691c",
+                "bytes": (2867980.9 * 2.0 + 528384.0) * 1024},
     "decode_q4": {"sources": ("kvq4.hip", "decode.hip", "common.hpp"),
-                  "sha1": "0fb1c7f54a42426359088c3578c9cca80deaa744",
-                  "bytes": (1148100.4 * 2.0 + 16640.1) * 1024},
+                  "sha1": "9d8406104c53dbdb88b1f4fefaf5076713434c5c",
+                  "bytes": (1148151.4 * 2.0 + 16641.9) * 1024},
     "decode": {"sources": ("decode.hip", "common.hpp"),
-               "sha1": "642a5529eba59c233ecfeeab8f85092e500c5ce1",
-               "bytes": (4195500.0 * 2.0 + 16642.0) * 1024},
+               "sha1": "c9d9a902f280df832bb299ffe1922fe72fd232dc",
+               "bytes": (4195498.4 * 2.0 + 16642.5) * 1024},
 }
 
 

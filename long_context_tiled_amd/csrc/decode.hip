@@ -324,32 +324,65 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   }
 }
 
+// One wave per (sequence, query head): the partials of all splits are merged
+// with weights exp(lse_s - max lse). A wave reads 64 / (D / 4) splits at a
+// time, one 16-byte piece of a partial row per lane, eight such rounds in
+// flight before the first use.
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
     float* __restrict__ o, float* __restrict__ lse, int nbh, int nsplit) {
-  constexpr int PER = D / 64;
+  constexpr int CL = D / 4;    // lanes per partial row
+  constexpr int SW = 64 / CL;  // splits per round
+  constexpr int U = 8;         // rounds per batch of loads
   const int lane = threadIdx.x & 63;
   const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (bh >= nbh) return;
+  const int c4 = lane % CL;
+  const int sl = lane / CL;
   const float* ls = ws_lse + (size_t)bh * nsplit;
+  const float* os = ws_o + (size_t)bh * nsplit * D + 4 * c4;
   float big = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) big = fmaxf(big, ls[s]);
+  for (int s = lane; s < nsplit; s += 64) big = fmaxf(big, ls[s]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) big = fmaxf(big, __shfl_xor(big, m));
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  float out[PER];
+  for (int s0 = sl; s0 < nsplit; s0 += SW * U) {
+    f32x4 x[U];
+    float l[U];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) out[i] = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float w = expf(ls[s] - big);
-    wsum += w;
-    const float* os = ws_o + ((size_t)bh * nsplit + s) * D;
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + SW * u;
+      x[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      l[u] = -INFINITY;
+      if (s < nsplit) {
+        x[u] = *reinterpret_cast<const f32x4*>(os + (size_t)s * D);
+        l[u] = ls[s];
+      }
+    }
 #pragma unroll
-    for (int i = 0; i < PER; ++i) out[i] += w * os[lane + 64 * i];
+    for (int u = 0; u < U; ++u) {
+      const float w = expf(l[u] - big);  // 0 for a split past the end
+      wsum += w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(w, x[u][i], acc[i]);
+    }
+  }
+#pragma unroll
+  for (int m = CL; m < 64; m <<= 1) {
+    wsum += __shfl_xor(wsum, m);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], m);
   }
   const float inv = 1.f / wsum;
+  if (sl == 0) {
+    f32x4 val;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) o[(size_t)bh * D + lane + 64 * i] = out[i] * inv;
-  if (lane == 0) lse[bh] = big + logf(wsum);
+    for (int i = 0; i < 4; ++i) val[i] = acc[i] * inv;
+    *reinterpret_cast<f32x4*>(o + (size_t)bh * D + 4 * c4) = val;
+    if (lane == 0) lse[bh] = big + logf(wsum);
+  }
 }
 
 template <int D>
