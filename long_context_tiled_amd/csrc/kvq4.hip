@@ -381,16 +381,19 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
   };
 
   // O accumulator: acc[db][r] = O[head 4 grp + r][channel 16 db + hl]
-  // (P is the A operand of the PV product, the V codes the B operand). The
-  // running max, the row sum and the skip state stay per head hl.
+  // (P is the A operand of the PV product, the V codes the B operand), and
+  // the row sum of that head in lr[r]: the sum of the same fp16 P the
+  // product multiplies, so O is an exact weighted mean of the dequantised V
+  // (fp16 rounding moves the LSE by at most 2^-12 relative in l). The running
+  // max and the skip state stay per head hl.
   f32x4 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[db][r] = 0.f;
+  f32x4 lr = {0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY;  // running max over kept tiles: the skip test's reference
   float m_ref = -INFINITY;  // reference max of the exponentials accumulated so far
-  float lsum = 0.f;
   uint64_t skipped = 0;
   auto decide = [&](float tmax, int t, bool& keep) -> bool {
     keep = !(tmax < m_run - tau_raw);
@@ -441,11 +444,11 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
       const float mn = keep_cur ? fmaxf(m_ref, t_cur) : m_ref;
       if (__ballot(mn > m_ref) != 0ull) {
         const float alpha = mn > m_ref ? exp2_fast((m_ref - mn) * c) : 1.f;
-        lsum *= alpha;
         m_ref = mn;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float ar = of_head(alpha, r);
+          lr[r] *= ar;
 #pragma unroll
           for (int db = 0; db < DB; ++db) acc[db][r] *= ar;
         }
@@ -453,16 +456,11 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
       // a skipped head's exponentials are exp2(-inf) = 0
       const float nmc = keep_cur ? -m_ref * c : -INFINITY;
       f16x8 pf[2];
-      float part = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = exp2_fast(__builtin_fmaf(s_cur[2 * ks + (e >> 2)][e & 3], c, nmc));
-          part += p;
-          pf[ks][e] = (_Float16)p;
-        }
-      lsum += part;
+        for (int e = 0; e < 8; ++e)
+          pf[ks][e] = (_Float16)exp2_fast(__builtin_fmaf(s_cur[2 * ks + (e >> 2)][e & 3], c, nmc));
       // sum_j of the fp16 P of head 4 grp + r in pt[r], from the same MFMA
       // path (B = ones)
       f32x4 pt = {0.f, 0.f, 0.f, 0.f};
@@ -470,6 +468,8 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
       for (int ks = 0; ks < 2; ++ks)
         pt = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[ks], __builtin_bit_cast(f16x8, ones16), pt, 0,
                                                     0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) lr[r] += pt[r];
       // O += s_c (P . (1024 + codes)) + (z_c - 1024 s_c) sum_j p_j
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
@@ -500,19 +500,17 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
     for (int t = 0; t < ntile; ++t) mrow[t] = (uint8_t)((skipped >> t) & 1u);
   }
 
-  float ltot = lsum + xor16(lsum);
-  ltot += xor32(ltot);
-  if (head_ok && grp == 0) ws_lse[bh * nsplit + sp] = (m_ref * c + __log2f(ltot)) * kLn2;
-  const float inv = 1.f / ltot;
   const size_t bh0 = (size_t)b * Hq + g * G;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const float ir = of_head(inv, r);
+    const float mr = of_head(m_ref, r);
     const int h = 4 * grp + r;
     if (h < G) {
+      const float ir = 1.f / lr[r];
       float* dst = ws_o + ((bh0 + h) * nsplit + sp) * D + hl;
 #pragma unroll
       for (int db = 0; db < DB; ++db) dst[16 * db] = acc[db][r] * ir;
+      if (hl == 0) ws_lse[(bh0 + h) * nsplit + sp] = (mr * c + __log2f(lr[r])) * kLn2;
     }
   }
 }
