@@ -26,15 +26,20 @@
 // Decode split kernel: one wave per (sequence, KV head, split), no LDS.
 //   q.K on v_mfma_f32_16x16x32_bf16: q exact in bf16, each code c expanded to
 //   the exact bf16 value 128 + c (bits 0x4300 | c, one and-or per pair of
-//   codes), and the offset folded into the zero point: q.k^ = s (q.(128 + c))
-//   + (z - 128 s) sum(q), with sum(q) from the same MFMA on a row of ones.
-//   P.V on v_mfma_f32_16x16x32_f16: P rounded to fp16, codes expanded to the
-//   exact fp16 values 1024 + c (bits 0x6400 | c), the offset again folded into
-//   the zero point: sum_j p_j v^_jc = s_c (P.(1024 + c)) + (z_c - 1024 s_c)
-//   sum(P), with sum(P) from an MFMA over the same fp16 P, so the offset
-//   cancels up to fp32 rounding. P is that product's A operand and the codes its B
-//   operand, so O comes out head-major and each lane needs the parameter of
-//   one channel per 16-channel block.
+//   codes), the MFMA accumulator started at -128 sum(q) so that it returns
+//   q.c, and q.k^ = s (q.c) + z sum(q), with sum(q) from the same MFMA on a
+//   row of ones.
+//   P.V on v_mfma_f32_16x16x32_f16: codes expanded by masks alone to the exact
+//   fp16 values 1024 + c (word positions 0, 1, 4, 5) and 1024 + 16 c
+//   (positions 2, 3, 6, 7), and P' = 16 P on the keys of the first kind
+//   (exponent + 4), P on the others, rounded to fp16. Then
+//   P'.(expanded) = 16 P.c + 1024 sum(P'); with the accumulator started at
+//   -1024 sum(P'), sum_j p_j v^_jc = (s_c / 16) (16 P.c) + z_c sum(P). sum(P)
+//   and sum(P') come from MFMAs over the same fp16 P' (B = per-position
+//   weights 1/16 and 1, then ones), so the offset cancels up to fp32 rounding
+//   and sum(P) is also the row sum l. P is that product's A operand and the
+//   codes its B operand, so O comes out head-major and each lane needs the
+//   parameter of one channel per 16-channel block.
 //   Key order inside a tile: S^T row 4 grp + r of block mb holds key
 //   16 grp + 4 mb + r, so lane (head, grp) owns keys 16 grp .. 16 grp + 15 and
 //   its P fragment for PV k-step ks is keys 16 grp + 8 ks .. + 7, which is
@@ -199,12 +204,14 @@ __device__ __forceinline__ u32x2 ld2(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
 // sees every register it writes, for the MFMA read hazards).
 struct ExpandConsts {
   uint32_t mask;     // 0x000f000f
+  uint32_t mask4;    // 0x00f000f0
   uint32_t bmagic;   // 0x43004300: bf16 128 in both halves
   uint32_t hmagic;   // 0x64006400: fp16 1024 in both halves
 };
 __device__ __forceinline__ ExpandConsts expand_consts() {
   ExpandConsts k;
   asm volatile("s_mov_b32 %0, 0x000f000f" : "=s"(k.mask));
+  asm volatile("s_mov_b32 %0, 0x00f000f0" : "=s"(k.mask4));
   asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(k.bmagic));
   asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(k.hmagic));
   return k;
@@ -212,6 +219,7 @@ __device__ __forceinline__ ExpandConsts expand_consts() {
 
 // One storage word -> its 8 codes as bf16 values 128 + c, element order:
 // nibble n of each 16-bit half, moved to bits 0..3 and or-ed into 0x4300.
+// (bf16 has 7 mantissa bits, so a nibble cannot stay at bits 4..7.)
 __device__ __forceinline__ bf16x8 expand_word_bf16(uint32_t w, const ExpandConsts& k) {
   u32x4 r;
   r[0] = (w & k.mask) | k.bmagic;
@@ -221,17 +229,22 @@ __device__ __forceinline__ bf16x8 expand_word_bf16(uint32_t w, const ExpandConst
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// One storage word -> its 8 codes as the exact fp16 values 1024 + c, element
-// order: nibble n of each 16-bit half, moved to bits 0..3 and or-ed into
-// 0x6400 (fp16 1024, whose unit in the last place is 1).
+// One storage word -> its 8 codes as exact fp16 values, element order, by
+// masks alone (one shift, four and-ors): elements 0, 1, 4, 5 (nibbles 0 and
+// 2 of each 16-bit half) become 1024 + c, elements 2, 3, 6, 7 (nibbles 1 and
+// 3) become 1024 + 16 c: fp16 1024 (0x6400) has 10 mantissa bits and a unit
+// in the last place of 1, so mantissa bits 4..7 add 16 c. The other operand
+// carries the factor 16 on the first kind instead (see the decode kernel).
 __device__ __forceinline__ f16x8 expand_word_f16(uint32_t w, const ExpandConsts& k) {
+  const uint32_t w8 = w >> 8;
   u32x4 r;
   r[0] = (w & k.mask) | k.hmagic;
-  r[1] = ((w >> 4) & k.mask) | k.hmagic;
-  r[2] = ((w >> 8) & k.mask) | k.hmagic;
-  r[3] = ((w >> 12) & k.mask) | k.hmagic;
+  r[1] = (w & k.mask4) | k.hmagic;
+  r[2] = (w8 & k.mask) | k.hmagic;
+  r[3] = (w8 & k.mask4) | k.hmagic;
   return __builtin_bit_cast(f16x8, r);
 }
+
 
 __device__ __forceinline__ float param_s(uint32_t p) { return __builtin_bit_cast(float, p << 16); }
 __device__ __forceinline__ float param_z(uint32_t p) { return __builtin_bit_cast(float, p & 0xffff0000u); }
@@ -288,8 +301,9 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
     qf[ks] = as_bf16x8(x);
   }
   const ExpandConsts xk = expand_consts();
-  // sum_d q_d per head, accumulated by the MFMA itself (A = ones)
-  float qsum;
+  // sum_d q_d per head, accumulated by the MFMA itself (A = ones); the score
+  // MFMAs start from -128 sum(q), so they return q.c directly
+  float qsum, nqc;
   {
     const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
@@ -297,8 +311,12 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
     for (int ks = 0; ks < KS; ++ks)
       a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ones), qf[ks], a, 0, 0, 0);
     qsum = a[0];
+    nqc = -128.f * qsum;
   }
-  const u32x4 ones16 = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};  // fp16 1.0
+  // fp16 weights for sums over P' (P' = 16 P on positions 0, 1, 4, 5 of each
+  // key word, P elsewhere): sum(P) with 1/16 and 1, -1024 sum(P') with -1024.
+  const u32x4 wp = {0x2c002c00u, 0x3c003c00u, 0x2c002c00u, 0x3c003c00u};
+  const u32x4 wneg = {0xe400e400u, 0xe400e400u, 0xe400e400u, 0xe400e400u};
 
   // Per-tile registers: K codes (block mb: KS words of row 16 (hl >> 2) +
   // 4 mb + (hl & 3)), K parameters (keys 16 grp + 4 j .. + 3), V codes
@@ -351,17 +369,16 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
     const int key0 = key_begin + t * kTile;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+      f32x4 a = {nqc, nqc, nqc, nqc};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(expand_word_bf16(ks_.c[mb][ks], xk), qf[ks], a,
                                                     0, 0, 0);
-      // q.k^ = s (q.(128 + c)) + (z - 128 s) sum(q)
+      // q.k^ = s (q.c) + z sum(q)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const uint32_t p = ks_.p[mb][r];
-        const float sc = param_s(p);
-        s[mb][r] = __builtin_fmaf(sc, a[r], __builtin_fmaf(-128.f, sc, param_z(p)) * qsum);
+        s[mb][r] = __builtin_fmaf(param_s(p), a[r], param_z(p) * qsum);
       }
     }
     if (key0 + kTile > L) {
@@ -453,35 +470,45 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
           for (int db = 0; db < DB; ++db) acc[db][r] *= ar;
         }
       }
-      // a skipped head's exponentials are exp2(-inf) = 0
+      // P' = 16 P on the keys whose V codes expand to 1024 + c (positions
+      // 0, 1, 4, 5 of each key word: exponent + 4), P on the others; a
+      // skipped head's exponentials are exp2(-inf) = 0
       const float nmc = keep_cur ? -m_ref * c : -INFINITY;
+      const float nmc4 = nmc + 4.f;
       f16x8 pf[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          pf[ks][e] = (_Float16)exp2_fast(__builtin_fmaf(s_cur[2 * ks + (e >> 2)][e & 3], c, nmc));
-      // sum_j of the fp16 P of head 4 grp + r in pt[r], from the same MFMA
-      // path (B = ones)
-      f32x4 pt = {0.f, 0.f, 0.f, 0.f};
+          pf[ks][e] = (_Float16)exp2_fast(
+              __builtin_fmaf(s_cur[2 * ks + (e >> 2)][e & 3], c, (e & 2) ? nmc : nmc4));
+      // sum_j p_j (pt) and -1024 sum_j p'_j (u0) of head 4 grp + r, from
+      // MFMAs over the same fp16 P' (B = per-position weights, then -1024)
+      f32x4 pt = {0.f, 0.f, 0.f, 0.f}, u0 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        pt = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[ks], __builtin_bit_cast(f16x8, ones16), pt, 0,
+      for (int ks = 0; ks < 2; ++ks) {
+        pt = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[ks], __builtin_bit_cast(f16x8, wp), pt, 0, 0,
+                                                    0);
+        u0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[ks], __builtin_bit_cast(f16x8, wneg), u0, 0,
                                                     0, 0);
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) lr[r] += pt[r];
-      // O += s_c (P . (1024 + codes)) + (z_c - 1024 s_c) sum_j p_j
+      // P'.(expanded codes) = 16 P.c + 1024 sum(P'), so with the MFMA
+      // accumulator started at -1024 sum(P'):
+      // O += (s_c / 16) (16 P.c) + z_c sum_j p_j
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        f32x4 u = {0.f, 0.f, 0.f, 0.f};
+        f32x4 u = u0;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
           u = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[ks], expand_word_f16(vc.c[db][ks], xk), u, 0,
                                                      0, 0);
-        const float sc = param_s(vc.p[db]);
-        const float zc = __builtin_fmaf(-1024.f, sc, param_z(vc.p[db]));
+        const float sc16 = 0.0625f * param_s(vc.p[db]);
+        const float zc = param_z(vc.p[db]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[db][r] = __builtin_fmaf(sc, u[r], __builtin_fmaf(zc, pt[r], acc[db][r]));
+        for (int r = 0; r < 4; ++r)
+          acc[db][r] = __builtin_fmaf(sc16, u[r], __builtin_fmaf(zc, pt[r], acc[db][r]));
       }
     }
 #pragma unroll
