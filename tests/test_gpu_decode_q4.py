@@ -69,6 +69,41 @@ def test_quantiser_bit_exact(B, Hkv, L, d, seed, scale):
     _assert_same_cache(got, want)
 
 
+def _on_ties(rng, shape):
+    """bf16 blocks along the last axis whose codes sit on rounding ties: each
+    block holds its minimum z and z + 15 s0 (s0 a power of two, so s = s0),
+    and otherwise values z + (j + 1/2) s0 - exact ties of (x - z) / s - a
+    third of them moved one bf16 step up or down."""
+    lead = shape[:-1] + (1,)
+    s0 = 2.0 ** rng.integers(-8, 8, lead)
+    z = -s0 * rng.integers(0, 16, lead)
+    x = z + s0 * (rng.integers(0, 15, shape) + 0.5)
+    x[..., 0:1], x[..., 1:2] = z, z + 15 * s0
+    bits = synth.f32_to_bf16_bits(x.astype(np.float32))
+    assert np.array_equal(synth.bf16_bits_to_f32(bits), x.astype(np.float32))
+    step = rng.integers(-1, 2, shape).astype(np.int32)
+    step[..., :2] = 0
+    return (bits.astype(np.int32) + step).astype(np.uint16)
+
+
+def test_quantiser_bit_exact_on_ties():
+    """Codes at and one step beside exact half-integer quotients, where a
+    reciprocal multiply alone could round the other way."""
+    import torch
+    import long_context_tiled_amd as lib
+    rng = np.random.default_rng(11)
+    B, Hkv, L, d = 2, 2, 192, 128
+    k = _on_ties(rng, (B, Hkv, L, d))
+    # V blocks run along the 64 keys of a tile, per channel
+    vt = _on_ties(rng, (B, Hkv, L // 64, d, 64))
+    v = np.ascontiguousarray(vt.transpose(0, 1, 2, 4, 3).reshape(B, Hkv, L, d))
+    print("[q4] quantise on ties", flush=True)
+    got = _host(lib.quantize_q4(_dev(k), _dev(v)))
+    torch.cuda.synchronize()
+    want = kvq4.encode(synth.bf16_bits_to_f32(k), synth.bf16_bits_to_f32(v))
+    _assert_same_cache(got, want, "ties")
+
+
 def _decode_case(q, k, v, taus, name):
     import torch
     import long_context_tiled_amd as lib
