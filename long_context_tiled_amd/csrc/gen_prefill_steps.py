@@ -209,9 +209,10 @@ class Step:
                 off = (tile_bytes if which == "V" else 0) + i * 1024
                 tmp = "%[vt]" if n % 2 == 0 else "%[vz]"
                 n += 1
-                groups.append([Ins(f"v_add_u32 {tmp}, %[t1], %[{g}{i}]", "valu"),
-                               Ins(f"s_add_u32 m0, %[t2], {off}", "salu"),
-                               Ins("s_nop 0", "salu"),
+                # the VALU add sits between the M0 write and the copy that
+                # reads M0, which needs one wait state there
+                groups.append([Ins(f"s_add_u32 m0, %[t2], {off}", "salu"),
+                               Ins(f"v_add_u32 {tmp}, %[t1], %[{g}{i}]", "valu"),
                                Ins(f"buffer_load_dwordx4 {tmp}, {rs}, 0 offen lds", "vmem")])
         return groups
 
@@ -236,7 +237,7 @@ class Step:
         running row sum once. (Adding every exponential straight into the
         running sum loses the small terms once that sum is large: over
         millions of keys the row sum, and so the LSE, came out low.)"""
-        out = []
+        heads, tails = [], []
         first = {0: True, 1: True}
         for gp in range(32):
             ch, i2 = gp >> 2, gp & 3
@@ -250,20 +251,29 @@ class Step:
             w = f"v{PREG + 4 * (2 * kp + nb) + i2}"
             ps = f"v{PSUM + nb}"
             nm = f"%[nm{nb}]"
-            out += [
+            heads.append([
                 Ins(f"v_fma_f32 {t0}, {s0}, %[c], {nm}", "valu", wr=[t0], rd=[s0]),
                 Ins(f"v_fma_f32 {t1}, {s1}, %[c], {nm}", "valu", wr=[t1], rd=[s1]),
                 Ins(f"v_exp_f32 {t0}, {t0}", "trans", wr=[t0], rd=[t0]),
                 Ins(f"v_exp_f32 {t1}, {t1}", "trans", wr=[t1], rd=[t1]),
-                Ins(f"v_cvt_pk_bf16_f32 {w}, {t0}, {t1}", "valu", wr=[w], rd=[t0, t1],
-                    tag=("pf", kp)),
-            ]
+            ])
+            tail = [Ins(f"v_cvt_pk_bf16_f32 {w}, {t0}, {t1}", "valu", wr=[w], rd=[t0, t1],
+                        tag=("pf", kp))]
             if first[nb]:
-                out.append(Ins(f"v_add_f32 {ps}, {t0}, {t1}", "valu", wr=[ps], rd=[t0, t1]))
+                tail.append(Ins(f"v_add_f32 {ps}, {t0}, {t1}", "valu", wr=[ps], rd=[t0, t1]))
                 first[nb] = False
             else:
-                out += [Ins(f"v_add_f32 {t0}, {t0}, {t1}", "valu", wr=[t0], rd=[t0, t1]),
-                        Ins(f"v_add_f32 {ps}, {ps}, {t0}", "valu", wr=[ps], rd=[ps, t0])]
+                tail += [Ins(f"v_add_f32 {t0}, {t0}, {t1}", "valu", wr=[t0], rd=[t0, t1]),
+                         Ins(f"v_add_f32 {ps}, {ps}, {t0}", "valu", wr=[ps], rd=[ps, t0])]
+            tails.append(tail)
+        # Pairs are software-pipelined by one: the scale-and-shift of pair
+        # gp + 1 sits between the exponentials of pair gp and their first
+        # reader, so no wait state is needed after a v_exp (the temporaries
+        # rotate over three register pairs).
+        out = list(heads[0])
+        for gp in range(1, 32):
+            out += heads[gp][:2] + tails[gp - 1] + heads[gp][2:]
+        out += tails[31]
         for nb in range(2):
             out.append(Ins(f"v_add_f32 %[lo{nb}], %[lo{nb}], v{PSUM + nb}", "valu",
                            rd=[f"v{PSUM + nb}"]))
