@@ -46,14 +46,14 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # figure no longer applies and is reported as null.
 MEASURED_TRAFFIC = {
     "prefill": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp"),
-                "sha1": "283e872ac435cb2fce3d1e020a23f4d9532e691c",
-                "bytes": (2867980.9 * 2.0 + 528384.0) * 1024},
+                "sha1": "7c0518924172943a1849f963d98c60f203460e96",
+                "bytes": (3919360.3 * 2.0 + 528384.0) * 1024},
     "decode_q4": {"sources": ("kvq4.hip", "decode.hip", "common.hpp"),
-                  "sha1": "9d8406104c53dbdb88b1f4fefaf5076713434c5c",
-                  "bytes": (1148151.4 * 2.0 + 16641.9) * 1024},
+                  "sha1": "6ae98e52bd1eca651830e5346940d63ad61c7697",
+                  "bytes": (1148198.3 * 2.0 + 16646.6) * 1024},
     "decode": {"sources": ("decode.hip", "common.hpp"),
                "sha1": "c9d9a902f280df832bb299ffe1922fe72fd232dc",
-               "bytes": (4195498.4 * 2.0 + 16642.5) * 1024},
+               "bytes": (4195503.2 * 2.0 + 16641.4) * 1024},
 }
 
 
