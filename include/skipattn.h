@@ -218,10 +218,12 @@ int attn_kv_quantize_q4_range(const void* k, const void* v, uint8_t* kq,
 /*
  * attn_decode_q4 - attn_decode over a 4-bit cache: the same rule, splits,
  * outputs, mask and workspace (attn_decode_workspace_bytes), with the keys
- * and values taken as code * s + z from kq/kp and vq/vp (layout above). The
- * products run in fp16 with fp32 accumulation on the exact codes; q is
- * rounded to fp16 after a per-head power-of-two scaling that keeps it in
- * range, and the probabilities are rounded to fp16 for the value product.
+ * and values taken as code * s + z from kq/kp and vq/vp (layout above).
+ * Both products run on the exact codes with fp32 accumulation: q.K in bf16
+ * (q as given), P.V in fp16 with the probabilities rounded to fp16 (times 16
+ * on half of the keys, an exact scaling), and the row sum taken over the
+ * same fp16 probabilities, so O is an exact weighted mean of the dequantised
+ * values and the LSE moves by at most about 4e-4 from that rounding.
  */
 int attn_decode_q4(const void* q, const uint8_t* kq, const uint32_t* kp,
                    const uint8_t* vq, const uint32_t* vp, float* o,
