@@ -1,6 +1,7 @@
 """Benchmark of libskipattn on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-cpu]
+                    [--only LEG] [--prefill-workload prefill_128k|prefill_32k|prefill_8k]
 
 A step is one pass of the whole hot path: a causal GQA prefill at 128K
 context (B=1, Hq=8, Hkv=1, N=131072, d=128) followed by a split-K decode
@@ -15,6 +16,10 @@ executed TFLOP/s, dense and actual GB/s) and the fp64 oracle's throughput on
 the host cores over a bounded sample of the same workloads. Timed calls
 write no skip mask (an optional output); the sweep reads each tau's mask
 from one extra call outside its timing.
+
+``--prefill-workload`` puts the 32K (B=1, Hq=64, Hkv=8) or 8K (B=1, Hq=32,
+Hkv=8) causal prefill shape in the 128K one's place; the default line is the
+128K step.
 
 Beside the step, the same decode workload is run over the 4-bit asymmetric
 KV cache (attn_kv_quantize_q4 once, then attn_decode_q4 timed like the bf16
@@ -174,7 +179,7 @@ def _cpu_decode_q4_head(i):
             oracle.decode_head(synth.bf16_bits_to_f64(q[hh]), k, v, math.inf)
 
 
-def cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=768, nkv=32, nkv_q4=16):
+def cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=768, nkv=32, nkv_q4=16, pname="prefill_128k"):
     """The fp64 oracle as it stands, timed on a bounded sample of each
     workload with one process per host core (fp64 widening of the inputs is
     done before the clock starts)."""
@@ -184,6 +189,7 @@ def cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=768, nkv=32, nkv_q4=16):
     cores = min(16, os.cpu_count() or 1)
     N, d = pq.shape[2], pq.shape[3]
     nt = N // 64
+    nblocks = min(nblocks, nt)
     qbs = [int(x) for x in np.linspace(0, nt - 1, nblocks).astype(int)]
     _CPU.clear()
     _CPU.update(pq=pq[0, 0], pk=synth.bf16_bits_to_f64(pk[0, 0]),
@@ -214,7 +220,7 @@ def cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=768, nkv=32, nkv_q4=16):
     pairs = sum(64 * (qb * 64) + 64 * 65 // 2 for qb in qbs)
     pre = dict(value=float(4.0 * d * pairs / pwall / 1e12), unit="TFLOP/s", cores=cores,
                kind="oracle",
-               sample=f"prefill_128k head 0: {nblocks} of {nt} query blocks spread evenly, "
+               sample=f"{pname} head 0: {nblocks} of {nt} query blocks spread evenly, "
                       f"tau=inf, fp64 numpy, {pwall:.1f} s wall")
     kv_bytes = len(picks) * 2.0 * L * d * 2
     dec = dict(value=float(kv_bytes / dwall / 1e9), unit="GB/s", cores=cores, kind="oracle",
@@ -241,6 +247,9 @@ def main():
                     help="profile one leg only (the JSON line then reports that leg)")
     ap.add_argument("--no-q4", action="store_true",
                     help="skip the 4-bit KV-cache decode measured beside the step")
+    ap.add_argument("--prefill-workload", default="prefill_128k",
+                    choices=["prefill_128k", "prefill_32k", "prefill_8k"],
+                    help="prefill shape of the step (default: the 128K one)")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB, a reference "
                          "dispatch of known traffic for hardware byte counters")
@@ -257,7 +266,8 @@ def main():
 
     lib.load()
     dev = torch.device("cuda:0")
-    pcfg = synth.workload("prefill_128k")
+    pname = args.prefill_workload
+    pcfg = synth.workload(pname)
     dcfg = synth.workload("decode_128k")
     t0 = time.perf_counter()
     pq, pk, pv = synth.make_prefill(pcfg, reading=args.reading)
@@ -331,7 +341,7 @@ def main():
     out = dict(metric=METRIC, n_gpus=1, steps=args.steps, warmup=args.warmup,
                ms_per_step=round(wall_ms, 4), higher_is_better=True, scaling="weak",
                vs_baseline=None, dtype="bf16", data="synthetic")
-    cfg = dict(workload="prefill_128k + decode_128k, tau=inf",
+    cfg = dict(workload=f"{pname} + decode_128k, tau=inf",
                prefill=dict(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, causal=True),
                decode=dict(B=DB, Hq=DHq, Hkv=DHkv, L=L, d=Dd, split=4096),
                reading=args.reading, inputs="seeded N(0,1) bf16 + sinks/band/window")
@@ -343,7 +353,8 @@ def main():
         out.update(value=round(p_tf, 3), unit="TFLOP/s")
         out["roofline"] = dict(bound="mfma", achieved=round(p_tf, 3), peak=PEAK_BF16_TFLOPS,
                                unit="TFLOP/s", frac=round(p_tf / PEAK_BF16_TFLOPS, 4),
-                               traffic=measured_traffic("prefill"),
+                               traffic=(measured_traffic("prefill")
+                                        if pname == "prefill_128k" else None),
                                kernel="prefill_kernel<128,true,4>",
                                avg_ms=round(p_ms, 4),
                                per_launch_flops=dense_flops)
@@ -414,7 +425,7 @@ def main():
             prefill(tau, pmask)
             m = pmask.cpu().numpy()
             ex, vis, kept = prefill_exec_flops(m, d)
-            sweep.append(dict(leg="prefill_128k", tau=str(tau), ms=round(ms, 4),
+            sweep.append(dict(leg=pname, tau=str(tau), ms=round(ms, 4),
                               skip_fraction=round(1 - kept / vis, 4),
                               tflops_dense=round(dense_flops / ms / 1e9, 3),
                               tflops_executed=round(ex / ms / 1e9, 3)))
@@ -449,7 +460,7 @@ def main():
 
     if not args.no_cpu:
         print("# cpu baseline (fp64 oracle on a bounded sample)", file=sys.stderr, flush=True)
-        pre, dec, dq4 = cpu_baseline(pq, pk, pv, dq, dk, dv)
+        pre, dec, dq4 = cpu_baseline(pq, pk, pv, dq, dk, dv, pname=pname)
         out["cpu_baseline"] = pre if run_p else (dec if run_d else dq4)
         out["cpu_baseline_decode"] = dec
         out["cpu_baseline_decode_q4"] = dq4
