@@ -319,16 +319,21 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
   const u32x4 wneg = {0xe400e400u, 0xe400e400u, 0xe400e400u, 0xe400e400u};
 
   // Per-tile registers: K codes (block mb: KS words of row 16 (hl >> 2) +
-  // 4 mb + (hl & 3)), K parameters (keys 16 grp + 4 j .. + 3), V codes
-  // (block db: words 2 grp, 2 grp + 1 of channel row 16 db + hl) and the V
-  // parameter of channel 16 db + hl. V has two register sets, so the V of
-  // tile t + 1 is in flight while the PV of tile t waits for its own.
+  // 4 mb + (hl & 3)), K parameters (keys 16 grp + 4 j .. + 3), V codes and
+  // the V parameter of channel 16 db + hl. V codes come as one 16-byte load
+  // per pair of blocks (2 dp, 2 dp + 1): lane (hl, grp) reads half grp >> 1
+  // of channel row 32 dp + 16 (grp & 1) + hl (the pair's 32 rows, 1 KB, in
+  // one instruction); swapping rows between lane groups 2i and 2i + 1
+  // (v_permlane16_swap) then leaves every lane words 2 grp, 2 grp + 1 of
+  // both rows 32 dp + hl and 32 dp + 16 + hl, the B fragments of the pair.
+  // V has two register sets, so the V of tile t + 1 is in flight while the
+  // PV of tile t waits for its own.
   struct KSet {
     uint32_t c[4][KS];
     u32x4 p[4];
   };
   struct VSet {
-    u32x2 c[DB];
+    u32x4 c[DB / 2];
     uint32_t p[DB];
   };
   KSet ka, kb;  // K of even tiles in ka, of odd tiles in kb
@@ -358,8 +363,9 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
     const uint32_t tile = rd ? (uint32_t)(tile_begin + t) : 0u;
     const uint32_t no = rd ? 0u : kNoRead;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-      vs.c[db] = ld2<kNT>(vrs, no + ((tile * D + 16 * db + hl) * 32 + 8 * grp));
+    for (int dp = 0; dp < DB / 2; ++dp)
+      vs.c[dp] = ld4<kNT>(vrs, no + ((tile * D + 32 * dp + 16 * (grp & 1) + hl) * 32 +
+                                     16 * (grp >> 1)));
 #pragma unroll
     for (int db = 0; db < DB; ++db) vs.p[db] = ld1<kRT>(vprs, no + (tile * D + 16 * db + hl) * 4);
   };
@@ -498,17 +504,25 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
       // accumulator started at -1024 sum(P'):
       // O += (s_c / 16) (16 P.c) + z_c sum_j p_j
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        f32x4 u = u0;
+      for (int dp = 0; dp < DB / 2; ++dp) {
+        // odd lane groups' words 0, 1 <-> even lane groups' words 2, 3
+        const u32x2 s0 = __builtin_amdgcn_permlane16_swap(vc.c[dp][0], vc.c[dp][2], false, false);
+        const u32x2 s1 = __builtin_amdgcn_permlane16_swap(vc.c[dp][1], vc.c[dp][3], false, false);
+        const uint32_t w[2][2] = {{s0[0], s1[0]}, {s0[1], s1[1]}};  // [block of the pair][ks]
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          u = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[ks], expand_word_f16(vc.c[db][ks], xk), u, 0,
-                                                     0, 0);
-        const float sc16 = 0.0625f * param_s(vc.p[db]);
-        const float zc = param_z(vc.p[db]);
+        for (int h = 0; h < 2; ++h) {
+          const int db = 2 * dp + h;
+          f32x4 u = u0;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          acc[db][r] = __builtin_fmaf(sc16, u[r], __builtin_fmaf(zc, pt[r], acc[db][r]));
+          for (int ks = 0; ks < 2; ++ks)
+            u = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[ks], expand_word_f16(w[h][ks], xk), u, 0,
+                                                       0, 0);
+          const float sc16 = 0.0625f * param_s(vc.p[db]);
+          const float zc = param_z(vc.p[db]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[db][r] = __builtin_fmaf(sc16, u[r], __builtin_fmaf(zc, pt[r], acc[db][r]));
+        }
       }
     }
 #pragma unroll
