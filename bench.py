@@ -52,13 +52,13 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 MEASURED_TRAFFIC = {
     "prefill": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp"),
                 "sha1": "7c0518924172943a1849f963d98c60f203460e96",
-                "bytes": (3919360.3 * 2.0 + 528384.0) * 1024},
+                "bytes": (4023991.9 * 2.0 + 528384.0) * 1024},
     "decode_q4": {"sources": ("kvq4.hip", "decode.hip", "common.hpp"),
-                  "sha1": "6ae98e52bd1eca651830e5346940d63ad61c7697",
-                  "bytes": (1148198.3 * 2.0 + 16646.6) * 1024},
+                  "sha1": "1a08d7c9e6b44641acad0d8207fdeba5c64774b1",
+                  "bytes": (1148103.0 * 2.0 + 16650.9) * 1024},
     "decode": {"sources": ("decode.hip", "common.hpp"),
                "sha1": "c9d9a902f280df832bb299ffe1922fe72fd232dc",
-               "bytes": (4195503.2 * 2.0 + 16641.4) * 1024},
+               "bytes": (4195496.3 * 2.0 + 16642.0) * 1024},
 }
 
 
