@@ -41,6 +41,15 @@ margin is positive.
 ``forced`` lets a caller impose decisions on chosen tiles (-1 free, 0 keep,
 1 skip), so that a result computed with another rounding of the scores can be
 re-evaluated under that caller's decisions.
+
+Parity unpinned: the readings listed above (per-row test over every valid
+row, natural-logit units with the 1/sqrt(d) scale, the strict comparison,
+per-head decisions in decode, the split size) are conventions; the pages
+print no numeric example of the rule, so no test can tie them to the pages.
+The functions themselves are pinned outside their own code: a scalar
+brute-force online softmax, the textbook softmax attention at tau = inf, the
+prefix-max closed form of the decisions, the dropped-mass bound, hand-built
+golden cases and the split/merge identity (the oracle tests).
 """
 from __future__ import annotations
 

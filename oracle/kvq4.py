@@ -36,6 +36,11 @@ the readings taken here:
   vq uint8 [B, Hkv, T, d, 32] with T = ceil(L / 64) (per tile and channel,
   the 64 keys' codes; keys at or past L have code 0 and take no part in the
   tile's minimum and maximum); vp uint32 [B, Hkv, T, d].
+
+Parity unpinned: these format choices are readings, not the pages' (which
+give no block size, rounding or layout). What the tests pin is that the code
+implements them: hand-derived layout bytes, exact round trips of caches
+built on the code grid, and the error bound of uniform quantisation.
 """
 from __future__ import annotations
 
