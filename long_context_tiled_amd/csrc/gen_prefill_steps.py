@@ -936,7 +936,7 @@ def main(out_path=None):
              "// Per-key-tile steps of the prefill kernel (see the script's docstring for",
              "// the schedule, the register plan and the hazard rules).",
              "#pragma once", ""]
-    for d, budget in ((128, 20.0), (64, 30.0)):
+    for d, budget in ((128, 26.0), (64, 30.0)):
         parts.append(f"namespace d{d} {{")
         for h in helpers_cxx(d):
             parts.append(h)
