@@ -51,14 +51,14 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # figure no longer applies and is reported as null.
 MEASURED_TRAFFIC = {
     "prefill": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp"),
-                "sha1": "7c0518924172943a1849f963d98c60f203460e96",
-                "bytes": (4023991.9 * 2.0 + 528384.0) * 1024},
+                "sha1": "997b1712c691d713dcef2bad76a69c55fe5807a3",
+                "bytes": (2749866.4 * 2.0 + 528384.0) * 1024},
     "decode_q4": {"sources": ("kvq4.hip", "decode.hip", "common.hpp"),
                   "sha1": "1a08d7c9e6b44641acad0d8207fdeba5c64774b1",
-                  "bytes": (1148103.0 * 2.0 + 16650.9) * 1024},
+                  "bytes": (1148083.9 * 2.0 + 16647.2) * 1024},
     "decode": {"sources": ("decode.hip", "common.hpp"),
                "sha1": "c9d9a902f280df832bb299ffe1922fe72fd232dc",
-               "bytes": (4195496.3 * 2.0 + 16642.0) * 1024},
+               "bytes": (4195496.4 * 2.0 + 16641.2) * 1024},
 }
 
 
