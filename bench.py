@@ -54,7 +54,7 @@ MEASURED_TRAFFIC = {
                 "sha1": "997b1712c691d713dcef2bad76a69c55fe5807a3",
                 "bytes": (2749866.4 * 2.0 + 528384.0) * 1024},
     "decode_q4": {"sources": ("kvq4.hip", "decode.hip", "common.hpp"),
-                  "sha1": "1a08d7c9e6b44641acad0d8207fdeba5c64774b1",
+                  "sha1": "0de8a66b284ec5266f1614bb5422477539b227b6",
                   "bytes": (1148083.9 * 2.0 + 16647.2) * 1024},
     "decode": {"sources": ("decode.hip", "common.hpp"),
                "sha1": "c9d9a902f280df832bb299ffe1922fe72fd232dc",

@@ -23,7 +23,8 @@
 //   kq [B,Hkv,L,d/2] u8, kp [B,Hkv,L] u32, vq [B,Hkv,T,d,32] u8 (64 keys of a
 //   channel per tile, keys past L code 0), vp [B,Hkv,T,d] u32, T = ceil(L/64).
 //
-// Decode split kernel: one wave per (sequence, KV head, split), no LDS.
+// Decode split kernel: one wave per (sequence, KV head, split), no LDS
+// memory (only ds_bpermute lane exchanges).
 //   q.K on v_mfma_f32_16x16x32_bf16: q exact in bf16, each code c expanded to
 //   the exact bf16 value 128 + c (bits 0x4300 | c, one and-or per pair of
 //   codes), the MFMA accumulator started at -128 sum(q) so that it returns
