@@ -1,0 +1,145 @@
+"""GPU parity on seeded random shapes: batch, head counts and group sizes,
+ragged lengths, both head sizes, causal or not, structured or plain inputs,
+several tau. Every case compares full outputs with the fp64 oracle through
+the C ABI (skip masks exact except near-margin tiles, O within 1e-2, LSE
+within 1e-3; 4-bit codes bit for bit)."""
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import kvq4
+from tests import _parity
+
+pytestmark = pytest.mark.gpu
+INF = math.inf
+
+
+def _dev(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _taus(rng):
+    return (INF, float(np.round(rng.uniform(0.5, 8.0), 2)), 0.0)
+
+
+def _prefill_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        Hkv = int(rng.integers(1, 4))
+        G = int(rng.choice([1, 2, 3, 4, 5, 8]))
+        cfg = dict(kind="prefill", id=200 + i, B=int(rng.integers(1, 3)), Hq=G * Hkv,
+                   Hkv=Hkv, N=int(rng.integers(1, 700)), d=int(rng.choice([64, 128])),
+                   causal=bool(rng.integers(2)), sinks=bool(rng.integers(2)),
+                   band=bool(rng.integers(2)))
+        out.append((f"p{i}_B{cfg['B']}_H{cfg['Hq']}x{Hkv}_N{cfg['N']}_d{cfg['d']}"
+                    f"{'_c' if cfg['causal'] else ''}", cfg, _taus(rng)))
+    return out
+
+
+def _decode_cases(n, seed, base_id):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        Hkv = int(rng.integers(1, 3))
+        G = int(rng.integers(1, 17))
+        cfg = dict(kind="decode", id=base_id + i, B=int(rng.integers(1, 4)), Hq=G * Hkv,
+                   Hkv=Hkv, L=int(rng.integers(1, 9000)), d=int(rng.choice([64, 128])),
+                   sinks=bool(rng.integers(2)), window=bool(rng.integers(2)))
+        out.append((f"d{i}_B{cfg['B']}_H{cfg['Hq']}x{Hkv}_L{cfg['L']}_d{cfg['d']}", cfg,
+                    _taus(rng)))
+    return out
+
+
+PREFILL = _prefill_cases(24, 2026)
+DECODE = _decode_cases(16, 2027, 240)
+DECODE_Q4 = _decode_cases(12, 2028, 270)
+
+
+@pytest.mark.parametrize("name,cfg,taus", PREFILL, ids=[c[0] for c in PREFILL])
+def test_prefill_random_shape(name, cfg, taus):
+    import torch
+    import long_context_tiled_amd as lib
+    q, k, v = synth.make_prefill(cfg)
+    dq, dk, dv = _dev(q), _dev(k), _dev(v)
+    for tau in taus:
+        print(f"[random] {name} tau={tau}", flush=True)
+        o, lse, mask = lib.prefill(dq, dk, dv, cfg["causal"], tau, want_mask=True)
+        torch.cuda.synchronize()
+        rep = _parity.check_prefill(q, k, v, cfg["causal"], tau, o.cpu().numpy(),
+                                    lse.cpu().numpy(), mask.cpu().numpy())
+        print(f"  {rep}", flush=True)
+        assert rep.ok(), str(rep)
+
+
+@pytest.mark.parametrize("name,cfg,taus", PREFILL[:10], ids=[c[0] for c in PREFILL[:10]])
+def test_prefill_chunk_random_start(name, cfg, taus):
+    """A chunk at the end of the sequence: causal chunks start on a tile
+    boundary, non-causal ones anywhere."""
+    import torch
+    import long_context_tiled_amd as lib
+    q, k, v = synth.make_prefill(cfg)
+    N = q.shape[2]
+    rng = np.random.default_rng(cfg["id"])
+    q0 = int(rng.integers(0, N))
+    if cfg["causal"]:
+        q0 -= q0 % 64
+    dk, dv = _dev(k), _dev(v)
+    for tau in taus[:2]:
+        print(f"[random] chunk {name} q0={q0} tau={tau}", flush=True)
+        o, lse, mask = lib.prefill_chunk(_dev(q[:, :, q0:]), dk, dv, cfg["causal"], tau,
+                                         want_mask=True)
+        torch.cuda.synchronize()
+        rep = _parity.check_prefill(q[:, :, q0:], k, v, cfg["causal"], tau, o.cpu().numpy(),
+                                    lse.cpu().numpy(), mask.cpu().numpy(), q0=q0)
+        print(f"  {rep}", flush=True)
+        assert rep.ok(), str(rep)
+
+
+@pytest.mark.parametrize("name,cfg,taus", DECODE, ids=[c[0] for c in DECODE])
+def test_decode_random_shape(name, cfg, taus):
+    import torch
+    import long_context_tiled_amd as lib
+    q, k, v = synth.make_decode(cfg)
+    dq, dk, dv = _dev(q), _dev(k), _dev(v)
+    for tau in taus:
+        print(f"[random] {name} tau={tau}", flush=True)
+        o, lse, mask = lib.decode(dq, dk, dv, tau, want_mask=True)
+        torch.cuda.synchronize()
+        rep = _parity.check_decode(q, k, v, tau, o.cpu().numpy(), lse.cpu().numpy(),
+                                   mask.cpu().numpy())
+        print(f"  {rep}", flush=True)
+        assert rep.ok(), str(rep)
+
+
+@pytest.mark.parametrize("name,cfg,taus", DECODE_Q4, ids=[c[0] for c in DECODE_Q4])
+def test_decode_q4_random_shape(name, cfg, taus):
+    import torch
+    import long_context_tiled_amd as lib
+    q, k, v = synth.make_decode(cfg)
+    L = k.shape[2]
+    Hkv = k.shape[1]
+    print(f"[random] q4 {name}: quantise", flush=True)
+    cache = lib.quantize_q4(_dev(k), _dev(v))
+    torch.cuda.synchronize()
+    enc = kvq4.encode(synth.bf16_bits_to_f32(k), synth.bf16_bits_to_f32(v))
+    got = {n: t.cpu().numpy() for n, t in cache.items()}
+    for n in ("kq", "kp", "vq", "vp"):
+        g = got[n].view(np.uint32) if n in ("kp", "vp") else got[n]
+        assert np.array_equal(g, enc[n]), f"{n} differs from the oracle's encoding"
+
+    def kv_for(b, g):
+        return (kvq4.decode_k(enc["kq"][b, g], enc["kp"][b, g]),
+                kvq4.decode_v(enc["vq"][b, g], enc["vp"][b, g], L))
+    dq = _dev(q)
+    for tau in taus:
+        print(f"[random] q4 {name} tau={tau}", flush=True)
+        o, lse, mask = lib.decode_q4(dq, cache, L, tau, want_mask=True)
+        torch.cuda.synchronize()
+        rep = _parity.check_decode(q, None, None, tau, o.cpu().numpy(), lse.cpu().numpy(),
+                                   mask.cpu().numpy(), kv_for=kv_for, Hkv=Hkv)
+        print(f"  {rep}", flush=True)
+        assert rep.ok(), str(rep)
