@@ -52,13 +52,13 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 MEASURED_TRAFFIC = {
     "prefill": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp"),
                 "sha1": "997b1712c691d713dcef2bad76a69c55fe5807a3",
-                "bytes": (2749866.4 * 2.0 + 528384.0) * 1024},
+                "bytes": (2711139.9 * 2.0 + 528384.0) * 1024},
     "decode_q4": {"sources": ("kvq4.hip", "decode.hip", "common.hpp"),
                   "sha1": "0de8a66b284ec5266f1614bb5422477539b227b6",
-                  "bytes": (1148083.9 * 2.0 + 16647.2) * 1024},
+                  "bytes": (1148209.9 * 2.0 + 16642.4) * 1024},
     "decode": {"sources": ("decode.hip", "common.hpp"),
                "sha1": "c9d9a902f280df832bb299ffe1922fe72fd232dc",
-               "bytes": (4195496.4 * 2.0 + 16641.2) * 1024},
+               "bytes": (4195501.5 * 2.0 + 16641.6) * 1024},
 }
 
 
