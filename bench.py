@@ -53,8 +53,8 @@ MEASURED_TRAFFIC = {
     "prefill": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp"),
                 "sha1": "997b1712c691d713dcef2bad76a69c55fe5807a3",
                 "bytes": (2711139.9 * 2.0 + 528384.0) * 1024},
-    "decode_q4": {"sources": ("kvq4.hip", "decode.hip", "common.hpp"),
-                  "sha1": "0de8a66b284ec5266f1614bb5422477539b227b6",
+    "decode_q4": {"sources": ("kvq4.hip", "kvq_common.hpp", "decode.hip", "common.hpp"),
+                  "sha1": "277b7165a12ceab7053f3eb692423e54e83dc42f",
                   "bytes": (1148209.9 * 2.0 + 16642.4) * 1024},
     "decode": {"sources": ("decode.hip", "common.hpp"),
                "sha1": "c9d9a902f280df832bb299ffe1922fe72fd232dc",

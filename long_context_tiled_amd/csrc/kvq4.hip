@@ -50,47 +50,20 @@
 //   Every load instruction reads whole 128-byte lines of codes (K: 4 runs of
 //   4 rows; V: 16 rows of 32 bytes) with the non-temporal policy; the small
 //   parameter words use the default policy.
-#include "common.hpp"
+#include "kvq_common.hpp"
 #include "launch.hpp"
 
 namespace skipattn {
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-
 namespace {
 
-constexpr uint32_t kCfg = 0x00020000u;     // raw 32-bit buffer, range-checked
-constexpr uint32_t kNoRead = 0x80000000u;  // tile offset of a load that reads nothing
+using namespace kvq;
 
-__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
-  return __builtin_bit_cast(float, bits16 << 16);
-}
-
-// Non-negative finite fp32 rounded up to the bf16 grid.
-__device__ __forceinline__ float bf16_round_up(float x) {
-  uint32_t b = __builtin_bit_cast(uint32_t, x);
-  if (b & 0xffffu) b = (b + 0x10000u) & 0xffff0000u;
-  return __builtin_bit_cast(float, b);
-}
-
-// Block parameters and codes. The fp32 subtract and divide are rounded to
-// nearest even and are not fused with anything: they decide integers.
-__device__ __forceinline__ float block_scale(float lo, float hi) {
-  return bf16_round_up(__fdiv_rn(__fsub_rn(hi, lo), 15.0f));
-}
-__device__ __forceinline__ uint32_t code_of(float x, float s, float z) {
-  if (!(s > 0.f)) return 0u;
-  const float r = rintf(__fdiv_rn(__fsub_rn(x, z), s));
-  return (uint32_t)fminf(fmaxf(r, 0.f), 15.f);
-}
 // Eight codes (element order) -> one storage word.
 __device__ __forceinline__ uint32_t pack_word(const uint32_t (&c)[8]) {
   const uint32_t lo = c[0] | (c[2] << 4) | (c[4] << 8) | (c[6] << 12);
   const uint32_t hi = c[1] | (c[3] << 4) | (c[5] << 8) | (c[7] << 12);
   return lo | (hi << 16);
-}
-__device__ __forceinline__ uint32_t pack_params(float s, float z) {
-  return (__builtin_bit_cast(uint32_t, s) >> 16) | (__builtin_bit_cast(uint32_t, z) & 0xffff0000u);
 }
 
 // ---------------------------------------------------------------- quantiser
@@ -132,10 +105,10 @@ __global__ __launch_bounds__(256) void quant_k_kernel(const uint16_t* __restrict
     hi = fmaxf(hi, __shfl_xor(hi, off));
   }
   if (!ok) return;
-  const float s = block_scale(lo, hi);
+  const float s = block_scale<15>(lo, hi);
   uint32_t c[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = code_of(x[i], s, lo);
+  for (int i = 0; i < 8; ++i) c[i] = code_of<15>(x[i], s, lo);
   reinterpret_cast<uint32_t*>(kq + row * (D / 2))[w] = pack_word(c);
   if (w == 0) kp[row] = pack_params(s, lo);
 }
@@ -164,7 +137,7 @@ __global__ __launch_bounds__(D) void quant_v_kernel(const uint16_t* __restrict__
     lo = fminf(lo, x[j]);
     hi = fmaxf(hi, x[j]);
   }
-  const float s = block_scale(lo, hi);
+  const float s = block_scale<15>(lo, hi);
   const long long blk = (bg * T + t) * D + ch;
   u32x4 out[2];
 #pragma unroll
@@ -173,7 +146,7 @@ __global__ __launch_bounds__(D) void quant_v_kernel(const uint16_t* __restrict__
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int j = 8 * wd + e;
-      c[e] = j < n ? code_of(x[j], s, lo) : 0u;
+      c[e] = j < n ? code_of<15>(x[j], s, lo) : 0u;
     }
     out[wd >> 2][wd & 3] = pack_word(c);
   }
@@ -184,20 +157,6 @@ __global__ __launch_bounds__(D) void quant_v_kernel(const uint16_t* __restrict__
 }
 
 // ------------------------------------------------------------ decode kernel
-constexpr int kNT = 2;  // non-temporal cache policy
-constexpr int kRT = 0;  // default cache policy
-template <int AUX>
-__device__ __forceinline__ u32x4 ld4(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, AUX));
-}
-template <int AUX>
-__device__ __forceinline__ uint32_t ld1(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(rs, (int)off, 0, AUX);
-}
-template <int AUX>
-__device__ __forceinline__ u32x2 ld2(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, AUX));
-}
 
 // The constants of the expand_word functions, held in registers: gfx9 VOP3 encodings
 // take no literal, so with the mask in an SGPR and the magic in a VGPR the
@@ -247,8 +206,6 @@ __device__ __forceinline__ f16x8 expand_word_f16(uint32_t w, const ExpandConsts&
 }
 
 
-__device__ __forceinline__ float param_s(uint32_t p) { return __builtin_bit_cast(float, p << 16); }
-__device__ __forceinline__ float param_z(uint32_t p) { return __builtin_bit_cast(float, p & 0xffff0000u); }
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
