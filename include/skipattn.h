@@ -237,6 +237,43 @@ int attn_decode_q4_check(const void* q, const uint8_t* kq, const uint32_t* kp,
                          const uint8_t* skip_mask, const void* workspace,
                          size_t workspace_bytes);
 
+/*
+ * 2-bit asymmetric KV cache: the same talk's lossy but faster width. The
+ * blocks, parameters and rounding are those of the 4-bit cache with 3 in
+ * place of 15 (s = (maximum - z) / 3 rounded up to bf16, code = clamp(rint(
+ * (x - z) / s), 0, 3)). A 32-bit word holds 16 consecutive elements:
+ * elements 0, 2, .., 14 in the 2-bit fields 0..7 of bits 0-15 and elements
+ * 1, 3, .., 15 in those of bits 16-31. Arrays (T = ceil(L / 64)), all
+ * 16-byte aligned:
+ *   kq  uint8  [B, Hkv, L, d/4]       K codes, row by row
+ *   kp  uint32 [B, Hkv, L]            K parameter word per key
+ *   vq  uint8  [B, Hkv, T, d, 16]     V codes: per tile and channel, the 64
+ *                                     keys' codes (keys past L: code 0)
+ *   vp  uint32 [B, Hkv, T, d]         V parameter word per (tile, channel)
+ * The quantisers and the decode take the arguments, follow the rules and
+ * return the errors of their 4-bit counterparts. In the decode, P.V runs on
+ * fp16 probabilities scaled by 64, 16, 4 or 1 (exact) per key, with the
+ * same bound on the LSE.
+ */
+int attn_kv_quantize_q2(const void* k, const void* v, uint8_t* kq, uint32_t* kp,
+                        uint8_t* vq, uint32_t* vp, int B, int Hkv, int L,
+                        int d, void* stream);
+int attn_kv_quantize_q2_range(const void* k, const void* v, uint8_t* kq,
+                              uint32_t* kp, uint8_t* vq, uint32_t* vp, int B,
+                              int Hkv, int L, int d, int k0, int k1,
+                              void* stream);
+int attn_decode_q2(const void* q, const uint8_t* kq, const uint32_t* kp,
+                   const uint8_t* vq, const uint32_t* vp, float* o,
+                   float* lse, int B, int Hq, int Hkv, int L, int d,
+                   float tau, uint8_t* skip_mask, void* workspace,
+                   size_t workspace_bytes, void* stream);
+int attn_decode_q2_check(const void* q, const uint8_t* kq, const uint32_t* kp,
+                         const uint8_t* vq, const uint32_t* vp,
+                         const float* o, const float* lse, int B, int Hq,
+                         int Hkv, int L, int d, float tau,
+                         const uint8_t* skip_mask, const void* workspace,
+                         size_t workspace_bytes);
+
 /* Text for the last nonzero return on this thread ("" if none). */
 const char* attn_last_error(void);
 

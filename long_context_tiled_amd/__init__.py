@@ -6,11 +6,13 @@ from ._lib import (OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, TILE, SPLIT,
                    load, attn_prefill, attn_decode, attn_decode_workspace_bytes,
                    attn_last_error, prefill, decode, q4_shapes, attn_kv_quantize_q4,
                    attn_decode_q4, quantize_q4, decode_q4, attn_prefill_chunk, prefill_chunk,
-                   empty_q4)
+                   empty_q4, q2_shapes, attn_kv_quantize_q2, attn_decode_q2, quantize_q2,
+                   decode_q2, empty_q2)
 
 __all__ = ["OK", "EINVAL", "EUNSUPPORTED", "EWORKSPACE", "EHIP", "TILE", "SPLIT",
            "KEPT", "SKIPPED", "NOT_VISITED", "EXPORTS", "LIB_PATH", "SkipAttnError",
            "load", "attn_prefill", "attn_decode", "attn_decode_workspace_bytes",
            "attn_last_error", "prefill", "decode", "q4_shapes", "attn_kv_quantize_q4",
            "attn_decode_q4", "quantize_q4", "decode_q4", "attn_prefill_chunk",
-           "prefill_chunk", "empty_q4"]
+           "prefill_chunk", "empty_q4", "q2_shapes", "attn_kv_quantize_q2",
+           "attn_decode_q2", "quantize_q2", "decode_q2", "empty_q2"]

@@ -23,7 +23,9 @@ KEPT, SKIPPED, NOT_VISITED = 0, 1, 2
 EXPORTS = ("attn_prefill", "attn_decode", "attn_decode_workspace_bytes",
            "attn_prefill_check", "attn_decode_check", "attn_last_error",
            "attn_kv_quantize_q4", "attn_decode_q4", "attn_decode_q4_check",
-           "attn_prefill_chunk", "attn_prefill_chunk_check", "attn_kv_quantize_q4_range")
+           "attn_prefill_chunk", "attn_prefill_chunk_check", "attn_kv_quantize_q4_range",
+           "attn_kv_quantize_q2", "attn_kv_quantize_q2_range", "attn_decode_q2",
+           "attn_decode_q2_check")
 
 _lib = None
 
@@ -59,16 +61,19 @@ def load() -> ctypes.CDLL:
     lib.attn_decode_check.restype = i
     lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i]
     lib.attn_decode_workspace_bytes.restype = sz
-    lib.attn_kv_quantize_q4.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
-    lib.attn_kv_quantize_q4.restype = i
-    lib.attn_kv_quantize_q4_range.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
-    lib.attn_kv_quantize_q4_range.restype = i
-    lib.attn_decode_q4.argtypes = [vp, vp, vp, vp, vp, f32p, f32p, i, i, i, i, i, f, u8p, vp,
-                                   sz, vp]
-    lib.attn_decode_q4.restype = i
-    lib.attn_decode_q4_check.argtypes = [vp, vp, vp, vp, vp, f32p, f32p, i, i, i, i, i, f,
-                                         u8p, vp, sz]
-    lib.attn_decode_q4_check.restype = i
+    for w in ("q4", "q2"):
+        fn = getattr(lib, f"attn_kv_quantize_{w}")
+        fn.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
+        fn.restype = i
+        fn = getattr(lib, f"attn_kv_quantize_{w}_range")
+        fn.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+        fn.restype = i
+        fn = getattr(lib, f"attn_decode_{w}")
+        fn.argtypes = [vp, vp, vp, vp, vp, f32p, f32p, i, i, i, i, i, f, u8p, vp, sz, vp]
+        fn.restype = i
+        fn = getattr(lib, f"attn_decode_{w}_check")
+        fn.argtypes = [vp, vp, vp, vp, vp, f32p, f32p, i, i, i, i, i, f, u8p, vp, sz]
+        fn.restype = i
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -181,45 +186,48 @@ def attn_decode(q, k, v, o, lse, tau: float, workspace, skip_mask=None,
 
 def q4_shapes(B: int, Hkv: int, L: int, d: int) -> dict:
     """Shapes of the 4-bit cache arrays (kq, kp, vq, vp)."""
+    return _cache_shapes(4, B, Hkv, L, d)
+
+
+def q2_shapes(B: int, Hkv: int, L: int, d: int) -> dict:
+    """Shapes of the 2-bit cache arrays (kq, kp, vq, vp)."""
+    return _cache_shapes(2, B, Hkv, L, d)
+
+
+def _cache_shapes(bits, B, Hkv, L, d):
     T = (L + TILE - 1) // TILE
-    return dict(kq=(B, Hkv, L, d // 2), kp=(B, Hkv, L), vq=(B, Hkv, T, d, 32),
-                vp=(B, Hkv, T, d))
+    per_byte = 8 // bits
+    return dict(kq=(B, Hkv, L, d // per_byte), kp=(B, Hkv, L),
+                vq=(B, Hkv, T, d, TILE // per_byte), vp=(B, Hkv, T, d))
 
 
-def _check_q4(cache, B, Hkv, L, d):
+def _check_cache(bits, cache, B, Hkv, L, d):
     import torch
-    shp = q4_shapes(B, Hkv, L, d)
+    shp = _cache_shapes(bits, B, Hkv, L, d)
     for name, dt in (("kq", torch.uint8), ("kp", torch.int32), ("vq", torch.uint8),
                      ("vp", torch.int32)):
         _check(cache[name], name, dt, shp[name])
 
 
-def attn_kv_quantize_q4(k, v, cache, stream=None, key_range=None) -> None:
-    """Enqueue the 4-bit quantiser: k/v [B,Hkv,L,d] bf16 -> cache dict of
-    kq uint8, kp int32 (parameter words), vq uint8, vp int32 tensors with the
-    shapes of q4_shapes(). ``key_range=(k0, k1)`` writes only those keys
-    (k0 a multiple of 64), e.g. a chunk appended after a chunked prefill."""
+def _quantize(bits, k, v, cache, stream, key_range):
     import torch
     B, Hkv, L, d = k.shape
     _check(k, "k", torch.bfloat16, (B, Hkv, L, d))
     _check(v, "v", torch.bfloat16, (B, Hkv, L, d))
-    _check_q4(cache, B, Hkv, L, d)
+    _check_cache(bits, cache, B, Hkv, L, d)
     k0, k1 = (0, L) if key_range is None else key_range
-    rc = load().attn_kv_quantize_q4_range(_ptr(k), _ptr(v), _ptr(cache["kq"]), _ptr(cache["kp"]),
-                                          _ptr(cache["vq"]), _ptr(cache["vp"]), B, Hkv, L, d,
-                                          int(k0), int(k1), _stream(stream))
+    fn = getattr(load(), f"attn_kv_quantize_q{bits}_range")
+    rc = fn(_ptr(k), _ptr(v), _ptr(cache["kq"]), _ptr(cache["kp"]), _ptr(cache["vq"]),
+            _ptr(cache["vp"]), B, Hkv, L, d, int(k0), int(k1), _stream(stream))
     _raise(rc)
 
 
-def attn_decode_q4(q, cache, L: int, o, lse, tau: float, workspace, skip_mask=None,
-                   stream=None) -> None:
-    """Enqueue split-K decode over a 4-bit cache (dict as for
-    attn_kv_quantize_q4, holding L keys); other arguments as attn_decode."""
+def _decode_cache(bits, q, cache, L, o, lse, tau, workspace, skip_mask, stream):
     import torch
     B, Hq, d = q.shape
     Hkv = cache["kp"].shape[1]
     _check(q, "q", torch.bfloat16, (B, Hq, d))
-    _check_q4(cache, B, Hkv, L, d)
+    _check_cache(bits, cache, B, Hkv, L, d)
     _check(o, "o", torch.float32, (B, Hq, d))
     _check(lse, "lse", torch.float32, (B, Hq))
     if skip_mask is not None:
@@ -227,21 +235,56 @@ def attn_decode_q4(q, cache, L: int, o, lse, tau: float, workspace, skip_mask=No
     if workspace.device.type != "cuda" or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
     nbytes = workspace.numel() * workspace.element_size()
-    rc = load().attn_decode_q4(_ptr(q), _ptr(cache["kq"]), _ptr(cache["kp"]),
-                               _ptr(cache["vq"]), _ptr(cache["vp"]), _ptr(o), _ptr(lse), B,
-                               Hq, Hkv, L, d, float(tau), _ptr(skip_mask), _ptr(workspace),
-                               nbytes, _stream(stream))
+    fn = getattr(load(), f"attn_decode_q{bits}")
+    rc = fn(_ptr(q), _ptr(cache["kq"]), _ptr(cache["kp"]), _ptr(cache["vq"]),
+            _ptr(cache["vp"]), _ptr(o), _ptr(lse), B, Hq, Hkv, L, d, float(tau),
+            _ptr(skip_mask), _ptr(workspace), nbytes, _stream(stream))
     _raise(rc)
+
+
+def attn_kv_quantize_q4(k, v, cache, stream=None, key_range=None) -> None:
+    """Enqueue the 4-bit quantiser: k/v [B,Hkv,L,d] bf16 -> cache dict of
+    kq uint8, kp int32 (parameter words), vq uint8, vp int32 tensors with the
+    shapes of q4_shapes(). ``key_range=(k0, k1)`` writes only those keys
+    (k0 a multiple of 64), e.g. a chunk appended after a chunked prefill."""
+    _quantize(4, k, v, cache, stream, key_range)
+
+
+def attn_kv_quantize_q2(k, v, cache, stream=None, key_range=None) -> None:
+    """The 2-bit quantiser; arguments as attn_kv_quantize_q4, shapes of q2_shapes()."""
+    _quantize(2, k, v, cache, stream, key_range)
+
+
+def attn_decode_q4(q, cache, L: int, o, lse, tau: float, workspace, skip_mask=None,
+                   stream=None) -> None:
+    """Enqueue split-K decode over a 4-bit cache (dict as for
+    attn_kv_quantize_q4, holding L keys); other arguments as attn_decode."""
+    _decode_cache(4, q, cache, L, o, lse, tau, workspace, skip_mask, stream)
+
+
+def attn_decode_q2(q, cache, L: int, o, lse, tau: float, workspace, skip_mask=None,
+                   stream=None) -> None:
+    """Split-K decode over a 2-bit cache; arguments as attn_decode_q4."""
+    _decode_cache(2, q, cache, L, o, lse, tau, workspace, skip_mask, stream)
 
 
 # ---- allocation conveniences around the entry points ----
 
-def empty_q4(B: int, Hkv: int, L: int, d: int, device) -> dict:
-    """Allocate (uninitialised) 4-bit cache arrays for L keys."""
+def _empty_cache(bits, B, Hkv, L, d, device):
     import torch
-    shp = q4_shapes(B, Hkv, L, d)
+    shp = _cache_shapes(bits, B, Hkv, L, d)
     return {n: torch.empty(shp[n], dtype=torch.uint8 if n in ("kq", "vq") else torch.int32,
                            device=device) for n in shp}
+
+
+def empty_q4(B: int, Hkv: int, L: int, d: int, device) -> dict:
+    """Allocate (uninitialised) 4-bit cache arrays for L keys."""
+    return _empty_cache(4, B, Hkv, L, d, device)
+
+
+def empty_q2(B: int, Hkv: int, L: int, d: int, device) -> dict:
+    """Allocate (uninitialised) 2-bit cache arrays for L keys."""
+    return _empty_cache(2, B, Hkv, L, d, device)
 
 
 def quantize_q4(k, v, stream=None) -> dict:
@@ -252,10 +295,15 @@ def quantize_q4(k, v, stream=None) -> dict:
     return cache
 
 
-def decode_q4(q, cache, L: int, tau: float = math.inf, want_mask: bool = False,
-              workspace=None, stream=None):
-    """Allocate outputs (and the workspace if not given) and call
-    attn_decode_q4. Returns (o, lse, mask)."""
+def quantize_q2(k, v, stream=None) -> dict:
+    """Allocate a 2-bit cache with torch and fill it from bf16 k, v."""
+    B, Hkv, L, d = k.shape
+    cache = empty_q2(B, Hkv, L, d, k.device)
+    attn_kv_quantize_q2(k, v, cache, stream)
+    return cache
+
+
+def _decode_alloc(bits, q, cache, L, tau, want_mask, workspace, stream):
     import torch
     B, Hq, d = q.shape
     o = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
@@ -267,8 +315,21 @@ def decode_q4(q, cache, L: int, tau: float = math.inf, want_mask: bool = False,
     if workspace is None:
         nbytes = max(16, attn_decode_workspace_bytes(B, Hq, L, d))
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    attn_decode_q4(q, cache, L, o, lse, tau, workspace, mask, stream)
+    _decode_cache(bits, q, cache, L, o, lse, tau, workspace, mask, stream)
     return o, lse, mask
+
+
+def decode_q4(q, cache, L: int, tau: float = math.inf, want_mask: bool = False,
+              workspace=None, stream=None):
+    """Allocate outputs (and the workspace if not given) and call
+    attn_decode_q4. Returns (o, lse, mask)."""
+    return _decode_alloc(4, q, cache, L, tau, want_mask, workspace, stream)
+
+
+def decode_q2(q, cache, L: int, tau: float = math.inf, want_mask: bool = False,
+              workspace=None, stream=None):
+    """As decode_q4, over a 2-bit cache."""
+    return _decode_alloc(2, q, cache, L, tau, want_mask, workspace, stream)
 
 
 # ---- allocation conveniences around the two bf16 entry points ----

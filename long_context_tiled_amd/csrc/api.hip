@@ -175,10 +175,17 @@ int attn_decode_q4_check(const void* q, const uint8_t* kq, const uint32_t* kp,
                            workspace_bytes);
 }
 
-int attn_decode_q4(const void* q, const uint8_t* kq, const uint32_t* kp, const uint8_t* vq,
-                   const uint32_t* vp, float* o, float* lse, int B, int Hq, int Hkv, int L, int d,
-                   float tau, uint8_t* skip_mask, void* workspace, size_t workspace_bytes,
-                   void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The shared body of the 4-bit and 2-bit cache decodes: both take the same
+// arguments and differ only in the kernels.
+int decode_quantized(int (*launch)(const skipattn::DecodeQ4Args&), const char* what,
+                     const void* q, const uint8_t* kq, const uint32_t* kp, const uint8_t* vq,
+                     const uint32_t* vp, float* o, float* lse, int B, int Hq, int Hkv, int L,
+                     int d, float tau, uint8_t* skip_mask, void* workspace,
+                     size_t workspace_bytes, void* stream) {
   if (int e = attn_decode_q4_check(q, kq, kp, vq, vp, o, lse, B, Hq, Hkv, L, d, tau, skip_mask,
                                    workspace, workspace_bytes))
     return e;
@@ -189,15 +196,16 @@ int attn_decode_q4(const void* q, const uint8_t* kq, const uint32_t* kp, const u
   skipattn::DecodeQ4Args a{q,         kq,   kp,     vq, vp,     o,  lse,      skip_mask,
                            ws_o,      ws_lse, B,   Hq, Hkv, L, d, nsplit,
                            tau_raw(tau, d), exp2_scale(d), stream};
-  if (skipattn::launch_decode_q4(a) != 0) return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
+  if (launch(a) != 0) return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return fail(SKIPATTN_EHIP, "decode_q4 launch: %s", hipGetErrorString(err));
+  if (err != hipSuccess) return fail(SKIPATTN_EHIP, "%s launch: %s", what, hipGetErrorString(err));
   return SKIPATTN_OK;
 }
 
-int attn_kv_quantize_q4_range(const void* k, const void* v, uint8_t* kq, uint32_t* kp,
-                              uint8_t* vq, uint32_t* vp, int B, int Hkv, int L, int d, int k0,
-                              int k1, void* stream) {
+// The shared body of the 4-bit and 2-bit quantisers.
+int quantize_range(int (*launch)(const skipattn::QuantArgs&), const void* k, const void* v,
+                   uint8_t* kq, uint32_t* kp, uint8_t* vq, uint32_t* vp, int B, int Hkv, int L,
+                   int d, int k0, int k1, void* stream) {
   g_err[0] = '\0';
   if (!k || !v || !kq || !kp || !vq || !vp) return fail(SKIPATTN_EINVAL, "NULL tensor pointer");
   if (B < 0 || L < 0 || d < 0) return fail(SKIPATTN_EINVAL, "negative size (B=%d L=%d d=%d)", B, L, d);
@@ -217,15 +225,63 @@ int attn_kv_quantize_q4_range(const void* k, const void* v, uint8_t* kq, uint32_
     return fail(SKIPATTN_EUNSUPPORTED, "k0 (%d) must be a multiple of 64", k0);
   if (B == 0 || k1 == k0) return SKIPATTN_OK;
   skipattn::QuantArgs a{k, v, kq, kp, vq, vp, B, Hkv, L, d, k0, k1, stream};
-  if (skipattn::launch_kv_quantize_q4(a) != 0) return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
+  if (launch(a) != 0) return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(SKIPATTN_EHIP, "quantize launch: %s", hipGetErrorString(err));
   return SKIPATTN_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int attn_decode_q4(const void* q, const uint8_t* kq, const uint32_t* kp, const uint8_t* vq,
+                   const uint32_t* vp, float* o, float* lse, int B, int Hq, int Hkv, int L, int d,
+                   float tau, uint8_t* skip_mask, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  return decode_quantized(skipattn::launch_decode_q4, "decode_q4", q, kq, kp, vq, vp, o, lse, B,
+                          Hq, Hkv, L, d, tau, skip_mask, workspace, workspace_bytes, stream);
+}
+
+int attn_kv_quantize_q4_range(const void* k, const void* v, uint8_t* kq, uint32_t* kp,
+                              uint8_t* vq, uint32_t* vp, int B, int Hkv, int L, int d, int k0,
+                              int k1, void* stream) {
+  return quantize_range(skipattn::launch_kv_quantize_q4, k, v, kq, kp, vq, vp, B, Hkv, L, d, k0,
+                        k1, stream);
+}
+
 int attn_kv_quantize_q4(const void* k, const void* v, uint8_t* kq, uint32_t* kp, uint8_t* vq,
                         uint32_t* vp, int B, int Hkv, int L, int d, void* stream) {
   return attn_kv_quantize_q4_range(k, v, kq, kp, vq, vp, B, Hkv, L, d, 0, L < 0 ? 0 : L, stream);
+}
+
+int attn_decode_q2_check(const void* q, const uint8_t* kq, const uint32_t* kp,
+                         const uint8_t* vq, const uint32_t* vp, const float* o,
+                         const float* lse, int B, int Hq, int Hkv, int L, int d, float tau,
+                         const uint8_t* skip_mask, const void* workspace,
+                         size_t workspace_bytes) {
+  return attn_decode_q4_check(q, kq, kp, vq, vp, o, lse, B, Hq, Hkv, L, d, tau, skip_mask,
+                              workspace, workspace_bytes);
+}
+
+int attn_decode_q2(const void* q, const uint8_t* kq, const uint32_t* kp, const uint8_t* vq,
+                   const uint32_t* vp, float* o, float* lse, int B, int Hq, int Hkv, int L, int d,
+                   float tau, uint8_t* skip_mask, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  return decode_quantized(skipattn::launch_decode_q2, "decode_q2", q, kq, kp, vq, vp, o, lse, B,
+                          Hq, Hkv, L, d, tau, skip_mask, workspace, workspace_bytes, stream);
+}
+
+int attn_kv_quantize_q2_range(const void* k, const void* v, uint8_t* kq, uint32_t* kp,
+                              uint8_t* vq, uint32_t* vp, int B, int Hkv, int L, int d, int k0,
+                              int k1, void* stream) {
+  return quantize_range(skipattn::launch_kv_quantize_q2, k, v, kq, kp, vq, vp, B, Hkv, L, d, k0,
+                        k1, stream);
+}
+
+int attn_kv_quantize_q2(const void* k, const void* v, uint8_t* kq, uint32_t* kp, uint8_t* vq,
+                        uint32_t* vp, int B, int Hkv, int L, int d, void* stream) {
+  return attn_kv_quantize_q2_range(k, v, kq, kp, vq, vp, B, Hkv, L, d, 0, L < 0 ? 0 : L, stream);
 }
 
 }  // extern "C"

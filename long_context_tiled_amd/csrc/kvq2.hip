@@ -1,0 +1,512 @@
+// 2-bit asymmetric KV cache: the quantiser (bf16 K, V -> stored format) and
+// the split-K decode that reads the stored format directly.
+//
+// Method: the TurboAttention talk page ("Technical Deep Dive", the pre-fill /
+// decoding workflow and the trade-offs it lists) stores the KV cache as
+// low-bit asymmetric integers with a floating zero point per block, with a
+// near-lossless 4-bit and a lossy, faster 2-bit option; this file is the
+// 2-bit option (kvq4.hip the 4-bit one). Decoding runs the Skip-Softmax rule
+// (TensorRT-LLM Skip Softmax summary page, "Key Points", "Detailed Analysis")
+// per query head over 64-key tiles, each 4096-key split with its own running
+// maximum, exactly as the other decodes do.
+//
+// Format (readings where the pages are silent): blocks as for 4-bit (a K
+// block is one key row, a V block one channel of one 64-key tile); z = block
+// minimum, s = (max - z) / 3 in fp32 rounded up to bf16, code =
+// clamp(rint((x - z) / s), 0, 3) in fp32. A 32-bit word holds 16 consecutive
+// elements: the even ones in the 2-bit fields of bits 0-15, the odd ones in
+// those of bits 16-31. kq [B,Hkv,L,d/4] u8, kp [B,Hkv,L] u32, vq
+// [B,Hkv,T,d,16] u8 (64 keys of a channel per tile, keys past L code 0),
+// vp [B,Hkv,T,d] u32, T = ceil(L/64).
+//
+// Decode split kernel: one wave per (sequence, KV head, split), the layout
+// of the 4-bit decode (P the A operand of the PV product, O head-major, two
+// register sets per operand, no LDS memory):
+//   q.K on v_mfma_f32_16x16x32_bf16: each code expanded to the exact bf16
+//   value 128 + c (field moved to bits 0..1 and or-ed into 0x4300), the
+//   accumulator started at -128 sum(q), so q.k^ = s (q.c) + z sum(q).
+//   P.V on v_mfma_f32_16x16x32_f16: codes expanded by masks alone to the
+//   exact fp16 values 1024 + 4^f c, f the field's place in its byte (fp16
+//   1024 has 10 mantissa bits, so 64 c fits), and the factor moved to P:
+//   P' = (64 / 4^f) P (exponent input + 6 - 2f), rounded to fp16 (<= 64).
+//   Then P'.(expanded) = 64 P.c + 1024 sum(P'); with the accumulator started
+//   at -1024 sum(P'), sum_j p_j v^_jc = (s_c / 64) (64 P.c) + z_c sum(P),
+//   where sum(P) (also the row sum) and -1024 sum(P') come from MFMAs over
+//   the same fp16 P'.
+//   Key order inside a tile as for 4-bit: lane (head, grp) owns keys
+//   16 grp .. 16 grp + 15, which are word grp of every V code row (its two
+//   halves the two PV k-steps), and its K rows are 16 (hl >> 2) + 4 mb +
+//   (hl & 3) with lane group grp reading the d range [grp d/4, (grp+1) d/4),
+//   word ks / 2, half ks % 2 for k-step ks. Every code load covers whole
+//   128-byte lines with the non-temporal policy.
+#include "kvq_common.hpp"
+#include "launch.hpp"
+
+namespace skipattn {
+
+namespace {
+
+using namespace kvq;
+
+// Sixteen codes (element order) -> one storage word.
+__device__ __forceinline__ uint32_t pack_word2(const uint32_t (&c)[16]) {
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int f = 0; f < 8; ++f) {
+    lo |= c[2 * f] << (2 * f);
+    hi |= c[2 * f + 1] << (2 * f);
+  }
+  return lo | (hi << 16);
+}
+
+// ---------------------------------------------------------------- quantiser
+// K: W = D/16 lanes per key row, each lane one word (16 elements: 32 bytes of
+// bf16 in by two 16-byte loads, 4 bytes of codes out); the row's minimum and
+// maximum by xor shuffles. Rows are the keys k0 .. k1 - 1 of every (b, g).
+template <int D>
+__global__ __launch_bounds__(256) void quant_k2_kernel(const uint16_t* __restrict__ k,
+                                                       uint8_t* __restrict__ kq,
+                                                       uint32_t* __restrict__ kp,
+                                                       long long rows, int L, int k0, int nk) {
+  constexpr int W = D / 16;
+  const int lane = threadIdx.x & 63;
+  const long long idx = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / W) + lane / W;
+  const int w = lane % W;
+  const bool ok = idx < rows;
+  const long long row = ok ? (idx / nk) * L + k0 + idx % nk : 0;  // key row in the cache
+  float x[16];
+  if (ok) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(k + row * D + 16 * w);
+    const u32x4 r0 = src[0], r1 = src[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16_to_f32(r0[i] & 0xffffu);
+      x[2 * i + 1] = bf16_to_f32(r0[i] >> 16);
+      x[8 + 2 * i] = bf16_to_f32(r1[i] & 0xffffu);
+      x[8 + 2 * i + 1] = bf16_to_f32(r1[i] >> 16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = 0.f;
+  }
+  float lo = x[0], hi = x[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) {
+    lo = fminf(lo, x[i]);
+    hi = fmaxf(hi, x[i]);
+  }
+#pragma unroll
+  for (int off = 1; off < W; off <<= 1) {
+    lo = fminf(lo, __shfl_xor(lo, off));
+    hi = fmaxf(hi, __shfl_xor(hi, off));
+  }
+  if (!ok) return;
+  const float s = block_scale<3>(lo, hi);
+  uint32_t c[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) c[i] = code_of<3>(x[i], s, lo);
+  reinterpret_cast<uint32_t*>(kq + row * (D / 4))[w] = pack_word2(c);
+  if (w == 0) kp[row] = pack_params(s, lo);
+}
+
+// V: one thread per channel of one 64-key tile (block = one (b, g, tile));
+// the tile's 64 values of the channel in registers, its 16-byte code row out
+// as one store. Tiles t0 .. t0 + nt - 1; a tile holds its keys below k1.
+template <int D>
+__global__ __launch_bounds__(D) void quant_v2_kernel(const uint16_t* __restrict__ v,
+                                                     uint8_t* __restrict__ vq,
+                                                     uint32_t* __restrict__ vp, int L, int T,
+                                                     int t0, int nt, int k1) {
+  const int ch = threadIdx.x;
+  const long long bg = blockIdx.x / nt;
+  const int t = t0 + blockIdx.x % nt;
+  const int n = min(kTile, k1 - kTile * t);
+  const uint16_t* src = v + (bg * L + (long long)kTile * t) * D + ch;
+  float x[kTile];
+#pragma unroll
+  for (int j = 0; j < kTile; ++j) x[j] = j < n ? bf16_to_f32(src[(long long)j * D]) : x[0];
+  float lo = x[0], hi = x[0];
+#pragma unroll
+  for (int j = 1; j < kTile; ++j) {
+    lo = fminf(lo, x[j]);
+    hi = fmaxf(hi, x[j]);
+  }
+  const float s = block_scale<3>(lo, hi);
+  const long long blk = (bg * T + t) * D + ch;
+  u32x4 out;
+#pragma unroll
+  for (int wd = 0; wd < 4; ++wd) {
+    uint32_t c[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int j = 16 * wd + e;
+      c[e] = j < n ? code_of<3>(x[j], s, lo) : 0u;
+    }
+    out[wd] = pack_word2(c);
+  }
+  *reinterpret_cast<u32x4*>(vq + blk * 16) = out;
+  vp[blk] = pack_params(s, lo);
+}
+
+// ------------------------------------------------------------ decode kernel
+// The constants of the code expansions, in registers so that each
+// shift-free mask-and-or is one v_and_or_b32 (gfx9 VOP3 takes no literal):
+// the four 2-bit field masks of both 16-bit halves in SGPRs, the bf16 and
+// fp16 magics in VGPRs.
+struct Expand2Consts {
+  uint32_t m[4];    // 0x00030003 << 2 f
+  uint32_t bmagic;  // 0x43004300: bf16 128 in both halves
+  uint32_t hmagic;  // 0x64006400: fp16 1024 in both halves
+};
+__device__ __forceinline__ Expand2Consts expand2_consts() {
+  Expand2Consts k;
+  asm volatile("s_mov_b32 %0, 0x00030003" : "=s"(k.m[0]));
+  asm volatile("s_mov_b32 %0, 0x000c000c" : "=s"(k.m[1]));
+  asm volatile("s_mov_b32 %0, 0x00300030" : "=s"(k.m[2]));
+  asm volatile("s_mov_b32 %0, 0x00c000c0" : "=s"(k.m[3]));
+  asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(k.bmagic));
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(k.hmagic));
+  return k;
+}
+
+// Half h of a storage word (elements 8 h .. 8 h + 7) -> bf16 values 128 + c,
+// element order: field f of each half of byte h, moved to bits 0..1.
+__device__ __forceinline__ bf16x8 expand2_bf16(uint32_t w, int h, const Expand2Consts& k) {
+  const uint32_t x = h ? (w >> 8) : w;
+  u32x4 r;
+  r[0] = (x & k.m[0]) | k.bmagic;
+  r[1] = ((x >> 2) & k.m[0]) | k.bmagic;
+  r[2] = ((x >> 4) & k.m[0]) | k.bmagic;
+  r[3] = ((x >> 6) & k.m[0]) | k.bmagic;
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Half h of a storage word -> fp16 values 1024 + 4^f c (field f in place).
+__device__ __forceinline__ f16x8 expand2_f16(uint32_t w, int h, const Expand2Consts& k) {
+  const uint32_t x = h ? (w >> 8) : w;
+  u32x4 r;
+#pragma unroll
+  for (int f = 0; f < 4; ++f) r[f] = (x & k.m[f]) | k.hmagic;
+  return __builtin_bit_cast(f16x8, r);
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void decode_q2_split_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ kq,
+    const uint32_t* __restrict__ kp, const uint8_t* __restrict__ vq,
+    const uint32_t* __restrict__ vp, float* __restrict__ ws_o, float* __restrict__ ws_lse,
+    uint8_t* __restrict__ mask, int Hq, int Hkv, int L, int nsplit, float tau_raw, float c,
+    int nwork) {
+  constexpr int KS = D / 32;  // QK k-steps
+  constexpr int KW = D / 64;  // code words per lane per K row
+  constexpr int DB = D / 16;  // 16-channel blocks of O and of V code rows
+  constexpr int RB = D / 4;   // bytes of codes per K row
+  static_assert(kSplit / kTile <= 64, "the per-lane skip bits hold one split");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int work = blockIdx.x * 4 + wave;
+  if (work >= nwork) return;  // whole wave leaves; the kernel has no barrier
+  const int sp = work % nsplit;
+  const int bg = work / nsplit;
+  const int g = bg % Hkv;
+  const int b = bg / Hkv;
+  const int G = Hq / Hkv;
+  const int hl = lane & 15;
+  const int grp = lane >> 4;
+  const int T = (L + kTile - 1) / kTile;
+
+  const size_t head = (size_t)(b * Hkv + g);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(kq + head * L * RB), (short)0, L * RB, kCfg);
+  const __amdgpu_buffer_rsrc_t kprs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(kp + head * L), (short)0, L * 4, kCfg);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(vq + head * T * D * 16), (short)0, T * D * 16, kCfg);
+  const __amdgpu_buffer_rsrc_t vprs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(vp + head * T * D), (short)0, T * D * 4, kCfg);
+
+  const int key_begin = sp * kSplit;
+  const int key_end = min(L, key_begin + kSplit);
+  const int ntile = (key_end - key_begin + kTile - 1) / kTile;
+  const int tile_begin = key_begin / kTile;
+  const bool head_ok = hl < G;
+  const size_t bh = (size_t)b * Hq + g * G + hl;
+
+  // q^T fragments (B operand, n = head): lane group grp holds d range
+  // [grp D/4, (grp + 1) D/4), k-step ks its elements 8 ks .. 8 ks + 7.
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (head_ok) x = ldg16(q + bh * D + grp * (D / 4) + 8 * ks);
+    qf[ks] = as_bf16x8(x);
+  }
+  const Expand2Consts xk = expand2_consts();
+  // sum_d q_d per head from the MFMA itself (A = ones); the score MFMAs start
+  // from -128 sum(q), so they return q.c directly
+  float qsum, nqc;
+  {
+    const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ones), qf[ks], a, 0, 0, 0);
+    qsum = a[0];
+    nqc = -128.f * qsum;
+  }
+  // fp16 weights for sums over P' (P' = (64 / 4^f) P for the keys of field
+  // f): sum(P) with 4^f / 64 = 1/64, 1/16, 1/4, 1; -1024 sum(P') with -1024.
+  const u32x4 wp = {0x24002400u, 0x2c002c00u, 0x34003400u, 0x3c003c00u};
+  const u32x4 wneg = {0xe400e400u, 0xe400e400u, 0xe400e400u, 0xe400e400u};
+
+  // Per-tile registers: K codes (block mb: KW words of row 16 (hl >> 2) +
+  // 4 mb + (hl & 3)), K parameters (keys 16 grp + 4 j .. + 3), V codes (word
+  // grp of channel row 16 db + hl) and the V parameter of that channel; two
+  // register sets each, as in the 4-bit decode.
+  struct KSet {
+    uint32_t c[4][KW];
+    u32x4 p[4];
+  };
+  struct VSet {
+    uint32_t c[DB];
+    uint32_t p[DB];
+  };
+  KSet ka, kb;
+  VSet va, vb;
+  const int krow = 16 * (hl >> 2) + (hl & 3);
+  auto kload = [&](KSet& ks_, int t) {
+    const uint32_t tb = t < ntile ? (uint32_t)(key_begin + t * kTile) : 0u;
+    const uint32_t no = t < ntile ? 0u : kNoRead;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const uint32_t off = no + (tb + krow + 4 * mb) * RB + grp * (RB / 4);
+      if constexpr (KW == 2) {
+        const u32x2 x = ld2<kNT>(krs, off);
+        ks_.c[mb][0] = x[0];
+        ks_.c[mb][1] = x[1];
+      } else {
+        ks_.c[mb][0] = ld1<kNT>(krs, off);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ks_.p[j] = ld4<kRT>(kprs, no + (tb + 16 * grp + 4 * j) * 4);
+  };
+  auto vload = [&](VSet& vs, int t, bool want) {
+    const bool rd = want && t < ntile;
+    const uint32_t tile = rd ? (uint32_t)(tile_begin + t) : 0u;
+    const uint32_t no = rd ? 0u : kNoRead;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      vs.c[db] = ld1<kNT>(vrs, no + ((tile * D + 16 * db + hl) * 16 + 4 * grp));
+#pragma unroll
+    for (int db = 0; db < DB; ++db) vs.p[db] = ld1<kRT>(vprs, no + (tile * D + 16 * db + hl) * 4);
+  };
+
+  // Scores of one tile (raw q.k^ units), masked past L, and the tile max.
+  auto scores = [&](const KSet& ks_, int t, f32x4 (&s)[4]) -> float {
+    const int key0 = key_begin + t * kTile;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      f32x4 a = {nqc, nqc, nqc, nqc};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(expand2_bf16(ks_.c[mb][ks >> 1], ks & 1, xk),
+                                                    qf[ks], a, 0, 0, 0);
+      // q.k^ = s (q.c) + z sum(q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t p = ks_.p[mb][r];
+        s[mb][r] = __builtin_fmaf(param_s(p), a[r], param_z(p) * qsum);
+      }
+    }
+    if (key0 + kTile > L) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (key0 + 16 * grp + 4 * mb + r >= L) s[mb][r] = -INFINITY;
+    }
+    float x = s[0][0];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x = fmaxf(x, s[mb][r]);
+    x = fmaxf(x, xor16(x));
+    return fmaxf(x, xor32(x));
+  };
+
+  // O: acc[db][r] = O[head 4 grp + r][channel 16 db + hl]; lr[r] the row sum
+  // of that head over the same fp16 P the product multiplies. The running
+  // max and the skip state stay per head hl.
+  f32x4 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[db][r] = 0.f;
+  f32x4 lr = {0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;  // running max over kept tiles: the skip test's reference
+  float m_ref = -INFINITY;  // reference max of the exponentials accumulated so far
+  uint64_t skipped = 0;
+  auto decide = [&](float tmax, int t, bool& keep) -> bool {
+    keep = !(tmax < m_run - tau_raw);
+    if (keep) m_run = fmaxf(m_run, tmax);
+    else skipped |= 1ull << t;
+    return __ballot(keep && head_ok) != 0ull;
+  };
+  // value of head 4 grp + r, from the lane of grp 0 that holds it per head
+  const int hsrc = 16 * grp;  // byte address of lane 4 grp, for ds_bpermute
+  auto of_head = [&](float x, int r) -> float {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                         hsrc + 4 * r, __builtin_bit_cast(int, x)));
+  };
+
+  // K runs two tiles ahead of the scores and V one tile ahead of the PV, with
+  // the same load order and no-read loads as the 4-bit decode.
+  kload(ka, 0);
+  kload(kb, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 s_cur[4];
+  float t_cur = scores(ka, 0, s_cur);
+  bool keep_cur;
+  bool any_cur = decide(t_cur, 0, keep_cur);
+  vload(va, 0, any_cur);
+  __builtin_amdgcn_sched_barrier(0);
+  kload(ka, 2);
+  __builtin_amdgcn_sched_barrier(0);
+
+  auto step = [&](int t, KSet& kn, const VSet& vc, VSet& vn) {
+    f32x4 s_nx[4];
+    float t_nx = -INFINITY;
+    bool keep_nx = false, any_nx = false;
+    if (t + 1 < ntile) {
+      t_nx = scores(kn, t + 1, s_nx);
+      any_nx = decide(t_nx, t + 1, keep_nx);
+    }
+    vload(vn, t + 1, any_nx);
+    __builtin_amdgcn_sched_barrier(0);
+    kload(kn, t + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    if (any_cur) {
+      const float mn = keep_cur ? fmaxf(m_ref, t_cur) : m_ref;
+      if (__ballot(mn > m_ref) != 0ull) {
+        const float alpha = mn > m_ref ? exp2_fast((m_ref - mn) * c) : 1.f;
+        m_ref = mn;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float ar = of_head(alpha, r);
+          lr[r] *= ar;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[db][r] *= ar;
+        }
+      }
+      // P' = (64 / 4^f) P, f = the field of the key's code (element e of a
+      // k-step: f = e / 2), i.e. exponent input + 6 - 2 f; a skipped head's
+      // exponentials are exp2(-inf) = 0
+      const float nmc = keep_cur ? -m_ref * c : -INFINITY;
+      f16x8 pf[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pf[ks][e] = (_Float16)exp2_fast(__builtin_fmaf(
+              s_cur[2 * ks + (e >> 2)][e & 3], c, nmc + (float)(6 - 2 * (e >> 1))));
+      // sum_j p_j (pt) and -1024 sum_j p'_j (u0) of head 4 grp + r
+      f32x4 pt = {0.f, 0.f, 0.f, 0.f}, u0 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        pt = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[ks], __builtin_bit_cast(f16x8, wp), pt, 0, 0,
+                                                    0);
+        u0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[ks], __builtin_bit_cast(f16x8, wneg), u0, 0,
+                                                    0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) lr[r] += pt[r];
+      // P'.(expanded codes) = 64 P.c + 1024 sum(P'); from -1024 sum(P'):
+      // O += (s_c / 64) (64 P.c) + z_c sum_j p_j
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        f32x4 u = u0;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          u = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[ks], expand2_f16(vc.c[db], ks, xk), u, 0, 0,
+                                                     0);
+        const float sc64 = 0.015625f * param_s(vc.p[db]);
+        const float zc = param_z(vc.p[db]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc[db][r] = __builtin_fmaf(sc64, u[r], __builtin_fmaf(zc, pt[r], acc[db][r]));
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) s_cur[mb] = s_nx[mb];
+    t_cur = t_nx;
+    keep_cur = keep_nx;
+    any_cur = any_nx;
+  };
+  for (int t = 0; t < ntile; t += 2) {
+    step(t, kb, va, vb);
+    step(t + 1, ka, vb, va);
+  }
+
+  if (mask != nullptr && lane < G) {  // lane < G: grp 0, head hl = lane
+    uint8_t* mrow = mask + bh * T + tile_begin;
+    for (int t = 0; t < ntile; ++t) mrow[t] = (uint8_t)((skipped >> t) & 1u);
+  }
+
+  const size_t bh0 = (size_t)b * Hq + g * G;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float mr = of_head(m_ref, r);
+    const int h = 4 * grp + r;
+    if (h < G) {
+      const float ir = 1.f / lr[r];
+      float* dst = ws_o + ((bh0 + h) * nsplit + sp) * D + hl;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) dst[16 * db] = acc[db][r] * ir;
+      if (hl == 0) ws_lse[(bh0 + h) * nsplit + sp] = (mr * c + __log2f(lr[r])) * kLn2;
+    }
+  }
+}
+
+template <int D>
+int launch_q2_d(const QuantArgs& a) {
+  constexpr int RPW = 64 / (D / 16);  // key rows per wave
+  const int nk = a.k1 - a.k0;
+  const long long rows = (long long)a.B * a.Hkv * nk;
+  const long long waves = (rows + RPW - 1) / RPW;
+  const long long g1 = (waves + 3) / 4;
+  const int T = (a.L + kTile - 1) / kTile;
+  const int t0 = a.k0 / kTile;
+  const int nt = (a.k1 + kTile - 1) / kTile - t0;
+  const long long g2 = (long long)a.B * a.Hkv * nt;
+  if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return -1;
+  hipLaunchKernelGGL((quant_k2_kernel<D>), dim3((unsigned)g1), dim3(256), 0, (hipStream_t)a.stream,
+                     (const uint16_t*)a.k, a.kq, a.kp, rows, a.L, a.k0, nk);
+  hipLaunchKernelGGL((quant_v2_kernel<D>), dim3((unsigned)g2), dim3(D), 0, (hipStream_t)a.stream,
+                     (const uint16_t*)a.v, a.vq, a.vp, a.L, T, t0, nt, a.k1);
+  return 0;
+}
+
+template <int D>
+int launch_dq2_d(const DecodeQ4Args& a) {
+  const long long nwork = (long long)a.B * a.Hkv * a.nsplit;
+  if (nwork > 0x7fffffffLL) return -1;
+  const unsigned g1 = (unsigned)((nwork + 3) / 4);
+  hipLaunchKernelGGL((decode_q2_split_kernel<D>), dim3(g1), dim3(256), 0, (hipStream_t)a.stream,
+                     (const uint16_t*)a.q, a.kq, a.kp, a.vq, a.vp, a.ws_o, a.ws_lse, a.mask, a.Hq,
+                     a.Hkv, a.L, a.nsplit, a.tau_raw, a.c, (int)nwork);
+  return launch_decode_merge(a.ws_o, a.ws_lse, a.o, a.lse, a.B * a.Hq, a.d, a.nsplit, a.stream);
+}
+
+}  // namespace
+
+int launch_kv_quantize_q2(const QuantArgs& a) {
+  return a.d == 128 ? launch_q2_d<128>(a) : launch_q2_d<64>(a);
+}
+
+int launch_decode_q2(const DecodeQ4Args& a) {
+  return a.d == 128 ? launch_dq2_d<128>(a) : launch_dq2_d<64>(a);
+}
+
+}  // namespace skipattn

@@ -39,7 +39,7 @@ struct DecodeArgs {
 struct QuantArgs {
   const void* k;  // bf16 [B, Hkv, L, d]
   const void* v;
-  uint8_t* kq;    // 4-bit codes and parameter words, layout in kvq4.hip
+  uint8_t* kq;    // codes and parameter words, layout in kvq4.hip / kvq2.hip
   uint32_t* kp;
   uint8_t* vq;
   uint32_t* vp;
@@ -71,6 +71,9 @@ int launch_prefill(const PrefillArgs& a);
 int launch_decode(const DecodeArgs& a);
 int launch_kv_quantize_q4(const QuantArgs& a);
 int launch_decode_q4(const DecodeQ4Args& a);
+// The 2-bit cache (layout in kvq2.hip) takes the same arguments.
+int launch_kv_quantize_q2(const QuantArgs& a);
+int launch_decode_q2(const DecodeQ4Args& a);
 // The log-sum-exp merge of per-split partials (shared by both decodes).
 int launch_decode_merge(const float* ws_o, const float* ws_lse, float* o, float* lse, int nbh,
                         int d, int nsplit, void* stream);

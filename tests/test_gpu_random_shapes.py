@@ -2,14 +2,14 @@
 ragged lengths, both head sizes, causal or not, structured or plain inputs,
 several tau. Every case compares full outputs with the fp64 oracle through
 the C ABI (skip masks exact except near-margin tiles, O within 1e-2, LSE
-within 1e-3; 4-bit codes bit for bit)."""
+within 1e-3; 4-bit and 2-bit codes bit for bit)."""
 import math
 
 import numpy as np
 import pytest
 
 import synth
-from oracle import kvq4
+from oracle import kvq2, kvq4
 from tests import _parity
 
 pytestmark = pytest.mark.gpu
@@ -57,6 +57,7 @@ def _decode_cases(n, seed, base_id):
 PREFILL = _prefill_cases(24, 2026)
 DECODE = _decode_cases(16, 2027, 240)
 DECODE_Q4 = _decode_cases(12, 2028, 270)
+DECODE_Q2 = _decode_cases(8, 2029, 290)
 
 
 @pytest.mark.parametrize("name,cfg,taus", PREFILL, ids=[c[0] for c in PREFILL])
@@ -115,31 +116,43 @@ def test_decode_random_shape(name, cfg, taus):
         assert rep.ok(), str(rep)
 
 
-@pytest.mark.parametrize("name,cfg,taus", DECODE_Q4, ids=[c[0] for c in DECODE_Q4])
-def test_decode_q4_random_shape(name, cfg, taus):
+def _quantized_case(width, name, cfg, taus):
     import torch
     import long_context_tiled_amd as lib
+    codec = {4: kvq4, 2: kvq2}[width]
+    quantize = {4: lib.quantize_q4, 2: lib.quantize_q2}[width]
+    decode = {4: lib.decode_q4, 2: lib.decode_q2}[width]
     q, k, v = synth.make_decode(cfg)
     L = k.shape[2]
     Hkv = k.shape[1]
-    print(f"[random] q4 {name}: quantise", flush=True)
-    cache = lib.quantize_q4(_dev(k), _dev(v))
+    print(f"[random] q{width} {name}: quantise", flush=True)
+    cache = quantize(_dev(k), _dev(v))
     torch.cuda.synchronize()
-    enc = kvq4.encode(synth.bf16_bits_to_f32(k), synth.bf16_bits_to_f32(v))
+    enc = codec.encode(synth.bf16_bits_to_f32(k), synth.bf16_bits_to_f32(v))
     got = {n: t.cpu().numpy() for n, t in cache.items()}
     for n in ("kq", "kp", "vq", "vp"):
         g = got[n].view(np.uint32) if n in ("kp", "vp") else got[n]
         assert np.array_equal(g, enc[n]), f"{n} differs from the oracle's encoding"
 
     def kv_for(b, g):
-        return (kvq4.decode_k(enc["kq"][b, g], enc["kp"][b, g]),
-                kvq4.decode_v(enc["vq"][b, g], enc["vp"][b, g], L))
+        return (codec.decode_k(enc["kq"][b, g], enc["kp"][b, g]),
+                codec.decode_v(enc["vq"][b, g], enc["vp"][b, g], L))
     dq = _dev(q)
     for tau in taus:
-        print(f"[random] q4 {name} tau={tau}", flush=True)
-        o, lse, mask = lib.decode_q4(dq, cache, L, tau, want_mask=True)
+        print(f"[random] q{width} {name} tau={tau}", flush=True)
+        o, lse, mask = decode(dq, cache, L, tau, want_mask=True)
         torch.cuda.synchronize()
         rep = _parity.check_decode(q, None, None, tau, o.cpu().numpy(), lse.cpu().numpy(),
                                    mask.cpu().numpy(), kv_for=kv_for, Hkv=Hkv)
         print(f"  {rep}", flush=True)
         assert rep.ok(), str(rep)
+
+
+@pytest.mark.parametrize("name,cfg,taus", DECODE_Q4, ids=[c[0] for c in DECODE_Q4])
+def test_decode_q4_random_shape(name, cfg, taus):
+    _quantized_case(4, name, cfg, taus)
+
+
+@pytest.mark.parametrize("name,cfg,taus", DECODE_Q2, ids=[c[0] for c in DECODE_Q2])
+def test_decode_q2_random_shape(name, cfg, taus):
+    _quantized_case(2, name, cfg, taus)
