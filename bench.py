@@ -54,8 +54,11 @@ MEASURED_TRAFFIC = {
                 "sha1": "997b1712c691d713dcef2bad76a69c55fe5807a3",
                 "bytes": (2711139.9 * 2.0 + 528384.0) * 1024},
     "decode_q4": {"sources": ("kvq4.hip", "kvq_common.hpp", "decode.hip", "common.hpp"),
-                  "sha1": "277b7165a12ceab7053f3eb692423e54e83dc42f",
-                  "bytes": (1148209.9 * 2.0 + 16642.4) * 1024},
+                  "sha1": "170ceb2aa79f0da93f7c422fd8cc6ab49029d7b1",
+                  "bytes": (1148234.6 * 2.0 + 16641.8) * 1024},
+    "decode_q2": {"sources": ("kvq2.hip", "kvq_common.hpp", "decode.hip", "common.hpp"),
+                  "sha1": "aae03c6900d117687fc8780f1f04507ead3887bc",
+                  "bytes": (623771.7 * 2.0 + 16640.0) * 1024},
     "decode": {"sources": ("decode.hip", "common.hpp"),
                "sha1": "c9d9a902f280df832bb299ffe1922fe72fd232dc",
                "bytes": (4195501.5 * 2.0 + 16641.6) * 1024},
@@ -72,7 +75,9 @@ def _source_sha1(names):
 
 
 def measured_traffic(leg):
-    t = MEASURED_TRAFFIC[leg]
+    t = MEASURED_TRAFFIC.get(leg)
+    if t is None:
+        return None
     return t["bytes"] if _source_sha1(t["sources"]) == t["sha1"] else None
 
 
@@ -107,18 +112,27 @@ def decode_bytes(B, Hkv, L, d, mask=None, G=1):
     return dense, dense / 2 + v_bytes
 
 
-def q4_bytes(B, Hkv, L, d, mask=None, G=1):
-    """Bytes of the 4-bit cache the decode must read: K codes (d/2 per key)
-    and parameter words (4 per key), and per V tile its codes (32 d) and
-    parameter words (4 d) when at least one head of the KV group keeps it."""
+def qcache_bytes(bits, B, Hkv, L, d, mask=None, G=1):
+    """Bytes of a bits-wide cache (4 or 2) the decode must read: K codes
+    (d bits / 8 per key) and parameter words (4 per key), and per V tile its
+    codes (8 bits d) and parameter words (4 d) when at least one head of the
+    KV group keeps it."""
     T = (L + 63) // 64
-    k_b = float(B * Hkv * L * (d // 2 + 4))
-    v_tile = 36.0 * d
+    k_b = float(B * Hkv * L * (d * bits // 8 + 4))
+    v_tile = (8.0 * bits + 4.0) * d
     if mask is None:
         return k_b + B * Hkv * T * v_tile
     Bm, Hq, nt = mask.shape
     keep_any = (mask.reshape(Bm, Hkv, G, nt) == 0).any(axis=2)
     return k_b + float(keep_any.sum()) * v_tile
+
+
+def q4_bytes(B, Hkv, L, d, mask=None, G=1):
+    return qcache_bytes(4, B, Hkv, L, d, mask, G)
+
+
+def q2_bytes(B, Hkv, L, d, mask=None, G=1):
+    return qcache_bytes(2, B, Hkv, L, d, mask, G)
 
 
 class Timer:
@@ -166,20 +180,22 @@ def _cpu_decode_head(job):
         oracle.decode_head(synth.bf16_bits_to_f64(q[hh]), k, v, math.inf)
 
 
-def _cpu_decode_q4_head(i):
+def _cpu_decode_q_head(item):
     from threadpoolctl import threadpool_limits
     import oracle
     import synth
-    from oracle import kvq4
+    from oracle import kvq2, kvq4
+    key, i = item
+    codec = {"dq4": kvq4, "dq2": kvq2}[key]
     with threadpool_limits(1):
-        e, q, L = _CPU["dq4"][i]
-        k = kvq4.decode_k(e["kq"], e["kp"])
-        v = kvq4.decode_v(e["vq"], e["vp"], L)
+        e, q, L = _CPU[key][i]
+        k = codec.decode_k(e["kq"], e["kp"])
+        v = codec.decode_v(e["vq"], e["vp"], L)
         for hh in range(q.shape[0]):
             oracle.decode_head(synth.bf16_bits_to_f64(q[hh]), k, v, math.inf)
 
 
-def cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=768, nkv=32, nkv_q4=16, pname="prefill_128k"):
+def cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=768, nkv=32, nkv_q=16, pname="prefill_128k"):
     """The fp64 oracle as it stands, timed on a bounded sample of each
     workload with one process per host core (fp64 widening of the inputs is
     done before the clock starts)."""
@@ -200,11 +216,14 @@ def cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=768, nkv=32, nkv_q4=16, pname="
     picks = [(b, g) for b in range(B) for g in range(Hkv)][:nkv]
     _CPU["dkv"] = [(synth.bf16_bits_to_f64(dk[b, g]), synth.bf16_bits_to_f64(dv[b, g]),
                     dq[b, g * G:(g + 1) * G]) for b, g in picks]
-    from oracle import kvq4
-    picks4 = picks[:nkv_q4]
-    _CPU["dq4"] = [(kvq4.encode(synth.bf16_bits_to_f32(dk[b, g]), synth.bf16_bits_to_f32(dv[b, g])),
-                    dq[b, g * G:(g + 1) * G], L) for b, g in picks4]
+    from oracle import kvq2, kvq4
+    pickq = picks[:nkv_q]
+    for key, codec in (("dq4", kvq4), ("dq2", kvq2)):
+        _CPU[key] = [(codec.encode(synth.bf16_bits_to_f32(dk[b, g]),
+                                   synth.bf16_bits_to_f32(dv[b, g])),
+                      dq[b, g * G:(g + 1) * G], L) for b, g in pickq]
     ctx = mp.get_context("fork")
+    qwall = {}
     with ctx.Pool(cores) as pool:
         t0 = time.perf_counter()
         pool.map(_cpu_prefill_block, qbs, chunksize=1)
@@ -213,9 +232,10 @@ def cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=768, nkv=32, nkv_q4=16, pname="
         pool.map(_cpu_decode_head, [(i, hh) for i in range(len(picks)) for hh in range(G)],
                  chunksize=1)
         dwall = time.perf_counter() - t0
-        t0 = time.perf_counter()
-        pool.map(_cpu_decode_q4_head, list(range(len(picks4))), chunksize=1)
-        qwall = time.perf_counter() - t0
+        for key in ("dq4", "dq2"):
+            t0 = time.perf_counter()
+            pool.map(_cpu_decode_q_head, [(key, i) for i in range(len(pickq))], chunksize=1)
+            qwall[key] = time.perf_counter() - t0
     _CPU.clear()
     pairs = sum(64 * (qb * 64) + 64 * 65 // 2 for qb in qbs)
     pre = dict(value=float(4.0 * d * pairs / pwall / 1e12), unit="TFLOP/s", cores=cores,
@@ -226,11 +246,15 @@ def cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=768, nkv=32, nkv_q4=16, pname="
     dec = dict(value=float(kv_bytes / dwall / 1e9), unit="GB/s", cores=cores, kind="oracle",
                sample=f"decode_128k: {len(picks)} KV heads x {G} query heads, tau=inf, "
                       f"fp64 numpy, {dwall:.1f} s wall")
-    q4b = len(picks4) * float(L * (d // 2 + 4) + ((L + 63) // 64) * 36 * d)
-    dq4 = dict(value=float(q4b / qwall / 1e9), unit="GB/s", cores=cores, kind="oracle",
-               sample=f"decode_128k over the 4-bit cache: {len(picks4)} KV heads x {G} query "
-                      f"heads, dequantise + fp64 decode oracle, tau=inf, {qwall:.1f} s wall")
-    return pre, dec, dq4
+    quant = {}
+    for key, bits in (("dq4", 4), ("dq2", 2)):
+        nb = qcache_bytes(bits, len(pickq), 1, L, d)
+        quant[key] = dict(value=float(nb / qwall[key] / 1e9), unit="GB/s", cores=cores,
+                          kind="oracle",
+                          sample=f"decode_128k over the {bits}-bit cache: {len(pickq)} KV heads "
+                                 f"x {G} query heads, dequantise + fp64 decode oracle, tau=inf, "
+                                 f"{qwall[key]:.1f} s wall")
+    return pre, dec, quant["dq4"], quant["dq2"]
 
 
 # ---------------------------------------------------------------------- main
@@ -243,10 +267,11 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--reading", default="S", choices=["S", "P"])
-    ap.add_argument("--only", default="both", choices=["both", "prefill", "decode", "decode_q4"],
+    ap.add_argument("--only", default="both",
+                    choices=["both", "prefill", "decode", "decode_q4", "decode_q2"],
                     help="profile one leg only (the JSON line then reports that leg)")
     ap.add_argument("--no-q4", action="store_true",
-                    help="skip the 4-bit KV-cache decode measured beside the step")
+                    help="skip the 4-bit and 2-bit KV-cache decodes measured beside the step")
     ap.add_argument("--prefill-workload", default="prefill_128k",
                     choices=["prefill_128k", "prefill_32k", "prefill_8k"],
                     help="prefill shape of the step (default: the 128K one)")
@@ -305,7 +330,9 @@ def main():
 
     run_p = args.only in ("both", "prefill")
     run_d = args.only in ("both", "decode")
-    run_q = args.only == "decode_q4" or (args.only == "both" and not args.no_q4)
+    # quantised-cache decodes measured beside the step (width in bits)
+    widths = [w for w in (4, 2)
+              if args.only == f"decode_q{w}" or (args.only == "both" and not args.no_q4)]
 
     # Timed calls pass no skip-mask buffer (the mask is an optional output
     # for analysis); the tau sweep takes one extra masked call per tau to
@@ -375,43 +402,49 @@ def main():
                                    kernel="decode_split_kernel<128>",
                                    avg_ms=round(d_ms, 4), per_launch_bytes=dense_b)
 
-    if run_q:
-        # 4-bit KV cache of the same decode workload: quantised once (timed
-        # on its own), then attn_decode_q4 timed like the bf16 decode.
+    qdecode = {}
+    for w in widths:
+        # The same decode workload over a w-bit KV cache: quantised once
+        # (timed on its own), then attn_decode_q{w} timed like the bf16 decode.
+        quantize = getattr(lib, f"quantize_q{w}")
         tq0 = Timer()
         with tq0:
-            cache = lib.quantize_q4(uk, uv)
+            cache = quantize(uk, uv)
         torch.cuda.synchronize()
-        q4b = q4_bytes(DB, DHkv, L, Dd)
+        qb = qcache_bytes(w, DB, DHkv, L, Dd)
+        entry = getattr(lib, f"attn_decode_q{w}")
 
-        def decode_q4(tau, mask=None):
-            lib.attn_decode_q4(uq, cache, L, do, dlse, tau, ws, mask)
+        def decode_q(tau, mask=None, entry=entry, cache=cache):
+            entry(uq, cache, L, do, dlse, tau, ws, mask)
 
+        qdecode[w] = decode_q
         for _ in range(args.warmup):
-            decode_q4(math.inf)
-        tq4 = Timer()
+            decode_q(math.inf)
+        tqw = Timer()
         torch.cuda.synchronize()
         for _ in range(args.steps):
-            with tq4:
-                decode_q4(math.inf)
+            with tqw:
+                decode_q(math.inf)
         torch.cuda.synchronize()
-        q_ms = float(np.mean(tq4.ms()))
+        q_ms = float(np.mean(tqw.ms()))
         dense_b, _ = decode_bytes(DB, DHkv, L, Dd)
-        gbs_q = q4b / (q_ms * 1e-3) / 1e9
-        dq4 = dict(value=round(gbs_q, 2), unit="GB/s", ms=round(q_ms, 4),
-                   frac_of_hbm=round(gbs_q / PEAK_HBM_GBS, 4), per_call_bytes=q4b,
-                   gbs_bf16_equivalent=round(dense_b / (q_ms * 1e-3) / 1e9, 2),
-                   traffic=measured_traffic("decode_q4"),
-                   quantise_ms=round(float(tq0.ms()[0]), 4),
-                   kernels="decode_q4_split_kernel<128> + decode_merge_kernel<128>")
-        out["decode_q4"] = dq4
-        if args.only == "decode_q4":
-            out.update(value=round(gbs_q, 2), unit="GB/s")
+        gbs_q = qb / (q_ms * 1e-3) / 1e9
+        leg = f"decode_q{w}"
+        out[leg] = dict(value=round(gbs_q, 2), unit="GB/s", ms=round(q_ms, 4),
+                        frac_of_hbm=round(gbs_q / PEAK_HBM_GBS, 4), per_call_bytes=qb,
+                        gbs_bf16_equivalent=round(dense_b / (q_ms * 1e-3) / 1e9, 2),
+                        traffic=measured_traffic(leg),
+                        quantise_ms=round(float(tq0.ms()[0]), 4),
+                        kernels=f"decode_q{w}_split_kernel<128> + decode_merge_kernel<128>")
+        if args.only == leg:
+            # the step is this leg alone: its per-call time, its workload
+            out.update(value=round(gbs_q, 2), unit="GB/s", ms_per_step=round(q_ms, 4))
+            out["config"]["workload"] = f"decode_128k over the {w}-bit KV cache, tau=inf"
             out["roofline"] = dict(bound="hbm", achieved=round(gbs_q, 2), peak=PEAK_HBM_GBS,
                                    unit="GB/s", frac=round(gbs_q / PEAK_HBM_GBS, 4),
-                                   traffic=measured_traffic("decode_q4"),
-                                   kernel="decode_q4_split_kernel<128>",
-                                   avg_ms=round(q_ms, 4), per_launch_bytes=q4b)
+                                   traffic=measured_traffic(leg),
+                                   kernel=f"decode_q{w}_split_kernel<128>",
+                                   avg_ms=round(q_ms, 4), per_launch_bytes=qb)
 
     if not args.no_sweep:
         sweep = []
@@ -443,27 +476,30 @@ def main():
                               skip_fraction=round(float((m == 1).mean()), 4),
                               gbs_dense=round(dense_b / ms / 1e6, 2),
                               gbs_actual=round(act_b / ms / 1e6, 2)))
-        for tau in dcfg["taus"] if run_q else []:
-            t = Timer()
-            for _ in range(3):
-                with t:
-                    decode_q4(tau)
-            torch.cuda.synchronize()
-            ms = float(np.median(t.ms()))
-            decode_q4(tau, dmask)
-            m = dmask.cpu().numpy()
-            act_b = q4_bytes(DB, DHkv, L, Dd, m, DHq // DHkv)
-            sweep.append(dict(leg="decode_128k_q4", tau=str(tau), ms=round(ms, 4),
-                              skip_fraction=round(float((m == 1).mean()), 4),
-                              gbs_actual=round(act_b / ms / 1e6, 2)))
+        for w in widths:
+            for tau in dcfg["taus"]:
+                t = Timer()
+                for _ in range(3):
+                    with t:
+                        qdecode[w](tau)
+                torch.cuda.synchronize()
+                ms = float(np.median(t.ms()))
+                qdecode[w](tau, dmask)
+                m = dmask.cpu().numpy()
+                act_b = qcache_bytes(w, DB, DHkv, L, Dd, m, DHq // DHkv)
+                sweep.append(dict(leg=f"decode_128k_q{w}", tau=str(tau), ms=round(ms, 4),
+                                  skip_fraction=round(float((m == 1).mean()), 4),
+                                  gbs_actual=round(act_b / ms / 1e6, 2)))
         out["tau_sweep"] = sweep
 
     if not args.no_cpu:
         print("# cpu baseline (fp64 oracle on a bounded sample)", file=sys.stderr, flush=True)
-        pre, dec, dq4 = cpu_baseline(pq, pk, pv, dq, dk, dv, pname=pname)
-        out["cpu_baseline"] = pre if run_p else (dec if run_d else dq4)
+        pre, dec, dq4, dq2 = cpu_baseline(pq, pk, pv, dq, dk, dv, pname=pname)
+        legs = {"both": pre, "prefill": pre, "decode": dec, "decode_q4": dq4, "decode_q2": dq2}
+        out["cpu_baseline"] = legs[args.only]
         out["cpu_baseline_decode"] = dec
         out["cpu_baseline_decode_q4"] = dq4
+        out["cpu_baseline_decode_q2"] = dq2
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -22,9 +22,11 @@
 // Decode split kernel: one wave per (sequence, KV head, split), the layout
 // of the 4-bit decode (P the A operand of the PV product, O head-major, two
 // register sets per operand, no LDS memory):
-//   q.K on v_mfma_f32_16x16x32_bf16: each code expanded to the exact bf16
-//   value 128 + c (field moved to bits 0..1 and or-ed into 0x4300), the
-//   accumulator started at -128 sum(q), so q.k^ = s (q.c) + z sum(q).
+//   q.K on v_mfma_f32_16x16x32_bf16: each code expanded by a mask and an
+//   or into 0x4300 to the exact bf16 value 128 + F c, F = 1, 4 or 16 by the
+//   element's place in its word (three shifted copies of a word hold all its
+//   fields at bits 0..5 of each half); q enters divided by F (exact), the
+//   accumulator starts at -128 sum(q / F), so q.k^ = s (q.c) + z sum(q).
 //   P.V on v_mfma_f32_16x16x32_f16: codes expanded by masks alone to the
 //   exact fp16 values 1024 + 4^f c, f the field's place in its byte (fp16
 //   1024 has 10 mantissa bits, so 64 c fits), and the factor moved to P:
@@ -169,16 +171,36 @@ __device__ __forceinline__ Expand2Consts expand2_consts() {
   return k;
 }
 
-// Half h of a storage word (elements 8 h .. 8 h + 7) -> bf16 values 128 + c,
-// element order: field f of each half of byte h, moved to bits 0..1.
+// Half h of a storage word (elements 8 h .. 8 h + 7) -> bf16 values
+// 128 + F c by masks alone: element pair p (elements 2 p, 2 p + 1, field p of
+// each 16-bit half) is read from w, w >> 6 or w >> 12 with its field left at
+// bit 0, 2 or 4 (bf16 128 has 7 mantissa bits), so F = kScaleK[p]. The q
+// fragment is divided by the same F (a power of two: exact in bf16).
+constexpr int kScaleK[8] = {1, 4, 16, 1, 4, 16, 1, 4};
 __device__ __forceinline__ bf16x8 expand2_bf16(uint32_t w, int h, const Expand2Consts& k) {
-  const uint32_t x = h ? (w >> 8) : w;
+  const uint32_t x6 = w >> 6;
   u32x4 r;
-  r[0] = (x & k.m[0]) | k.bmagic;
-  r[1] = ((x >> 2) & k.m[0]) | k.bmagic;
-  r[2] = ((x >> 4) & k.m[0]) | k.bmagic;
-  r[3] = ((x >> 6) & k.m[0]) | k.bmagic;
+  if (h == 0) {
+    r[0] = (w & k.m[0]) | k.bmagic;
+    r[1] = (w & k.m[1]) | k.bmagic;
+    r[2] = (w & k.m[2]) | k.bmagic;
+    r[3] = (x6 & k.m[0]) | k.bmagic;
+  } else {
+    const uint32_t x12 = w >> 12;
+    r[0] = (x6 & k.m[1]) | k.bmagic;
+    r[1] = (x6 & k.m[2]) | k.bmagic;
+    r[2] = (x12 & k.m[0]) | k.bmagic;
+    r[3] = (x12 & k.m[1]) | k.bmagic;
+  }
   return __builtin_bit_cast(bf16x8, r);
+}
+
+// bf16 pair word x with both halves divided by f (1, 4 or 16): exact.
+__device__ __forceinline__ uint32_t bf16x2_div(uint32_t x, int f) {
+  const float inv = 1.f / (float)f;
+  const uint32_t lo = __builtin_bit_cast(uint32_t, bf16_to_f32(x & 0xffffu) * inv) >> 16;
+  const uint32_t hi = __builtin_bit_cast(uint32_t, bf16_to_f32(x >> 16) * inv) & 0xffff0000u;
+  return lo | hi;
 }
 
 // Half h of a storage word -> fp16 values 1024 + 4^f c (field f in place).
@@ -234,26 +256,33 @@ __global__ __launch_bounds__(256, 2) void decode_q2_split_kernel(
   const size_t bh = (size_t)b * Hq + g * G + hl;
 
   // q^T fragments (B operand, n = head): lane group grp holds d range
-  // [grp D/4, (grp + 1) D/4), k-step ks its elements 8 ks .. 8 ks + 7.
-  bf16x8 qf[KS];
+  // [grp D/4, (grp + 1) D/4), k-step ks its elements 8 ks .. 8 ks + 7; qf
+  // as given, qs divided by the expansion's factors (element pair p of word
+  // half ks & 1 by kScaleK[4 (ks & 1) + p]).
+  bf16x8 qf[KS], qs[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     u32x4 x = {0u, 0u, 0u, 0u};
     if (head_ok) x = ldg16(q + bh * D + grp * (D / 4) + 8 * ks);
     qf[ks] = as_bf16x8(x);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) x[p] = bf16x2_div(x[p], kScaleK[4 * (ks & 1) + p]);
+    qs[ks] = as_bf16x8(x);
   }
   const Expand2Consts xk = expand2_consts();
-  // sum_d q_d per head from the MFMA itself (A = ones); the score MFMAs start
-  // from -128 sum(q), so they return q.c directly
+  // sum_d q_d and sum_d q_d / F_d per head from the MFMA itself (A = ones);
+  // the score MFMAs start from -128 sum(q / F), so they return q.c directly
   float qsum, nqc;
   {
     const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    f32x4 a = {0.f, 0.f, 0.f, 0.f}, as = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int ks = 0; ks < KS; ++ks) {
       a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ones), qf[ks], a, 0, 0, 0);
+      as = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ones), qs[ks], as, 0, 0, 0);
+    }
     qsum = a[0];
-    nqc = -128.f * qsum;
+    nqc = -128.f * as[0];
   }
   // fp16 weights for sums over P' (P' = (64 / 4^f) P for the keys of field
   // f): sum(P) with 4^f / 64 = 1/64, 1/16, 1/4, 1; -1024 sum(P') with -1024.
@@ -292,15 +321,20 @@ __global__ __launch_bounds__(256, 2) void decode_q2_split_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) ks_.p[j] = ld4<kRT>(kprs, no + (tb + 16 * grp + 4 * j) * 4);
   };
+  // the lane's byte in a tile's V code rows and parameter words; the
+  // channel blocks follow at constant offsets (the loads' immediate field)
+  const uint32_t vcl = 16 * hl + 4 * grp;
+  const uint32_t vpl = 4 * hl;
   auto vload = [&](VSet& vs, int t, bool want) {
     const bool rd = want && t < ntile;
     const uint32_t tile = rd ? (uint32_t)(tile_begin + t) : 0u;
     const uint32_t no = rd ? 0u : kNoRead;
+    const uint32_t cb = no + tile * (D * 16) + vcl;
+    const uint32_t pb = no + tile * (D * 4) + vpl;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-      vs.c[db] = ld1<kNT>(vrs, no + ((tile * D + 16 * db + hl) * 16 + 4 * grp));
+    for (int db = 0; db < DB; ++db) vs.c[db] = ld1<kNT>(vrs, cb + 256 * db);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) vs.p[db] = ld1<kRT>(vprs, no + (tile * D + 16 * db + hl) * 4);
+    for (int db = 0; db < DB; ++db) vs.p[db] = ld1<kRT>(vprs, pb + 64 * db);
   };
 
   // Scores of one tile (raw q.k^ units), masked past L, and the tile max.
@@ -312,7 +346,7 @@ __global__ __launch_bounds__(256, 2) void decode_q2_split_kernel(
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(expand2_bf16(ks_.c[mb][ks >> 1], ks & 1, xk),
-                                                    qf[ks], a, 0, 0, 0);
+                                                    qs[ks], a, 0, 0, 0);
       // q.k^ = s (q.c) + z sum(q)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -321,6 +355,7 @@ __global__ __launch_bounds__(256, 2) void decode_q2_split_kernel(
       }
     }
     if (key0 + kTile > L) {
+      asm volatile("");  // keeps this a branch taken on the last tile only
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll

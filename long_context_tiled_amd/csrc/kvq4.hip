@@ -316,16 +316,20 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) ks_.p[j] = ld4<kRT>(kprs, no + (tb + 16 * grp + 4 * j) * 4);
   };
+  // the lane's byte in a tile's V code rows and parameter words; the
+  // channel blocks follow at constant offsets (the loads' immediate field)
+  const uint32_t vcl = (16 * (grp & 1) + hl) * 32 + 16 * (grp >> 1);
+  const uint32_t vpl = 4 * hl;
   auto vload = [&](VSet& vs, int t, bool want) {
     const bool rd = want && t < ntile;
     const uint32_t tile = rd ? (uint32_t)(tile_begin + t) : 0u;
     const uint32_t no = rd ? 0u : kNoRead;
+    const uint32_t cb = no + tile * (D * 32) + vcl;
+    const uint32_t pb = no + tile * (D * 4) + vpl;
 #pragma unroll
-    for (int dp = 0; dp < DB / 2; ++dp)
-      vs.c[dp] = ld4<kNT>(vrs, no + ((tile * D + 32 * dp + 16 * (grp & 1) + hl) * 32 +
-                                     16 * (grp >> 1)));
+    for (int dp = 0; dp < DB / 2; ++dp) vs.c[dp] = ld4<kNT>(vrs, cb + 1024 * dp);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) vs.p[db] = ld1<kRT>(vprs, no + (tile * D + 16 * db + hl) * 4);
+    for (int db = 0; db < DB; ++db) vs.p[db] = ld1<kRT>(vprs, pb + 64 * db);
   };
 
   // Scores of one tile (raw q.k^ units), masked past L, and the tile max.

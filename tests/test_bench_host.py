@@ -62,6 +62,15 @@ def test_q4_bytes(bench):
     assert got == 1 * 2 * 130 * (2 + 4) + 3 * 36 * 4
 
 
+def test_q2_bytes(bench):
+    # per key: d/4 bytes of K codes + 4 of K parameters; per V tile and
+    # channel: 16 bytes of codes + 4 of parameters
+    assert bench.q2_bytes(16, 8, 131072, 128) == 16 * 8 * 131072 * (32 + 4 + 20 * 128 / 64)
+    assert bench.q2_bytes(16, 8, 131072, 128) == 1275068416
+    got = bench.q2_bytes(1, 2, 130, 4, _mask_two_groups(), G=2)
+    assert got == 1 * 2 * 130 * (1 + 4) + 3 * 20 * 4
+
+
 def test_measured_traffic_follows_the_sources(bench, monkeypatch):
     for leg, entry in bench.MEASURED_TRAFFIC.items():
         want = entry["bytes"] if bench._source_sha1(entry["sources"]) == entry["sha1"] else None
