@@ -6,7 +6,7 @@ path. It shares no code with the HIP kernels.
 """
 from .attention import (TILE, SPLIT, KEPT, SKIPPED, NOT_VISITED, prefill,
                         prefill_blocks, decode, decode_head)
-from . import kvq2, kvq4
+from . import kvq2, kvq4, sas
 
 __all__ = ["TILE", "SPLIT", "KEPT", "SKIPPED", "NOT_VISITED", "prefill",
-           "prefill_blocks", "decode", "decode_head", "kvq2", "kvq4"]
+           "prefill_blocks", "decode", "decode_head", "kvq2", "kvq4", "sas"]
