@@ -54,13 +54,13 @@ MEASURED_TRAFFIC = {
                 "sha1": "997b1712c691d713dcef2bad76a69c55fe5807a3",
                 "bytes": (2711139.9 * 2.0 + 528384.0) * 1024},
     "decode_q4": {"sources": ("kvq4.hip", "kvq_common.hpp", "decode.hip", "common.hpp"),
-                  "sha1": "170ceb2aa79f0da93f7c422fd8cc6ab49029d7b1",
+                  "sha1": "90cb67a117b9a33e8f688dfe392fb27ebc0c77da",
                   "bytes": (1148234.6 * 2.0 + 16641.8) * 1024},
     "decode_q2": {"sources": ("kvq2.hip", "kvq_common.hpp", "decode.hip", "common.hpp"),
-                  "sha1": "aae03c6900d117687fc8780f1f04507ead3887bc",
+                  "sha1": "23b5cbd49630c20bb83ed4ab273787b1c32a4639",
                   "bytes": (623771.7 * 2.0 + 16640.0) * 1024},
     "decode": {"sources": ("decode.hip", "common.hpp"),
-               "sha1": "c9d9a902f280df832bb299ffe1922fe72fd232dc",
+               "sha1": "9ba368983da045d60281a064227f2dc6aaa181cf",
                "bytes": (4195501.5 * 2.0 + 16641.6) * 1024},
 }
 
@@ -272,6 +272,8 @@ def main():
                     help="profile one leg only (the JSON line then reports that leg)")
     ap.add_argument("--no-q4", action="store_true",
                     help="skip the 4-bit and 2-bit KV-cache decodes measured beside the step")
+    ap.add_argument("--no-sas", action="store_true",
+                    help="skip the decodes with the SAS exponential measured beside the step")
     ap.add_argument("--prefill-workload", default="prefill_128k",
                     choices=["prefill_128k", "prefill_32k", "prefill_8k"],
                     help="prefill shape of the step (default: the 128K one)")
@@ -401,6 +403,30 @@ def main():
                                    traffic=measured_traffic("decode"),
                                    kernel="decode_split_kernel<128>",
                                    avg_ms=round(d_ms, 4), per_launch_bytes=dense_b)
+
+    if run_d and not args.no_sas:
+        # The bf16 decode with the SAS exponential (degree 2 and 3): its time
+        # and how far its outputs move from the exact decode's on this input.
+        decode(math.inf)
+        torch.cuda.synchronize()
+        o_ex, l_ex = do.clone(), dlse.clone()
+        for deg in (2, 3):
+            for _ in range(args.warmup):
+                lib.attn_decode_sas(uq, uk, uv, do, dlse, math.inf, deg, ws)
+            ts = Timer()
+            torch.cuda.synchronize()
+            for _ in range(args.steps):
+                with ts:
+                    lib.attn_decode_sas(uq, uk, uv, do, dlse, math.inf, deg, ws)
+            torch.cuda.synchronize()
+            s_ms = float(np.mean(ts.ms()))
+            dense_b, _ = decode_bytes(DB, DHkv, L, Dd)
+            out[f"decode_sas{deg}"] = dict(
+                value=round(dense_b / (s_ms * 1e-3) / 1e9, 2), unit="GB/s", ms=round(s_ms, 4),
+                max_abs_o_drift=float((do - o_ex).abs().max()),
+                max_abs_lse_drift=float((dlse - l_ex).abs().max()),
+                kernels=f"decode_split_kernel<128, {deg}> + decode_merge_kernel<128>")
+        del o_ex, l_ex
 
     qdecode = {}
     for w in widths:

@@ -169,6 +169,25 @@ int attn_decode_check(const void* q, const void* k, const void* v,
                       size_t workspace_bytes);
 
 /*
+ * attn_decode_sas - attn_decode with the Sparse Activated SoftMax
+ * exponential (TurboAttention talk page, "Technical Deep Dive", its Sparse
+ * Activated SoftMax part): inside each split every exponential of the
+ * online softmax, the probabilities e^-(m - s) and the rescale factor when
+ * a kept tile raises the running maximum m, is taken as T[n] p(f), with
+ * n = floor(x), f = x - n for x = m - s in logits, T[n] = e^-n for n < 6
+ * and 0 from 6 on, and p the least-squares polynomial of degree `degree`
+ * (2 or 3) for e^-f on [0, 1]. The skip decisions, splits, merge, outputs,
+ * mask and workspace are those of attn_decode; `degree` 0 is attn_decode
+ * itself. Results depend on the order in which the running maximum rises
+ * (the tiles are taken in ascending key order, as for the rule).
+ * Errors as for attn_decode, and SKIPATTN_EINVAL for another degree.
+ */
+int attn_decode_sas(const void* q, const void* k, const void* v, float* o,
+                    float* lse, int B, int Hq, int Hkv, int L, int d,
+                    float tau, int degree, uint8_t* skip_mask,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * 4-bit asymmetric KV cache (TurboAttention talk page, "Technical Deep Dive"
  * and its pre-fill / decoding workflow: the cache is stored and moved as
  * low-bit asymmetric integers with a floating zero point per block and is

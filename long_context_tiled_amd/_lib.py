@@ -25,7 +25,7 @@ EXPORTS = ("attn_prefill", "attn_decode", "attn_decode_workspace_bytes",
            "attn_kv_quantize_q4", "attn_decode_q4", "attn_decode_q4_check",
            "attn_prefill_chunk", "attn_prefill_chunk_check", "attn_kv_quantize_q4_range",
            "attn_kv_quantize_q2", "attn_kv_quantize_q2_range", "attn_decode_q2",
-           "attn_decode_q2_check")
+           "attn_decode_q2_check", "attn_decode_sas")
 
 _lib = None
 
@@ -57,6 +57,8 @@ def load() -> ctypes.CDLL:
     lib.attn_prefill_chunk_check.restype = i
     lib.attn_decode.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, f, u8p, vp, sz, vp]
     lib.attn_decode.restype = i
+    lib.attn_decode_sas.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, f, i, u8p, vp, sz, vp]
+    lib.attn_decode_sas.restype = i
     lib.attn_decode_check.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, f, u8p, vp, sz]
     lib.attn_decode_check.restype = i
     lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i]
@@ -165,6 +167,13 @@ def attn_decode(q, k, v, o, lse, tau: float, workspace, skip_mask=None,
     [B,Hq,d] fp32, lse [B,Hq] fp32 and, if given, skip_mask [B,Hq,ceil(L/64)]
     uint8. ``workspace`` is a device tensor of at least
     attn_decode_workspace_bytes(B, Hq, L, d) bytes."""
+    attn_decode_sas(q, k, v, o, lse, tau, 0, workspace, skip_mask, stream)
+
+
+def attn_decode_sas(q, k, v, o, lse, tau: float, degree: int, workspace, skip_mask=None,
+                    stream=None) -> None:
+    """attn_decode with the SAS exponential of polynomial degree 2 or 3
+    (0: exact exponentials, i.e. attn_decode)."""
     import torch
     B, Hq, d = q.shape
     Hkv, L = k.shape[1], k.shape[2]
@@ -178,9 +187,9 @@ def attn_decode(q, k, v, o, lse, tau: float, workspace, skip_mask=None,
     if workspace.device.type != "cuda" or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
     nbytes = workspace.numel() * workspace.element_size()
-    rc = load().attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv,
-                            L, d, float(tau), _ptr(skip_mask), _ptr(workspace), nbytes,
-                            _stream(stream))
+    rc = load().attn_decode_sas(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv,
+                                L, d, float(tau), int(degree), _ptr(skip_mask),
+                                _ptr(workspace), nbytes, _stream(stream))
     _raise(rc)
 
 
@@ -366,9 +375,10 @@ def prefill_chunk(q, k, v, causal: bool, tau: float = math.inf, want_mask: bool 
 
 
 def decode(q, k, v, tau: float = math.inf, want_mask: bool = False, workspace=None,
-           stream=None):
-    """Allocate outputs (and the workspace if not given) and call attn_decode.
-    Returns (o, lse, mask)."""
+           stream=None, sas: int = 0):
+    """Allocate outputs (and the workspace if not given) and call attn_decode
+    (attn_decode_sas with polynomial degree ``sas`` if nonzero). Returns
+    (o, lse, mask)."""
     import torch
     B, Hq, d = q.shape
     L = k.shape[2]
@@ -381,5 +391,5 @@ def decode(q, k, v, tau: float = math.inf, want_mask: bool = False, workspace=No
     if workspace is None:
         nbytes = max(16, attn_decode_workspace_bytes(B, Hq, L, d))
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    attn_decode(q, k, v, o, lse, tau, workspace, mask, stream)
+    attn_decode_sas(q, k, v, o, lse, tau, sas, workspace, mask, stream)
     return o, lse, mask

@@ -146,15 +146,24 @@ int attn_decode_check(const void* q, const void* k, const void* v, const float* 
 int attn_decode(const void* q, const void* k, const void* v, float* o, float* lse, int B,
                 int Hq, int Hkv, int L, int d, float tau, uint8_t* skip_mask, void* workspace,
                 size_t workspace_bytes, void* stream) {
+  return attn_decode_sas(q, k, v, o, lse, B, Hq, Hkv, L, d, tau, 0, skip_mask, workspace,
+                         workspace_bytes, stream);
+}
+
+int attn_decode_sas(const void* q, const void* k, const void* v, float* o, float* lse, int B,
+                    int Hq, int Hkv, int L, int d, float tau, int degree, uint8_t* skip_mask,
+                    void* workspace, size_t workspace_bytes, void* stream) {
   if (int e = attn_decode_check(q, k, v, o, lse, B, Hq, Hkv, L, d, tau, skip_mask, workspace,
                                 workspace_bytes))
     return e;
+  if (degree != 0 && degree != 2 && degree != 3)
+    return fail(SKIPATTN_EINVAL, "SAS degree must be 2 or 3, or 0 for exact (got %d)", degree);
   if (B == 0 || L == 0) return SKIPATTN_OK;
   const int nsplit = (L + SKIPATTN_SPLIT - 1) / SKIPATTN_SPLIT;
   float* ws_o = (float*)workspace;
   float* ws_lse = ws_o + (size_t)B * Hq * nsplit * d;
   skipattn::DecodeArgs a{q, k, v, o, lse, skip_mask, ws_o, ws_lse, B, Hq, Hkv, L, d, nsplit,
-                         tau_raw(tau, d), exp2_scale(d), stream};
+                         tau_raw(tau, d), exp2_scale(d), stream, degree};
   if (skipattn::launch_decode(a) != 0) return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(SKIPATTN_EHIP, "decode launch: %s", hipGetErrorString(err));

@@ -74,7 +74,32 @@ __device__ __forceinline__ void pair_fix(u32x4& r0, u32x4& r1, bool lo) {
   }
 }
 
-template <int D>
+// Sparse Activated SoftMax exponential (TurboAttention talk page,
+// "Technical Deep Dive", its Sparse Activated SoftMax part): e^-x for x >= 0
+// as T[n] p(f), n = floor(x), f = x - n, with T[n] = e^-n for n < 6 and 0
+// from 6 on, and p the least-squares polynomial of degree DEG for e^-f on
+// [0, 1] (solution of its normal equations, rounded to fp32). The
+// exponential unit gives e^-n for the integer n in one instruction, which
+// here stands in for the six-entry table (the same values to fp32
+// rounding); x = +inf gives 0.
+template <int DEG>
+__device__ __forceinline__ float sas_exp(float x) {
+  const float f = __builtin_amdgcn_fractf(x);
+  const float t = exp2_fast((x - f) * -1.44269504f);
+  float p;
+  if constexpr (DEG == 2)
+    p = __builtin_fmaf(__builtin_fmaf(0.30871853f, f, -0.9305485f), f, 0.9944886f);
+  else
+    p = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(-0.10250045f, f, 0.46246922f), f,
+                                      -0.99204874f),
+                       f, 0.99961364f);
+  return x < 6.f ? t * p : 0.f;
+}
+
+// SAS = 0: exact exponentials; SAS = 2 or 3: every exponential of the
+// split's online softmax (the probabilities and the rescale factor) is
+// sas_exp<SAS> of the distance below the running maximum in logits.
+template <int D, int SAS>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ ws_o,
@@ -255,7 +280,11 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
       // ---- online softmax for the heads that keep tile t ----
       const float mn = keep_cur ? fmaxf(m_ref, t_cur) : m_ref;
       if (mn > m_ref) {
-        const float alpha = exp2_fast((m_ref - mn) * c);
+        float alpha;
+        if constexpr (SAS == 0)
+          alpha = exp2_fast((m_ref - mn) * c);
+        else
+          alpha = sas_exp<SAS>((mn - m_ref) * (c * kLn2));
         lsum *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -273,8 +302,18 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
         for (int i2 = 0; i2 < 4; ++i2) {
           const int mb = 2 * ks + (i2 >> 1);
           const int r0 = 2 * (i2 & 1);
-          float p0 = exp2_fast(__builtin_fmaf(s_cur[mb][r0], c, nmc));
-          float p1 = exp2_fast(__builtin_fmaf(s_cur[mb][r0 + 1], c, nmc));
+          float p0, p1;
+          if constexpr (SAS == 0) {
+            p0 = exp2_fast(__builtin_fmaf(s_cur[mb][r0], c, nmc));
+            p1 = exp2_fast(__builtin_fmaf(s_cur[mb][r0 + 1], c, nmc));
+          } else {
+            // x = (m_ref - s) c ln 2, logits below the running maximum; the
+            // difference first, so that x >= 0 exactly (a fused form can
+            // round the maximum's own x below 0, across SAS's step at 0)
+            const float cn = c * kLn2;
+            p0 = sas_exp<SAS>((m_ref - s_cur[mb][r0]) * cn);
+            p1 = sas_exp<SAS>((m_ref - s_cur[mb][r0 + 1]) * cn);
+          }
           if (!keep_cur) { p0 = 0.f; p1 = 0.f; }
           part += p0 + p1;
           w[i2] = pack_bf16x2(p0, p1);
@@ -392,7 +431,9 @@ static int launch_d(const DecodeArgs& a) {
   if (nwork > 0x7fffffffLL || nbh > 0x7fffffffLL) return -1;
   const unsigned g1 = (unsigned)((nwork + 3) / 4);
   const unsigned g2 = (unsigned)((nbh + 3) / 4);
-  hipLaunchKernelGGL((decode_split_kernel<D>), dim3(g1), dim3(256), 0, (hipStream_t)a.stream,
+  auto kern = a.sas == 2 ? decode_split_kernel<D, 2>
+              : a.sas == 3 ? decode_split_kernel<D, 3> : decode_split_kernel<D, 0>;
+  hipLaunchKernelGGL(kern, dim3(g1), dim3(256), 0, (hipStream_t)a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      a.ws_o, a.ws_lse, a.mask, a.Hq, a.Hkv, a.L, a.nsplit, a.tau_raw,
                      a.c, (int)nwork);

@@ -34,6 +34,7 @@ struct DecodeArgs {
   float tau_raw;
   float c;
   void* stream;
+  int sas;        // 0: exact exponentials; 2 or 3: SAS polynomial degree
 };
 
 struct QuantArgs {

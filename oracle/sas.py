@@ -126,6 +126,7 @@ def decode_head(qvec: np.ndarray, k: np.ndarray, v: np.ndarray, tau: float, degr
         acc = np.zeros(d)
         l = 0.0
         jump_abs = 0.0   # possible absolute change of l from rounding at steps
+        jump_o = 0.0     # the same, weighted by 2 max |v_j| of the key
         jump_rel = 0.0   # possible relative change of everything accumulated
         for t in range(t0, min(nt, t0 + per)):
             if dec[t] != KEPT:
@@ -142,17 +143,19 @@ def decode_head(qvec: np.ndarray, k: np.ndarray, v: np.ndarray, tau: float, degr
                 acc *= alpha
                 l *= alpha
                 jump_abs *= alpha
+                jump_o *= alpha
                 m = mn
             x = m - st
             p = exp_fn(x)
             acc += p @ v[TILE * t:TILE * t + st.shape[0]]
             l += float(p.sum())
-            jump_abs += _near_jumps(degree, x, near)
+            steps = _near_jumps(degree, x, near)
+            jump_abs += float(steps.sum())
+            jump_o += float(steps @ (2.0 * np.abs(v[TILE * t:TILE * t + st.shape[0]]).max(axis=1)))
         if l > 0.0:
             parts.append((acc / l, m + math.log(l)))
-            rel = jump_abs / l + jump_rel
-            lse_slack = max(lse_slack, rel)
-            o_slack = max(o_slack, 2.0 * rel * vmax)
+            lse_slack = max(lse_slack, jump_abs / l + jump_rel)
+            o_slack = max(o_slack, jump_o / l + 2.0 * jump_rel * vmax)
     if not parts:
         return np.full(d, np.nan), -math.inf, dec, margin, (lse_slack, o_slack)
     lses = np.array([p[1] for p in parts])
@@ -164,12 +167,15 @@ def decode_head(qvec: np.ndarray, k: np.ndarray, v: np.ndarray, tau: float, degr
 
 
 def _near_jumps(degree, x, near):
-    """Sum of the steps of SAS at the integers within ``near`` of entries of x."""
+    """Per entry of x: the step of SAS at an integer within ``near`` of it, else 0."""
     x = np.asarray(x, np.float64)
     xf = np.where(np.isfinite(x), x, -1.0)
     k = np.rint(xf)
     hit = (k >= 1) & (k <= TABLE_SIZE) & (np.abs(xf - k) < near)
-    return float(sum(_boundary_jump(degree, int(kk)) for kk in k[hit]))
+    out = np.zeros(x.shape)
+    for i in np.nonzero(hit)[0]:
+        out[i] = _boundary_jump(degree, int(k[i]))
+    return out
 
 
 def _near_jump_rel(degree, x, near):

@@ -145,10 +145,13 @@ def check_prefill(q_bits, k_bits, v_bits, causal, tau, o, lse, mask, blocks=None
 
 
 def check_decode(q_bits, k_bits, v_bits, tau, o, lse, mask, heads=None,
-                 split=oracle.SPLIT, kv_for=None, Hkv=None) -> Report:
+                 split=oracle.SPLIT, kv_for=None, Hkv=None, sas=0) -> Report:
     """``kv_for(b, g)`` -> (k, v) fp64 (L, d) replaces the bf16 K/V (then
     k_bits and v_bits may be None and Hkv must be given): the 4-bit cache
-    is checked against the oracle on its dequantised values."""
+    is checked against the oracle on its dequantised values. ``sas`` = 2 or
+    3 checks against the SAS decode oracle of that degree; its tolerances
+    grow by the oracle's bound on the steps of SAS that the kernel's fp32
+    arguments may fall on the other side of."""
     B, Hq, d = q_bits.shape
     if kv_for is None:
         Hkv = k_bits.shape[1]
@@ -168,7 +171,11 @@ def check_decode(q_bits, k_bits, v_bits, tau, o, lse, mask, heads=None,
             cache[(b, g)] = kv_for(b, g)
         k, v = cache[(b, g)]
         qv = synth.bf16_bits_to_f64(q_bits[b, h])
-        ro, rl, dec, margin = oracle.decode_head(qv, k, v, tau, split)
+        def head(forced=None):
+            if sas:
+                return oracle.sas.decode_head(qv, k, v, tau, sas, split, forced)
+            return oracle.decode_head(qv, k, v, tau, split, forced) + ((0.0, 0.0),)
+        ro, rl, dec, margin, slack = head()
         visited = np.ones(dec.shape, bool)
         forced, amb, hard = _compare_decisions(mask[b, h].astype(np.int16),
                                                dec.astype(np.int16), margin, visited)
@@ -176,13 +183,14 @@ def check_decode(q_bits, k_bits, v_bits, tau, o, lse, mask, heads=None,
             bad = np.nonzero(mask[b, h] != dec)[0][:4]
             rep.notes.append(f"b={b} h={h} tiles={bad.tolist()} margin={margin[bad].tolist()}")
         if forced is not None:
-            ro, rl, _, _ = oracle.decode_head(qv, k, v, tau, split, forced)
+            ro, rl, _, _, slack = head(forced)
         rep.tiles += dec.size
         rep.skipped += int((mask[b, h] == 1).sum())
         rep.ambiguous += amb
         rep.hard_mismatch += hard
-        rep.o_err = max(rep.o_err, max_abs_err(o[b, h], ro))
-        rep.lse_err = max(rep.lse_err, max_abs_err(lse[b, h], rl))
+        # errors beyond the slack the SAS steps allow count against the tolerance
+        rep.o_err = max(rep.o_err, max(0.0, max_abs_err(o[b, h], ro) - slack[1]))
+        rep.lse_err = max(rep.lse_err, max(0.0, max_abs_err(lse[b, h], rl) - slack[0]))
     return rep
 
 
