@@ -54,13 +54,13 @@ MEASURED_TRAFFIC = {
                 "sha1": "997b1712c691d713dcef2bad76a69c55fe5807a3",
                 "bytes": (2711139.9 * 2.0 + 528384.0) * 1024},
     "decode_q4": {"sources": ("kvq4.hip", "kvq_common.hpp", "decode.hip", "common.hpp"),
-                  "sha1": "90cb67a117b9a33e8f688dfe392fb27ebc0c77da",
+                  "sha1": "cd4804ff4cf9010b83b8a6c63007cd33dbdc7b85",
                   "bytes": (1148234.6 * 2.0 + 16641.8) * 1024},
     "decode_q2": {"sources": ("kvq2.hip", "kvq_common.hpp", "decode.hip", "common.hpp"),
-                  "sha1": "23b5cbd49630c20bb83ed4ab273787b1c32a4639",
+                  "sha1": "f2a3384decbfa4800ad06886b2314c5a872c6114",
                   "bytes": (623771.7 * 2.0 + 16640.0) * 1024},
     "decode": {"sources": ("decode.hip", "common.hpp"),
-               "sha1": "9ba368983da045d60281a064227f2dc6aaa181cf",
+               "sha1": "037e2d1c54ff97bf3d7d038802d458d5b7c2bdf7",
                "bytes": (4195501.5 * 2.0 + 16641.6) * 1024},
 }
 
@@ -453,6 +453,17 @@ def main():
                 decode_q(math.inf)
         torch.cuda.synchronize()
         q_ms = float(np.mean(tqw.ms()))
+        # the same decode with the SAS exponential (degree 2), timed alike
+        dec_sas = getattr(lib, f"decode_q{w}")
+        for _ in range(args.warmup):
+            dec_sas(uq, cache, L, math.inf, workspace=ws, sas=2)
+        tsw = Timer()
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            with tsw:
+                dec_sas(uq, cache, L, math.inf, workspace=ws, sas=2)
+        torch.cuda.synchronize()
+        sas_ms = float(np.mean(tsw.ms()))
         dense_b, _ = decode_bytes(DB, DHkv, L, Dd)
         gbs_q = qb / (q_ms * 1e-3) / 1e9
         leg = f"decode_q{w}"
@@ -461,6 +472,7 @@ def main():
                         gbs_bf16_equivalent=round(dense_b / (q_ms * 1e-3) / 1e9, 2),
                         traffic=measured_traffic(leg),
                         quantise_ms=round(float(tq0.ms()[0]), 4),
+                        sas2_ms=round(sas_ms, 4),
                         kernels=f"decode_q{w}_split_kernel<128> + decode_merge_kernel<128>")
         if args.only == leg:
             # the step is this leg alone: its per-call time, its workload

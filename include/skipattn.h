@@ -293,6 +293,24 @@ int attn_decode_q2_check(const void* q, const uint8_t* kq, const uint32_t* kp,
                          const uint8_t* skip_mask, const void* workspace,
                          size_t workspace_bytes);
 
+/*
+ * attn_decode_q4_sas, attn_decode_q2_sas - attn_decode_q4 and
+ * attn_decode_q2 with the SAS exponential of attn_decode_sas (the quantised
+ * KV cache and SAS together, as in the talk's decoding workflow); `degree`
+ * 2 or 3, 0 for exact exponentials. Arguments and errors as for the
+ * quantised decodes, and SKIPATTN_EINVAL for another degree.
+ */
+int attn_decode_q4_sas(const void* q, const uint8_t* kq, const uint32_t* kp,
+                       const uint8_t* vq, const uint32_t* vp, float* o,
+                       float* lse, int B, int Hq, int Hkv, int L, int d,
+                       float tau, int degree, uint8_t* skip_mask,
+                       void* workspace, size_t workspace_bytes, void* stream);
+int attn_decode_q2_sas(const void* q, const uint8_t* kq, const uint32_t* kp,
+                       const uint8_t* vq, const uint32_t* vp, float* o,
+                       float* lse, int B, int Hq, int Hkv, int L, int d,
+                       float tau, int degree, uint8_t* skip_mask,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* Text for the last nonzero return on this thread ("" if none). */
 const char* attn_last_error(void);
 

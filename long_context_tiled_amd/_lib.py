@@ -25,7 +25,8 @@ EXPORTS = ("attn_prefill", "attn_decode", "attn_decode_workspace_bytes",
            "attn_kv_quantize_q4", "attn_decode_q4", "attn_decode_q4_check",
            "attn_prefill_chunk", "attn_prefill_chunk_check", "attn_kv_quantize_q4_range",
            "attn_kv_quantize_q2", "attn_kv_quantize_q2_range", "attn_decode_q2",
-           "attn_decode_q2_check", "attn_decode_sas")
+           "attn_decode_q2_check", "attn_decode_sas", "attn_decode_q4_sas",
+           "attn_decode_q2_sas")
 
 _lib = None
 
@@ -72,6 +73,9 @@ def load() -> ctypes.CDLL:
         fn.restype = i
         fn = getattr(lib, f"attn_decode_{w}")
         fn.argtypes = [vp, vp, vp, vp, vp, f32p, f32p, i, i, i, i, i, f, u8p, vp, sz, vp]
+        fn.restype = i
+        fn = getattr(lib, f"attn_decode_{w}_sas")
+        fn.argtypes = [vp, vp, vp, vp, vp, f32p, f32p, i, i, i, i, i, f, i, u8p, vp, sz, vp]
         fn.restype = i
         fn = getattr(lib, f"attn_decode_{w}_check")
         fn.argtypes = [vp, vp, vp, vp, vp, f32p, f32p, i, i, i, i, i, f, u8p, vp, sz]
@@ -231,7 +235,7 @@ def _quantize(bits, k, v, cache, stream, key_range):
     _raise(rc)
 
 
-def _decode_cache(bits, q, cache, L, o, lse, tau, workspace, skip_mask, stream):
+def _decode_cache(bits, q, cache, L, o, lse, tau, workspace, skip_mask, stream, sas=0):
     import torch
     B, Hq, d = q.shape
     Hkv = cache["kp"].shape[1]
@@ -244,10 +248,13 @@ def _decode_cache(bits, q, cache, L, o, lse, tau, workspace, skip_mask, stream):
     if workspace.device.type != "cuda" or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
     nbytes = workspace.numel() * workspace.element_size()
-    fn = getattr(load(), f"attn_decode_q{bits}")
-    rc = fn(_ptr(q), _ptr(cache["kq"]), _ptr(cache["kp"]), _ptr(cache["vq"]),
-            _ptr(cache["vp"]), _ptr(o), _ptr(lse), B, Hq, Hkv, L, d, float(tau),
-            _ptr(skip_mask), _ptr(workspace), nbytes, _stream(stream))
+    args = [_ptr(q), _ptr(cache["kq"]), _ptr(cache["kp"]), _ptr(cache["vq"]),
+            _ptr(cache["vp"]), _ptr(o), _ptr(lse), B, Hq, Hkv, L, d, float(tau)]
+    tail = [_ptr(skip_mask), _ptr(workspace), nbytes, _stream(stream)]
+    if sas:
+        rc = getattr(load(), f"attn_decode_q{bits}_sas")(*args, int(sas), *tail)
+    else:
+        rc = getattr(load(), f"attn_decode_q{bits}")(*args, *tail)
     _raise(rc)
 
 
@@ -312,7 +319,7 @@ def quantize_q2(k, v, stream=None) -> dict:
     return cache
 
 
-def _decode_alloc(bits, q, cache, L, tau, want_mask, workspace, stream):
+def _decode_alloc(bits, q, cache, L, tau, want_mask, workspace, stream, sas=0):
     import torch
     B, Hq, d = q.shape
     o = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
@@ -324,21 +331,22 @@ def _decode_alloc(bits, q, cache, L, tau, want_mask, workspace, stream):
     if workspace is None:
         nbytes = max(16, attn_decode_workspace_bytes(B, Hq, L, d))
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    _decode_cache(bits, q, cache, L, o, lse, tau, workspace, mask, stream)
+    _decode_cache(bits, q, cache, L, o, lse, tau, workspace, mask, stream, sas)
     return o, lse, mask
 
 
 def decode_q4(q, cache, L: int, tau: float = math.inf, want_mask: bool = False,
-              workspace=None, stream=None):
+              workspace=None, stream=None, sas: int = 0):
     """Allocate outputs (and the workspace if not given) and call
-    attn_decode_q4. Returns (o, lse, mask)."""
-    return _decode_alloc(4, q, cache, L, tau, want_mask, workspace, stream)
+    attn_decode_q4 (attn_decode_q4_sas of degree ``sas`` if nonzero).
+    Returns (o, lse, mask)."""
+    return _decode_alloc(4, q, cache, L, tau, want_mask, workspace, stream, sas)
 
 
 def decode_q2(q, cache, L: int, tau: float = math.inf, want_mask: bool = False,
-              workspace=None, stream=None):
+              workspace=None, stream=None, sas: int = 0):
     """As decode_q4, over a 2-bit cache."""
-    return _decode_alloc(2, q, cache, L, tau, want_mask, workspace, stream)
+    return _decode_alloc(2, q, cache, L, tau, want_mask, workspace, stream, sas)
 
 
 # ---- allocation conveniences around the two bf16 entry points ----

@@ -193,8 +193,12 @@ namespace {
 int decode_quantized(int (*launch)(const skipattn::DecodeQ4Args&), const char* what,
                      const void* q, const uint8_t* kq, const uint32_t* kp, const uint8_t* vq,
                      const uint32_t* vp, float* o, float* lse, int B, int Hq, int Hkv, int L,
-                     int d, float tau, uint8_t* skip_mask, void* workspace,
+                     int d, float tau, int degree, uint8_t* skip_mask, void* workspace,
                      size_t workspace_bytes, void* stream) {
+  if (degree != 0 && degree != 2 && degree != 3) {
+    g_err[0] = '\0';
+    return fail(SKIPATTN_EINVAL, "SAS degree must be 2 or 3, or 0 for exact (got %d)", degree);
+  }
   if (int e = attn_decode_q4_check(q, kq, kp, vq, vp, o, lse, B, Hq, Hkv, L, d, tau, skip_mask,
                                    workspace, workspace_bytes))
     return e;
@@ -204,7 +208,7 @@ int decode_quantized(int (*launch)(const skipattn::DecodeQ4Args&), const char* w
   float* ws_lse = ws_o + (size_t)B * Hq * nsplit * d;
   skipattn::DecodeQ4Args a{q,         kq,   kp,     vq, vp,     o,  lse,      skip_mask,
                            ws_o,      ws_lse, B,   Hq, Hkv, L, d, nsplit,
-                           tau_raw(tau, d), exp2_scale(d), stream};
+                           tau_raw(tau, d), exp2_scale(d), stream, degree};
   if (launch(a) != 0) return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(SKIPATTN_EHIP, "%s launch: %s", what, hipGetErrorString(err));
@@ -249,7 +253,7 @@ int attn_decode_q4(const void* q, const uint8_t* kq, const uint32_t* kp, const u
                    float tau, uint8_t* skip_mask, void* workspace, size_t workspace_bytes,
                    void* stream) {
   return decode_quantized(skipattn::launch_decode_q4, "decode_q4", q, kq, kp, vq, vp, o, lse, B,
-                          Hq, Hkv, L, d, tau, skip_mask, workspace, workspace_bytes, stream);
+                          Hq, Hkv, L, d, tau, 0, skip_mask, workspace, workspace_bytes, stream);
 }
 
 int attn_kv_quantize_q4_range(const void* k, const void* v, uint8_t* kq, uint32_t* kp,
@@ -278,7 +282,27 @@ int attn_decode_q2(const void* q, const uint8_t* kq, const uint32_t* kp, const u
                    float tau, uint8_t* skip_mask, void* workspace, size_t workspace_bytes,
                    void* stream) {
   return decode_quantized(skipattn::launch_decode_q2, "decode_q2", q, kq, kp, vq, vp, o, lse, B,
-                          Hq, Hkv, L, d, tau, skip_mask, workspace, workspace_bytes, stream);
+                          Hq, Hkv, L, d, tau, 0, skip_mask, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_q4_sas(const void* q, const uint8_t* kq, const uint32_t* kp,
+                       const uint8_t* vq, const uint32_t* vp, float* o, float* lse, int B,
+                       int Hq, int Hkv, int L, int d, float tau, int degree,
+                       uint8_t* skip_mask, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return decode_quantized(skipattn::launch_decode_q4, "decode_q4", q, kq, kp, vq, vp, o, lse, B,
+                          Hq, Hkv, L, d, tau, degree, skip_mask, workspace, workspace_bytes,
+                          stream);
+}
+
+int attn_decode_q2_sas(const void* q, const uint8_t* kq, const uint32_t* kp,
+                       const uint8_t* vq, const uint32_t* vp, float* o, float* lse, int B,
+                       int Hq, int Hkv, int L, int d, float tau, int degree,
+                       uint8_t* skip_mask, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return decode_quantized(skipattn::launch_decode_q2, "decode_q2", q, kq, kp, vq, vp, o, lse, B,
+                          Hq, Hkv, L, d, tau, degree, skip_mask, workspace, workspace_bytes,
+                          stream);
 }
 
 int attn_kv_quantize_q2_range(const void* k, const void* v, uint8_t* kq, uint32_t* kp,

@@ -29,6 +29,7 @@
 // Merge kernel: one wave per (b, query head): LSE = log sum_s e^lse_s and
 // O = sum_s e^(lse_s - LSE) O_s.
 #include "common.hpp"
+#include "sas.hpp"
 #include "launch.hpp"
 
 namespace skipattn {
@@ -72,28 +73,6 @@ __device__ __forceinline__ void pair_fix(u32x4& r0, u32x4& r1, bool lo) {
     r0[e] = lo ? r0[e] : y1;
     r1[e] = lo ? y0 : r1[e];
   }
-}
-
-// Sparse Activated SoftMax exponential (TurboAttention talk page,
-// "Technical Deep Dive", its Sparse Activated SoftMax part): e^-x for x >= 0
-// as T[n] p(f), n = floor(x), f = x - n, with T[n] = e^-n for n < 6 and 0
-// from 6 on, and p the least-squares polynomial of degree DEG for e^-f on
-// [0, 1] (solution of its normal equations, rounded to fp32). The
-// exponential unit gives e^-n for the integer n in one instruction, which
-// here stands in for the six-entry table (the same values to fp32
-// rounding); x = +inf gives 0.
-template <int DEG>
-__device__ __forceinline__ float sas_exp(float x) {
-  const float f = __builtin_amdgcn_fractf(x);
-  const float t = exp2_fast((x - f) * -1.44269504f);
-  float p;
-  if constexpr (DEG == 2)
-    p = __builtin_fmaf(__builtin_fmaf(0.30871853f, f, -0.9305485f), f, 0.9944886f);
-  else
-    p = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(-0.10250045f, f, 0.46246922f), f,
-                                      -0.99204874f),
-                       f, 0.99961364f);
-  return x < 6.f ? t * p : 0.f;
 }
 
 // SAS = 0: exact exponentials; SAS = 2 or 3: every exponential of the

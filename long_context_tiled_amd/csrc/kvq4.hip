@@ -51,6 +51,7 @@
 //   4 rows; V: 16 rows of 32 bytes) with the non-temporal policy; the small
 //   parameter words use the default policy.
 #include "kvq_common.hpp"
+#include "sas.hpp"
 #include "launch.hpp"
 
 namespace skipattn {
@@ -207,7 +208,9 @@ __device__ __forceinline__ f16x8 expand_word_f16(uint32_t w, const ExpandConsts&
 
 
 
-template <int D>
+// SAS = 0: exact exponentials; 2 or 3: the SAS exponential of that degree
+// for every exponential of the split's online softmax.
+template <int D, int SAS>
 __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kq,
     const uint32_t* __restrict__ kp, const uint8_t* __restrict__ vq,
@@ -428,7 +431,11 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
     if (any_cur) {
       const float mn = keep_cur ? fmaxf(m_ref, t_cur) : m_ref;
       if (__ballot(mn > m_ref) != 0ull) {
-        const float alpha = mn > m_ref ? exp2_fast((m_ref - mn) * c) : 1.f;
+        float alpha;
+        if constexpr (SAS == 0)
+          alpha = mn > m_ref ? exp2_fast((m_ref - mn) * c) : 1.f;
+        else
+          alpha = mn > m_ref ? sas_exp<SAS>((mn - m_ref) * (c * kLn2)) : 1.f;
         m_ref = mn;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -448,8 +455,14 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          pf[ks][e] = (_Float16)exp2_fast(
-              __builtin_fmaf(s_cur[2 * ks + (e >> 2)][e & 3], c, (e & 2) ? nmc : nmc4));
+          if constexpr (SAS == 0)
+            pf[ks][e] = (_Float16)exp2_fast(
+                __builtin_fmaf(s_cur[2 * ks + (e >> 2)][e & 3], c, (e & 2) ? nmc : nmc4));
+          else  // x from the difference, so x >= 0 exactly
+            pf[ks][e] = keep_cur ? (_Float16)sas_exp_scaled<SAS>(
+                                       (m_ref - s_cur[2 * ks + (e >> 2)][e & 3]) * (c * kLn2),
+                                       (e & 2) ? 0.f : 4.f)
+                                 : (_Float16)0.f;
       // sum_j p_j (pt) and -1024 sum_j p'_j (u0) of head 4 grp + r, from
       // MFMAs over the same fp16 P' (B = per-position weights, then -1024)
       f32x4 pt = {0.f, 0.f, 0.f, 0.f}, u0 = {0.f, 0.f, 0.f, 0.f};
@@ -541,7 +554,9 @@ int launch_dq_d(const DecodeQ4Args& a) {
   const long long nwork = (long long)a.B * a.Hkv * a.nsplit;
   if (nwork > 0x7fffffffLL) return -1;
   const unsigned g1 = (unsigned)((nwork + 3) / 4);
-  hipLaunchKernelGGL((decode_q4_split_kernel<D>), dim3(g1), dim3(256), 0, (hipStream_t)a.stream,
+  auto kern = a.sas == 2 ? decode_q4_split_kernel<D, 2>
+              : a.sas == 3 ? decode_q4_split_kernel<D, 3> : decode_q4_split_kernel<D, 0>;
+  hipLaunchKernelGGL(kern, dim3(g1), dim3(256), 0, (hipStream_t)a.stream,
                      (const uint16_t*)a.q, a.kq, a.kp, a.vq, a.vp, a.ws_o, a.ws_lse, a.mask, a.Hq,
                      a.Hkv, a.L, a.nsplit, a.tau_raw, a.c, (int)nwork);
   return launch_decode_merge(a.ws_o, a.ws_lse, a.o, a.lse, a.B * a.Hq, a.d, a.nsplit, a.stream);

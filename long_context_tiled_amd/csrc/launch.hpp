@@ -64,6 +64,7 @@ struct DecodeQ4Args {
   float tau_raw;
   float c;
   void* stream;
+  int sas;        // 0: exact exponentials; 2 or 3: SAS polynomial degree
 };
 
 // Each returns 0 when the kernels were enqueued, nonzero if the grid cannot

@@ -98,3 +98,45 @@ def test_decode_sas_workload_sampled(degree):
         print(f"  {rep}", flush=True)
         assert rep.ok(), str(rep)
         del o, lse, mask
+
+
+QCASES = [
+    ("q_gqa4_ragged", _cfg(id=120), (INF, 4.0)),
+    ("q_g8_d64_edge", _cfg(B=1, Hq=8, Hkv=1, L=4097, d=64, id=121), (INF, 2.0)),
+    ("q_g16_plain", _cfg(B=1, Hq=16, Hkv=1, L=9000, id=122, sinks=False, window=False),
+     (INF,)),
+]
+
+
+@pytest.mark.parametrize("width", [4, 2])
+@pytest.mark.parametrize("degree", [2, 3])
+@pytest.mark.parametrize("name,cfg,taus", QCASES, ids=[c[0] for c in QCASES])
+def test_decode_quantized_sas(name, cfg, taus, degree, width):
+    """The quantised cache and SAS together: against the SAS oracle on the
+    oracle's dequantised cache."""
+    import torch
+    import long_context_tiled_amd as lib
+    from oracle import kvq2, kvq4
+    codec = {4: kvq4, 2: kvq2}[width]
+    quantize = {4: lib.quantize_q4, 2: lib.quantize_q2}[width]
+    decode = {4: lib.decode_q4, 2: lib.decode_q2}[width]
+    q, k, v = synth.make_decode(cfg)
+    Hkv, L = k.shape[1], k.shape[2]
+    print(f"[sas] q{width} {name}: quantise", flush=True)
+    cache = quantize(_dev(k), _dev(v))
+    enc = codec.encode(synth.bf16_bits_to_f32(k), synth.bf16_bits_to_f32(v))
+
+    def kv_for(b, g):
+        return (codec.decode_k(enc["kq"][b, g], enc["kp"][b, g]),
+                codec.decode_v(enc["vq"][b, g], enc["vp"][b, g], L))
+    dq = _dev(q)
+    for tau in taus:
+        print(f"[sas] q{width} {name} degree={degree} tau={tau}", flush=True)
+        o, lse, mask = decode(dq, cache, L, tau, want_mask=True, sas=degree)
+        _, _, mask0 = decode(dq, cache, L, tau, want_mask=True)
+        torch.cuda.synchronize()
+        assert torch.equal(mask, mask0), "SAS must not change the skip decisions"
+        rep = _parity.check_decode(q, None, None, tau, o.cpu().numpy(), lse.cpu().numpy(),
+                                   mask.cpu().numpy(), kv_for=kv_for, Hkv=Hkv, sas=degree)
+        print(f"  {rep}", flush=True)
+        assert rep.ok(), str(rep)
