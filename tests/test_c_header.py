@@ -1,6 +1,7 @@
 """The C ABI from plain C: include/skipattn.h compiles as C99 with every
 warning an error, and a C program linked against libskipattn.so calls the
-validation entry points and the workspace-size query (no GPU needed)."""
+validation entry points, the workspace-size query and the SAS entry points
+with a rejected degree (no GPU needed)."""
 import os
 import shutil
 import subprocess
@@ -43,6 +44,15 @@ PROGRAM = textwrap.dedent(r"""
                             INFINITY, NULL, P, 16) != SKIPATTN_EWORKSPACE) bad = 1;
       if (attn_decode_check(P, P, P, (float*)P, (float*)P, 16, 64, 8, 131072, 128,
                             INFINITY, NULL, P, ws) != SKIPATTN_OK) bad = 1;
+      /* SAS degrees other than 0, 2, 3 are rejected before any launch */
+      if (attn_decode_sas(P, P, P, (float*)P, (float*)P, 16, 64, 8, 131072, 128,
+                          INFINITY, 5, NULL, P, ws, NULL) != SKIPATTN_EINVAL) bad = 1;
+      if (attn_decode_q4_sas(P, (const uint8_t*)P, (const uint32_t*)P, (const uint8_t*)P,
+                             (const uint32_t*)P, (float*)P, (float*)P, 16, 64, 8, 131072,
+                             128, INFINITY, 1, NULL, P, ws, NULL) != SKIPATTN_EINVAL) bad = 1;
+      if (attn_decode_q2_sas(P, (const uint8_t*)P, (const uint32_t*)P, (const uint8_t*)P,
+                             (const uint32_t*)P, (float*)P, (float*)P, 16, 64, 8, 131072,
+                             128, INFINITY, -2, NULL, P, ws, NULL) != SKIPATTN_EINVAL) bad = 1;
       printf(bad ? "FAIL\n" : "OK\n");
       return bad;
     }
