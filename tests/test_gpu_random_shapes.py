@@ -2,7 +2,8 @@
 ragged lengths, both head sizes, causal or not, structured or plain inputs,
 several tau. Every case compares full outputs with the fp64 oracle through
 the C ABI (skip masks exact except near-margin tiles, O within 1e-2, LSE
-within 1e-3; 4-bit and 2-bit codes bit for bit)."""
+within 1e-3; 4-bit and 2-bit codes bit for bit; the SAS decodes against the
+SAS oracle)."""
 import math
 
 import numpy as np
@@ -58,6 +59,7 @@ PREFILL = _prefill_cases(24, 2026)
 DECODE = _decode_cases(16, 2027, 240)
 DECODE_Q4 = _decode_cases(12, 2028, 270)
 DECODE_Q2 = _decode_cases(8, 2029, 290)
+DECODE_SAS = _decode_cases(10, 2030, 300)
 
 
 @pytest.mark.parametrize("name,cfg,taus", PREFILL, ids=[c[0] for c in PREFILL])
@@ -116,7 +118,7 @@ def test_decode_random_shape(name, cfg, taus):
         assert rep.ok(), str(rep)
 
 
-def _quantized_case(width, name, cfg, taus):
+def _quantized_case(width, name, cfg, taus, sas=0):
     import torch
     import long_context_tiled_amd as lib
     codec = {4: kvq4, 2: kvq2}[width]
@@ -140,10 +142,10 @@ def _quantized_case(width, name, cfg, taus):
     dq = _dev(q)
     for tau in taus:
         print(f"[random] q{width} {name} tau={tau}", flush=True)
-        o, lse, mask = decode(dq, cache, L, tau, want_mask=True)
+        o, lse, mask = decode(dq, cache, L, tau, want_mask=True, sas=sas)
         torch.cuda.synchronize()
         rep = _parity.check_decode(q, None, None, tau, o.cpu().numpy(), lse.cpu().numpy(),
-                                   mask.cpu().numpy(), kv_for=kv_for, Hkv=Hkv)
+                                   mask.cpu().numpy(), kv_for=kv_for, Hkv=Hkv, sas=sas)
         print(f"  {rep}", flush=True)
         assert rep.ok(), str(rep)
 
@@ -156,3 +158,23 @@ def test_decode_q4_random_shape(name, cfg, taus):
 @pytest.mark.parametrize("name,cfg,taus", DECODE_Q2, ids=[c[0] for c in DECODE_Q2])
 def test_decode_q2_random_shape(name, cfg, taus):
     _quantized_case(2, name, cfg, taus)
+
+
+@pytest.mark.parametrize("name,cfg,taus", DECODE_SAS, ids=[c[0] for c in DECODE_SAS])
+def test_decode_sas_random_shape(name, cfg, taus):
+    """SAS decodes on random shapes: the bf16 cache for every case, then the
+    4-bit or 2-bit cache by turns; degree 2 or 3 by turns."""
+    import torch
+    import long_context_tiled_amd as lib
+    degree = 2 + cfg["id"] % 2
+    q, k, v = synth.make_decode(cfg)
+    dq, dk, dv = _dev(q), _dev(k), _dev(v)
+    for tau in taus[:2]:
+        print(f"[random] sas{degree} {name} tau={tau}", flush=True)
+        o, lse, mask = lib.decode(dq, dk, dv, tau, want_mask=True, sas=degree)
+        torch.cuda.synchronize()
+        rep = _parity.check_decode(q, k, v, tau, o.cpu().numpy(), lse.cpu().numpy(),
+                                   mask.cpu().numpy(), sas=degree)
+        print(f"  {rep}", flush=True)
+        assert rep.ok(), str(rep)
+    _quantized_case(4 if cfg["id"] % 4 < 2 else 2, name, cfg, taus[:1], sas=degree)
