@@ -15,6 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def bench():
     spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
     mod = importlib.util.module_from_spec(spec)
+    sys.modules[spec.name] = mod   # the CPU leg's process pool pickles its functions by name
     spec.loader.exec_module(mod)
     return mod
 
@@ -85,3 +86,20 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_cpu_baseline_runs_on_tiny_inputs(bench):
+    # the host leg of bench.py (the oracle timed on a sample), at toy sizes
+    import synth
+    rng = np.random.default_rng(0)
+
+    def bits(*shape):
+        return synth.f32_to_bf16_bits(rng.normal(size=shape).astype(np.float32))
+    pq, pk, pv = bits(1, 1, 256, 64), bits(1, 1, 256, 64), bits(1, 1, 256, 64)
+    dq, dk, dv = bits(2, 4, 64), bits(2, 2, 300, 64), bits(2, 2, 300, 64)
+    pre, dec, dq4, dq2 = bench.cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=4, nkv=3, nkv_q=2,
+                                            pname="tiny")
+    for r in (pre, dec, dq4, dq2):
+        assert r["kind"] == "oracle" and r["value"] > 0 and r["cores"] >= 1
+    assert pre["unit"] == "TFLOP/s" and dq2["unit"] == "GB/s"
+    assert "2-bit" in dq2["sample"] and "4-bit" in dq4["sample"]
