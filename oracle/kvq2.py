@@ -32,8 +32,9 @@ Readings, as for the 4-bit format except where stated:
 
 Parity unpinned: these format choices are readings, not the pages'. The
 tests pin that the code implements them: hand-derived layout bytes, exact
-round trips of caches built on the code grid, and the error bound of
-uniform quantisation.
+round trips of caches built on the code grid, hand-derived codes where
+(x - z) / s is exactly k + 1/2 (ties go to the even code), and the error
+bound of uniform quantisation.
 """
 from __future__ import annotations
 

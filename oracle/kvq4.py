@@ -40,7 +40,9 @@ the readings taken here:
 Parity unpinned: these format choices are readings, not the pages' (which
 give no block size, rounding or layout). What the tests pin is that the code
 implements them: hand-derived layout bytes, exact round trips of caches
-built on the code grid, and the error bound of uniform quantisation.
+built on the code grid, hand-derived codes where (x - z) / s is exactly
+k + 1/2 (ties go to the even code), and the error bound of uniform
+quantisation.
 """
 from __future__ import annotations
 

@@ -36,7 +36,9 @@ are readings, not values the pages print. The tests pin the functions:
 the fit's residual is orthogonal to 1, f, .., f^deg under numerical
 quadrature; the table values and the cut at 6; the error bounds; with exact
 exponentials the online loop reproduces the exact decode oracle; with a
-single kept tile (no rescale) it equals the direct formula.
+single kept tile (no rescale) it equals the direct formula; and a
+hand-derived two-tile case, whose running maximum rises by 2.25 logits,
+fixes SAS on the rescale factor as well as on the probabilities.
 """
 from __future__ import annotations
 

@@ -118,3 +118,20 @@ def test_partial_tile_uses_only_present_keys():
     assert np.all(s[0, 0, 1] * 15 >= tail.max(0) - tail.min(0))
     c, _, _ = kvq4.quantize_v(v)
     assert np.all(c[0, 0, 1, :, 6:] == 0)
+
+
+def test_golden_rounding_ties_go_to_even():
+    # (x - z) / s exactly k + 1/2: hand-derived codes (ties to the even
+    # code), both as K rows and as V channels of one 64-key tile.
+    g = json.load(open(GOLDEN))["ties"]
+    for row in g["rows"]:
+        x = np.array(row["x"], np.float32)
+        c, s, z = kvq4.quantize_k(x[None, None, None, :])
+        assert float(s.ravel()[0]) == row["s"] and float(z.ravel()[0]) == row["z"]
+        assert list(c.ravel()) == row["codes"], row
+        assert row["codes"] != row["half_up_would_give"]
+        v = np.zeros((1, 1, 8, 4), np.float32)
+        v[0, 0, :, 1] = x                            # channel 1 over the tile's 8 keys
+        cv, sv, zv = kvq4.quantize_v(v)
+        assert float(sv[0, 0, 0, 1]) == row["s"] and float(zv[0, 0, 0, 1]) == row["z"]
+        assert list(cv[0, 0, 0, 1, :8]) == row["codes"], row

@@ -131,3 +131,33 @@ def test_slack_counts_arguments_at_the_steps():
     k[1, 0] = 0.5                    # x = 0.75: no step nearby
     _, _, _, _, (ls, os_) = sas.decode_head(q, k, v, math.inf, 2)
     assert ls == 0 and os_ == 0
+
+
+def test_golden_two_tile_rescale_uses_sas():
+    # A hand-derived case whose running maximum rises by 2.25 logits between
+    # the two tiles: the expected O and LSE apply T[n] p(f) to the
+    # probabilities and to the rescale factor alike (tests/golden).
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "sas_two_tile.json")))
+    d, L = 4, 128
+    q = np.array([2.0, 0.0, 0.0, 0.0])
+    k = np.zeros((L, d))
+    k[:, 0] = -100.0
+    k[0, 0] = 0.0
+    k[64, 0] = 2.25
+    v = np.zeros((L, d))
+    v[:, 2] = 1.0
+    v[0] = [1.0, 0.0, 0.0, 0.0]
+    v[64] = [0.0, 1.0, 0.0, 0.0]
+    for case in g["cases"]:
+        dg = case["degree"]
+        assert np.allclose(sas.poly_coeffs(dg), case["coeffs"], rtol=0, atol=1e-14)
+        assert abs(float(sas.sas_exp(np.array([2.25]), dg)[0]) - case["alpha"]) < 1e-15
+        o, lse, dec, _, _ = sas.decode_head(q, k, v, math.inf, dg)
+        assert np.all(dec == oracle.KEPT)
+        assert np.abs(o - np.array(case["o"])).max() < 1e-12, (dg, o)
+        assert abs(lse - case["lse"]) < 1e-12, (dg, lse)
+        # the case separates SAS on the rescale factor from an exact one
+        assert np.abs(np.array(case["o"]) - np.array(case["o_if_alpha_exact"])).max() > 1e-6
+        assert abs(case["lse"] - case["lse_if_alpha_exact"]) > 1e-6
