@@ -41,12 +41,15 @@
  * Return codes
  *   SKIPATTN_OK           0
  *   SKIPATTN_EINVAL       1  NULL q/k/v/o/lse pointer; negative size;
- *                            Hq or Hkv < 1 or Hq % Hkv != 0; causal not 0/1;
- *                            tau NaN or < 0; a pointer not 16-byte aligned;
- *                            an element count beyond 2^40
- *   SKIPATTN_EUNSUPPORTED 2  d not in {64, 128}; decode with Hq/Hkv > 16;
- *                            one head of K/V over 2^31 - 2^16 bytes
- *                            (N * d * 2, L * d * 2)
+ *                            Hq or Hkv < 1 or Hq % Hkv != 0; d not in
+ *                            {64, 128}; causal not 0/1; tau NaN or < 0; a
+ *                            pointer not 16-byte aligned; an element count
+ *                            beyond 2^40; a cache capacity below the
+ *                            attended length (the _cap entry points)
+ *   SKIPATTN_EUNSUPPORTED 2  one head of K/V over 2^31 - 2^16 bytes
+ *                            (N * d * 2, L * d * 2); a causal chunk that
+ *                            does not start on a 64-key boundary; a
+ *                            quantiser key range starting off a tile
  *   SKIPATTN_EWORKSPACE   3  decode workspace NULL or smaller than
  *                            attn_decode_workspace_bytes()
  *   SKIPATTN_EHIP         4  a kernel launch failed (hipGetLastError)
@@ -118,6 +121,19 @@ int attn_prefill_chunk(const void* q, const void* k, const void* v, float* o,
                        int causal, float tau, uint8_t* skip_mask, void* stream);
 
 /*
+ * attn_prefill_chunk_cap - attn_prefill_chunk over K and V held in a cache
+ * allocated for `cap` keys per (sequence, KV head), of which the first N
+ * exist (chunked prefill into a preallocated cache):
+ *   k, v  bf16 [B, Hkv, cap, d]   rows N .. cap - 1 are not read
+ * cap >= N (SKIPATTN_EINVAL otherwise); every other argument, result and
+ * error as for attn_prefill_chunk, which is the case cap == N.
+ */
+int attn_prefill_chunk_cap(const void* q, const void* k, const void* v, float* o,
+                           float* lse, int B, int Hq, int Hkv, int Nq, int N,
+                           int cap, int d, int causal, float tau,
+                           uint8_t* skip_mask, void* stream);
+
+/*
  * attn_decode_workspace_bytes - bytes of device scratch attn_decode needs:
  * B * Hq * ceil(L / 4096) * (d + 1) * 4 (per-split partial outputs and
  * log-sum-exps). Returns 0 for invalid or empty sizes.
@@ -184,6 +200,21 @@ int attn_decode_check(const void* q, const void* k, const void* v,
  */
 int attn_decode_sas(const void* q, const void* k, const void* v, float* o,
                     float* lse, int B, int Hq, int Hkv, int L, int d,
+                    float tau, int degree, uint8_t* skip_mask,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_cap - attn_decode_sas over a KV cache allocated for `cap` keys
+ * per (sequence, KV head), of which the first L are attended (a cache that
+ * is appended to between decode steps):
+ *   k, v  bf16 [B, Hkv, cap, d]   rows L .. cap - 1 are not read
+ * cap >= L (SKIPATTN_EINVAL otherwise); `degree` 0 for exact exponentials,
+ * 2 or 3 for SAS; the mask is [B, Hq, ceil(L/64)] and the workspace that of
+ * attn_decode_workspace_bytes(B, Hq, L, d). attn_decode is the case
+ * cap == L, degree == 0.
+ */
+int attn_decode_cap(const void* q, const void* k, const void* v, float* o,
+                    float* lse, int B, int Hq, int Hkv, int L, int cap, int d,
                     float tau, int degree, uint8_t* skip_mask,
                     void* workspace, size_t workspace_bytes, void* stream);
 
@@ -309,6 +340,26 @@ int attn_decode_q2_sas(const void* q, const uint8_t* kq, const uint32_t* kp,
                        const uint8_t* vq, const uint32_t* vp, float* o,
                        float* lse, int B, int Hq, int Hkv, int L, int d,
                        float tau, int degree, uint8_t* skip_mask,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_q4_cap, attn_decode_q2_cap - the quantised decodes over cache
+ * arrays sized for `cap` keys (the shapes above with cap in place of L, as
+ * written by attn_kv_quantize_q4_range / _q2_range with L = cap), of which
+ * the first L keys are attended: a cache appended to chunk by chunk and
+ * decoded at its current length. cap >= L (SKIPATTN_EINVAL otherwise);
+ * `degree` as for attn_decode_q4_sas; other arguments, results and errors as
+ * for attn_decode_q4 / attn_decode_q2 (the case cap == L).
+ */
+int attn_decode_q4_cap(const void* q, const uint8_t* kq, const uint32_t* kp,
+                       const uint8_t* vq, const uint32_t* vp, float* o,
+                       float* lse, int B, int Hq, int Hkv, int L, int cap,
+                       int d, float tau, int degree, uint8_t* skip_mask,
+                       void* workspace, size_t workspace_bytes, void* stream);
+int attn_decode_q2_cap(const void* q, const uint8_t* kq, const uint32_t* kp,
+                       const uint8_t* vq, const uint32_t* vp, float* o,
+                       float* lse, int B, int Hq, int Hkv, int L, int cap,
+                       int d, float tau, int degree, uint8_t* skip_mask,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* Text for the last nonzero return on this thread ("" if none). */

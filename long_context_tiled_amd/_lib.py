@@ -26,7 +26,8 @@ EXPORTS = ("attn_prefill", "attn_decode", "attn_decode_workspace_bytes",
            "attn_prefill_chunk", "attn_prefill_chunk_check", "attn_kv_quantize_q4_range",
            "attn_kv_quantize_q2", "attn_kv_quantize_q2_range", "attn_decode_q2",
            "attn_decode_q2_check", "attn_decode_sas", "attn_decode_q4_sas",
-           "attn_decode_q2_sas")
+           "attn_decode_q2_sas", "attn_prefill_chunk_cap", "attn_decode_cap",
+           "attn_decode_q4_cap", "attn_decode_q2_cap")
 
 _lib = None
 
@@ -55,11 +56,17 @@ def load() -> ctypes.CDLL:
     lib.attn_prefill_chunk.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, i, i, f, u8p, vp]
     lib.attn_prefill_chunk.restype = i
     lib.attn_prefill_chunk_check.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, i, i, f, u8p]
+    lib.attn_prefill_chunk_cap.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, i, i, i, f, u8p,
+                                           vp]
+    lib.attn_prefill_chunk_cap.restype = i
     lib.attn_prefill_chunk_check.restype = i
     lib.attn_decode.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, f, u8p, vp, sz, vp]
     lib.attn_decode.restype = i
     lib.attn_decode_sas.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, f, i, u8p, vp, sz, vp]
     lib.attn_decode_sas.restype = i
+    lib.attn_decode_cap.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, i, f, i, u8p, vp, sz,
+                                    vp]
+    lib.attn_decode_cap.restype = i
     lib.attn_decode_check.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, f, u8p, vp, sz]
     lib.attn_decode_check.restype = i
     lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i]
@@ -76,6 +83,9 @@ def load() -> ctypes.CDLL:
         fn.restype = i
         fn = getattr(lib, f"attn_decode_{w}_sas")
         fn.argtypes = [vp, vp, vp, vp, vp, f32p, f32p, i, i, i, i, i, f, i, u8p, vp, sz, vp]
+        fn.restype = i
+        fn = getattr(lib, f"attn_decode_{w}_cap")
+        fn.argtypes = [vp, vp, vp, vp, vp, f32p, f32p, i, i, i, i, i, i, f, i, u8p, vp, sz, vp]
         fn.restype = i
         fn = getattr(lib, f"attn_decode_{w}_check")
         fn.argtypes = [vp, vp, vp, vp, vp, f32p, f32p, i, i, i, i, i, f, u8p, vp, sz]
@@ -140,24 +150,32 @@ def attn_prefill(q, k, v, o, lse, causal: bool, tau: float, skip_mask=None,
 
 
 def attn_prefill_chunk(q, k, v, o, lse, causal: bool, tau: float, skip_mask=None,
-                       stream=None) -> None:
+                       stream=None, N=None) -> None:
     """Enqueue chunked prefill: q [B,Hq,Nq,d] are the last Nq of the N
-    positions of k/v [B,Hkv,N,d]; writes o [B,Hq,Nq,d], lse [B,Hq,Nq] and, if
-    given, skip_mask [B,Hq,ceil(Nq/64),ceil(N/64)]."""
+    positions held in k/v [B,Hkv,cap,d] (N = cap unless given: a cache
+    allocated for cap keys whose first N exist); writes o [B,Hq,Nq,d],
+    lse [B,Hq,Nq] and, if given, skip_mask [B,Hq,ceil(Nq/64),ceil(N/64)]."""
     import torch
     B, Hq, Nq, d = q.shape
-    Hkv, N = k.shape[1], k.shape[2]
+    Hkv, cap = k.shape[1], k.shape[2]
+    N = cap if N is None else int(N)
     _check(q, "q", torch.bfloat16, (B, Hq, Nq, d))
-    _check(k, "k", torch.bfloat16, (B, Hkv, N, d))
-    _check(v, "v", torch.bfloat16, (B, Hkv, N, d))
+    _check(k, "k", torch.bfloat16, (B, Hkv, cap, d))
+    _check(v, "v", torch.bfloat16, (B, Hkv, cap, d))
     _check(o, "o", torch.float32, (B, Hq, Nq, d))
     _check(lse, "lse", torch.float32, (B, Hq, Nq))
     if skip_mask is not None:
         _check(skip_mask, "skip_mask", torch.uint8,
                (B, Hq, (Nq + TILE - 1) // TILE, (N + TILE - 1) // TILE))
-    rc = load().attn_prefill_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv,
+    so = load()
+    if N == cap:
+        rc = so.attn_prefill_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv,
                                    Nq, N, d, int(bool(causal)), float(tau), _ptr(skip_mask),
                                    _stream(stream))
+    else:
+        rc = so.attn_prefill_chunk_cap(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq,
+                                       Hkv, Nq, N, cap, d, int(bool(causal)), float(tau),
+                                       _ptr(skip_mask), _stream(stream))
     _raise(rc)
 
 
@@ -175,15 +193,18 @@ def attn_decode(q, k, v, o, lse, tau: float, workspace, skip_mask=None,
 
 
 def attn_decode_sas(q, k, v, o, lse, tau: float, degree: int, workspace, skip_mask=None,
-                    stream=None) -> None:
+                    stream=None, L=None) -> None:
     """attn_decode with the SAS exponential of polynomial degree 2 or 3
-    (0: exact exponentials, i.e. attn_decode)."""
+    (0: exact exponentials, i.e. attn_decode). k/v may be a cache allocated
+    for cap = k.shape[2] keys of which the first ``L`` are attended
+    (attn_decode_cap); L defaults to cap."""
     import torch
     B, Hq, d = q.shape
-    Hkv, L = k.shape[1], k.shape[2]
+    Hkv, cap = k.shape[1], k.shape[2]
+    L = cap if L is None else int(L)
     _check(q, "q", torch.bfloat16, (B, Hq, d))
-    _check(k, "k", torch.bfloat16, (B, Hkv, L, d))
-    _check(v, "v", torch.bfloat16, (B, Hkv, L, d))
+    _check(k, "k", torch.bfloat16, (B, Hkv, cap, d))
+    _check(v, "v", torch.bfloat16, (B, Hkv, cap, d))
     _check(o, "o", torch.float32, (B, Hq, d))
     _check(lse, "lse", torch.float32, (B, Hq))
     if skip_mask is not None:
@@ -191,8 +212,14 @@ def attn_decode_sas(q, k, v, o, lse, tau: float, degree: int, workspace, skip_ma
     if workspace.device.type != "cuda" or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
     nbytes = workspace.numel() * workspace.element_size()
-    rc = load().attn_decode_sas(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv,
+    so = load()
+    if L == cap:
+        rc = so.attn_decode_sas(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv,
                                 L, d, float(tau), int(degree), _ptr(skip_mask),
+                                _ptr(workspace), nbytes, _stream(stream))
+    else:
+        rc = so.attn_decode_cap(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv,
+                                L, cap, d, float(tau), int(degree), _ptr(skip_mask),
                                 _ptr(workspace), nbytes, _stream(stream))
     _raise(rc)
 
@@ -238,9 +265,9 @@ def _quantize(bits, k, v, cache, stream, key_range):
 def _decode_cache(bits, q, cache, L, o, lse, tau, workspace, skip_mask, stream, sas=0):
     import torch
     B, Hq, d = q.shape
-    Hkv = cache["kp"].shape[1]
+    Hkv, cap = cache["kp"].shape[1], cache["kp"].shape[2]   # arrays sized for cap keys
     _check(q, "q", torch.bfloat16, (B, Hq, d))
-    _check_cache(bits, cache, B, Hkv, L, d)
+    _check_cache(bits, cache, B, Hkv, cap, d)
     _check(o, "o", torch.float32, (B, Hq, d))
     _check(lse, "lse", torch.float32, (B, Hq))
     if skip_mask is not None:
@@ -248,13 +275,18 @@ def _decode_cache(bits, q, cache, L, o, lse, tau, workspace, skip_mask, stream, 
     if workspace.device.type != "cuda" or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
     nbytes = workspace.numel() * workspace.element_size()
-    args = [_ptr(q), _ptr(cache["kq"]), _ptr(cache["kp"]), _ptr(cache["vq"]),
-            _ptr(cache["vp"]), _ptr(o), _ptr(lse), B, Hq, Hkv, L, d, float(tau)]
+    ptrs = [_ptr(q), _ptr(cache["kq"]), _ptr(cache["kp"]), _ptr(cache["vq"]),
+            _ptr(cache["vp"]), _ptr(o), _ptr(lse)]
     tail = [_ptr(skip_mask), _ptr(workspace), nbytes, _stream(stream)]
-    if sas:
-        rc = getattr(load(), f"attn_decode_q{bits}_sas")(*args, int(sas), *tail)
+    so = load()
+    if L != cap:
+        rc = getattr(so, f"attn_decode_q{bits}_cap")(*ptrs, B, Hq, Hkv, int(L), cap, d,
+                                                      float(tau), int(sas), *tail)
+    elif sas:
+        rc = getattr(so, f"attn_decode_q{bits}_sas")(*ptrs, B, Hq, Hkv, int(L), d, float(tau),
+                                                      int(sas), *tail)
     else:
-        rc = getattr(load(), f"attn_decode_q{bits}")(*args, *tail)
+        rc = getattr(so, f"attn_decode_q{bits}")(*ptrs, B, Hq, Hkv, int(L), d, float(tau), *tail)
     _raise(rc)
 
 
@@ -274,7 +306,9 @@ def attn_kv_quantize_q2(k, v, cache, stream=None, key_range=None) -> None:
 def attn_decode_q4(q, cache, L: int, o, lse, tau: float, workspace, skip_mask=None,
                    stream=None) -> None:
     """Enqueue split-K decode over a 4-bit cache (dict as for
-    attn_kv_quantize_q4, holding L keys); other arguments as attn_decode."""
+    attn_kv_quantize_q4) of the first L keys; arrays sized for more keys
+    than L (an appended cache) go through attn_decode_q4_cap. Other
+    arguments as attn_decode."""
     _decode_cache(4, q, cache, L, o, lse, tau, workspace, skip_mask, stream)
 
 
@@ -367,29 +401,31 @@ def prefill(q, k, v, causal: bool, tau: float = math.inf, want_mask: bool = Fals
 
 
 def prefill_chunk(q, k, v, causal: bool, tau: float = math.inf, want_mask: bool = False,
-                  stream=None):
-    """Allocate outputs with torch and call attn_prefill_chunk. Returns (o, lse, mask)."""
+                  stream=None, N=None):
+    """Allocate outputs with torch and call attn_prefill_chunk (k/v may be a
+    cache allocated for more than the N keys that exist). Returns (o, lse, mask)."""
     import torch
     B, Hq, Nq, d = q.shape
-    N = k.shape[2]
+    N = k.shape[2] if N is None else int(N)
     o = torch.empty((B, Hq, Nq, d), dtype=torch.float32, device=q.device)
     lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
     mask = None
     if want_mask:
         mask = torch.empty((B, Hq, (Nq + TILE - 1) // TILE, (N + TILE - 1) // TILE),
                            dtype=torch.uint8, device=q.device)
-    attn_prefill_chunk(q, k, v, o, lse, causal, tau, mask, stream)
+    attn_prefill_chunk(q, k, v, o, lse, causal, tau, mask, stream, N=N)
     return o, lse, mask
 
 
 def decode(q, k, v, tau: float = math.inf, want_mask: bool = False, workspace=None,
-           stream=None, sas: int = 0):
+           stream=None, sas: int = 0, L=None):
     """Allocate outputs (and the workspace if not given) and call attn_decode
-    (attn_decode_sas with polynomial degree ``sas`` if nonzero). Returns
+    (attn_decode_sas with polynomial degree ``sas`` if nonzero; over the
+    first ``L`` keys of a larger cache, attn_decode_cap). Returns
     (o, lse, mask)."""
     import torch
     B, Hq, d = q.shape
-    L = k.shape[2]
+    L = k.shape[2] if L is None else int(L)
     o = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     mask = None
@@ -399,5 +435,5 @@ def decode(q, k, v, tau: float = math.inf, want_mask: bool = False, workspace=No
     if workspace is None:
         nbytes = max(16, attn_decode_workspace_bytes(B, Hq, L, d))
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    attn_decode_sas(q, k, v, o, lse, tau, sas, workspace, mask, stream)
+    attn_decode_sas(q, k, v, o, lse, tau, sas, workspace, mask, stream, L=L)
     return o, lse, mask

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ ws_o,
     float* __restrict__ ws_lse, uint8_t* __restrict__ mask, int Hq, int Hkv,
-    int L, int nsplit, float tau_raw, float c, int nwork) {
+    int L, int cap, int nhs, int nsplit, float tau_raw, float c, int nwork) {
   constexpr int KS = D / 32;        // k-steps over d (32 each) for S^T
   constexpr int DB = D / 16;        // 16-row d blocks of O^T
   constexpr int VB = (2 * D) / 64;  // 4-key x 8-d V blocks per lane
@@ -95,15 +95,17 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   const int work = blockIdx.x * 4 + wave;
   if (work >= nwork) return;  // whole wave leaves; the kernel has no barrier
   const int sp = work % nsplit;
-  const int bg = work / nsplit;
+  const int hs = (work / nsplit) % nhs;  // which 16 query heads of the group
+  const int bg = work / nsplit / nhs;
   const int g = bg % Hkv;
   const int b = bg / Hkv;
   const int G = Hq / Hkv;
+  const int hoff = 16 * hs;  // first head of this wave's slice, within the group
   const int hl = lane & 15;   // head slot
   const int grp = lane >> 4;  // lane group 0..3
   char* vs_ = smem[wave];
 
-  const size_t kv_off = (size_t)(b * Hkv + g) * L * D;
+  const size_t kv_off = (size_t)(b * Hkv + g) * cap * D;  // heads are cap rows apart
   const int head_bytes = L * D * 2;
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(k + kv_off), (short)0, head_bytes, kBufferCfg);
@@ -113,8 +115,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   const int key_begin = sp * kSplit;
   const int key_end = min(L, key_begin + kSplit);
   const int ntile = (key_end - key_begin + kTile - 1) / kTile;
-  const bool head_ok = hl < G;
-  const size_t bh = (size_t)b * Hq + g * G + hl;
+  const bool head_ok = hoff + hl < G;
+  const size_t bh = (size_t)b * Hq + g * G + hoff + hl;
 
   // q^T fragments: B[k = d][n = head].
   bf16x8 qf[KS];
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     any_cur = any_nx;
   }
 
-  if (mask != nullptr && lane < G) {  // lane < G: grp 0, head hl = lane
+  if (mask != nullptr && lane < 16 && head_ok) {  // grp 0: head slot hl = lane
     uint8_t* mrow = mask + bh * ntile_all + key_begin / kTile;
     for (int t = 0; t < ntile; ++t) mrow[t] = (uint8_t)((skipped >> t) & 1u);
   }
@@ -405,7 +407,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
 
 template <int D>
 static int launch_d(const DecodeArgs& a) {
-  const long long nwork = (long long)a.B * a.Hkv * a.nsplit;
+  // one wave per (sequence, KV head, slice of up to 16 query heads, split)
+  const int nhs = (a.Hq / a.Hkv + 15) / 16;
+  const long long nwork = (long long)a.B * a.Hkv * nhs * a.nsplit;
   const long long nbh = (long long)a.B * a.Hq;
   if (nwork > 0x7fffffffLL || nbh > 0x7fffffffLL) return -1;
   const unsigned g1 = (unsigned)((nwork + 3) / 4);
@@ -414,7 +418,7 @@ static int launch_d(const DecodeArgs& a) {
               : a.sas == 3 ? decode_split_kernel<D, 3> : decode_split_kernel<D, 0>;
   hipLaunchKernelGGL(kern, dim3(g1), dim3(256), 0, (hipStream_t)a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     a.ws_o, a.ws_lse, a.mask, a.Hq, a.Hkv, a.L, a.nsplit, a.tau_raw,
+                     a.ws_o, a.ws_lse, a.mask, a.Hq, a.Hkv, a.L, a.cap, nhs, a.nsplit, a.tau_raw,
                      a.c, (int)nwork);
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(g2), dim3(256), 0, (hipStream_t)a.stream,
                      a.ws_o, a.ws_lse, a.o, a.lse, (int)nbh, a.nsplit);

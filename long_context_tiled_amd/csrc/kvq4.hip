@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kq,
     const uint32_t* __restrict__ kp, const uint8_t* __restrict__ vq,
     const uint32_t* __restrict__ vp, float* __restrict__ ws_o, float* __restrict__ ws_lse,
-    uint8_t* __restrict__ mask, int Hq, int Hkv, int L, int nsplit, float tau_raw, float c,
+    uint8_t* __restrict__ mask, int Hq, int Hkv, int L, int cap, int nhs, int nsplit, float tau_raw, float c,
     int nwork) {
   constexpr int KS = D / 32;  // QK k-steps; words per lane per K row
   constexpr int DB = D / 16;  // 16-channel blocks of O^T and of V code rows
@@ -227,30 +227,33 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
   const int work = blockIdx.x * 4 + wave;
   if (work >= nwork) return;  // whole wave leaves; the kernel has no barrier
   const int sp = work % nsplit;
-  const int bg = work / nsplit;
+  const int hs = (work / nsplit) % nhs;  // which 16 query heads of the group
+  const int bg = work / nsplit / nhs;
   const int g = bg % Hkv;
   const int b = bg / Hkv;
   const int G = Hq / Hkv;
+  const int hoff = 16 * hs;  // first head of this wave's slice, within the group
   const int hl = lane & 15;
   const int grp = lane >> 4;
   const int T = (L + kTile - 1) / kTile;
+  const int Tc = (cap + kTile - 1) / kTile;  // tiles the arrays are sized for
 
   const size_t head = (size_t)(b * Hkv + g);
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(kq + head * L * RB), (short)0, L * RB, kCfg);
+      (void*)(kq + head * cap * RB), (short)0, L * RB, kCfg);
   const __amdgpu_buffer_rsrc_t kprs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(kp + head * L), (short)0, L * 4, kCfg);
+      (void*)(kp + head * cap), (short)0, L * 4, kCfg);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(vq + head * T * D * 32), (short)0, T * D * 32, kCfg);
+      (void*)(vq + head * Tc * D * 32), (short)0, T * D * 32, kCfg);
   const __amdgpu_buffer_rsrc_t vprs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(vp + head * T * D), (short)0, T * D * 4, kCfg);
+      (void*)(vp + head * Tc * D), (short)0, T * D * 4, kCfg);
 
   const int key_begin = sp * kSplit;
   const int key_end = min(L, key_begin + kSplit);
   const int ntile = (key_end - key_begin + kTile - 1) / kTile;
   const int tile_begin = key_begin / kTile;
-  const bool head_ok = hl < G;
-  const size_t bh = (size_t)b * Hq + g * G + hl;
+  const bool head_ok = hoff + hl < G;
+  const size_t bh = (size_t)b * Hq + g * G + hoff + hl;
 
   // q^T fragments (B operand, n = head): lane group grp holds d range
   // [grp D/4, (grp + 1) D/4), k-step ks its elements 8 ks .. 8 ks + 7.
@@ -511,17 +514,17 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
     step(t + 1, ka, vb, va);
   }
 
-  if (mask != nullptr && lane < G) {  // lane < G: grp 0, head hl = lane
+  if (mask != nullptr && lane < 16 && head_ok) {  // grp 0: head slot hl = lane
     uint8_t* mrow = mask + bh * T + tile_begin;
     for (int t = 0; t < ntile; ++t) mrow[t] = (uint8_t)((skipped >> t) & 1u);
   }
 
-  const size_t bh0 = (size_t)b * Hq + g * G;
+  const size_t bh0 = (size_t)b * Hq + g * G + hoff;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float mr = of_head(m_ref, r);
     const int h = 4 * grp + r;
-    if (h < G) {
+    if (hoff + h < G) {
       const float ir = 1.f / lr[r];
       float* dst = ws_o + ((bh0 + h) * nsplit + sp) * D + hl;
 #pragma unroll
@@ -551,14 +554,16 @@ int launch_q_d(const QuantArgs& a) {
 
 template <int D>
 int launch_dq_d(const DecodeQ4Args& a) {
-  const long long nwork = (long long)a.B * a.Hkv * a.nsplit;
+  // one wave per (sequence, KV head, slice of up to 16 query heads, split)
+  const int nhs = (a.Hq / a.Hkv + 15) / 16;
+  const long long nwork = (long long)a.B * a.Hkv * nhs * a.nsplit;
   if (nwork > 0x7fffffffLL) return -1;
   const unsigned g1 = (unsigned)((nwork + 3) / 4);
   auto kern = a.sas == 2 ? decode_q4_split_kernel<D, 2>
               : a.sas == 3 ? decode_q4_split_kernel<D, 3> : decode_q4_split_kernel<D, 0>;
   hipLaunchKernelGGL(kern, dim3(g1), dim3(256), 0, (hipStream_t)a.stream,
                      (const uint16_t*)a.q, a.kq, a.kp, a.vq, a.vp, a.ws_o, a.ws_lse, a.mask, a.Hq,
-                     a.Hkv, a.L, a.nsplit, a.tau_raw, a.c, (int)nwork);
+                     a.Hkv, a.L, a.cap, nhs, a.nsplit, a.tau_raw, a.c, (int)nwork);
   return launch_decode_merge(a.ws_o, a.ws_lse, a.o, a.lse, a.B * a.Hq, a.d, a.nsplit, a.stream);
 }
 

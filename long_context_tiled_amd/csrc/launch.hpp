@@ -16,6 +16,7 @@ struct PrefillArgs {
   int B, Hq, Hkv, N, d, causal;
   int Nq;         // queries: key positions N - Nq .. N - 1 (Nq == N: self-attention)
   int q0t;        // (N - Nq) / 64
+  int cap;        // rows allocated per K/V head (>= N; N for a cache of exactly N keys)
   float tau_raw;  // tau * sqrt(d): threshold in raw q.k units (+inf = dense)
   float c;        // log2(e) / sqrt(d)
   void* stream;
@@ -31,6 +32,7 @@ struct DecodeArgs {
   float* ws_o;    // [B, Hq, nsplit, d] per-split normalised outputs
   float* ws_lse;  // [B, Hq, nsplit] per-split natural-log LSE
   int B, Hq, Hkv, L, d, nsplit;
+  int cap;        // rows allocated per K/V head (>= L)
   float tau_raw;
   float c;
   void* stream;
@@ -61,6 +63,7 @@ struct DecodeQ4Args {
   float* ws_o;
   float* ws_lse;
   int B, Hq, Hkv, L, d, nsplit;
+  int cap;        // keys the cache arrays are sized for (>= L)
   float tau_raw;
   float c;
   void* stream;

@@ -148,7 +148,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ o,
     float* __restrict__ lse, uint8_t* __restrict__ mask, int Hq, int Hkv,
-    int Nq_arg, int N, int q0t_arg, float tau_raw, float c, int nqg, int ny) {
+    int Nq_arg, int N, int q0t_arg, int cap_arg, float tau_raw, float c, int nqg, int ny) {
   // Nq queries (the chunk) at key positions 64 q0t .. 64 q0t + Nq - 1 of N
   // keys: query tile qb of the chunk is tile qb + q0t of the key axis. The
   // whole-sequence instance (CHUNK false) has Nq = N and q0t = 0 as
@@ -156,6 +156,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
   // the same values passed at run time).
   const int Nq = CHUNK ? Nq_arg : N;
   const int q0t = CHUNK ? q0t_arg : 0;
+  const int cap = CHUNK ? cap_arg : N;  // rows allocated per K/V head
   constexpr int QPW = 4 / HPW;   // query tiles per workgroup
   constexpr int MB = D / 32;     // 32-row d blocks of O^T
   using T = PrefillTile<D>;
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
   const int nkb_w = wave_valid ? (CAUSAL ? qbg + 1 : nkb) : 0;
 
   const int head_bytes = N * D * 2;
-  const size_t kv_off = (size_t)(b * Hkv + g) * N * D;
+  const size_t kv_off = (size_t)(b * Hkv + g) * cap * D;
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(k + kv_off), (short)0, head_bytes, kBufferCfg);
   const __amdgpu_buffer_rsrc_t vrs =
@@ -375,7 +376,7 @@ static int launch_one(const PrefillArgs& a) {
   if (blocks > 0x7fffffffLL) return -1;
   hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, HPW, kStages, CHUNK>), dim3((unsigned)blocks), dim3(256),
                      0, (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                     (const uint16_t*)a.v, a.o, a.lse, a.mask, a.Hq, a.Hkv, a.Nq, a.N, a.q0t,
+                     (const uint16_t*)a.v, a.o, a.lse, a.mask, a.Hq, a.Hkv, a.Nq, a.N, a.q0t, a.cap,
                      a.tau_raw, a.c, nqg, ny);
   return 0;
 }
@@ -390,7 +391,7 @@ static int launch_g(const PrefillArgs& a) {
 
 template <int D, bool CAUSAL>
 static int launch_h(const PrefillArgs& a) {
-  if (a.Nq != a.N || a.q0t != 0) return launch_g<D, CAUSAL, true>(a);
+  if (a.Nq != a.N || a.q0t != 0 || a.cap != a.N) return launch_g<D, CAUSAL, true>(a);
   return launch_g<D, CAUSAL, false>(a);
 }
 

@@ -46,7 +46,7 @@ def _pcheck(**kw):
     ({"B": -1}, 1), ({"N": -5}, 1), ({"Hq": 0}, 1), ({"Hkv": 0}, 1), ({"Hq": 7, "Hkv": 2}, 1),
     ({"causal": 2}, 1), ({"tau": math.nan}, 1), ({"tau": -1.0}, 1), ({"tau": -INF}, 1),
     ({"q": P + 8}, 1), ({"o": P + 4}, 1), ({"B": 1 << 20, "N": 1 << 20}, 1),
-    ({"d": 96}, 2), ({"d": 256}, 2), ({"d": 0}, 2),
+    ({"d": 96}, 1), ({"d": 256}, 1), ({"d": 0}, 1), ({"d": 32}, 1),
     # one head of K/V must stay below 2^31 - 2^16 bytes (32-bit buffer offsets)
     ({"N": HEAD_LIMIT // 256}, 0), ({"N": HEAD_LIMIT // 256 + 1}, 2),
     ({"N": HEAD_LIMIT // 128 + 1, "d": 64}, 2),
@@ -62,7 +62,7 @@ def test_prefill_entry_rejects_before_any_launch():
     rc = so.attn_prefill(None, P, P, P, P, 1, 8, 2, 1024, 128, 1, 4.0, None, None)
     assert rc == lib.EINVAL and "NULL" in lib.attn_last_error()
     rc = so.attn_prefill(P, P, P, P, P, 1, 8, 2, 1024, 96, 1, 4.0, None, None)
-    assert rc == lib.EUNSUPPORTED
+    assert rc == lib.EINVAL and "d must be" in lib.attn_last_error()
 
 
 def _dcheck(**kw):
@@ -78,10 +78,11 @@ def _dcheck(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     ({}, 0), ({"tau": INF}, 0), ({"L": 1}, 0), ({"L": 4097}, 0), ({"d": 64}, 0),
-    ({"Hq": 16, "Hkv": 1}, 0), ({"B": 0, "ws": None, "wsb": 0}, 0),
+    ({"Hq": 16, "Hkv": 1}, 0), ({"Hq": 17, "Hkv": 1}, 0), ({"Hq": 64, "Hkv": 1}, 0),
+    ({"B": 0, "ws": None, "wsb": 0}, 0),
     ({"q": None}, 1), ({"Hq": 65}, 1), ({"tau": math.nan}, 1), ({"tau": -0.5}, 1),
     ({"L": -1}, 1), ({"ws": P + 4}, 1),
-    ({"Hq": 17, "Hkv": 1}, 2), ({"d": 80}, 2),
+    ({"d": 80}, 1),
     ({"L": HEAD_LIMIT // 256}, 0), ({"L": HEAD_LIMIT // 256 + 1}, 2),
     ({"L": HEAD_LIMIT // 128 + 1, "d": 64}, 2),
     ({"ws": None}, 3), ({"wsb": 100}, 3),
@@ -123,7 +124,7 @@ def _q4check(**kw):
     ({}, 0), ({"tau": INF}, 0), ({"L": 70, "d": 64}, 0), ({"B": 0, "ws": None, "wsb": 0}, 0),
     ({"kq": None}, 1), ({"kp": None}, 1), ({"vq": None}, 1), ({"vp": None}, 1),
     ({"kp": P + 4}, 1), ({"vq": P + 8}, 1), ({"q": None}, 1), ({"tau": -1.0}, 1),
-    ({"d": 96}, 2), ({"Hq": 34, "Hkv": 2}, 2), ({"L": HEAD_LIMIT // 256 + 1}, 2),
+    ({"d": 96}, 1), ({"Hq": 34, "Hkv": 2}, 0), ({"L": HEAD_LIMIT // 256 + 1}, 2),
     ({"wsb": 64}, 3),
 ])
 def test_decode_q4_validation(kw, code):
@@ -137,7 +138,7 @@ def test_quantise_q4_rejects_before_any_launch():
     assert so.attn_kv_quantize_q4(None, P, P, P, P, P, 1, 8, 4096, 128, None) == lib.EINVAL
     assert so.attn_kv_quantize_q4(P, P, P, P + 4, P, P, 1, 8, 4096, 128, None) == lib.EINVAL
     assert so.attn_kv_quantize_q4(P, P, P, P, P, P, 1, 0, 4096, 128, None) == lib.EINVAL
-    assert so.attn_kv_quantize_q4(P, P, P, P, P, P, 1, 8, 4096, 80, None) == lib.EUNSUPPORTED
+    assert so.attn_kv_quantize_q4(P, P, P, P, P, P, 1, 8, 4096, 80, None) == lib.EINVAL
     assert so.attn_kv_quantize_q4(P, P, P, P, P, P, 1, 1, HEAD_LIMIT // 256 + 1, 128,
                                   None) == lib.EUNSUPPORTED
 
@@ -160,7 +161,7 @@ def _ccheck(**kw):
     ({}, 0), ({"Nq": 4096}, 0), ({"Nq": 0}, 0), ({"Nq": 64, "N": 4160}, 0),
     ({"Nq": 100, "N": 164}, 0), ({"Nq": 100, "N": 4096, "causal": 0}, 0),
     ({"Nq": 4097}, 1), ({"Nq": -1}, 1), ({"q": None}, 1), ({"causal": 3}, 1),
-    ({"Nq": 100, "N": 4096}, 2), ({"Nq": 1, "N": 4096}, 2), ({"d": 96}, 2),
+    ({"Nq": 100, "N": 4096}, 2), ({"Nq": 1, "N": 4096}, 2), ({"d": 96}, 1),
 ])
 def test_prefill_chunk_validation(kw, code):
     assert _ccheck(**kw) == code
@@ -174,3 +175,35 @@ def test_quantise_q4_range_rejects_before_any_launch():
     assert r(P, P, P, P, P, P, 1, 8, 4096, 128, 128, 64, None) == lib.EINVAL
     assert r(P, P, P, P, P, P, 1, 8, 4096, 128, 0, 4097, None) == lib.EINVAL
     assert r(P, P, P, P, P, P, 1, 8, 4096, 128, -64, 64, None) == lib.EINVAL
+
+
+def test_capacity_entry_points_reject_before_any_launch():
+    # a cache allocated for `cap` keys of which the first L (N) are used:
+    # cap below the attended length is EINVAL; every case here returns before
+    # any HIP call
+    so = lib.load()
+    ws = lib.attn_decode_workspace_bytes(2, 8, 5000, 128)
+    assert so.attn_decode_cap(P, P, P, P, P, 2, 8, 2, 5000, 4999, 128, 4.0, 0, None, P, ws,
+                              None) == lib.EINVAL
+    assert "cap" in lib.attn_last_error()
+    assert so.attn_decode_cap(P, P, P, P, P, 2, 8, 2, 5000, 8192, 128, 4.0, 1, None, P, ws,
+                              None) == lib.EINVAL            # degree 1
+    assert so.attn_decode_cap(P, P, P, P, P, 2, 8, 2, 5000, 8192, 128, 4.0, 0, None, P, ws - 4,
+                              None) == lib.EWORKSPACE
+    assert so.attn_decode_cap(P, P, P, P, P, 0, 8, 2, 5000, 8192, 128, 4.0, 0, None, None, 0,
+                              None) == lib.OK                # empty work
+    for fn in (so.attn_decode_q4_cap, so.attn_decode_q2_cap):
+        assert fn(P, P, P, P, P, P, P, 2, 8, 2, 5000, 4096, 128, 4.0, 0, None, P, ws,
+                  None) == lib.EINVAL
+        assert fn(P, P, None, P, P, P, P, 2, 8, 2, 5000, 8192, 128, 4.0, 0, None, P, ws,
+                  None) == lib.EINVAL
+        assert fn(P, P, P, P, P, P, P, 2, 8, 2, 5000, 8192, 96, 4.0, 0, None, P, ws,
+                  None) == lib.EINVAL
+        assert fn(P, P, P, P, P, P, P, 0, 8, 2, 5000, 8192, 128, 4.0, 0, None, P, ws,
+                  None) == lib.OK
+    r = so.attn_prefill_chunk_cap
+    assert r(P, P, P, P, P, 1, 8, 2, 512, 4096, 4095, 128, 1, 4.0, None, None) == lib.EINVAL
+    assert r(P, P, P, P, P, 1, 8, 2, 100, 4096, 8192, 128, 1, 4.0, None, None) == lib.EUNSUPPORTED
+    assert r(P, P, P, P, P, 0, 8, 2, 512, 4096, 8192, 128, 1, 4.0, None, None) == lib.OK
+    assert r(P, P, P, P, P, 1 << 12, 8, 2, 512, 4096, 1 << 28, 128, 1, 4.0, None,
+             None) == lib.EINVAL                             # cache beyond 2^40 elements

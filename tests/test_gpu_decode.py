@@ -62,14 +62,15 @@ def test_decode_edge_lengths(L):
         assert rep.ok(), str(rep)
 
 
-def test_decode_rejects_bad_workspace_and_group():
+def test_decode_rejects_bad_workspace_and_head_dim():
     import torch
     import long_context_tiled_amd as lib
-    q = torch.zeros((1, 32, 128), dtype=torch.bfloat16, device="cuda")
-    k = torch.zeros((1, 1, 128, 128), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((1, 32, 96), dtype=torch.bfloat16, device="cuda")
+    k96 = torch.zeros((1, 1, 128, 96), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(lib.SkipAttnError) as e:
-        lib.decode(q, k, k, 1.0)
-    assert e.value.code == lib.EUNSUPPORTED
+        lib.decode(q, k96, k96, 1.0)
+    assert e.value.code == lib.EINVAL
+    k = torch.zeros((1, 1, 128, 128), dtype=torch.bfloat16, device="cuda")
     q = torch.zeros((1, 8, 128), dtype=torch.bfloat16, device="cuda")
     o = torch.zeros((1, 8, 128), dtype=torch.float32, device="cuda")
     lse = torch.zeros((1, 8), dtype=torch.float32, device="cuda")
