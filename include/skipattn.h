@@ -362,6 +362,27 @@ int attn_decode_q2_cap(const void* q, const uint8_t* kq, const uint32_t* kp,
                        int d, float tau, int degree, uint8_t* skip_mask,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * attn_decode_noalloc - attn_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments, kernels, results and errors, with
+ * no workspace argument. The per-split partials go to a device scratch array
+ * inside the library, SKIPATTN_DECODE_SCRATCH_BYTES (32 MiB) on each GPU it
+ * runs on, held until the process ends; a call whose partials would need
+ * more (attn_decode_workspace_bytes(B, Hq, L, d) > 32 MiB; decode at B = 16,
+ * Hq = 64, L = 131072, d = 128 needs 16.9 MB) returns SKIPATTN_EWORKSPACE
+ * before any launch. The call allocates and frees nothing. Every call on a
+ * GPU shares that GPU's scratch: calls that may overlap on one GPU (other
+ * streams, other threads) race and must be ordered by the caller. No
+ * scratch content carries over between calls (each call writes every
+ * partial it reads). The first call on a device looks up the scratch's
+ * address there (SKIPATTN_EHIP if that fails).
+ */
+#define SKIPATTN_DECODE_SCRATCH_BYTES (32u << 20)
+int attn_decode_noalloc(const void* q, const void* k, const void* v, float* o,
+                        float* lse, int B, int Hq, int Hkv, int L, int d,
+                        float tau, uint8_t* skip_mask, void* stream);
+
 /* Text for the last nonzero return on this thread ("" if none). */
 const char* attn_last_error(void);
 

@@ -27,7 +27,7 @@ EXPORTS = ("attn_prefill", "attn_decode", "attn_decode_workspace_bytes",
            "attn_kv_quantize_q2", "attn_kv_quantize_q2_range", "attn_decode_q2",
            "attn_decode_q2_check", "attn_decode_sas", "attn_decode_q4_sas",
            "attn_decode_q2_sas", "attn_prefill_chunk_cap", "attn_decode_cap",
-           "attn_decode_q4_cap", "attn_decode_q2_cap")
+           "attn_decode_q4_cap", "attn_decode_q2_cap", "attn_decode_noalloc")
 
 _lib = None
 
@@ -67,6 +67,8 @@ def load() -> ctypes.CDLL:
     lib.attn_decode_cap.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, i, f, i, u8p, vp, sz,
                                     vp]
     lib.attn_decode_cap.restype = i
+    lib.attn_decode_noalloc.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, f, u8p, vp]
+    lib.attn_decode_noalloc.restype = i
     lib.attn_decode_check.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, f, u8p, vp, sz]
     lib.attn_decode_check.restype = i
     lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i]
@@ -221,6 +223,27 @@ def attn_decode_sas(q, k, v, o, lse, tau: float, degree: int, workspace, skip_ma
         rc = so.attn_decode_cap(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv,
                                 L, cap, d, float(tau), int(degree), _ptr(skip_mask),
                                 _ptr(workspace), nbytes, _stream(stream))
+    _raise(rc)
+
+
+DECODE_SCRATCH_BYTES = 32 << 20
+
+
+def attn_decode_noalloc(q, k, v, o, lse, tau: float, skip_mask=None, stream=None) -> None:
+    """attn_decode without a workspace: the per-split partials go to the
+    library's 32 MiB device scratch (calls that overlap on one GPU race)."""
+    import torch
+    B, Hq, d = q.shape
+    Hkv, L = k.shape[1], k.shape[2]
+    _check(q, "q", torch.bfloat16, (B, Hq, d))
+    _check(k, "k", torch.bfloat16, (B, Hkv, L, d))
+    _check(v, "v", torch.bfloat16, (B, Hkv, L, d))
+    _check(o, "o", torch.float32, (B, Hq, d))
+    _check(lse, "lse", torch.float32, (B, Hq))
+    if skip_mask is not None:
+        _check(skip_mask, "skip_mask", torch.uint8, (B, Hq, (L + TILE - 1) // TILE))
+    rc = load().attn_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv,
+                                    L, d, float(tau), _ptr(skip_mask), _stream(stream))
     _raise(rc)
 
 

@@ -295,6 +295,28 @@ int attn_decode_cap(const void* q, const void* k, const void* v, float* o, float
                        workspace_bytes, stream);
 }
 
+int attn_decode_noalloc(const void* q, const void* k, const void* v, float* o, float* lse,
+                        int B, int Hq, int Hkv, int L, int d, float tau, uint8_t* skip_mask,
+                        void* stream) {
+  // attn_decode's checks, with the device scratch in place of the workspace
+  // (a non-null, aligned stand-in address: the checks never dereference it)
+  const void* stand_in = reinterpret_cast<const void*>(uintptr_t(256));
+  const int e = decode_check(q, k, v, o, lse, B, Hq, Hkv, L, L, d, tau, stand_in,
+                             skipattn::kDecodeScratchBytes);
+  if (e == SKIPATTN_EWORKSPACE)
+    return fail(SKIPATTN_EWORKSPACE,
+                "attn_decode_noalloc: the per-split partials need %zu bytes, more than the "
+                "%zu-byte device scratch (attn_decode takes a workspace of any size)",
+                attn_decode_workspace_bytes(B, Hq, L, d), skipattn::kDecodeScratchBytes);
+  if (e) return e;
+  if (B == 0 || L == 0) return SKIPATTN_OK;
+  void* ws = nullptr;
+  if (skipattn::decode_scratch(&ws) != 0)
+    return fail(SKIPATTN_EHIP, "attn_decode_noalloc: no device address for the scratch");
+  return decode_launch(q, k, v, o, lse, B, Hq, Hkv, L, L, d, tau, 0, skip_mask, ws,
+                       skipattn::kDecodeScratchBytes, stream);
+}
+
 int attn_decode_q4_check(const void* q, const uint8_t* kq, const uint32_t* kp,
                          const uint8_t* vq, const uint32_t* vp, const float* o,
                          const float* lse, int B, int Hq, int Hkv, int L, int d, float tau,

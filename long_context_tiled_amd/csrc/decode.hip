@@ -28,6 +28,8 @@
 //
 // Merge kernel: one wave per (b, query head): LSE = log sum_s e^lse_s and
 // O = sum_s e^(lse_s - LSE) O_s.
+#include <atomic>
+
 #include "common.hpp"
 #include "sas.hpp"
 #include "launch.hpp"
@@ -427,6 +429,32 @@ static int launch_d(const DecodeArgs& a) {
 
 int launch_decode(const DecodeArgs& a) {
   return a.d == 128 ? launch_d<128>(a) : launch_d<64>(a);
+}
+
+// Device scratch for callers that cannot allocate (attn_decode_noalloc):
+// the per-split partials live in this file-scope array instead of a
+// caller's workspace. Each GPU the library runs on holds its own copy for
+// the life of the process. In host code `scratch` is only a stand-in for
+// the symbol; its device address comes from hipGetSymbolAddress, taken once
+// per device and kept below.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+}  // namespace
+
+int decode_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // with `dev` current: the address of this device's copy of the array
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return -2;
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return 0;
 }
 
 int launch_decode_merge(const float* ws_o, const float* ws_lse, float* o, float* lse, int nbh,

@@ -79,6 +79,11 @@ int launch_decode_q4(const DecodeQ4Args& a);
 // The 2-bit cache (layout in kvq2.hip) takes the same arguments.
 int launch_kv_quantize_q2(const QuantArgs& a);
 int launch_decode_q2(const DecodeQ4Args& a);
+// Bytes of the device-resident decode scratch (decode.hip), and its address
+// on the current device (0 on success; the first call on a device looks it
+// up with that device current).
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+int decode_scratch(void** ptr);
 // The log-sum-exp merge of per-split partials (shared by both decodes).
 int launch_decode_merge(const float* ws_o, const float* ws_lse, float* o, float* lse, int nbh,
                         int d, int nsplit, void* stream);

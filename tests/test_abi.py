@@ -207,3 +207,19 @@ def test_capacity_entry_points_reject_before_any_launch():
     assert r(P, P, P, P, P, 0, 8, 2, 512, 4096, 8192, 128, 1, 4.0, None, None) == lib.OK
     assert r(P, P, P, P, P, 1 << 12, 8, 2, 512, 4096, 1 << 28, 128, 1, 4.0, None,
              None) == lib.EINVAL                             # cache beyond 2^40 elements
+
+
+def test_noalloc_decode_rejects_before_any_launch():
+    # the device scratch holds 32 MiB of per-split partials: a call needing
+    # more is refused before any HIP call, as are invalid arguments
+    so = lib.load()
+    assert lib.attn_decode_workspace_bytes(16, 64, 131072, 128) <= lib.DECODE_SCRATCH_BYTES
+    assert lib.attn_decode_workspace_bytes(32, 64, 131072, 128) > lib.DECODE_SCRATCH_BYTES
+    rc = so.attn_decode_noalloc(P, P, P, P, P, 32, 64, 8, 131072, 128, INF, None, None)
+    assert rc == lib.EWORKSPACE and "scratch" in lib.attn_last_error()
+    assert so.attn_decode_noalloc(P, P, P, P, P, 16, 64, 8, 131072, 96, INF, None,
+                                  None) == lib.EINVAL
+    assert so.attn_decode_noalloc(None, P, P, P, P, 16, 64, 8, 131072, 128, INF, None,
+                                  None) == lib.EINVAL
+    assert so.attn_decode_noalloc(P, P, P, P, P, 0, 64, 8, 131072, 128, INF, None,
+                                  None) == lib.OK
