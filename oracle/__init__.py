@@ -5,8 +5,9 @@ check and by the benchmark's CPU-baseline leg, never by the library's product
 path. It shares no code with the HIP kernels.
 """
 from .attention import (TILE, SPLIT, KEPT, SKIPPED, NOT_VISITED, prefill,
-                        prefill_blocks, decode, decode_head)
+                        prefill_blocks, prefill_decisions, decode, decode_head,
+                        decode_heads)
 from . import kvq2, kvq4, sas
 
 __all__ = ["TILE", "SPLIT", "KEPT", "SKIPPED", "NOT_VISITED", "prefill",
-           "prefill_blocks", "decode", "decode_head", "kvq2", "kvq4", "sas"]
+           "prefill_blocks", "prefill_decisions", "decode", "decode_head", "decode_heads", "kvq2", "kvq4", "sas"]

@@ -85,6 +85,7 @@ def _decide(t: np.ndarray, valid: np.ndarray, visited: np.ndarray, tau: float,
     t        (nb, R, nt) per-row tile maxima, nb independent decision blocks
     valid    (nb, R) rows that take part in the vote
     visited  (nb, nt) tiles each block visits
+    tau      the threshold: a float, or an (nb, 1) array of one per block
     returns decisions (nb, nt) uint8 and margins (nb, nt) float64.
     """
     nb, R, nt = t.shape
@@ -122,15 +123,10 @@ def _softmax_kept(s: np.ndarray, kept: np.ndarray, v: np.ndarray):
     return o, lse
 
 
-def prefill_blocks(qrows: np.ndarray, k: np.ndarray, v: np.ndarray, qb0: int,
-                   causal: bool, tau: float, forced: np.ndarray | None = None):
-    """Oracle for consecutive 64-row query blocks of one (batch, head).
-
-    qrows  (R, d) fp64 rows qb0*64 ... qb0*64 + R - 1 (R <= nb*64; the last
-           block may be partial only if it ends at N)
-    k, v   (N, d) fp64 keys and values of the head's KV group
-    Returns o (R, d), lse (R,), decisions (nb, nt), margins (nb, nt).
-    """
+def _block_scores(qrows: np.ndarray, k: np.ndarray, qb0: int, causal: bool):
+    """Scores of consecutive query rows qb0*64 ... (causal: -inf past the
+    diagonal), the per-row tile maxima grouped into 64-row decision blocks,
+    the rows that vote and the tiles each block visits."""
     R, d = qrows.shape
     N = k.shape[0]
     nt = (N + TILE - 1) // TILE
@@ -153,6 +149,38 @@ def prefill_blocks(qrows: np.ndarray, k: np.ndarray, v: np.ndarray, qb0: int,
         visited = np.arange(nt)[None, :] <= qbs[:, None]
     else:
         visited = np.ones((nb, nt), bool)
+    return s, t, valid, visited
+
+
+def prefill_decisions(qrows: np.ndarray, k: np.ndarray, qb0: int, causal: bool, taus):
+    """The skip decisions alone (no softmax) of consecutive 64-row query
+    blocks of one (batch, head), for each threshold in ``taus``: the scores
+    and tile maxima are formed once and the rule is run per tau.
+    Returns {tau: (decisions (nb, nt), margins (nb, nt))}."""
+    _, t, valid, visited = _block_scores(qrows, k, qb0, causal)
+    taus = list(taus)
+    nb = t.shape[0]
+    # one pass of the rule over the blocks repeated once per tau, each copy
+    # with its own threshold (the copies are independent decision blocks)
+    tau_col = np.repeat(np.asarray(taus, np.float64), nb)[:, None]
+    dec, margin = _decide(np.concatenate([t] * len(taus)), np.concatenate([valid] * len(taus)),
+                          np.concatenate([visited] * len(taus)), tau_col, None)
+    return {tau: (dec[i * nb:(i + 1) * nb], margin[i * nb:(i + 1) * nb])
+            for i, tau in enumerate(taus)}
+
+
+def prefill_blocks(qrows: np.ndarray, k: np.ndarray, v: np.ndarray, qb0: int,
+                   causal: bool, tau: float, forced: np.ndarray | None = None):
+    """Oracle for consecutive 64-row query blocks of one (batch, head).
+
+    qrows  (R, d) fp64 rows qb0*64 ... qb0*64 + R - 1 (R <= nb*64; the last
+           block may be partial only if it ends at N)
+    k, v   (N, d) fp64 keys and values of the head's KV group
+    Returns o (R, d), lse (R,), decisions (nb, nt), margins (nb, nt).
+    """
+    R = qrows.shape[0]
+    N = k.shape[0]
+    s, t, valid, visited = _block_scores(qrows, k, qb0, causal)
     dec, margin = _decide(t, valid, visited, tau, forced)
     keep_tile = dec == KEPT
     kept = np.repeat(np.repeat(keep_tile, TILE, axis=1), TILE, axis=0)
@@ -195,33 +223,53 @@ def prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool,
     return dict(o=o, lse=lse, mask=mask, margin=margin)
 
 
-def decode_head(qvec: np.ndarray, k: np.ndarray, v: np.ndarray, tau: float,
-                split: int = SPLIT, forced: np.ndarray | None = None):
-    """Oracle for one query token against one KV head.
+def decode_heads(qs: np.ndarray, k: np.ndarray, v: np.ndarray, tau: float,
+                 split: int = SPLIT, forced: np.ndarray | None = None):
+    """Oracle for several query heads (one token each) against one KV head.
 
-    qvec (d,), k/v (L, d) fp64. Each split of ``split`` keys (a multiple of
-    64) runs the rule with its own running max. Returns o (d,), lse,
-    decisions (nt,), margins (nt,).
+    qs (n, d), k/v (L, d) fp64. Each split of ``split`` keys (a multiple of
+    64) runs the rule with its own running max, per head. ``forced`` (n, nt)
+    int8, if given, imposes decisions where it is >= 0. Returns o (n, d),
+    lse (n,), decisions (n, nt), margins (n, nt).
     """
     if split % TILE:
         raise ValueError("split must be a multiple of 64")
+    n = qs.shape[0]
     L = k.shape[0]
     nt = (L + TILE - 1) // TILE
-    s = _scores(qvec[None, :], k)          # (1, L)
-    t = _tile_max(s, nt)[0]                # (nt,)
+    s = _scores(qs, k)                     # (n, L)
+    t = _tile_max(s, nt)                   # (n, nt)
+    # every (head, split) is its own decision block with its own running
+    # maximum: split sp holds tiles sp*per .. sp*per + per - 1 (the last one
+    # may be short; its missing tiles are not visited)
     per = split // TILE
-    dec = np.empty(nt, np.uint8)
-    margin = np.empty(nt)
-    for t0 in range(0, nt, per):
-        t1 = min(nt, t0 + per)
-        fc = None if forced is None else forced[None, t0:t1]
-        dd, mm = _decide(t[None, None, t0:t1], np.ones((1, 1), bool),
-                         np.ones((1, t1 - t0), bool), tau, fc)
-        dec[t0:t1] = dd[0]
-        margin[t0:t1] = mm[0]
-    kept = np.repeat(dec == KEPT, TILE)[:L][None, :]
+    nsp = (nt + per - 1) // per
+    tt = np.full((n, nsp * per), -np.inf)
+    tt[:, :nt] = t
+    visited = np.zeros((n, nsp * per), bool)
+    visited[:, :nt] = True
+    fc = None
+    if forced is not None:
+        fc = np.full((n, nsp * per), -1, np.int8)
+        fc[:, :nt] = forced
+        fc = fc.reshape(n * nsp, per)
+    dd, mm = _decide(tt.reshape(n * nsp, 1, per), np.ones((n * nsp, 1), bool),
+                     visited.reshape(n * nsp, per), tau, fc)
+    dec = dd.reshape(n, nsp * per)[:, :nt].copy()
+    margin = mm.reshape(n, nsp * per)[:, :nt].copy()
+    kept = np.repeat(dec == KEPT, TILE, axis=1)[:, :L]
     o, lse = _softmax_kept(s, kept, v)
-    return o[0], lse[0], dec, margin
+    return o, lse, dec, margin
+
+
+def decode_head(qvec: np.ndarray, k: np.ndarray, v: np.ndarray, tau: float,
+                split: int = SPLIT, forced: np.ndarray | None = None):
+    """Oracle for one query token against one KV head: decode_heads for a
+    single head. qvec (d,), k/v (L, d) fp64. Returns o (d,), lse,
+    decisions (nt,), margins (nt,)."""
+    fc = None if forced is None else np.asarray(forced)[None, :]
+    o, lse, dec, margin = decode_heads(qvec[None, :], k, v, tau, split, fc)
+    return o[0], lse[0], dec[0], margin[0]
 
 
 def decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, tau: float,

@@ -127,6 +127,36 @@ class PrefillChecker:
         return rep
 
 
+    def check_blocks(self, b, h, qb0, qb1, tau, o_gpu, lse_gpu, mask_gpu) -> Report:
+        """Query blocks qb0 .. qb1 - 1 of one head in one oracle call (the
+        rule runs over all of them at once); o_gpu/lse_gpu are their rows,
+        mask_gpu (qb1 - qb0, nt)."""
+        rep = Report()
+        k, v = self.kv(b, h // self.G)
+        r0, r1 = qb0 * 64, min(self.N, qb1 * 64)
+        qrows = synth.bf16_bits_to_f64(self.q[b, h, r0:r1])
+        o, lse, dec, margin = oracle.prefill_blocks(qrows, k, v, qb0 + self.q0t, self.causal, tau)
+        visited = dec != oracle.NOT_VISITED
+        if not np.array_equal(mask_gpu[~visited], dec[~visited]):
+            rep.hard_mismatch += int((mask_gpu[~visited] != dec[~visited]).sum())
+            rep.notes.append(f"not-visited marks differ at b={b} h={h} qb={qb0}..{qb1 - 1}")
+        forced, amb, hard = _compare_decisions(mask_gpu.astype(np.int16),
+                                               dec.astype(np.int16), margin, visited)
+        rep.ambiguous += amb
+        rep.hard_mismatch += hard
+        if hard:
+            bad = np.argwhere((mask_gpu != dec) & visited)[:4]
+            rep.notes.append(f"b={b} h={h} (qb-{qb0}, kb)={bad.tolist()}")
+        if forced is not None:
+            o, lse, _, _ = oracle.prefill_blocks(qrows, k, v, qb0 + self.q0t, self.causal, tau,
+                                                 forced)
+        rep.tiles += int(visited.sum())
+        rep.skipped += int((mask_gpu[visited] == 1).sum())
+        rep.o_err = max_abs_err(o_gpu, o)
+        rep.lse_err = max_abs_err(lse_gpu, lse)
+        return rep
+
+
 def check_prefill(q_bits, k_bits, v_bits, causal, tau, o, lse, mask, blocks=None,
                   q0: int = 0) -> Report:
     """Compare full GPU outputs (numpy) over the given (b, h, qb) blocks
@@ -161,36 +191,49 @@ def check_decode(q_bits, k_bits, v_bits, tau, o, lse, mask, heads=None,
     G = Hq // Hkv
     if heads is None:
         heads = [(b, h) for b in range(B) for h in range(Hq)]
-    heads = sorted(heads, key=lambda x: (x[0], x[1] // G, x[1]))
+    groups = {}
+    for b, h in sorted(heads):
+        groups.setdefault((b, h // G), []).append(h)
     rep = Report()
-    cache = {}
-    for b, h in heads:
-        g = h // G
-        if (b, g) not in cache:
-            cache.clear()
-            cache[(b, g)] = kv_for(b, g)
-        k, v = cache[(b, g)]
-        qv = synth.bf16_bits_to_f64(q_bits[b, h])
-        def head(forced=None):
+    for (b, g), hs in groups.items():
+        k, v = kv_for(b, g)
+        qs = synth.bf16_bits_to_f64(q_bits[b, hs])
+        gpu_mask = mask[b, hs]
+
+        def run(sel, forced=None):
+            """Oracle for heads hs[i], i in sel: o, lse, dec, margin, slack."""
             if sas:
-                return oracle.sas.decode_head(qv, k, v, tau, sas, split, forced)
-            return oracle.decode_head(qv, k, v, tau, split, forced) + ((0.0, 0.0),)
-        ro, rl, dec, margin, slack = head()
+                outs = [oracle.sas.decode_head(qs[i], k, v, tau, sas, split,
+                                               None if forced is None else forced[j])
+                        for j, i in enumerate(sel)]
+                return (np.stack([x[0] for x in outs]), np.array([x[1] for x in outs]),
+                        np.stack([x[2] for x in outs]), np.stack([x[3] for x in outs]),
+                        [x[4] for x in outs])
+            ro, rl, dec, margin = oracle.decode_heads(qs[sel], k, v, tau, split, forced)
+            return ro, rl, dec, margin, [(0.0, 0.0)] * len(sel)
+
+        allh = list(range(len(hs)))
+        ro, rl, dec, margin, slack = run(allh)
         visited = np.ones(dec.shape, bool)
-        forced, amb, hard = _compare_decisions(mask[b, h].astype(np.int16),
+        forced, amb, hard = _compare_decisions(gpu_mask.astype(np.int16),
                                                dec.astype(np.int16), margin, visited)
         if hard:
-            bad = np.nonzero(mask[b, h] != dec)[0][:4]
-            rep.notes.append(f"b={b} h={h} tiles={bad.tolist()} margin={margin[bad].tolist()}")
+            bad = np.argwhere(gpu_mask != dec)[:4]
+            rep.notes.append(f"b={b} (head, tile)={[(hs[i], t) for i, t in bad.tolist()]} "
+                             f"margin={[float(margin[i, t]) for i, t in bad.tolist()]}")
         if forced is not None:
-            ro, rl, _, _, slack = head(forced)
+            redo = [i for i in allh if (forced[i] >= 0).any()]
+            o2, l2, _, _, s2 = run(redo, forced[redo])
+            for j, i in enumerate(redo):
+                ro[i], rl[i], slack[i] = o2[j], l2[j], s2[j]
         rep.tiles += dec.size
-        rep.skipped += int((mask[b, h] == 1).sum())
+        rep.skipped += int((gpu_mask == 1).sum())
         rep.ambiguous += amb
         rep.hard_mismatch += hard
         # errors beyond the slack the SAS steps allow count against the tolerance
-        rep.o_err = max(rep.o_err, max(0.0, max_abs_err(o[b, h], ro) - slack[1]))
-        rep.lse_err = max(rep.lse_err, max(0.0, max_abs_err(lse[b, h], rl) - slack[0]))
+        for i, h in enumerate(hs):
+            rep.o_err = max(rep.o_err, max(0.0, max_abs_err(o[b, h], ro[i]) - slack[i][1]))
+            rep.lse_err = max(rep.lse_err, max(0.0, max_abs_err(lse[b, h], rl[i]) - slack[i][0]))
     return rep
 
 

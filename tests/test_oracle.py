@@ -397,3 +397,51 @@ def test_parity_error_measure_refuses_nan():
     assert _parity.max_abs_err([1.0], [float("inf")]) == float("inf")
     r = _parity.Report(o_err=_parity.max_abs_err([float("nan")], [0.0]))
     assert not r.ok()
+
+
+def test_decisions_only_path_equals_full_blocks():
+    # the decisions-only entry (scores and tile maxima once, the rule per tau)
+    # gives the decisions and margins of the full block oracle
+    rng = np.random.default_rng(11)
+    N, d = 700, 64
+    u = rng.normal(size=d)
+    u /= np.linalg.norm(u)
+    q = rng.normal(size=(N, d)) + 0.5 * math.sqrt(d) * u
+    k = rng.normal(size=(N, d))
+    k[:3] += 6.0 * math.sqrt(d) * u   # sink keys ~24 logits up: later tiles skip
+    v = rng.normal(size=(N, d))
+    for causal in (True, False):
+        for qb0, nrows in ((0, 256), (4, 700 - 256)):
+            rows = q[qb0 * 64:qb0 * 64 + nrows]
+            got = oracle.prefill_decisions(rows, k, qb0, causal, (math.inf, 4.0, 1.0))
+            for tau, (dec, margin) in got.items():
+                _, _, dref, mref = oracle.prefill_blocks(rows, k, v, qb0, causal, tau)
+                assert np.array_equal(dec, dref)
+                assert np.array_equal(margin, mref, equal_nan=True)
+            assert (got[1.0][0] == oracle.SKIPPED).any()
+
+
+def test_decode_heads_is_decode_head_per_head():
+    # the multi-head decode oracle: per head, the decisions and margins of
+    # the one-head call, outputs to rounding, forced decisions honoured
+    rng = np.random.default_rng(12)
+    L, d = 9000, 64
+    u = rng.normal(size=d)
+    u /= np.linalg.norm(u)
+    qs = rng.normal(size=(5, d)) + 0.5 * math.sqrt(d) * u
+    k = rng.normal(size=(L, d))
+    k[[0, 4100, 8200]] += 6.0 * math.sqrt(d) * u
+    v = rng.normal(size=(L, d))
+    for tau in (math.inf, 4.0):
+        o, lse, dec, margin = oracle.decode_heads(qs, k, v, tau)
+        for i in range(5):
+            o1, l1, d1, m1 = oracle.decode_head(qs[i], k, v, tau)
+            assert np.array_equal(dec[i], d1)
+            assert np.allclose(margin[i], m1, rtol=0, atol=1e-12)
+            assert np.abs(o[i] - o1).max() < 1e-13 and abs(lse[i] - l1) < 1e-13
+    assert (dec == oracle.SKIPPED).any()
+    forced = np.full(dec.shape, -1, np.int8)
+    forced[2, 3] = 1 - dec[2, 3]
+    _, _, dec2, _ = oracle.decode_heads(qs, k, v, 4.0, forced=forced)
+    assert dec2[2, 3] == forced[2, 3]
+    assert np.array_equal(np.delete(dec2, 2, axis=0), np.delete(dec, 2, axis=0))
