@@ -21,7 +21,9 @@ from one extra call outside its timing.
 Hkv=8) causal prefill shape in the 128K one's place; the default line is the
 128K step.
 
-Beside the step, the same decode workload is run over the 4-bit asymmetric
+Beside the step, the 8K and 32K causal prefill workloads are timed alone
+(``prefill_8k``, ``prefill_32k``: TFLOP/s, fraction of the bf16 peak, their
+tau sweeps), and the same decode workload is run over the 4-bit asymmetric
 KV cache (attn_kv_quantize_q4 once, then attn_decode_q4 timed like the bf16
 decode): ``decode_q4`` reports GB/s of the 4-bit bytes read, its fraction of
 HBM peak and the bf16-equivalent rate.
@@ -195,6 +197,17 @@ def _cpu_decode_q_head(item):
             oracle.decode_head(synth.bf16_bits_to_f64(q[hh]), k, v, math.inf)
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=768, nkv=32, nkv_q=16, pname="prefill_128k"):
     """The fp64 oracle as it stands, timed on a bounded sample of each
     workload with one process per host core (fp64 widening of the inputs is
@@ -202,7 +215,7 @@ def cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=768, nkv=32, nkv_q=16, pname="p
     import multiprocessing as mp
 
     import synth
-    cores = min(16, os.cpu_count() or 1)
+    cores = min(16, os.cpu_count() or 1)      # worker processes actually used
     N, d = pq.shape[2], pq.shape[3]
     nt = N // 64
     nblocks = min(nblocks, nt)
@@ -237,20 +250,21 @@ def cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=768, nkv=32, nkv_q=16, pname="p
             pool.map(_cpu_decode_q_head, [(key, i) for i in range(len(pickq))], chunksize=1)
             qwall[key] = time.perf_counter() - t0
     _CPU.clear()
+    host = dict(host_cores=os.cpu_count(), host_cpu=_cpu_model())
     pairs = sum(64 * (qb * 64) + 64 * 65 // 2 for qb in qbs)
     pre = dict(value=float(4.0 * d * pairs / pwall / 1e12), unit="TFLOP/s", cores=cores,
-               kind="oracle",
+               kind="oracle", **host,
                sample=f"{pname} head 0: {nblocks} of {nt} query blocks spread evenly, "
                       f"tau=inf, fp64 numpy, {pwall:.1f} s wall")
     kv_bytes = len(picks) * 2.0 * L * d * 2
-    dec = dict(value=float(kv_bytes / dwall / 1e9), unit="GB/s", cores=cores, kind="oracle",
+    dec = dict(value=float(kv_bytes / dwall / 1e9), unit="GB/s", cores=cores, kind="oracle", **host,
                sample=f"decode_128k: {len(picks)} KV heads x {G} query heads, tau=inf, "
                       f"fp64 numpy, {dwall:.1f} s wall")
     quant = {}
     for key, bits in (("dq4", 4), ("dq2", 2)):
         nb = qcache_bytes(bits, len(pickq), 1, L, d)
         quant[key] = dict(value=float(nb / qwall[key] / 1e9), unit="GB/s", cores=cores,
-                          kind="oracle",
+                          kind="oracle", **host,
                           sample=f"decode_128k over the {bits}-bit cache: {len(pickq)} KV heads "
                                  f"x {G} query heads, dequantise + fp64 decode oracle, tau=inf, "
                                  f"{qwall[key]:.1f} s wall")
@@ -277,6 +291,8 @@ def main():
     ap.add_argument("--prefill-workload", default="prefill_128k",
                     choices=["prefill_128k", "prefill_32k", "prefill_8k"],
                     help="prefill shape of the step (default: the 128K one)")
+    ap.add_argument("--no-other-prefill", action="store_true",
+                    help="skip the 8K and 32K causal prefill workloads timed beside the step")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB, a reference "
                          "dispatch of known traffic for hardware byte counters")
@@ -483,6 +499,57 @@ def main():
                                    traffic=measured_traffic(leg),
                                    kernel=f"decode_q{w}_split_kernel<128>",
                                    avg_ms=round(q_ms, 4), per_launch_bytes=qb)
+
+    if run_p and args.only == "both" and not args.no_other_prefill:
+        # the other causal prefill workloads, timed alone like the step's
+        # prefill (mean of K calls at tau = inf, median of 3 per tau)
+        for oname in ("prefill_8k", "prefill_32k"):
+            if oname == pname:
+                continue
+            ocfg = synth.workload(oname)
+            oq, ok_, ov = synth.make_prefill(ocfg, reading=args.reading)
+            OB, OHq, ON, Od = oq.shape
+            xq, xk, xv = _dev(oq, dev), _dev(ok_, dev), _dev(ov, dev)
+            xo = torch.empty((OB, OHq, ON, Od), dtype=torch.float32, device=dev)
+            xl = torch.empty((OB, OHq, ON), dtype=torch.float32, device=dev)
+            ont = (ON + 63) // 64
+            xm = torch.empty((OB, OHq, ont, ont), dtype=torch.uint8, device=dev)
+
+            def oprefill(tau, mask=None):
+                lib.attn_prefill(xq, xk, xv, xo, xl, True, tau, mask)
+
+            for _ in range(args.warmup):
+                oprefill(math.inf)
+            to = Timer()
+            torch.cuda.synchronize()
+            for _ in range(args.steps):
+                with to:
+                    oprefill(math.inf)
+            torch.cuda.synchronize()
+            o_ms = float(np.mean(to.ms()))
+            of = prefill_dense_flops(OB, OHq, ON, Od)
+            entry = dict(value=round(of / (o_ms * 1e-3) / 1e12, 3), unit="TFLOP/s",
+                         ms=round(o_ms, 4),
+                         frac_of_peak=round(of / (o_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         per_call_flops=of,
+                         shape=dict(B=OB, Hq=OHq, Hkv=ok_.shape[1], N=ON, d=Od, causal=True))
+            taus = []
+            for tau in ocfg["taus"][1:]:
+                t = Timer()
+                for _ in range(3):
+                    with t:
+                        oprefill(tau)
+                torch.cuda.synchronize()
+                ms = float(np.median(t.ms()))
+                oprefill(tau, xm)
+                ex, vis, kept = prefill_exec_flops(xm.cpu().numpy(), Od)
+                taus.append(dict(tau=str(tau), ms=round(ms, 4), skip_fraction=round(1 - kept / vis, 4),
+                                 tflops_dense=round(of / ms / 1e9, 3),
+                                 tflops_executed=round(ex / ms / 1e9, 3)))
+            entry["tau_sweep"] = taus
+            out[oname] = entry
+            del xq, xk, xv, xo, xl, xm
+            torch.cuda.empty_cache()
 
     if not args.no_sweep:
         sweep = []

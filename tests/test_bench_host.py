@@ -101,5 +101,6 @@ def test_cpu_baseline_runs_on_tiny_inputs(bench):
                                             pname="tiny")
     for r in (pre, dec, dq4, dq2):
         assert r["kind"] == "oracle" and r["value"] > 0 and r["cores"] >= 1
+        assert r["host_cores"] == os.cpu_count() and r["cores"] <= r["host_cores"]
     assert pre["unit"] == "TFLOP/s" and dq2["unit"] == "GB/s"
     assert "2-bit" in dq2["sample"] and "4-bit" in dq4["sample"]
