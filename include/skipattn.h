@@ -134,6 +134,34 @@ int attn_prefill_chunk_cap(const void* q, const void* k, const void* v, float* o
                            uint8_t* skip_mask, void* stream);
 
 /*
+ * attn_prefill_qk8 - attn_prefill with QK^T on block-quantised 8-bit
+ * operands (TurboAttention talk page, "Technical Deep Dive" and "Key
+ * Findings": symmetric 8-bit quantisation of the matrix-product operands,
+ * block-wise inside the flash blocks). Q and K are quantised to fp8 E4M3
+ * per 64-row tile (a query tile of Q, a key tile of K) and S = Q K^T runs on
+ * the fp8 matrix cores; V, P V, the softmax and the skip rule are as in
+ * attn_prefill. Per tile: scale s = (largest |x| in the tile) / 448 in fp32
+ * (1 for a tile of zeros); code = the E4M3 value nearest clamp(x / s, -448,
+ * 448) (fp32 division; ties to the even mantissa; a value that rounds to
+ * zero is code 0). The scores are those of the dequantised q^ = code * s_q,
+ * k^ = code * s_k.
+ *
+ *   q, k, v, o, lse, causal, tau, skip_mask  as for attn_prefill
+ *   workspace  device scratch of at least attn_prefill_qk8_workspace_bytes();
+ *              on return (once the stream has synchronised) it holds, each
+ *              part starting on a 256-byte boundary: Q codes uint8 [B, Hq,
+ *              N, d], K codes uint8 [B, Hkv, N, d], Q scales fp32 [B, Hq,
+ *              ceil(N/64)], K scales fp32 [B, Hkv, ceil(N/64)].
+ * Errors as for attn_prefill; SKIPATTN_EWORKSPACE if the workspace is NULL
+ * or too small.
+ */
+size_t attn_prefill_qk8_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
+int attn_prefill_qk8(const void* q, const void* k, const void* v, float* o,
+                     float* lse, int B, int Hq, int Hkv, int N, int d,
+                     int causal, float tau, uint8_t* skip_mask,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * attn_decode_workspace_bytes - bytes of device scratch attn_decode needs:
  * B * Hq * ceil(L / 4096) * (d + 1) * 4 (per-split partial outputs and
  * log-sum-exps). Returns 0 for invalid or empty sizes.

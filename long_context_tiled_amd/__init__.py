@@ -8,7 +8,8 @@ from ._lib import (OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, TILE, SPLIT,
                    attn_decode_q4, quantize_q4, decode_q4, attn_prefill_chunk, prefill_chunk,
                    empty_q4, q2_shapes, attn_kv_quantize_q2, attn_decode_q2, quantize_q2,
                    decode_q2, empty_q2, attn_decode_noalloc,
-                   DECODE_SCRATCH_BYTES)
+                   DECODE_SCRATCH_BYTES, attn_prefill_qk8, attn_prefill_qk8_workspace_bytes,
+                   qk8_workspace_parts, prefill_qk8)
 
 __all__ = ["OK", "EINVAL", "EUNSUPPORTED", "EWORKSPACE", "EHIP", "TILE", "SPLIT",
            "KEPT", "SKIPPED", "NOT_VISITED", "EXPORTS", "LIB_PATH", "SkipAttnError",
@@ -17,4 +18,5 @@ __all__ = ["OK", "EINVAL", "EUNSUPPORTED", "EWORKSPACE", "EHIP", "TILE", "SPLIT"
            "attn_decode_q4", "quantize_q4", "decode_q4", "attn_prefill_chunk",
            "prefill_chunk", "empty_q4", "q2_shapes", "attn_kv_quantize_q2",
            "attn_decode_q2", "quantize_q2", "decode_q2", "empty_q2",
-           "attn_decode_noalloc", "DECODE_SCRATCH_BYTES"]
+           "attn_decode_noalloc", "DECODE_SCRATCH_BYTES", "attn_prefill_qk8",
+           "attn_prefill_qk8_workspace_bytes", "qk8_workspace_parts", "prefill_qk8"]

@@ -27,7 +27,8 @@ EXPORTS = ("attn_prefill", "attn_decode", "attn_decode_workspace_bytes",
            "attn_kv_quantize_q2", "attn_kv_quantize_q2_range", "attn_decode_q2",
            "attn_decode_q2_check", "attn_decode_sas", "attn_decode_q4_sas",
            "attn_decode_q2_sas", "attn_prefill_chunk_cap", "attn_decode_cap",
-           "attn_decode_q4_cap", "attn_decode_q2_cap", "attn_decode_noalloc")
+           "attn_decode_q4_cap", "attn_decode_q2_cap", "attn_decode_noalloc",
+           "attn_prefill_qk8", "attn_prefill_qk8_workspace_bytes")
 
 _lib = None
 
@@ -67,6 +68,11 @@ def load() -> ctypes.CDLL:
     lib.attn_decode_cap.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, i, f, i, u8p, vp, sz,
                                     vp]
     lib.attn_decode_cap.restype = i
+    lib.attn_prefill_qk8.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, i, f, u8p, vp, sz,
+                                     vp]
+    lib.attn_prefill_qk8.restype = i
+    lib.attn_prefill_qk8_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.attn_prefill_qk8_workspace_bytes.restype = sz
     lib.attn_decode_noalloc.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, f, u8p, vp]
     lib.attn_decode_noalloc.restype = i
     lib.attn_decode_check.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, f, u8p, vp, sz]
@@ -178,6 +184,56 @@ def attn_prefill_chunk(q, k, v, o, lse, causal: bool, tau: float, skip_mask=None
         rc = so.attn_prefill_chunk_cap(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq,
                                        Hkv, Nq, N, cap, d, int(bool(causal)), float(tau),
                                        _ptr(skip_mask), _stream(stream))
+    _raise(rc)
+
+
+def attn_prefill_qk8_workspace_bytes(B: int, Hq: int, Hkv: int, N: int, d: int) -> int:
+    return int(load().attn_prefill_qk8_workspace_bytes(B, Hq, Hkv, N, d))
+
+
+def qk8_workspace_parts(workspace, B: int, Hq: int, Hkv: int, N: int, d: int) -> dict:
+    """Views of an attn_prefill_qk8 workspace: Q codes uint8 [B,Hq,N,d], K
+    codes [B,Hkv,N,d], Q scales fp32 [B,Hq,ceil(N/64)], K scales
+    [B,Hkv,ceil(N/64)] (each part starts on a 256-byte boundary)."""
+    import torch
+    nt = (N + TILE - 1) // TILE
+    al = lambda x: (x + 255) // 256 * 256
+    sizes = [("qc", B * Hq * N * d), ("kc", B * Hkv * N * d), ("qs", B * Hq * nt * 4),
+             ("ks", B * Hkv * nt * 4)]
+    out, off = {}, 0
+    w = workspace.view(torch.uint8)
+    for name, n in sizes:
+        out[name] = w[off:off + n]
+        off += al(n)
+    out["qc"] = out["qc"].view(B, Hq, N, d)
+    out["kc"] = out["kc"].view(B, Hkv, N, d)
+    out["qs"] = out["qs"].view(torch.float32).view(B, Hq, nt)
+    out["ks"] = out["ks"].view(torch.float32).view(B, Hkv, nt)
+    return out
+
+
+def attn_prefill_qk8(q, k, v, o, lse, causal: bool, tau: float, workspace, skip_mask=None,
+                     stream=None) -> None:
+    """attn_prefill with QK^T on block-quantised fp8 (E4M3) Q and K; the
+    workspace (attn_prefill_qk8_workspace_bytes) receives the codes and
+    scales (qk8_workspace_parts)."""
+    import torch
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    _check(q, "q", torch.bfloat16, (B, Hq, N, d))
+    _check(k, "k", torch.bfloat16, (B, Hkv, N, d))
+    _check(v, "v", torch.bfloat16, (B, Hkv, N, d))
+    _check(o, "o", torch.float32, (B, Hq, N, d))
+    _check(lse, "lse", torch.float32, (B, Hq, N))
+    if skip_mask is not None:
+        nt = (N + TILE - 1) // TILE
+        _check(skip_mask, "skip_mask", torch.uint8, (B, Hq, nt, nt))
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = load().attn_prefill_qk8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N,
+                                 d, int(bool(causal)), float(tau), _ptr(skip_mask),
+                                 _ptr(workspace), nbytes, _stream(stream))
     _raise(rc)
 
 
@@ -421,6 +477,26 @@ def prefill(q, k, v, causal: bool, tau: float = math.inf, want_mask: bool = Fals
         mask = torch.empty((B, Hq, nt, nt), dtype=torch.uint8, device=q.device)
     attn_prefill(q, k, v, o, lse, causal, tau, mask, stream)
     return o, lse, mask
+
+
+def prefill_qk8(q, k, v, causal: bool, tau: float = math.inf, want_mask: bool = False,
+                workspace=None, stream=None):
+    """Allocate outputs (and the workspace if not given) and call
+    attn_prefill_qk8. Returns (o, lse, mask, workspace)."""
+    import torch
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    mask = None
+    if want_mask:
+        nt = (N + TILE - 1) // TILE
+        mask = torch.empty((B, Hq, nt, nt), dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        nbytes = max(256, attn_prefill_qk8_workspace_bytes(B, Hq, Hkv, N, d))
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    attn_prefill_qk8(q, k, v, o, lse, causal, tau, workspace, mask, stream)
+    return o, lse, mask, workspace
 
 
 def prefill_chunk(q, k, v, causal: bool, tau: float = math.inf, want_mask: bool = False,

@@ -156,6 +156,23 @@ int prefill_launch(const void* q, const void* k, const void* v, float* o, float*
   return SKIPATTN_OK;
 }
 
+// Workspace of attn_prefill_qk8: fp8 codes of Q and K, then their tile
+// scales, each part 256-byte aligned.
+struct Qk8Layout {
+  size_t qc, kc, qs, ks, total;
+};
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+Qk8Layout qk8_layout(int B, int Hq, int Hkv, int N, int d) {
+  Qk8Layout l;
+  const size_t nt = ((size_t)N + SKIPATTN_TILE - 1) / SKIPATTN_TILE;
+  l.qc = 0;
+  l.kc = l.qc + align256((size_t)B * Hq * N * d);
+  l.qs = l.kc + align256((size_t)B * Hkv * N * d);
+  l.ks = l.qs + align256((size_t)B * Hq * nt * 4);
+  l.total = l.ks + align256((size_t)B * Hkv * nt * 4);
+  return l;
+}
+
 int decode_launch(const void* q, const void* k, const void* v, float* o, float* lse, int B,
                   int Hq, int Hkv, int L, int cap, int d, float tau, int degree,
                   uint8_t* skip_mask, void* workspace, size_t workspace_bytes, void* stream) {
@@ -259,6 +276,38 @@ int attn_prefill(const void* q, const void* k, const void* v, float* o, float* l
                  int B, int Hq, int Hkv, int N, int d, int causal, float tau,
                  uint8_t* skip_mask, void* stream) {
   return prefill_launch(q, k, v, o, lse, B, Hq, Hkv, N, N, N, d, causal, tau, skip_mask, stream);
+}
+
+size_t attn_prefill_qk8_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
+  return qk8_layout(B, Hq, Hkv, N, d).total;
+}
+
+int attn_prefill_qk8(const void* q, const void* k, const void* v, float* o, float* lse, int B,
+                     int Hq, int Hkv, int N, int d, int causal, float tau, uint8_t* skip_mask,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (int e = prefill_check(q, k, v, o, lse, B, Hq, Hkv, N, N, N, d, causal, tau, skip_mask))
+    return e;
+  if (B == 0 || N == 0) return SKIPATTN_OK;
+  const Qk8Layout l = qk8_layout(B, Hq, Hkv, N, d);
+  if (workspace == nullptr || workspace_bytes < l.total)
+    return fail(SKIPATTN_EWORKSPACE, "prefill_qk8 workspace needs %zu bytes (got %zu)", l.total,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (!aligned16(workspace)) return fail(SKIPATTN_EINVAL, "workspace must be 16-byte aligned");
+  char* ws = (char*)workspace;
+  uint8_t* qc = (uint8_t*)(ws + l.qc);
+  uint8_t* kc = (uint8_t*)(ws + l.kc);
+  float* qs = (float*)(ws + l.qs);
+  float* ks = (float*)(ws + l.ks);
+  if (skipattn::launch_quantize_fp8(q, qc, qs, (long long)B * Hq, N, d, stream) != 0 ||
+      skipattn::launch_quantize_fp8(k, kc, ks, (long long)B * Hkv, N, d, stream) != 0)
+    return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
+  skipattn::PrefillArgs a{qc, kc, v, o, lse, skip_mask, B, Hq, Hkv, N, d, causal,
+                          N,  0,  N, tau_raw(tau, d), exp2_scale(d), stream, qs, ks};
+  if (skipattn::launch_prefill(a) != 0) return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(SKIPATTN_EHIP, "prefill_qk8 launch: %s", hipGetErrorString(err));
+  return SKIPATTN_OK;
 }
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int L, int d) {

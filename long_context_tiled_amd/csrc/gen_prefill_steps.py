@@ -67,10 +67,12 @@ import os
 import re
 import sys
 
-NOP_MFMA_VALU = 12
+NOP_MFMA_VALU = 12       # 8-pass MFMA (bf16 32x32x16) result -> VALU read
+NOP_MFMA16_VALU = 20     # 16-pass MFMA (fp8 32x32x64) result -> VALU read
 NOP_VALU_MFMA = 4
 NOP_TRANS_VALU = 1
 NOP_MFMA_READ_LOAD = 2
+NOP_MFMA16_READ_LOAD = 4
 NOP_VALU_PERM = 2
 
 COST = {"v_exp_f32": 8.2, "v_cvt_pk_bf16_f32": 6.0}
@@ -82,6 +84,8 @@ PREG = 96     # P^T operand, v[96:127]
 TREG = 48     # exp temporaries, three pairs v[48:53]
 VADR = 54     # V^T read addresses, v[54 : 54 + 2 MB)
 KADR = 62     # K read addresses, v62 / v63 alternating
+KADR8 = 40    # fp8 QK: K read addresses of k-step / half pairs, v[40:43) (phase A only;
+              # the vote uses these registers after phase A)
 VOTE = 40     # vote temporaries, v[40:46)
 PSUM = 46     # this tile's partial row sums, v46 (query half 0) and v47 (half 1)
 OB = 64       # first AGPR of O^T
@@ -110,19 +114,22 @@ class Ins:
         op = text.split()[0]
         self.cost = COST.get(op, COST_DEFAULT) if kind in ("valu", "trans", "perm") else (
             1.0 if kind == "salu" else 0.0)
+        self.is_mfma = kind in ("mfma", "mfma16")
 
 
 class Step:
     """One step variant for one head dim and buffer assignment."""
 
-    def __init__(self, d, variant, x, y, budget, loop=False, dma=False):
+    def __init__(self, d, variant, x, y, budget, loop=False, dma=False, f8=False):
         self.loop = loop
         self.dma = dma
         self.d = d
+        self.f8 = f8          # QK^T on fp8 codes (32x32x64, 16 passes), PV in bf16
         self.MB = d // 32
-        self.KS = d // 16
+        self.KS = d // 64 if f8 else d // 16   # QK k-steps
         self.QB = OB + 32 * self.MB
-        self.rowBytes = 2 * d
+        self.rowBytes = 2 * d                  # V rows (bf16)
+        self.kRowBytes = d if f8 else 2 * d    # K and Q rows
         self.variant = variant
         self.x = x  # buffer holding tile n (exp / PV)
         self.y = y  # buffer receiving tile n + 1 (QK / max)
@@ -138,6 +145,11 @@ class Step:
         return rng("v", self.s_reg(buf, a, nb), 16)
 
     def kfrag(self, j, a=0):
+        if self.f8:
+            # fragments of key half 0 in v[80:95], key half 1 in v[64:79]: the
+            # V^T fragments of PV k-step 0 (v[80:95]) may then be loaded as
+            # soon as key half 0's QK MFMAs have read theirs
+            return rng("v", KREG + 8 * (j ^ 2), 8)
         return rng("v", KREG + 4 * j, 4)
 
     def vfrag(self, j, mb):
@@ -148,6 +160,8 @@ class Step:
         return rng("v", PREG + 4 * (2 * kp + nb), 4)
 
     def qfrag(self, ks, nb):
+        if self.f8:
+            return rng("a", self.QB + 16 * ks + 8 * nb, 8)
         return rng("a", self.QB + 8 * ks + 4 * nb, 4)
 
     def oblk(self, mb, nb):
@@ -158,6 +172,28 @@ class Step:
         fragment address of k-step ks is the tile base XOR 32 ks (the swizzle
         only moves address bits 4..7; the tile base has bits 0..9 clear)."""
         out = []
+        if self.f8:
+            # 32 bytes per lane: 16-byte chunks 4 ks + 2 hh and the next one,
+            # at address kb0 ^ 64 ks and that ^ 16 (the swizzle moves only
+            # address bits 4..6 within a 128-byte row); key half 1 is the
+            # immediate offset of 32 rows. The addresses of (ks, chunk) != (0, 0)
+            # are formed once, with key half 0's loads.
+            names = {(0, 0): "%[kb0]", (0, 1): f"v{KADR8}", (1, 0): f"v{KADR8 + 1}",
+                     (1, 1): f"v{KADR8 + 2}"}
+            if a == 0:
+                for jj in range(2):
+                    if (ks, jj) != (0, 0):
+                        out.append(Ins(f"v_xor_b32 {names[(ks, jj)]}, {64 * ks + 16 * jj}, %[kb0]",
+                                       "valu", wr=[names[(ks, jj)]]))
+            dst = self.kfrag(j, 0)
+            base = KREG + 8 * (j ^ 2)
+            off = a * 32 * self.kRowBytes
+            for jj in range(2):
+                adr = names[(ks, jj)]
+                part = rng("v", base + 4 * jj, 4)
+                out.append(Ins(f"ds_read_b128 {part}, {adr} offset:{off}", "lds",
+                               wr=[part], rd=[adr]))
+            return out
         if ks == 0:
             adr = "%[kb0]"
         else:
@@ -200,19 +236,29 @@ class Step:
         range check, which zero-fills keys past N, covers voffset only), the
         LDS destination into M0. %[t1] is the tile's byte offset, %[t2] this
         wave's LDS destination base."""
-        ipw = 64 // (1024 // self.rowBytes) // 4
-        tile_bytes = 64 * self.rowBytes
         groups = []
         n = 0
-        for which, rs, g in (("K", "%[krs]", "gk"), ("V", "%[vrs]", "gv")):
+        if self.f8:
+            # K (fp8 rows) and V (bf16 rows) tiles differ in size: %[t1] / %[t4]
+            # are their byte offsets, %[t2] / %[t5] this wave's LDS bases
+            parts = (("K", "%[krs]", "gk", "%[t1]", "%[t2]", 64 * self.kRowBytes // 4096),
+                     ("V", "%[vrs]", "gv", "%[t4]", "%[t5]", 64 * self.rowBytes // 4096))
+        else:
+            ipw = 64 // (1024 // self.rowBytes) // 4
+            tile_bytes = 64 * self.rowBytes
+            parts = (("K", "%[krs]", "gk", "%[t1]", "%[t2]", ipw),
+                     ("V", "%[vrs]", "gv", "%[t1]", "%[t2]", ipw))
+        for which, rs, g, toff, lbase, ipw in parts:
             for i in range(ipw):
-                off = (tile_bytes if which == "V" else 0) + i * 1024
+                off = i * 1024
+                if not self.f8 and which == "V":
+                    off += tile_bytes
                 tmp = "%[vt]" if n % 2 == 0 else "%[vz]"
                 n += 1
                 # the VALU add sits between the M0 write and the copy that
                 # reads M0, which needs one wait state there
-                groups.append([Ins(f"s_add_u32 m0, %[t2], {off}", "salu"),
-                               Ins(f"v_add_u32 {tmp}, %[t1], %[{g}{i}]", "valu"),
+                groups.append([Ins(f"s_add_u32 m0, {lbase}, {off}", "salu"),
+                               Ins(f"v_add_u32 {tmp}, {toff}, %[{g}{i}]", "valu"),
                                Ins(f"buffer_load_dwordx4 {tmp}, {rs}, 0 offen lds", "vmem")])
         return groups
 
@@ -222,6 +268,9 @@ class Step:
         qf = self.qfrag(ks, nb)
         src_c = "0" if ks == 0 else s
         rd = [kf, qf] + ([] if ks == 0 else [s])
+        if self.f8:
+            return Ins(f"v_mfma_f32_32x32x64_f8f6f4 {s}, {kf}, {qf}, {src_c}", "mfma16", wr=[s],
+                       rd=rd)
         return Ins(f"v_mfma_f32_32x32x16_bf16 {s}, {kf}, {qf}, {src_c}", "mfma", wr=[s], rd=rd)
 
     def pv_mfma(self, ks, mb, nb):
@@ -251,9 +300,10 @@ class Step:
             w = f"v{PREG + 4 * (2 * kp + nb) + i2}"
             ps = f"v{PSUM + nb}"
             nm = f"%[nm{nb}]"
+            cc = "%[ce]" if self.f8 else "%[c]"
             heads.append([
-                Ins(f"v_fma_f32 {t0}, {s0}, %[c], {nm}", "valu", wr=[t0], rd=[s0]),
-                Ins(f"v_fma_f32 {t1}, {s1}, %[c], {nm}", "valu", wr=[t1], rd=[s1]),
+                Ins(f"v_fma_f32 {t0}, {s0}, {cc}, {nm}", "valu", wr=[t0], rd=[s0]),
+                Ins(f"v_fma_f32 {t1}, {s1}, {cc}, {nm}", "valu", wr=[t1], rd=[s1]),
                 Ins(f"v_exp_f32 {t0}, {t0}", "trans", wr=[t0], rd=[t0]),
                 Ins(f"v_exp_f32 {t1}, {t1}", "trans", wr=[t1], rd=[t1]),
             ])
@@ -299,7 +349,12 @@ class Step:
 
     def vote_stream(self):
         v = [f"v{VOTE + i}" for i in range(6)]
-        return [
+        pre = []
+        if self.f8:
+            # fp8 scores are in code units: times q scale x k scale of the tile
+            pre = [Ins("v_mul_f32 %[tm0], %[tm0], %[qa]", "valu"),
+                   Ins("v_mul_f32 %[tm1], %[tm1], %[qa]", "valu")]
+        return pre + [
             Ins(f"v_mov_b32 {v[0]}, %[tm0]", "valu", wr=[v[0]]),
             Ins(f"v_mov_b32 {v[1]}, %[tm0]", "valu", wr=[v[1]]),
             Ins(f"v_mov_b32 {v[2]}, %[tm1]", "valu", wr=[v[2]]),
@@ -341,7 +396,8 @@ class Step:
         exp_q = self.exp_stream() if self.pv else []
         max_q = (self.max_stream() + self.vote_stream()) if self.qk else []
         KS, MB = self.KS, self.MB
-        n_slots = (4 * KS if self.qk else 0) + (8 * MB if self.pv else 0)
+        qk_w = 2 if self.f8 else 1      # a 16-pass QK MFMA holds two 8-pass slots
+        n_slots = (4 * KS * qk_w if self.qk else 0) + (8 * MB if self.pv else 0)
         total_valu = sum(i.cost for i in exp_q) + sum(i.cost for i in max_q)
         budget = max(self.budget, total_valu / max(n_slots, 1))
         pos = {"exp": 0, "max": 0}
@@ -350,7 +406,7 @@ class Step:
 
         def mfma(ins):      # an MFMA, then the next tile-copy group if any
             seq.append(ins)
-            if dma_q and len([x for x in seq if x.kind == "mfma"]) >= 2:
+            if dma_q and len([x for x in seq if x.is_mfma]) >= 2:
                 seq.extend(dma_q.pop(0))
 
         def max_ready(ins):
@@ -385,8 +441,8 @@ class Step:
         # phase A --------------------------------------------------------
         if self.qk:
             order = [(a, ks) for a in range(2) for ks in range(KS)]
-            seq += self.k_load(0, 0, 0)
-            seq += self.k_load(0, 1, 1)
+            seq += self.k_load(*order[0], 0)
+            seq += self.k_load(*order[1], 1)
             if self.pv:
                 pull(2 * budget, use_max=False)
             for n, (a, ks) in enumerate(order):
@@ -395,9 +451,12 @@ class Step:
                     mfma(self.qk_mfma(ks, a, nb, j))
                     if nb == 0 and n + 2 < len(order):
                         seq += self.k_load(*order[n + 2], (n + 2) & 3)
-                    if nb == 0 and self.pv and n == len(order) // 2 + 2:
+                    # V^T fragments of PV k-step 0: bf16, once the K fragments
+                    # they overwrite are read; fp8, after key half 0's MFMAs
+                    v0_at = KS if self.f8 else len(order) // 2 + 2
+                    if nb == 0 and self.pv and n == v0_at:
                         seq += self.v_loads(0)
-                    pull(budget)
+                    pull(budget * qk_w)
                 # key half 0 final after its last k-step; its maxima wait two
                 # more k-steps (four MFMAs) to clear the MFMA result latency
                 if a == 0 and ks == KS - 1:
@@ -460,7 +519,9 @@ class Step:
             if ins.kind == "lds":
                 for r in ins.wr:
                     if r in last_mfma_read:
-                        gap = NOP_MFMA_READ_LOAD - slots_since(last_mfma_read[r])
+                        ridx, rkind = last_mfma_read[r]
+                        wait = NOP_MFMA16_READ_LOAD if rkind == "mfma16" else NOP_MFMA_READ_LOAD
+                        gap = wait - slots_since(ridx)
                         if gap > 0:
                             emit(f"s_nop {gap - 1}", gap)
             if need_lds >= 0:
@@ -472,9 +533,10 @@ class Step:
                 if r not in last_w:
                     continue
                 widx, wkind = last_w[r]
-                if wkind == "mfma" and ins.kind in ("valu", "trans"):
-                    need = max(need, NOP_MFMA_VALU - slots_since(widx))
-                elif wkind in ("valu", "trans") and ins.kind == "mfma":
+                mwait = NOP_MFMA16_VALU if wkind == "mfma16" else NOP_MFMA_VALU
+                if wkind in ("mfma", "mfma16") and ins.kind in ("valu", "trans"):
+                    need = max(need, mwait - slots_since(widx))
+                elif wkind in ("valu", "trans") and ins.kind in ("mfma", "mfma16"):
                     need = max(need, NOP_VALU_MFMA - slots_since(widx))
                 elif wkind == "trans" and ins.kind in ("valu", "trans", "perm"):
                     need = max(need, NOP_TRANS_VALU - slots_since(widx))
@@ -482,8 +544,8 @@ class Step:
                     need = max(need, NOP_VALU_PERM - slots_since(widx))
                 elif wkind == "perm" and ins.kind in ("valu", "perm"):
                     need = max(need, 1 - slots_since(widx))
-                if wkind == "mfma" and ins.kind == "perm":
-                    need = max(need, NOP_MFMA_VALU - slots_since(widx))
+                if wkind in ("mfma", "mfma16") and ins.kind == "perm":
+                    need = max(need, mwait - slots_since(widx))
             while need > 0:
                 n = min(need, 8)
                 emit(f"s_nop {n - 1}", n)
@@ -496,9 +558,9 @@ class Step:
                     lds_of_reg[r] = len(lds_seq) - 1
             for r in ins.wr:
                 last_w[r] = (idx, ins.kind)
-            if ins.kind == "mfma":
+            if ins.kind in ("mfma", "mfma16"):
                 for r in ins.rd:
-                    last_mfma_read[r] = idx
+                    last_mfma_read[r] = (idx, ins.kind)
         if len(lds_seq) > waited:
             emit("s_waitcnt lgkmcnt(0)")
         self.out = out
@@ -508,17 +570,19 @@ class Step:
         """Rough cycle estimate: each MFMA slot max(32, vector work + 8)."""
         t = 0.0
         cur = None
+        slot = 32.0
         for ins in self.seq:
-            if ins.kind == "mfma":
+            if ins.is_mfma:
                 if cur is not None:
-                    t += max(32.0, cur + 8.0)
+                    t += max(slot, cur + 8.0)
                 cur = 0.0
+                slot = 64.0 if ins.kind == "mfma16" else 32.0
             elif cur is not None:
                 cur += ins.cost
             else:
                 t += ins.cost
         if cur is not None:
-            t += max(32.0, cur + 8.0)
+            t += max(slot, cur + 8.0)
         return t
 
     # ---- C++ ------------------------------------------------------------
@@ -583,11 +647,11 @@ def asm_function(head, name, args, body, outs, ins_, clob, pre=(), post=()):
         "}"])
 
 
-def helpers_cxx(d):
+def helpers_cxx(d, f8=False):
     """Blocks outside the key loop that touch the fixed registers."""
-    MB, KS = d // 32, d // 16
+    MB, KS = d // 32, (d // 64 if f8 else d // 16)
     QB = OB + 32 * MB
-    row_bytes = 2 * d
+    row_bytes = d if f8 else 2 * d      # Q rows in LDS
     o_regs = [f"a{r}" for r in range(OB, OB + 32 * MB)]
     parts = []
 
@@ -598,19 +662,35 @@ def helpers_cxx(d):
 
     # Q^T fragments into AGPRs
     body = []
-    for ks in range(KS):
-        adr = "%[qb0]" if ks == 0 else f"v{KADR + (ks & 1)}"
-        if ks:
-            body.append(f"v_xor_b32 {adr}, {32 * ks}, %[qb0]")
-        for nb in range(2):
-            lo = QB + 8 * ks + 4 * nb
-            body.append(f"ds_read_b128 a[{lo}:{lo + 3}], {adr} offset:{nb * 32 * row_bytes}")
-    body.append("s_waitcnt lgkmcnt(0)")
+    if f8:
+        # fp8 rows of d bytes: per k-step (64 d) and query half, 32 bytes per
+        # lane from chunks at qb0 ^ 64 ks and that ^ 16
+        for ks in range(KS):
+            for jj in range(2):
+                x = 64 * ks + 16 * jj
+                adr = "%[qb0]" if x == 0 else f"v{KADR + jj}"
+                if x:
+                    body.append(f"v_xor_b32 {adr}, {x}, %[qb0]")
+                for nb in range(2):
+                    lo = QB + 16 * ks + 8 * nb + 4 * jj
+                    body.append(f"ds_read_b128 a[{lo}:{lo + 3}], {adr} offset:{nb * 32 * row_bytes}")
+            body.append("s_waitcnt lgkmcnt(0)")
+        nq = 16 * KS
+    else:
+        for ks in range(KS):
+            adr = "%[qb0]" if ks == 0 else f"v{KADR + (ks & 1)}"
+            if ks:
+                body.append(f"v_xor_b32 {adr}, {32 * ks}, %[qb0]")
+            for nb in range(2):
+                lo = QB + 8 * ks + 4 * nb
+                body.append(f"ds_read_b128 a[{lo}:{lo + 3}], {adr} offset:{nb * 32 * row_bytes}")
+        body.append("s_waitcnt lgkmcnt(0)")
+        nq = 8 * KS
     parts.append(asm_function(
-        f"// Q^T fragments of the wave's 64 queries into a[{QB}:{QB + 8 * KS - 1}]; qb0 is the "
+        f"// Q^T fragments of the wave's 64 queries into a[{QB}:{QB + nq - 1}]; qb0 is the "
         "k-step 0 fragment address",
         "load_q", ["uint32_t qb0"], body, [], ['[qb0] "v"(qb0)'],
-        [f"a{r}" for r in range(QB, QB + 8 * KS)] + [f"v{KADR}", f"v{KADR + 1}"]))
+        [f"a{r}" for r in range(QB, QB + nq)] + [f"v{KADR}", f"v{KADR + 1}"]))
 
     # rescale O: query half nb by alpha_nb (blocks (mb, nb))
     body = []
@@ -689,21 +769,25 @@ def _rename(lines, mapping):
     return out
 
 
-def _step_lines(d, variant, x, y, budget, dma=True):
-    st = Step(d, variant, x, y, budget, loop=True, dma=dma).build().fix_hazards()
+QA = {"A": "%[qa0]", "B": "%[qa1]"}   # fp8: q scale x k scale of the tile in buffer A / B
+
+
+def _step_lines(d, variant, x, y, budget, dma=True, f8=False):
+    st = Step(d, variant, x, y, budget, loop=True, dma=dma, f8=f8).build().fix_hazards()
     return _rename(st.out, {"%[mi0]": "%[m0]", "%[mi1]": "%[m1]", "%[mo0]": "%[m0]",
-                            "%[mo1]": "%[m1]", "%[lo0]": "%[ls0]", "%[lo1]": "%[ls1]"})
+                            "%[mo1]": "%[m1]", "%[lo0]": "%[ls0]", "%[lo1]": "%[ls1]",
+                            "%[qa]": QA[y]})
 
 
-def _vote_again_lines():
+def _vote_again_lines(f8=False, y="A"):
     """The vote once more on masked maxima (tm recomputed), m always updated
     when kept."""
     body = []
-    for ins in Step(128, "qk", "A", "A", 0, loop=True).vote_stream():
+    for ins in Step(128, "qk", "A", "A", 0, loop=True, f8=f8).vote_stream():
         body.append(ins.text.replace("s_andn2_b64 %[k0], %[keep], %[rare]", "s_mov_b64 %[k0], %[keep]"))
     # vote temporaries: a VALU write feeds v_permlane32_swap after 4 instructions
     return _rename(body, {"%[mi0]": "%[m0]", "%[mi1]": "%[m1]", "%[mo0]": "%[m0]",
-                          "%[mo1]": "%[m1]"})
+                          "%[mo1]": "%[m1]", "%[qa]": QA[y]})
 
 
 def _mask_lines(d, y):
@@ -752,9 +836,9 @@ def _rescale_lines(d):
 
 LOOP_ARGS = """// Operands of the key loop. Scalars are wave-uniform (SGPRs); krs / vrs are
 // raw buffer descriptors of the K and V head; mask_row is the skip-mask row
-// of this wave's query tile (0 when no mask is written).
+// of this wave's query tile (0 when no mask is written).{f8doc}
 struct LoopArgs {{
-  uint32_t frag, tr0, tr1, gk[{ipw}], gv[{ipw}];
+  uint32_t frag, tr0, tr1, gk[{ipwk}], gv[{ipwv}];
   int lim_base[2];
   float lazy;
   int nkb_wg, nkb_w, qb, N;
@@ -762,17 +846,29 @@ struct LoopArgs {{
   u32x4 krs, vrs;
   uint32_t wl, smem;
   uint64_t mask_row;
-  uint64_t val[2];
+  uint64_t val[2];{f8fields}
 }};
 """
+LOOP_ARGS_F8_DOC = """
+// fp8 QK^T: ksp points at the K tile scales of this KV head (one fp32 per
+// 64-key tile), sqv is this wave's Q tile scale, nkbm1 the last key tile,
+// wlv the wave's LDS base for V tile copies (wl: for K)."""
+LOOP_ARGS_F8_FIELDS = """
+  uint64_t ksp;
+  float sqv;
+  int nkbm1;
+  uint32_t wlv;"""
 
 
-def loop_cxx(d, causal, budget):
+def loop_cxx(d, causal, budget, f8=False):
     MB = d // 32
-    row_bytes = 2 * d
-    tile_bytes = 64 * row_bytes
-    stage_bytes = 2 * tile_bytes
-    ipw = 64 // (1024 // row_bytes) // 4
+    row_bytes = 2 * d                        # V rows (bf16)
+    krow = d if f8 else 2 * d                # K rows: fp8 codes or bf16
+    tile_k = 64 * krow
+    tile_v = 64 * row_bytes
+    stage_bytes = tile_k + tile_v
+    ipwk = tile_k // 1024 // 4               # copy instructions per wave and tile
+    ipwv = tile_v // 1024 // 4
     L = []
 
     def lab(name):
@@ -791,12 +887,16 @@ def loop_cxx(d, causal, budget):
                 "v_add_u32 %[kb0], %[t0], %[frag]"]
 
     def vaddr():   # %[vb0/1] = V^T read bases of tile kb
-        return slot_base("%[t0]", 0) + [f"s_add_u32 %[t0], %[t0], {tile_bytes}",
+        return slot_base("%[t0]", 0) + [f"s_add_u32 %[t0], %[t0], {tile_k}",
                 "v_add_u32 %[vb0], %[t0], %[tr0]", "v_add_u32 %[vb1], %[t0], %[tr1]"]
 
-    def nmc():
-        return ["v_mul_f32 %[nm0], %[mr0], %[c]", "v_mul_f32 %[nm1], %[mr1], %[c]",
-                "v_xor_b32 %[nm0], 0x80000000, %[nm0]", "v_xor_b32 %[nm1], 0x80000000, %[nm1]"]
+    def nmc(x):
+        out = ["v_mul_f32 %[nm0], %[mr0], %[c]", "v_mul_f32 %[nm1], %[mr1], %[c]",
+               "v_xor_b32 %[nm0], 0x80000000, %[nm0]", "v_xor_b32 %[nm1], 0x80000000, %[nm1]"]
+        if f8:
+            # the exponent input's multiplier for tile kb's code-unit scores
+            out.append(f"v_mul_f32 %[ce], {QA[x]}, %[c]")
+        return out
 
     def rare(kbn):  # %[rare] = all ones when tile kbn needs the mask
         out = [f"s_lshl_b32 %[t3], {kbn}, 6", "s_add_u32 %[t3], %[t3], 64",
@@ -810,7 +910,7 @@ def loop_cxx(d, causal, budget):
         out = ["s_cmp_lg_u64 %[rare], 0", f"s_cbranch_scc0 {lab('nm' + tag)}",
                f"s_lshl_b32 %[t0], {kbn}, 6",
                "v_subrev_u32 %[lim0], %[t0], %[L0]", "v_subrev_u32 %[lim1], %[t0], %[L1]"]
-        out += _mask_lines(d, y) + _vote_again_lines()
+        out += _mask_lines(d, y) + _vote_again_lines(f8, y)
         # skip-mask byte of tile kbn (0 kept, 1 skipped), written by lane 0
         out += [f"{lab('nm' + tag)}:",
                 "s_cmp_lg_u64 %[mptr], 0", f"s_cbranch_scc0 {lab('ns' + tag)}",
@@ -826,27 +926,54 @@ def loop_cxx(d, causal, budget):
         # %[t1] = byte offset of tile kb + 3, %[t2] = this wave's LDS base for
         # it. Its slot held tile kb - 2, which every wave finished before the
         # barrier at the top of this trip; a tile past the end only wastes
-        # the copy (zero-filled past N).
-        return slot_base("%[t2]", 3) + [
-                "s_sub_u32 %[t2], %[t2], %[smem]", "s_add_u32 %[t2], %[t2], %[wl]",
-                "s_add_u32 %[t1], %[kb], 3", f"s_mul_i32 %[t1], %[t1], {tile_bytes}"]
+        # the copy (zero-filled past N). fp8: K and V tiles differ in size,
+        # %[t4] / %[t5] are the V tile's offset and LDS base.
+        out = slot_base("%[t2]", 3) + ["s_sub_u32 %[t2], %[t2], %[smem]"]
+        if f8:
+            out += ["s_add_u32 %[t5], %[t2], %[wlv]",
+                    "s_add_u32 %[t4], %[kb], 3", f"s_mul_i32 %[t4], %[t4], {tile_v}"]
+        out += ["s_add_u32 %[t2], %[t2], %[wl]",
+                "s_add_u32 %[t1], %[kb], 3", f"s_mul_i32 %[t1], %[t1], {tile_k}"]
+        return out
 
     def dma_alone():
         out = []
-        for g in Step(d, "qk", "A", "A", 0, loop=True, dma=True).dma_groups():
+        for g in Step(d, "qk", "A", "A", 0, loop=True, dma=True, f8=f8).dma_groups():
             out += [i.text for i in g]
         return out
+
+    def kscale_next(y):
+        # fp8: the scale of tile kb + 1 (loaded a trip ago) into its buffer's
+        # A = q scale x k scale, and the load of tile kb + 3's (same buffer
+        # parity). Every LDS read is complete here, so lgkmcnt(0) only waits
+        # for that scalar load; an SMEM load in flight during the steps only
+        # makes their LDS waits stricter.
+        sk = "%[sk0]" if y == "A" else "%[sk1]"
+        return ["s_waitcnt lgkmcnt(0)",
+                f"v_mul_f32 {QA[y]}, %[sqv], {sk}",
+                "s_add_u32 %[t3], %[kb], 3", "s_min_u32 %[t3], %[t3], %[nkbm1]",
+                "s_lshl_b32 %[t3], %[t3], 2", "s_nop 0",
+                f"s_load_dword {sk}, %[ksp], %[t3]"]
 
     # -- init ------------------------------------------------------------
     L += ["v_mov_b32 %[m0], 0xff800000", "v_mov_b32 %[m1], 0xff800000",
           "v_mov_b32 %[mr0], 0xff800000", "v_mov_b32 %[mr1], 0xff800000",
           "v_mov_b32 %[ls0], 0", "v_mov_b32 %[ls1], 0",
           "s_mov_b32 %[kb], 0", "s_mov_b64 %[keep], 0", "s_mov_b64 %[grow], 0"]
+    if f8:
+        # scales of tiles 0 and 1; tile 0's A; then the load of tile 2's
+        L += ["s_load_dword %[sk0], %[ksp], 0x0",
+              "s_min_u32 %[t3], %[nkbm1], 1", "s_lshl_b32 %[t3], %[t3], 2",
+              "s_load_dword %[sk1], %[ksp], %[t3]",
+              "s_waitcnt lgkmcnt(0)",
+              "v_mul_f32 %[qa0], %[sqv], %[sk0]",
+              "s_min_u32 %[t3], %[nkbm1], 2", "s_lshl_b32 %[t3], %[t3], 2", "s_nop 0",
+              "s_load_dword %[sk0], %[ksp], %[t3]"]
     # tile 0 scored into buffer A and voted on
     L += ["s_cmp_gt_i32 %[nkbw], 0", f"s_cbranch_scc0 {lab('loop')}"]
     L += ["s_mov_b32 %[t0], %[smem]", "v_add_u32 %[kb0], %[t0], %[frag]"]
     L += rare("0")
-    L += _step_lines(d, "qk", "A", "A", budget, dma=False)
+    L += _step_lines(d, "qk", "A", "A", budget, dma=False, f8=f8)
     L += after_vote("0", "A", "p0")
     L += [f"{lab('loop')}:"]
     for x, y in (("A", "B"), ("B", "A")):
@@ -857,17 +984,19 @@ def loop_cxx(d, causal, budget):
             # (tiles kb + 1, kb + 2), and every wave is past the previous
             # trip, so the slots of tiles kb - 2, kb - 1 are free
             L += ["s_waitcnt vmcnt(0)", "s_barrier"]
-        L += dma_target() + [f"{lab('cp' + t)}:",
-              "s_add_u32 %[t0], %[kb], 1", "s_cmp_lt_i32 %[t0], %[nkbw]",
+        L += dma_target() + [f"{lab('cp' + t)}:"]
+        if f8:
+            L += kscale_next(y)
+        L += ["s_add_u32 %[t0], %[kb], 1", "s_cmp_lt_i32 %[t0], %[nkbw]",
               f"s_cbranch_scc0 {lab('last' + t)}"]
         L += kaddr() + ["s_add_u32 %[t0], %[kb], 1"] + rare("%[t0]")
         L += ["s_cmp_lg_u64 %[keep], 0", f"s_cbranch_scc0 {lab('skip' + t)}",
               "s_cmp_lg_u64 %[grow], 0", f"s_cbranch_scc0 {lab('nr' + t)}"]
         L += _rescale_lines(d)
-        L += [f"{lab('nr' + t)}:"] + nmc() + vaddr()
-        L += _step_lines(d, "full", x, y, budget)
+        L += [f"{lab('nr' + t)}:"] + nmc(x) + vaddr()
+        L += _step_lines(d, "full", x, y, budget, f8=f8)
         L += [f"s_branch {lab('voted' + t)}", f"{lab('skip' + t)}:"]
-        L += _step_lines(d, "qk", y, y, budget)
+        L += _step_lines(d, "qk", y, y, budget, f8=f8)
         L += [f"{lab('voted' + t)}:", "s_add_u32 %[t1], %[kb], 1"]
         L += after_vote("%[t1]", y, t)
         L += [f"s_branch {lab('end' + t)}",
@@ -875,8 +1004,8 @@ def loop_cxx(d, causal, budget):
               "s_cmp_lg_u64 %[keep], 0", f"s_cbranch_scc0 {lab('idle' + t)}",
               "s_cmp_lg_u64 %[grow], 0", f"s_cbranch_scc0 {lab('nrl' + t)}"]
         L += _rescale_lines(d)
-        L += [f"{lab('nrl' + t)}:"] + nmc() + vaddr()
-        L += _step_lines(d, "pv", x, x, budget)
+        L += [f"{lab('nrl' + t)}:"] + nmc(x) + vaddr()
+        L += _step_lines(d, "pv", x, x, budget, f8=f8)
         L += [f"s_branch {lab('ld' + t)}", f"{lab('idle' + t)}:"]
         L += dma_alone()
         L += [f"{lab('ld' + t)}:", "s_mov_b64 %[keep], 0",
@@ -884,6 +1013,8 @@ def loop_cxx(d, causal, budget):
               "s_add_u32 %[kb], %[kb], 1",
               "s_cmp_lt_i32 %[kb], %[nkbwg]", f"s_cbranch_scc0 {lab('done')}"]
     L += [f"s_branch {lab('loop')}", f"{lab('done')}:", "s_waitcnt vmcnt(0)"]
+    if f8:
+        L += ["s_waitcnt lgkmcnt(0)"]     # no scalar load may land after the block
 
 
     outs = ['[m0] "=&v"(m[0])', '[m1] "=&v"(m[1])', '[mr0] "=&v"(mref[0])', '[mr1] "=&v"(mref[1])',
@@ -898,12 +1029,19 @@ def loop_cxx(d, causal, budget):
             '[k1] "=&s"(s64[3])', '[rare] "=&s"(s64[4])', '[sx] "=&s"(s64[5])']
     ins_ = ['[frag] "v"(a.frag)', '[tr0] "v"(a.tr0)', '[tr1] "v"(a.tr1)',
             '[L0] "v"(a.lim_base[0])', '[L1] "v"(a.lim_base[1])', '[lazy] "v"(a.lazy)']
-    ins_ += [f'[gk{i}] "v"(a.gk[{i}])' for i in range(ipw)]
-    ins_ += [f'[gv{i}] "v"(a.gv[{i}])' for i in range(ipw)]
+    ins_ += [f'[gk{i}] "v"(a.gk[{i}])' for i in range(ipwk)]
+    ins_ += [f'[gv{i}] "v"(a.gv[{i}])' for i in range(ipwv)]
     ins_ += ['[nkbwg] "s"(a.nkb_wg)', '[nkbw] "s"(a.nkb_w)', '[qb] "s"(a.qb)', '[N] "s"(a.N)',
              '[tau] "s"(a.tau)', '[c] "s"(a.c)', '[krs] "s"(a.krs)', '[vrs] "s"(a.vrs)',
              '[wl] "s"(a.wl)', '[smem] "s"(a.smem)', '[mptr] "s"(a.mask_row)',
              '[val0] "s"(a.val[0])', '[val1] "s"(a.val[1])']
+    nvt, ns32 = 11, 8
+    if f8:
+        outs += ['[qa0] "=&v"(vtmp[11])', '[qa1] "=&v"(vtmp[12])', '[ce] "=&v"(vtmp[13])',
+                 '[sk0] "=&s"(s32[1])', '[sk1] "=&s"(s32[2])', '[t4] "=&s"(s32[3])',
+                 '[t5] "=&s"(s32[8])']
+        ins_ += ['[ksp] "s"(a.ksp)', '[sqv] "v"(a.sqv)', '[nkbm1] "s"(a.nkbm1)', '[wlv] "s"(a.wlv)']
+        nvt, ns32 = 14, 9
     clob = [f"v{r}" for r in range(VOTE, 256)]
     clob += [f"a{r}" for r in range(OB, OB + 32 * MB)] + ["vcc", "scc", "m0"]
     body = []
@@ -911,15 +1049,15 @@ def loop_cxx(d, causal, budget):
         body.append(t)
     # %[mpp] is the 64-bit pair (mp, mp_hi): spelled out below
     text = "\n".join(f'      "{t}\\n\\t"' for t in body)
-    head = (f"// The key loop of one wave, d = {d}, {'causal' if causal else 'full'} attention "
-            f"({len(body)} lines)")
+    head = (f"// The key loop of one wave, d = {d}, {'causal' if causal else 'full'} attention"
+            f"{', QK^T on fp8 codes' if f8 else ''} ({len(body)} lines)")
     name = f"key_loop_{'causal' if causal else 'full'}"
     return "\n".join([
         head,
         f"__device__ __forceinline__ void {name}(const LoopArgs& a, float (&m)[2], float (&mref)[2], "
         "float (&lsum)[2]) {",
-        "  float vtmp[11];",
-        "  uint32_t s32[8];",
+        f"  float vtmp[{nvt}];",
+        f"  uint32_t s32[{ns32}];",
         "  uint64_t s64[6];",
         "  asm volatile(",
         text,
@@ -936,17 +1074,22 @@ def main(out_path=None):
              "// Per-key-tile steps of the prefill kernel (see the script's docstring for",
              "// the schedule, the register plan and the hazard rules).",
              "#pragma once", ""]
-    for d, budget in ((128, 26.0), (64, 30.0)):
-        parts.append(f"namespace d{d} {{")
-        for h in helpers_cxx(d):
+    for d, budget, f8 in ((128, 26.0, False), (64, 30.0, False), (128, 26.0, True),
+                          (64, 30.0, True)):
+        ns = f"d{d}f8" if f8 else f"d{d}"
+        parts.append(f"namespace {ns} {{")
+        for h in helpers_cxx(d, f8):
             parts.append(h)
             parts.append("")
-        ipw = 64 // (1024 // (2 * d)) // 4
-        parts.append(LOOP_ARGS.format(ipw=ipw))
+        ipwv = 64 * 2 * d // 1024 // 4
+        ipwk = 64 * d // 1024 // 4 if f8 else ipwv
+        parts.append(LOOP_ARGS.format(ipwk=ipwk, ipwv=ipwv,
+                                      f8doc=LOOP_ARGS_F8_DOC if f8 else "",
+                                      f8fields=LOOP_ARGS_F8_FIELDS if f8 else ""))
         for causal in (True, False):
-            parts.append(loop_cxx(d, causal, budget))
+            parts.append(loop_cxx(d, causal, budget, f8))
             parts.append("")
-        parts.append(f"}}  // namespace d{d}")
+        parts.append(f"}}  // namespace {ns}")
         parts.append("")
     with open(out_path or os.path.join(here, "prefill_steps.inc"), "w") as f:
         f.write("\n".join(parts))

@@ -20,6 +20,11 @@ struct PrefillArgs {
   float tau_raw;  // tau * sqrt(d): threshold in raw q.k units (+inf = dense)
   float c;        // log2(e) / sqrt(d)
   void* stream;
+  // fp8 QK^T: q and k are E4M3 codes (uint8, same shapes) with per-tile
+  // scales qscale [B, Hq, ceil(Nq/64)], kscale [B, Hkv, ceil(cap/64)];
+  // both null for bf16 q and k
+  const float* qscale = nullptr;
+  const float* kscale = nullptr;
 };
 
 struct DecodeArgs {
@@ -79,6 +84,11 @@ int launch_decode_q4(const DecodeQ4Args& a);
 // The 2-bit cache (layout in kvq2.hip) takes the same arguments.
 int launch_kv_quantize_q2(const QuantArgs& a);
 int launch_decode_q2(const DecodeQ4Args& a);
+// Block-quantised fp8 (E4M3) codes of a bf16 tensor [X, N, D]: codes uint8
+// [X, N, D] and one fp32 scale per 64-row block, scales [X, ceil(N/64)]
+// (fp8.hip). Returns nonzero if the grid cannot be expressed.
+int launch_quantize_fp8(const void* x, uint8_t* codes, float* scales, long long X, int N, int D,
+                        void* stream);
 // Bytes of the device-resident decode scratch (decode.hip), and its address
 // on the current device (0 on success; the first call on a device looks it
 // up with that device current).

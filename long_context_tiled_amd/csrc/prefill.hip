@@ -61,13 +61,20 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr uint32_t kBufferCfg = 0x00020000u;  // raw 32-bit buffer, range-checked
 
-template <int D>
+// Tile geometry: V rows are bf16 (2 D bytes); K and Q rows are bf16 too, or
+// fp8 codes (D bytes) when QK^T runs on 8-bit operands.
+template <int D, bool F8>
 struct PrefillTile {
-  static constexpr int rowBytes = 2 * D;
-  static constexpr int chunks = D / 8;               // 16-byte chunks per row
-  static constexpr int bytes = kTile * rowBytes;      // one K or V tile
+  static constexpr int rowBytes = 2 * D;              // V
+  static constexpr int chunks = rowBytes / 16;        // 16-byte chunks per V row
+  static constexpr int bytes = kTile * rowBytes;      // one V tile
   static constexpr int rowsPerInstr = 1024 / rowBytes;
   static constexpr int instrPerWave = kTile / rowsPerInstr / 4;
+  static constexpr int kRowBytes = F8 ? D : 2 * D;    // K and Q
+  static constexpr int kChunks = kRowBytes / 16;
+  static constexpr int kBytes = kTile * kRowBytes;    // one K (or Q) tile
+  static constexpr int kRowsPerInstr = 1024 / kRowBytes;
+  static constexpr int kInstrPerWave = kTile / kRowsPerInstr / 4;
 };
 
 // Tiles sit in LDS unpadded; the 16-byte chunk c of row r is stored at
@@ -83,9 +90,16 @@ struct PrefillTile {
 //   quads: g = 4 (r & 3) for d = 128, g = 4 ((r >> 1) & 1) for d = 64.
 // XOR by g keeps chunk blocks 4 mb aligned, so the V^T address of block mb
 // is that of block 0 XOR 64 mb.
+// The K / Q swizzle by row size in bytes: 256-byte rows (bf16, d = 128),
+// 128-byte rows (bf16 d = 64, fp8 d = 128) and 64-byte rows (fp8 d = 64),
+// one-to-one on the rows that share a 16-lane read.
+template <int RB>
+__device__ __forceinline__ int swz_row(int r) {
+  return RB == 256 ? (r & 15) : RB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+}
 template <int D>
 __device__ __forceinline__ int swz_k(int r) {
-  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+  return swz_row<2 * D>(r);
 }
 template <int D>
 __device__ __forceinline__ int swz_v(int r) {
@@ -136,18 +150,35 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, lds_void* lds, 
 #include "prefill_steps.inc"
 #pragma clang diagnostic pop
 
-// Calls the d = 128 or d = 64 version of a generated block.
-#define SKA_CALL(D_, fn, ...)                \
-  do {                                       \
-    if constexpr ((D_) == 128) d128::fn(__VA_ARGS__); \
-    else d64::fn(__VA_ARGS__);               \
+// Calls the d = 128 or d = 64 version of a generated block (bf16 QK^T, or
+// fp8 QK^T when F8_ is set).
+#define SKA_CALL(D_, F8_, fn, ...)                                  \
+  do {                                                              \
+    if constexpr ((D_) == 128 && !(F8_)) d128::fn(__VA_ARGS__);     \
+    else if constexpr ((D_) == 64 && !(F8_)) d64::fn(__VA_ARGS__);  \
+    else if constexpr ((D_) == 128) d128f8::fn(__VA_ARGS__);        \
+    else d64f8::fn(__VA_ARGS__);                                    \
   } while (0)
 
-template <int D, bool CAUSAL, int HPW, int STAGES, bool CHUNK>
+template <int D, bool F8>
+struct LoopArgsOf;
+template <> struct LoopArgsOf<128, false> { using type = d128::LoopArgs; };
+template <> struct LoopArgsOf<64, false> { using type = d64::LoopArgs; };
+template <> struct LoopArgsOf<128, true> { using type = d128f8::LoopArgs; };
+template <> struct LoopArgsOf<64, true> { using type = d64f8::LoopArgs; };
+
+// F8: Q and K are fp8 (E4M3) codes with one fp32 scale per 64-row Q tile
+// (qsc, [B, Hq, ceil(Nq/64)]) and per 64-key K tile (ksc, [B, Hkv,
+// ceil(cap/64)]); S^T = K . Q^T runs on v_mfma_f32_32x32x64_f8f6f4 in code
+// units and each tile's scores are scaled by q scale x k scale where they
+// are used (the skip test's tile maxima and the exponent input). V and PV
+// stay bf16.
+template <int D, bool CAUSAL, int HPW, int STAGES, bool CHUNK, bool F8>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void prefill_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ o,
-    float* __restrict__ lse, uint8_t* __restrict__ mask, int Hq, int Hkv,
+    float* __restrict__ lse, uint8_t* __restrict__ mask, const float* __restrict__ qsc,
+    const float* __restrict__ ksc, int Hq, int Hkv,
     int Nq_arg, int N, int q0t_arg, int cap_arg, float tau_raw, float c, int nqg, int ny) {
   // Nq queries (the chunk) at key positions 64 q0t .. 64 q0t + Nq - 1 of N
   // keys: query tile qb of the chunk is tile qb + q0t of the key axis. The
@@ -159,11 +190,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
   const int cap = CHUNK ? cap_arg : N;  // rows allocated per K/V head
   constexpr int QPW = 4 / HPW;   // query tiles per workgroup
   constexpr int MB = D / 32;     // 32-row d blocks of O^T
-  using T = PrefillTile<D>;
-  constexpr int STAGE_BYTES = 2 * T::bytes;
+  using T = PrefillTile<D, F8>;
+  constexpr int KRB = T::kRowBytes;
+  constexpr int STAGE_BYTES = T::kBytes + T::bytes;  // K tile then V tile
   // STAGES K/V slots, tile t in slot t % STAGES. The four Q tiles are
   // staged in slots 3-4 before the loop.
-  static_assert(STAGES == 5 && 4 * T::bytes == 2 * STAGE_BYTES, "slot plan");
+  static_assert(STAGES == 5 && 4 * T::kBytes <= 2 * STAGE_BYTES, "slot plan");
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
   typedef __attribute__((address_space(3))) char lds_char;
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_char*)smem;  // LDS byte address
@@ -191,64 +223,75 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
   const int nkb_wg = CAUSAL ? min(nkb, qg * QPW + QPW + q0t) : nkb;
   const int nkb_w = wave_valid ? (CAUSAL ? qbg + 1 : nkb) : 0;
 
-  const int head_bytes = N * D * 2;
-  const size_t kv_off = (size_t)(b * Hkv + g) * cap * D;
+  const int k_head_bytes = N * KRB;
+  const int v_head_bytes = N * D * 2;
+  const size_t kv_row0 = (size_t)(b * Hkv + g) * cap;  // first row of the head's K/V
+  const uint8_t* kh = k + kv_row0 * KRB;
+  const uint16_t* vh = v + kv_row0 * D;
   const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(k + kv_off), (short)0, head_bytes, kBufferCfg);
+      __builtin_amdgcn_make_buffer_rsrc((void*)kh, (short)0, k_head_bytes, kBufferCfg);
   const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(v + kv_off), (short)0, head_bytes, kBufferCfg);
+      __builtin_amdgcn_make_buffer_rsrc((void*)vh, (short)0, v_head_bytes, kBufferCfg);
   const size_t bh = (size_t)b * Hq + h;
-  const __amdgpu_buffer_rsrc_t qrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(q + bh * Nq * D), (short)0, Nq * D * 2, kBufferCfg);
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(q + bh * Nq * KRB), (short)0, Nq * KRB, kBufferCfg);
 
   // Per-lane load geometry for the direct-to-LDS copies: instruction i of
-  // wave w fills LDS bytes [1024 (w * IPW + i), +1024) of the tile.
+  // wave w fills LDS bytes [1024 (w * IPW + i), +1024) of the tile (K and V
+  // tiles each; their instruction counts differ when K is fp8).
   constexpr int IPW = T::instrPerWave;
-  int ld_gk[IPW], ld_gv[IPW];  // global byte offsets within the head, relative to key 0
+  constexpr int KIPW = T::kInstrPerWave;
+  int ld_gk[KIPW], ld_gv[IPW];  // global byte offsets within the head, relative to key 0
+#pragma unroll
+  for (int i = 0; i < KIPW; ++i) {
+    const int r = (wave * KIPW + i) * T::kRowsPerInstr + lane / T::kChunks;
+    const int slot = lane % T::kChunks;
+    ld_gk[i] = r * KRB + 16 * (slot ^ swz_row<KRB>(r));
+  }
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
     const int r = (wave * IPW + i) * T::rowsPerInstr + lane / T::chunks;
     const int slot = lane % T::chunks;
-    ld_gk[i] = r * T::rowBytes + 16 * (slot ^ swz_k<D>(r));
     ld_gv[i] = r * T::rowBytes + 16 * (slot ^ swz_v<D>(r));
   }
 
   auto issue_tile = [&](int kb) __attribute__((always_inline)) {
     char* st = smem + (kb % STAGES) * STAGE_BYTES;
-    const int base = kb * kTile * T::rowBytes;
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      lds_void* dk = (lds_void*)(st + 1024 * (wave * IPW + i));
-      dma16(krs, dk, base + ld_gk[i]);
+    for (int i = 0; i < KIPW; ++i) {
+      lds_void* dk = (lds_void*)(st + 1024 * (wave * KIPW + i));
+      dma16(krs, dk, kb * T::kBytes + ld_gk[i]);
     }
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-      lds_void* dv = (lds_void*)(st + T::bytes + 1024 * (wave * IPW + i));
-      dma16(vrs, dv, base + ld_gv[i]);
+      lds_void* dv = (lds_void*)(st + T::kBytes + 1024 * (wave * IPW + i));
+      dma16(vrs, dv, kb * T::bytes + ld_gv[i]);
     }
   };
 
   // The wave's 64 query rows go to its own swizzled LDS tile once (rows past
   // N read as zero), and from there into AGPRs.
-  const uint32_t q_lds = (uint32_t)(3 * STAGE_BYTES + wave * T::bytes);
+  const uint32_t q_lds = (uint32_t)(3 * STAGE_BYTES + wave * T::kBytes);
   if (wave_valid) {
-    constexpr int QI = T::bytes / 1024;  // 1 KB copy instructions per Q tile
+    constexpr int QI = T::kBytes / 1024;  // 1 KB copy instructions per Q tile
 #pragma unroll
     for (int i = 0; i < QI; ++i) {
-      const int r = i * T::rowsPerInstr + lane / T::chunks;
-      const int slot = lane % T::chunks;
-      const int cc = slot ^ swz_k<D>(r);
-      dma16(qrs, (lds_void*)(smem + q_lds + 1024 * i), (qb * kTile + r) * T::rowBytes + cc * 16);
+      const int r = i * T::kRowsPerInstr + lane / T::kChunks;
+      const int slot = lane % T::kChunks;
+      const int cc = slot ^ swz_row<KRB>(r);
+      dma16(qrs, (lds_void*)(smem + q_lds + 1024 * i), (qb * kTile + r) * KRB + cc * 16);
     }
   }
 
   // K / Q fragment reads (A / B operands of S^T = K . Q^T): lane l reads row
-  // (32 a + l32) of a swizzled tile, 16-byte chunk 2 ks + hh. With rows 32
-  // apart sharing the swizzle, the second row half is the immediate offset
-  // 32 rowBytes, and the chunk XOR (2 ks + hh) ^ g moves only address bits
-  // 4..7 (bits below the row): the k-step ks address is frag ^ (32 ks) for a
-  // 1 KB-aligned tile base.
-  const uint32_t frag = (uint32_t)(l32 * T::rowBytes + 16 * (hh ^ swz_k<D>(l32)));
+  // (32 a + l32) of a swizzled tile. bf16: 16-byte chunk 2 ks + hh; fp8: the
+  // chunks 4 ks + 2 hh and 4 ks + 2 hh + 1. With rows 32 apart sharing the
+  // swizzle, the second row half is an immediate offset, and the chunk XOR
+  // moves only address bits below the row: the k-step address is frag ^
+  // (32 ks) (bf16) or frag ^ (64 ks) with the second chunk at ^ 16 (fp8),
+  // for a 1 KB-aligned tile base.
+  const uint32_t frag =
+      (uint32_t)(l32 * KRB + 16 * ((F8 ? 2 * hh : hh) ^ swz_row<KRB>(l32)));
 
   // ds_read_b64_tr_b16 geometry for the V^T operand: lane k of a 16-lane
   // group fetches 4 consecutive d of key row (16 ks + key_base + k / 4); the
@@ -266,27 +309,26 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
   }
 
   // Prologue: Q tiles (slots 3-4) and K/V tiles 0-2 copied; Q^T into AGPRs.
-  SKA_CALL(D, zero_o);
+  SKA_CALL(D, F8, zero_o);
   for (int t = 0; t < 3; ++t)
     if (t < nkb_wg) issue_tile(t);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  if (0 < nkb_w) SKA_CALL(D, load_q, smem_lds + q_lds + frag);
+  if (0 < nkb_w) SKA_CALL(D, F8, load_q, smem_lds + q_lds + frag);
   __syncthreads();  // slots 3-4 are K/V slots from here on
 
   // The key loop runs as one generated block (barriers, tile copies, the
   // pipelined steps, votes, rescales, masks). Its scalar operands must be
   // wave-uniform.
   const float lazy_raw = 8.0f / c;  // 8 in log2 units, as a raw-score gap
-  typename std::conditional<D == 128, d128::LoopArgs, d64::LoopArgs>::type la;
+  typename LoopArgsOf<D, F8>::type la;
   la.frag = frag;
   la.tr0 = tr0[0];
   la.tr1 = tr0[1];
 #pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    la.gk[i] = (uint32_t)ld_gk[i];
-    la.gv[i] = (uint32_t)ld_gv[i];
-  }
+  for (int i = 0; i < KIPW; ++i) la.gk[i] = (uint32_t)ld_gk[i];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) la.gv[i] = (uint32_t)ld_gv[i];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int qrow = qb * kTile + nb * 32 + l32;  // row within the chunk
@@ -302,23 +344,30 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
   la.N = N;
   la.tau = tau_raw;
   la.c = c;
-  auto rsrc = [&](const uint16_t* p) {
+  auto rsrc = [&](const void* p, int bytes) {
     const uint64_t a = (uint64_t)(uintptr_t)p;
     u32x4 r;
     r[0] = (uint32_t)a;
     r[1] = (uint32_t)(a >> 32) & 0xffffu;  // stride 0
-    r[2] = (uint32_t)head_bytes;
+    r[2] = (uint32_t)bytes;
     r[3] = kBufferCfg;
     return r;
   };
-  la.krs = rsrc(k + kv_off);
-  la.vrs = rsrc(v + kv_off);
-  la.wl = smem_lds + (uint32_t)(wave * IPW * 1024);
+  la.krs = rsrc(kh, k_head_bytes);
+  la.vrs = rsrc(vh, v_head_bytes);
+  la.wl = smem_lds + (uint32_t)(wave * KIPW * 1024);
   la.smem = smem_lds;
   la.mask_row = mask != nullptr ? (uint64_t)(uintptr_t)(mask + (bh * nqb + qb) * nkb) : 0ull;
+  if constexpr (F8) {
+    const int nkbc = (cap + kTile - 1) / kTile;  // K scales per head
+    la.ksp = (uint64_t)(uintptr_t)(ksc + (size_t)(b * Hkv + g) * nkbc);
+    la.sqv = wave_valid ? qsc[bh * nqb + qb] : 1.f;
+    la.nkbm1 = nkb - 1;
+    la.wlv = smem_lds + (uint32_t)(T::kBytes + wave * IPW * 1024);
+  }
   float m[2], mref[2], lsum[2];
-  if constexpr (CAUSAL) SKA_CALL(D, key_loop_causal, la, m, mref, lsum);
-  else SKA_CALL(D, key_loop_full, la, m, mref, lsum);
+  if constexpr (CAUSAL) SKA_CALL(D, F8, key_loop_causal, la, m, mref, lsum);
+  else SKA_CALL(D, F8, key_loop_full, la, m, mref, lsum);
   (void)m;
 
   if (!wave_valid) return;
@@ -334,15 +383,20 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
     for (int mb = 0; mb < MB; ++mb) {
       float ov[16];
       const int id = 2 * mb + nb;
-      if (id == 0) SKA_CALL(D, read_o_00, ov);
-      if (id == 1) SKA_CALL(D, read_o_01, ov);
-      if (id == 2) SKA_CALL(D, read_o_10, ov);
-      if (id == 3) SKA_CALL(D, read_o_11, ov);
-      if constexpr (MB == 4) {
+      if (id == 0) SKA_CALL(D, F8, read_o_00, ov);
+      if (id == 1) SKA_CALL(D, F8, read_o_01, ov);
+      if (id == 2) SKA_CALL(D, F8, read_o_10, ov);
+      if (id == 3) SKA_CALL(D, F8, read_o_11, ov);
+      if constexpr (MB == 4 && !F8) {
         if (id == 4) d128::read_o_20(ov);
         if (id == 5) d128::read_o_21(ov);
         if (id == 6) d128::read_o_30(ov);
         if (id == 7) d128::read_o_31(ov);
+      } else if constexpr (MB == 4) {
+        if (id == 4) d128f8::read_o_20(ov);
+        if (id == 5) d128f8::read_o_21(ov);
+        if (id == 6) d128f8::read_o_30(ov);
+        if (id == 7) d128f8::read_o_31(ov);
       }
       if (row < Nq) {
         float* orow = o + (bh * Nq + row) * D;
@@ -365,7 +419,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
 
 constexpr int kStages = 5;
 
-template <int D, bool CAUSAL, int HPW, bool CHUNK>
+template <int D, bool CAUSAL, int HPW, bool CHUNK, bool F8>
 static int launch_one(const PrefillArgs& a) {
   const int nqb = (a.Nq + kTile - 1) / kTile;
   constexpr int QPW = 4 / HPW;
@@ -374,30 +428,35 @@ static int launch_one(const PrefillArgs& a) {
   const int ny = a.B * a.Hkv * (G / HPW);
   const long long blocks = (long long)nqg * ny;
   if (blocks > 0x7fffffffLL) return -1;
-  hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, HPW, kStages, CHUNK>), dim3((unsigned)blocks), dim3(256),
-                     0, (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                     (const uint16_t*)a.v, a.o, a.lse, a.mask, a.Hq, a.Hkv, a.Nq, a.N, a.q0t, a.cap,
-                     a.tau_raw, a.c, nqg, ny);
+  hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, HPW, kStages, CHUNK, F8>), dim3((unsigned)blocks),
+                     dim3(256), 0, (hipStream_t)a.stream, (const uint8_t*)a.q, (const uint8_t*)a.k,
+                     (const uint16_t*)a.v, a.o, a.lse, a.mask, a.qscale, a.kscale, a.Hq, a.Hkv,
+                     a.Nq, a.N, a.q0t, a.cap, a.tau_raw, a.c, nqg, ny);
   return 0;
 }
 
-template <int D, bool CAUSAL, bool CHUNK>
+template <int D, bool CAUSAL, bool CHUNK, bool F8>
 static int launch_g(const PrefillArgs& a) {
   const int G = a.Hq / a.Hkv;
-  if (G % 4 == 0) return launch_one<D, CAUSAL, 4, CHUNK>(a);
-  if (G % 2 == 0) return launch_one<D, CAUSAL, 2, CHUNK>(a);
-  return launch_one<D, CAUSAL, 1, CHUNK>(a);
+  if (G % 4 == 0) return launch_one<D, CAUSAL, 4, CHUNK, F8>(a);
+  if (G % 2 == 0) return launch_one<D, CAUSAL, 2, CHUNK, F8>(a);
+  return launch_one<D, CAUSAL, 1, CHUNK, F8>(a);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F8>
 static int launch_h(const PrefillArgs& a) {
-  if (a.Nq != a.N || a.q0t != 0 || a.cap != a.N) return launch_g<D, CAUSAL, true>(a);
-  return launch_g<D, CAUSAL, false>(a);
+  if (a.Nq != a.N || a.q0t != 0 || a.cap != a.N) return launch_g<D, CAUSAL, true, F8>(a);
+  return launch_g<D, CAUSAL, false, F8>(a);
+}
+
+template <bool F8>
+static int launch_f(const PrefillArgs& a) {
+  if (a.d == 128) return a.causal ? launch_h<128, true, F8>(a) : launch_h<128, false, F8>(a);
+  return a.causal ? launch_h<64, true, F8>(a) : launch_h<64, false, F8>(a);
 }
 
 int launch_prefill(const PrefillArgs& a) {
-  if (a.d == 128) return a.causal ? launch_h<128, true>(a) : launch_h<128, false>(a);
-  return a.causal ? launch_h<64, true>(a) : launch_h<64, false>(a);
+  return a.qscale != nullptr ? launch_f<true>(a) : launch_f<false>(a);
 }
 
 }  // namespace skipattn

@@ -76,10 +76,13 @@ def _compare_decisions(gpu_dec, ref_dec, margin, visited):
 class PrefillChecker:
     """Caches fp64 copies of K/V per (b, kv head) for repeated block checks."""
 
-    def __init__(self, q_bits, k_bits, v_bits, causal: bool, q0: int = 0):
+    def __init__(self, q_bits, k_bits, v_bits, causal: bool, q0: int = 0, qf=None, kf=None):
         """q_bits may be a chunk: its row r sits at key position q0 + r
-        (q0 a multiple of 64 when causal)."""
+        (q0 a multiple of 64 when causal). ``qf`` / ``kf``, fp64 arrays of
+        the same shapes, replace the bf16 Q / K values (e.g. the oracle's
+        dequantised 8-bit Q and K)."""
         self.q, self.k, self.v = q_bits, k_bits, v_bits
+        self.qf, self.kf = qf, kf
         self.causal = causal
         B, Hq, N, d = q_bits.shape
         self.B, self.Hq, self.N, self.d = B, Hq, N, d
@@ -94,16 +97,21 @@ class PrefillChecker:
         if key not in self._kv:
             if len(self._kv) > 2:
                 self._kv.clear()
-            self._kv[key] = (synth.bf16_bits_to_f64(self.k[b, g]),
-                             synth.bf16_bits_to_f64(self.v[b, g]))
+            kk = self.kf[b, g] if self.kf is not None else synth.bf16_bits_to_f64(self.k[b, g])
+            self._kv[key] = (kk, synth.bf16_bits_to_f64(self.v[b, g]))
         return self._kv[key]
+
+    def qrows(self, b, h, r0, r1):
+        if self.qf is not None:
+            return np.asarray(self.qf[b, h, r0:r1], np.float64)
+        return synth.bf16_bits_to_f64(self.q[b, h, r0:r1])
 
     def check_block(self, b, h, qb, tau, o_gpu, lse_gpu, mask_gpu) -> Report:
         """o_gpu/lse_gpu: numpy rows of this block; mask_gpu: (nt,) uint8."""
         rep = Report()
         k, v = self.kv(b, h // self.G)
         r0, r1 = qb * 64, min(self.N, qb * 64 + 64)
-        qrows = synth.bf16_bits_to_f64(self.q[b, h, r0:r1])
+        qrows = self.qrows(b, h, r0, r1)
         o, lse, dec, margin = oracle.prefill_blocks(qrows, k, v, qb + self.q0t, self.causal, tau)
         dec, margin = dec[0], margin[0]
         visited = dec != oracle.NOT_VISITED
@@ -134,7 +142,7 @@ class PrefillChecker:
         rep = Report()
         k, v = self.kv(b, h // self.G)
         r0, r1 = qb0 * 64, min(self.N, qb1 * 64)
-        qrows = synth.bf16_bits_to_f64(self.q[b, h, r0:r1])
+        qrows = self.qrows(b, h, r0, r1)
         o, lse, dec, margin = oracle.prefill_blocks(qrows, k, v, qb0 + self.q0t, self.causal, tau)
         visited = dec != oracle.NOT_VISITED
         if not np.array_equal(mask_gpu[~visited], dec[~visited]):
@@ -158,10 +166,11 @@ class PrefillChecker:
 
 
 def check_prefill(q_bits, k_bits, v_bits, causal, tau, o, lse, mask, blocks=None,
-                  q0: int = 0) -> Report:
+                  q0: int = 0, qf=None, kf=None) -> Report:
     """Compare full GPU outputs (numpy) over the given (b, h, qb) blocks
-    (q_bits and the outputs may be a chunk starting at key position q0)."""
-    chk = PrefillChecker(q_bits, k_bits, v_bits, causal, q0)
+    (q_bits and the outputs may be a chunk starting at key position q0;
+    qf / kf as for PrefillChecker)."""
+    chk = PrefillChecker(q_bits, k_bits, v_bits, causal, q0, qf, kf)
     if blocks is None:
         blocks = [(b, h, qb) for b in range(chk.B) for h in range(chk.Hq)
                   for qb in range(chk.nt)]

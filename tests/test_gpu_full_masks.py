@@ -184,3 +184,59 @@ def test_prefill_one_whole_head_masks(name, h):
               f"ambiguous={amb} hard_mismatch={hard}", flush=True)
         assert tiles == nt * (nt + 1) // 2
         assert hard == 0, bad
+
+
+def test_prefill_8k_qk8_every_block():
+    # the 8-bit QK^T prefill over every query block of prefill_8k at every
+    # tau, against the oracle on the dequantised Q and K
+    import torch
+    import long_context_tiled_amd as lib
+    from oracle import fp8
+    cfg = synth.workload("prefill_8k")
+    print("[full] generating prefill_8k (qk8)", flush=True)
+    q, k, v = synth.make_prefill(cfg)
+    dq, dk, dv = _dev(q), _dev(k), _dev(v)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    nt = (N + 63) // 64
+    ws = torch.empty(lib.attn_prefill_qk8_workspace_bytes(B, Hq, Hkv, N, d), dtype=torch.uint8,
+                     device="cuda")
+    out = {}
+    for tau in cfg["taus"]:
+        o, lse, mask, _ = lib.prefill_qk8(dq, dk, dv, True, tau, want_mask=True, workspace=ws)
+        torch.cuda.synchronize()
+        out[tau] = (o.cpu().numpy(), lse.cpu().numpy(), mask.cpu().numpy())
+        del o, lse, mask
+    parts = {n: t.cpu().numpy() for n, t in lib.qk8_workspace_parts(ws, B, Hq, Hkv, N, d).items()}
+    del dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    qc, qs = fp8.quantize(synth.bf16_bits_to_f32(q))
+    kc, ks = fp8.quantize(synth.bf16_bits_to_f32(k))
+    assert np.array_equal(parts["qc"], qc) and np.array_equal(parts["kc"], kc)
+    assert np.array_equal(parts["qs"], qs) and np.array_equal(parts["ks"], ks)
+    qf, kf = fp8.dequantize(qc, qs), fp8.dequantize(kc, ks)
+
+    def head(bh):
+        b, h = bh
+        chk = _parity.PrefillChecker(q, k, v, True, qf=qf, kf=kf)
+        reps = {}
+        for tau, (o, lse, mask) in out.items():
+            rep = _parity.Report()
+            for qb0 in range(0, nt, 16):
+                qb1 = min(nt, qb0 + 16)
+                r0, r1 = qb0 * 64, min(N, qb1 * 64)
+                rep.merge(chk.check_blocks(b, h, qb0, qb1, tau, o[b, h, r0:r1],
+                                           lse[b, h, r0:r1], mask[b, h, qb0:qb1]))
+            reps[tau] = rep
+        return reps
+
+    total = {tau: _parity.Report() for tau in out}
+    with _one_blas_thread(), ThreadPoolExecutor(_threads()) as ex:
+        for i, reps in enumerate(ex.map(head, [(b, h) for b in range(B) for h in range(Hq)])):
+            for tau, r in reps.items():
+                total[tau].merge(r)
+            if i % 8 == 7:
+                print(f"[full] prefill_8k qk8 {i + 1} of {B * Hq} heads checked", flush=True)
+    for tau, rep in total.items():
+        print(f"[full] prefill_8k qk8 tau={tau} blocks={B * Hq * nt} {rep}", flush=True)
+        assert rep.ok(), str(rep)
