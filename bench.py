@@ -21,7 +21,10 @@ from one extra call outside its timing.
 Hkv=8) causal prefill shape in the 128K one's place; the default line is the
 128K step.
 
-Beside the step, the 8K and 32K causal prefill workloads are timed alone
+Beside the step, the same prefill with block-quantised fp8 QK^T
+(``prefill_qk8``: time including the quantisers, TFLOP/s dense-equivalent,
+fraction of the bf16 peak and of the fp8/bf16 mixed peak, drift from the
+exact prefill, tau sweep), the 8K and 32K causal prefill workloads are timed alone
 (``prefill_8k``, ``prefill_32k``: TFLOP/s, fraction of the bf16 peak, their
 tau sweeps), and the same decode workload is run over the 4-bit asymmetric
 KV cache (attn_kv_quantize_q4 once, then attn_decode_q4 timed like the bf16
@@ -45,6 +48,10 @@ if ROOT not in sys.path:
 
 METRIC = "prefill attn TFLOP/s (dense-equiv) & decode KV GB/s at 128K ctx, per τ"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+# the fp8-QK^T prefill does half its dense flops (QK^T) at the fp8 rate and
+# half (PV) at the bf16 rate: its MFMA ceiling is the harmonic mix
+PEAK_QK8_TFLOPS = 2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_BF16_TFLOPS)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 # HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE,
@@ -53,17 +60,20 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # figure no longer applies and is reported as null.
 MEASURED_TRAFFIC = {
     "prefill": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp"),
-                "sha1": "997b1712c691d713dcef2bad76a69c55fe5807a3",
-                "bytes": (2711139.9 * 2.0 + 528384.0) * 1024},
+                "sha1": "2a771a86ca5f49e7aa3968e13920c7815371302e",
+                "bytes": (2926160.6 * 2.0 + 528384.0) * 1024},
+    "prefill_qk8": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp", "fp8.hip"),
+                    "sha1": "c88ad7fd36d3fb1b701d2eb27bf115a628eba1bf",
+                    "bytes": (1792088.5 * 2.0 + 528385.5) * 1024},
     "decode_q4": {"sources": ("kvq4.hip", "kvq_common.hpp", "decode.hip", "common.hpp"),
-                  "sha1": "cd4804ff4cf9010b83b8a6c63007cd33dbdc7b85",
-                  "bytes": (1148234.6 * 2.0 + 16641.8) * 1024},
+                  "sha1": "47b7a50a18c93662f8b90d6a249268374d829e4a",
+                  "bytes": (1148070.9 * 2.0 + 16642.1) * 1024},
     "decode_q2": {"sources": ("kvq2.hip", "kvq_common.hpp", "decode.hip", "common.hpp"),
-                  "sha1": "f2a3384decbfa4800ad06886b2314c5a872c6114",
-                  "bytes": (623771.7 * 2.0 + 16640.0) * 1024},
+                  "sha1": "4233cbf13641664a2e555ef2ea645bc20e4de13e",
+                  "bytes": (623764.7 * 2.0 + 16640.1) * 1024},
     "decode": {"sources": ("decode.hip", "common.hpp"),
-               "sha1": "037e2d1c54ff97bf3d7d038802d458d5b7c2bdf7",
-               "bytes": (4195501.5 * 2.0 + 16641.6) * 1024},
+               "sha1": "0dd07902f20697310ae72199f10d1c43220f3099",
+               "bytes": (4195471.4 * 2.0 + 16641.3) * 1024},
 }
 
 
@@ -282,7 +292,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--reading", default="S", choices=["S", "P"])
     ap.add_argument("--only", default="both",
-                    choices=["both", "prefill", "decode", "decode_q4", "decode_q2"],
+                    choices=["both", "prefill", "decode", "decode_q4", "decode_q2",
+                             "prefill_qk8"],
                     help="profile one leg only (the JSON line then reports that leg)")
     ap.add_argument("--no-q4", action="store_true",
                     help="skip the 4-bit and 2-bit KV-cache decodes measured beside the step")
@@ -291,6 +302,8 @@ def main():
     ap.add_argument("--prefill-workload", default="prefill_128k",
                     choices=["prefill_128k", "prefill_32k", "prefill_8k"],
                     help="prefill shape of the step (default: the 128K one)")
+    ap.add_argument("--no-qk8", action="store_true",
+                    help="skip the prefill with fp8 QK^T measured beside the step")
     ap.add_argument("--no-other-prefill", action="store_true",
                     help="skip the 8K and 32K causal prefill workloads timed beside the step")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
@@ -347,6 +360,7 @@ def main():
         del src, dst
 
     run_p = args.only in ("both", "prefill")
+    run_qk8 = args.only == "prefill_qk8" or (args.only == "both" and not args.no_qk8)
     run_d = args.only in ("both", "decode")
     # quantised-cache decodes measured beside the step (width in bits)
     widths = [w for w in (4, 2)
@@ -499,6 +513,71 @@ def main():
                                    traffic=measured_traffic(leg),
                                    kernel=f"decode_q{w}_split_kernel<128>",
                                    avg_ms=round(q_ms, 4), per_launch_bytes=qb)
+
+    if run_qk8:
+        # The same prefill with block-quantised fp8 QK^T (attn_prefill_qk8):
+        # the quantisers and the prefill kernel, timed per call like the step.
+        qws = torch.empty(lib.attn_prefill_qk8_workspace_bytes(B, Hq, Hkv, N, d),
+                          dtype=torch.uint8, device=dev)
+
+        def prefill8(tau, mask=None):
+            lib.attn_prefill_qk8(tq, tk, tv, po, plse, True, tau, qws, mask)
+
+        for _ in range(args.warmup):
+            prefill8(math.inf)
+        t8 = Timer()
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            with t8:
+                prefill8(math.inf)
+        torch.cuda.synchronize()
+        q8_ms = float(np.mean(t8.ms()))
+        q8_tf = dense_flops / (q8_ms * 1e-3) / 1e12
+        # drift from the exact bf16 prefill on the same inputs
+        prefill(math.inf)
+        torch.cuda.synchronize()
+        o_ex, l_ex = po.clone(), plse.clone()
+        prefill8(math.inf)
+        torch.cuda.synchronize()
+        drift_o = float((po - o_ex).abs().max())
+        drift_l = float((plse - l_ex).abs().max())
+        del o_ex, l_ex
+        taus8 = []
+        if not args.no_sweep:
+            for tau in pcfg["taus"][1:]:
+                t = Timer()
+                for _ in range(3):
+                    with t:
+                        prefill8(tau)
+                torch.cuda.synchronize()
+                ms = float(np.median(t.ms()))
+                prefill8(tau, pmask)
+                ex, vis, kept = prefill_exec_flops(pmask.cpu().numpy(), d)
+                taus8.append(dict(tau=str(tau), ms=round(ms, 4),
+                                  skip_fraction=round(1 - kept / vis, 4),
+                                  tflops_dense=round(dense_flops / ms / 1e9, 3),
+                                  tflops_executed=round(ex / ms / 1e9, 3)))
+        out["prefill_qk8"] = dict(
+            value=round(q8_tf, 3), unit="TFLOP/s", ms=round(q8_ms, 4),
+            frac_of_bf16_peak=round(q8_tf / PEAK_BF16_TFLOPS, 4),
+            frac_of_mixed_peak=round(q8_tf / PEAK_QK8_TFLOPS, 4),
+            mixed_peak=round(PEAK_QK8_TFLOPS, 1),
+            max_abs_o_drift=drift_o, max_abs_lse_drift=drift_l, tau_sweep=taus8,
+            traffic=measured_traffic("prefill_qk8"),
+            kernels="quant_fp8_kernel<128> x 2 + prefill_kernel<128,true,4,5,false,true>",
+            note="QK^T on fp8 E4M3 codes (64-row tiles, fp32 scales), PV in bf16; time "
+                 "includes quantising Q and K")
+        if args.only == "prefill_qk8":
+            out.update(value=round(q8_tf, 3), unit="TFLOP/s", ms_per_step=round(q8_ms, 4),
+                       dtype="fp8 QK^T, bf16 PV")
+            out["config"]["workload"] = f"{pname} with fp8 QK^T, tau=inf"
+            out["roofline"] = dict(bound="mfma", achieved=round(q8_tf, 3), peak=PEAK_QK8_TFLOPS,
+                                   unit="TFLOP/s", frac=round(q8_tf / PEAK_QK8_TFLOPS, 4),
+                                   traffic=measured_traffic("prefill_qk8"),
+                                   kernel="prefill_kernel<128,true,4,5,false,true> + quantisers",
+                                   avg_ms=round(q8_ms, 4), per_launch_flops=dense_flops)
+        del qws
+        torch.cuda.empty_cache()
 
     if run_p and args.only == "both" and not args.no_other_prefill:
         # the other causal prefill workloads, timed alone like the step's
