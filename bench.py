@@ -302,6 +302,8 @@ def main():
     ap.add_argument("--prefill-workload", default="prefill_128k",
                     choices=["prefill_128k", "prefill_32k", "prefill_8k"],
                     help="prefill shape of the step (default: the 128K one)")
+    ap.add_argument("--tau", type=float, default=math.inf,
+                    help="tau of the timed prefill calls (default inf: the step); for counter runs")
     ap.add_argument("--no-qk8", action="store_true",
                     help="skip the prefill with fp8 QK^T measured beside the step")
     ap.add_argument("--no-other-prefill", action="store_true",
@@ -377,7 +379,7 @@ def main():
 
     for _ in range(args.warmup):
         if run_p:
-            prefill(math.inf)
+            prefill(args.tau)
         if run_d:
             decode(math.inf)
     torch.cuda.synchronize()
@@ -388,7 +390,7 @@ def main():
     for _ in range(args.steps):
         if run_p:
             with tp:
-                prefill(math.inf)
+                prefill(args.tau)
         if run_d:
             with td:
                 decode(math.inf)
@@ -400,12 +402,17 @@ def main():
     out = dict(metric=METRIC, n_gpus=1, steps=args.steps, warmup=args.warmup,
                ms_per_step=round(wall_ms, 4), higher_is_better=True, scaling="weak",
                vs_baseline=None, dtype="bf16", data="synthetic")
-    cfg = dict(workload=f"{pname} + decode_128k, tau=inf",
+    cfg = dict(workload=f"{pname} + decode_128k, tau=inf" if math.isinf(args.tau) else
+               f"{pname} at tau={args.tau} + decode_128k, tau=inf",
                prefill=dict(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, causal=True),
                decode=dict(B=DB, Hq=DHq, Hkv=DHkv, L=L, d=Dd, split=4096),
                reading=args.reading, inputs="seeded N(0,1) bf16 + sinks/band/window")
     out["config"] = cfg
 
+    if run_p and not math.isinf(args.tau):
+        prefill(args.tau, pmask)
+        _, vis, kept = prefill_exec_flops(pmask.cpu().numpy(), d)
+        out["tiles_at_tau"] = dict(tau=args.tau, visited=vis, kept=kept)
     if run_p:
         p_ms = float(np.mean(tp.ms()))
         p_tf = dense_flops / (p_ms * 1e-3) / 1e12
@@ -524,15 +531,19 @@ def main():
             lib.attn_prefill_qk8(tq, tk, tv, po, plse, True, tau, qws, mask)
 
         for _ in range(args.warmup):
-            prefill8(math.inf)
+            prefill8(args.tau)
         t8 = Timer()
         torch.cuda.synchronize()
         for _ in range(args.steps):
             with t8:
-                prefill8(math.inf)
+                prefill8(args.tau)
         torch.cuda.synchronize()
         q8_ms = float(np.mean(t8.ms()))
         q8_tf = dense_flops / (q8_ms * 1e-3) / 1e12
+        if not math.isinf(args.tau):
+            prefill8(args.tau, pmask)
+            _, vis8, kept8 = prefill_exec_flops(pmask.cpu().numpy(), d)
+            out["tiles_at_tau_qk8"] = dict(tau=args.tau, visited=vis8, kept=kept8)
         # drift from the exact bf16 prefill on the same inputs
         prefill(math.inf)
         torch.cuda.synchronize()
@@ -555,6 +566,7 @@ def main():
                 ex, vis, kept = prefill_exec_flops(pmask.cpu().numpy(), d)
                 taus8.append(dict(tau=str(tau), ms=round(ms, 4),
                                   skip_fraction=round(1 - kept / vis, 4),
+                                  tiles_visited=vis, tiles_kept=kept,
                                   tflops_dense=round(dense_flops / ms / 1e9, 3),
                                   tflops_executed=round(ex / ms / 1e9, 3)))
         out["prefill_qk8"] = dict(
@@ -644,6 +656,7 @@ def main():
             ex, vis, kept = prefill_exec_flops(m, d)
             sweep.append(dict(leg=pname, tau=str(tau), ms=round(ms, 4),
                               skip_fraction=round(1 - kept / vis, 4),
+                              tiles_visited=vis, tiles_kept=kept,
                               tflops_dense=round(dense_flops / ms / 1e9, 3),
                               tflops_executed=round(ex / ms / 1e9, 3)))
         for tau in dcfg["taus"] if run_d else []:
