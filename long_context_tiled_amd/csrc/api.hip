@@ -150,7 +150,9 @@ int prefill_launch(const void* q, const void* k, const void* v, float* o, float*
                           Hq, Hkv,   N,  d,  causal,
                           Nq, causal ? (N - Nq) / SKIPATTN_TILE : 0,
                           cap, tau_raw(tau, d), exp2_scale(d), stream};
-  if (skipattn::launch_prefill(a) != 0) return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
+  const int lr = skipattn::launch_prefill(a);
+  if (lr == -1) return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
+  if (lr != 0) return fail(SKIPATTN_EHIP, "prefill: device query for the work queue failed");
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(SKIPATTN_EHIP, "prefill launch: %s", hipGetErrorString(err));
   return SKIPATTN_OK;
@@ -304,7 +306,9 @@ int attn_prefill_qk8(const void* q, const void* k, const void* v, float* o, floa
     return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
   skipattn::PrefillArgs a{qc, kc, v, o, lse, skip_mask, B, Hq, Hkv, N, d, causal,
                           N,  0,  N, tau_raw(tau, d), exp2_scale(d), stream, qs, ks};
-  if (skipattn::launch_prefill(a) != 0) return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
+  const int lr = skipattn::launch_prefill(a);
+  if (lr == -1) return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
+  if (lr != 0) return fail(SKIPATTN_EHIP, "prefill_qk8: device query for the work queue failed");
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(SKIPATTN_EHIP, "prefill_qk8 launch: %s", hipGetErrorString(err));
   return SKIPATTN_OK;

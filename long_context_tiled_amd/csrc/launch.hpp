@@ -76,7 +76,9 @@ struct DecodeQ4Args {
 };
 
 // Each returns 0 when the kernels were enqueued, nonzero if the grid cannot
-// be expressed; launch errors are read back by the caller.
+// be expressed (launch_prefill: -1, or -2 when the device's work-queue
+// address or compute-unit count cannot be read); launch errors are read back
+// by the caller.
 int launch_prefill(const PrefillArgs& a);
 int launch_decode(const DecodeArgs& a);
 int launch_kv_quantize_q4(const QuantArgs& a);

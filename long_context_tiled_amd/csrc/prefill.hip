@@ -13,7 +13,12 @@
 //   so the skip vote of a decision tile is a single wave ballot. The waves of
 //   a workgroup are HPW heads of one grouped-query KV group x (4 / HPW)
 //   consecutive query tiles, and share every K/V tile through LDS.
-//   Grid order is longest-first for causal attention.
+//   A work item is one such workgroup's share (a query tile group of a head
+//   group). Items are numbered longest-first for causal attention; the grid
+//   holds one workgroup per compute unit, each starting on item blockIdx.x
+//   and then taking the next unclaimed item from a device-wide counter, so
+//   that compute units (and XCDs, whose clocks differ) that finish early
+//   take more of the work.
 //
 // Data movement
 //   K and V tiles (64 keys x d, bf16) go from HBM/L2 straight into LDS with
@@ -50,6 +55,8 @@
 // Units: scores stay raw (q.k) in registers. The test compares
 // t < m - tau * sqrt(d); exponentials use exp2 with log2(e)/sqrt(d) folded
 // into one FMA per score.
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "common.hpp"
@@ -179,7 +186,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
     const uint16_t* __restrict__ v, float* __restrict__ o,
     float* __restrict__ lse, uint8_t* __restrict__ mask, const float* __restrict__ qsc,
     const float* __restrict__ ksc, int Hq, int Hkv,
-    int Nq_arg, int N, int q0t_arg, int cap_arg, float tau_raw, float c, int nqg, int ny) {
+    int Nq_arg, int N, int q0t_arg, int cap_arg, float tau_raw, float c, int nqg, int ny,
+    uint32_t* __restrict__ queue, int total) {
   // Nq queries (the chunk) at key positions 64 q0t .. 64 q0t + Nq - 1 of N
   // keys: query tile qb of the chunk is tile qb + q0t of the key axis. The
   // whole-sequence instance (CHUNK false) has Nq = N and q0t = 0 as
@@ -200,224 +208,299 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
   typedef __attribute__((address_space(3))) char lds_char;
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_char*)smem;  // LDS byte address
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
   const int G = Hq / Hkv;
   const int gper = G / HPW;
 
-  const int lin = blockIdx.x;
-  const int y = lin % ny;
-  const int qg = CAUSAL ? (nqg - 1 - lin / ny) : lin / ny;
-  const int b = y / (Hkv * gper);
-  const int rem = y % (Hkv * gper);
-  const int g = rem / gper;
-  const int h = g * G + (rem % gper) * HPW + (wave % HPW);
-  const int qb = qg * QPW + wave / HPW;   // query tile within the chunk
-  const int qbg = qb + q0t;               // the same tile on the key axis
-  const int nqb = (Nq + kTile - 1) / kTile;
-  const int nkb = (N + kTile - 1) / kTile;
-  const bool wave_valid = qb < nqb;
-  const int nkb_wg = CAUSAL ? min(nkb, qg * QPW + QPW + q0t) : nkb;
-  const int nkb_w = wave_valid ? (CAUSAL ? qbg + 1 : nkb) : 0;
+  auto run_item = [&](const int lin, uint32_t& nxt) __attribute__((always_inline)) {
+    // The lane geometry is re-derived for every item from an opaque copy of
+    // the thread index: hoisted out of the item loop, it would stay live
+    // through the key loop and the epilogue, and the compiler's registers
+    // would no longer fit below the key loop's fixed register plan.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int l32 = lane & 31;
+    const int hh = lane >> 5;
+    const int y = lin % ny;
+    const int qg = CAUSAL ? (nqg - 1 - lin / ny) : lin / ny;
+    const int b = y / (Hkv * gper);
+    const int rem = y % (Hkv * gper);
+    const int g = rem / gper;
+    const int h = g * G + (rem % gper) * HPW + (wave % HPW);
+    const int qb = qg * QPW + wave / HPW;   // query tile within the chunk
+    const int qbg = qb + q0t;               // the same tile on the key axis
+    const int nqb = (Nq + kTile - 1) / kTile;
+    const int nkb = (N + kTile - 1) / kTile;
+    const bool wave_valid = qb < nqb;
+    const int nkb_wg = CAUSAL ? min(nkb, qg * QPW + QPW + q0t) : nkb;
+    const int nkb_w = wave_valid ? (CAUSAL ? qbg + 1 : nkb) : 0;
 
-  const int k_head_bytes = N * KRB;
-  const int v_head_bytes = N * D * 2;
-  const size_t kv_row0 = (size_t)(b * Hkv + g) * cap;  // first row of the head's K/V
-  const uint8_t* kh = k + kv_row0 * KRB;
-  const uint16_t* vh = v + kv_row0 * D;
-  const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)kh, (short)0, k_head_bytes, kBufferCfg);
-  const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)vh, (short)0, v_head_bytes, kBufferCfg);
-  const size_t bh = (size_t)b * Hq + h;
-  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(q + bh * Nq * KRB), (short)0, Nq * KRB, kBufferCfg);
+    const int k_head_bytes = N * KRB;
+    const int v_head_bytes = N * D * 2;
+    const size_t kv_row0 = (size_t)(b * Hkv + g) * cap;  // first row of the head's K/V
+    const uint8_t* kh = k + kv_row0 * KRB;
+    const uint16_t* vh = v + kv_row0 * D;
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)kh, (short)0, k_head_bytes, kBufferCfg);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)vh, (short)0, v_head_bytes, kBufferCfg);
+    const size_t bh = (size_t)b * Hq + h;
+    const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(q + bh * Nq * KRB), (short)0, Nq * KRB, kBufferCfg);
 
-  // Per-lane load geometry for the direct-to-LDS copies: instruction i of
-  // wave w fills LDS bytes [1024 (w * IPW + i), +1024) of the tile (K and V
-  // tiles each; their instruction counts differ when K is fp8).
-  constexpr int IPW = T::instrPerWave;
-  constexpr int KIPW = T::kInstrPerWave;
-  int ld_gk[KIPW], ld_gv[IPW];  // global byte offsets within the head, relative to key 0
-#pragma unroll
-  for (int i = 0; i < KIPW; ++i) {
-    const int r = (wave * KIPW + i) * T::kRowsPerInstr + lane / T::kChunks;
-    const int slot = lane % T::kChunks;
-    ld_gk[i] = r * KRB + 16 * (slot ^ swz_row<KRB>(r));
-  }
-#pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    const int r = (wave * IPW + i) * T::rowsPerInstr + lane / T::chunks;
-    const int slot = lane % T::chunks;
-    ld_gv[i] = r * T::rowBytes + 16 * (slot ^ swz_v<D>(r));
-  }
-
-  auto issue_tile = [&](int kb) __attribute__((always_inline)) {
-    char* st = smem + (kb % STAGES) * STAGE_BYTES;
-#pragma unroll
+    // Per-lane load geometry for the direct-to-LDS copies: instruction i of
+    // wave w fills LDS bytes [1024 (w * IPW + i), +1024) of the tile (K and V
+    // tiles each; their instruction counts differ when K is fp8).
+    constexpr int IPW = T::instrPerWave;
+    constexpr int KIPW = T::kInstrPerWave;
+    int ld_gk[KIPW], ld_gv[IPW];  // global byte offsets within the head, relative to key 0
+  #pragma unroll
     for (int i = 0; i < KIPW; ++i) {
-      lds_void* dk = (lds_void*)(st + 1024 * (wave * KIPW + i));
-      dma16(krs, dk, kb * T::kBytes + ld_gk[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      lds_void* dv = (lds_void*)(st + T::kBytes + 1024 * (wave * IPW + i));
-      dma16(vrs, dv, kb * T::bytes + ld_gv[i]);
-    }
-  };
-
-  // The wave's 64 query rows go to its own swizzled LDS tile once (rows past
-  // N read as zero), and from there into AGPRs.
-  const uint32_t q_lds = (uint32_t)(3 * STAGE_BYTES + wave * T::kBytes);
-  if (wave_valid) {
-    constexpr int QI = T::kBytes / 1024;  // 1 KB copy instructions per Q tile
-#pragma unroll
-    for (int i = 0; i < QI; ++i) {
-      const int r = i * T::kRowsPerInstr + lane / T::kChunks;
+      const int r = (wave * KIPW + i) * T::kRowsPerInstr + lane / T::kChunks;
       const int slot = lane % T::kChunks;
-      const int cc = slot ^ swz_row<KRB>(r);
-      dma16(qrs, (lds_void*)(smem + q_lds + 1024 * i), (qb * kTile + r) * KRB + cc * 16);
+      ld_gk[i] = r * KRB + 16 * (slot ^ swz_row<KRB>(r));
     }
-  }
+  #pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int r = (wave * IPW + i) * T::rowsPerInstr + lane / T::chunks;
+      const int slot = lane % T::chunks;
+      ld_gv[i] = r * T::rowBytes + 16 * (slot ^ swz_v<D>(r));
+    }
 
-  // K / Q fragment reads (A / B operands of S^T = K . Q^T): lane l reads row
-  // (32 a + l32) of a swizzled tile. bf16: 16-byte chunk 2 ks + hh; fp8: the
-  // chunks 4 ks + 2 hh and 4 ks + 2 hh + 1. With rows 32 apart sharing the
-  // swizzle, the second row half is an immediate offset, and the chunk XOR
-  // moves only address bits below the row: the k-step address is frag ^
-  // (32 ks) (bf16) or frag ^ (64 ks) with the second chunk at ^ 16 (fp8),
-  // for a 1 KB-aligned tile base.
-  const uint32_t frag =
-      (uint32_t)(l32 * KRB + 16 * ((F8 ? 2 * hh : hh) ^ swz_row<KRB>(l32)));
-
-  // ds_read_b64_tr_b16 geometry for the V^T operand: lane k of a 16-lane
-  // group fetches 4 consecutive d of key row (16 ks + key_base + k / 4); the
-  // instruction hands lane i of the group element (i % 4) of the chunks of
-  // lanes 4e + i / 4, e = 0..3, i.e. 4 keys of one d column. For 32-d block
-  // mb the swizzled address is (that of block 0) ^ (64 mb).
-  const int grp16 = lane >> 4;
-  const int k16 = lane & 15;
-  uint32_t tr0[2];  // block-0 address of each 4-key half, within a tile
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int row = 4 * (grp16 >> 1) + (k16 >> 2) + 8 * half;
-    const int d = 16 * (grp16 & 1) + 4 * (k16 & 3);
-    tr0[half] = (uint32_t)(row * T::rowBytes + 16 * ((d >> 3) ^ swz_v<D>(row)) + 2 * (d & 7));
-  }
-
-  // Prologue: Q tiles (slots 3-4) and K/V tiles 0-2 copied; Q^T into AGPRs.
-  SKA_CALL(D, F8, zero_o);
-  for (int t = 0; t < 3; ++t)
-    if (t < nkb_wg) issue_tile(t);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-  if (0 < nkb_w) SKA_CALL(D, F8, load_q, smem_lds + q_lds + frag);
-  __syncthreads();  // slots 3-4 are K/V slots from here on
-
-  // The key loop runs as one generated block (barriers, tile copies, the
-  // pipelined steps, votes, rescales, masks). Its scalar operands must be
-  // wave-uniform.
-  const float lazy_raw = 8.0f / c;  // 8 in log2 units, as a raw-score gap
-  typename LoopArgsOf<D, F8>::type la;
-  la.frag = frag;
-  la.tr0 = tr0[0];
-  la.tr1 = tr0[1];
-#pragma unroll
-  for (int i = 0; i < KIPW; ++i) la.gk[i] = (uint32_t)ld_gk[i];
-#pragma unroll
-  for (int i = 0; i < IPW; ++i) la.gv[i] = (uint32_t)ld_gv[i];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int qrow = qb * kTile + nb * 32 + l32;  // row within the chunk
-    const int qpos = qbg * kTile + nb * 32 + l32; // its key position
-    const int last = CAUSAL ? min(N - 1, qpos) : N - 1;  // last key this row may see
-    la.lim_base[nb] = last - 4 * hh;
-    la.val[nb] = __ballot(qrow < Nq);
-  }
-  la.lazy = lazy_raw;
-  la.nkb_wg = nkb_wg;
-  la.nkb_w = __builtin_amdgcn_readfirstlane(nkb_w);
-  la.qb = __builtin_amdgcn_readfirstlane(qbg);  // the diagonal tile
-  la.N = N;
-  la.tau = tau_raw;
-  la.c = c;
-  auto rsrc = [&](const void* p, int bytes) {
-    const uint64_t a = (uint64_t)(uintptr_t)p;
-    u32x4 r;
-    r[0] = (uint32_t)a;
-    r[1] = (uint32_t)(a >> 32) & 0xffffu;  // stride 0
-    r[2] = (uint32_t)bytes;
-    r[3] = kBufferCfg;
-    return r;
-  };
-  la.krs = rsrc(kh, k_head_bytes);
-  la.vrs = rsrc(vh, v_head_bytes);
-  la.wl = smem_lds + (uint32_t)(wave * KIPW * 1024);
-  la.smem = smem_lds;
-  la.mask_row = mask != nullptr ? (uint64_t)(uintptr_t)(mask + (bh * nqb + qb) * nkb) : 0ull;
-  if constexpr (F8) {
-    const int nkbc = (cap + kTile - 1) / kTile;  // K scales per head
-    la.ksp = (uint64_t)(uintptr_t)(ksc + (size_t)(b * Hkv + g) * nkbc);
-    la.sqv = wave_valid ? qsc[bh * nqb + qb] : 1.f;
-    la.nkbm1 = nkb - 1;
-    la.wlv = smem_lds + (uint32_t)(T::kBytes + wave * IPW * 1024);
-  }
-  float m[2], mref[2], lsum[2];
-  if constexpr (CAUSAL) SKA_CALL(D, F8, key_loop_causal, la, m, mref, lsum);
-  else SKA_CALL(D, F8, key_loop_full, la, m, mref, lsum);
-  (void)m;
-
-  if (!wave_valid) return;
-  drain_mfma();
-
-  // ---- epilogue: O = O^T / l, LSE = m / sqrt(d) + ln l ----
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const float ltot = swap_halves_sum(lsum[nb]);
-    const float inv = 1.f / ltot;
-    const int row = qb * kTile + nb * 32 + l32;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      float ov[16];
-      const int id = 2 * mb + nb;
-      if (id == 0) SKA_CALL(D, F8, read_o_00, ov);
-      if (id == 1) SKA_CALL(D, F8, read_o_01, ov);
-      if (id == 2) SKA_CALL(D, F8, read_o_10, ov);
-      if (id == 3) SKA_CALL(D, F8, read_o_11, ov);
-      if constexpr (MB == 4 && !F8) {
-        if (id == 4) d128::read_o_20(ov);
-        if (id == 5) d128::read_o_21(ov);
-        if (id == 6) d128::read_o_30(ov);
-        if (id == 7) d128::read_o_31(ov);
-      } else if constexpr (MB == 4) {
-        if (id == 4) d128f8::read_o_20(ov);
-        if (id == 5) d128f8::read_o_21(ov);
-        if (id == 6) d128f8::read_o_30(ov);
-        if (id == 7) d128f8::read_o_31(ov);
+    auto issue_tile = [&](int kb) __attribute__((always_inline)) {
+      char* st = smem + (kb % STAGES) * STAGE_BYTES;
+  #pragma unroll
+      for (int i = 0; i < KIPW; ++i) {
+        lds_void* dk = (lds_void*)(st + 1024 * (wave * KIPW + i));
+        dma16(krs, dk, kb * T::kBytes + ld_gk[i]);
       }
-      if (row < Nq) {
-        float* orow = o + (bh * Nq + row) * D;
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          f32x4 val;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) val[i] = ov[4 * r4 + i] * inv;
-          *reinterpret_cast<f32x4*>(orow + mb * 32 + 8 * r4 + 4 * hh) = val;
+  #pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        lds_void* dv = (lds_void*)(st + T::kBytes + 1024 * (wave * IPW + i));
+        dma16(vrs, dv, kb * T::bytes + ld_gv[i]);
+      }
+    };
+
+    // The wave's 64 query rows go to its own swizzled LDS tile once (rows past
+    // N read as zero), and from there into AGPRs.
+    const uint32_t q_lds = (uint32_t)(3 * STAGE_BYTES + wave * T::kBytes);
+    if (wave_valid) {
+      constexpr int QI = T::kBytes / 1024;  // 1 KB copy instructions per Q tile
+  #pragma unroll
+      for (int i = 0; i < QI; ++i) {
+        const int r = i * T::kRowsPerInstr + lane / T::kChunks;
+        const int slot = lane % T::kChunks;
+        const int cc = slot ^ swz_row<KRB>(r);
+        dma16(qrs, (lds_void*)(smem + q_lds + 1024 * i), (qb * kTile + r) * KRB + cc * 16);
+      }
+    }
+
+    // K / Q fragment reads (A / B operands of S^T = K . Q^T): lane l reads row
+    // (32 a + l32) of a swizzled tile. bf16: 16-byte chunk 2 ks + hh; fp8: the
+    // chunks 4 ks + 2 hh and 4 ks + 2 hh + 1. With rows 32 apart sharing the
+    // swizzle, the second row half is an immediate offset, and the chunk XOR
+    // moves only address bits below the row: the k-step address is frag ^
+    // (32 ks) (bf16) or frag ^ (64 ks) with the second chunk at ^ 16 (fp8),
+    // for a 1 KB-aligned tile base.
+    const uint32_t frag =
+        (uint32_t)(l32 * KRB + 16 * ((F8 ? 2 * hh : hh) ^ swz_row<KRB>(l32)));
+
+    // ds_read_b64_tr_b16 geometry for the V^T operand: lane k of a 16-lane
+    // group fetches 4 consecutive d of key row (16 ks + key_base + k / 4); the
+    // instruction hands lane i of the group element (i % 4) of the chunks of
+    // lanes 4e + i / 4, e = 0..3, i.e. 4 keys of one d column. For 32-d block
+    // mb the swizzled address is (that of block 0) ^ (64 mb).
+    const int grp16 = lane >> 4;
+    const int k16 = lane & 15;
+    uint32_t tr0[2];  // block-0 address of each 4-key half, within a tile
+  #pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int row = 4 * (grp16 >> 1) + (k16 >> 2) + 8 * half;
+      const int d = 16 * (grp16 & 1) + 4 * (k16 & 3);
+      tr0[half] = (uint32_t)(row * T::rowBytes + 16 * ((d >> 3) ^ swz_v<D>(row)) + 2 * (d & 7));
+    }
+
+    // Prologue: Q tiles (slots 3-4) and K/V tiles 0-2 copied; Q^T into AGPRs.
+    SKA_CALL(D, F8, zero_o);
+    for (int t = 0; t < 3; ++t)
+      if (t < nkb_wg) issue_tile(t);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (0 < nkb_w) SKA_CALL(D, F8, load_q, smem_lds + q_lds + frag);
+    __syncthreads();  // slots 3-4 are K/V slots from here on
+
+    // The key loop runs as one generated block (barriers, tile copies, the
+    // pipelined steps, votes, rescales, masks). Its scalar operands must be
+    // wave-uniform.
+    const float lazy_raw = 8.0f / c;  // 8 in log2 units, as a raw-score gap
+    typename LoopArgsOf<D, F8>::type la;
+    la.frag = frag;
+    la.tr0 = tr0[0];
+    la.tr1 = tr0[1];
+  #pragma unroll
+    for (int i = 0; i < KIPW; ++i) la.gk[i] = (uint32_t)ld_gk[i];
+  #pragma unroll
+    for (int i = 0; i < IPW; ++i) la.gv[i] = (uint32_t)ld_gv[i];
+  #pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int qrow = qb * kTile + nb * 32 + l32;  // row within the chunk
+      const int qpos = qbg * kTile + nb * 32 + l32; // its key position
+      const int last = CAUSAL ? min(N - 1, qpos) : N - 1;  // last key this row may see
+      la.lim_base[nb] = last - 4 * hh;
+      la.val[nb] = __ballot(qrow < Nq);
+    }
+    la.lazy = lazy_raw;
+    la.nkb_wg = nkb_wg;
+    la.nkb_w = __builtin_amdgcn_readfirstlane(nkb_w);
+    la.qb = __builtin_amdgcn_readfirstlane(qbg);  // the diagonal tile
+    la.N = N;
+    la.tau = tau_raw;
+    la.c = c;
+    auto rsrc = [&](const void* p, int bytes) {
+      const uint64_t a = (uint64_t)(uintptr_t)p;
+      u32x4 r;
+      r[0] = (uint32_t)a;
+      r[1] = (uint32_t)(a >> 32) & 0xffffu;  // stride 0
+      r[2] = (uint32_t)bytes;
+      r[3] = kBufferCfg;
+      return r;
+    };
+    la.krs = rsrc(kh, k_head_bytes);
+    la.vrs = rsrc(vh, v_head_bytes);
+    la.wl = smem_lds + (uint32_t)(wave * KIPW * 1024);
+    la.smem = smem_lds;
+    la.mask_row = mask != nullptr ? (uint64_t)(uintptr_t)(mask + (bh * nqb + qb) * nkb) : 0ull;
+    if constexpr (F8) {
+      const int nkbc = (cap + kTile - 1) / kTile;  // K scales per head
+      la.ksp = (uint64_t)(uintptr_t)(ksc + (size_t)(b * Hkv + g) * nkbc);
+      la.sqv = wave_valid ? qsc[bh * nqb + qb] : 1.f;
+      la.nkbm1 = nkb - 1;
+      la.wlv = smem_lds + (uint32_t)(T::kBytes + wave * IPW * 1024);
+    }
+    float m[2], mref[2], lsum[2];
+    if constexpr (CAUSAL) SKA_CALL(D, F8, key_loop_causal, la, m, mref, lsum);
+    else SKA_CALL(D, F8, key_loop_full, la, m, mref, lsum);
+    (void)m;
+
+    // Claim the next item as this one's key loop ends: a claim made earlier
+    // would bind a workgroup to its next item before it is known to be
+    // among the first free, which undoes the longest-first balance when
+    // there are few items per workgroup.
+    uint32_t claim = 0;
+    if (tid == 0) claim = atomicAdd(queue, 1u);
+    nxt = __builtin_amdgcn_readfirstlane(claim) + gridDim.x;  // meaningful in wave 0
+    if (!wave_valid) return;
+    drain_mfma();
+
+    // ---- epilogue: O = O^T / l, LSE = m / sqrt(d) + ln l ----
+  #pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const float ltot = swap_halves_sum(lsum[nb]);
+      const float inv = 1.f / ltot;
+      const int row = qb * kTile + nb * 32 + l32;
+  #pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        float ov[16];
+        const int id = 2 * mb + nb;
+        if (id == 0) SKA_CALL(D, F8, read_o_00, ov);
+        if (id == 1) SKA_CALL(D, F8, read_o_01, ov);
+        if (id == 2) SKA_CALL(D, F8, read_o_10, ov);
+        if (id == 3) SKA_CALL(D, F8, read_o_11, ov);
+        if constexpr (MB == 4 && !F8) {
+          if (id == 4) d128::read_o_20(ov);
+          if (id == 5) d128::read_o_21(ov);
+          if (id == 6) d128::read_o_30(ov);
+          if (id == 7) d128::read_o_31(ov);
+        } else if constexpr (MB == 4) {
+          if (id == 4) d128f8::read_o_20(ov);
+          if (id == 5) d128f8::read_o_21(ov);
+          if (id == 6) d128f8::read_o_30(ov);
+          if (id == 7) d128f8::read_o_31(ov);
+        }
+        if (row < Nq) {
+          float* orow = o + (bh * Nq + row) * D;
+  #pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            f32x4 val;
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) val[i] = ov[4 * r4 + i] * inv;
+            *reinterpret_cast<f32x4*>(orow + mb * 32 + 8 * r4 + 4 * hh) = val;
+          }
         }
       }
+      if (row < Nq && hh == 0) lse[bh * Nq + row] = (mref[nb] * c + __log2f(ltot)) * kLn2;
     }
-    if (row < Nq && hh == 0) lse[bh * Nq + row] = (mref[nb] * c + __log2f(ltot)) * kLn2;
+    if (CAUSAL && mask != nullptr) {
+      for (int kb = qbg + 1 + lane; kb < nkb; kb += 64)
+        mask[(bh * nqb + qb) * nkb + kb] = 2;
+    }
+  };
+
+  uint32_t* const bcast = reinterpret_cast<uint32_t*>(smem);
+  int item = blockIdx.x;
+  while (item < total) {
+    uint32_t nxt = 0;
+    run_item(item, nxt);
+    __syncthreads();  // every wave is done with the LDS tiles
+    if (threadIdx.x == 0) bcast[0] = nxt;
+    __syncthreads();
+    item = __builtin_amdgcn_readfirstlane(bcast[0]);
+    __syncthreads();  // read before the next item's copies overwrite slot 0
   }
-  if (CAUSAL && mask != nullptr) {
-    for (int kb = qbg + 1 + lane; kb < nkb; kb += 64)
-      mask[(bh * nqb + qb) * nkb + kb] = 2;
+  // The last workgroup out returns the counter pair to zero for the next
+  // call that uses this slot. Every claim of every workgroup (its result
+  // consumed above) precedes that workgroup's count.
+  if (threadIdx.x == 0) {
+    __threadfence();
+    if (atomicAdd(queue + 1, 1u) == gridDim.x - 1) {
+      __threadfence();
+      atomicExch(queue, 0u);
+      atomicExch(queue + 1, 0u);
+    }
   }
 }
 
 constexpr int kStages = 5;
+
+// Work-item counters of the persistent prefill grid: kQueueSlots pairs
+// (next item, workgroups finished), each in its own 64-byte line, zero at
+// load and returned to zero by the last workgroup of every call. A call
+// takes the next slot in turn, so calls in flight at the same time on
+// different streams share a slot only when kQueueSlots - 1 other prefill
+// calls were made between them. Each GPU holds its own copy; host code uses
+// the address from hipGetSymbolAddress, taken once per device.
+constexpr int kQueueSlots = 1024;
+static __device__ __align__(256) uint32_t prefill_queue[kQueueSlots * 16];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<uint32_t*> g_queue_addr[kMaxDevices];
+std::atomic<int> g_num_cu[kMaxDevices];
+std::atomic<uint32_t> g_next_slot{0};
+
+// The current device's counter array and compute-unit count.
+int queue_and_cus(uint32_t** q, int* ncu) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -2;
+  uint32_t* p = g_queue_addr[dev].load(std::memory_order_acquire);
+  int n = g_num_cu[dev].load(std::memory_order_acquire);
+  if (p == nullptr || n <= 0) {
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(prefill_queue)) != hipSuccess || a == nullptr)
+      return -2;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      return -2;
+    p = static_cast<uint32_t*>(a);
+    g_queue_addr[dev].store(p, std::memory_order_release);
+    g_num_cu[dev].store(n, std::memory_order_release);
+  }
+  *q = p;
+  *ncu = n;
+  return 0;
+}
+}  // namespace
 
 template <int D, bool CAUSAL, int HPW, bool CHUNK, bool F8>
 static int launch_one(const PrefillArgs& a) {
@@ -426,12 +509,19 @@ static int launch_one(const PrefillArgs& a) {
   const int nqg = (nqb + QPW - 1) / QPW;
   const int G = a.Hq / a.Hkv;
   const int ny = a.B * a.Hkv * (G / HPW);
-  const long long blocks = (long long)nqg * ny;
-  if (blocks > 0x7fffffffLL) return -1;
-  hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, HPW, kStages, CHUNK, F8>), dim3((unsigned)blocks),
+  const long long items = (long long)nqg * ny;
+  if (items > 0x7fffffffLL) return -1;
+  if (items == 0) return 0;
+  uint32_t* queue = nullptr;
+  int ncu = 0;
+  if (queue_and_cus(&queue, &ncu) != 0) return -2;
+  queue += 16 * (g_next_slot.fetch_add(1, std::memory_order_relaxed) % kQueueSlots);
+  // one workgroup per compute unit (the tile slots fill the LDS)
+  const int grid = (int)std::min<long long>(items, ncu);
+  hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, HPW, kStages, CHUNK, F8>), dim3((unsigned)grid),
                      dim3(256), 0, (hipStream_t)a.stream, (const uint8_t*)a.q, (const uint8_t*)a.k,
                      (const uint16_t*)a.v, a.o, a.lse, a.mask, a.qscale, a.kscale, a.Hq, a.Hkv,
-                     a.Nq, a.N, a.q0t, a.cap, a.tau_raw, a.c, nqg, ny);
+                     a.Nq, a.N, a.q0t, a.cap, a.tau_raw, a.c, nqg, ny, queue, (int)items);
   return 0;
 }
 

@@ -173,3 +173,41 @@ def test_prefill_workload_sampled(name, count):
         print(f"  skip_fraction={frac:.4f} {rep}", flush=True)
         assert rep.ok(), str(rep)
         del o, lse, mask
+
+
+def test_prefill_work_queue_reuse_and_streams():
+    """The persistent grid takes work items from a per-call device counter
+    pair that the call's last workgroup returns to zero. More calls than
+    there are counter slots, alternating between two streams with outputs
+    pre-filled with NaN, must each reproduce the first call's bytes (a lost
+    or doubly taken item would leave NaN or differ)."""
+    import torch
+    import long_context_tiled_amd as lib
+    # 2 x 4 KV groups x 64 query tiles = 512 work items, more than the CUs
+    cfg = _case(B=2, Hq=16, Hkv=4, N=4096, d=128, causal=True, sinks=True, band=True,
+                id=16)
+    q, k, v = synth.make_prefill(cfg)
+    dq, dk, dv = _dev(q), _dev(k), _dev(v)
+    B, Hq, N, d = q.shape
+    o_ref = torch.empty((B, Hq, N, d), dtype=torch.float32, device="cuda")
+    l_ref = torch.empty((B, Hq, N), dtype=torch.float32, device="cuda")
+    lib.attn_prefill(dq, dk, dv, o_ref, l_ref, True, 4.0)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [(torch.empty_like(o_ref), torch.empty_like(l_ref)) for _ in streams]
+    bad = []
+    for i in range(1100):
+        s = i % 2
+        o, l = outs[s]
+        with torch.cuda.stream(streams[s]):
+            o.fill_(math.nan)
+            l.fill_(math.nan)
+            lib.attn_prefill(dq, dk, dv, o, l, True, 4.0)
+        if i % 2 == 1 or i == 1099:
+            torch.cuda.synchronize()
+            for j in ((0, 1) if i % 2 == 1 else (0,)):
+                oj, lj = outs[j]
+                if not (torch.equal(oj, o_ref) and torch.equal(lj, l_ref)):
+                    bad.append(i - (i % 2) + j)
+    print(f"[prefill] 1100 calls on two streams: {len(bad)} differ", flush=True)
+    assert not bad, bad[:10]
