@@ -24,7 +24,10 @@ Hkv=8) causal prefill shape in the 128K one's place; the default line is the
 Beside the step, the same prefill with block-quantised fp8 QK^T
 (``prefill_qk8``: time including the quantisers, TFLOP/s dense-equivalent,
 fraction of the bf16 peak and of the fp8/bf16 mixed peak, drift from the
-exact prefill, tau sweep), the 8K and 32K causal prefill workloads are timed alone
+exact prefill, tau sweep), the same prefill with the SAS exponential of degree
+2 and 3 (``prefill_sas2``, ``prefill_sas3``: TFLOP/s dense-equivalent, time
+relative to the exact prefill, drift from it, tau sweep), the 8K and 32K
+causal prefill workloads are timed alone
 (``prefill_8k``, ``prefill_32k``: TFLOP/s, fraction of the bf16 peak, their
 tau sweeps), and the same decode workload is run over the 4-bit asymmetric
 KV cache (attn_kv_quantize_q4 once, then attn_decode_q4 timed like the bf16
@@ -319,7 +322,8 @@ def main():
     ap.add_argument("--no-q4", action="store_true",
                     help="skip the 4-bit and 2-bit KV-cache decodes measured beside the step")
     ap.add_argument("--no-sas", action="store_true",
-                    help="skip the decodes with the SAS exponential measured beside the step")
+                    help="skip the decodes and the prefill with the SAS exponential measured "
+                         "beside the step")
     ap.add_argument("--prefill-workload", default="prefill_128k",
                     choices=["prefill_128k", "prefill_32k", "prefill_8k"],
                     help="prefill shape of the step (default: the 128K one)")
@@ -608,6 +612,42 @@ def main():
                                    avg_ms=round(q8_ms, 4), per_launch_flops=dense_flops)
         del qws
         torch.cuda.empty_cache()
+
+    if run_p and args.only == "both" and not args.no_sas:
+        # The step's prefill with the SAS exponential (degree 2 and 3): time,
+        # and how far its outputs move from the exact prefill's on this input.
+        prefill(math.inf)
+        torch.cuda.synchronize()
+        o_ex, l_ex = po.clone(), plse.clone()
+        for deg in (2, 3):
+            def prefill_sas(tau, mask=None, deg=deg):
+                lib.attn_prefill_sas(tq, tk, tv, po, plse, True, tau, deg, mask)
+
+            warm_up(lambda: prefill_sas(math.inf), args.warmup)
+            ts = Timer()
+            torch.cuda.synchronize()
+            for _ in range(args.steps):
+                with ts:
+                    prefill_sas(math.inf)
+            torch.cuda.synchronize()
+            s_ms = float(np.mean(ts.ms()))
+            drift_o = float((po - o_ex).abs().max())
+            drift_l = float((plse - l_ex).abs().max())
+            sweep = []
+            if not args.no_sweep:
+                for tau in pcfg["taus"][1:]:
+                    t = Timer()
+                    for _ in range(3):
+                        with t:
+                            prefill_sas(tau)
+                    torch.cuda.synchronize()
+                    sweep.append(dict(tau=str(tau), ms=round(float(np.median(t.ms())), 4)))
+            out[f"prefill_sas{deg}"] = dict(
+                value=round(dense_flops / (s_ms * 1e-3) / 1e12, 3), unit="TFLOP/s",
+                ms=round(s_ms, 4), vs_exact=round(p_ms / s_ms, 4),
+                max_abs_o_drift=drift_o, max_abs_lse_drift=drift_l, tau_sweep=sweep,
+                kernel=f"prefill_kernel<128,true,4,5,false,false,{deg}>")
+        del o_ex, l_ex
 
     if run_p and args.only == "both" and not args.no_other_prefill:
         # the other causal prefill workloads, timed alone like the step's

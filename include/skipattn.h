@@ -134,6 +134,27 @@ int attn_prefill_chunk_cap(const void* q, const void* k, const void* v, float* o
                            uint8_t* skip_mask, void* stream);
 
 /*
+ * attn_prefill_sas - attn_prefill with the Sparse Activated SoftMax
+ * exponential (TurboAttention talk page, "Technical Deep Dive", its Sparse
+ * Activated SoftMax part): every exponential of each query row's online
+ * softmax, the probabilities e^-(m - s) and the rescale factor when a kept
+ * tile raises the row's running maximum m, is taken as T[n] p(f), with
+ * n = floor(x), f = x - n for the gap x in logits, T[n] = e^-n for n < 6 and
+ * 0 from 6 on, and p the least-squares polynomial of degree `degree` (2 or
+ * 3) for e^-f on [0, 1] (the exponential of attn_decode_sas). The skip
+ * decisions, outputs and mask are those of attn_prefill; `degree` 0 is
+ * attn_prefill itself. Results depend on the order in which the running
+ * maximum rises (ascending key tiles, as for the rule). It computes more
+ * vector instructions per score than the exact exponential (the exponential
+ * unit still gives e^-n), so it is slower; it exists as the pages' option.
+ * Errors as for attn_prefill, and SKIPATTN_EINVAL for another degree.
+ */
+int attn_prefill_sas(const void* q, const void* k, const void* v, float* o,
+                     float* lse, int B, int Hq, int Hkv, int N, int d,
+                     int causal, float tau, int degree, uint8_t* skip_mask,
+                     void* stream);
+
+/*
  * attn_prefill_qk8 - attn_prefill with QK^T on block-quantised 8-bit
  * operands (TurboAttention talk page, "Technical Deep Dive" and "Key
  * Findings": symmetric 8-bit quantisation of the matrix-product operands,

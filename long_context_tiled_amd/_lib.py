@@ -25,7 +25,7 @@ EXPORTS = ("attn_prefill", "attn_decode", "attn_decode_workspace_bytes",
            "attn_kv_quantize_q4", "attn_decode_q4", "attn_decode_q4_check",
            "attn_prefill_chunk", "attn_prefill_chunk_check", "attn_kv_quantize_q4_range",
            "attn_kv_quantize_q2", "attn_kv_quantize_q2_range", "attn_decode_q2",
-           "attn_decode_q2_check", "attn_decode_sas", "attn_decode_q4_sas",
+           "attn_decode_q2_check", "attn_decode_sas", "attn_decode_q4_sas", "attn_prefill_sas",
            "attn_decode_q2_sas", "attn_prefill_chunk_cap", "attn_decode_cap",
            "attn_decode_q4_cap", "attn_decode_q2_cap", "attn_decode_noalloc",
            "attn_prefill_qk8", "attn_prefill_qk8_workspace_bytes")
@@ -65,6 +65,8 @@ def load() -> ctypes.CDLL:
     lib.attn_decode.restype = i
     lib.attn_decode_sas.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, f, i, u8p, vp, sz, vp]
     lib.attn_decode_sas.restype = i
+    lib.attn_prefill_sas.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, i, f, i, u8p, vp]
+    lib.attn_prefill_sas.restype = i
     lib.attn_decode_cap.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, i, f, i, u8p, vp, sz,
                                     vp]
     lib.attn_decode_cap.restype = i
@@ -154,6 +156,27 @@ def attn_prefill(q, k, v, o, lse, causal: bool, tau: float, skip_mask=None,
     rc = load().attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq,
                              Hkv, N, d, int(bool(causal)), float(tau),
                              _ptr(skip_mask), _stream(stream))
+    _raise(rc)
+
+
+def attn_prefill_sas(q, k, v, o, lse, causal: bool, tau: float, degree: int, skip_mask=None,
+                     stream=None) -> None:
+    """Enqueue attn_prefill_sas: attn_prefill with the SAS exponential of
+    polynomial degree ``degree`` (2 or 3; 0 = exact)."""
+    import torch
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    _check(q, "q", torch.bfloat16, (B, Hq, N, d))
+    _check(k, "k", torch.bfloat16, (B, Hkv, N, d))
+    _check(v, "v", torch.bfloat16, (B, Hkv, N, d))
+    _check(o, "o", torch.float32, (B, Hq, N, d))
+    _check(lse, "lse", torch.float32, (B, Hq, N))
+    if skip_mask is not None:
+        nt = (N + TILE - 1) // TILE
+        _check(skip_mask, "skip_mask", torch.uint8, (B, Hq, nt, nt))
+    rc = load().attn_prefill_sas(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N,
+                                 d, int(bool(causal)), float(tau), int(degree), _ptr(skip_mask),
+                                 _stream(stream))
     _raise(rc)
 
 
@@ -465,8 +488,9 @@ def decode_q2(q, cache, L: int, tau: float = math.inf, want_mask: bool = False,
 # ---- allocation conveniences around the two bf16 entry points ----
 
 def prefill(q, k, v, causal: bool, tau: float = math.inf, want_mask: bool = False,
-            stream=None):
-    """Allocate outputs with torch and call attn_prefill. Returns (o, lse, mask)."""
+            stream=None, sas: int = 0):
+    """Allocate outputs with torch and call attn_prefill (attn_prefill_sas of
+    polynomial degree ``sas`` if nonzero). Returns (o, lse, mask)."""
     import torch
     B, Hq, N, d = q.shape
     o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
@@ -475,7 +499,10 @@ def prefill(q, k, v, causal: bool, tau: float = math.inf, want_mask: bool = Fals
     if want_mask:
         nt = (N + TILE - 1) // TILE
         mask = torch.empty((B, Hq, nt, nt), dtype=torch.uint8, device=q.device)
-    attn_prefill(q, k, v, o, lse, causal, tau, mask, stream)
+    if sas:
+        attn_prefill_sas(q, k, v, o, lse, causal, tau, sas, mask, stream)
+    else:
+        attn_prefill(q, k, v, o, lse, causal, tau, mask, stream)
     return o, lse, mask
 
 

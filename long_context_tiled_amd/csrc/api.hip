@@ -142,7 +142,7 @@ namespace {
 
 int prefill_launch(const void* q, const void* k, const void* v, float* o, float* lse, int B,
                    int Hq, int Hkv, int Nq, int N, int cap, int d, int causal, float tau,
-                   uint8_t* skip_mask, void* stream) {
+                   uint8_t* skip_mask, void* stream, int sas = 0) {
   if (int e = prefill_check(q, k, v, o, lse, B, Hq, Hkv, Nq, N, cap, d, causal, tau, skip_mask))
     return e;
   if (B == 0 || Nq == 0) return SKIPATTN_OK;
@@ -150,8 +150,10 @@ int prefill_launch(const void* q, const void* k, const void* v, float* o, float*
                           Hq, Hkv,   N,  d,  causal,
                           Nq, causal ? (N - Nq) / SKIPATTN_TILE : 0,
                           cap, tau_raw(tau, d), exp2_scale(d), stream};
+  a.sas = sas;
   const int lr = skipattn::launch_prefill(a);
   if (lr == -1) return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
+  if (lr == -3) return fail(SKIPATTN_EUNSUPPORTED, "SAS prefill: whole-sequence bf16 only");
   if (lr != 0) return fail(SKIPATTN_EHIP, "prefill: device query for the work queue failed");
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(SKIPATTN_EHIP, "prefill launch: %s", hipGetErrorString(err));
@@ -278,6 +280,15 @@ int attn_prefill(const void* q, const void* k, const void* v, float* o, float* l
                  int B, int Hq, int Hkv, int N, int d, int causal, float tau,
                  uint8_t* skip_mask, void* stream) {
   return prefill_launch(q, k, v, o, lse, B, Hq, Hkv, N, N, N, d, causal, tau, skip_mask, stream);
+}
+
+int attn_prefill_sas(const void* q, const void* k, const void* v, float* o, float* lse, int B,
+                     int Hq, int Hkv, int N, int d, int causal, float tau, int degree,
+                     uint8_t* skip_mask, void* stream) {
+  if (degree != 0 && degree != 2 && degree != 3)
+    return fail(SKIPATTN_EINVAL, "SAS degree must be 0, 2 or 3 (got %d)", degree);
+  return prefill_launch(q, k, v, o, lse, B, Hq, Hkv, N, N, N, d, causal, tau, skip_mask, stream,
+                        degree);
 }
 
 size_t attn_prefill_qk8_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {

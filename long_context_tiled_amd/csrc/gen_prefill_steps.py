@@ -120,8 +120,9 @@ class Ins:
 class Step:
     """One step variant for one head dim and buffer assignment."""
 
-    def __init__(self, d, variant, x, y, budget, loop=False, dma=False, f8=False):
+    def __init__(self, d, variant, x, y, budget, loop=False, dma=False, f8=False, sas=0):
         self.loop = loop
+        self.sas = sas        # 0: exp2; 2 or 3: the SAS exponential of that degree
         self.dma = dma
         self.d = d
         self.f8 = f8          # QK^T on fp8 codes (32x32x64, 16 passes), PV in bf16
@@ -281,6 +282,73 @@ class Step:
                    tag=("pv", ks))
 
     def exp_stream(self):
+        if self.sas:
+            return self.sas_stream()
+        return self.exp2_stream()
+
+    def sas_stream(self):
+        """The SAS exponential per score: x = (mref - s) / sqrt(d) clamped to
+        [0, 7] (nm = mref / sqrt(d), %[c] = 1 / sqrt(d)), n = floor x,
+        f = x - n, P = e^-n (the exponential unit on -n log2 e) x
+        clamp(6 - n, 0, 1) (0 from n = 6 on) x p(f) (Horner on the SGPR
+        coefficients %[sa0..3]); then pack, sums as exp2_stream. Pairs use two
+        register slots: P in v48-v51, two temporaries per score in v52-v53
+        and v40-v45 (the vote temporaries: every vote instruction of a step
+        follows its last exponential)."""
+        heads, tails = [], []
+        first = {0: True, 1: True}
+        tmp = [52, 53, 40, 41, 42, 43, 44, 45]
+        deg = self.sas
+        for gp in range(32):
+            ch, i2 = gp >> 2, gp & 3
+            kp, nb = ch >> 1, ch & 1
+            a = kp >> 1
+            r0 = 8 * (kp & 1) + 2 * i2
+            sl = gp % 2
+            ss = [f"v{self.s_reg(self.x, a, nb, r0 + i)}" for i in range(2)]
+            ts = [f"v{TREG + 2 * sl + i}" for i in range(2)]
+            us = [f"v{tmp[4 * sl + 2 * i]}" for i in range(2)]
+            ws = [f"v{tmp[4 * sl + 2 * i + 1]}" for i in range(2)]
+            w = f"v{PREG + 4 * (2 * kp + nb) + i2}"
+            ps = f"v{PSUM + nb}"
+            nm = f"%[nm{nb}]"
+            seqs = []
+            for sc, t, u, wf in zip(ss, ts, us, ws):
+                q = [Ins(f"v_fma_f32 {t}, -{sc}, %[c], {nm}", "valu", wr=[t], rd=[sc]),
+                     Ins(f"v_med3_f32 {t}, {t}, 0, %[c7]", "valu", wr=[t], rd=[t]),
+                     Ins(f"v_floor_f32 {u}, {t}", "valu", wr=[u], rd=[t]),
+                     Ins(f"v_sub_f32 {wf}, {t}, {u}", "valu", wr=[wf], rd=[t, u]),
+                     Ins(f"v_sub_f32_e64 {t}, %[c6], {u} clamp", "valu", wr=[t], rd=[u]),
+                     Ins(f"v_mul_f32 {u}, 0xbfb8aa3b, {u}", "valu", wr=[u], rd=[u]),
+                     Ins(f"v_exp_f32 {u}, {u}", "trans", wr=[u], rd=[u]),
+                     Ins(f"v_mul_f32 {u}, {u}, {t}", "valu", wr=[u], rd=[u, t]),
+                     Ins(f"v_mov_b32 {t}, %[sa{deg}]", "valu", wr=[t])]
+                q += [Ins(f"v_fma_f32 {t}, {t}, {wf}, %[sa{j}]", "valu", wr=[t], rd=[t, wf])
+                      for j in range(deg - 1, -1, -1)]
+                q.append(Ins(f"v_mul_f32 {t}, {t}, {u}", "valu", wr=[t], rd=[t, u]))
+                seqs.append(q)
+            heads.append([x for pair in zip(*seqs) for x in pair])
+            t0, t1 = ts
+            tail = [Ins(f"v_cvt_pk_bf16_f32 {w}, {t0}, {t1}", "valu", wr=[w], rd=[t0, t1],
+                        tag=("pf", kp))]
+            if first[nb]:
+                tail.append(Ins(f"v_add_f32 {ps}, {t0}, {t1}", "valu", wr=[ps], rd=[t0, t1]))
+                first[nb] = False
+            else:
+                tail += [Ins(f"v_add_f32 {t0}, {t0}, {t1}", "valu", wr=[t0], rd=[t0, t1]),
+                         Ins(f"v_add_f32 {ps}, {ps}, {t0}", "valu", wr=[ps], rd=[ps, t0])]
+            tails.append(tail)
+        # pair gp's sequence runs ahead of pair gp - 1's pack and sums
+        out = list(heads[0])
+        for gp in range(1, 32):
+            out += heads[gp] + tails[gp - 1]
+        out += tails[31]
+        for nb in range(2):
+            out.append(Ins(f"v_add_f32 %[lo{nb}], %[lo{nb}], v{PSUM + nb}", "valu",
+                           rd=[f"v{PSUM + nb}"]))
+        return out
+
+    def exp2_stream(self):
         """Per score pair: scale-and-shift, exp2, pack to bf16, pair sum into
         this tile's partial row sum; at the end each partial sum joins the
         running row sum once. (Adding every exponential straight into the
@@ -772,8 +840,8 @@ def _rename(lines, mapping):
 QA = {"A": "%[qa0]", "B": "%[qa1]"}   # fp8: q scale x k scale of the tile in buffer A / B
 
 
-def _step_lines(d, variant, x, y, budget, dma=True, f8=False):
-    st = Step(d, variant, x, y, budget, loop=True, dma=dma, f8=f8).build().fix_hazards()
+def _step_lines(d, variant, x, y, budget, dma=True, f8=False, sas=0):
+    st = Step(d, variant, x, y, budget, loop=True, dma=dma, f8=f8, sas=sas).build().fix_hazards()
     return _rename(st.out, {"%[mi0]": "%[m0]", "%[mi1]": "%[m1]", "%[mo0]": "%[m0]",
                             "%[mo1]": "%[m1]", "%[lo0]": "%[ls0]", "%[lo1]": "%[ls1]",
                             "%[qa]": QA[y]})
@@ -807,17 +875,38 @@ def _mask_lines(d, y):
     return body
 
 
-def _rescale_lines(d):
-    """alpha = m > mref ? exp2((mref - m) c) : 1; lsum *= alpha; mref = max;
-    O half nb *= alpha_nb. Drains the MFMAs first."""
+def _sas_lines(x, t, u, w, deg):
+    """x := SAS(x) for x in raw units times %[c] = 1 / sqrt(d) already (the
+    sequence of Step.sas_stream, hazards written out)."""
+    return [f"v_med3_f32 {x}, {x}, 0, %[c7]",
+            f"v_floor_f32 {u}, {x}",
+            f"v_sub_f32 {w}, {x}, {u}",
+            f"v_sub_f32_e64 {t}, %[c6], {u} clamp",
+            f"v_mul_f32 {u}, 0xbfb8aa3b, {u}",
+            f"v_exp_f32 {u}, {u}", "s_nop 0",
+            f"v_mul_f32 {u}, {u}, {t}",
+            f"v_mov_b32 {x}, %[sa{deg}]"] + [
+            f"v_fma_f32 {x}, {x}, {w}, %[sa{j}]" for j in range(deg - 1, -1, -1)] + [
+            f"v_mul_f32 {x}, {x}, {u}"]
+
+
+def _rescale_lines(d, sas=0):
+    """alpha = m > mref ? exp2((mref - m) c) : 1 (SAS: SAS((m - mref) c),
+    c = 1 / sqrt(d)); lsum *= alpha; mref = max; O half nb *= alpha_nb.
+    Drains the MFMAs first."""
     MB = d // 32
     al = ["v52", "v53"]
     body = ["s_nop 7", "s_nop 7", "s_nop 7"]
     for nb in range(2):
-        body += [f"v_sub_f32 {al[nb]}, %[mr{nb}], %[m{nb}]",
-                 f"v_mul_f32 {al[nb]}, {al[nb]}, %[c]",
-                 f"v_exp_f32 {al[nb]}, {al[nb]}",
-                 f"v_cmp_gt_f32 vcc, %[m{nb}], %[mr{nb}]",
+        if sas:
+            body += [f"v_sub_f32 {al[nb]}, %[m{nb}], %[mr{nb}]",
+                     f"v_mul_f32 {al[nb]}, %[c], {al[nb]}"]
+            body += _sas_lines(al[nb], f"v{TREG}", f"v{TREG + 1}", f"v{TREG + 2}", sas)
+        else:
+            body += [f"v_sub_f32 {al[nb]}, %[mr{nb}], %[m{nb}]",
+                     f"v_mul_f32 {al[nb]}, {al[nb]}, %[c]",
+                     f"v_exp_f32 {al[nb]}, {al[nb]}"]
+        body += [f"v_cmp_gt_f32 vcc, %[m{nb}], %[mr{nb}]",
                  f"v_cndmask_b32 {al[nb]}, 1.0, {al[nb]}, vcc",
                  f"v_mul_f32 %[ls{nb}], %[ls{nb}], {al[nb]}",
                  f"v_max_f32 %[mr{nb}], %[mr{nb}], %[m{nb}]"]
@@ -853,6 +942,13 @@ LOOP_ARGS_F8_DOC = """
 // fp8 QK^T: ksp points at the K tile scales of this KV head (one fp32 per
 // 64-key tile), sqv is this wave's Q tile scale, nkbm1 the last key tile,
 // wlv the wave's LDS base for V tile copies (wl: for K)."""
+LOOP_ARGS_SAS_DOC = """
+// SAS exponential: c is 1 / sqrt(d) (not log2(e) / sqrt(d)), lazy is 0 (the
+// reference max is always the running max), sa the polynomial's
+// coefficients a0 .. a3 (a3 unused at degree 2), c6 = 6, c7 = 7."""
+LOOP_ARGS_SAS_FIELDS = """
+  float sa[4];
+  float c6, c7;"""
 LOOP_ARGS_F8_FIELDS = """
   uint64_t ksp;
   float sqv;
@@ -860,7 +956,7 @@ LOOP_ARGS_F8_FIELDS = """
   uint32_t wlv;"""
 
 
-def loop_cxx(d, causal, budget, f8=False):
+def loop_cxx(d, causal, budget, f8=False, sas=0):
     MB = d // 32
     row_bytes = 2 * d                        # V rows (bf16)
     krow = d if f8 else 2 * d                # K rows: fp8 codes or bf16
@@ -891,6 +987,8 @@ def loop_cxx(d, causal, budget, f8=False):
                 "v_add_u32 %[vb0], %[t0], %[tr0]", "v_add_u32 %[vb1], %[t0], %[tr1]"]
 
     def nmc(x):
+        if sas:  # mref / sqrt(d), the exponent input's offset
+            return ["v_mul_f32 %[nm0], %[mr0], %[c]", "v_mul_f32 %[nm1], %[mr1], %[c]"]
         out = ["v_mul_f32 %[nm0], %[mr0], %[c]", "v_mul_f32 %[nm1], %[mr1], %[c]",
                "v_xor_b32 %[nm0], 0x80000000, %[nm0]", "v_xor_b32 %[nm1], 0x80000000, %[nm1]"]
         if f8:
@@ -992,9 +1090,9 @@ def loop_cxx(d, causal, budget, f8=False):
         L += kaddr() + ["s_add_u32 %[t0], %[kb], 1"] + rare("%[t0]")
         L += ["s_cmp_lg_u64 %[keep], 0", f"s_cbranch_scc0 {lab('skip' + t)}",
               "s_cmp_lg_u64 %[grow], 0", f"s_cbranch_scc0 {lab('nr' + t)}"]
-        L += _rescale_lines(d)
+        L += _rescale_lines(d, sas)
         L += [f"{lab('nr' + t)}:"] + nmc(x) + vaddr()
-        L += _step_lines(d, "full", x, y, budget, f8=f8)
+        L += _step_lines(d, "full", x, y, budget, f8=f8, sas=sas)
         L += [f"s_branch {lab('voted' + t)}", f"{lab('skip' + t)}:"]
         L += _step_lines(d, "qk", y, y, budget, f8=f8)
         L += [f"{lab('voted' + t)}:", "s_add_u32 %[t1], %[kb], 1"]
@@ -1003,9 +1101,9 @@ def loop_cxx(d, causal, budget, f8=False):
               f"{lab('last' + t)}:", "s_cmp_eq_u32 %[t0], %[nkbw]", f"s_cbranch_scc0 {lab('idle' + t)}",
               "s_cmp_lg_u64 %[keep], 0", f"s_cbranch_scc0 {lab('idle' + t)}",
               "s_cmp_lg_u64 %[grow], 0", f"s_cbranch_scc0 {lab('nrl' + t)}"]
-        L += _rescale_lines(d)
+        L += _rescale_lines(d, sas)
         L += [f"{lab('nrl' + t)}:"] + nmc(x) + vaddr()
-        L += _step_lines(d, "pv", x, x, budget, f8=f8)
+        L += _step_lines(d, "pv", x, x, budget, f8=f8, sas=sas)
         L += [f"s_branch {lab('ld' + t)}", f"{lab('idle' + t)}:"]
         L += dma_alone()
         L += [f"{lab('ld' + t)}:", "s_mov_b64 %[keep], 0",
@@ -1042,6 +1140,9 @@ def loop_cxx(d, causal, budget, f8=False):
                  '[t5] "=&s"(s32[8])']
         ins_ += ['[ksp] "s"(a.ksp)', '[sqv] "v"(a.sqv)', '[nkbm1] "s"(a.nkbm1)', '[wlv] "s"(a.wlv)']
         nvt, ns32 = 14, 9
+    if sas:
+        ins_ += [f'[sa{j}] "s"(a.sa[{j}])' for j in range(sas + 1)]
+        ins_ += ['[c6] "s"(a.c6)', '[c7] "s"(a.c7)']
     clob = [f"v{r}" for r in range(VOTE, 256)]
     clob += [f"a{r}" for r in range(OB, OB + 32 * MB)] + ["vcc", "scc", "m0"]
     body = []
@@ -1050,7 +1151,8 @@ def loop_cxx(d, causal, budget, f8=False):
     # %[mpp] is the 64-bit pair (mp, mp_hi): spelled out below
     text = "\n".join(f'      "{t}\\n\\t"' for t in body)
     head = (f"// The key loop of one wave, d = {d}, {'causal' if causal else 'full'} attention"
-            f"{', QK^T on fp8 codes' if f8 else ''} ({len(body)} lines)")
+            f"{', QK^T on fp8 codes' if f8 else ''}"
+            f"{f', SAS exponential of degree {sas}' if sas else ''} ({len(body)} lines)")
     name = f"key_loop_{'causal' if causal else 'full'}"
     return "\n".join([
         head,
@@ -1074,9 +1176,10 @@ def main(out_path=None):
              "// Per-key-tile steps of the prefill kernel (see the script's docstring for",
              "// the schedule, the register plan and the hazard rules).",
              "#pragma once", ""]
-    for d, budget, f8 in ((128, 26.0, False), (64, 30.0, False), (128, 26.0, True),
-                          (64, 30.0, True)):
-        ns = f"d{d}f8" if f8 else f"d{d}"
+    for d, budget, f8, sas in ((128, 26.0, False, 0), (64, 30.0, False, 0), (128, 26.0, True, 0),
+                               (64, 30.0, True, 0), (128, 26.0, False, 2), (128, 26.0, False, 3),
+                               (64, 30.0, False, 2), (64, 30.0, False, 3)):
+        ns = f"d{d}f8" if f8 else (f"d{d}s{sas}" if sas else f"d{d}")
         parts.append(f"namespace {ns} {{")
         for h in helpers_cxx(d, f8):
             parts.append(h)
@@ -1084,10 +1187,12 @@ def main(out_path=None):
         ipwv = 64 * 2 * d // 1024 // 4
         ipwk = 64 * d // 1024 // 4 if f8 else ipwv
         parts.append(LOOP_ARGS.format(ipwk=ipwk, ipwv=ipwv,
-                                      f8doc=LOOP_ARGS_F8_DOC if f8 else "",
-                                      f8fields=LOOP_ARGS_F8_FIELDS if f8 else ""))
+                                      f8doc=LOOP_ARGS_F8_DOC if f8 else (
+                                          LOOP_ARGS_SAS_DOC if sas else ""),
+                                      f8fields=LOOP_ARGS_F8_FIELDS if f8 else (
+                                          LOOP_ARGS_SAS_FIELDS if sas else "")))
         for causal in (True, False):
-            parts.append(loop_cxx(d, causal, budget, f8))
+            parts.append(loop_cxx(d, causal, budget, f8, sas))
             parts.append("")
         parts.append(f"}}  // namespace {ns}")
         parts.append("")

@@ -25,6 +25,9 @@ struct PrefillArgs {
   // both null for bf16 q and k
   const float* qscale = nullptr;
   const float* kscale = nullptr;
+  // 0: exact exponentials; 2 or 3: the SAS exponential of that degree (bf16
+  // whole-sequence prefill only)
+  int sas = 0;
 };
 
 struct DecodeArgs {
@@ -76,9 +79,9 @@ struct DecodeQ4Args {
 };
 
 // Each returns 0 when the kernels were enqueued, nonzero if the grid cannot
-// be expressed (launch_prefill: -1, or -2 when the device's work-queue
-// address or compute-unit count cannot be read); launch errors are read back
-// by the caller.
+// be expressed (launch_prefill: -1, -2 when the device's work-queue address
+// or compute-unit count cannot be read, -3 for an SAS request outside the
+// bf16 whole-sequence prefill); launch errors are read back by the caller.
 int launch_prefill(const PrefillArgs& a);
 int launch_decode(const DecodeArgs& a);
 int launch_kv_quantize_q4(const QuantArgs& a);

@@ -61,6 +61,7 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "sas.hpp"
 
 namespace skipattn {
 
@@ -159,20 +160,28 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, lds_void* lds, 
 
 // Calls the d = 128 or d = 64 version of a generated block (bf16 QK^T, or
 // fp8 QK^T when F8_ is set).
-#define SKA_CALL(D_, F8_, fn, ...)                                  \
-  do {                                                              \
-    if constexpr ((D_) == 128 && !(F8_)) d128::fn(__VA_ARGS__);     \
-    else if constexpr ((D_) == 64 && !(F8_)) d64::fn(__VA_ARGS__);  \
-    else if constexpr ((D_) == 128) d128f8::fn(__VA_ARGS__);        \
-    else d64f8::fn(__VA_ARGS__);                                    \
+#define SKA_CALL(D_, F8_, SAS_, fn, ...)                                         \
+  do {                                                                           \
+    if constexpr ((SAS_) == 2 && (D_) == 128) d128s2::fn(__VA_ARGS__);           \
+    else if constexpr ((SAS_) == 2) d64s2::fn(__VA_ARGS__);                      \
+    else if constexpr ((SAS_) == 3 && (D_) == 128) d128s3::fn(__VA_ARGS__);      \
+    else if constexpr ((SAS_) == 3) d64s3::fn(__VA_ARGS__);                      \
+    else if constexpr ((D_) == 128 && !(F8_)) d128::fn(__VA_ARGS__);             \
+    else if constexpr ((D_) == 64 && !(F8_)) d64::fn(__VA_ARGS__);              \
+    else if constexpr ((D_) == 128) d128f8::fn(__VA_ARGS__);                    \
+    else d64f8::fn(__VA_ARGS__);                                                \
   } while (0)
 
-template <int D, bool F8>
+template <int D, bool F8, int SAS>
 struct LoopArgsOf;
-template <> struct LoopArgsOf<128, false> { using type = d128::LoopArgs; };
-template <> struct LoopArgsOf<64, false> { using type = d64::LoopArgs; };
-template <> struct LoopArgsOf<128, true> { using type = d128f8::LoopArgs; };
-template <> struct LoopArgsOf<64, true> { using type = d64f8::LoopArgs; };
+template <> struct LoopArgsOf<128, false, 0> { using type = d128::LoopArgs; };
+template <> struct LoopArgsOf<64, false, 0> { using type = d64::LoopArgs; };
+template <> struct LoopArgsOf<128, true, 0> { using type = d128f8::LoopArgs; };
+template <> struct LoopArgsOf<64, true, 0> { using type = d64f8::LoopArgs; };
+template <> struct LoopArgsOf<128, false, 2> { using type = d128s2::LoopArgs; };
+template <> struct LoopArgsOf<64, false, 2> { using type = d64s2::LoopArgs; };
+template <> struct LoopArgsOf<128, false, 3> { using type = d128s3::LoopArgs; };
+template <> struct LoopArgsOf<64, false, 3> { using type = d64s3::LoopArgs; };
 
 // F8: Q and K are fp8 (E4M3) codes with one fp32 scale per 64-row Q tile
 // (qsc, [B, Hq, ceil(Nq/64)]) and per 64-key K tile (ksc, [B, Hkv,
@@ -180,7 +189,12 @@ template <> struct LoopArgsOf<64, true> { using type = d64f8::LoopArgs; };
 // units and each tile's scores are scaled by q scale x k scale where they
 // are used (the skip test's tile maxima and the exponent input). V and PV
 // stay bf16.
-template <int D, bool CAUSAL, int HPW, int STAGES, bool CHUNK, bool F8>
+// SAS (2 or 3, bf16 QK^T only): every exponential of the online softmax, the
+// probabilities and the rescale factor, is the SAS exponential of that
+// degree (T[floor x] p(x - floor x), x the logit gap), with the reference
+// maximum kept equal to the running maximum (no deferred rescale: SAS of a
+// product is not the product of SAS values).
+template <int D, bool CAUSAL, int HPW, int STAGES, bool CHUNK, bool F8, int SAS>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void prefill_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ o,
@@ -322,19 +336,19 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
     }
 
     // Prologue: Q tiles (slots 3-4) and K/V tiles 0-2 copied; Q^T into AGPRs.
-    SKA_CALL(D, F8, zero_o);
+    SKA_CALL(D, F8, SAS, zero_o);
     for (int t = 0; t < 3; ++t)
       if (t < nkb_wg) issue_tile(t);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if (0 < nkb_w) SKA_CALL(D, F8, load_q, smem_lds + q_lds + frag);
+    if (0 < nkb_w) SKA_CALL(D, F8, SAS, load_q, smem_lds + q_lds + frag);
     __syncthreads();  // slots 3-4 are K/V slots from here on
 
     // The key loop runs as one generated block (barriers, tile copies, the
     // pipelined steps, votes, rescales, masks). Its scalar operands must be
     // wave-uniform.
     const float lazy_raw = 8.0f / c;  // 8 in log2 units, as a raw-score gap
-    typename LoopArgsOf<D, F8>::type la;
+    typename LoopArgsOf<D, F8, SAS>::type la;
     la.frag = frag;
     la.tr0 = tr0[0];
     la.tr1 = tr0[1];
@@ -357,6 +371,14 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
     la.N = N;
     la.tau = tau_raw;
     la.c = c;
+    if constexpr (SAS != 0) {
+      la.c = c * kLn2;  // 1 / sqrt(d): the SAS argument is in logits
+      la.lazy = 0.f;
+#pragma unroll
+      for (int j = 0; j <= SAS; ++j) la.sa[j] = SAS == 2 ? kSasPoly2[j] : kSasPoly3[j];
+      la.c6 = 6.f;
+      la.c7 = 7.f;
+    }
     auto rsrc = [&](const void* p, int bytes) {
       const uint64_t a = (uint64_t)(uintptr_t)p;
       u32x4 r;
@@ -379,8 +401,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
       la.wlv = smem_lds + (uint32_t)(T::kBytes + wave * IPW * 1024);
     }
     float m[2], mref[2], lsum[2];
-    if constexpr (CAUSAL) SKA_CALL(D, F8, key_loop_causal, la, m, mref, lsum);
-    else SKA_CALL(D, F8, key_loop_full, la, m, mref, lsum);
+    if constexpr (CAUSAL) SKA_CALL(D, F8, SAS, key_loop_causal, la, m, mref, lsum);
+    else SKA_CALL(D, F8, SAS, key_loop_full, la, m, mref, lsum);
     (void)m;
 
     // Claim the next item as this one's key loop ends: a claim made earlier
@@ -403,10 +425,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
       for (int mb = 0; mb < MB; ++mb) {
         float ov[16];
         const int id = 2 * mb + nb;
-        if (id == 0) SKA_CALL(D, F8, read_o_00, ov);
-        if (id == 1) SKA_CALL(D, F8, read_o_01, ov);
-        if (id == 2) SKA_CALL(D, F8, read_o_10, ov);
-        if (id == 3) SKA_CALL(D, F8, read_o_11, ov);
+        if (id == 0) SKA_CALL(D, F8, SAS, read_o_00, ov);
+        if (id == 1) SKA_CALL(D, F8, SAS, read_o_01, ov);
+        if (id == 2) SKA_CALL(D, F8, SAS, read_o_10, ov);
+        if (id == 3) SKA_CALL(D, F8, SAS, read_o_11, ov);
         if constexpr (MB == 4 && !F8) {
           if (id == 4) d128::read_o_20(ov);
           if (id == 5) d128::read_o_21(ov);
@@ -502,7 +524,7 @@ int queue_and_cus(uint32_t** q, int* ncu) {
 }
 }  // namespace
 
-template <int D, bool CAUSAL, int HPW, bool CHUNK, bool F8>
+template <int D, bool CAUSAL, int HPW, bool CHUNK, bool F8, int SAS>
 static int launch_one(const PrefillArgs& a) {
   const int nqb = (a.Nq + kTile - 1) / kTile;
   constexpr int QPW = 4 / HPW;
@@ -518,25 +540,25 @@ static int launch_one(const PrefillArgs& a) {
   queue += 16 * (g_next_slot.fetch_add(1, std::memory_order_relaxed) % kQueueSlots);
   // one workgroup per compute unit (the tile slots fill the LDS)
   const int grid = (int)std::min<long long>(items, ncu);
-  hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, HPW, kStages, CHUNK, F8>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, HPW, kStages, CHUNK, F8, SAS>), dim3((unsigned)grid),
                      dim3(256), 0, (hipStream_t)a.stream, (const uint8_t*)a.q, (const uint8_t*)a.k,
                      (const uint16_t*)a.v, a.o, a.lse, a.mask, a.qscale, a.kscale, a.Hq, a.Hkv,
                      a.Nq, a.N, a.q0t, a.cap, a.tau_raw, a.c, nqg, ny, queue, (int)items);
   return 0;
 }
 
-template <int D, bool CAUSAL, bool CHUNK, bool F8>
+template <int D, bool CAUSAL, bool CHUNK, bool F8, int SAS>
 static int launch_g(const PrefillArgs& a) {
   const int G = a.Hq / a.Hkv;
-  if (G % 4 == 0) return launch_one<D, CAUSAL, 4, CHUNK, F8>(a);
-  if (G % 2 == 0) return launch_one<D, CAUSAL, 2, CHUNK, F8>(a);
-  return launch_one<D, CAUSAL, 1, CHUNK, F8>(a);
+  if (G % 4 == 0) return launch_one<D, CAUSAL, 4, CHUNK, F8, SAS>(a);
+  if (G % 2 == 0) return launch_one<D, CAUSAL, 2, CHUNK, F8, SAS>(a);
+  return launch_one<D, CAUSAL, 1, CHUNK, F8, SAS>(a);
 }
 
 template <int D, bool CAUSAL, bool F8>
 static int launch_h(const PrefillArgs& a) {
-  if (a.Nq != a.N || a.q0t != 0 || a.cap != a.N) return launch_g<D, CAUSAL, true, F8>(a);
-  return launch_g<D, CAUSAL, false, F8>(a);
+  if (a.Nq != a.N || a.q0t != 0 || a.cap != a.N) return launch_g<D, CAUSAL, true, F8, 0>(a);
+  return launch_g<D, CAUSAL, false, F8, 0>(a);
 }
 
 template <bool F8>
@@ -545,7 +567,21 @@ static int launch_f(const PrefillArgs& a) {
   return a.causal ? launch_h<64, true, F8>(a) : launch_h<64, false, F8>(a);
 }
 
+// The SAS key loops exist for the whole-sequence bf16 prefill only.
+template <int SAS>
+static int launch_s(const PrefillArgs& a) {
+  if (a.d == 128)
+    return a.causal ? launch_g<128, true, false, false, SAS>(a)
+                    : launch_g<128, false, false, false, SAS>(a);
+  return a.causal ? launch_g<64, true, false, false, SAS>(a)
+                  : launch_g<64, false, false, false, SAS>(a);
+}
+
 int launch_prefill(const PrefillArgs& a) {
+  if (a.sas != 0) {
+    if (a.qscale != nullptr || a.Nq != a.N || a.q0t != 0 || a.cap != a.N) return -3;
+    return a.sas == 2 ? launch_s<2>(a) : launch_s<3>(a);
+  }
   return a.qscale != nullptr ? launch_f<true>(a) : launch_f<false>(a);
 }
 

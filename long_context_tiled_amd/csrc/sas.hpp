@@ -1,4 +1,5 @@
-// The Sparse Activated SoftMax exponential, shared by the decodes.
+// The Sparse Activated SoftMax exponential, shared by the decodes and the
+// prefill's SAS key loops.
 #pragma once
 
 #include "common.hpp"
@@ -13,14 +14,19 @@ namespace skipattn {
 // exponential unit gives e^-n for the integer n in one instruction, which
 // here stands in for the six-entry table (the same values to fp32
 // rounding); x = +inf gives 0.
+// Coefficients a0 .. a_DEG of p (the prefill's generated key loop takes them
+// as operands).
+constexpr float kSasPoly2[3] = {0.9944886f, -0.9305485f, 0.30871853f};
+constexpr float kSasPoly3[4] = {0.99961364f, -0.99204874f, 0.46246922f, -0.10250045f};
+
 template <int DEG>
 __device__ __forceinline__ float sas_poly(float f) {
   if constexpr (DEG == 2)
-    return __builtin_fmaf(__builtin_fmaf(0.30871853f, f, -0.9305485f), f, 0.9944886f);
+    return __builtin_fmaf(__builtin_fmaf(kSasPoly2[2], f, kSasPoly2[1]), f, kSasPoly2[0]);
   else
-    return __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(-0.10250045f, f, 0.46246922f), f,
-                                         -0.99204874f),
-                          f, 0.99961364f);
+    return __builtin_fmaf(
+        __builtin_fmaf(__builtin_fmaf(kSasPoly3[3], f, kSasPoly3[2]), f, kSasPoly3[1]), f,
+        kSasPoly3[0]);
 }
 
 template <int DEG>

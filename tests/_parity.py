@@ -76,12 +76,16 @@ def _compare_decisions(gpu_dec, ref_dec, margin, visited):
 class PrefillChecker:
     """Caches fp64 copies of K/V per (b, kv head) for repeated block checks."""
 
-    def __init__(self, q_bits, k_bits, v_bits, causal: bool, q0: int = 0, qf=None, kf=None):
+    def __init__(self, q_bits, k_bits, v_bits, causal: bool, q0: int = 0, qf=None, kf=None,
+                 sas: int = 0):
         """q_bits may be a chunk: its row r sits at key position q0 + r
         (q0 a multiple of 64 when causal). ``qf`` / ``kf``, fp64 arrays of
         the same shapes, replace the bf16 Q / K values (e.g. the oracle's
-        dequantised 8-bit Q and K)."""
+        dequantised 8-bit Q and K). ``sas`` = 2 or 3: the reference is the
+        SAS prefill oracle of that degree, and each row's error beyond the
+        slack its SAS steps allow counts against the tolerance."""
         self.q, self.k, self.v = q_bits, k_bits, v_bits
+        self.sas = sas
         self.qf, self.kf = qf, kf
         self.causal = causal
         B, Hq, N, d = q_bits.shape
@@ -106,13 +110,33 @@ class PrefillChecker:
             return np.asarray(self.qf[b, h, r0:r1], np.float64)
         return synth.bf16_bits_to_f64(self.q[b, h, r0:r1])
 
+    def _ref(self, qrows, k, v, qb, tau, forced=None):
+        """o, lse, decisions, margins, slack (rows, 2) or None."""
+        if self.sas:
+            return oracle.sas.prefill_blocks(qrows, k, v, qb + self.q0t, self.causal, tau,
+                                             self.sas, forced)
+        o, lse, dec, margin = oracle.prefill_blocks(qrows, k, v, qb + self.q0t, self.causal,
+                                                    tau, forced)
+        return o, lse, dec, margin, None
+
+    @staticmethod
+    def _errs(o_gpu, lse_gpu, o, lse, slack):
+        if slack is None:
+            return max_abs_err(o_gpu, o), max_abs_err(lse_gpu, lse)
+        eo = np.abs(np.asarray(o_gpu, np.float64) - o).max(axis=1)
+        el = np.abs(np.asarray(lse_gpu, np.float64) - lse)
+        if not (np.all(np.isfinite(eo)) and np.all(np.isfinite(el))):
+            return math.inf, math.inf
+        return (float(np.maximum(eo - slack[:, 1], 0.0).max()),
+                float(np.maximum(el - slack[:, 0], 0.0).max()))
+
     def check_block(self, b, h, qb, tau, o_gpu, lse_gpu, mask_gpu) -> Report:
         """o_gpu/lse_gpu: numpy rows of this block; mask_gpu: (nt,) uint8."""
         rep = Report()
         k, v = self.kv(b, h // self.G)
         r0, r1 = qb * 64, min(self.N, qb * 64 + 64)
         qrows = self.qrows(b, h, r0, r1)
-        o, lse, dec, margin = oracle.prefill_blocks(qrows, k, v, qb + self.q0t, self.causal, tau)
+        o, lse, dec, margin, slack = self._ref(qrows, k, v, qb, tau)
         dec, margin = dec[0], margin[0]
         visited = dec != oracle.NOT_VISITED
         if not np.array_equal(mask_gpu[~visited], dec[~visited]):
@@ -126,12 +150,10 @@ class PrefillChecker:
             bad = np.nonzero((mask_gpu != dec) & visited)[0][:4]
             rep.notes.append(f"b={b} h={h} qb={qb} kb={bad.tolist()} margin={margin[bad].tolist()}")
         if forced is not None:
-            o, lse, _, _ = oracle.prefill_blocks(qrows, k, v, qb + self.q0t, self.causal, tau,
-                                                 forced[None, :])
+            o, lse, _, _, slack = self._ref(qrows, k, v, qb, tau, forced[None, :])
         rep.tiles += int(visited.sum())
         rep.skipped += int((mask_gpu[visited] == 1).sum())
-        rep.o_err = max_abs_err(o_gpu, o)
-        rep.lse_err = max_abs_err(lse_gpu, lse)
+        rep.o_err, rep.lse_err = self._errs(o_gpu, lse_gpu, o, lse, slack)
         return rep
 
 
@@ -166,11 +188,11 @@ class PrefillChecker:
 
 
 def check_prefill(q_bits, k_bits, v_bits, causal, tau, o, lse, mask, blocks=None,
-                  q0: int = 0, qf=None, kf=None) -> Report:
+                  q0: int = 0, qf=None, kf=None, sas: int = 0) -> Report:
     """Compare full GPU outputs (numpy) over the given (b, h, qb) blocks
     (q_bits and the outputs may be a chunk starting at key position q0;
-    qf / kf as for PrefillChecker)."""
-    chk = PrefillChecker(q_bits, k_bits, v_bits, causal, q0, qf, kf)
+    qf / kf / sas as for PrefillChecker)."""
+    chk = PrefillChecker(q_bits, k_bits, v_bits, causal, q0, qf, kf, sas)
     if blocks is None:
         blocks = [(b, h, qb) for b in range(chk.B) for h in range(chk.Hq)
                   for qb in range(chk.nt)]

@@ -223,3 +223,15 @@ def test_noalloc_decode_rejects_before_any_launch():
                                   None) == lib.EINVAL
     assert so.attn_decode_noalloc(P, P, P, P, P, 0, 64, 8, 131072, 128, INF, None,
                                   None) == lib.OK
+
+
+def test_prefill_sas_rejects_before_any_launch():
+    so = lib.load()
+    # an unknown degree, and attn_prefill's own checks (NULL pointer, head dim)
+    assert so.attn_prefill_sas(P, P, P, P, P, 1, 8, 2, 1024, 128, 1, 4.0, 1, None,
+                               None) == lib.EINVAL
+    assert "degree" in lib.attn_last_error()
+    assert so.attn_prefill_sas(None, P, P, P, P, 1, 8, 2, 1024, 128, 1, 4.0, 2, None,
+                               None) == lib.EINVAL
+    assert so.attn_prefill_sas(P, P, P, P, P, 1, 8, 2, 1024, 96, 1, 4.0, 3, None,
+                               None) == lib.EINVAL
