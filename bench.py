@@ -62,12 +62,13 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # Keyed by the SHA-1 of the kernel's source files: once a kernel changes the
 # figure no longer applies and is reported as null.
 MEASURED_TRAFFIC = {
-    "prefill": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp"),
-                "sha1": "2a771a86ca5f49e7aa3968e13920c7815371302e",
-                "bytes": (2926160.6 * 2.0 + 528384.0) * 1024},
-    "prefill_qk8": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp", "fp8.hip"),
-                    "sha1": "c88ad7fd36d3fb1b701d2eb27bf115a628eba1bf",
-                    "bytes": (1792088.5 * 2.0 + 528385.5) * 1024},
+    "prefill": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp", "sas.hpp"),
+                "sha1": "69c12776ebf294d0d281bb272d208b1e7c6523a1",
+                "bytes": (2674125.6 * 2.0 + 528520.1) * 1024},
+    "prefill_qk8": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp", "sas.hpp",
+                                "fp8.hip"),
+                    "sha1": "89669bc9f1e78ed048da48ec453043c1f92ffd38",
+                    "bytes": (1693239.7 * 2.0 + 528520.1) * 1024},
     "decode_q4": {"sources": ("kvq4.hip", "kvq_common.hpp", "decode.hip", "common.hpp"),
                   "sha1": "47b7a50a18c93662f8b90d6a249268374d829e4a",
                   "bytes": (1148070.9 * 2.0 + 16642.1) * 1024},
