@@ -491,6 +491,9 @@ def main():
                 kernels=f"decode_split_kernel<128, {deg}> + decode_merge_kernel<128>")
         del o_ex, l_ex
 
+    # the split kernel each width runs at decode_128k's group size (G = 8):
+    # the 2-bit decode packs two KV groups per wave for G <= 8
+    qkern = {4: "decode_q4_split_kernel<128>", 2: "decode_q2_pair_kernel<128>"}
     qdecode = {}
     for w in widths:
         # The same decode workload over a w-bit KV cache: quantised once
@@ -534,7 +537,7 @@ def main():
                         traffic=measured_traffic(leg),
                         quantise_ms=round(float(tq0.ms()[0]), 4),
                         sas2_ms=round(sas_ms, 4),
-                        kernels=f"decode_q{w}_split_kernel<128> + decode_merge_kernel<128>")
+                        kernels=f"{qkern[w]} + decode_merge_kernel<128>")
         if args.only == leg:
             # the step is this leg alone: its per-call time, its workload
             out.update(value=round(gbs_q, 2), unit="GB/s", ms_per_step=round(q_ms, 4))
@@ -542,7 +545,7 @@ def main():
             out["roofline"] = dict(bound="hbm", achieved=round(gbs_q, 2), peak=PEAK_HBM_GBS,
                                    unit="GB/s", frac=round(gbs_q / PEAK_HBM_GBS, 4),
                                    traffic=measured_traffic(leg),
-                                   kernel=f"decode_q{w}_split_kernel<128>",
+                                   kernel=qkern[w],
                                    avg_ms=round(q_ms, 4), per_launch_bytes=qb)
 
     if run_qk8:

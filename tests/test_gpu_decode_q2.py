@@ -102,6 +102,10 @@ SMALL = [
     ("g8_split_edge", _cfg(B=1, Hq=8, Hkv=1, L=4097, id=82), (INF, 4.0)),
     ("g16", _cfg(B=1, Hq=16, Hkv=1, L=9000, id=83), (INF, 3.0)),
     ("g3_d64", _cfg(B=3, Hq=6, Hkv=2, L=12345, d=64, id=84), (INF, 0.0, 2.0)),
+    # two KV groups per wave: an odd last group without a partner, and G = 8
+    # at d = 64 over two splits
+    ("g5_hkv3_odd_pair", _cfg(B=2, Hq=15, Hkv=3, L=5000, id=85), (INF, 3.0)),
+    ("g8_hkv4_d64", _cfg(B=1, Hq=32, Hkv=4, L=8192, d=64, id=86), (INF, 4.0)),
 ]
 
 
