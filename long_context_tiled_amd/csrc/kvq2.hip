@@ -373,8 +373,7 @@ __global__ __launch_bounds__(256, 2) void decode_q2_split_kernel(
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) x = fmaxf(x, s[mb][r]);
-    x = fmaxf(x, xor16(x));
-    return fmaxf(x, xor32(x));
+    return max_over_row_groups(x);
   };
 
   // O: acc[db][r] = O[head 4 grp + r][channel 16 db + hl]; lr[r] the row sum
@@ -708,8 +707,7 @@ __global__ __launch_bounds__(256, 2) void decode_q2_pair_kernel(
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) x = fmaxf(x, s[mb][r]);
-    x = fmaxf(x, xor16(x));
-    return fmaxf(x, xor32(x));
+    return max_over_row_groups(x);
   };
 
   f32x4 acc[DB];
