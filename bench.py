@@ -69,15 +69,17 @@ MEASURED_TRAFFIC = {
                                 "fp8.hip"),
                     "sha1": "89669bc9f1e78ed048da48ec453043c1f92ffd38",
                     "bytes": (1693239.7 * 2.0 + 528520.1) * 1024},
-    "decode_q4": {"sources": ("kvq4.hip", "kvq_common.hpp", "decode.hip", "common.hpp"),
-                  "sha1": "47b7a50a18c93662f8b90d6a249268374d829e4a",
-                  "bytes": (1148070.9 * 2.0 + 16642.1) * 1024},
-    "decode_q2": {"sources": ("kvq2.hip", "kvq_common.hpp", "decode.hip", "common.hpp"),
-                  "sha1": "4233cbf13641664a2e555ef2ea645bc20e4de13e",
-                  "bytes": (623764.7 * 2.0 + 16640.1) * 1024},
-    "decode": {"sources": ("decode.hip", "common.hpp"),
-               "sha1": "0dd07902f20697310ae72199f10d1c43220f3099",
-               "bytes": (4195471.4 * 2.0 + 16641.3) * 1024},
+    "decode_q4": {"sources": ("kvq4.hip", "kvq_common.hpp", "decode.hip", "common.hpp", "sas.hpp",
+                                "lane_max.hpp"),
+                  "sha1": "4daa3e73a88c0e1c574626f9f3c321cd86a65a21",
+                  "bytes": (1148071.4 * 2.0 + 16646.4) * 1024},
+    "decode_q2": {"sources": ("kvq2.hip", "kvq_common.hpp", "decode.hip", "common.hpp", "sas.hpp",
+                                "lane_max.hpp"),
+                  "sha1": "6db8b055d4d30d710f1c74bbd87814e61f04da10",
+                  "bytes": (623807.6 * 2.0 + 16640.6) * 1024},
+    "decode": {"sources": ("decode.hip", "common.hpp", "sas.hpp", "lane_max.hpp"),
+               "sha1": "333142df1d615caa64770921eb2ebcb71ade361c",
+               "bytes": (4195498.3 * 2.0 + 16641.4) * 1024},
 }
 
 

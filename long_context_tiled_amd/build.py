@@ -21,7 +21,8 @@ BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.hip", "prefill.hip", "decode.hip", "kvq4.hip", "kvq2.hip", "fp8.hip"]
-HEADERS = ["common.hpp", "launch.hpp", "kvq_common.hpp", "sas.hpp", "prefill_steps.inc"]
+HEADERS = ["common.hpp", "launch.hpp", "kvq_common.hpp", "lane_max.hpp", "sas.hpp",
+           "prefill_steps.inc"]
 
 # Packed fp32 VALU ops are disabled: hipcc otherwise forms them from plain
 # float code.

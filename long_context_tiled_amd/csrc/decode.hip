@@ -31,6 +31,7 @@
 #include <atomic>
 
 #include "common.hpp"
+#include "lane_max.hpp"
 #include "sas.hpp"
 #include "launch.hpp"
 

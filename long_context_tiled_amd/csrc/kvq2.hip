@@ -42,6 +42,7 @@
 //   word ks / 2, half ks % 2 for k-step ks. Every code load covers whole
 //   128-byte lines with the non-temporal policy.
 #include "kvq_common.hpp"
+#include "lane_max.hpp"
 #include "sas.hpp"
 #include "launch.hpp"
 

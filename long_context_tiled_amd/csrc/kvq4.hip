@@ -51,6 +51,7 @@
 //   4 rows; V: 16 rows of 32 bytes) with the non-temporal policy; the small
 //   parameter words use the default policy.
 #include "kvq_common.hpp"
+#include "lane_max.hpp"
 #include "sas.hpp"
 #include "launch.hpp"
 
