@@ -225,9 +225,9 @@ def _cpu_decode_q_head(item):
     import synth
     from oracle import kvq2, kvq4
     key, i = item
-    codec = {"dq4": kvq4, "dq2": kvq2}[key]
     with threadpool_limits(1):
-        e, q, L = _CPU[key][i]
+        e, q, L, w = _CPU[key][i]
+        codec = {4: kvq4, 2: kvq2}[w]
         k = codec.decode_k(e["kq"], e["kp"])
         v = codec.decode_v(e["vq"], e["vp"], L)
         for hh in range(q.shape[0]):
@@ -245,7 +245,8 @@ def _cpu_model():
     return None
 
 
-def cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=768, nkv=32, nkv_q=16, pname="prefill_128k"):
+def cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=768, nkv=32, nkv_q=16, pname="prefill_128k",
+                 hybrid_bits=None):
     """The fp64 oracle as it stands, timed on a bounded sample of each
     workload with one process per host core (fp64 widening of the inputs is
     done before the clock starts)."""
@@ -268,10 +269,16 @@ def cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=768, nkv=32, nkv_q=16, pname="p
                     dq[b, g * G:(g + 1) * G]) for b, g in picks]
     from oracle import kvq2, kvq4
     pickq = picks[:nkv_q]
-    for key, codec in (("dq4", kvq4), ("dq2", kvq2)):
-        _CPU[key] = [(codec.encode(synth.bf16_bits_to_f32(dk[b, g]),
-                                   synth.bf16_bits_to_f32(dv[b, g])),
-                      dq[b, g * G:(g + 1) * G], L) for b, g in pickq]
+    qkeys = [("dq4", lambda g: 4), ("dq2", lambda g: 2)]
+    if hybrid_bits is not None:   # each KV head at its width in the hybrid cache
+        qkeys.append(("dqh", lambda g: hybrid_bits[g]))
+    for key, width in qkeys:
+        _CPU[key] = []
+        for b, g in pickq:
+            codec = {4: kvq4, 2: kvq2}[width(g)]
+            _CPU[key].append((codec.encode(synth.bf16_bits_to_f32(dk[b, g]),
+                                           synth.bf16_bits_to_f32(dv[b, g])),
+                              dq[b, g * G:(g + 1) * G], L, width(g)))
     ctx = mp.get_context("fork")
     qwall = {}
     with ctx.Pool(cores) as pool:
@@ -282,7 +289,7 @@ def cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=768, nkv=32, nkv_q=16, pname="p
         pool.map(_cpu_decode_head, [(i, hh) for i in range(len(picks)) for hh in range(G)],
                  chunksize=1)
         dwall = time.perf_counter() - t0
-        for key in ("dq4", "dq2"):
+        for key, _ in qkeys:
             t0 = time.perf_counter()
             pool.map(_cpu_decode_q_head, [(key, i) for i in range(len(pickq))], chunksize=1)
             qwall[key] = time.perf_counter() - t0
@@ -305,7 +312,14 @@ def cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=768, nkv=32, nkv_q=16, pname="p
                           sample=f"decode_128k over the {bits}-bit cache: {len(pickq)} KV heads "
                                  f"x {G} query heads, dequantise + fp64 decode oracle, tau=inf, "
                                  f"{qwall[key]:.1f} s wall")
-    return pre, dec, quant["dq4"], quant["dq2"]
+    if hybrid_bits is not None:
+        nb = sum(qcache_bytes(hybrid_bits[g], 1, 1, L, d) for _, g in pickq)
+        quant["dqh"] = dict(value=float(nb / qwall["dqh"] / 1e9), unit="GB/s", cores=cores,
+                            kind="oracle", **host,
+                            sample=f"decode_128k over the hybrid cache: {len(pickq)} KV heads "
+                                   f"(each at its width) x {G} query heads, dequantise + fp64 "
+                                   f"decode oracle, tau=inf, {qwall['dqh']:.1f} s wall")
+    return pre, dec, quant["dq4"], quant["dq2"], quant.get("dqh")
 
 
 # ---------------------------------------------------------------------- main
@@ -320,10 +334,11 @@ def main():
     ap.add_argument("--reading", default="S", choices=["S", "P"])
     ap.add_argument("--only", default="both",
                     choices=["both", "prefill", "decode", "decode_q4", "decode_q2",
-                             "prefill_qk8"],
+                             "decode_hybrid", "prefill_qk8"],
                     help="profile one leg only (the JSON line then reports that leg)")
     ap.add_argument("--no-q4", action="store_true",
-                    help="skip the 4-bit and 2-bit KV-cache decodes measured beside the step")
+                    help="skip the 4-bit, 2-bit and hybrid KV-cache decodes measured beside "
+                         "the step")
     ap.add_argument("--no-sas", action="store_true",
                     help="skip the decodes and the prefill with the SAS exponential measured "
                          "beside the step")
@@ -395,6 +410,7 @@ def main():
     # quantised-cache decodes measured beside the step (width in bits)
     widths = [w for w in (4, 2)
               if args.only == f"decode_q{w}" or (args.only == "both" and not args.no_q4)]
+    run_hy = args.only == "decode_hybrid" or (args.only == "both" and not args.no_q4)
 
     # Timed calls pass no skip-mask buffer (the mask is an optional output
     # for analysis); the tau sweep takes one extra masked call per tau to
@@ -549,6 +565,47 @@ def main():
                                    traffic=measured_traffic(leg),
                                    kernel=qkern[w],
                                    avg_ms=round(q_ms, 4), per_launch_bytes=qb)
+
+    hdecode = None
+    if run_hy:
+        # The same decode workload over a hybrid cache, its KV heads
+        # alternating 4 bits (even heads) and 2 bits (odd heads): quantised
+        # once (timed on its own), then attn_decode_hybrid timed like the rest.
+        hbits = tuple(4 if g % 2 == 0 else 2 for g in range(DHkv))
+        tqh = Timer()
+        with tqh:
+            hcache = lib.quantize_hybrid(uk, uv, hbits)
+        torch.cuda.synchronize()
+        hb = sum(qcache_bytes(w, DB, hbits.count(w), L, Dd) for w in (4, 2))
+
+        def hdecode(tau, mask=None):
+            lib.attn_decode_hybrid(uq, hcache, L, do, dlse, tau, ws, mask)
+
+        warm_up(lambda: hdecode(math.inf), args.warmup)
+        th = Timer()
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            with th:
+                hdecode(math.inf)
+        torch.cuda.synchronize()
+        h_ms = float(np.mean(th.ms()))
+        gbs_h = hb / (h_ms * 1e-3) / 1e9
+        dense_b, _ = decode_bytes(DB, DHkv, L, Dd)
+        hkern = "decode_q4_split_kernel<128> + decode_q2_pair_kernel<128>"
+        out["decode_hybrid"] = dict(value=round(gbs_h, 2), unit="GB/s", ms=round(h_ms, 4),
+                                    frac_of_hbm=round(gbs_h / PEAK_HBM_GBS, 4),
+                                    per_call_bytes=hb, kv_bits=list(hbits),
+                                    gbs_bf16_equivalent=round(dense_b / (h_ms * 1e-3) / 1e9, 2),
+                                    quantise_ms=round(float(tqh.ms()[0]), 4),
+                                    kernels=f"{hkern} + decode_merge_kernel<128>")
+        if args.only == "decode_hybrid":
+            out.update(value=round(gbs_h, 2), unit="GB/s", ms_per_step=round(h_ms, 4))
+            out["config"]["workload"] = ("decode_128k over the hybrid cache (KV heads "
+                                         "alternating 4 and 2 bits), tau=inf")
+            out["roofline"] = dict(bound="hbm", achieved=round(gbs_h, 2), peak=PEAK_HBM_GBS,
+                                   unit="GB/s", frac=round(gbs_h / PEAK_HBM_GBS, 4),
+                                   traffic=None, kernel=hkern,
+                                   avg_ms=round(h_ms, 4), per_launch_bytes=hb)
 
     if run_qk8:
         # The same prefill with block-quantised fp8 QK^T (attn_prefill_qk8):
@@ -750,16 +807,41 @@ def main():
                 sweep.append(dict(leg=f"decode_128k_q{w}", tau=str(tau), ms=round(ms, 4),
                                   skip_fraction=round(float((m == 1).mean()), 4),
                                   gbs_actual=round(act_b / ms / 1e6, 2)))
+        if hdecode is not None:
+            for tau in dcfg["taus"]:
+                t = Timer()
+                for _ in range(3):
+                    with t:
+                        hdecode(tau)
+                torch.cuda.synchronize()
+                ms = float(np.median(t.ms()))
+                hdecode(tau, dmask)
+                m = dmask.cpu().numpy()
+                G = DHq // DHkv
+                act_b = sum(qcache_bytes(w, DB, hbits.count(w), L, Dd,
+                                         m.reshape(DB, DHkv, G, -1)[:, [g for g in range(DHkv)
+                                                                        if hbits[g] == w]]
+                                         .reshape(DB, -1, m.shape[-1]), G)
+                            for w in (4, 2))
+                sweep.append(dict(leg="decode_128k_hybrid", tau=str(tau), ms=round(ms, 4),
+                                  skip_fraction=round(float((m == 1).mean()), 4),
+                                  gbs_actual=round(act_b / ms / 1e6, 2)))
         out["tau_sweep"] = sweep
 
     if not args.no_cpu:
         print("# cpu baseline (fp64 oracle on a bounded sample)", file=sys.stderr, flush=True)
-        pre, dec, dq4, dq2 = cpu_baseline(pq, pk, pv, dq, dk, dv, pname=pname)
-        legs = {"both": pre, "prefill": pre, "decode": dec, "decode_q4": dq4, "decode_q2": dq2}
+        pre, dec, dq4, dq2, dqh = cpu_baseline(
+            pq, pk, pv, dq, dk, dv, pname=pname,
+            hybrid_bits=tuple(4 if g % 2 == 0 else 2 for g in range(dk.shape[1])) if run_hy
+            else None)
+        legs = {"both": pre, "prefill": pre, "decode": dec, "decode_q4": dq4, "decode_q2": dq2,
+                "decode_hybrid": dqh}
         out["cpu_baseline"] = legs[args.only]
         out["cpu_baseline_decode"] = dec
         out["cpu_baseline_decode_q4"] = dq4
         out["cpu_baseline_decode_q2"] = dq2
+        if dqh is not None:
+            out["cpu_baseline_decode_hybrid"] = dqh
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

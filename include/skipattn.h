@@ -412,6 +412,62 @@ int attn_decode_q2_cap(const void* q, const uint8_t* kq, const uint32_t* kp,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Hybrid 2/4-bit KV cache (TurboAttention talk page, "Technical Deep Dive":
+ * the cache keeps its less critical parts at 2 bits and its more important
+ * parts at 4). The talk gives no rule for which parts are which; here the
+ * unit is the KV head and the caller chooses: kv_bits is a HOST array of
+ * Hkv bytes, kv_bits[g] = 4 or 2 the width of KV head g (any other value:
+ * SKIPATTN_EINVAL). Hkv <= 256 (SKIPATTN_EUNSUPPORTED beyond). The heads of
+ * each width live in arrays of their own, in increasing head order: with
+ * H4 heads at 4 bits and H2 at 2 bits, (kq4, kp4, vq4, vp4) is a 4-bit
+ * cache of H4 heads (layout of attn_kv_quantize_q4 with Hkv = H4) and
+ * (kq2, kp2, vq2, vp2) a 2-bit cache of H2 heads (Hkv = H2); a width with
+ * no head takes NULL pointers. Every head's codes are byte-identical to
+ * those of the single-width quantiser of its width.
+ *
+ * attn_kv_quantize_hybrid(_range) - K, V bf16 [B, Hkv, L, d] -> the two
+ * caches; key ranges, errors and the rewriting of partial tiles as for
+ * attn_kv_quantize_q4(_range). Every check is made before the first launch.
+ *
+ * attn_decode_hybrid - attn_decode over a hybrid cache: q, o, lse, the mask
+ * and the workspace (attn_decode_workspace_bytes(B, Hq, L, d)) are those of
+ * attn_decode over all Hq query heads; the query heads of KV head g attend
+ * to its keys and values as stored at kv_bits[g] bits, with the products,
+ * rule and rounding of attn_decode_q4 or attn_decode_q2. The two widths run
+ * as two split launches into one set of per-split partials, then one merge.
+ * attn_decode_hybrid_cap - the same over arrays sized for `cap` keys, of
+ * which the first L are attended, with `degree` as for attn_decode_q4_sas.
+ */
+int attn_kv_quantize_hybrid(const void* k, const void* v, const uint8_t* kv_bits,
+                            uint8_t* kq4, uint32_t* kp4, uint8_t* vq4,
+                            uint32_t* vp4, uint8_t* kq2, uint32_t* kp2,
+                            uint8_t* vq2, uint32_t* vp2, int B, int Hkv, int L,
+                            int d, void* stream);
+int attn_kv_quantize_hybrid_range(const void* k, const void* v,
+                                  const uint8_t* kv_bits, uint8_t* kq4,
+                                  uint32_t* kp4, uint8_t* vq4, uint32_t* vp4,
+                                  uint8_t* kq2, uint32_t* kp2, uint8_t* vq2,
+                                  uint32_t* vp2, int B, int Hkv, int L, int d,
+                                  int k0, int k1, void* stream);
+int attn_decode_hybrid(const void* q, const uint8_t* kv_bits,
+                       const uint8_t* kq4, const uint32_t* kp4,
+                       const uint8_t* vq4, const uint32_t* vp4,
+                       const uint8_t* kq2, const uint32_t* kp2,
+                       const uint8_t* vq2, const uint32_t* vp2, float* o,
+                       float* lse, int B, int Hq, int Hkv, int L, int d,
+                       float tau, uint8_t* skip_mask, void* workspace,
+                       size_t workspace_bytes, void* stream);
+int attn_decode_hybrid_cap(const void* q, const uint8_t* kv_bits,
+                           const uint8_t* kq4, const uint32_t* kp4,
+                           const uint8_t* vq4, const uint32_t* vp4,
+                           const uint8_t* kq2, const uint32_t* kp2,
+                           const uint8_t* vq2, const uint32_t* vp2, float* o,
+                           float* lse, int B, int Hq, int Hkv, int L, int cap,
+                           int d, float tau, int degree, uint8_t* skip_mask,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
  * attn_decode_noalloc - attn_decode for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc): the same arguments, kernels, results and errors, with

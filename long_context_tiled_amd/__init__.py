@@ -9,7 +9,9 @@ from ._lib import (OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, TILE, SPLIT,
                    empty_q4, q2_shapes, attn_kv_quantize_q2, attn_decode_q2, quantize_q2,
                    decode_q2, empty_q2, attn_decode_noalloc,
                    DECODE_SCRATCH_BYTES, attn_prefill_qk8, attn_prefill_qk8_workspace_bytes,
-                   qk8_workspace_parts, prefill_qk8, attn_prefill_sas)
+                   qk8_workspace_parts, prefill_qk8, attn_prefill_sas, hybrid_shapes,
+                   attn_kv_quantize_hybrid, attn_decode_hybrid, empty_hybrid, quantize_hybrid,
+                   decode_hybrid)
 
 __all__ = ["OK", "EINVAL", "EUNSUPPORTED", "EWORKSPACE", "EHIP", "TILE", "SPLIT",
            "KEPT", "SKIPPED", "NOT_VISITED", "EXPORTS", "LIB_PATH", "SkipAttnError",
@@ -20,4 +22,5 @@ __all__ = ["OK", "EINVAL", "EUNSUPPORTED", "EWORKSPACE", "EHIP", "TILE", "SPLIT"
            "attn_decode_q2", "quantize_q2", "decode_q2", "empty_q2",
            "attn_decode_noalloc", "DECODE_SCRATCH_BYTES", "attn_prefill_qk8",
            "attn_prefill_qk8_workspace_bytes", "qk8_workspace_parts", "prefill_qk8",
-           "attn_prefill_sas"]
+           "attn_prefill_sas", "hybrid_shapes", "attn_kv_quantize_hybrid",
+           "attn_decode_hybrid", "empty_hybrid", "quantize_hybrid", "decode_hybrid"]

@@ -28,7 +28,8 @@ EXPORTS = ("attn_prefill", "attn_decode", "attn_decode_workspace_bytes",
            "attn_decode_q2_check", "attn_decode_sas", "attn_decode_q4_sas", "attn_prefill_sas",
            "attn_decode_q2_sas", "attn_prefill_chunk_cap", "attn_decode_cap",
            "attn_decode_q4_cap", "attn_decode_q2_cap", "attn_decode_noalloc",
-           "attn_prefill_qk8", "attn_prefill_qk8_workspace_bytes")
+           "attn_prefill_qk8", "attn_prefill_qk8_workspace_bytes", "attn_kv_quantize_hybrid",
+           "attn_kv_quantize_hybrid_range", "attn_decode_hybrid", "attn_decode_hybrid_cap")
 
 _lib = None
 
@@ -100,6 +101,17 @@ def load() -> ctypes.CDLL:
         fn = getattr(lib, f"attn_decode_{w}_check")
         fn.argtypes = [vp, vp, vp, vp, vp, f32p, f32p, i, i, i, i, i, f, u8p, vp, sz]
         fn.restype = i
+    c8 = [vp] * 8   # the two caches' kq, kp, vq, vp
+    lib.attn_kv_quantize_hybrid.argtypes = [vp, vp, vp] + c8 + [i, i, i, i, vp]
+    lib.attn_kv_quantize_hybrid.restype = i
+    lib.attn_kv_quantize_hybrid_range.argtypes = [vp, vp, vp] + c8 + [i, i, i, i, i, i, vp]
+    lib.attn_kv_quantize_hybrid_range.restype = i
+    lib.attn_decode_hybrid.argtypes = [vp, vp] + c8 + [f32p, f32p, i, i, i, i, i, f, u8p, vp, sz,
+                                                       vp]
+    lib.attn_decode_hybrid.restype = i
+    lib.attn_decode_hybrid_cap.argtypes = [vp, vp] + c8 + [f32p, f32p, i, i, i, i, i, i, f, i, u8p,
+                                                           vp, sz, vp]
+    lib.attn_decode_hybrid_cap.restype = i
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -420,6 +432,91 @@ def attn_decode_q2(q, cache, L: int, o, lse, tau: float, workspace, skip_mask=No
     _decode_cache(2, q, cache, L, o, lse, tau, workspace, skip_mask, stream)
 
 
+def _bits_arg(bits):
+    bits = tuple(int(b) for b in bits)
+    return bits, (ctypes.c_uint8 * max(1, len(bits)))(*bits)
+
+
+def _hybrid_ptrs(cache):
+    out = []
+    for w in ("q4", "q2"):
+        c = cache[w]
+        out += [None] * 4 if c is None else [_ptr(c["kq"]), _ptr(c["kp"]), _ptr(c["vq"]),
+                                             _ptr(c["vp"])]
+    return out
+
+
+def hybrid_shapes(kv_bits, B: int, L: int, d: int) -> dict:
+    """Shapes of a hybrid cache's two sub-caches: {"q4": shapes or None,
+    "q2": shapes or None}; KV head g is stored at kv_bits[g] (4 or 2) bits,
+    each width's heads in increasing order."""
+    n4 = sum(1 for b in kv_bits if b == 4)
+    n2 = sum(1 for b in kv_bits if b == 2)
+    return {"q4": _cache_shapes(4, B, n4, L, d) if n4 else None,
+            "q2": _cache_shapes(2, B, n2, L, d) if n2 else None}
+
+
+def _check_hybrid(cache, B, Hkv, L, d):
+    bits = tuple(cache["bits"])
+    if len(bits) != Hkv:
+        raise ValueError(f"kv_bits has {len(bits)} entries for {Hkv} KV heads")
+    n = {4: sum(1 for b in bits if b == 4), 2: sum(1 for b in bits if b == 2)}
+    for w, key in ((4, "q4"), (2, "q2")):
+        if n[w]:
+            _check_cache(w, cache[key], B, n[w], L, d)
+        elif cache[key] is not None:
+            raise ValueError(f"no head is stored at {w} bits but cache['{key}'] is given")
+
+
+def attn_kv_quantize_hybrid(k, v, cache, stream=None, key_range=None) -> None:
+    """Enqueue the hybrid quantiser: k/v [B,Hkv,L,d] bf16 -> cache dict
+    {"bits": per-KV-head widths (4 or 2), "q4": 4-bit cache dict of the
+    4-bit heads or None, "q2": likewise} (shapes of hybrid_shapes());
+    ``key_range`` as for attn_kv_quantize_q4."""
+    import torch
+    B, Hkv, L, d = k.shape
+    _check(k, "k", torch.bfloat16, (B, Hkv, L, d))
+    _check(v, "v", torch.bfloat16, (B, Hkv, L, d))
+    _check_hybrid(cache, B, Hkv, L, d)
+    _, arr = _bits_arg(cache["bits"])
+    k0, k1 = (0, L) if key_range is None else key_range
+    rc = load().attn_kv_quantize_hybrid_range(_ptr(k), _ptr(v), arr, *_hybrid_ptrs(cache), B, Hkv,
+                                              L, d, int(k0), int(k1), _stream(stream))
+    _raise(rc)
+
+
+def attn_decode_hybrid(q, cache, L: int, o, lse, tau: float, workspace, skip_mask=None,
+                       stream=None, sas: int = 0) -> None:
+    """Enqueue split-K decode over a hybrid cache (dict as for
+    attn_kv_quantize_hybrid) of the first L keys; the sub-caches may be sized
+    for more keys. Other arguments as attn_decode; ``sas`` as for
+    decode_q4."""
+    import torch
+    B, Hq, d = q.shape
+    sub = cache["q4"] if cache["q4"] is not None else cache["q2"]
+    cap = sub["kp"].shape[2]
+    Hkv = len(cache["bits"])
+    _check(q, "q", torch.bfloat16, (B, Hq, d))
+    _check_hybrid(cache, B, Hkv, cap, d)
+    _check(o, "o", torch.float32, (B, Hq, d))
+    _check(lse, "lse", torch.float32, (B, Hq))
+    if skip_mask is not None:
+        _check(skip_mask, "skip_mask", torch.uint8, (B, Hq, (L + TILE - 1) // TILE))
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    _, arr = _bits_arg(cache["bits"])
+    so = load()
+    head = [_ptr(q), arr] + _hybrid_ptrs(cache) + [_ptr(o), _ptr(lse)]
+    tail = [_ptr(skip_mask), _ptr(workspace), nbytes, _stream(stream)]
+    if L != cap or sas:
+        rc = so.attn_decode_hybrid_cap(*head, B, Hq, Hkv, int(L), cap, d, float(tau), int(sas),
+                                       *tail)
+    else:
+        rc = so.attn_decode_hybrid(*head, B, Hq, Hkv, int(L), d, float(tau), *tail)
+    _raise(rc)
+
+
 # ---- allocation conveniences around the entry points ----
 
 def _empty_cache(bits, B, Hkv, L, d, device):
@@ -455,6 +552,25 @@ def quantize_q2(k, v, stream=None) -> dict:
     return cache
 
 
+def empty_hybrid(kv_bits, B: int, L: int, d: int, device) -> dict:
+    """Allocate (uninitialised) hybrid cache arrays for L keys."""
+    bits = tuple(int(b) for b in kv_bits)
+    n4 = sum(1 for b in bits if b == 4)
+    n2 = sum(1 for b in bits if b == 2)
+    return {"bits": bits,
+            "q4": _empty_cache(4, B, n4, L, d, device) if n4 else None,
+            "q2": _empty_cache(2, B, n2, L, d, device) if n2 else None}
+
+
+def quantize_hybrid(k, v, kv_bits, stream=None) -> dict:
+    """Allocate a hybrid cache with torch (KV head g at kv_bits[g] bits) and
+    fill it from bf16 k, v."""
+    B, Hkv, L, d = k.shape
+    cache = empty_hybrid(kv_bits, B, L, d, k.device)
+    attn_kv_quantize_hybrid(k, v, cache, stream)
+    return cache
+
+
 def _decode_alloc(bits, q, cache, L, tau, want_mask, workspace, stream, sas=0):
     import torch
     B, Hq, d = q.shape
@@ -467,7 +583,10 @@ def _decode_alloc(bits, q, cache, L, tau, want_mask, workspace, stream, sas=0):
     if workspace is None:
         nbytes = max(16, attn_decode_workspace_bytes(B, Hq, L, d))
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    _decode_cache(bits, q, cache, L, o, lse, tau, workspace, mask, stream, sas)
+    if bits == "hybrid":
+        attn_decode_hybrid(q, cache, L, o, lse, tau, workspace, mask, stream, sas)
+    else:
+        _decode_cache(bits, q, cache, L, o, lse, tau, workspace, mask, stream, sas)
     return o, lse, mask
 
 
@@ -483,6 +602,12 @@ def decode_q2(q, cache, L: int, tau: float = math.inf, want_mask: bool = False,
               workspace=None, stream=None, sas: int = 0):
     """As decode_q4, over a 2-bit cache."""
     return _decode_alloc(2, q, cache, L, tau, want_mask, workspace, stream, sas)
+
+
+def decode_hybrid(q, cache, L: int, tau: float = math.inf, want_mask: bool = False,
+                  workspace=None, stream=None, sas: int = 0):
+    """As decode_q4, over a hybrid cache (dict of quantize_hybrid)."""
+    return _decode_alloc("hybrid", q, cache, L, tau, want_mask, workspace, stream, sas)
 
 
 # ---- allocation conveniences around the two bf16 entry points ----

@@ -230,10 +230,10 @@ int decode_quantized(int (*launch)(const skipattn::DecodeQ4Args&), const char* w
   return SKIPATTN_OK;
 }
 
-// The shared body of the 4-bit and 2-bit quantisers.
-int quantize_range(int (*launch)(const skipattn::QuantArgs&), const void* k, const void* v,
-                   uint8_t* kq, uint32_t* kp, uint8_t* vq, uint32_t* vp, int B, int Hkv, int L,
-                   int d, int k0, int k1, void* stream) {
+// The checks of the 4-bit and 2-bit quantisers (Hkv: heads of k and v).
+int quantize_check(const void* k, const void* v, const uint8_t* kq, const uint32_t* kp,
+                   const uint8_t* vq, const uint32_t* vp, int B, int Hkv, int L, int d, int k0,
+                   int k1) {
   g_err[0] = '\0';
   if (!k || !v || !kq || !kp || !vq || !vp) return fail(SKIPATTN_EINVAL, "NULL tensor pointer");
   if (B < 0 || L < 0 || d < 0) return fail(SKIPATTN_EINVAL, "negative size (B=%d L=%d d=%d)", B, L, d);
@@ -251,11 +251,131 @@ int quantize_range(int (*launch)(const skipattn::QuantArgs&), const void* k, con
                 kMaxHeadBytes);
   if (k0 % SKIPATTN_TILE != 0)
     return fail(SKIPATTN_EUNSUPPORTED, "k0 (%d) must be a multiple of 64", k0);
+  return SKIPATTN_OK;
+}
+
+// Enqueue a checked quantiser call; with map.n the cache holds those heads.
+int quantize_launch(int (*launch)(const skipattn::QuantArgs&), const void* k, const void* v,
+                    uint8_t* kq, uint32_t* kp, uint8_t* vq, uint32_t* vp, int B, int Hkv, int L,
+                    int d, int k0, int k1, void* stream, const skipattn::KvHeadMap& map) {
   if (B == 0 || k1 == k0) return SKIPATTN_OK;
   skipattn::QuantArgs a{k, v, kq, kp, vq, vp, B, Hkv, L, d, k0, k1, stream};
+  if (map.n) {
+    a.Hkv = map.n;
+    a.map = map;
+  }
   if (launch(a) != 0) return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(SKIPATTN_EHIP, "quantize launch: %s", hipGetErrorString(err));
+  return SKIPATTN_OK;
+}
+
+// The shared body of the 4-bit and 2-bit quantisers.
+int quantize_range(int (*launch)(const skipattn::QuantArgs&), const void* k, const void* v,
+                   uint8_t* kq, uint32_t* kp, uint8_t* vq, uint32_t* vp, int B, int Hkv, int L,
+                   int d, int k0, int k1, void* stream) {
+  if (int e = quantize_check(k, v, kq, kp, vq, vp, B, Hkv, L, d, k0, k1)) return e;
+  return quantize_launch(launch, k, v, kq, kp, vq, vp, B, Hkv, L, d, k0, k1, stream,
+                         skipattn::KvHeadMap{});
+}
+
+// The head maps of a hybrid cache's two widths from the per-head widths
+// (host array of Hkv entries, each 4 or 2): each width's heads in
+// increasing order.
+int hybrid_maps(const uint8_t* kv_bits, int Hkv, skipattn::KvHeadMap& m4,
+                skipattn::KvHeadMap& m2) {
+  g_err[0] = '\0';
+  if (!kv_bits) return fail(SKIPATTN_EINVAL, "NULL kv_bits");
+  if (Hkv < 1) return fail(SKIPATTN_EINVAL, "Hkv must be >= 1 (got %d)", Hkv);
+  if (Hkv > skipattn::kMaxMappedHeads)
+    return fail(SKIPATTN_EUNSUPPORTED, "a hybrid cache holds at most %d KV heads (got %d)",
+                skipattn::kMaxMappedHeads, Hkv);
+  m4 = skipattn::KvHeadMap{};
+  m2 = skipattn::KvHeadMap{};
+  m4.n_in = m2.n_in = Hkv;
+  for (int g = 0; g < Hkv; ++g) {
+    if (kv_bits[g] == 4) {
+      m4.g[m4.n++] = (uint8_t)g;
+    } else if (kv_bits[g] == 2) {
+      m2.g[m2.n++] = (uint8_t)g;
+    } else {
+      return fail(SKIPATTN_EINVAL, "kv_bits[%d] must be 4 or 2 (got %d)", g, (int)kv_bits[g]);
+    }
+  }
+  return SKIPATTN_OK;
+}
+
+int hybrid_quantize(const void* k, const void* v, const uint8_t* kv_bits, uint8_t* kq4,
+                    uint32_t* kp4, uint8_t* vq4, uint32_t* vp4, uint8_t* kq2, uint32_t* kp2,
+                    uint8_t* vq2, uint32_t* vp2, int B, int Hkv, int L, int d, int k0, int k1,
+                    void* stream) {
+  skipattn::KvHeadMap m4, m2;
+  if (int e = hybrid_maps(kv_bits, Hkv, m4, m2)) return e;
+  // every check before the first launch
+  if (m4.n)
+    if (int e = quantize_check(k, v, kq4, kp4, vq4, vp4, B, Hkv, L, d, k0, k1)) return e;
+  if (m2.n)
+    if (int e = quantize_check(k, v, kq2, kp2, vq2, vp2, B, Hkv, L, d, k0, k1)) return e;
+  if (m4.n)
+    if (int e = quantize_launch(skipattn::launch_kv_quantize_q4, k, v, kq4, kp4, vq4, vp4, B, Hkv,
+                                L, d, k0, k1, stream, m4))
+      return e;
+  if (m2.n)
+    if (int e = quantize_launch(skipattn::launch_kv_quantize_q2, k, v, kq2, kp2, vq2, vp2, B, Hkv,
+                                L, d, k0, k1, stream, m2))
+      return e;
+  return SKIPATTN_OK;
+}
+
+// Decode over a hybrid cache: each width's split kernel writes its heads'
+// rows of one set of partials (and of the mask), then one merge.
+int hybrid_decode(const void* q, const uint8_t* kv_bits, const uint8_t* kq4,
+                  const uint32_t* kp4, const uint8_t* vq4, const uint32_t* vp4,
+                  const uint8_t* kq2, const uint32_t* kp2, const uint8_t* vq2,
+                  const uint32_t* vp2, float* o, float* lse, int B, int Hq, int Hkv, int L,
+                  int cap, int d, float tau, int degree, uint8_t* skip_mask, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  skipattn::KvHeadMap m4, m2;
+  if (int e = hybrid_maps(kv_bits, Hkv, m4, m2)) return e;
+  if (m4.n)
+    if (int e = cache_ptrs_check(kq4, kp4, vq4, vp4)) return e;
+  if (m2.n)
+    if (int e = cache_ptrs_check(kq2, kp2, vq2, vp2)) return e;
+  // The bf16 checks cover every other argument; a code array stands in for k and v.
+  const uint8_t* any = m4.n ? kq4 : kq2;
+  if (int e = decode_check(q, any, any, o, lse, B, Hq, Hkv, L, cap, d, tau, workspace,
+                           workspace_bytes))
+    return e;
+  if (int e = check_degree(degree)) return e;
+  if (B == 0 || L == 0) return SKIPATTN_OK;
+  const int nsplit = (L + SKIPATTN_SPLIT - 1) / SKIPATTN_SPLIT;
+  const int G = Hq / Hkv;
+  float* ws_o = (float*)workspace;
+  float* ws_lse = ws_o + (size_t)B * Hq * nsplit * d;
+  struct Part {
+    int (*launch)(const skipattn::DecodeQ4Args&);
+    const skipattn::KvHeadMap* map;
+    const uint8_t* kq;
+    const uint32_t* kp;
+    const uint8_t* vq;
+    const uint32_t* vp;
+  } parts[2] = {{skipattn::launch_decode_q4, &m4, kq4, kp4, vq4, vp4},
+                {skipattn::launch_decode_q2, &m2, kq2, kp2, vq2, vp2}};
+  for (const Part& p : parts) {
+    if (p.map->n == 0) continue;
+    skipattn::DecodeQ4Args a{q,      p.kq,     p.kp, p.vq, p.vp,  o, lse, skip_mask, ws_o,
+                             ws_lse, B,        Hq,   Hkv,  L,     d, nsplit, cap,
+                             tau_raw(tau, d), exp2_scale(d), stream, degree};
+    a.Hq = p.map->n * G;
+    a.Hkv = p.map->n;
+    a.map = *p.map;
+    a.merge = false;
+    if (p.launch(a) != 0) return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
+  }
+  if (skipattn::launch_decode_merge(ws_o, ws_lse, o, lse, B * Hq, d, nsplit, stream) != 0)
+    return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(SKIPATTN_EHIP, "decode_hybrid launch: %s", hipGetErrorString(err));
   return SKIPATTN_OK;
 }
 
@@ -478,6 +598,42 @@ int attn_kv_quantize_q2_range(const void* k, const void* v, uint8_t* kq, uint32_
 int attn_kv_quantize_q2(const void* k, const void* v, uint8_t* kq, uint32_t* kp, uint8_t* vq,
                         uint32_t* vp, int B, int Hkv, int L, int d, void* stream) {
   return attn_kv_quantize_q2_range(k, v, kq, kp, vq, vp, B, Hkv, L, d, 0, L < 0 ? 0 : L, stream);
+}
+
+int attn_kv_quantize_hybrid_range(const void* k, const void* v, const uint8_t* kv_bits,
+                                  uint8_t* kq4, uint32_t* kp4, uint8_t* vq4, uint32_t* vp4,
+                                  uint8_t* kq2, uint32_t* kp2, uint8_t* vq2, uint32_t* vp2,
+                                  int B, int Hkv, int L, int d, int k0, int k1, void* stream) {
+  return hybrid_quantize(k, v, kv_bits, kq4, kp4, vq4, vp4, kq2, kp2, vq2, vp2, B, Hkv, L, d,
+                         k0, k1, stream);
+}
+
+int attn_kv_quantize_hybrid(const void* k, const void* v, const uint8_t* kv_bits, uint8_t* kq4,
+                            uint32_t* kp4, uint8_t* vq4, uint32_t* vp4, uint8_t* kq2,
+                            uint32_t* kp2, uint8_t* vq2, uint32_t* vp2, int B, int Hkv, int L,
+                            int d, void* stream) {
+  return hybrid_quantize(k, v, kv_bits, kq4, kp4, vq4, vp4, kq2, kp2, vq2, vp2, B, Hkv, L, d, 0,
+                         L < 0 ? 0 : L, stream);
+}
+
+int attn_decode_hybrid(const void* q, const uint8_t* kv_bits, const uint8_t* kq4,
+                       const uint32_t* kp4, const uint8_t* vq4, const uint32_t* vp4,
+                       const uint8_t* kq2, const uint32_t* kp2, const uint8_t* vq2,
+                       const uint32_t* vp2, float* o, float* lse, int B, int Hq, int Hkv, int L,
+                       int d, float tau, uint8_t* skip_mask, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return hybrid_decode(q, kv_bits, kq4, kp4, vq4, vp4, kq2, kp2, vq2, vp2, o, lse, B, Hq, Hkv, L,
+                       L, d, tau, 0, skip_mask, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_hybrid_cap(const void* q, const uint8_t* kv_bits, const uint8_t* kq4,
+                           const uint32_t* kp4, const uint8_t* vq4, const uint32_t* vp4,
+                           const uint8_t* kq2, const uint32_t* kp2, const uint8_t* vq2,
+                           const uint32_t* vp2, float* o, float* lse, int B, int Hq, int Hkv,
+                           int L, int cap, int d, float tau, int degree, uint8_t* skip_mask,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return hybrid_decode(q, kv_bits, kq4, kp4, vq4, vp4, kq2, kp2, vq2, vp2, o, lse, B, Hq, Hkv, L,
+                       cap, d, tau, degree, skip_mask, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

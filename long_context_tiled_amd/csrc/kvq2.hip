@@ -71,16 +71,18 @@ template <int D>
 __global__ __launch_bounds__(256) void quant_k2_kernel(const uint16_t* __restrict__ k,
                                                        uint8_t* __restrict__ kq,
                                                        uint32_t* __restrict__ kp,
-                                                       long long rows, int L, int k0, int nk) {
+                                                       long long rows, int L, int k0, int nk,
+    const KvHeadMap hm) {
   constexpr int W = D / 16;
   const int lane = threadIdx.x & 63;
   const long long idx = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / W) + lane / W;
   const int w = lane % W;
   const bool ok = idx < rows;
   const long long row = ok ? (idx / nk) * L + k0 + idx % nk : 0;  // key row in the cache
+  const long long src_row = ok ? full_slice(idx / nk, hm) * L + k0 + idx % nk : 0;
   float x[16];
   if (ok) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(k + row * D + 16 * w);
+    const u32x4* src = reinterpret_cast<const u32x4*>(k + src_row * D + 16 * w);
     const u32x4 r0 = src[0], r1 = src[1];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -120,12 +122,13 @@ template <int D>
 __global__ __launch_bounds__(D) void quant_v2_kernel(const uint16_t* __restrict__ v,
                                                      uint8_t* __restrict__ vq,
                                                      uint32_t* __restrict__ vp, int L, int T,
-                                                     int t0, int nt, int k1) {
+                                                     int t0, int nt, int k1,
+    const KvHeadMap hm) {
   const int ch = threadIdx.x;
   const long long bg = blockIdx.x / nt;
   const int t = t0 + blockIdx.x % nt;
   const int n = min(kTile, k1 - kTile * t);
-  const uint16_t* src = v + (bg * L + (long long)kTile * t) * D + ch;
+  const uint16_t* src = v + (full_slice(bg, hm) * L + (long long)kTile * t) * D + ch;
   float x[kTile];
 #pragma unroll
   for (int j = 0; j < kTile; ++j) x[j] = j < n ? bf16_to_f32(src[(long long)j * D]) : x[0];
@@ -222,7 +225,7 @@ __global__ __launch_bounds__(256, 2) void decode_q2_split_kernel(
     const uint32_t* __restrict__ kp, const uint8_t* __restrict__ vq,
     const uint32_t* __restrict__ vp, float* __restrict__ ws_o, float* __restrict__ ws_lse,
     uint8_t* __restrict__ mask, int Hq, int Hkv, int L, int cap, int nhs, int nsplit, float tau_raw, float c,
-    int nwork) {
+    int nwork, const KvHeadMap hm) {
   constexpr int KS = D / 32;  // QK k-steps
   constexpr int KW = D / 64;  // code words per lane per K row
   constexpr int DB = D / 16;  // 16-channel blocks of O and of V code rows
@@ -260,7 +263,9 @@ __global__ __launch_bounds__(256, 2) void decode_q2_split_kernel(
   const int ntile = (key_end - key_begin + kTile - 1) / kTile;
   const int tile_begin = key_begin / kTile;
   const bool head_ok = hoff + hl < G;
-  const size_t bh = (size_t)b * Hq + g * G + hoff + hl;
+  // rows of q, the partials and the mask: those of the full set of heads
+  const int Hqo = hm.n ? hm.n_in * G : Hq;
+  const size_t bh = (size_t)b * Hqo + full_head(g, hm) * G + hoff + hl;
 
   // q^T fragments (B operand, n = head): lane group grp holds d range
   // [grp D/4, (grp + 1) D/4), k-step ks its elements 8 ks .. 8 ks + 7; qf
@@ -505,7 +510,7 @@ __global__ __launch_bounds__(256, 2) void decode_q2_split_kernel(
     for (int t = 0; t < ntile; ++t) mrow[t] = (uint8_t)((skipped >> t) & 1u);
   }
 
-  const size_t bh0 = (size_t)b * Hq + g * G + hoff;
+  const size_t bh0 = (size_t)b * Hqo + full_head(g, hm) * G + hoff;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float mr = of_head(m_ref, r);
@@ -538,7 +543,7 @@ __global__ __launch_bounds__(256, 2) void decode_q2_pair_kernel(
     const uint32_t* __restrict__ kp, const uint8_t* __restrict__ vq,
     const uint32_t* __restrict__ vp, float* __restrict__ ws_o, float* __restrict__ ws_lse,
     uint8_t* __restrict__ mask, int Hq, int Hkv, int L, int cap, int nsplit, float tau_raw,
-    float c, int nwork) {
+    float c, int nwork, const KvHeadMap hm) {
   constexpr int KS = D / 16;  // q.K k-steps per 16-key block (16 d of each group)
   constexpr int KW = D / 32;  // code words per lane per K row (half a row)
   constexpr int DB = D / 16;  // 16-channel blocks of O and of V code rows
@@ -597,7 +602,10 @@ __global__ __launch_bounds__(256, 2) void decode_q2_pair_kernel(
   const int tile_begin = key_begin / kTile;
   const int hcol = hl & 7;                          // head of the column within its group
   const bool head_ok = hcol < G && (col_g == 0 || b_ok);
-  const size_t bh = (size_t)b * Hq + (col_g ? gB : gA) * G + hcol;
+  // rows of q, the partials and the mask: those of the full set of heads
+  const int Hqo = hm.n ? hm.n_in * G : Hq;
+  const int gAo = full_head(gA, hm), gBo = full_head(gB, hm);
+  const size_t bh = (size_t)b * Hqo + (col_g ? gBo : gAo) * G + hcol;
   const bool q_on = col_g == gh && head_ok;         // this lane's q fragment is the column's
 
   // q^T fragments (B operand, n = head column): k-step ks holds elements
@@ -847,9 +855,9 @@ __global__ __launch_bounds__(256, 2) void decode_q2_pair_kernel(
   for (int r = 0; r < 4; ++r) {
     const float mr = of_head(m_ref, r);
     const int hh = 4 * (grp & 1) + r;
-    const int g = gh ? gB : gA;
+    const int go = gh ? gBo : gAo;
     if (hh < G && (gh == 0 || b_ok)) {
-      const size_t bhr = (size_t)b * Hq + g * G + hh;
+      const size_t bhr = (size_t)b * Hqo + go * G + hh;
       const float ir = 1.f / lr[r];
       float* dst = ws_o + (bhr * nsplit + sp) * D + hl;
 #pragma unroll
@@ -872,9 +880,9 @@ int launch_q2_d(const QuantArgs& a) {
   const long long g2 = (long long)a.B * a.Hkv * nt;
   if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return -1;
   hipLaunchKernelGGL((quant_k2_kernel<D>), dim3((unsigned)g1), dim3(256), 0, (hipStream_t)a.stream,
-                     (const uint16_t*)a.k, a.kq, a.kp, rows, a.L, a.k0, nk);
+                     (const uint16_t*)a.k, a.kq, a.kp, rows, a.L, a.k0, nk, a.map);
   hipLaunchKernelGGL((quant_v2_kernel<D>), dim3((unsigned)g2), dim3(D), 0, (hipStream_t)a.stream,
-                     (const uint16_t*)a.v, a.vq, a.vp, a.L, T, t0, nt, a.k1);
+                     (const uint16_t*)a.v, a.vq, a.vp, a.L, T, t0, nt, a.k1, a.map);
   return 0;
 }
 
@@ -890,7 +898,8 @@ int launch_dq2_d(const DecodeQ4Args& a) {
                 : a.sas == 3 ? decode_q2_pair_kernel<D, 3> : decode_q2_pair_kernel<D, 0>;
     hipLaunchKernelGGL(kern, dim3(g1), dim3(256), 0, (hipStream_t)a.stream,
                        (const uint16_t*)a.q, a.kq, a.kp, a.vq, a.vp, a.ws_o, a.ws_lse, a.mask,
-                       a.Hq, a.Hkv, a.L, a.cap, a.nsplit, a.tau_raw, a.c, (int)nwork);
+                       a.Hq, a.Hkv, a.L, a.cap, a.nsplit, a.tau_raw, a.c, (int)nwork, a.map);
+    if (!a.merge) return 0;
     return launch_decode_merge(a.ws_o, a.ws_lse, a.o, a.lse, a.B * a.Hq, a.d, a.nsplit, a.stream);
   }
   // one wave per (sequence, KV head, slice of up to 16 query heads, split)
@@ -902,7 +911,8 @@ int launch_dq2_d(const DecodeQ4Args& a) {
               : a.sas == 3 ? decode_q2_split_kernel<D, 3> : decode_q2_split_kernel<D, 0>;
   hipLaunchKernelGGL(kern, dim3(g1), dim3(256), 0, (hipStream_t)a.stream,
                      (const uint16_t*)a.q, a.kq, a.kp, a.vq, a.vp, a.ws_o, a.ws_lse, a.mask, a.Hq,
-                     a.Hkv, a.L, a.cap, nhs, a.nsplit, a.tau_raw, a.c, (int)nwork);
+                     a.Hkv, a.L, a.cap, nhs, a.nsplit, a.tau_raw, a.c, (int)nwork, a.map);
+  if (!a.merge) return 0;
   return launch_decode_merge(a.ws_o, a.ws_lse, a.o, a.lse, a.B * a.Hq, a.d, a.nsplit, a.stream);
 }
 

@@ -4,6 +4,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "launch.hpp"
 
 namespace skipattn {
 
@@ -15,6 +16,17 @@ constexpr uint32_t kCfg = 0x00020000u;     // raw 32-bit buffer, range-checked
 constexpr uint32_t kNoRead = 0x80000000u;  // tile offset of a load that reads nothing
 constexpr int kNT = 2;                     // non-temporal cache policy
 constexpr int kRT = 0;                     // default cache policy
+
+// Head numbering of a cache that holds some of the KV heads (a hybrid
+// cache's heads of one width): (b, head) slice bg = b * n + i of the cache
+// comes from slice b * n_in + g[i] of the full set, and its query heads are
+// rows of the full set's query heads.
+__device__ __forceinline__ long long full_slice(long long bg, const KvHeadMap& hm) {
+  return hm.n ? (bg / hm.n) * hm.n_in + hm.g[bg % hm.n] : bg;
+}
+__device__ __forceinline__ int full_head(int g, const KvHeadMap& hm) {
+  return hm.n ? hm.g[g] : g;
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __builtin_bit_cast(float, bits16 << 16);

@@ -47,6 +47,16 @@ struct DecodeArgs {
   int sas;        // 0: exact exponentials; 2 or 3: SAS polynomial degree
 };
 
+// The KV heads of one width of a hybrid cache (heads of different widths in
+// arrays of their own): head i of such a sub-cache is head g[i] of the n_in
+// heads of the full set. n = 0: no map (the cache holds every head).
+constexpr int kMaxMappedHeads = 256;
+struct KvHeadMap {
+  int n = 0;
+  int n_in = 0;
+  uint8_t g[kMaxMappedHeads] = {};
+};
+
 struct QuantArgs {
   const void* k;  // bf16 [B, Hkv, L, d]
   const void* v;
@@ -57,6 +67,9 @@ struct QuantArgs {
   int B, Hkv, L, d;
   int k0, k1;     // keys written: k0 .. k1 - 1 (k0 a multiple of 64)
   void* stream;
+  // map.n: the cache holds map.n (= Hkv) heads, head i quantised from head
+  // map.g[i] of the map.n_in heads of k and v ([B, map.n_in, L, d])
+  KvHeadMap map = {};
 };
 
 struct DecodeQ4Args {
@@ -76,6 +89,11 @@ struct DecodeQ4Args {
   float c;
   void* stream;
   int sas;        // 0: exact exponentials; 2 or 3: SAS polynomial degree
+  // map.n: the cache holds map.n (= Hkv) of the map.n_in KV heads; q, the
+  // per-split partials and the mask then hold the rows of all of them
+  // ([B, map.n_in * Hq / Hkv, ...]), and this call touches its heads' rows
+  KvHeadMap map = {};
+  bool merge = true;  // false: the split kernel only (the caller merges)
 };
 
 // Each returns 0 when the kernels were enqueued, nonzero if the grid cannot

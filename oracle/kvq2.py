@@ -8,8 +8,8 @@ What the pages fix (TurboAttention talk page, "Technical Deep Dive", the
 pre-fill / decoding workflow and the trade-offs it lists): KV-cache storage
 in low-bit asymmetric integers with a floating zero point per block, in a
 4-bit (near-lossless) and a 2-bit (lossy, faster) option. This module is the
-2-bit option; the 4-bit one is ``kvq4``. The pages give no rule for mixing
-the two inside one cache, so each cache here is entirely one width.
+2-bit option; the 4-bit one is ``kvq4``; ``kvq_hybrid`` mixes the two in
+one cache, one width per KV head.
 
 Readings, as for the 4-bit format except where stated:
 

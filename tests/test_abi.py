@@ -235,3 +235,51 @@ def test_prefill_sas_rejects_before_any_launch():
                                None) == lib.EINVAL
     assert so.attn_prefill_sas(P, P, P, P, P, 1, 8, 2, 1024, 96, 1, 4.0, 3, None,
                                None) == lib.EINVAL
+
+
+def _bits(*b):
+    import ctypes
+    return (ctypes.c_uint8 * len(b))(*b)
+
+
+def test_hybrid_entry_points_reject_before_any_launch():
+    so = lib.load()
+    c4, c2 = [P] * 4, [P] * 4
+    # quantiser: widths other than 4 and 2, NULL kv_bits, too many heads,
+    # NULL arrays of a width that has heads, the single-width checks
+    q = so.attn_kv_quantize_hybrid
+    assert q(P, P, _bits(4, 3), *c4, *c2, 1, 2, 4096, 128, None) == lib.EINVAL
+    assert "kv_bits[1]" in lib.attn_last_error()
+    assert q(P, P, None, *c4, *c2, 1, 2, 4096, 128, None) == lib.EINVAL
+    assert q(P, P, _bits(*([4] * 257)), *c4, *c2, 1, 257, 4096, 128, None) == lib.EUNSUPPORTED
+    assert q(P, P, _bits(4, 2), *c4, None, P, P, P, 1, 2, 4096, 128, None) == lib.EINVAL
+    assert q(P, P, _bits(4, 2), *c4, *c2, 1, 2, 4096, 96, None) == lib.EINVAL
+    # the arrays of a width with no head are not looked at
+    assert q(P, P, _bits(2, 2), P + 4, P, P, P, *c2, 0, 2, 4096, 128, None) == lib.OK
+    assert q(P, P, _bits(4, 2), P + 4, P, P, P, *c2, 0, 2, 4096, 128, None) == lib.EINVAL
+    # a width with no head takes NULL arrays (B = 0: nothing launched)
+    assert q(P, P, _bits(2, 2), None, None, None, None, *c2, 0, 2, 4096, 128, None) == lib.OK
+    assert q(P, P, _bits(4, 4), *c4, None, None, None, None, 0, 2, 4096, 128, None) == lib.OK
+    r = so.attn_kv_quantize_hybrid_range
+    assert r(P, P, _bits(4, 2), *c4, *c2, 1, 2, 4096, 128, 32, 64, None) == lib.EUNSUPPORTED
+    assert r(P, P, _bits(4, 2), *c4, *c2, 1, 2, 4096, 128, 0, 4097, None) == lib.EINVAL
+    # decode
+    ws = lib.attn_decode_workspace_bytes(16, 64, 4096, 128)
+    d = so.attn_decode_hybrid
+    args = lambda bits, a4, a2, **kw: ([P, bits, *a4, *a2, P, P, kw.get("B", 16), kw.get("Hq", 64),
+                                        kw.get("Hkv", 8), 4096, kw.get("d", 128), 4.0, None, P,
+                                        kw.get("ws", ws), None])
+    b8 = _bits(4, 2, 4, 2, 4, 2, 4, 2)
+    assert d(*args(b8, c4, c2, d=96)) == lib.EINVAL
+    assert d(*args(b8, c4, c2, ws=ws - 1)) == lib.EWORKSPACE
+    assert d(*args(b8, c4, [P, None, P, P])) == lib.EINVAL
+    assert d(*args(b8, [P, P, P + 8, P], c2)) == lib.EINVAL
+    assert d(*args(_bits(4, 2, 4, 2, 4, 2, 4, 1), c4, c2)) == lib.EINVAL
+    assert d(*args(b8, c4, c2, Hq=60)) == lib.EINVAL
+    assert d(*args(_bits(4, 4, 4, 4, 4, 4, 4, 4), c4, [None] * 4, B=0)) == lib.OK
+    dc = so.attn_decode_hybrid_cap
+    base = [P, b8, *c4, *c2, P, P, 16, 64, 8, 4096]
+    tail = [None, P, lib.attn_decode_workspace_bytes(16, 64, 4096, 128), None]
+    assert dc(*base, 4000, 128, 4.0, 0, *tail) == lib.EINVAL      # cap < L
+    assert dc(*base, 8192, 128, 4.0, 1, *tail) == lib.EINVAL      # degree 1
+    assert "degree" in lib.attn_last_error()

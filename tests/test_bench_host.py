@@ -97,10 +97,13 @@ def test_cpu_baseline_runs_on_tiny_inputs(bench):
         return synth.f32_to_bf16_bits(rng.normal(size=shape).astype(np.float32))
     pq, pk, pv = bits(1, 1, 256, 64), bits(1, 1, 256, 64), bits(1, 1, 256, 64)
     dq, dk, dv = bits(2, 4, 64), bits(2, 2, 300, 64), bits(2, 2, 300, 64)
-    pre, dec, dq4, dq2 = bench.cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=4, nkv=3, nkv_q=2,
-                                            pname="tiny")
-    for r in (pre, dec, dq4, dq2):
+    pre, dec, dq4, dq2, dqh = bench.cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=4, nkv=3,
+                                                 nkv_q=2, pname="tiny", hybrid_bits=(4, 2))
+    for r in (pre, dec, dq4, dq2, dqh):
         assert r["kind"] == "oracle" and r["value"] > 0 and r["cores"] >= 1
         assert r["host_cores"] == os.cpu_count() and r["cores"] <= r["host_cores"]
     assert pre["unit"] == "TFLOP/s" and dq2["unit"] == "GB/s"
-    assert "2-bit" in dq2["sample"] and "4-bit" in dq4["sample"]
+    assert "2-bit" in dq2["sample"] and "4-bit" in dq4["sample"] and "hybrid" in dqh["sample"]
+    # without a hybrid width list the hybrid leg is not run
+    assert bench.cpu_baseline(pq, pk, pv, dq, dk, dv, nblocks=2, nkv=1, nkv_q=1,
+                              pname="tiny")[4] is None
