@@ -7,8 +7,8 @@ path. It shares no code with the HIP kernels.
 from .attention import (TILE, SPLIT, KEPT, SKIPPED, NOT_VISITED, prefill,
                         prefill_blocks, prefill_decisions, decode, decode_head,
                         decode_heads)
-from . import fp8, int8, kvq2, kvq4, kvq_hybrid, sas
+from . import fp8, fp8pv, int8, kvq2, kvq4, kvq_hybrid, sas
 
 __all__ = ["TILE", "SPLIT", "KEPT", "SKIPPED", "NOT_VISITED", "prefill",
-           "prefill_blocks", "prefill_decisions", "decode", "decode_head", "decode_heads", "fp8", "int8", "kvq2", "kvq4",
+           "prefill_blocks", "prefill_decisions", "decode", "decode_head", "decode_heads", "fp8", "fp8pv", "int8", "kvq2", "kvq4",
            "kvq_hybrid", "sas"]
