@@ -183,6 +183,32 @@ int attn_prefill_qk8(const void* q, const void* k, const void* v, float* o,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_prefill_pv8 - attn_prefill with the P.V product on 8-bit operands too
+ * (TurboAttention talk page, "Technical Deep Dive" and "Key Findings": both
+ * products of blockwise attention on block-quantised 8-bit operands), QK^T
+ * in bf16 (qk8 = 0) or as in attn_prefill_qk8 (qk8 = 1; any other value:
+ * SKIPATTN_EINVAL). V is quantised by the call into E4M3 codes with one fp32
+ * scale per (sequence, KV head), s = (largest |v| of the head) / 448 (1 for
+ * a head of zeros), code = E4M3 of v / s (fp32 division, ties to even). Each
+ * probability, taken relative to the row's reference maximum (the running
+ * maximum as of the last rescale, which moves once some row of the 64-row
+ * block has grown past it by more than 8 ln 2, taking every grown row to its
+ * running maximum), is rounded to E4M3 without a scale (it stays below 2^8)
+ * before it multiplies V's codes; the row sums stay over the unrounded
+ * probabilities. O = s (sum of E4M3(p) codes) / l, LSE = m_ref + ln l.
+ * Skip decisions follow the rule on the (bf16 or 8-bit) scores. Arguments,
+ * outputs and errors as for attn_prefill, whole sequences only, plus the
+ * workspace: attn_prefill_pv8_workspace_bytes(B, Hq, Hkv, N, d, qk8) bytes,
+ * 16-byte aligned (SKIPATTN_EWORKSPACE if smaller or NULL), holding the V
+ * code blocks, their scales and (qk8) the parts of attn_prefill_qk8's.
+ */
+size_t attn_prefill_pv8_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int qk8);
+int attn_prefill_pv8(const void* q, const void* k, const void* v, float* o,
+                     float* lse, int B, int Hq, int Hkv, int N, int d,
+                     int causal, float tau, int qk8, uint8_t* skip_mask,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * attn_decode_workspace_bytes - bytes of device scratch attn_decode needs:
  * B * Hq * ceil(L / 4096) * (d + 1) * 4 (per-split partial outputs and
  * log-sum-exps). Returns 0 for invalid or empty sizes.

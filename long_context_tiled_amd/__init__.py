@@ -11,7 +11,8 @@ from ._lib import (OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, TILE, SPLIT,
                    DECODE_SCRATCH_BYTES, attn_prefill_qk8, attn_prefill_qk8_workspace_bytes,
                    qk8_workspace_parts, prefill_qk8, attn_prefill_sas, hybrid_shapes,
                    attn_kv_quantize_hybrid, attn_decode_hybrid, empty_hybrid, quantize_hybrid,
-                   decode_hybrid)
+                   decode_hybrid, attn_prefill_pv8, attn_prefill_pv8_workspace_bytes,
+                   pv8_workspace_parts, prefill_pv8)
 
 __all__ = ["OK", "EINVAL", "EUNSUPPORTED", "EWORKSPACE", "EHIP", "TILE", "SPLIT",
            "KEPT", "SKIPPED", "NOT_VISITED", "EXPORTS", "LIB_PATH", "SkipAttnError",
@@ -23,4 +24,6 @@ __all__ = ["OK", "EINVAL", "EUNSUPPORTED", "EWORKSPACE", "EHIP", "TILE", "SPLIT"
            "attn_decode_noalloc", "DECODE_SCRATCH_BYTES", "attn_prefill_qk8",
            "attn_prefill_qk8_workspace_bytes", "qk8_workspace_parts", "prefill_qk8",
            "attn_prefill_sas", "hybrid_shapes", "attn_kv_quantize_hybrid",
-           "attn_decode_hybrid", "empty_hybrid", "quantize_hybrid", "decode_hybrid"]
+           "attn_decode_hybrid", "empty_hybrid", "quantize_hybrid", "decode_hybrid",
+           "attn_prefill_pv8", "attn_prefill_pv8_workspace_bytes", "pv8_workspace_parts",
+           "prefill_pv8"]

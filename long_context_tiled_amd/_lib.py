@@ -29,7 +29,8 @@ EXPORTS = ("attn_prefill", "attn_decode", "attn_decode_workspace_bytes",
            "attn_decode_q2_sas", "attn_prefill_chunk_cap", "attn_decode_cap",
            "attn_decode_q4_cap", "attn_decode_q2_cap", "attn_decode_noalloc",
            "attn_prefill_qk8", "attn_prefill_qk8_workspace_bytes", "attn_kv_quantize_hybrid",
-           "attn_kv_quantize_hybrid_range", "attn_decode_hybrid", "attn_decode_hybrid_cap")
+           "attn_kv_quantize_hybrid_range", "attn_decode_hybrid", "attn_decode_hybrid_cap",
+           "attn_prefill_pv8", "attn_prefill_pv8_workspace_bytes")
 
 _lib = None
 
@@ -74,6 +75,11 @@ def load() -> ctypes.CDLL:
     lib.attn_prefill_qk8.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, i, f, u8p, vp, sz,
                                      vp]
     lib.attn_prefill_qk8.restype = i
+    lib.attn_prefill_pv8.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, i, f, i, u8p, vp, sz,
+                                     vp]
+    lib.attn_prefill_pv8.restype = i
+    lib.attn_prefill_pv8_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.attn_prefill_pv8_workspace_bytes.restype = sz
     lib.attn_prefill_qk8_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.attn_prefill_qk8_workspace_bytes.restype = sz
     lib.attn_decode_noalloc.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, f, u8p, vp]
@@ -269,6 +275,58 @@ def attn_prefill_qk8(q, k, v, o, lse, causal: bool, tau: float, workspace, skip_
     rc = load().attn_prefill_qk8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N,
                                  d, int(bool(causal)), float(tau), _ptr(skip_mask),
                                  _ptr(workspace), nbytes, _stream(stream))
+    _raise(rc)
+
+
+def attn_prefill_pv8_workspace_bytes(B: int, Hq: int, Hkv: int, N: int, d: int,
+                                     qk8: bool) -> int:
+    return int(load().attn_prefill_pv8_workspace_bytes(B, Hq, Hkv, N, d, int(bool(qk8))))
+
+
+def pv8_workspace_parts(workspace, B: int, Hq: int, Hkv: int, N: int, d: int, qk8: bool) -> dict:
+    """Views of an attn_prefill_pv8 workspace: V code blocks uint8
+    [B,Hkv,ceil(N/64),d,64], the V tiles' largest |v| fp32 [B,Hkv,ceil(N/64)],
+    the V scales fp32 [B,Hkv], and (qk8) the attn_prefill_qk8 parts (each
+    part starts on a 256-byte boundary)."""
+    import torch
+    nt = (N + TILE - 1) // TILE
+    al = lambda x: (x + 255) // 256 * 256
+    w = workspace.view(torch.uint8)
+    out, off = {}, 0
+    for name, n in (("vc", B * Hkv * nt * TILE * d), ("vt", B * Hkv * nt * 4), ("vs", B * Hkv * 4)):
+        out[name] = w[off:off + n]
+        off += al(n)
+    out["vc"] = out["vc"].view(B, Hkv, nt, d, TILE)
+    out["vt"] = out["vt"].view(torch.float32).view(B, Hkv, nt)
+    out["vs"] = out["vs"].view(torch.float32).view(B, Hkv)
+    if qk8:
+        out.update(qk8_workspace_parts(w[off:], B, Hq, Hkv, N, d))
+    return out
+
+
+def attn_prefill_pv8(q, k, v, o, lse, causal: bool, tau: float, workspace, qk8: bool = False,
+                     skip_mask=None, stream=None) -> None:
+    """attn_prefill with P.V on 8-bit operands (V as E4M3 codes with one scale
+    per KV head, probabilities rounded to E4M3), QK^T in bf16 or (qk8) as in
+    attn_prefill_qk8; the workspace (attn_prefill_pv8_workspace_bytes)
+    receives the codes and scales (pv8_workspace_parts)."""
+    import torch
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    _check(q, "q", torch.bfloat16, (B, Hq, N, d))
+    _check(k, "k", torch.bfloat16, (B, Hkv, N, d))
+    _check(v, "v", torch.bfloat16, (B, Hkv, N, d))
+    _check(o, "o", torch.float32, (B, Hq, N, d))
+    _check(lse, "lse", torch.float32, (B, Hq, N))
+    if skip_mask is not None:
+        nt = (N + TILE - 1) // TILE
+        _check(skip_mask, "skip_mask", torch.uint8, (B, Hq, nt, nt))
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = load().attn_prefill_pv8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N,
+                                 d, int(bool(causal)), float(tau), int(bool(qk8)),
+                                 _ptr(skip_mask), _ptr(workspace), nbytes, _stream(stream))
     _raise(rc)
 
 
@@ -648,6 +706,26 @@ def prefill_qk8(q, k, v, causal: bool, tau: float = math.inf, want_mask: bool = 
         nbytes = max(256, attn_prefill_qk8_workspace_bytes(B, Hq, Hkv, N, d))
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     attn_prefill_qk8(q, k, v, o, lse, causal, tau, workspace, mask, stream)
+    return o, lse, mask, workspace
+
+
+def prefill_pv8(q, k, v, causal: bool, tau: float = math.inf, qk8: bool = False,
+                want_mask: bool = False, workspace=None, stream=None):
+    """Allocate outputs (and the workspace if not given) and call
+    attn_prefill_pv8. Returns (o, lse, mask, workspace)."""
+    import torch
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    mask = None
+    if want_mask:
+        nt = (N + TILE - 1) // TILE
+        mask = torch.empty((B, Hq, nt, nt), dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        nbytes = max(256, attn_prefill_pv8_workspace_bytes(B, Hq, Hkv, N, d, qk8))
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    attn_prefill_pv8(q, k, v, o, lse, causal, tau, workspace, qk8, mask, stream)
     return o, lse, mask, workspace
 
 

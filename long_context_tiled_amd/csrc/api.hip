@@ -177,6 +177,22 @@ Qk8Layout qk8_layout(int B, int Hq, int Hkv, int N, int d) {
   return l;
 }
 
+// Workspace of attn_prefill_pv8: the V code blocks, the V tiles' largest
+// |v| (scratch), the V scales, then (qk8) the parts of attn_prefill_qk8.
+struct Pv8Layout {
+  size_t vc, vt, vs, qk, total;
+};
+Pv8Layout pv8_layout(int B, int Hq, int Hkv, int N, int d, int qk8) {
+  Pv8Layout l;
+  const size_t nt = ((size_t)N + SKIPATTN_TILE - 1) / SKIPATTN_TILE;
+  l.vc = 0;
+  l.vt = l.vc + align256((size_t)B * Hkv * nt * SKIPATTN_TILE * d);
+  l.vs = l.vt + align256((size_t)B * Hkv * nt * 4);
+  l.qk = l.vs + align256((size_t)B * Hkv * 4);
+  l.total = l.qk + (qk8 ? qk8_layout(B, Hq, Hkv, N, d).total : 0);
+  return l;
+}
+
 int decode_launch(const void* q, const void* k, const void* v, float* o, float* lse, int B,
                   int Hq, int Hkv, int L, int cap, int d, float tau, int degree,
                   uint8_t* skip_mask, void* workspace, size_t workspace_bytes, void* stream) {
@@ -409,6 +425,55 @@ int attn_prefill_sas(const void* q, const void* k, const void* v, float* o, floa
     return fail(SKIPATTN_EINVAL, "SAS degree must be 0, 2 or 3 (got %d)", degree);
   return prefill_launch(q, k, v, o, lse, B, Hq, Hkv, N, N, N, d, causal, tau, skip_mask, stream,
                         degree);
+}
+
+size_t attn_prefill_pv8_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int qk8) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
+  return pv8_layout(B, Hq, Hkv, N, d, qk8 != 0).total;
+}
+
+int attn_prefill_pv8(const void* q, const void* k, const void* v, float* o, float* lse, int B,
+                     int Hq, int Hkv, int N, int d, int causal, float tau, int qk8,
+                     uint8_t* skip_mask, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int e = prefill_check(q, k, v, o, lse, B, Hq, Hkv, N, N, N, d, causal, tau, skip_mask))
+    return e;
+  if (qk8 != 0 && qk8 != 1) return fail(SKIPATTN_EINVAL, "qk8 must be 0 or 1 (got %d)", qk8);
+  if (B == 0 || N == 0) return SKIPATTN_OK;
+  const Pv8Layout l = pv8_layout(B, Hq, Hkv, N, d, qk8);
+  if (workspace == nullptr || workspace_bytes < l.total)
+    return fail(SKIPATTN_EWORKSPACE, "prefill_pv8 workspace needs %zu bytes (got %zu)", l.total,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (!aligned16(workspace)) return fail(SKIPATTN_EINVAL, "workspace must be 16-byte aligned");
+  char* ws = (char*)workspace;
+  uint8_t* vc = (uint8_t*)(ws + l.vc);
+  float* vt = (float*)(ws + l.vt);
+  float* vs = (float*)(ws + l.vs);
+  if (skipattn::launch_quantize_v8(v, vc, vt, vs, (long long)B * Hkv, N, d, stream) != 0)
+    return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
+  skipattn::PrefillArgs a{q,  k,  vc, o, lse, skip_mask, B, Hq, Hkv, N, d, causal,
+                          N,  0,  N, tau_raw(tau, d), exp2_scale(d), stream};
+  a.vscale = vs;
+  if (qk8) {
+    const Qk8Layout lq = qk8_layout(B, Hq, Hkv, N, d);
+    char* wq = ws + l.qk;
+    uint8_t* qc = (uint8_t*)(wq + lq.qc);
+    uint8_t* kc = (uint8_t*)(wq + lq.kc);
+    float* qs = (float*)(wq + lq.qs);
+    float* ks = (float*)(wq + lq.ks);
+    if (skipattn::launch_quantize_fp8(q, qc, qs, (long long)B * Hq, N, d, stream) != 0 ||
+        skipattn::launch_quantize_fp8(k, kc, ks, (long long)B * Hkv, N, d, stream) != 0)
+      return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
+    a.q = qc;
+    a.k = kc;
+    a.qscale = qs;
+    a.kscale = ks;
+  }
+  const int lr = skipattn::launch_prefill(a);
+  if (lr == -1) return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
+  if (lr != 0) return fail(SKIPATTN_EHIP, "prefill_pv8: device query for the work queue failed");
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(SKIPATTN_EHIP, "prefill_pv8 launch: %s", hipGetErrorString(err));
+  return SKIPATTN_OK;
 }
 
 size_t attn_prefill_qk8_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {

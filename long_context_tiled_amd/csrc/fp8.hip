@@ -104,7 +104,147 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
   }
 }
 
+// ---- V for the 8-bit P.V product: one scale per (sequence, KV head) ----
+// (TurboAttention talk page, "Technical Deep Dive": the PV product on 8-bit
+// operands too.) A per-tile scale would not factor out of P.V, whose sum
+// runs over every key tile into one accumulator, so V takes one scale per
+// head: s = (largest |v| of the head) / 448, 1 for a head of zeros. Three
+// passes: the tiles' largest |v|, the head's scale, the codes.
+//
+// Code layout, per head and 64-key tile t: D rows of 64 bytes; row c holds
+// channel c's codes in the order of the P.V contraction index j (j = 32 h +
+// 16 a + 4 i + e holds key 32 a + 8 i + 4 h + e of the tile: the order in
+// which a lane's probabilities come out of the S^T accumulators), with the
+// row's 16-byte chunk x stored at chunk x ^ ((c >> 2) & 3) so that the
+// kernel's 16-lane reads of 16 consecutive rows hit distinct LDS banks.
+// Keys past N have code 0.
+
+// Largest |v| of each 64-key tile: thread t reads row t / 4 of the tile.
+template <int D>
+__global__ __launch_bounds__(256) void v8_tile_max_kernel(const uint16_t* __restrict__ x,
+                                                          float* __restrict__ tmax, int N,
+                                                          int nt) {
+  constexpr int E = D / 4;
+  __shared__ float wmax[4];
+  const long long xi = blockIdx.x / nt;
+  const int t = blockIdx.x % nt;
+  const int tid = threadIdx.x;
+  const int row = t * kTile + (tid >> 2);
+  float m = 0.f;
+  if (row < N) {
+    const uint16_t* src = x + ((size_t)xi * N + row) * D + (tid & 3) * E;
+#pragma unroll
+    for (int p = 0; p < E / 8; ++p) {
+      const u32x4 w = ldg16(src + 8 * p);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        m = fmaxf(m, fmaxf(fabsf(bf16_bits_f32(w[i] & 0xffffu)), fabsf(bf16_bits_f32(w[i] >> 16))));
+    }
+  }
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) m = fmaxf(m, __shfl_xor(m, sh));
+  if ((tid & 63) == 0) wmax[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0) tmax[blockIdx.x] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+}
+
+// The head's scale from its tiles' maxima.
+__global__ __launch_bounds__(256) void v8_head_scale_kernel(const float* __restrict__ tmax,
+                                                            float* __restrict__ vscale, int nt) {
+  __shared__ float wmax[4];
+  const int tid = threadIdx.x;
+  const float* src = tmax + (size_t)blockIdx.x * nt;
+  float m = 0.f;
+  for (int t = tid; t < nt; t += 256) m = fmaxf(m, src[t]);
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) m = fmaxf(m, __shfl_xor(m, sh));
+  if ((tid & 63) == 0) wmax[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0) {
+    m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    vscale[blockIdx.x] = m > 0.f ? m / 448.f : 1.f;
+  }
+}
+
+// Codes of one tile: the tile's bf16 rows go to LDS (rows past N as zeros),
+// then thread t writes 64 D / 256 bytes of the tile's code block, gathering
+// each byte's key and channel from LDS.
+template <int D>
+__global__ __launch_bounds__(256) void v8_quant_kernel(const uint16_t* __restrict__ x,
+                                                       const float* __restrict__ vscale,
+                                                       uint8_t* __restrict__ codes, int N,
+                                                       int nt) {
+  constexpr int E = D / 4;
+  constexpr int BPT = 64 * D / 256;  // code bytes per thread: 32 (D = 128) or 16
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kTile][D];
+  const long long xi = blockIdx.x / nt;
+  const int t = blockIdx.x % nt;
+  const int tid = threadIdx.x;
+  {
+    const int r = tid >> 2;
+    const int row = t * kTile + r;
+    const uint16_t* src = x + ((size_t)xi * N + (row < N ? row : 0)) * D + (tid & 3) * E;
+#pragma unroll
+    for (int p = 0; p < E / 8; ++p) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (row < N) w = ldg16(src + 8 * p);
+      *reinterpret_cast<u32x4*>(&tile[r][(tid & 3) * E + 8 * p]) = w;
+    }
+  }
+  __syncthreads();
+  const float sc = vscale[xi];
+  const int c = tid / (256 / D);                 // channel (code row)
+  const int p0 = (tid % (256 / D)) * BPT;        // first byte of this thread in the row
+  const int sw = (c >> 2) & 3;
+  uint8_t* dst = codes + ((size_t)xi * nt + t) * (64 * D) + c * 64 + p0;
+#pragma unroll
+  for (int q = 0; q < BPT / 16; ++q) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int p = p0 + 16 * q + 4 * i + b;             // stored byte position
+        const int j = 16 * ((p >> 4) ^ sw) + (p & 15);     // contraction index
+        const int key = 32 * ((j >> 4) & 1) + 8 * ((j >> 2) & 3) + 4 * (j >> 5) + (j & 3);
+        const float v = bf16_bits_f32(tile[key][c]);
+        const float y = fminf(fmaxf(v / sc, -448.f), 448.f);
+        word |= e4m3_code(y) << (8 * b);
+      }
+      w[i] = word;
+    }
+    *reinterpret_cast<u32x4*>(dst + 16 * q) = w;
+  }
+}
+
 }  // namespace
+
+int launch_quantize_v8(const void* v, uint8_t* codes, float* tmax, float* vscale, long long X,
+                       int N, int D, void* stream) {
+  const int nt = (N + kTile - 1) / kTile;
+  const long long blocks = X * nt;
+  if (blocks <= 0) return 0;
+  if (blocks > 0x7fffffffLL) return -1;
+  hipStream_t st = (hipStream_t)stream;
+  const uint16_t* x = (const uint16_t*)v;
+  if (D == 128) {
+    hipLaunchKernelGGL((v8_tile_max_kernel<128>), dim3((unsigned)blocks), dim3(256), 0, st, x,
+                       tmax, N, nt);
+    hipLaunchKernelGGL(v8_head_scale_kernel, dim3((unsigned)X), dim3(256), 0, st, tmax, vscale,
+                       nt);
+    hipLaunchKernelGGL((v8_quant_kernel<128>), dim3((unsigned)blocks), dim3(256), 0, st, x,
+                       vscale, codes, N, nt);
+  } else {
+    hipLaunchKernelGGL((v8_tile_max_kernel<64>), dim3((unsigned)blocks), dim3(256), 0, st, x,
+                       tmax, N, nt);
+    hipLaunchKernelGGL(v8_head_scale_kernel, dim3((unsigned)X), dim3(256), 0, st, tmax, vscale,
+                       nt);
+    hipLaunchKernelGGL((v8_quant_kernel<64>), dim3((unsigned)blocks), dim3(256), 0, st, x,
+                       vscale, codes, N, nt);
+  }
+  return 0;
+}
 
 int launch_quantize_fp8(const void* x, uint8_t* codes, float* scales, long long X, int N, int D,
                         void* stream) {

@@ -75,12 +75,13 @@ NOP_MFMA_READ_LOAD = 2
 NOP_MFMA16_READ_LOAD = 4
 NOP_VALU_PERM = 2
 
-COST = {"v_exp_f32": 8.2, "v_cvt_pk_bf16_f32": 6.0}
+COST = {"v_exp_f32": 8.2, "v_cvt_pk_bf16_f32": 6.0, "v_cvt_pk_fp8_f32": 6.0}
 COST_DEFAULT = 4.2
 
 SBUF = {"A": 128, "B": 192}
 KREG = 64     # K / V^T fragments, v[64:95]
-PREG = 96     # P^T operand, v[96:127]
+PREG = 96     # P^T operand, v[96:127] (8-bit P.V: v[96:111])
+VF8 = (80, 88, 64, 72)  # 8-bit P.V: V^T fragment of 32-d block mb, 8 registers
 TREG = 48     # exp temporaries, three pairs v[48:53]
 VADR = 54     # V^T read addresses, v[54 : 54 + 2 MB)
 KADR = 62     # K read addresses, v62 / v63 alternating
@@ -120,8 +121,10 @@ class Ins:
 class Step:
     """One step variant for one head dim and buffer assignment."""
 
-    def __init__(self, d, variant, x, y, budget, loop=False, dma=False, f8=False, sas=0):
+    def __init__(self, d, variant, x, y, budget, loop=False, dma=False, f8=False, sas=0,
+                 v8=False):
         self.loop = loop
+        self.v8 = v8          # P.V on fp8: one 32x32x64 MFMA per (d block, query half)
         self.sas = sas        # 0: exp2; 2 or 3: the SAS exponential of that degree
         self.dma = dma
         self.d = d
@@ -130,6 +133,7 @@ class Step:
         self.KS = d // 64 if f8 else d // 16   # QK k-steps
         self.QB = OB + 32 * self.MB
         self.rowBytes = 2 * d                  # V rows (bf16)
+        self.vTileBytes = 64 * d if v8 else 64 * self.rowBytes
         self.kRowBytes = d if f8 else 2 * d    # K and Q rows
         self.variant = variant
         self.x = x  # buffer holding tile n (exp / PV)
@@ -159,6 +163,34 @@ class Step:
 
     def pfrag(self, kp, nb):
         return rng("v", PREG + 4 * (2 * kp + nb), 4)
+
+    def pfrag8(self, nb):
+        # 8-bit P.V: query half nb's probabilities of the whole tile, 32 bytes
+        return rng("v", PREG + 8 * nb, 8)
+
+    def vfrag8(self, mb):
+        return rng("v", VF8[mb], 8)
+
+    def v_loads8(self, mbs):
+        """8-bit P.V: V^T fragments of the given 32-d blocks. Row c of the
+        tile's code block (64 bytes) holds channel c in contraction order;
+        lane l reads row 32 mb + (l & 31), 32 bytes: the chunk at %[vb0]
+        and the one at %[vb1] (= %[vb0] ^ 16), block mb 2 KB further."""
+        out = []
+        for mb in mbs:
+            base = VF8[mb]
+            for half, adr in ((0, "%[vb0]"), (1, "%[vb1]")):
+                dst = rng("v", base + 4 * half, 4)
+                out.append(Ins(f"ds_read_b128 {dst}, {adr} offset:{2048 * mb}", "lds",
+                               wr=[dst], rd=[adr]))
+        return out
+
+    def pv8_mfma(self, mb, nb):
+        o = self.oblk(mb, nb)
+        vf = self.vfrag8(mb)
+        pf = self.pfrag8(nb)
+        return Ins(f"v_mfma_f32_32x32x64_f8f6f4 {o}, {vf}, {pf}, {o}", "mfma16", wr=[o],
+                   rd=[vf, pf, o], tag=("pv8", nb))
 
     def qfrag(self, ks, nb):
         if self.f8:
@@ -239,11 +271,11 @@ class Step:
         wave's LDS destination base."""
         groups = []
         n = 0
-        if self.f8:
-            # K (fp8 rows) and V (bf16 rows) tiles differ in size: %[t1] / %[t4]
-            # are their byte offsets, %[t2] / %[t5] this wave's LDS bases
+        if self.f8 or self.v8:
+            # K and V tiles of different formats: %[t1] / %[t4] are their byte
+            # offsets, %[t2] / %[t5] this wave's LDS bases
             parts = (("K", "%[krs]", "gk", "%[t1]", "%[t2]", 64 * self.kRowBytes // 4096),
-                     ("V", "%[vrs]", "gv", "%[t4]", "%[t5]", 64 * self.rowBytes // 4096))
+                     ("V", "%[vrs]", "gv", "%[t4]", "%[t5]", self.vTileBytes // 4096))
         else:
             ipw = 64 // (1024 // self.rowBytes) // 4
             tile_bytes = 64 * self.rowBytes
@@ -252,7 +284,7 @@ class Step:
         for which, rs, g, toff, lbase, ipw in parts:
             for i in range(ipw):
                 off = i * 1024
-                if not self.f8 and which == "V":
+                if not (self.f8 or self.v8) and which == "V":
                     off += tile_bytes
                 tmp = "%[vt]" if n % 2 == 0 else "%[vz]"
                 n += 1
@@ -285,6 +317,37 @@ class Step:
         if self.sas:
             return self.sas_stream()
         return self.exp2_stream()
+
+    def pairs(self):
+        """Score pairs (a, nb, r0) of a tile in exponential order: key step by
+        key step for the bf16 P.V (its k-steps consume keys 16 at a time);
+        query half by query half for the 8-bit P.V (one MFMA per query half
+        takes all 64 keys)."""
+        if self.v8:
+            return [(a, nb, r0) for nb in range(2) for a in range(2) for r0 in range(0, 16, 2)]
+        out = []
+        for gp in range(32):
+            ch, i2 = gp >> 2, gp & 3
+            kp, nb = ch >> 1, ch & 1
+            out.append((kp >> 1, nb, 8 * (kp & 1) + 2 * i2))
+        return out
+
+    def pack(self, a, nb, r0, t0, t1):
+        """The pair's P^T operand write: bf16 pair (key step kp), or two fp8
+        bytes of the query half's 32-byte operand: accumulator element r of
+        key half a is contraction index 16 a + r, byte (r & 3) of register
+        4 a + (r >> 2)."""
+        if self.v8:
+            w = f"v{PREG + 8 * nb + 4 * a + (r0 >> 2)}"
+            if r0 & 2:   # bytes 2-3: the high half, the low half kept
+                return Ins(f"v_cvt_pk_fp8_f32 {w}, {t0}, {t1} op_sel:[0,0,1]", "valu", wr=[w],
+                           rd=[t0, t1, w], tag=("pf8", nb))
+            return Ins(f"v_cvt_pk_fp8_f32 {w}, {t0}, {t1}", "valu", wr=[w], rd=[t0, t1],
+                       tag=("pf8", nb))
+        kp = 2 * a + (r0 >> 3)
+        w = f"v{PREG + 4 * (2 * kp + nb) + ((r0 & 7) >> 1)}"
+        return Ins(f"v_cvt_pk_bf16_f32 {w}, {t0}, {t1}", "valu", wr=[w], rd=[t0, t1],
+                   tag=("pf", kp))
 
     def sas_stream(self):
         """The SAS exponential per score: x = (mref - s) / sqrt(d) clamped to
@@ -349,23 +412,20 @@ class Step:
         return out
 
     def exp2_stream(self):
-        """Per score pair: scale-and-shift, exp2, pack to bf16, pair sum into
+        """Per score pair: scale-and-shift, exp2, pack (bf16, or fp8 for the
+        8-bit P.V: the weights stay below 2^8, inside E4M3's range, so they
+        are rounded without a scale), pair sum into
         this tile's partial row sum; at the end each partial sum joins the
         running row sum once. (Adding every exponential straight into the
         running sum loses the small terms once that sum is large: over
         millions of keys the row sum, and so the LSE, came out low.)"""
         heads, tails = [], []
         first = {0: True, 1: True}
-        for gp in range(32):
-            ch, i2 = gp >> 2, gp & 3
-            kp, nb = ch >> 1, ch & 1
-            a = kp >> 1
-            r0 = 8 * (kp & 1) + 2 * i2
+        for gp, (a, nb, r0) in enumerate(self.pairs()):
             s0 = f"v{self.s_reg(self.x, a, nb, r0)}"
             s1 = f"v{self.s_reg(self.x, a, nb, r0 + 1)}"
             t0 = f"v{TREG + 2 * (gp % 3)}"
             t1 = f"v{TREG + 2 * (gp % 3) + 1}"
-            w = f"v{PREG + 4 * (2 * kp + nb) + i2}"
             ps = f"v{PSUM + nb}"
             nm = f"%[nm{nb}]"
             cc = "%[ce]" if self.f8 else "%[c]"
@@ -375,8 +435,7 @@ class Step:
                 Ins(f"v_exp_f32 {t0}, {t0}", "trans", wr=[t0], rd=[t0]),
                 Ins(f"v_exp_f32 {t1}, {t1}", "trans", wr=[t1], rd=[t1]),
             ])
-            tail = [Ins(f"v_cvt_pk_bf16_f32 {w}, {t0}, {t1}", "valu", wr=[w], rd=[t0, t1],
-                        tag=("pf", kp))]
+            tail = [self.pack(a, nb, r0, t0, t1)]
             if first[nb]:
                 tail.append(Ins(f"v_add_f32 {ps}, {t0}, {t1}", "valu", wr=[ps], rd=[t0, t1]))
                 first[nb] = False
@@ -465,7 +524,8 @@ class Step:
         max_q = (self.max_stream() + self.vote_stream()) if self.qk else []
         KS, MB = self.KS, self.MB
         qk_w = 2 if self.f8 else 1      # a 16-pass QK MFMA holds two 8-pass slots
-        n_slots = (4 * KS * qk_w if self.qk else 0) + (8 * MB if self.pv else 0)
+        pv_slots = 4 * MB if self.v8 else 8 * MB   # 2 MB 16-pass or 8 MB 8-pass MFMAs
+        n_slots = (4 * KS * qk_w if self.qk else 0) + (pv_slots if self.pv else 0)
         total_valu = sum(i.cost for i in exp_q) + sum(i.cost for i in max_q)
         budget = max(self.budget, total_valu / max(n_slots, 1))
         pos = {"exp": 0, "max": 0}
@@ -494,10 +554,10 @@ class Step:
                 used += cand[1].cost
                 pos[cand[0]] += 1
 
-        def exp_needed(ks):
+        def exp_needed(ks, kind="pf"):
             last = -1
             for i, ins in enumerate(exp_q):
-                if ins.tag and ins.tag[0] == "pf" and ins.tag[1] <= ks:
+                if ins.tag and ins.tag[0] == kind and ins.tag[1] <= ks:
                     last = i
             return last + 1
 
@@ -505,10 +565,17 @@ class Step:
             if not self.loop:
                 seq += [Ins("v_mov_b32 %[lo0], %[li0]", "valu"),
                         Ins("v_mov_b32 %[lo1], %[li1]", "valu")]
-            seq += self.v_addr()
+            if not self.v8:
+                seq += self.v_addr()
         # phase A --------------------------------------------------------
         if self.qk:
             order = [(a, ks) for a in range(2) for ks in range(KS)]
+            v8_after = {}
+            if self.v8:
+                for mb in range(MB):
+                    mine = set(expand(self.vfrag8(mb)))
+                    v8_after[mb] = max([n for n in range(len(order))
+                                        if mine & set(expand(self.kfrag(n & 3)))], default=-1)
             seq += self.k_load(*order[0], 0)
             seq += self.k_load(*order[1], 1)
             if self.pv:
@@ -520,10 +587,20 @@ class Step:
                     if nb == 0 and n + 2 < len(order):
                         seq += self.k_load(*order[n + 2], (n + 2) & 3)
                     # V^T fragments of PV k-step 0: bf16, once the K fragments
-                    # they overwrite are read; fp8, after key half 0's MFMAs
-                    v0_at = KS if self.f8 else len(order) // 2 + 2
-                    if nb == 0 and self.pv and n == v0_at:
-                        seq += self.v_loads(0)
+                    # they overwrite are read; fp8, after key half 0's MFMAs.
+                    # 8-bit P.V: each block's fragment right after the last
+                    # MFMA that reads a K fragment in its registers (after
+                    # the first MFMA when none does)
+                    if self.v8 and self.pv:
+                        due = [mb for mb in range(MB)
+                               if (v8_after[mb] == n and nb == 1)
+                               or (v8_after[mb] < 0 and n == 0 and nb == 0)]
+                        if due:
+                            seq += self.v_loads8(due)
+                    elif not self.v8:
+                        v0_at = KS if self.f8 else len(order) // 2 + 2
+                        if nb == 0 and self.pv and n == v0_at:
+                            seq += self.v_loads(0)
                     pull(budget * qk_w)
                 # key half 0 final after its last k-step; its maxima wait two
                 # more k-steps (four MFMAs) to clear the MFMA result latency
@@ -533,10 +610,21 @@ class Step:
                     done_half.add(0)
             done_half.add(1)
         elif self.pv:
-            seq += self.v_loads(0)
+            seq += self.v_loads8(range(MB)) if self.v8 else self.v_loads(0)
 
         # phase B --------------------------------------------------------
-        if self.pv:
+        if self.pv and self.v8:
+            # one 16-pass MFMA per (d block, query half); a query half's
+            # probabilities must all be packed before its first MFMA
+            for nb in range(2):
+                need = exp_needed(nb, "pf8")
+                while pos["exp"] < need:
+                    seq.append(exp_q[pos["exp"]])
+                    pos["exp"] += 1
+                for mb in range(MB):
+                    mfma(self.pv8_mfma(mb, nb))
+                    pull(2 * budget)
+        elif self.pv:
             for ks in range(4):
                 need = exp_needed(ks)
                 while pos["exp"] < need:
@@ -840,8 +928,9 @@ def _rename(lines, mapping):
 QA = {"A": "%[qa0]", "B": "%[qa1]"}   # fp8: q scale x k scale of the tile in buffer A / B
 
 
-def _step_lines(d, variant, x, y, budget, dma=True, f8=False, sas=0):
-    st = Step(d, variant, x, y, budget, loop=True, dma=dma, f8=f8, sas=sas).build().fix_hazards()
+def _step_lines(d, variant, x, y, budget, dma=True, f8=False, sas=0, v8=False):
+    st = Step(d, variant, x, y, budget, loop=True, dma=dma, f8=f8, sas=sas,
+              v8=v8).build().fix_hazards()
     return _rename(st.out, {"%[mi0]": "%[m0]", "%[mi1]": "%[m1]", "%[mo0]": "%[m0]",
                             "%[mo1]": "%[m1]", "%[lo0]": "%[ls0]", "%[lo1]": "%[ls1]",
                             "%[qa]": QA[y]})
@@ -949,6 +1038,11 @@ LOOP_ARGS_SAS_DOC = """
 LOOP_ARGS_SAS_FIELDS = """
   float sa[4];
   float c6, c7;"""
+LOOP_ARGS_V8_DOC = """
+// 8-bit P.V: V tiles are E4M3 code blocks (d rows of 64 bytes); wlv is the
+// wave's LDS base for their copies (wl: for K)."""
+LOOP_ARGS_V8_FIELDS = """
+  uint32_t wlv;"""
 LOOP_ARGS_F8_FIELDS = """
   uint64_t ksp;
   float sqv;
@@ -956,12 +1050,12 @@ LOOP_ARGS_F8_FIELDS = """
   uint32_t wlv;"""
 
 
-def loop_cxx(d, causal, budget, f8=False, sas=0):
+def loop_cxx(d, causal, budget, f8=False, sas=0, v8=False):
     MB = d // 32
     row_bytes = 2 * d                        # V rows (bf16)
     krow = d if f8 else 2 * d                # K rows: fp8 codes or bf16
     tile_k = 64 * krow
-    tile_v = 64 * row_bytes
+    tile_v = 64 * d if v8 else 64 * row_bytes   # 8-bit P.V: d rows of 64 codes
     stage_bytes = tile_k + tile_v
     ipwk = tile_k // 1024 // 4               # copy instructions per wave and tile
     ipwv = tile_v // 1024 // 4
@@ -1027,7 +1121,7 @@ def loop_cxx(d, causal, budget, f8=False, sas=0):
         # the copy (zero-filled past N). fp8: K and V tiles differ in size,
         # %[t4] / %[t5] are the V tile's offset and LDS base.
         out = slot_base("%[t2]", 3) + ["s_sub_u32 %[t2], %[t2], %[smem]"]
-        if f8:
+        if f8 or v8:
             out += ["s_add_u32 %[t5], %[t2], %[wlv]",
                     "s_add_u32 %[t4], %[kb], 3", f"s_mul_i32 %[t4], %[t4], {tile_v}"]
         out += ["s_add_u32 %[t2], %[t2], %[wl]",
@@ -1036,7 +1130,7 @@ def loop_cxx(d, causal, budget, f8=False, sas=0):
 
     def dma_alone():
         out = []
-        for g in Step(d, "qk", "A", "A", 0, loop=True, dma=True, f8=f8).dma_groups():
+        for g in Step(d, "qk", "A", "A", 0, loop=True, dma=True, f8=f8, v8=v8).dma_groups():
             out += [i.text for i in g]
         return out
 
@@ -1071,7 +1165,7 @@ def loop_cxx(d, causal, budget, f8=False, sas=0):
     L += ["s_cmp_gt_i32 %[nkbw], 0", f"s_cbranch_scc0 {lab('loop')}"]
     L += ["s_mov_b32 %[t0], %[smem]", "v_add_u32 %[kb0], %[t0], %[frag]"]
     L += rare("0")
-    L += _step_lines(d, "qk", "A", "A", budget, dma=False, f8=f8)
+    L += _step_lines(d, "qk", "A", "A", budget, dma=False, f8=f8, v8=v8)
     L += after_vote("0", "A", "p0")
     L += [f"{lab('loop')}:"]
     for x, y in (("A", "B"), ("B", "A")):
@@ -1092,9 +1186,9 @@ def loop_cxx(d, causal, budget, f8=False, sas=0):
               "s_cmp_lg_u64 %[grow], 0", f"s_cbranch_scc0 {lab('nr' + t)}"]
         L += _rescale_lines(d, sas)
         L += [f"{lab('nr' + t)}:"] + nmc(x) + vaddr()
-        L += _step_lines(d, "full", x, y, budget, f8=f8, sas=sas)
+        L += _step_lines(d, "full", x, y, budget, f8=f8, sas=sas, v8=v8)
         L += [f"s_branch {lab('voted' + t)}", f"{lab('skip' + t)}:"]
-        L += _step_lines(d, "qk", y, y, budget, f8=f8)
+        L += _step_lines(d, "qk", y, y, budget, f8=f8, v8=v8)
         L += [f"{lab('voted' + t)}:", "s_add_u32 %[t1], %[kb], 1"]
         L += after_vote("%[t1]", y, t)
         L += [f"s_branch {lab('end' + t)}",
@@ -1103,7 +1197,7 @@ def loop_cxx(d, causal, budget, f8=False, sas=0):
               "s_cmp_lg_u64 %[grow], 0", f"s_cbranch_scc0 {lab('nrl' + t)}"]
         L += _rescale_lines(d, sas)
         L += [f"{lab('nrl' + t)}:"] + nmc(x) + vaddr()
-        L += _step_lines(d, "pv", x, x, budget, f8=f8, sas=sas)
+        L += _step_lines(d, "pv", x, x, budget, f8=f8, sas=sas, v8=v8)
         L += [f"s_branch {lab('ld' + t)}", f"{lab('idle' + t)}:"]
         L += dma_alone()
         L += [f"{lab('ld' + t)}:", "s_mov_b64 %[keep], 0",
@@ -1140,6 +1234,10 @@ def loop_cxx(d, causal, budget, f8=False, sas=0):
                  '[t5] "=&s"(s32[8])']
         ins_ += ['[ksp] "s"(a.ksp)', '[sqv] "v"(a.sqv)', '[nkbm1] "s"(a.nkbm1)', '[wlv] "s"(a.wlv)']
         nvt, ns32 = 14, 9
+    elif v8:
+        outs += ['[t4] "=&s"(s32[3])', '[t5] "=&s"(s32[8])']
+        ins_ += ['[wlv] "s"(a.wlv)']
+        ns32 = 9
     if sas:
         ins_ += [f'[sa{j}] "s"(a.sa[{j}])' for j in range(sas + 1)]
         ins_ += ['[c6] "s"(a.c6)', '[c7] "s"(a.c7)']
@@ -1152,6 +1250,7 @@ def loop_cxx(d, causal, budget, f8=False, sas=0):
     text = "\n".join(f'      "{t}\\n\\t"' for t in body)
     head = (f"// The key loop of one wave, d = {d}, {'causal' if causal else 'full'} attention"
             f"{', QK^T on fp8 codes' if f8 else ''}"
+            f"{', P.V on fp8 codes' if v8 else ''}"
             f"{f', SAS exponential of degree {sas}' if sas else ''} ({len(body)} lines)")
     name = f"key_loop_{'causal' if causal else 'full'}"
     return "\n".join([
@@ -1176,23 +1275,30 @@ def main(out_path=None):
              "// Per-key-tile steps of the prefill kernel (see the script's docstring for",
              "// the schedule, the register plan and the hazard rules).",
              "#pragma once", ""]
-    for d, budget, f8, sas in ((128, 26.0, False, 0), (64, 30.0, False, 0), (128, 26.0, True, 0),
-                               (64, 30.0, True, 0), (128, 26.0, False, 2), (128, 26.0, False, 3),
-                               (64, 30.0, False, 2), (64, 30.0, False, 3)):
-        ns = f"d{d}f8" if f8 else (f"d{d}s{sas}" if sas else f"d{d}")
+    for d, budget, f8, sas, v8 in ((128, 26.0, False, 0, False), (64, 30.0, False, 0, False),
+                                   (128, 26.0, True, 0, False), (64, 30.0, True, 0, False),
+                                   (128, 26.0, False, 2, False), (128, 26.0, False, 3, False),
+                                   (64, 30.0, False, 2, False), (64, 30.0, False, 3, False),
+                                   (128, 26.0, False, 0, True), (64, 30.0, False, 0, True),
+                                   (128, 26.0, True, 0, True), (64, 30.0, True, 0, True)):
+        ns = (f"d{d}" + ("f8" if f8 else "") + ("v8" if v8 else "")) if not sas else f"d{d}s{sas}"
         parts.append(f"namespace {ns} {{")
         for h in helpers_cxx(d, f8):
             parts.append(h)
             parts.append("")
         ipwv = 64 * 2 * d // 1024 // 4
         ipwk = 64 * d // 1024 // 4 if f8 else ipwv
+        if v8:
+            ipwv = d // 64       # 64 d bytes per V tile, 1 KB per copy, 4 waves
         parts.append(LOOP_ARGS.format(ipwk=ipwk, ipwv=ipwv,
                                       f8doc=LOOP_ARGS_F8_DOC if f8 else (
-                                          LOOP_ARGS_SAS_DOC if sas else ""),
+                                          LOOP_ARGS_SAS_DOC if sas else (
+                                              LOOP_ARGS_V8_DOC if v8 else "")),
                                       f8fields=LOOP_ARGS_F8_FIELDS if f8 else (
-                                          LOOP_ARGS_SAS_FIELDS if sas else "")))
+                                          LOOP_ARGS_SAS_FIELDS if sas else (
+                                              LOOP_ARGS_V8_FIELDS if v8 else ""))))
         for causal in (True, False):
-            parts.append(loop_cxx(d, causal, budget, f8, sas))
+            parts.append(loop_cxx(d, causal, budget, f8, sas, v8))
             parts.append("")
         parts.append(f"}}  // namespace {ns}")
         parts.append("")

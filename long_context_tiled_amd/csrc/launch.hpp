@@ -28,6 +28,10 @@ struct PrefillArgs {
   // 0: exact exponentials; 2 or 3: the SAS exponential of that degree (bf16
   // whole-sequence prefill only)
   int sas = 0;
+  // 8-bit P.V (whole-sequence prefill only): v holds E4M3 code blocks
+  // [B, Hkv, ceil(N/64), d, 64] (launch_quantize_v8) and vscale [B, Hkv]
+  // their scales; null for bf16 V
+  const float* vscale = nullptr;
 };
 
 struct DecodeArgs {
@@ -98,8 +102,9 @@ struct DecodeQ4Args {
 
 // Each returns 0 when the kernels were enqueued, nonzero if the grid cannot
 // be expressed (launch_prefill: -1, -2 when the device's work-queue address
-// or compute-unit count cannot be read, -3 for an SAS request outside the
-// bf16 whole-sequence prefill); launch errors are read back by the caller.
+// or compute-unit count cannot be read, -3 for an SAS or 8-bit P.V request
+// outside their whole-sequence prefills); launch errors are read back by the
+// caller.
 int launch_prefill(const PrefillArgs& a);
 int launch_decode(const DecodeArgs& a);
 int launch_kv_quantize_q4(const QuantArgs& a);
@@ -112,6 +117,11 @@ int launch_decode_q2(const DecodeQ4Args& a);
 // (fp8.hip). Returns nonzero if the grid cannot be expressed.
 int launch_quantize_fp8(const void* x, uint8_t* codes, float* scales, long long X, int N, int D,
                         void* stream);
+// V codes for the 8-bit P.V prefill (fp8.hip): bf16 V [X, N, D] -> E4M3
+// codes in the kernel's tile blocks [X, ceil(N/64), D, 64] with one fp32
+// scale per head, vscale [X]; tmax [X, ceil(N/64)] is scratch.
+int launch_quantize_v8(const void* v, uint8_t* codes, float* tmax, float* vscale, long long X,
+                       int N, int D, void* stream);
 // Bytes of the device-resident decode scratch (decode.hip), and its address
 // on the current device (0 on success; the first call on a device looks it
 // up with that device current).

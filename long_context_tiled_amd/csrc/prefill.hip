@@ -69,15 +69,17 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr uint32_t kBufferCfg = 0x00020000u;  // raw 32-bit buffer, range-checked
 
-// Tile geometry: V rows are bf16 (2 D bytes); K and Q rows are bf16 too, or
-// fp8 codes (D bytes) when QK^T runs on 8-bit operands.
-template <int D, bool F8>
+// Tile geometry: V rows are bf16 (2 D bytes), or with the 8-bit P.V (V8) a
+// V tile is a block of D rows of 64 E4M3 codes (one row per channel, in the
+// contraction order of the P.V product); K and Q rows are bf16 too, or fp8
+// codes (D bytes) when QK^T runs on 8-bit operands.
+template <int D, bool F8, bool V8 = false>
 struct PrefillTile {
-  static constexpr int rowBytes = 2 * D;              // V
+  static constexpr int rowBytes = 2 * D;              // V (bf16)
   static constexpr int chunks = rowBytes / 16;        // 16-byte chunks per V row
-  static constexpr int bytes = kTile * rowBytes;      // one V tile
+  static constexpr int bytes = V8 ? kTile * D : kTile * rowBytes;  // one V tile
   static constexpr int rowsPerInstr = 1024 / rowBytes;
-  static constexpr int instrPerWave = kTile / rowsPerInstr / 4;
+  static constexpr int instrPerWave = bytes / 1024 / 4;
   static constexpr int kRowBytes = F8 ? D : 2 * D;    // K and Q
   static constexpr int kChunks = kRowBytes / 16;
   static constexpr int kBytes = kTile * kRowBytes;    // one K (or Q) tile
@@ -159,10 +161,14 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, lds_void* lds, 
 #pragma clang diagnostic pop
 
 // Calls the d = 128 or d = 64 version of a generated block (bf16 QK^T, or
-// fp8 QK^T when F8_ is set).
-#define SKA_CALL(D_, F8_, SAS_, fn, ...)                                         \
+// fp8 QK^T when F8_ is set; P.V on fp8 codes when V8_ is set).
+#define SKA_CALL(D_, F8_, SAS_, V8_, fn, ...)                                    \
   do {                                                                           \
-    if constexpr ((SAS_) == 2 && (D_) == 128) d128s2::fn(__VA_ARGS__);           \
+    if constexpr ((V8_) && (D_) == 128 && (F8_)) d128f8v8::fn(__VA_ARGS__);      \
+    else if constexpr ((V8_) && (D_) == 128) d128v8::fn(__VA_ARGS__);            \
+    else if constexpr ((V8_) && (F8_)) d64f8v8::fn(__VA_ARGS__);                 \
+    else if constexpr (V8_) d64v8::fn(__VA_ARGS__);                              \
+    else if constexpr ((SAS_) == 2 && (D_) == 128) d128s2::fn(__VA_ARGS__);      \
     else if constexpr ((SAS_) == 2) d64s2::fn(__VA_ARGS__);                      \
     else if constexpr ((SAS_) == 3 && (D_) == 128) d128s3::fn(__VA_ARGS__);      \
     else if constexpr ((SAS_) == 3) d64s3::fn(__VA_ARGS__);                      \
@@ -172,16 +178,20 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, lds_void* lds, 
     else d64f8::fn(__VA_ARGS__);                                                \
   } while (0)
 
-template <int D, bool F8, int SAS>
+template <int D, bool F8, int SAS, bool V8>
 struct LoopArgsOf;
-template <> struct LoopArgsOf<128, false, 0> { using type = d128::LoopArgs; };
-template <> struct LoopArgsOf<64, false, 0> { using type = d64::LoopArgs; };
-template <> struct LoopArgsOf<128, true, 0> { using type = d128f8::LoopArgs; };
-template <> struct LoopArgsOf<64, true, 0> { using type = d64f8::LoopArgs; };
-template <> struct LoopArgsOf<128, false, 2> { using type = d128s2::LoopArgs; };
-template <> struct LoopArgsOf<64, false, 2> { using type = d64s2::LoopArgs; };
-template <> struct LoopArgsOf<128, false, 3> { using type = d128s3::LoopArgs; };
-template <> struct LoopArgsOf<64, false, 3> { using type = d64s3::LoopArgs; };
+template <> struct LoopArgsOf<128, false, 0, false> { using type = d128::LoopArgs; };
+template <> struct LoopArgsOf<64, false, 0, false> { using type = d64::LoopArgs; };
+template <> struct LoopArgsOf<128, true, 0, false> { using type = d128f8::LoopArgs; };
+template <> struct LoopArgsOf<64, true, 0, false> { using type = d64f8::LoopArgs; };
+template <> struct LoopArgsOf<128, false, 2, false> { using type = d128s2::LoopArgs; };
+template <> struct LoopArgsOf<64, false, 2, false> { using type = d64s2::LoopArgs; };
+template <> struct LoopArgsOf<128, false, 3, false> { using type = d128s3::LoopArgs; };
+template <> struct LoopArgsOf<64, false, 3, false> { using type = d64s3::LoopArgs; };
+template <> struct LoopArgsOf<128, false, 0, true> { using type = d128v8::LoopArgs; };
+template <> struct LoopArgsOf<64, false, 0, true> { using type = d64v8::LoopArgs; };
+template <> struct LoopArgsOf<128, true, 0, true> { using type = d128f8v8::LoopArgs; };
+template <> struct LoopArgsOf<64, true, 0, true> { using type = d64f8v8::LoopArgs; };
 
 // F8: Q and K are fp8 (E4M3) codes with one fp32 scale per 64-row Q tile
 // (qsc, [B, Hq, ceil(Nq/64)]) and per 64-key K tile (ksc, [B, Hkv,
@@ -194,12 +204,18 @@ template <> struct LoopArgsOf<64, false, 3> { using type = d64s3::LoopArgs; };
 // degree (T[floor x] p(x - floor x), x the logit gap), with the reference
 // maximum kept equal to the running maximum (no deferred rescale: SAS of a
 // product is not the product of SAS values).
-template <int D, bool CAUSAL, int HPW, int STAGES, bool CHUNK, bool F8, int SAS>
+// V8 (whole-sequence only): P.V runs on v_mfma_f32_32x32x64_f8f6f4 with V as
+// E4M3 code blocks (vsc: one fp32 scale per KV head, [B, Hkv]) and the
+// probabilities rounded to E4M3 as they are packed: relative to the
+// reference maximum they stay below 2^8, inside E4M3's range, so they take
+// no scale. The row sums stay over the unrounded probabilities, and the
+// head's V scale multiplies O with 1 / l.
+template <int D, bool CAUSAL, int HPW, int STAGES, bool CHUNK, bool F8, int SAS, bool V8>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void prefill_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
-    const uint16_t* __restrict__ v, float* __restrict__ o,
+    const uint8_t* __restrict__ v, float* __restrict__ o,
     float* __restrict__ lse, uint8_t* __restrict__ mask, const float* __restrict__ qsc,
-    const float* __restrict__ ksc, int Hq, int Hkv,
+    const float* __restrict__ ksc, const float* __restrict__ vsc, int Hq, int Hkv,
     int Nq_arg, int N, int q0t_arg, int cap_arg, float tau_raw, float c, int nqg, int ny,
     uint32_t* __restrict__ queue, int total) {
   // Nq queries (the chunk) at key positions 64 q0t .. 64 q0t + Nq - 1 of N
@@ -212,13 +228,15 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
   const int cap = CHUNK ? cap_arg : N;  // rows allocated per K/V head
   constexpr int QPW = 4 / HPW;   // query tiles per workgroup
   constexpr int MB = D / 32;     // 32-row d blocks of O^T
-  using T = PrefillTile<D, F8>;
+  using T = PrefillTile<D, F8, V8>;
   constexpr int KRB = T::kRowBytes;
   constexpr int STAGE_BYTES = T::kBytes + T::bytes;  // K tile then V tile
   // STAGES K/V slots, tile t in slot t % STAGES. The four Q tiles are
-  // staged in slots 3-4 before the loop.
-  static_assert(STAGES == 5 && 4 * T::kBytes <= 2 * STAGE_BYTES, "slot plan");
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
+  // staged from slot 3 on before the loop (with 8-bit V tiles and bf16 Q
+  // they run past the slots).
+  constexpr int SMEM_BYTES = std::max(STAGES * STAGE_BYTES, 3 * STAGE_BYTES + 4 * T::kBytes);
+  static_assert(STAGES == 5 && SMEM_BYTES <= 160 * 1024, "slot plan");
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
   typedef __attribute__((address_space(3))) char lds_char;
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_char*)smem;  // LDS byte address
 
@@ -251,10 +269,11 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
     const int nkb_w = wave_valid ? (CAUSAL ? qbg + 1 : nkb) : 0;
 
     const int k_head_bytes = N * KRB;
-    const int v_head_bytes = N * D * 2;
+    // V8: the head's code blocks, nkb of them (N = cap for the V8 instances)
+    const int v_head_bytes = V8 ? nkb * T::bytes : N * D * 2;
     const size_t kv_row0 = (size_t)(b * Hkv + g) * cap;  // first row of the head's K/V
     const uint8_t* kh = k + kv_row0 * KRB;
-    const uint16_t* vh = v + kv_row0 * D;
+    const uint8_t* vh = V8 ? v + (size_t)(b * Hkv + g) * nkb * T::bytes : v + kv_row0 * D * 2;
     const __amdgpu_buffer_rsrc_t krs =
         __builtin_amdgcn_make_buffer_rsrc((void*)kh, (short)0, k_head_bytes, kBufferCfg);
     const __amdgpu_buffer_rsrc_t vrs =
@@ -277,9 +296,14 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
     }
   #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-      const int r = (wave * IPW + i) * T::rowsPerInstr + lane / T::chunks;
-      const int slot = lane % T::chunks;
-      ld_gv[i] = r * T::rowBytes + 16 * (slot ^ swz_v<D>(r));
+      if constexpr (V8) {
+        // code blocks are stored as they sit in LDS: a linear copy
+        ld_gv[i] = (wave * IPW + i) * 1024 + 16 * lane;
+      } else {
+        const int r = (wave * IPW + i) * T::rowsPerInstr + lane / T::chunks;
+        const int slot = lane % T::chunks;
+        ld_gv[i] = r * T::rowBytes + 16 * (slot ^ swz_v<D>(r));
+      }
     }
 
     auto issue_tile = [&](int kb) __attribute__((always_inline)) {
@@ -334,21 +358,29 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
       const int d = 16 * (grp16 & 1) + 4 * (k16 & 3);
       tr0[half] = (uint32_t)(row * T::rowBytes + 16 * ((d >> 3) ^ swz_v<D>(row)) + 2 * (d & 7));
     }
+    if constexpr (V8) {
+      // V^T operand of the 8-bit P.V: lane l reads code row l32 of each
+      // 32-row block, contraction indices 32 hh .. 32 hh + 31: chunks 2 hh
+      // and 2 hh + 1, stored at chunk (x ^ ((row >> 2) & 3)); the second
+      // is the first's address ^ 16, block mb 2 KB further
+      tr0[0] = (uint32_t)(l32 * 64 + 16 * ((2 * hh) ^ ((l32 >> 2) & 3)));
+      tr0[1] = tr0[0] ^ 16u;
+    }
 
     // Prologue: Q tiles (slots 3-4) and K/V tiles 0-2 copied; Q^T into AGPRs.
-    SKA_CALL(D, F8, SAS, zero_o);
+    SKA_CALL(D, F8, SAS, V8, zero_o);
     for (int t = 0; t < 3; ++t)
       if (t < nkb_wg) issue_tile(t);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if (0 < nkb_w) SKA_CALL(D, F8, SAS, load_q, smem_lds + q_lds + frag);
+    if (0 < nkb_w) SKA_CALL(D, F8, SAS, V8, load_q, smem_lds + q_lds + frag);
     __syncthreads();  // slots 3-4 are K/V slots from here on
 
     // The key loop runs as one generated block (barriers, tile copies, the
     // pipelined steps, votes, rescales, masks). Its scalar operands must be
     // wave-uniform.
     const float lazy_raw = 8.0f / c;  // 8 in log2 units, as a raw-score gap
-    typename LoopArgsOf<D, F8, SAS>::type la;
+    typename LoopArgsOf<D, F8, SAS, V8>::type la;
     la.frag = frag;
     la.tr0 = tr0[0];
     la.tr1 = tr0[1];
@@ -399,10 +431,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
       la.sqv = wave_valid ? qsc[bh * nqb + qb] : 1.f;
       la.nkbm1 = nkb - 1;
       la.wlv = smem_lds + (uint32_t)(T::kBytes + wave * IPW * 1024);
+    } else if constexpr (V8) {
+      la.wlv = smem_lds + (uint32_t)(T::kBytes + wave * IPW * 1024);
     }
     float m[2], mref[2], lsum[2];
-    if constexpr (CAUSAL) SKA_CALL(D, F8, SAS, key_loop_causal, la, m, mref, lsum);
-    else SKA_CALL(D, F8, SAS, key_loop_full, la, m, mref, lsum);
+    if constexpr (CAUSAL) SKA_CALL(D, F8, SAS, V8, key_loop_causal, la, m, mref, lsum);
+    else SKA_CALL(D, F8, SAS, V8, key_loop_full, la, m, mref, lsum);
     (void)m;
 
     // Claim the next item as this one's key loop ends: a claim made earlier
@@ -415,20 +449,21 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
     if (!wave_valid) return;
     drain_mfma();
 
-    // ---- epilogue: O = O^T / l, LSE = m / sqrt(d) + ln l ----
+    // ---- epilogue: O = O^T / l (V8: times the head's V scale), LSE = m / sqrt(d) + ln l ----
+    const float oscale = V8 ? vsc[b * Hkv + g] : 1.f;
   #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const float ltot = swap_halves_sum(lsum[nb]);
-      const float inv = 1.f / ltot;
+      const float inv = oscale / ltot;
       const int row = qb * kTile + nb * 32 + l32;
   #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         float ov[16];
         const int id = 2 * mb + nb;
-        if (id == 0) SKA_CALL(D, F8, SAS, read_o_00, ov);
-        if (id == 1) SKA_CALL(D, F8, SAS, read_o_01, ov);
-        if (id == 2) SKA_CALL(D, F8, SAS, read_o_10, ov);
-        if (id == 3) SKA_CALL(D, F8, SAS, read_o_11, ov);
+        if (id == 0) SKA_CALL(D, F8, SAS, V8, read_o_00, ov);
+        if (id == 1) SKA_CALL(D, F8, SAS, V8, read_o_01, ov);
+        if (id == 2) SKA_CALL(D, F8, SAS, V8, read_o_10, ov);
+        if (id == 3) SKA_CALL(D, F8, SAS, V8, read_o_11, ov);
         if constexpr (MB == 4 && !F8) {
           if (id == 4) d128::read_o_20(ov);
           if (id == 5) d128::read_o_21(ov);
@@ -524,7 +559,7 @@ int queue_and_cus(uint32_t** q, int* ncu) {
 }
 }  // namespace
 
-template <int D, bool CAUSAL, int HPW, bool CHUNK, bool F8, int SAS>
+template <int D, bool CAUSAL, int HPW, bool CHUNK, bool F8, int SAS, bool V8 = false>
 static int launch_one(const PrefillArgs& a) {
   const int nqb = (a.Nq + kTile - 1) / kTile;
   constexpr int QPW = 4 / HPW;
@@ -540,19 +575,20 @@ static int launch_one(const PrefillArgs& a) {
   queue += 16 * (g_next_slot.fetch_add(1, std::memory_order_relaxed) % kQueueSlots);
   // one workgroup per compute unit (the tile slots fill the LDS)
   const int grid = (int)std::min<long long>(items, ncu);
-  hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, HPW, kStages, CHUNK, F8, SAS>), dim3((unsigned)grid),
-                     dim3(256), 0, (hipStream_t)a.stream, (const uint8_t*)a.q, (const uint8_t*)a.k,
-                     (const uint16_t*)a.v, a.o, a.lse, a.mask, a.qscale, a.kscale, a.Hq, a.Hkv,
+  hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, HPW, kStages, CHUNK, F8, SAS, V8>),
+                     dim3((unsigned)grid), dim3(256), 0, (hipStream_t)a.stream,
+                     (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v, a.o, a.lse,
+                     a.mask, a.qscale, a.kscale, a.vscale, a.Hq, a.Hkv,
                      a.Nq, a.N, a.q0t, a.cap, a.tau_raw, a.c, nqg, ny, queue, (int)items);
   return 0;
 }
 
-template <int D, bool CAUSAL, bool CHUNK, bool F8, int SAS>
+template <int D, bool CAUSAL, bool CHUNK, bool F8, int SAS, bool V8 = false>
 static int launch_g(const PrefillArgs& a) {
   const int G = a.Hq / a.Hkv;
-  if (G % 4 == 0) return launch_one<D, CAUSAL, 4, CHUNK, F8, SAS>(a);
-  if (G % 2 == 0) return launch_one<D, CAUSAL, 2, CHUNK, F8, SAS>(a);
-  return launch_one<D, CAUSAL, 1, CHUNK, F8, SAS>(a);
+  if (G % 4 == 0) return launch_one<D, CAUSAL, 4, CHUNK, F8, SAS, V8>(a);
+  if (G % 2 == 0) return launch_one<D, CAUSAL, 2, CHUNK, F8, SAS, V8>(a);
+  return launch_one<D, CAUSAL, 1, CHUNK, F8, SAS, V8>(a);
 }
 
 template <int D, bool CAUSAL, bool F8>
@@ -577,7 +613,22 @@ static int launch_s(const PrefillArgs& a) {
                   : launch_g<64, false, false, false, SAS>(a);
 }
 
+// The 8-bit P.V key loops exist for the whole-sequence prefill (QK^T in bf16
+// or fp8).
+template <bool F8>
+static int launch_v8(const PrefillArgs& a) {
+  if (a.d == 128)
+    return a.causal ? launch_g<128, true, false, F8, 0, true>(a)
+                    : launch_g<128, false, false, F8, 0, true>(a);
+  return a.causal ? launch_g<64, true, false, F8, 0, true>(a)
+                  : launch_g<64, false, false, F8, 0, true>(a);
+}
+
 int launch_prefill(const PrefillArgs& a) {
+  if (a.vscale != nullptr) {
+    if (a.sas != 0 || a.Nq != a.N || a.q0t != 0 || a.cap != a.N) return -3;
+    return a.qscale != nullptr ? launch_v8<true>(a) : launch_v8<false>(a);
+  }
   if (a.sas != 0) {
     if (a.qscale != nullptr || a.Nq != a.N || a.q0t != 0 || a.cap != a.N) return -3;
     return a.sas == 2 ? launch_s<2>(a) : launch_s<3>(a);

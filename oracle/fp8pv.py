@@ -115,11 +115,13 @@ def pv8_blocks(qrows: np.ndarray, k: np.ndarray, vvals: np.ndarray, v_scale: flo
     (in logits). ``round_p`` rounds the probabilities (identity: no rounding).
 
     Returns o (R, d), lse (R,), decisions (nb, nt), margins (nb, nt), slack
-    (R, 2) and amb (nb,) bool. slack[:, 1] bounds how far O may move if
-    probabilities within score_err of an E4M3 rounding midpoint round the
-    other way; slack[:, 0] (LSE) is 0. amb marks blocks where the rescale
-    test came within score_err of its margin (the kernel's reference may
-    then move at another tile).
+    (R, 2) and amb (nb,) bool. slack bounds, to first order, how far LSE
+    (slack[:, 0]) and O (slack[:, 1]) may move when every score is off by up
+    to score_err: the probability-weighted mean of score_err for the LSE;
+    for O that times 2 max |v|, plus the change of probabilities within
+    score_err of an E4M3 rounding midpoint that round the other way. amb
+    marks blocks where the rescale test came within score_err of its margin
+    (the kernel's reference may then move at another tile).
     """
     R, d = qrows.shape
     N = k.shape[0]
@@ -128,6 +130,7 @@ def pv8_blocks(qrows: np.ndarray, k: np.ndarray, vvals: np.ndarray, v_scale: flo
     nblk, nt = dec.shape
     err = np.broadcast_to(np.asarray(score_err, np.float64), s.shape)
     vkey = np.abs(vvals).max(axis=1) if vvals.size else np.zeros(N)
+    vmax = float(vkey.max()) if vkey.size else 0.0
     o = np.empty((R, d))
     lse = np.empty(R)
     slack = np.zeros((R, 2))
@@ -140,6 +143,7 @@ def pv8_blocks(qrows: np.ndarray, k: np.ndarray, vvals: np.ndarray, v_scale: flo
         acc = np.zeros((n, d))
         l = np.zeros(n)
         jo = np.zeros(n)
+        je = np.zeros(n)      # sum of p times the score error
         for tt in range(nt):
             if dec[bi, tt] != KEPT:
                 continue
@@ -158,17 +162,20 @@ def pv8_blocks(qrows: np.ndarray, k: np.ndarray, vvals: np.ndarray, v_scale: flo
                 acc *= alpha[:, None]
                 l *= alpha
                 jo *= alpha
+                je *= alpha
                 mref = np.where(up, m, mref)
             ok = np.isfinite(st) & np.isfinite(mref)[:, None]
             p = np.where(ok, np.exp(np.where(ok, st - mref[:, None], 0.0)), 0.0)
             acc += round_p(p) @ vvals[k0:k1]
             l += p.sum(axis=1)
+            je += (p * et).sum(axis=1)
             # a probability off by a factor exp(+-err) may round to a neighbour
             near = _near_midpoint(p, np.expm1(et))
             jo += (near * _e4m3_spacing(p)) @ vkey[k0:k1]
         o[r0:r1] = v_scale * acc / l[:, None]
         lse[r0:r1] = mref + np.log(l)
-        slack[r0:r1, 1] = v_scale * jo / l
+        slack[r0:r1, 0] = je / l
+        slack[r0:r1, 1] = v_scale * (jo + 2.0 * vmax * je) / l
     return o, lse, dec, margin, slack, amb
 
 

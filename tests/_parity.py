@@ -77,15 +77,24 @@ class PrefillChecker:
     """Caches fp64 copies of K/V per (b, kv head) for repeated block checks."""
 
     def __init__(self, q_bits, k_bits, v_bits, causal: bool, q0: int = 0, qf=None, kf=None,
-                 sas: int = 0):
+                 sas: int = 0, pv8: bool = False, score_err_rel: float = 0.0):
         """q_bits may be a chunk: its row r sits at key position q0 + r
         (q0 a multiple of 64 when causal). ``qf`` / ``kf``, fp64 arrays of
         the same shapes, replace the bf16 Q / K values (e.g. the oracle's
         dequantised 8-bit Q and K). ``sas`` = 2 or 3: the reference is the
         SAS prefill oracle of that degree, and each row's error beyond the
-        slack its SAS steps allow counts against the tolerance."""
+        slack its SAS steps allow counts against the tolerance. ``pv8``: the
+        reference is the 8-bit P.V oracle on the oracle's V codes; a kernel
+        score may differ from the oracle's by up to score_err_rel times the
+        sum of |q_i k_i| / sqrt(d) (plus 2^-17), which sets how close to an
+        E4M3 rounding point a probability must be for either rounding to
+        count as right (the slack), and a block whose rescale test came that
+        close to its margin is counted as ambiguous, its outputs unchecked."""
         self.q, self.k, self.v = q_bits, k_bits, v_bits
         self.sas = sas
+        self.pv8 = pv8
+        self.score_err_rel = score_err_rel
+        self._amb = False
         self.qf, self.kf = qf, kf
         self.causal = causal
         B, Hq, N, d = q_bits.shape
@@ -102,7 +111,11 @@ class PrefillChecker:
             if len(self._kv) > 2:
                 self._kv.clear()
             kk = self.kf[b, g] if self.kf is not None else synth.bf16_bits_to_f64(self.k[b, g])
-            self._kv[key] = (kk, synth.bf16_bits_to_f64(self.v[b, g]))
+            if self.pv8:
+                codes, sv = oracle.fp8pv.quantize_v(synth.bf16_bits_to_f32(self.v[b, g]))
+                self._kv[key] = (kk, (oracle.fp8.e4m3_value(codes), float(sv)))
+            else:
+                self._kv[key] = (kk, synth.bf16_bits_to_f64(self.v[b, g]))
         return self._kv[key]
 
     def qrows(self, b, h, r0, r1):
@@ -112,6 +125,14 @@ class PrefillChecker:
 
     def _ref(self, qrows, k, v, qb, tau, forced=None):
         """o, lse, decisions, margins, slack (rows, 2) or None."""
+        if self.pv8:
+            vvals, sv = v
+            err = (self.score_err_rel * (np.abs(qrows) @ np.abs(k).T) / math.sqrt(k.shape[1])
+                   + 2.0 ** -17)
+            o, lse, dec, margin, slack, amb = oracle.fp8pv.pv8_blocks(
+                qrows, k, vvals, sv, qb + self.q0t, self.causal, tau, forced, score_err=err)
+            self._amb = bool(amb.any())
+            return o, lse, dec, margin, slack
         if self.sas:
             return oracle.sas.prefill_blocks(qrows, k, v, qb + self.q0t, self.causal, tau,
                                              self.sas, forced)
@@ -153,6 +174,10 @@ class PrefillChecker:
             o, lse, _, _, slack = self._ref(qrows, k, v, qb, tau, forced[None, :])
         rep.tiles += int(visited.sum())
         rep.skipped += int((mask_gpu[visited] == 1).sum())
+        if self.pv8 and self._amb:
+            rep.ambiguous += 1
+            rep.notes.append(f"b={b} h={h} qb={qb}: rescale test at its margin, outputs unchecked")
+            return rep
         rep.o_err, rep.lse_err = self._errs(o_gpu, lse_gpu, o, lse, slack)
         return rep
 
@@ -188,11 +213,12 @@ class PrefillChecker:
 
 
 def check_prefill(q_bits, k_bits, v_bits, causal, tau, o, lse, mask, blocks=None,
-                  q0: int = 0, qf=None, kf=None, sas: int = 0) -> Report:
+                  q0: int = 0, qf=None, kf=None, sas: int = 0, pv8: bool = False,
+                  score_err_rel: float = 0.0) -> Report:
     """Compare full GPU outputs (numpy) over the given (b, h, qb) blocks
     (q_bits and the outputs may be a chunk starting at key position q0;
-    qf / kf / sas as for PrefillChecker)."""
-    chk = PrefillChecker(q_bits, k_bits, v_bits, causal, q0, qf, kf, sas)
+    qf / kf / sas / pv8 / score_err_rel as for PrefillChecker)."""
+    chk = PrefillChecker(q_bits, k_bits, v_bits, causal, q0, qf, kf, sas, pv8, score_err_rel)
     if blocks is None:
         blocks = [(b, h, qb) for b in range(chk.B) for h in range(chk.Hq)
                   for qb in range(chk.nt)]

@@ -283,3 +283,19 @@ def test_hybrid_entry_points_reject_before_any_launch():
     assert dc(*base, 4000, 128, 4.0, 0, *tail) == lib.EINVAL      # cap < L
     assert dc(*base, 8192, 128, 4.0, 1, *tail) == lib.EINVAL      # degree 1
     assert "degree" in lib.attn_last_error()
+
+
+def test_prefill_pv8_rejects_before_any_launch():
+    so = lib.load()
+    ws = lib.attn_prefill_pv8_workspace_bytes(1, 8, 2, 1024, 128, True)
+    assert ws > lib.attn_prefill_pv8_workspace_bytes(1, 8, 2, 1024, 128, False) > 0
+    assert lib.attn_prefill_pv8_workspace_bytes(1, 8, 2, 1024, 96, False) == 0
+    call = lambda **kw: so.attn_prefill_pv8(
+        kw.get("q", P), P, P, P, P, 1, 8, 2, 1024, kw.get("d", 128), 1, 4.0, kw.get("qk8", 1),
+        None, kw.get("ws", P), kw.get("wsb", ws), None)
+    assert call(qk8=2) == lib.EINVAL and "qk8" in lib.attn_last_error()
+    assert call(wsb=ws - 1) == lib.EWORKSPACE
+    assert call(ws=None) == lib.EWORKSPACE
+    assert call(ws=P + 8) == lib.EINVAL
+    assert call(q=None) == lib.EINVAL
+    assert call(d=96) == lib.EINVAL
