@@ -63,20 +63,26 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # figure no longer applies and is reported as null.
 MEASURED_TRAFFIC = {
     "prefill": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp", "sas.hpp"),
-                "sha1": "69c12776ebf294d0d281bb272d208b1e7c6523a1",
-                "bytes": (2674125.6 * 2.0 + 528520.1) * 1024},
-    "prefill_qk8": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp", "sas.hpp",
-                                "fp8.hip"),
-                    "sha1": "89669bc9f1e78ed048da48ec453043c1f92ffd38",
-                    "bytes": (1693239.7 * 2.0 + 528520.1) * 1024},
-    "decode_q4": {"sources": ("kvq4.hip", "kvq_common.hpp", "decode.hip", "common.hpp", "sas.hpp",
-                                "lane_max.hpp"),
-                  "sha1": "4daa3e73a88c0e1c574626f9f3c321cd86a65a21",
-                  "bytes": (1148071.4 * 2.0 + 16646.4) * 1024},
-    "decode_q2": {"sources": ("kvq2.hip", "kvq_common.hpp", "decode.hip", "common.hpp", "sas.hpp",
-                                "lane_max.hpp"),
-                  "sha1": "6db8b055d4d30d710f1c74bbd87814e61f04da10",
-                  "bytes": (623807.6 * 2.0 + 16640.6) * 1024},
+                "sha1": "cbc71c8d9f903ea1581f15bfa677027d28070122",
+                "bytes": (2653769.6 * 2.0 + 528520.1) * 1024},
+    "prefill_qk8": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp", "sas.hpp", "fp8.hip"),
+                "sha1": "9165e4e61c19c8e1cd2d53acf44c974873d86382",
+                "bytes": (1699200.9 * 2.0 + 528520.1) * 1024},
+    "prefill_pv8": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp", "sas.hpp", "fp8.hip"),
+                "sha1": "9165e4e61c19c8e1cd2d53acf44c974873d86382",
+                "bytes": (1781203.9 * 2.0 + 528520.1) * 1024},
+    "prefill_qkv8": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp", "sas.hpp", "fp8.hip"),
+                "sha1": "9165e4e61c19c8e1cd2d53acf44c974873d86382",
+                "bytes": (1155616.2 * 2.0 + 528520.1) * 1024},
+    "decode_q4": {"sources": ("kvq4.hip", "kvq_common.hpp", "decode.hip", "common.hpp", "sas.hpp", "lane_max.hpp", "launch.hpp"),
+                "sha1": "919e9978be2785c80bb861343474c3de17bad052",
+                "bytes": (1148107.9 * 2.0 + 16647.0) * 1024},
+    "decode_q2": {"sources": ("kvq2.hip", "kvq_common.hpp", "decode.hip", "common.hpp", "sas.hpp", "lane_max.hpp", "launch.hpp"),
+                "sha1": "2c9227f0ddd985a6799442cc0229e22d8f7a41c0",
+                "bytes": (623803.9 * 2.0 + 16640.3) * 1024},
+    "decode_hybrid": {"sources": ("kvq4.hip", "kvq2.hip", "kvq_common.hpp", "decode.hip", "common.hpp", "sas.hpp", "lane_max.hpp", "launch.hpp"),
+                "sha1": "ff9f0815083a96decd4ecccad30f9dc980349fb0",
+                "bytes": (886088.4 * 2.0 + 16640.5) * 1024},
     "decode": {"sources": ("decode.hip", "common.hpp", "sas.hpp", "lane_max.hpp"),
                "sha1": "333142df1d615caa64770921eb2ebcb71ade361c",
                "bytes": (4195498.3 * 2.0 + 16641.4) * 1024},
@@ -334,7 +340,7 @@ def main():
     ap.add_argument("--reading", default="S", choices=["S", "P"])
     ap.add_argument("--only", default="both",
                     choices=["both", "prefill", "decode", "decode_q4", "decode_q2",
-                             "decode_hybrid", "prefill_qk8"],
+                             "decode_hybrid", "prefill_qk8", "prefill_pv8", "prefill_qkv8"],
                     help="profile one leg only (the JSON line then reports that leg)")
     ap.add_argument("--no-q4", action="store_true",
                     help="skip the 4-bit, 2-bit and hybrid KV-cache decodes measured beside "
@@ -348,7 +354,8 @@ def main():
     ap.add_argument("--tau", type=float, default=math.inf,
                     help="tau of the timed prefill calls (default inf: the step); for counter runs")
     ap.add_argument("--no-qk8", action="store_true",
-                    help="skip the prefill with fp8 QK^T measured beside the step")
+                    help="skip the prefills with 8-bit products (fp8 QK^T, fp8 PV, both) "
+                         "measured beside the step")
     ap.add_argument("--no-other-prefill", action="store_true",
                     help="skip the 8K and 32K causal prefill workloads timed beside the step")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
@@ -405,7 +412,6 @@ def main():
         del src, dst
 
     run_p = args.only in ("both", "prefill")
-    run_qk8 = args.only == "prefill_qk8" or (args.only == "both" and not args.no_qk8)
     run_d = args.only in ("both", "decode")
     # quantised-cache decodes measured beside the step (width in bits)
     widths = [w for w in (4, 2)
@@ -597,6 +603,7 @@ def main():
                                     per_call_bytes=hb, kv_bits=list(hbits),
                                     gbs_bf16_equivalent=round(dense_b / (h_ms * 1e-3) / 1e9, 2),
                                     quantise_ms=round(float(tqh.ms()[0]), 4),
+                                    traffic=measured_traffic("decode_hybrid"),
                                     kernels=f"{hkern} + decode_merge_kernel<128>")
         if args.only == "decode_hybrid":
             out.update(value=round(gbs_h, 2), unit="GB/s", ms_per_step=round(h_ms, 4))
@@ -604,17 +611,43 @@ def main():
                                          "alternating 4 and 2 bits), tau=inf")
             out["roofline"] = dict(bound="hbm", achieved=round(gbs_h, 2), peak=PEAK_HBM_GBS,
                                    unit="GB/s", frac=round(gbs_h / PEAK_HBM_GBS, 4),
-                                   traffic=None, kernel=hkern,
+                                   traffic=measured_traffic("decode_hybrid"), kernel=hkern,
                                    avg_ms=round(h_ms, 4), per_launch_bytes=hb)
 
-    if run_qk8:
-        # The same prefill with block-quantised fp8 QK^T (attn_prefill_qk8):
-        # the quantisers and the prefill kernel, timed per call like the step.
-        qws = torch.empty(lib.attn_prefill_qk8_workspace_bytes(B, Hq, Hkv, N, d),
-                          dtype=torch.uint8, device=dev)
+    # The same prefill with 8-bit operands (the quantisers and the prefill
+    # kernel, timed per call like the step): fp8 QK^T (attn_prefill_qk8), fp8
+    # P.V with bf16 QK^T and with fp8 QK^T (attn_prefill_pv8).
+    lowp = [("prefill_qk8", "fp8 QK^T, bf16 PV", PEAK_QK8_TFLOPS,
+             "prefill_kernel<128,true,4,5,false,true,0,false>",
+             "quant_fp8_kernel<128> x 2 + ",
+             "QK^T on fp8 E4M3 codes (64-row tiles, fp32 scales), PV in bf16; time "
+             "includes quantising Q and K"),
+            ("prefill_pv8", "bf16 QK^T, fp8 PV", PEAK_QK8_TFLOPS,
+             "prefill_kernel<128,true,4,5,false,false,0,true>",
+             "v8_tile_max_kernel<128> + v8_head_scale_kernel + v8_quant_kernel<128> + ",
+             "PV on fp8 E4M3 (V with one scale per KV head, probabilities rounded to E4M3 "
+             "relative to the reference maximum), QK^T in bf16; time includes quantising V"),
+            ("prefill_qkv8", "fp8 QK^T, fp8 PV", PEAK_FP8_TFLOPS,
+             "prefill_kernel<128,true,4,5,false,true,0,true>",
+             "quant_fp8_kernel<128> x 2 + v8 quantisers + ",
+             "both products on fp8 E4M3 (QK^T as prefill_qk8, PV as prefill_pv8); time "
+             "includes quantising Q, K and V")]
+    for leg, dtype8, peak8, kern8, quants8, note8 in lowp:
+        if not (args.only == leg or (args.only == "both" and not args.no_qk8)):
+            continue
+        if leg == "prefill_qk8":
+            qws = torch.empty(lib.attn_prefill_qk8_workspace_bytes(B, Hq, Hkv, N, d),
+                              dtype=torch.uint8, device=dev)
 
-        def prefill8(tau, mask=None):
-            lib.attn_prefill_qk8(tq, tk, tv, po, plse, True, tau, qws, mask)
+            def prefill8(tau, mask=None, qws=qws):
+                lib.attn_prefill_qk8(tq, tk, tv, po, plse, True, tau, qws, mask)
+        else:
+            both = leg == "prefill_qkv8"
+            qws = torch.empty(lib.attn_prefill_pv8_workspace_bytes(B, Hq, Hkv, N, d, both),
+                              dtype=torch.uint8, device=dev)
+
+            def prefill8(tau, mask=None, qws=qws, both=both):
+                lib.attn_prefill_pv8(tq, tk, tv, po, plse, True, tau, qws, both, mask)
 
         warm_up(lambda: prefill8(args.tau), args.warmup)
         t8 = Timer()
@@ -628,7 +661,7 @@ def main():
         if not math.isinf(args.tau):
             prefill8(args.tau, pmask)
             _, vis8, kept8 = prefill_exec_flops(pmask.cpu().numpy(), d)
-            out["tiles_at_tau_qk8"] = dict(tau=args.tau, visited=vis8, kept=kept8)
+            out[f"tiles_at_tau_{leg[8:]}"] = dict(tau=args.tau, visited=vis8, kept=kept8)
         # drift from the exact bf16 prefill on the same inputs
         prefill(math.inf)
         torch.cuda.synchronize()
@@ -654,24 +687,22 @@ def main():
                                   tiles_visited=vis, tiles_kept=kept,
                                   tflops_dense=round(dense_flops / ms / 1e9, 3),
                                   tflops_executed=round(ex / ms / 1e9, 3)))
-        out["prefill_qk8"] = dict(
+        out[leg] = dict(
             value=round(q8_tf, 3), unit="TFLOP/s", ms=round(q8_ms, 4),
             frac_of_bf16_peak=round(q8_tf / PEAK_BF16_TFLOPS, 4),
-            frac_of_mixed_peak=round(q8_tf / PEAK_QK8_TFLOPS, 4),
-            mixed_peak=round(PEAK_QK8_TFLOPS, 1),
+            frac_of_mixed_peak=round(q8_tf / peak8, 4),
+            mixed_peak=round(peak8, 1),
             max_abs_o_drift=drift_o, max_abs_lse_drift=drift_l, tau_sweep=taus8,
-            traffic=measured_traffic("prefill_qk8"),
-            kernels="quant_fp8_kernel<128> x 2 + prefill_kernel<128,true,4,5,false,true>",
-            note="QK^T on fp8 E4M3 codes (64-row tiles, fp32 scales), PV in bf16; time "
-                 "includes quantising Q and K")
-        if args.only == "prefill_qk8":
+            traffic=measured_traffic(leg),
+            kernels=quants8 + kern8, note=note8)
+        if args.only == leg:
             out.update(value=round(q8_tf, 3), unit="TFLOP/s", ms_per_step=round(q8_ms, 4),
-                       dtype="fp8 QK^T, bf16 PV")
-            out["config"]["workload"] = f"{pname} with fp8 QK^T, tau=inf"
-            out["roofline"] = dict(bound="mfma", achieved=round(q8_tf, 3), peak=PEAK_QK8_TFLOPS,
-                                   unit="TFLOP/s", frac=round(q8_tf / PEAK_QK8_TFLOPS, 4),
-                                   traffic=measured_traffic("prefill_qk8"),
-                                   kernel="prefill_kernel<128,true,4,5,false,true> + quantisers",
+                       dtype=dtype8)
+            out["config"]["workload"] = f"{pname} with {dtype8}, tau=inf"
+            out["roofline"] = dict(bound="mfma", achieved=round(q8_tf, 3), peak=peak8,
+                                   unit="TFLOP/s", frac=round(q8_tf / peak8, 4),
+                                   traffic=measured_traffic(leg),
+                                   kernel=kern8 + " + quantisers",
                                    avg_ms=round(q8_ms, 4), per_launch_flops=dense_flops)
         del qws
         torch.cuda.empty_cache()
@@ -836,7 +867,9 @@ def main():
             else None)
         legs = {"both": pre, "prefill": pre, "decode": dec, "decode_q4": dq4, "decode_q2": dq2,
                 "decode_hybrid": dqh}
-        out["cpu_baseline"] = legs[args.only]
+        # the 8-bit prefill legs report the exact prefill oracle's rate (their
+        # oracles are that oracle on quantised operands)
+        out["cpu_baseline"] = legs.get(args.only, pre)
         out["cpu_baseline_decode"] = dec
         out["cpu_baseline_decode_q4"] = dq4
         out["cpu_baseline_decode_q2"] = dq2
