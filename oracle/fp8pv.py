@@ -105,19 +105,23 @@ def _near_midpoint(p: np.ndarray, rel: np.ndarray) -> np.ndarray:
 
 def pv8_blocks(qrows: np.ndarray, k: np.ndarray, vvals: np.ndarray, v_scale: float, qb0: int,
                causal: bool, tau: float, forced: np.ndarray | None = None,
-               score_err: np.ndarray | float = 0.0, round_p=e4m3_round):
+               score_err: np.ndarray | float = 0.0, round_p=e4m3_round,
+               lin_err: np.ndarray | float | None = None):
     """8-bit P.V prefill for consecutive 64-row query blocks of one (batch,
     head).
 
     qrows (R, d) rows qb0*64 ..; k (N, d) fp64 keys; vvals (N, d) the E4M3
     values of V's codes, v_scale their scale. ``score_err`` bounds, per
     score (R, N) or for all, how far a kernel's score may sit from this one
-    (in logits). ``round_p`` rounds the probabilities (identity: no rounding).
+    (in logits); ``lin_err`` (default: score_err) is the error carried to
+    first order into the slack of LSE and O (0 where the kernel's scores are
+    as exact as the tolerances already assume). ``round_p`` rounds the
+    probabilities (identity: no rounding).
 
     Returns o (R, d), lse (R,), decisions (nb, nt), margins (nb, nt), slack
     (R, 2) and amb (nb,) bool. slack bounds, to first order, how far LSE
     (slack[:, 0]) and O (slack[:, 1]) may move when every score is off by up
-    to score_err: the probability-weighted mean of score_err for the LSE;
+    to lin_err: the probability-weighted mean of lin_err for the LSE;
     for O that times 2 max |v|, plus the change of probabilities within
     score_err of an E4M3 rounding midpoint that round the other way. amb
     marks blocks where the rescale test came within score_err of its margin
@@ -129,6 +133,7 @@ def pv8_blocks(qrows: np.ndarray, k: np.ndarray, vvals: np.ndarray, v_scale: flo
     dec, margin = _decide(t, valid, visited, tau, forced)
     nblk, nt = dec.shape
     err = np.broadcast_to(np.asarray(score_err, np.float64), s.shape)
+    lerr = err if lin_err is None else np.broadcast_to(np.asarray(lin_err, np.float64), s.shape)
     vkey = np.abs(vvals).max(axis=1) if vvals.size else np.zeros(N)
     vmax = float(vkey.max()) if vkey.size else 0.0
     o = np.empty((R, d))
@@ -168,7 +173,7 @@ def pv8_blocks(qrows: np.ndarray, k: np.ndarray, vvals: np.ndarray, v_scale: flo
             p = np.where(ok, np.exp(np.where(ok, st - mref[:, None], 0.0)), 0.0)
             acc += round_p(p) @ vvals[k0:k1]
             l += p.sum(axis=1)
-            je += (p * et).sum(axis=1)
+            je += (p * lerr[r0:r1, k0:k1]).sum(axis=1)
             # a probability off by a factor exp(+-err) may round to a neighbour
             near = _near_midpoint(p, np.expm1(et))
             jo += (near * _e4m3_spacing(p)) @ vkey[k0:k1]

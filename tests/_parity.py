@@ -77,7 +77,8 @@ class PrefillChecker:
     """Caches fp64 copies of K/V per (b, kv head) for repeated block checks."""
 
     def __init__(self, q_bits, k_bits, v_bits, causal: bool, q0: int = 0, qf=None, kf=None,
-                 sas: int = 0, pv8: bool = False, score_err_rel: float = 0.0):
+                 sas: int = 0, pv8: bool = False, score_err_rel: float = 0.0,
+                 lin_err: bool = True):
         """q_bits may be a chunk: its row r sits at key position q0 + r
         (q0 a multiple of 64 when causal). ``qf`` / ``kf``, fp64 arrays of
         the same shapes, replace the bf16 Q / K values (e.g. the oracle's
@@ -89,11 +90,15 @@ class PrefillChecker:
         sum of |q_i k_i| / sqrt(d) (plus 2^-17), which sets how close to an
         E4M3 rounding point a probability must be for either rounding to
         count as right (the slack), and a block whose rescale test came that
-        close to its margin is counted as ambiguous, its outputs unchecked."""
+        close to its margin is counted as ambiguous, its outputs unchecked.
+        ``lin_err``: the same error also widens O and LSE to first order
+        (for 8-bit QK^T, whose MFMA sums are inexact; bf16 QK^T scores are as
+        exact as the bf16 prefill's tolerances already assume)."""
         self.q, self.k, self.v = q_bits, k_bits, v_bits
         self.sas = sas
         self.pv8 = pv8
         self.score_err_rel = score_err_rel
+        self.lin_err = lin_err
         self._amb = False
         self.qf, self.kf = qf, kf
         self.causal = causal
@@ -130,7 +135,8 @@ class PrefillChecker:
             err = (self.score_err_rel * (np.abs(qrows) @ np.abs(k).T) / math.sqrt(k.shape[1])
                    + 2.0 ** -17)
             o, lse, dec, margin, slack, amb = oracle.fp8pv.pv8_blocks(
-                qrows, k, vvals, sv, qb + self.q0t, self.causal, tau, forced, score_err=err)
+                qrows, k, vvals, sv, qb + self.q0t, self.causal, tau, forced, score_err=err,
+                lin_err=None if self.lin_err else 0.0)
             self._amb = bool(amb.any())
             return o, lse, dec, margin, slack
         if self.sas:
@@ -214,11 +220,12 @@ class PrefillChecker:
 
 def check_prefill(q_bits, k_bits, v_bits, causal, tau, o, lse, mask, blocks=None,
                   q0: int = 0, qf=None, kf=None, sas: int = 0, pv8: bool = False,
-                  score_err_rel: float = 0.0) -> Report:
+                  score_err_rel: float = 0.0, lin_err: bool = True) -> Report:
     """Compare full GPU outputs (numpy) over the given (b, h, qb) blocks
     (q_bits and the outputs may be a chunk starting at key position q0;
-    qf / kf / sas / pv8 / score_err_rel as for PrefillChecker)."""
-    chk = PrefillChecker(q_bits, k_bits, v_bits, causal, q0, qf, kf, sas, pv8, score_err_rel)
+    qf / kf / sas / pv8 / score_err_rel / lin_err as for PrefillChecker)."""
+    chk = PrefillChecker(q_bits, k_bits, v_bits, causal, q0, qf, kf, sas, pv8, score_err_rel,
+                         lin_err)
     if blocks is None:
         blocks = [(b, h, qb) for b in range(chk.B) for h in range(chk.Hq)
                   for qb in range(chk.nt)]

@@ -240,3 +240,72 @@ def test_prefill_8k_qk8_every_block():
     for tau, rep in total.items():
         print(f"[full] prefill_8k qk8 tau={tau} blocks={B * Hq * nt} {rep}", flush=True)
         assert rep.ok(), str(rep)
+
+
+@pytest.mark.parametrize("qk8", [False, True], ids=["qk_bf16", "qk_fp8"])
+def test_prefill_8k_pv8_every_block(qk8):
+    # the prefill with the P.V product on fp8 (QK^T in bf16, or fp8 too) over
+    # every query block of one query head per KV head of prefill_8k (8 of 32
+    # heads, each KV head's code blocks in use) at every tau, against the
+    # 8-bit P.V oracle on the oracle's codes: probabilities within the score
+    # error of an E4M3 rounding point may round either way; with fp8 QK^T the
+    # MFMA's accumulation error also widens O and LSE to first order
+    import torch
+    import long_context_tiled_amd as lib
+    from oracle import fp8
+    cfg = synth.workload("prefill_8k")
+    print(f"[full] generating prefill_8k (pv8, qk8={qk8})", flush=True)
+    q, k, v = synth.make_prefill(cfg)
+    dq, dk, dv = _dev(q), _dev(k), _dev(v)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    nt = (N + 63) // 64
+    ws = torch.empty(lib.attn_prefill_pv8_workspace_bytes(B, Hq, Hkv, N, d, qk8),
+                     dtype=torch.uint8, device="cuda")
+    out = {}
+    for tau in cfg["taus"]:
+        o, lse, mask, _ = lib.prefill_pv8(dq, dk, dv, True, tau, qk8=qk8, want_mask=True,
+                                          workspace=ws)
+        torch.cuda.synchronize()
+        out[tau] = (o.cpu().numpy(), lse.cpu().numpy(), mask.cpu().numpy())
+        del o, lse, mask
+    parts = {n: t.cpu().numpy()
+             for n, t in lib.pv8_workspace_parts(ws, B, Hq, Hkv, N, d, qk8).items()}
+    del dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    qf = kf = None
+    if qk8:
+        qc, qs = fp8.quantize(synth.bf16_bits_to_f32(q))
+        kc, ks = fp8.quantize(synth.bf16_bits_to_f32(k))
+        assert np.array_equal(parts["qc"], qc) and np.array_equal(parts["kc"], kc)
+        qf, kf = fp8.dequantize(qc, qs), fp8.dequantize(kc, ks)
+
+    def head(bh):
+        b, h = bh
+        chk = _parity.PrefillChecker(q, k, v, True, qf=qf, kf=kf, pv8=True,
+                                     score_err_rel=2.0 ** -11 if qk8 else 2.0 ** -17,
+                                     lin_err=qk8)
+        reps = {}
+        for tau, (o, lse, mask) in out.items():
+            rep = _parity.Report()
+            for qb in range(nt):
+                r0, r1 = qb * 64, min(N, qb * 64 + 64)
+                rep.merge(chk.check_block(b, h, qb, tau, o[b, h, r0:r1], lse[b, h, r0:r1],
+                                          mask[b, h, qb]))
+            reps[tau] = rep
+        return reps
+
+    G = Hq // Hkv
+    heads = [(b, g * G + g % G) for b in range(B) for g in range(Hkv)]
+    total = {tau: _parity.Report() for tau in out}
+    with _one_blas_thread(), ThreadPoolExecutor(_threads()) as ex:
+        for i, reps in enumerate(ex.map(head, heads)):
+            for tau, r in reps.items():
+                total[tau].merge(r)
+            print(f"[full] prefill_8k pv8 qk8={qk8} {i + 1} of {len(heads)} heads checked",
+                  flush=True)
+    for tau, rep in total.items():
+        print(f"[full] prefill_8k pv8 qk8={qk8} tau={tau} blocks={len(heads) * nt} {rep}",
+              flush=True)
+        assert rep.ok(), str(rep)
+        assert rep.ambiguous <= len(heads) * nt // 100, str(rep)
