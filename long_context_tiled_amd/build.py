@@ -20,7 +20,7 @@ OUT = os.path.join(HERE, "libskipattn.so")
 BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "prefill.hip", "decode.hip", "kvq4.hip", "kvq2.hip", "fp8.hip"]
+SOURCES = ["api.hip", "prefill.hip", "decode.hip", "kvq4.hip", "kvq2.hip", "kvq_quant.hip", "fp8.hip"]
 HEADERS = ["common.hpp", "launch.hpp", "kvq_common.hpp", "lane_max.hpp", "sas.hpp",
            "prefill_steps.inc"]
 

@@ -1,5 +1,5 @@
-// 2-bit asymmetric KV cache: the quantiser (bf16 K, V -> stored format) and
-// the split-K decode that reads the stored format directly.
+// 2-bit asymmetric KV cache: the stored format and the split-K decode that
+// reads it directly (the quantisers that write it are in kvq_quant.hip).
 //
 // Method: the TurboAttention talk page ("Technical Deep Dive", the pre-fill /
 // decoding workflow and the trade-offs it lists) stores the KV cache as
@@ -51,109 +51,6 @@ namespace skipattn {
 namespace {
 
 using namespace kvq;
-
-// Sixteen codes (element order) -> one storage word.
-__device__ __forceinline__ uint32_t pack_word2(const uint32_t (&c)[16]) {
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int f = 0; f < 8; ++f) {
-    lo |= c[2 * f] << (2 * f);
-    hi |= c[2 * f + 1] << (2 * f);
-  }
-  return lo | (hi << 16);
-}
-
-// ---------------------------------------------------------------- quantiser
-// K: W = D/16 lanes per key row, each lane one word (16 elements: 32 bytes of
-// bf16 in by two 16-byte loads, 4 bytes of codes out); the row's minimum and
-// maximum by xor shuffles. Rows are the keys k0 .. k1 - 1 of every (b, g).
-template <int D>
-__global__ __launch_bounds__(256) void quant_k2_kernel(const uint16_t* __restrict__ k,
-                                                       uint8_t* __restrict__ kq,
-                                                       uint32_t* __restrict__ kp,
-                                                       long long rows, int L, int k0, int nk,
-    const KvHeadMap hm) {
-  constexpr int W = D / 16;
-  const int lane = threadIdx.x & 63;
-  const long long idx = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / W) + lane / W;
-  const int w = lane % W;
-  const bool ok = idx < rows;
-  const long long row = ok ? (idx / nk) * L + k0 + idx % nk : 0;  // key row in the cache
-  const long long src_row = ok ? full_slice(idx / nk, hm) * L + k0 + idx % nk : 0;
-  float x[16];
-  if (ok) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(k + src_row * D + 16 * w);
-    const u32x4 r0 = src[0], r1 = src[1];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = bf16_to_f32(r0[i] & 0xffffu);
-      x[2 * i + 1] = bf16_to_f32(r0[i] >> 16);
-      x[8 + 2 * i] = bf16_to_f32(r1[i] & 0xffffu);
-      x[8 + 2 * i + 1] = bf16_to_f32(r1[i] >> 16);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = 0.f;
-  }
-  float lo = x[0], hi = x[0];
-#pragma unroll
-  for (int i = 1; i < 16; ++i) {
-    lo = fminf(lo, x[i]);
-    hi = fmaxf(hi, x[i]);
-  }
-#pragma unroll
-  for (int off = 1; off < W; off <<= 1) {
-    lo = fminf(lo, __shfl_xor(lo, off));
-    hi = fmaxf(hi, __shfl_xor(hi, off));
-  }
-  if (!ok) return;
-  const float s = block_scale<3>(lo, hi);
-  uint32_t c[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) c[i] = code_of<3>(x[i], s, lo);
-  reinterpret_cast<uint32_t*>(kq + row * (D / 4))[w] = pack_word2(c);
-  if (w == 0) kp[row] = pack_params(s, lo);
-}
-
-// V: one thread per channel of one 64-key tile (block = one (b, g, tile));
-// the tile's 64 values of the channel in registers, its 16-byte code row out
-// as one store. Tiles t0 .. t0 + nt - 1; a tile holds its keys below k1.
-template <int D>
-__global__ __launch_bounds__(D) void quant_v2_kernel(const uint16_t* __restrict__ v,
-                                                     uint8_t* __restrict__ vq,
-                                                     uint32_t* __restrict__ vp, int L, int T,
-                                                     int t0, int nt, int k1,
-    const KvHeadMap hm) {
-  const int ch = threadIdx.x;
-  const long long bg = blockIdx.x / nt;
-  const int t = t0 + blockIdx.x % nt;
-  const int n = min(kTile, k1 - kTile * t);
-  const uint16_t* src = v + (full_slice(bg, hm) * L + (long long)kTile * t) * D + ch;
-  float x[kTile];
-#pragma unroll
-  for (int j = 0; j < kTile; ++j) x[j] = j < n ? bf16_to_f32(src[(long long)j * D]) : x[0];
-  float lo = x[0], hi = x[0];
-#pragma unroll
-  for (int j = 1; j < kTile; ++j) {
-    lo = fminf(lo, x[j]);
-    hi = fmaxf(hi, x[j]);
-  }
-  const float s = block_scale<3>(lo, hi);
-  const long long blk = (bg * T + t) * D + ch;
-  u32x4 out;
-#pragma unroll
-  for (int wd = 0; wd < 4; ++wd) {
-    uint32_t c[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int j = 16 * wd + e;
-      c[e] = j < n ? code_of<3>(x[j], s, lo) : 0u;
-    }
-    out[wd] = pack_word2(c);
-  }
-  *reinterpret_cast<u32x4*>(vq + blk * 16) = out;
-  vp[blk] = pack_params(s, lo);
-}
 
 // ------------------------------------------------------------ decode kernel
 // The constants of the code expansions, in registers so that each
@@ -868,25 +765,6 @@ __global__ __launch_bounds__(256, 2) void decode_q2_pair_kernel(
 }
 
 template <int D>
-int launch_q2_d(const QuantArgs& a) {
-  constexpr int RPW = 64 / (D / 16);  // key rows per wave
-  const int nk = a.k1 - a.k0;
-  const long long rows = (long long)a.B * a.Hkv * nk;
-  const long long waves = (rows + RPW - 1) / RPW;
-  const long long g1 = (waves + 3) / 4;
-  const int T = (a.L + kTile - 1) / kTile;
-  const int t0 = a.k0 / kTile;
-  const int nt = (a.k1 + kTile - 1) / kTile - t0;
-  const long long g2 = (long long)a.B * a.Hkv * nt;
-  if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return -1;
-  hipLaunchKernelGGL((quant_k2_kernel<D>), dim3((unsigned)g1), dim3(256), 0, (hipStream_t)a.stream,
-                     (const uint16_t*)a.k, a.kq, a.kp, rows, a.L, a.k0, nk, a.map);
-  hipLaunchKernelGGL((quant_v2_kernel<D>), dim3((unsigned)g2), dim3(D), 0, (hipStream_t)a.stream,
-                     (const uint16_t*)a.v, a.vq, a.vp, a.L, T, t0, nt, a.k1, a.map);
-  return 0;
-}
-
-template <int D>
 int launch_dq2_d(const DecodeQ4Args& a) {
   const int G = a.Hq / a.Hkv;
   if (G <= 8) {
@@ -917,10 +795,6 @@ int launch_dq2_d(const DecodeQ4Args& a) {
 }
 
 }  // namespace
-
-int launch_kv_quantize_q2(const QuantArgs& a) {
-  return a.d == 128 ? launch_q2_d<128>(a) : launch_q2_d<64>(a);
-}
 
 int launch_decode_q2(const DecodeQ4Args& a) {
   return a.d == 128 ? launch_dq2_d<128>(a) : launch_dq2_d<64>(a);

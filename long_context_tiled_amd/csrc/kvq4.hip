@@ -1,5 +1,5 @@
-// 4-bit asymmetric KV cache: the quantiser (bf16 K, V -> stored format) and
-// the split-K decode that reads the stored format directly.
+// 4-bit asymmetric KV cache: the stored format and the split-K decode that
+// reads it directly (the quantisers that write it are in kvq_quant.hip).
 //
 // Method: the TurboAttention talk page ("Technical Deep Dive" and the
 // pre-fill / decoding workflow) stores and moves the KV cache as low-bit
@@ -60,106 +60,6 @@ namespace skipattn {
 namespace {
 
 using namespace kvq;
-
-// Eight codes (element order) -> one storage word.
-__device__ __forceinline__ uint32_t pack_word(const uint32_t (&c)[8]) {
-  const uint32_t lo = c[0] | (c[2] << 4) | (c[4] << 8) | (c[6] << 12);
-  const uint32_t hi = c[1] | (c[3] << 4) | (c[5] << 8) | (c[7] << 12);
-  return lo | (hi << 16);
-}
-
-// ---------------------------------------------------------------- quantiser
-// K: W = D/8 lanes per key row, each lane one word (8 elements, 16 bytes of
-// bf16 in, 4 bytes of codes out); the row's min and max by xor shuffles.
-// Rows are the keys k0 .. k1 - 1 of every (b, g) of a cache holding L keys.
-template <int D>
-__global__ __launch_bounds__(256) void quant_k_kernel(const uint16_t* __restrict__ k,
-                                                      uint8_t* __restrict__ kq,
-                                                      uint32_t* __restrict__ kp,
-                                                      long long rows, int L, int k0, int nk,
-    const KvHeadMap hm) {
-  constexpr int W = D / 8;
-  const int lane = threadIdx.x & 63;
-  const long long idx = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / W) + lane / W;
-  const int w = lane % W;
-  const bool ok = idx < rows;
-  const long long row = ok ? (idx / nk) * L + k0 + idx % nk : 0;  // key row in the cache
-  const long long src_row = ok ? full_slice(idx / nk, hm) * L + k0 + idx % nk : 0;
-  float x[8];
-  if (ok) {
-    const u32x4 r = *reinterpret_cast<const u32x4*>(k + src_row * D + 8 * w);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = bf16_to_f32(r[i] & 0xffffu);
-      x[2 * i + 1] = bf16_to_f32(r[i] >> 16);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = 0.f;
-  }
-  float lo = x[0], hi = x[0];
-#pragma unroll
-  for (int i = 1; i < 8; ++i) {
-    lo = fminf(lo, x[i]);
-    hi = fmaxf(hi, x[i]);
-  }
-#pragma unroll
-  for (int off = 1; off < W; off <<= 1) {
-    lo = fminf(lo, __shfl_xor(lo, off));
-    hi = fmaxf(hi, __shfl_xor(hi, off));
-  }
-  if (!ok) return;
-  const float s = block_scale<15>(lo, hi);
-  uint32_t c[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = code_of<15>(x[i], s, lo);
-  reinterpret_cast<uint32_t*>(kq + row * (D / 2))[w] = pack_word(c);
-  if (w == 0) kp[row] = pack_params(s, lo);
-}
-
-// V: one thread per channel of one 64-key tile (block = one (b, g, tile)).
-// One pass: the tile's 64 values of the channel stay in registers (loads of
-// one key row are coalesced across the block's threads), and the channel's
-// 32-byte code row goes out as two 16-byte stores. Tiles t0 .. t0 + nt - 1
-// of a cache of T tiles; a tile holds its keys below k1.
-template <int D>
-__global__ __launch_bounds__(D) void quant_v_kernel(const uint16_t* __restrict__ v,
-                                                    uint8_t* __restrict__ vq,
-                                                    uint32_t* __restrict__ vp, int L, int T,
-                                                    int t0, int nt, int k1,
-    const KvHeadMap hm) {
-  const int ch = threadIdx.x;
-  const long long bg = blockIdx.x / nt;
-  const int t = t0 + blockIdx.x % nt;
-  const int n = min(kTile, k1 - kTile * t);
-  const uint16_t* src = v + (full_slice(bg, hm) * L + (long long)kTile * t) * D + ch;
-  float x[kTile];
-#pragma unroll
-  for (int j = 0; j < kTile; ++j) x[j] = j < n ? bf16_to_f32(src[(long long)j * D]) : x[0];
-  float lo = x[0], hi = x[0];
-#pragma unroll
-  for (int j = 1; j < kTile; ++j) {
-    lo = fminf(lo, x[j]);
-    hi = fmaxf(hi, x[j]);
-  }
-  const float s = block_scale<15>(lo, hi);
-  const long long blk = (bg * T + t) * D + ch;
-  u32x4 out[2];
-#pragma unroll
-  for (int wd = 0; wd < 8; ++wd) {
-    uint32_t c[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = 8 * wd + e;
-      c[e] = j < n ? code_of<15>(x[j], s, lo) : 0u;
-    }
-    out[wd >> 2][wd & 3] = pack_word(c);
-  }
-  u32x4* dst = reinterpret_cast<u32x4*>(vq + blk * 32);
-  dst[0] = out[0];
-  dst[1] = out[1];
-  vp[blk] = pack_params(s, lo);
-}
 
 // ------------------------------------------------------------ decode kernel
 
@@ -540,24 +440,6 @@ __global__ __launch_bounds__(256, 2) void decode_q4_split_kernel(
 }
 
 template <int D>
-int launch_q_d(const QuantArgs& a) {
-  const int nk = a.k1 - a.k0;
-  const long long rows = (long long)a.B * a.Hkv * nk;
-  const long long waves = (rows + (64 / (D / 8)) - 1) / (64 / (D / 8));
-  const long long g1 = (waves + 3) / 4;
-  const int T = (a.L + kTile - 1) / kTile;
-  const int t0 = a.k0 / kTile;
-  const int nt = (a.k1 + kTile - 1) / kTile - t0;
-  const long long g2 = (long long)a.B * a.Hkv * nt;
-  if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return -1;
-  hipLaunchKernelGGL((quant_k_kernel<D>), dim3((unsigned)g1), dim3(256), 0, (hipStream_t)a.stream,
-                     (const uint16_t*)a.k, a.kq, a.kp, rows, a.L, a.k0, nk, a.map);
-  hipLaunchKernelGGL((quant_v_kernel<D>), dim3((unsigned)g2), dim3(D), 0, (hipStream_t)a.stream,
-                     (const uint16_t*)a.v, a.vq, a.vp, a.L, T, t0, nt, a.k1, a.map);
-  return 0;
-}
-
-template <int D>
 int launch_dq_d(const DecodeQ4Args& a) {
   // one wave per (sequence, KV head, slice of up to 16 query heads, split)
   const int nhs = (a.Hq / a.Hkv + 15) / 16;
@@ -574,10 +456,6 @@ int launch_dq_d(const DecodeQ4Args& a) {
 }
 
 }  // namespace
-
-int launch_kv_quantize_q4(const QuantArgs& a) {
-  return a.d == 128 ? launch_q_d<128>(a) : launch_q_d<64>(a);
-}
 
 int launch_decode_q4(const DecodeQ4Args& a) {
   return a.d == 128 ? launch_dq_d<128>(a) : launch_dq_d<64>(a);
