@@ -30,9 +30,12 @@ relative to the exact prefill, drift from it, tau sweep), the 8K and 32K
 causal prefill workloads are timed alone
 (``prefill_8k``, ``prefill_32k``: TFLOP/s, fraction of the bf16 peak, their
 tau sweeps), and the same decode workload is run over the 4-bit asymmetric
-KV cache (attn_kv_quantize_q4 once, then attn_decode_q4 timed like the bf16
+KV cache (attn_kv_quantize_q4, then attn_decode_q4 timed like the bf16
 decode): ``decode_q4`` reports GB/s of the 4-bit bytes read, its fraction of
-HBM peak and the bf16-equivalent rate.
+HBM peak and the bf16-equivalent rate, and the quantiser's time per call
+rewriting the cache (``quantise_ms``, ``quantise_gbs`` of bf16 K and V read
+plus cache bytes written; ``quantise_first_ms`` for the first call, which
+also allocates the cache); likewise ``decode_q2`` and ``decode_hybrid``.
 """
 from __future__ import annotations
 
@@ -199,6 +202,23 @@ def warm_up(fn, n):
         if i % 4 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
+
+
+def time_quantiser(fn, cache_tensors, k, v, steps, warmup):
+    """A KV-cache quantiser rewriting a cache it has already written: ms per
+    call (HIP events, after warm-up) and GB/s of bytes it must move (bf16 K
+    and V read once, every cache byte written once)."""
+    import torch
+    warm_up(fn, warmup)
+    t = Timer()
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        with t:
+            fn()
+    torch.cuda.synchronize()
+    ms = float(np.mean(t.ms()))
+    moved = (k.numel() + v.numel()) * 2 + sum(x.numel() * x.element_size() for x in cache_tensors)
+    return ms, moved / (ms * 1e-3) / 1e9
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -520,8 +540,9 @@ def main():
     qkern = {4: "decode_q4_split_kernel<128>", 2: "decode_q2_pair_kernel<128>"}
     qdecode = {}
     for w in widths:
-        # The same decode workload over a w-bit KV cache: quantised once
-        # (timed on its own), then attn_decode_q{w} timed like the bf16 decode.
+        # The same decode workload over a w-bit KV cache: quantised (the first
+        # call timed on its own, then rewrites of the cache timed warm), then
+        # attn_decode_q{w} timed like the bf16 decode.
         quantize = getattr(lib, f"quantize_q{w}")
         tq0 = Timer()
         with tq0:
@@ -534,6 +555,9 @@ def main():
             entry(uq, cache, L, do, dlse, tau, ws, mask)
 
         qdecode[w] = decode_q
+        requant = getattr(lib, f"attn_kv_quantize_q{w}")
+        qz_ms, qz_gbs = time_quantiser(lambda: requant(uk, uv, cache), list(cache.values()), uk, uv,
+                                       args.steps, args.warmup)
         warm_up(lambda: decode_q(math.inf), args.warmup)
         tqw = Timer()
         torch.cuda.synchronize()
@@ -559,7 +583,8 @@ def main():
                         frac_of_hbm=round(gbs_q / PEAK_HBM_GBS, 4), per_call_bytes=qb,
                         gbs_bf16_equivalent=round(dense_b / (q_ms * 1e-3) / 1e9, 2),
                         traffic=measured_traffic(leg),
-                        quantise_ms=round(float(tq0.ms()[0]), 4),
+                        quantise_ms=round(qz_ms, 4), quantise_gbs=round(qz_gbs, 1),
+                        quantise_first_ms=round(float(tq0.ms()[0]), 4),
                         sas2_ms=round(sas_ms, 4),
                         kernels=f"{qkern[w]} + decode_merge_kernel<128>")
         if args.only == leg:
@@ -576,7 +601,8 @@ def main():
     if run_hy:
         # The same decode workload over a hybrid cache, its KV heads
         # alternating 4 bits (even heads) and 2 bits (odd heads): quantised
-        # once (timed on its own), then attn_decode_hybrid timed like the rest.
+        # (first call and warm rewrites timed), then attn_decode_hybrid timed
+        # like the rest.
         hbits = tuple(4 if g % 2 == 0 else 2 for g in range(DHkv))
         tqh = Timer()
         with tqh:
@@ -587,6 +613,9 @@ def main():
         def hdecode(tau, mask=None):
             lib.attn_decode_hybrid(uq, hcache, L, do, dlse, tau, ws, mask)
 
+        htensors = [x for w in ("q4", "q2") if hcache[w] is not None for x in hcache[w].values()]
+        hqz_ms, hqz_gbs = time_quantiser(lambda: lib.attn_kv_quantize_hybrid(uk, uv, hcache),
+                                         htensors, uk, uv, args.steps, args.warmup)
         warm_up(lambda: hdecode(math.inf), args.warmup)
         th = Timer()
         torch.cuda.synchronize()
@@ -602,7 +631,8 @@ def main():
                                     frac_of_hbm=round(gbs_h / PEAK_HBM_GBS, 4),
                                     per_call_bytes=hb, kv_bits=list(hbits),
                                     gbs_bf16_equivalent=round(dense_b / (h_ms * 1e-3) / 1e9, 2),
-                                    quantise_ms=round(float(tqh.ms()[0]), 4),
+                                    quantise_ms=round(hqz_ms, 4), quantise_gbs=round(hqz_gbs, 1),
+                                    quantise_first_ms=round(float(tqh.ms()[0]), 4),
                                     traffic=measured_traffic("decode_hybrid"),
                                     kernels=f"{hkern} + decode_merge_kernel<128>")
         if args.only == "decode_hybrid":
