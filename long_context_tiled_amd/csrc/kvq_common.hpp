@@ -18,12 +18,10 @@ constexpr int kNT = 2;                     // non-temporal cache policy
 constexpr int kRT = 0;                     // default cache policy
 
 // Head numbering of a cache that holds some of the KV heads (a hybrid
-// cache's heads of one width): (b, head) slice bg = b * n + i of the cache
-// comes from slice b * n_in + g[i] of the full set, and its query heads are
-// rows of the full set's query heads.
-__device__ __forceinline__ long long full_slice(long long bg, const KvHeadMap& hm) {
-  return hm.n ? (bg / hm.n) * hm.n_in + hm.g[bg % hm.n] : bg;
-}
+// cache's heads of one width): (b, head) slice b * n + i of the cache comes
+// from slice b * n_in + g[i] of the full set (the quantisers' src_slice),
+// and its query heads are rows of the full set's query heads: KV head i of
+// the cache is head full_head(i) of the full set.
 __device__ __forceinline__ int full_head(int g, const KvHeadMap& hm) {
   return hm.n ? hm.g[g] : g;
 }
