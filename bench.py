@@ -24,7 +24,9 @@ Hkv=8) causal prefill shape in the 128K one's place; the default line is the
 Beside the step, the same prefill with block-quantised fp8 QK^T
 (``prefill_qk8``: time including the quantisers, TFLOP/s dense-equivalent,
 fraction of the bf16 peak and of the fp8/bf16 mixed peak, drift from the
-exact prefill, tau sweep), the same prefill with the SAS exponential of degree
+exact prefill, tau sweep), likewise with fp8 P.V (``prefill_pv8``), both
+products on fp8 (``prefill_qkv8``) and int8 QK^T (``prefill_qki8``), the same
+prefill with the SAS exponential of degree
 2 and 3 (``prefill_sas2``, ``prefill_sas3``: TFLOP/s dense-equivalent, time
 relative to the exact prefill, drift from it, tau sweep), the 8K and 32K
 causal prefill workloads are timed alone
@@ -54,7 +56,7 @@ if ROOT not in sys.path:
 
 METRIC = "prefill attn TFLOP/s (dense-equiv) & decode KV GB/s at 128K ctx, per τ"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
-PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA (int8: 5000 TOP/s, the same rate)
 # the fp8-QK^T prefill does half its dense flops (QK^T) at the fp8 rate and
 # half (PV) at the bf16 rate: its MFMA ceiling is the harmonic mix
 PEAK_QK8_TFLOPS = 2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_BF16_TFLOPS)
@@ -360,7 +362,8 @@ def main():
     ap.add_argument("--reading", default="S", choices=["S", "P"])
     ap.add_argument("--only", default="both",
                     choices=["both", "prefill", "decode", "decode_q4", "decode_q2",
-                             "decode_hybrid", "prefill_qk8", "prefill_pv8", "prefill_qkv8"],
+                             "decode_hybrid", "prefill_qk8", "prefill_pv8", "prefill_qkv8",
+                             "prefill_qki8"],
                     help="profile one leg only (the JSON line then reports that leg)")
     ap.add_argument("--no-q4", action="store_true",
                     help="skip the 4-bit, 2-bit and hybrid KV-cache decodes measured beside "
@@ -374,8 +377,8 @@ def main():
     ap.add_argument("--tau", type=float, default=math.inf,
                     help="tau of the timed prefill calls (default inf: the step); for counter runs")
     ap.add_argument("--no-qk8", action="store_true",
-                    help="skip the prefills with 8-bit products (fp8 QK^T, fp8 PV, both) "
-                         "measured beside the step")
+                    help="skip the prefills with 8-bit products (fp8 QK^T, fp8 PV, both; "
+                         "int8 QK^T) measured beside the step")
     ap.add_argument("--no-other-prefill", action="store_true",
                     help="skip the 8K and 32K causal prefill workloads timed beside the step")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
@@ -646,31 +649,37 @@ def main():
 
     # The same prefill with 8-bit operands (the quantisers and the prefill
     # kernel, timed per call like the step): fp8 QK^T (attn_prefill_qk8), fp8
-    # P.V with bf16 QK^T and with fp8 QK^T (attn_prefill_pv8).
+    # P.V with bf16 QK^T and with fp8 QK^T (attn_prefill_pv8), int8 QK^T
+    # (attn_prefill_qki8; int8 MFMAs run at the fp8 rate).
     lowp = [("prefill_qk8", "fp8 QK^T, bf16 PV", PEAK_QK8_TFLOPS,
-             "prefill_kernel<128,true,4,5,false,true,0,false>",
+             "prefill_kernel<128,true,4,5,false,true,0,false,false>",
              "quant_fp8_kernel<128> x 2 + ",
              "QK^T on fp8 E4M3 codes (64-row tiles, fp32 scales), PV in bf16; time "
              "includes quantising Q and K"),
             ("prefill_pv8", "bf16 QK^T, fp8 PV", PEAK_QK8_TFLOPS,
-             "prefill_kernel<128,true,4,5,false,false,0,true>",
+             "prefill_kernel<128,true,4,5,false,false,0,true,false>",
              "v8_tile_max_kernel<128> + v8_head_scale_kernel + v8_quant_kernel<128> + ",
              "PV on fp8 E4M3 (V with one scale per KV head, probabilities rounded to E4M3 "
              "relative to the reference maximum), QK^T in bf16; time includes quantising V"),
             ("prefill_qkv8", "fp8 QK^T, fp8 PV", PEAK_FP8_TFLOPS,
-             "prefill_kernel<128,true,4,5,false,true,0,true>",
+             "prefill_kernel<128,true,4,5,false,true,0,true,false>",
              "quant_fp8_kernel<128> x 2 + v8 quantisers + ",
              "both products on fp8 E4M3 (QK^T as prefill_qk8, PV as prefill_pv8); time "
-             "includes quantising Q, K and V")]
+             "includes quantising Q, K and V"),
+            ("prefill_qki8", "int8 QK^T, bf16 PV", PEAK_QK8_TFLOPS,
+             "prefill_kernel<128,true,4,5,false,true,0,false,true>",
+             "quant_i8_kernel<128> x 2 + ",
+             "QK^T on symmetric int8 codes (64-row tiles, fp32 scales; exact int32 "
+             "products), PV in bf16; time includes quantising Q and K")]
     for leg, dtype8, peak8, kern8, quants8, note8 in lowp:
         if not (args.only == leg or (args.only == "both" and not args.no_qk8)):
             continue
-        if leg == "prefill_qk8":
+        if leg in ("prefill_qk8", "prefill_qki8"):
             qws = torch.empty(lib.attn_prefill_qk8_workspace_bytes(B, Hq, Hkv, N, d),
                               dtype=torch.uint8, device=dev)
 
-            def prefill8(tau, mask=None, qws=qws):
-                lib.attn_prefill_qk8(tq, tk, tv, po, plse, True, tau, qws, mask)
+            def prefill8(tau, mask=None, qws=qws, i8=leg == "prefill_qki8"):
+                lib.attn_prefill_qk8(tq, tk, tv, po, plse, True, tau, qws, mask, int8=i8)
         else:
             both = leg == "prefill_qkv8"
             qws = torch.empty(lib.attn_prefill_pv8_workspace_bytes(B, Hq, Hkv, N, d, both),
@@ -770,7 +779,7 @@ def main():
                 value=round(dense_flops / (s_ms * 1e-3) / 1e12, 3), unit="TFLOP/s",
                 ms=round(s_ms, 4), vs_exact=round(p_ms / s_ms, 4),
                 max_abs_o_drift=drift_o, max_abs_lse_drift=drift_l, tau_sweep=sweep,
-                kernel=f"prefill_kernel<128,true,4,5,false,false,{deg}>")
+                kernel=f"prefill_kernel<128,true,4,5,false,false,{deg},false,false>")
         del o_ex, l_ex
 
     if run_p and args.only == "both" and not args.no_other_prefill:

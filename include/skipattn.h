@@ -183,6 +183,24 @@ int attn_prefill_qk8(const void* q, const void* k, const void* v, float* o,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_prefill_qki8 - attn_prefill_qk8 with symmetric int8 operands, the
+ * pages' own 8-bit format for the QK^T product (TurboAttention talk page,
+ * "Technical Deep Dive": symmetric int8 quantisation block-wise inside the
+ * flash blocks). Q and K are quantised per 64-row tile: scale s = (largest
+ * |x| in the tile) / 127 in fp32 (1 for a tile of zeros), code =
+ * clamp(rint(x / s), -127, 127) (fp32 division, rint ties to even), and
+ * S = Q K^T runs on the int8 matrix cores, exact in int32, before the tile's
+ * scales apply. The scores are those of q^ = code * s_q, k^ = code * s_k.
+ * Arguments, outputs and errors as for attn_prefill_qk8, whole sequences
+ * only; the workspace is attn_prefill_qk8_workspace_bytes() bytes with the
+ * same parts, the codes as two's complement int8 bytes.
+ */
+int attn_prefill_qki8(const void* q, const void* k, const void* v, float* o,
+                      float* lse, int B, int Hq, int Hkv, int N, int d,
+                      int causal, float tau, uint8_t* skip_mask,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * attn_prefill_pv8 - attn_prefill with the P.V product on 8-bit operands too
  * (TurboAttention talk page, "Technical Deep Dive" and "Key Findings": both
  * products of blockwise attention on block-quantised 8-bit operands), QK^T

@@ -30,7 +30,7 @@ EXPORTS = ("attn_prefill", "attn_decode", "attn_decode_workspace_bytes",
            "attn_decode_q4_cap", "attn_decode_q2_cap", "attn_decode_noalloc",
            "attn_prefill_qk8", "attn_prefill_qk8_workspace_bytes", "attn_kv_quantize_hybrid",
            "attn_kv_quantize_hybrid_range", "attn_decode_hybrid", "attn_decode_hybrid_cap",
-           "attn_prefill_pv8", "attn_prefill_pv8_workspace_bytes")
+           "attn_prefill_pv8", "attn_prefill_pv8_workspace_bytes", "attn_prefill_qki8")
 
 _lib = None
 
@@ -75,6 +75,8 @@ def load() -> ctypes.CDLL:
     lib.attn_prefill_qk8.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, i, f, u8p, vp, sz,
                                      vp]
     lib.attn_prefill_qk8.restype = i
+    lib.attn_prefill_qki8.argtypes = lib.attn_prefill_qk8.argtypes
+    lib.attn_prefill_qki8.restype = i
     lib.attn_prefill_pv8.argtypes = [vp, vp, vp, f32p, f32p, i, i, i, i, i, i, f, i, u8p, vp, sz,
                                      vp]
     lib.attn_prefill_pv8.restype = i
@@ -254,10 +256,11 @@ def qk8_workspace_parts(workspace, B: int, Hq: int, Hkv: int, N: int, d: int) ->
 
 
 def attn_prefill_qk8(q, k, v, o, lse, causal: bool, tau: float, workspace, skip_mask=None,
-                     stream=None) -> None:
-    """attn_prefill with QK^T on block-quantised fp8 (E4M3) Q and K; the
-    workspace (attn_prefill_qk8_workspace_bytes) receives the codes and
-    scales (qk8_workspace_parts)."""
+                     stream=None, int8: bool = False) -> None:
+    """attn_prefill with QK^T on block-quantised fp8 (E4M3) Q and K, or
+    (``int8``, attn_prefill_qki8) symmetric int8 ones; the workspace
+    (attn_prefill_qk8_workspace_bytes) receives the codes and scales
+    (qk8_workspace_parts)."""
     import torch
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
@@ -272,9 +275,9 @@ def attn_prefill_qk8(q, k, v, o, lse, causal: bool, tau: float, workspace, skip_
     if workspace.device.type != "cuda" or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
     nbytes = workspace.numel() * workspace.element_size()
-    rc = load().attn_prefill_qk8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N,
-                                 d, int(bool(causal)), float(tau), _ptr(skip_mask),
-                                 _ptr(workspace), nbytes, _stream(stream))
+    fn = load().attn_prefill_qki8 if int8 else load().attn_prefill_qk8
+    rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d, int(bool(causal)),
+            float(tau), _ptr(skip_mask), _ptr(workspace), nbytes, _stream(stream))
     _raise(rc)
 
 
@@ -690,9 +693,10 @@ def prefill(q, k, v, causal: bool, tau: float = math.inf, want_mask: bool = Fals
 
 
 def prefill_qk8(q, k, v, causal: bool, tau: float = math.inf, want_mask: bool = False,
-                workspace=None, stream=None):
+                workspace=None, stream=None, int8: bool = False):
     """Allocate outputs (and the workspace if not given) and call
-    attn_prefill_qk8. Returns (o, lse, mask, workspace)."""
+    attn_prefill_qk8 (``int8``: attn_prefill_qki8). Returns (o, lse, mask,
+    workspace)."""
     import torch
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
@@ -705,7 +709,7 @@ def prefill_qk8(q, k, v, causal: bool, tau: float = math.inf, want_mask: bool = 
     if workspace is None:
         nbytes = max(256, attn_prefill_qk8_workspace_bytes(B, Hq, Hkv, N, d))
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    attn_prefill_qk8(q, k, v, o, lse, causal, tau, workspace, mask, stream)
+    attn_prefill_qk8(q, k, v, o, lse, causal, tau, workspace, mask, stream, int8=int8)
     return o, lse, mask, workspace
 
 

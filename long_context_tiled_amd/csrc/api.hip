@@ -395,6 +395,39 @@ int hybrid_decode(const void* q, const uint8_t* kv_bits, const uint8_t* kq4,
   return SKIPATTN_OK;
 }
 
+// The 8-bit QK^T prefills: Q and K quantised into the workspace (fp8 E4M3,
+// or symmetric int8), then the prefill on their codes.
+int prefill_qk8_impl(const void* q, const void* k, const void* v, float* o, float* lse, int B,
+                     int Hq, int Hkv, int N, int d, int causal, float tau, uint8_t* skip_mask,
+                     void* workspace, size_t workspace_bytes, void* stream, bool i8) {
+  const char* name = i8 ? "prefill_qki8" : "prefill_qk8";
+  if (int e = prefill_check(q, k, v, o, lse, B, Hq, Hkv, N, N, N, d, causal, tau, skip_mask))
+    return e;
+  if (B == 0 || N == 0) return SKIPATTN_OK;
+  const Qk8Layout l = qk8_layout(B, Hq, Hkv, N, d);
+  if (workspace == nullptr || workspace_bytes < l.total)
+    return fail(SKIPATTN_EWORKSPACE, "%s workspace needs %zu bytes (got %zu)", name, l.total,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (!aligned16(workspace)) return fail(SKIPATTN_EINVAL, "workspace must be 16-byte aligned");
+  char* ws = (char*)workspace;
+  uint8_t* qc = (uint8_t*)(ws + l.qc);
+  uint8_t* kc = (uint8_t*)(ws + l.kc);
+  float* qs = (float*)(ws + l.qs);
+  float* ks = (float*)(ws + l.ks);
+  auto quant = i8 ? skipattn::launch_quantize_i8 : skipattn::launch_quantize_fp8;
+  if (quant(q, qc, qs, (long long)B * Hq, N, d, stream) != 0 ||
+      quant(k, kc, ks, (long long)B * Hkv, N, d, stream) != 0)
+    return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
+  skipattn::PrefillArgs a{qc, kc, v, o, lse, skip_mask, B, Hq, Hkv, N, d, causal,
+                          N,  0,  N, tau_raw(tau, d), exp2_scale(d), stream, qs, ks};
+  a.qk_int8 = i8;
+  const int lr = skipattn::launch_prefill(a);
+  if (lr == -1) return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
+  if (lr != 0) return fail(SKIPATTN_EHIP, "%s: device query for the work queue failed", name);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(SKIPATTN_EHIP, "%s launch: %s", name, hipGetErrorString(err));
+  return SKIPATTN_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -484,30 +517,15 @@ size_t attn_prefill_qk8_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
 int attn_prefill_qk8(const void* q, const void* k, const void* v, float* o, float* lse, int B,
                      int Hq, int Hkv, int N, int d, int causal, float tau, uint8_t* skip_mask,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  if (int e = prefill_check(q, k, v, o, lse, B, Hq, Hkv, N, N, N, d, causal, tau, skip_mask))
-    return e;
-  if (B == 0 || N == 0) return SKIPATTN_OK;
-  const Qk8Layout l = qk8_layout(B, Hq, Hkv, N, d);
-  if (workspace == nullptr || workspace_bytes < l.total)
-    return fail(SKIPATTN_EWORKSPACE, "prefill_qk8 workspace needs %zu bytes (got %zu)", l.total,
-                workspace == nullptr ? (size_t)0 : workspace_bytes);
-  if (!aligned16(workspace)) return fail(SKIPATTN_EINVAL, "workspace must be 16-byte aligned");
-  char* ws = (char*)workspace;
-  uint8_t* qc = (uint8_t*)(ws + l.qc);
-  uint8_t* kc = (uint8_t*)(ws + l.kc);
-  float* qs = (float*)(ws + l.qs);
-  float* ks = (float*)(ws + l.ks);
-  if (skipattn::launch_quantize_fp8(q, qc, qs, (long long)B * Hq, N, d, stream) != 0 ||
-      skipattn::launch_quantize_fp8(k, kc, ks, (long long)B * Hkv, N, d, stream) != 0)
-    return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
-  skipattn::PrefillArgs a{qc, kc, v, o, lse, skip_mask, B, Hq, Hkv, N, d, causal,
-                          N,  0,  N, tau_raw(tau, d), exp2_scale(d), stream, qs, ks};
-  const int lr = skipattn::launch_prefill(a);
-  if (lr == -1) return fail(SKIPATTN_EUNSUPPORTED, "grid too large");
-  if (lr != 0) return fail(SKIPATTN_EHIP, "prefill_qk8: device query for the work queue failed");
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return fail(SKIPATTN_EHIP, "prefill_qk8 launch: %s", hipGetErrorString(err));
-  return SKIPATTN_OK;
+  return prefill_qk8_impl(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, tau, skip_mask, workspace,
+                          workspace_bytes, stream, false);
+}
+
+int attn_prefill_qki8(const void* q, const void* k, const void* v, float* o, float* lse, int B,
+                      int Hq, int Hkv, int N, int d, int causal, float tau, uint8_t* skip_mask,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_qk8_impl(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, tau, skip_mask, workspace,
+                          workspace_bytes, stream, true);
 }
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int L, int d) {

@@ -1,9 +1,10 @@
-// Block-quantised fp8 (E4M3) codes of Q and K for the 8-bit QK^T prefill.
+// Block-quantised 8-bit codes of Q and K for the 8-bit QK^T prefills (fp8
+// E4M3, or symmetric int8), and the V codes of the 8-bit P.V prefill.
 //
 // Method: the TurboAttention talk page ("Technical Deep Dive", "Key
 // Findings"; its pre-fill workflow) runs the products of blockwise attention
 // on symmetric 8-bit operands quantised block by block inside the flash
-// blocks. gfx950's 8-bit matrix cores take fp8; the block is a 64-row tile
+// blocks. gfx950's 8-bit matrix cores take fp8 and int8; the block is a 64-row tile
 // (a query tile of Q, a key tile of K), the decision tile of the skip rule.
 //
 // Per block: m = largest |x| over its rows (rows past N take no part);
@@ -12,6 +13,11 @@
 // value with ties to the even mantissa; a value that rounds to zero is
 // code 0. Codes [X, N, D] uint8 (row-major like the input), scales
 // [X, ceil(N/64)] fp32.
+//
+// The int8 reading (the pages name symmetric int8 for these operands):
+// scale s = m / 127, code = clamp(rint(x / s), -127, 127) (fp32 division,
+// rint ties to even; -128 unused), stored as two's complement bytes, for the
+// int8 matrix cores.
 //
 // One workgroup of 256 threads per block: thread t owns row t / 4 of the
 // block and D / 4 consecutive elements of it (16-byte loads and stores).
@@ -47,13 +53,16 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {
   return mag == 0u ? 0u : (mag | ((__builtin_bit_cast(uint32_t, y) >> 24) & 0x80u));
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restrict__ x,
-                                                        uint8_t* __restrict__ codes,
-                                                        float* __restrict__ scales, int N,
-                                                        int nt) {
+// One 64-row block per workgroup. I8 = false: E4M3 codes, scale m / 448;
+// I8 = true: symmetric int8 codes clamp(rint(x / s), -127, 127) (two's
+// complement bytes), scale m / 127; both with the division in fp32.
+template <int D, bool I8>
+__device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x,
+                                            uint8_t* __restrict__ codes,
+                                            float* __restrict__ scales, int N, int nt) {
   constexpr int E = D / 4;  // elements per thread
   static_assert(E % 16 == 0, "16-byte pieces");
+  constexpr float kMax = I8 ? 127.f : 448.f;
   __shared__ float wmax[4];
   const int blk = blockIdx.x;
   const long long xi = blk / nt;  // which (batch, head)
@@ -83,7 +92,7 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
   if ((tid & 63) == 0) wmax[tid >> 6] = m;
   __syncthreads();
   m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  const float sc = m > 0.f ? m / 448.f : 1.f;
+  const float sc = m > 0.f ? m / kMax : 1.f;
   if (tid == 0) scales[(size_t)xi * nt + t] = sc;
   if (!ok) return;
   uint8_t* dst = codes + ((size_t)xi * N + row) * D + (tid & 3) * E;
@@ -95,13 +104,34 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
       uint32_t word = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float y = fminf(fmaxf(v[16 * p + 4 * i + j] / sc, -448.f), 448.f);
-        word |= e4m3_code(y) << (8 * j);
+        const float y = v[16 * p + 4 * i + j] / sc;
+        uint32_t code;
+        if constexpr (I8)
+          code = (uint32_t)(int)fminf(fmaxf(__builtin_rintf(y), -kMax), kMax) & 0xffu;
+        else
+          code = e4m3_code(fminf(fmaxf(y, -kMax), kMax));
+        word |= code << (8 * j);
       }
       w[i] = word;
     }
     *reinterpret_cast<u32x4*>(dst + 16 * p) = w;
   }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restrict__ x,
+                                                        uint8_t* __restrict__ codes,
+                                                        float* __restrict__ scales, int N,
+                                                        int nt) {
+  quant_block<D, false>(x, codes, scales, N, nt);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restrict__ x,
+                                                       uint8_t* __restrict__ codes,
+                                                       float* __restrict__ scales, int N,
+                                                       int nt) {
+  quant_block<D, true>(x, codes, scales, N, nt);
 }
 
 // ---- V for the 8-bit P.V product: one scale per (sequence, KV head) ----
@@ -243,6 +273,21 @@ int launch_quantize_v8(const void* v, uint8_t* codes, float* tmax, float* vscale
     hipLaunchKernelGGL((v8_quant_kernel<64>), dim3((unsigned)blocks), dim3(256), 0, st, x,
                        vscale, codes, N, nt);
   }
+  return 0;
+}
+
+int launch_quantize_i8(const void* x, uint8_t* codes, float* scales, long long X, int N, int D,
+                       void* stream) {
+  const int nt = (N + kTile - 1) / kTile;
+  const long long blocks = X * nt;
+  if (blocks <= 0) return 0;
+  if (blocks > 0x7fffffffLL) return -1;
+  if (D == 128)
+    hipLaunchKernelGGL((quant_i8_kernel<128>), dim3((unsigned)blocks), dim3(256), 0,
+                       (hipStream_t)stream, (const uint16_t*)x, codes, scales, N, nt);
+  else
+    hipLaunchKernelGGL((quant_i8_kernel<64>), dim3((unsigned)blocks), dim3(256), 0,
+                       (hipStream_t)stream, (const uint16_t*)x, codes, scales, N, nt);
   return 0;
 }
 

@@ -122,8 +122,13 @@ class Step:
     """One step variant for one head dim and buffer assignment."""
 
     def __init__(self, d, variant, x, y, budget, loop=False, dma=False, f8=False, sas=0,
-                 v8=False):
+                 v8=False, i8=False):
         self.loop = loop
+        # QK^T on int8 codes: the fp8 operand layout (one byte per element),
+        # each 32x32x64 fp8 MFMA replaced by two 32x32x32 int8 MFMAs over the
+        # two 16-byte halves of the operands, int32 scores converted in place
+        # before the row maxima
+        self.i8 = i8
         self.v8 = v8          # P.V on fp8: one 32x32x64 MFMA per (d block, query half)
         self.sas = sas        # 0: exp2; 2 or 3: the SAS exponential of that degree
         self.dma = dma
@@ -295,6 +300,23 @@ class Step:
                                Ins(f"buffer_load_dwordx4 {tmp}, {rs}, 0 offen lds", "vmem")])
         return groups
 
+    def qk_mfmas(self, ks, a, nb, j):
+        """The QK^T MFMAs of one (k-step, key half, query half): one, or two
+        for int8 (contraction halves: operand registers 0-3, then 4-7; the
+        A and B halves hold the same d positions, so the sum is the same)."""
+        if not self.i8:
+            return [self.qk_mfma(ks, a, nb, j)]
+        s = self.s_blk(self.y, a, nb)
+        kb, qb = KREG + 8 * (j ^ 2), self.QB + 16 * ks + 8 * nb
+        out = []
+        for h in range(2):
+            kf, qf = rng("v", kb + 4 * h, 4), rng("a", qb + 4 * h, 4)
+            first = ks == 0 and h == 0
+            src_c = "0" if first else s
+            out.append(Ins(f"v_mfma_i32_32x32x32_i8 {s}, {kf}, {qf}, {src_c}", "mfma", wr=[s],
+                           rd=[kf, qf] + ([] if first else [s])))
+        return out
+
     def qk_mfma(self, ks, a, nb, j):
         s = self.s_blk(self.y, a, nb)
         kf = self.kfrag(j, 0)
@@ -457,7 +479,8 @@ class Step:
         return out
 
     def max_stream(self):
-        """Row maxima of the new tile: query half nb over both key halves."""
+        """Row maxima of the new tile: query half nb over both key halves
+        (int8 QK^T: each score pair converted from int32 in place first)."""
         out = []
         first = {0: True, 1: True}
         for a in range(2):
@@ -465,6 +488,9 @@ class Step:
                 for i in range(8):
                     r0 = self.s_reg(self.y, a, nb, 2 * i)
                     s0, s1 = f"v{r0}", f"v{r0 + 1}"
+                    if self.i8:
+                        out += [Ins(f"v_cvt_f32_i32 {x}, {x}", "valu", wr=[x], rd=[x],
+                                    tag=("blk", a)) for x in (s0, s1)]
                     tm = f"%[tm{nb}]"
                     if first[nb]:
                         out.append(Ins(f"v_max_f32 {tm}, {s0}, {s1}", "valu", rd=[s0, s1], tag=("blk", a)))
@@ -583,7 +609,8 @@ class Step:
             for n, (a, ks) in enumerate(order):
                 j = n & 3
                 for nb in range(2):
-                    mfma(self.qk_mfma(ks, a, nb, j))
+                    for ins in self.qk_mfmas(ks, a, nb, j):
+                        mfma(ins)
                     if nb == 0 and n + 2 < len(order):
                         seq += self.k_load(*order[n + 2], (n + 2) & 3)
                     # V^T fragments of PV k-step 0: bf16, once the K fragments
@@ -928,9 +955,9 @@ def _rename(lines, mapping):
 QA = {"A": "%[qa0]", "B": "%[qa1]"}   # fp8: q scale x k scale of the tile in buffer A / B
 
 
-def _step_lines(d, variant, x, y, budget, dma=True, f8=False, sas=0, v8=False):
+def _step_lines(d, variant, x, y, budget, dma=True, f8=False, sas=0, v8=False, i8=False):
     st = Step(d, variant, x, y, budget, loop=True, dma=dma, f8=f8, sas=sas,
-              v8=v8).build().fix_hazards()
+              v8=v8, i8=i8).build().fix_hazards()
     return _rename(st.out, {"%[mi0]": "%[m0]", "%[mi1]": "%[m1]", "%[mo0]": "%[m0]",
                             "%[mo1]": "%[m1]", "%[lo0]": "%[ls0]", "%[lo1]": "%[ls1]",
                             "%[qa]": QA[y]})
@@ -1050,7 +1077,7 @@ LOOP_ARGS_F8_FIELDS = """
   uint32_t wlv;"""
 
 
-def loop_cxx(d, causal, budget, f8=False, sas=0, v8=False):
+def loop_cxx(d, causal, budget, f8=False, sas=0, v8=False, i8=False):
     MB = d // 32
     row_bytes = 2 * d                        # V rows (bf16)
     krow = d if f8 else 2 * d                # K rows: fp8 codes or bf16
@@ -1165,7 +1192,7 @@ def loop_cxx(d, causal, budget, f8=False, sas=0, v8=False):
     L += ["s_cmp_gt_i32 %[nkbw], 0", f"s_cbranch_scc0 {lab('loop')}"]
     L += ["s_mov_b32 %[t0], %[smem]", "v_add_u32 %[kb0], %[t0], %[frag]"]
     L += rare("0")
-    L += _step_lines(d, "qk", "A", "A", budget, dma=False, f8=f8, v8=v8)
+    L += _step_lines(d, "qk", "A", "A", budget, dma=False, f8=f8, v8=v8, i8=i8)
     L += after_vote("0", "A", "p0")
     L += [f"{lab('loop')}:"]
     for x, y in (("A", "B"), ("B", "A")):
@@ -1186,9 +1213,9 @@ def loop_cxx(d, causal, budget, f8=False, sas=0, v8=False):
               "s_cmp_lg_u64 %[grow], 0", f"s_cbranch_scc0 {lab('nr' + t)}"]
         L += _rescale_lines(d, sas)
         L += [f"{lab('nr' + t)}:"] + nmc(x) + vaddr()
-        L += _step_lines(d, "full", x, y, budget, f8=f8, sas=sas, v8=v8)
+        L += _step_lines(d, "full", x, y, budget, f8=f8, sas=sas, v8=v8, i8=i8)
         L += [f"s_branch {lab('voted' + t)}", f"{lab('skip' + t)}:"]
-        L += _step_lines(d, "qk", y, y, budget, f8=f8, v8=v8)
+        L += _step_lines(d, "qk", y, y, budget, f8=f8, v8=v8, i8=i8)
         L += [f"{lab('voted' + t)}:", "s_add_u32 %[t1], %[kb], 1"]
         L += after_vote("%[t1]", y, t)
         L += [f"s_branch {lab('end' + t)}",
@@ -1249,7 +1276,7 @@ def loop_cxx(d, causal, budget, f8=False, sas=0, v8=False):
     # %[mpp] is the 64-bit pair (mp, mp_hi): spelled out below
     text = "\n".join(f'      "{t}\\n\\t"' for t in body)
     head = (f"// The key loop of one wave, d = {d}, {'causal' if causal else 'full'} attention"
-            f"{', QK^T on fp8 codes' if f8 else ''}"
+            f"{(', QK^T on int8 codes' if i8 else ', QK^T on fp8 codes') if f8 else ''}"
             f"{', P.V on fp8 codes' if v8 else ''}"
             f"{f', SAS exponential of degree {sas}' if sas else ''} ({len(body)} lines)")
     name = f"key_loop_{'causal' if causal else 'full'}"
@@ -1275,13 +1302,16 @@ def main(out_path=None):
              "// Per-key-tile steps of the prefill kernel (see the script's docstring for",
              "// the schedule, the register plan and the hazard rules).",
              "#pragma once", ""]
-    for d, budget, f8, sas, v8 in ((128, 26.0, False, 0, False), (64, 30.0, False, 0, False),
-                                   (128, 26.0, True, 0, False), (64, 30.0, True, 0, False),
-                                   (128, 26.0, False, 2, False), (128, 26.0, False, 3, False),
-                                   (64, 30.0, False, 2, False), (64, 30.0, False, 3, False),
-                                   (128, 26.0, False, 0, True), (64, 30.0, False, 0, True),
-                                   (128, 26.0, True, 0, True), (64, 30.0, True, 0, True)):
-        ns = (f"d{d}" + ("f8" if f8 else "") + ("v8" if v8 else "")) if not sas else f"d{d}s{sas}"
+    for d, budget, f8, sas, v8, i8 in (
+            (128, 26.0, False, 0, False, False), (64, 30.0, False, 0, False, False),
+            (128, 26.0, True, 0, False, False), (64, 30.0, True, 0, False, False),
+            (128, 26.0, False, 2, False, False), (128, 26.0, False, 3, False, False),
+            (64, 30.0, False, 2, False, False), (64, 30.0, False, 3, False, False),
+            (128, 26.0, False, 0, True, False), (64, 30.0, False, 0, True, False),
+            (128, 26.0, True, 0, True, False), (64, 30.0, True, 0, True, False),
+            (128, 26.0, True, 0, False, True), (64, 30.0, True, 0, False, True)):
+        ns = ((f"d{d}" + ("i8" if i8 else "f8" if f8 else "") + ("v8" if v8 else ""))
+              if not sas else f"d{d}s{sas}")
         parts.append(f"namespace {ns} {{")
         for h in helpers_cxx(d, f8):
             parts.append(h)
@@ -1298,7 +1328,7 @@ def main(out_path=None):
                                           LOOP_ARGS_SAS_FIELDS if sas else (
                                               LOOP_ARGS_V8_FIELDS if v8 else ""))))
         for causal in (True, False):
-            parts.append(loop_cxx(d, causal, budget, f8, sas, v8))
+            parts.append(loop_cxx(d, causal, budget, f8, sas, v8, i8))
             parts.append("")
         parts.append(f"}}  // namespace {ns}")
         parts.append("")

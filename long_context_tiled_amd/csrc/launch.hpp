@@ -32,6 +32,9 @@ struct PrefillArgs {
   // [B, Hkv, ceil(N/64), d, 64] (launch_quantize_v8) and vscale [B, Hkv]
   // their scales; null for bf16 V
   const float* vscale = nullptr;
+  // int8 QK^T (whole-sequence prefill only, P.V in bf16): q and k hold
+  // symmetric int8 codes with the fp8 path's tile scales (launch_quantize_i8)
+  bool qk_int8 = false;
 };
 
 struct DecodeArgs {
@@ -117,6 +120,9 @@ int launch_decode_q2(const DecodeQ4Args& a);
 // (fp8.hip). Returns nonzero if the grid cannot be expressed.
 int launch_quantize_fp8(const void* x, uint8_t* codes, float* scales, long long X, int N, int D,
                         void* stream);
+// The same blocks as symmetric int8 codes (scale m / 127; fp8.hip).
+int launch_quantize_i8(const void* x, uint8_t* codes, float* scales, long long X, int N, int D,
+                       void* stream);
 // V codes for the 8-bit P.V prefill (fp8.hip): bf16 V [X, N, D] -> E4M3
 // codes in the kernel's tile blocks [X, ceil(N/64), D, 64] with one fp32
 // scale per head, vscale [X]; tmax [X, ceil(N/64)] is scratch.

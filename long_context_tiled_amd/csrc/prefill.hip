@@ -161,10 +161,13 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, lds_void* lds, 
 #pragma clang diagnostic pop
 
 // Calls the d = 128 or d = 64 version of a generated block (bf16 QK^T, or
-// fp8 QK^T when F8_ is set; P.V on fp8 codes when V8_ is set).
-#define SKA_CALL(D_, F8_, SAS_, V8_, fn, ...)                                    \
+// fp8 QK^T when F8_ is set, int8 when I8_ is set too; P.V on fp8 codes when
+// V8_ is set).
+#define SKA_CALL(D_, F8_, SAS_, V8_, I8_, fn, ...)                               \
   do {                                                                           \
-    if constexpr ((V8_) && (D_) == 128 && (F8_)) d128f8v8::fn(__VA_ARGS__);      \
+    if constexpr ((I8_) && (D_) == 128) d128i8::fn(__VA_ARGS__);                 \
+    else if constexpr (I8_) d64i8::fn(__VA_ARGS__);                              \
+    else if constexpr ((V8_) && (D_) == 128 && (F8_)) d128f8v8::fn(__VA_ARGS__); \
     else if constexpr ((V8_) && (D_) == 128) d128v8::fn(__VA_ARGS__);            \
     else if constexpr ((V8_) && (F8_)) d64f8v8::fn(__VA_ARGS__);                 \
     else if constexpr (V8_) d64v8::fn(__VA_ARGS__);                              \
@@ -178,21 +181,27 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, lds_void* lds, 
     else d64f8::fn(__VA_ARGS__);                                                \
   } while (0)
 
-template <int D, bool F8, int SAS, bool V8>
+template <int D, bool F8, int SAS, bool V8, bool I8>
 struct LoopArgsOf;
-template <> struct LoopArgsOf<128, false, 0, false> { using type = d128::LoopArgs; };
-template <> struct LoopArgsOf<64, false, 0, false> { using type = d64::LoopArgs; };
-template <> struct LoopArgsOf<128, true, 0, false> { using type = d128f8::LoopArgs; };
-template <> struct LoopArgsOf<64, true, 0, false> { using type = d64f8::LoopArgs; };
-template <> struct LoopArgsOf<128, false, 2, false> { using type = d128s2::LoopArgs; };
-template <> struct LoopArgsOf<64, false, 2, false> { using type = d64s2::LoopArgs; };
-template <> struct LoopArgsOf<128, false, 3, false> { using type = d128s3::LoopArgs; };
-template <> struct LoopArgsOf<64, false, 3, false> { using type = d64s3::LoopArgs; };
-template <> struct LoopArgsOf<128, false, 0, true> { using type = d128v8::LoopArgs; };
-template <> struct LoopArgsOf<64, false, 0, true> { using type = d64v8::LoopArgs; };
-template <> struct LoopArgsOf<128, true, 0, true> { using type = d128f8v8::LoopArgs; };
-template <> struct LoopArgsOf<64, true, 0, true> { using type = d64f8v8::LoopArgs; };
+template <> struct LoopArgsOf<128, false, 0, false, false> { using type = d128::LoopArgs; };
+template <> struct LoopArgsOf<64, false, 0, false, false> { using type = d64::LoopArgs; };
+template <> struct LoopArgsOf<128, true, 0, false, false> { using type = d128f8::LoopArgs; };
+template <> struct LoopArgsOf<64, true, 0, false, false> { using type = d64f8::LoopArgs; };
+template <> struct LoopArgsOf<128, false, 2, false, false> { using type = d128s2::LoopArgs; };
+template <> struct LoopArgsOf<64, false, 2, false, false> { using type = d64s2::LoopArgs; };
+template <> struct LoopArgsOf<128, false, 3, false, false> { using type = d128s3::LoopArgs; };
+template <> struct LoopArgsOf<64, false, 3, false, false> { using type = d64s3::LoopArgs; };
+template <> struct LoopArgsOf<128, false, 0, true, false> { using type = d128v8::LoopArgs; };
+template <> struct LoopArgsOf<64, false, 0, true, false> { using type = d64v8::LoopArgs; };
+template <> struct LoopArgsOf<128, true, 0, true, false> { using type = d128f8v8::LoopArgs; };
+template <> struct LoopArgsOf<64, true, 0, true, false> { using type = d64f8v8::LoopArgs; };
+template <> struct LoopArgsOf<128, true, 0, false, true> { using type = d128i8::LoopArgs; };
+template <> struct LoopArgsOf<64, true, 0, false, true> { using type = d64i8::LoopArgs; };
 
+// I8 (with F8, whole-sequence only): Q and K are symmetric int8 codes with
+// the same tile scales; S^T runs on v_mfma_i32_32x32x32_i8 (two per fp8
+// MFMA: the contraction halves of the same operand registers), exact in
+// int32, and the scores are converted to fp32 before their row maxima.
 // F8: Q and K are fp8 (E4M3) codes with one fp32 scale per 64-row Q tile
 // (qsc, [B, Hq, ceil(Nq/64)]) and per 64-key K tile (ksc, [B, Hkv,
 // ceil(cap/64)]); S^T = K . Q^T runs on v_mfma_f32_32x32x64_f8f6f4 in code
@@ -210,7 +219,8 @@ template <> struct LoopArgsOf<64, true, 0, true> { using type = d64f8v8::LoopArg
 // reference maximum they stay below 2^8, inside E4M3's range, so they take
 // no scale. The row sums stay over the unrounded probabilities, and the
 // head's V scale multiplies O with 1 / l.
-template <int D, bool CAUSAL, int HPW, int STAGES, bool CHUNK, bool F8, int SAS, bool V8>
+template <int D, bool CAUSAL, int HPW, int STAGES, bool CHUNK, bool F8, int SAS, bool V8,
+          bool I8>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void prefill_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
     const uint8_t* __restrict__ v, float* __restrict__ o,
@@ -368,19 +378,19 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
     }
 
     // Prologue: Q tiles (slots 3-4) and K/V tiles 0-2 copied; Q^T into AGPRs.
-    SKA_CALL(D, F8, SAS, V8, zero_o);
+    SKA_CALL(D, F8, SAS, V8, I8, zero_o);
     for (int t = 0; t < 3; ++t)
       if (t < nkb_wg) issue_tile(t);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if (0 < nkb_w) SKA_CALL(D, F8, SAS, V8, load_q, smem_lds + q_lds + frag);
+    if (0 < nkb_w) SKA_CALL(D, F8, SAS, V8, I8, load_q, smem_lds + q_lds + frag);
     __syncthreads();  // slots 3-4 are K/V slots from here on
 
     // The key loop runs as one generated block (barriers, tile copies, the
     // pipelined steps, votes, rescales, masks). Its scalar operands must be
     // wave-uniform.
     const float lazy_raw = 8.0f / c;  // 8 in log2 units, as a raw-score gap
-    typename LoopArgsOf<D, F8, SAS, V8>::type la;
+    typename LoopArgsOf<D, F8, SAS, V8, I8>::type la;
     la.frag = frag;
     la.tr0 = tr0[0];
     la.tr1 = tr0[1];
@@ -435,8 +445,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
       la.wlv = smem_lds + (uint32_t)(T::kBytes + wave * IPW * 1024);
     }
     float m[2], mref[2], lsum[2];
-    if constexpr (CAUSAL) SKA_CALL(D, F8, SAS, V8, key_loop_causal, la, m, mref, lsum);
-    else SKA_CALL(D, F8, SAS, V8, key_loop_full, la, m, mref, lsum);
+    if constexpr (CAUSAL) SKA_CALL(D, F8, SAS, V8, I8, key_loop_causal, la, m, mref, lsum);
+    else SKA_CALL(D, F8, SAS, V8, I8, key_loop_full, la, m, mref, lsum);
     (void)m;
 
     // Claim the next item as this one's key loop ends: a claim made earlier
@@ -460,15 +470,20 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
       for (int mb = 0; mb < MB; ++mb) {
         float ov[16];
         const int id = 2 * mb + nb;
-        if (id == 0) SKA_CALL(D, F8, SAS, V8, read_o_00, ov);
-        if (id == 1) SKA_CALL(D, F8, SAS, V8, read_o_01, ov);
-        if (id == 2) SKA_CALL(D, F8, SAS, V8, read_o_10, ov);
-        if (id == 3) SKA_CALL(D, F8, SAS, V8, read_o_11, ov);
+        if (id == 0) SKA_CALL(D, F8, SAS, V8, I8, read_o_00, ov);
+        if (id == 1) SKA_CALL(D, F8, SAS, V8, I8, read_o_01, ov);
+        if (id == 2) SKA_CALL(D, F8, SAS, V8, I8, read_o_10, ov);
+        if (id == 3) SKA_CALL(D, F8, SAS, V8, I8, read_o_11, ov);
         if constexpr (MB == 4 && !F8) {
           if (id == 4) d128::read_o_20(ov);
           if (id == 5) d128::read_o_21(ov);
           if (id == 6) d128::read_o_30(ov);
           if (id == 7) d128::read_o_31(ov);
+        } else if constexpr (MB == 4 && I8) {
+          if (id == 4) d128i8::read_o_20(ov);
+          if (id == 5) d128i8::read_o_21(ov);
+          if (id == 6) d128i8::read_o_30(ov);
+          if (id == 7) d128i8::read_o_31(ov);
         } else if constexpr (MB == 4) {
           if (id == 4) d128f8::read_o_20(ov);
           if (id == 5) d128f8::read_o_21(ov);
@@ -559,7 +574,8 @@ int queue_and_cus(uint32_t** q, int* ncu) {
 }
 }  // namespace
 
-template <int D, bool CAUSAL, int HPW, bool CHUNK, bool F8, int SAS, bool V8 = false>
+template <int D, bool CAUSAL, int HPW, bool CHUNK, bool F8, int SAS, bool V8 = false,
+          bool I8 = false>
 static int launch_one(const PrefillArgs& a) {
   const int nqb = (a.Nq + kTile - 1) / kTile;
   constexpr int QPW = 4 / HPW;
@@ -575,7 +591,7 @@ static int launch_one(const PrefillArgs& a) {
   queue += 16 * (g_next_slot.fetch_add(1, std::memory_order_relaxed) % kQueueSlots);
   // one workgroup per compute unit (the tile slots fill the LDS)
   const int grid = (int)std::min<long long>(items, ncu);
-  hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, HPW, kStages, CHUNK, F8, SAS, V8>),
+  hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, HPW, kStages, CHUNK, F8, SAS, V8, I8>),
                      dim3((unsigned)grid), dim3(256), 0, (hipStream_t)a.stream,
                      (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v, a.o, a.lse,
                      a.mask, a.qscale, a.kscale, a.vscale, a.Hq, a.Hkv,
@@ -583,12 +599,12 @@ static int launch_one(const PrefillArgs& a) {
   return 0;
 }
 
-template <int D, bool CAUSAL, bool CHUNK, bool F8, int SAS, bool V8 = false>
+template <int D, bool CAUSAL, bool CHUNK, bool F8, int SAS, bool V8 = false, bool I8 = false>
 static int launch_g(const PrefillArgs& a) {
   const int G = a.Hq / a.Hkv;
-  if (G % 4 == 0) return launch_one<D, CAUSAL, 4, CHUNK, F8, SAS, V8>(a);
-  if (G % 2 == 0) return launch_one<D, CAUSAL, 2, CHUNK, F8, SAS, V8>(a);
-  return launch_one<D, CAUSAL, 1, CHUNK, F8, SAS, V8>(a);
+  if (G % 4 == 0) return launch_one<D, CAUSAL, 4, CHUNK, F8, SAS, V8, I8>(a);
+  if (G % 2 == 0) return launch_one<D, CAUSAL, 2, CHUNK, F8, SAS, V8, I8>(a);
+  return launch_one<D, CAUSAL, 1, CHUNK, F8, SAS, V8, I8>(a);
 }
 
 template <int D, bool CAUSAL, bool F8>
@@ -624,7 +640,22 @@ static int launch_v8(const PrefillArgs& a) {
                   : launch_g<64, false, false, F8, 0, true>(a);
 }
 
+// The int8 QK^T key loops exist for the whole-sequence prefill (P.V in bf16).
+static int launch_i8(const PrefillArgs& a) {
+  if (a.d == 128)
+    return a.causal ? launch_g<128, true, false, true, 0, false, true>(a)
+                    : launch_g<128, false, false, true, 0, false, true>(a);
+  return a.causal ? launch_g<64, true, false, true, 0, false, true>(a)
+                  : launch_g<64, false, false, true, 0, false, true>(a);
+}
+
 int launch_prefill(const PrefillArgs& a) {
+  if (a.qk_int8) {
+    if (a.qscale == nullptr || a.vscale != nullptr || a.sas != 0 || a.Nq != a.N || a.q0t != 0 ||
+        a.cap != a.N)
+      return -3;
+    return launch_i8(a);
+  }
   if (a.vscale != nullptr) {
     if (a.sas != 0 || a.Nq != a.N || a.q0t != 0 || a.cap != a.N) return -3;
     return a.qscale != nullptr ? launch_v8<true>(a) : launch_v8<false>(a);

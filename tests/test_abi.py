@@ -299,3 +299,20 @@ def test_prefill_pv8_rejects_before_any_launch():
     assert call(ws=P + 8) == lib.EINVAL
     assert call(q=None) == lib.EINVAL
     assert call(d=96) == lib.EINVAL
+
+
+def test_prefill_8bit_qk_rejects_before_any_launch():
+    # fp8 and int8 QK^T share the workspace layout and the checks
+    so = lib.load()
+    ws = lib.attn_prefill_qk8_workspace_bytes(1, 8, 2, 1024, 128)
+    assert ws > 0 and lib.attn_prefill_qk8_workspace_bytes(1, 8, 2, 1024, 96) == 0
+    for fn in (so.attn_prefill_qk8, so.attn_prefill_qki8):
+        call = lambda fn=fn, **kw: fn(
+            kw.get("q", P), P, P, P, P, 1, 8, 2, 1024, kw.get("d", 128), 1, kw.get("tau", 4.0),
+            None, kw.get("ws", P), kw.get("wsb", ws), None)
+        assert call(wsb=ws - 1) == lib.EWORKSPACE and "workspace" in lib.attn_last_error()
+        assert call(ws=None) == lib.EWORKSPACE
+        assert call(ws=P + 8) == lib.EINVAL
+        assert call(q=None) == lib.EINVAL
+        assert call(d=96) == lib.EINVAL
+        assert call(tau=-1.0) == lib.EINVAL

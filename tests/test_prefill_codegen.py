@@ -82,8 +82,8 @@ def _kernels(text):
 def test_compiler_keeps_out_of_reserved_registers(device_asm):
     kernels = _kernels(device_asm)
     # d x causal x heads-per-wave x (chunk x bf16 or fp8 QK, or SAS of degree 2 or 3,
-    # or 8-bit P.V with bf16 or fp8 QK)
-    assert len(kernels) == 96
+    # or 8-bit P.V with bf16 or fp8 QK, or int8 QK)
+    assert len(kernels) == 108
     for name, (lines, _) in kernels.items():
         bad = []
         for in_asm, ins in lines:
@@ -99,9 +99,9 @@ def test_compiler_keeps_out_of_reserved_registers(device_asm):
 
 def test_kernels_get_the_register_file_they_name(device_asm):
     for name, (_, desc) in _kernels(device_asm).items():
-        # template arguments: d, causal, heads per wave, stages, chunk, fp8 QK, SAS,
-        # 8-bit P.V
-        m = re.search(r"ILi(\d+)ELb[01]ELi\dELi5ELb[01]ELb([01])ELi[023]ELb[01]E", name)
+        # template arguments: d, causal, heads per wave, stages, chunk, 8-bit QK (fp8,
+        # or int8 with the last), SAS, 8-bit P.V, int8 QK
+        m = re.search(r"ILi(\d+)ELb[01]ELi\dELi5ELb[01]ELb([01])ELi[023]ELb[01]ELb[01]E", name)
         d, f8 = int(m.group(1)), m.group(2) == "1"
         # AGPRs: O^T (d per lane) and Q^T (d / 2 bf16, d / 4 fp8) above a[64]
         want = 256 + 64 + d + (d // 4 if f8 else d // 2)
