@@ -186,14 +186,16 @@ def test_prefill_one_whole_head_masks(name, h):
         assert hard == 0, bad
 
 
-def test_prefill_8k_qk8_every_block():
-    # the 8-bit QK^T prefill over every query block of prefill_8k at every
-    # tau, against the oracle on the dequantised Q and K
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+def test_prefill_8k_qk8_every_block(fmt):
+    # the 8-bit QK^T prefill (fp8 E4M3 or int8 codes) over every query block
+    # of prefill_8k at every tau, against the oracle on the dequantised Q and K
     import torch
     import long_context_tiled_amd as lib
-    from oracle import fp8
+    from oracle import fp8, int8
+    enc = int8 if fmt == "int8" else fp8
     cfg = synth.workload("prefill_8k")
-    print("[full] generating prefill_8k (qk8)", flush=True)
+    print(f"[full] generating prefill_8k (qk8 {fmt})", flush=True)
     q, k, v = synth.make_prefill(cfg)
     dq, dk, dv = _dev(q), _dev(k), _dev(v)
     B, Hq, N, d = q.shape
@@ -203,18 +205,20 @@ def test_prefill_8k_qk8_every_block():
                      device="cuda")
     out = {}
     for tau in cfg["taus"]:
-        o, lse, mask, _ = lib.prefill_qk8(dq, dk, dv, True, tau, want_mask=True, workspace=ws)
+        o, lse, mask, _ = lib.prefill_qk8(dq, dk, dv, True, tau, want_mask=True, workspace=ws,
+                                          int8=fmt == "int8")
         torch.cuda.synchronize()
         out[tau] = (o.cpu().numpy(), lse.cpu().numpy(), mask.cpu().numpy())
         del o, lse, mask
     parts = {n: t.cpu().numpy() for n, t in lib.qk8_workspace_parts(ws, B, Hq, Hkv, N, d).items()}
     del dq, dk, dv, ws
     torch.cuda.empty_cache()
-    qc, qs = fp8.quantize(synth.bf16_bits_to_f32(q))
-    kc, ks = fp8.quantize(synth.bf16_bits_to_f32(k))
-    assert np.array_equal(parts["qc"], qc) and np.array_equal(parts["kc"], kc)
+    qc, qs = enc.quantize(synth.bf16_bits_to_f32(q))
+    kc, ks = enc.quantize(synth.bf16_bits_to_f32(k))
+    assert np.array_equal(parts["qc"].view(qc.dtype), qc)
+    assert np.array_equal(parts["kc"].view(kc.dtype), kc)
     assert np.array_equal(parts["qs"], qs) and np.array_equal(parts["ks"], ks)
-    qf, kf = fp8.dequantize(qc, qs), fp8.dequantize(kc, ks)
+    qf, kf = enc.dequantize(qc, qs), enc.dequantize(kc, ks)
 
     def head(bh):
         b, h = bh
@@ -236,9 +240,10 @@ def test_prefill_8k_qk8_every_block():
             for tau, r in reps.items():
                 total[tau].merge(r)
             if i % 8 == 7:
-                print(f"[full] prefill_8k qk8 {i + 1} of {B * Hq} heads checked", flush=True)
+                print(f"[full] prefill_8k qk8 {fmt} {i + 1} of {B * Hq} heads checked",
+                      flush=True)
     for tau, rep in total.items():
-        print(f"[full] prefill_8k qk8 tau={tau} blocks={B * Hq * nt} {rep}", flush=True)
+        print(f"[full] prefill_8k qk8 {fmt} tau={tau} blocks={B * Hq * nt} {rep}", flush=True)
         assert rep.ok(), str(rep)
 
 
