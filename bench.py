@@ -67,27 +67,30 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # Keyed by the SHA-1 of the kernel's source files: once a kernel changes the
 # figure no longer applies and is reported as null.
 MEASURED_TRAFFIC = {
-    "prefill": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp", "sas.hpp"),
-                "sha1": "cbc71c8d9f903ea1581f15bfa677027d28070122",
-                "bytes": (2653769.6 * 2.0 + 528520.1) * 1024},
-    "prefill_qk8": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp", "sas.hpp", "fp8.hip"),
-                "sha1": "9165e4e61c19c8e1cd2d53acf44c974873d86382",
-                "bytes": (1699200.9 * 2.0 + 528520.1) * 1024},
-    "prefill_pv8": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp", "sas.hpp", "fp8.hip"),
-                "sha1": "9165e4e61c19c8e1cd2d53acf44c974873d86382",
-                "bytes": (1781203.9 * 2.0 + 528520.1) * 1024},
-    "prefill_qkv8": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp", "sas.hpp", "fp8.hip"),
-                "sha1": "9165e4e61c19c8e1cd2d53acf44c974873d86382",
-                "bytes": (1155616.2 * 2.0 + 528520.1) * 1024},
+    "prefill": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp", "sas.hpp", "launch.hpp"),
+                "sha1": "2611092779dcd55c961380237f98ac6eef1231a9",
+                "bytes": (2756535.4 * 2.0 + 528520.1) * 1024},
+    "prefill_qk8": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp", "sas.hpp", "launch.hpp", "fp8.hip"),
+                "sha1": "703ae988889ddecd4cbf4cc77bee73dacfd20cbf",
+                "bytes": (1704962.3 * 2.0 + 528520.1) * 1024},
+    "prefill_qki8": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp", "sas.hpp", "launch.hpp", "fp8.hip"),
+                "sha1": "703ae988889ddecd4cbf4cc77bee73dacfd20cbf",
+                "bytes": (1738403.4 * 2.0 + 528520.1) * 1024},
+    "prefill_pv8": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp", "sas.hpp", "launch.hpp", "fp8.hip"),
+                "sha1": "703ae988889ddecd4cbf4cc77bee73dacfd20cbf",
+                "bytes": (1775587.0 * 2.0 + 528520.1) * 1024},
+    "prefill_qkv8": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp", "sas.hpp", "launch.hpp", "fp8.hip"),
+                "sha1": "703ae988889ddecd4cbf4cc77bee73dacfd20cbf",
+                "bytes": (1163512.7 * 2.0 + 528520.1) * 1024},
     "decode_q4": {"sources": ("kvq4.hip", "kvq_common.hpp", "decode.hip", "common.hpp", "sas.hpp", "lane_max.hpp", "launch.hpp"),
-                "sha1": "919e9978be2785c80bb861343474c3de17bad052",
-                "bytes": (1148107.9 * 2.0 + 16647.0) * 1024},
+                "sha1": "89f1032dfc320c342979397f4edd240b87cc0c10",
+                "bytes": (1148140.6 * 2.0 + 16643.4) * 1024},
     "decode_q2": {"sources": ("kvq2.hip", "kvq_common.hpp", "decode.hip", "common.hpp", "sas.hpp", "lane_max.hpp", "launch.hpp"),
-                "sha1": "2c9227f0ddd985a6799442cc0229e22d8f7a41c0",
-                "bytes": (623803.9 * 2.0 + 16640.3) * 1024},
+                "sha1": "591dc032bb5f1fe1a42631e99505d3b3911b49fd",
+                "bytes": (623809.2 * 2.0 + 16641.0) * 1024},
     "decode_hybrid": {"sources": ("kvq4.hip", "kvq2.hip", "kvq_common.hpp", "decode.hip", "common.hpp", "sas.hpp", "lane_max.hpp", "launch.hpp"),
-                "sha1": "ff9f0815083a96decd4ecccad30f9dc980349fb0",
-                "bytes": (886088.4 * 2.0 + 16640.5) * 1024},
+                "sha1": "63aaf1176aa70d22b48ddec0c0c785fe92a9f75d",
+                "bytes": (886084.3 * 2.0 + 16641.0) * 1024},
     "decode": {"sources": ("decode.hip", "common.hpp", "sas.hpp", "lane_max.hpp"),
                "sha1": "333142df1d615caa64770921eb2ebcb71ade361c",
                "bytes": (4195498.3 * 2.0 + 16641.4) * 1024},
