@@ -178,3 +178,44 @@ def test_decode_sas_random_shape(name, cfg, taus):
         print(f"  {rep}", flush=True)
         assert rep.ok(), str(rep)
     _quantized_case(4 if cfg["id"] % 4 < 2 else 2, name, cfg, taus[:1], sas=degree)
+
+
+PREFILL8 = PREFILL[1::2]      # 12 of the shapes, each run in one 8-bit format
+_FORMATS8 = ("qk_fp8", "qk_int8", "pv8_qk_bf16", "pv8_qk_fp8")
+
+
+@pytest.mark.parametrize("name,cfg,taus", PREFILL8, ids=[c[0] for c in PREFILL8])
+def test_prefill_8bit_random_shape(name, cfg, taus):
+    """The 8-bit prefills on random shapes, the format by turns: fp8 or int8
+    QK^T against the exact oracle on the dequantised Q and K; fp8 P.V (QK^T
+    in bf16 or fp8) against the 8-bit P.V oracle with its rounding slack."""
+    import torch
+    import long_context_tiled_amd as lib
+    from oracle import fp8, int8
+    fmt = _FORMATS8[(cfg["id"] // 2) % 4]
+    q, k, v = synth.make_prefill(cfg)
+    dq, dk, dv = _dev(q), _dev(k), _dev(v)
+    qk_enc = int8 if fmt == "qk_int8" else fp8
+    qf = kf = None
+    if fmt != "pv8_qk_bf16":
+        qc, qs = qk_enc.quantize(synth.bf16_bits_to_f32(q))
+        kc, ks = qk_enc.quantize(synth.bf16_bits_to_f32(k))
+        qf, kf = qk_enc.dequantize(qc, qs), qk_enc.dequantize(kc, ks)
+    blocks = q.shape[0] * q.shape[1] * ((q.shape[2] + 63) // 64)
+    for tau in taus:
+        print(f"[random] {fmt} {name} tau={tau}", flush=True)
+        if fmt.startswith("qk_"):
+            o, lse, mask, _ = lib.prefill_qk8(dq, dk, dv, cfg["causal"], tau, want_mask=True,
+                                              int8=fmt == "qk_int8")
+            kw = {}
+        else:
+            qk8 = fmt == "pv8_qk_fp8"
+            o, lse, mask, _ = lib.prefill_pv8(dq, dk, dv, cfg["causal"], tau, qk8=qk8,
+                                              want_mask=True)
+            kw = dict(pv8=True, score_err_rel=2.0 ** -11 if qk8 else 2.0 ** -17, lin_err=qk8)
+        torch.cuda.synchronize()
+        rep = _parity.check_prefill(q, k, v, cfg["causal"], tau, o.cpu().numpy(),
+                                    lse.cpu().numpy(), mask.cpu().numpy(), qf=qf, kf=kf, **kw)
+        print(f"  {rep}", flush=True)
+        assert rep.ok(), str(rep)
+        assert rep.ambiguous <= max(1, blocks // 20), str(rep)
