@@ -7,8 +7,8 @@
 // to bf16, the code by an fp32 subtract, divide and rint) is kvq_common.hpp's.
 //
 // Both kernels are streams: every input byte is read once and every output
-// byte written once, so HBM bounds them, with the vector arithmetic (about 9
-// instructions per value) close behind. A wave first issues all of its loads
+// byte written once, so HBM bounds them, with the vector arithmetic (about
+// 11 instructions per value) close behind. A wave first issues all of its loads
 // (8 KB of K rows, or a whole 64-key V tile), then does the arithmetic.
 //   K: a lane holds two code words of a row (16 values for 4 bits, 32 for 2):
 //   words w and w + W of the row for the row's W = d / (2 x values per word)
