@@ -440,8 +440,12 @@ class Step:
         this tile's partial row sum; at the end each partial sum joins the
         running row sum once. (Adding every exponential straight into the
         running sum loses the small terms once that sum is large: over
-        millions of keys the row sum, and so the LSE, came out low.)"""
+        millions of keys the row sum, and so the LSE, came out low.)
+        int8 QK^T: a "full" step's scores are still int32 (only the wave's
+        last tile is converted in place after its vote, for the "pv" step),
+        so each is converted into its temporary before the scale-and-shift."""
         heads, tails = [], []
+        conv = self.i8 and self.variant == "full"
         first = {0: True, 1: True}
         for gp, (a, nb, r0) in enumerate(self.pairs()):
             s0 = f"v{self.s_reg(self.x, a, nb, r0)}"
@@ -451,7 +455,12 @@ class Step:
             ps = f"v{PSUM + nb}"
             nm = f"%[nm{nb}]"
             cc = "%[ce]" if self.f8 else "%[c]"
-            heads.append([
+            pre = []
+            if conv:
+                pre = [Ins(f"v_cvt_f32_i32 {t0}, {s0}", "valu", wr=[t0], rd=[s0]),
+                       Ins(f"v_cvt_f32_i32 {t1}, {s1}", "valu", wr=[t1], rd=[s1])]
+                s0, s1 = t0, t1
+            heads.append(pre + [
                 Ins(f"v_fma_f32 {t0}, {s0}, {cc}, {nm}", "valu", wr=[t0], rd=[s0]),
                 Ins(f"v_fma_f32 {t1}, {s1}, {cc}, {nm}", "valu", wr=[t1], rd=[s1]),
                 Ins(f"v_exp_f32 {t0}, {t0}", "trans", wr=[t0], rd=[t0]),
@@ -471,7 +480,7 @@ class Step:
         # rotate over three register pairs).
         out = list(heads[0])
         for gp in range(1, 32):
-            out += heads[gp][:2] + tails[gp - 1] + heads[gp][2:]
+            out += heads[gp][:-2] + tails[gp - 1] + heads[gp][-2:]
         out += tails[31]
         for nb in range(2):
             out.append(Ins(f"v_add_f32 %[lo{nb}], %[lo{nb}], v{PSUM + nb}", "valu",
@@ -480,7 +489,8 @@ class Step:
 
     def max_stream(self):
         """Row maxima of the new tile: query half nb over both key halves
-        (int8 QK^T: each score pair converted from int32 in place first)."""
+        (int8 QK^T: maxima of the int32 scores, which order as the scaled
+        scores do; the vote converts the two maxima)."""
         out = []
         first = {0: True, 1: True}
         for a in range(2):
@@ -488,25 +498,27 @@ class Step:
                 for i in range(8):
                     r0 = self.s_reg(self.y, a, nb, 2 * i)
                     s0, s1 = f"v{r0}", f"v{r0 + 1}"
-                    if self.i8:
-                        out += [Ins(f"v_cvt_f32_i32 {x}, {x}", "valu", wr=[x], rd=[x],
-                                    tag=("blk", a)) for x in (s0, s1)]
                     tm = f"%[tm{nb}]"
+                    mx, mx3 = ("v_max_i32", "v_max3_i32") if self.i8 else ("v_max_f32", "v_max3_f32")
                     if first[nb]:
-                        out.append(Ins(f"v_max_f32 {tm}, {s0}, {s1}", "valu", rd=[s0, s1], tag=("blk", a)))
+                        out.append(Ins(f"{mx} {tm}, {s0}, {s1}", "valu", rd=[s0, s1], tag=("blk", a)))
                         first[nb] = False
                     else:
-                        out.append(Ins(f"v_max3_f32 {tm}, {tm}, {s0}, {s1}", "valu", rd=[s0, s1],
+                        out.append(Ins(f"{mx3} {tm}, {tm}, {s0}, {s1}", "valu", rd=[s0, s1],
                                        tag=("blk", a)))
         return out
 
     def vote_stream(self):
         v = [f"v{VOTE + i}" for i in range(6)]
         pre = []
+        if self.i8:
+            # int8: the maxima of the int32 scores, converted (exact: < 2^24)
+            pre = [Ins("v_cvt_f32_i32 %[tm0], %[tm0]", "valu"),
+                   Ins("v_cvt_f32_i32 %[tm1], %[tm1]", "valu")]
         if self.f8:
-            # fp8 scores are in code units: times q scale x k scale of the tile
-            pre = [Ins("v_mul_f32 %[tm0], %[tm0], %[qa]", "valu"),
-                   Ins("v_mul_f32 %[tm1], %[tm1], %[qa]", "valu")]
+            # 8-bit scores are in code units: times q scale x k scale of the tile
+            pre += [Ins("v_mul_f32 %[tm0], %[tm0], %[qa]", "valu"),
+                    Ins("v_mul_f32 %[tm1], %[tm1], %[qa]", "valu")]
         return pre + [
             Ins(f"v_mov_b32 {v[0]}, %[tm0]", "valu", wr=[v[0]]),
             Ins(f"v_mov_b32 {v[1]}, %[tm0]", "valu", wr=[v[1]]),
@@ -1126,7 +1138,19 @@ def loop_cxx(d, causal, budget, f8=False, sas=0, v8=False, i8=False):
         return out
 
     def after_vote(kbn, y, tag):  # masked re-vote if needed, then the mask byte
-        out = ["s_cmp_lg_u64 %[rare], 0", f"s_cbranch_scc0 {lab('nm' + tag)}",
+        out = []
+        if i8:
+            # int8: the wave's last tile goes to a "pv" step (and, when it is
+            # the causal diagonal or the ragged end, through the masked
+            # re-vote) with fp32 scores: convert its int32 scores in place.
+            # Every other tile's scores stay int32 for the next "full" step.
+            regs = [SBUF[y] + 16 * (2 * a + nb) + r for a in range(2) for nb in range(2)
+                    for r in range(16)]
+            out += [f"s_add_u32 %[t3], {kbn}, 1", "s_cmp_eq_u32 %[t3], %[nkbw]",
+                    f"s_cbranch_scc0 {lab('nc' + tag)}"]
+            out += [f"v_cvt_f32_i32 v{r}, v{r}" for r in regs]
+            out += [f"{lab('nc' + tag)}:"]
+        out += ["s_cmp_lg_u64 %[rare], 0", f"s_cbranch_scc0 {lab('nm' + tag)}",
                f"s_lshl_b32 %[t0], {kbn}, 6",
                "v_subrev_u32 %[lim0], %[t0], %[L0]", "v_subrev_u32 %[lim1], %[t0], %[L1]"]
         out += _mask_lines(d, y) + _vote_again_lines(f8, y)
