@@ -68,20 +68,20 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # figure no longer applies and is reported as null.
 MEASURED_TRAFFIC = {
     "prefill": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp", "sas.hpp", "launch.hpp"),
-                "sha1": "5a3220a57379d57f80adeda83ddd504f795d9aa0",
-                "bytes": (2744277.5 * 2.0 + 528520.1) * 1024},
+                "sha1": "474d32ae78e620715f0f445753e1bd2f369cdab2",
+                "bytes": (2707060.4 * 2.0 + 528520.1) * 1024},
     "prefill_qk8": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp", "sas.hpp", "launch.hpp", "fp8.hip"),
-                "sha1": "423f3f527fae438b5a368c47d6856cfe00a5d51b",
-                "bytes": (1685153.3 * 2.0 + 528520.1) * 1024},
+                "sha1": "1db5b0e0bc130bbc71659f9eceaefe4bea504230",
+                "bytes": (1697532.9 * 2.0 + 528520.1) * 1024},
     "prefill_qki8": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp", "sas.hpp", "launch.hpp", "fp8.hip"),
-                "sha1": "423f3f527fae438b5a368c47d6856cfe00a5d51b",
-                "bytes": (1690949.6 * 2.0 + 528520.1) * 1024},
+                "sha1": "1db5b0e0bc130bbc71659f9eceaefe4bea504230",
+                "bytes": (1701842.8 * 2.0 + 528520.1) * 1024},
     "prefill_pv8": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp", "sas.hpp", "launch.hpp", "fp8.hip"),
-                "sha1": "423f3f527fae438b5a368c47d6856cfe00a5d51b",
-                "bytes": (1777313.9 * 2.0 + 528520.1) * 1024},
+                "sha1": "1db5b0e0bc130bbc71659f9eceaefe4bea504230",
+                "bytes": (1778258.2 * 2.0 + 528520.1) * 1024},
     "prefill_qkv8": {"sources": ("prefill.hip", "prefill_steps.inc", "common.hpp", "sas.hpp", "launch.hpp", "fp8.hip"),
-                "sha1": "423f3f527fae438b5a368c47d6856cfe00a5d51b",
-                "bytes": (1149431.1 * 2.0 + 528520.1) * 1024},
+                "sha1": "1db5b0e0bc130bbc71659f9eceaefe4bea504230",
+                "bytes": (1162283.7 * 2.0 + 528520.1) * 1024},
     "decode_q4": {"sources": ("kvq4.hip", "kvq_common.hpp", "decode.hip", "common.hpp", "sas.hpp", "lane_max.hpp", "launch.hpp"),
                 "sha1": "89f1032dfc320c342979397f4edd240b87cc0c10",
                 "bytes": (1148140.6 * 2.0 + 16643.4) * 1024},

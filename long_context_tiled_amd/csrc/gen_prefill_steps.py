@@ -303,7 +303,13 @@ class Step:
     def qk_mfmas(self, ks, a, nb, j):
         """The QK^T MFMAs of one (k-step, key half, query half): one, or two
         for int8 (contraction halves: operand registers 0-3, then 4-7; the
-        A and B halves hold the same d positions, so the sum is the same)."""
+        A and B halves hold the same d positions, so the sum is the same).
+        The int8 sums start from the bits of the inline constant 1/(2 pi),
+        0x3e22f983: an int32 score s, |s| <= 127 * 127 * 128 < 2^21, comes
+        out as the bits of the float K0 + s 2^-26 (K0 = 1/(2 pi) and the sum
+        share the binade [1/8, 1/4), whose ulp is 2^-26), so the scores are
+        exact fp32 values without a conversion, and their int32 order is
+        the order of s."""
         if not self.i8:
             return [self.qk_mfma(ks, a, nb, j)]
         s = self.s_blk(self.y, a, nb)
@@ -312,7 +318,7 @@ class Step:
         for h in range(2):
             kf, qf = rng("v", kb + 4 * h, 4), rng("a", qb + 4 * h, 4)
             first = ks == 0 and h == 0
-            src_c = "0" if first else s
+            src_c = "0.15915494" if first else s
             out.append(Ins(f"v_mfma_i32_32x32x32_i8 {s}, {kf}, {qf}, {src_c}", "mfma", wr=[s],
                            rd=[kf, qf] + ([] if first else [s])))
         return out
@@ -441,11 +447,10 @@ class Step:
         running row sum once. (Adding every exponential straight into the
         running sum loses the small terms once that sum is large: over
         millions of keys the row sum, and so the LSE, came out low.)
-        int8 QK^T: a "full" step's scores are still int32 (only the wave's
-        last tile is converted in place after its vote, for the "pv" step),
-        so each is converted into its temporary before the scale-and-shift."""
+        int8 QK^T: a "full" step's scores are the floats K0 + s 2^-26 (see
+        qk_mfmas) and the multiplier is 2^26 times the code-unit one, so the
+        offset's shift takes K0 2^26 times it off as well (nmc)."""
         heads, tails = [], []
-        conv = self.i8 and self.variant == "full"
         first = {0: True, 1: True}
         for gp, (a, nb, r0) in enumerate(self.pairs()):
             s0 = f"v{self.s_reg(self.x, a, nb, r0)}"
@@ -455,12 +460,7 @@ class Step:
             ps = f"v{PSUM + nb}"
             nm = f"%[nm{nb}]"
             cc = "%[ce]" if self.f8 else "%[c]"
-            pre = []
-            if conv:
-                pre = [Ins(f"v_cvt_f32_i32 {t0}, {s0}", "valu", wr=[t0], rd=[s0]),
-                       Ins(f"v_cvt_f32_i32 {t1}, {s1}", "valu", wr=[t1], rd=[s1])]
-                s0, s1 = t0, t1
-            heads.append(pre + [
+            heads.append([
                 Ins(f"v_fma_f32 {t0}, {s0}, {cc}, {nm}", "valu", wr=[t0], rd=[s0]),
                 Ins(f"v_fma_f32 {t1}, {s1}, {cc}, {nm}", "valu", wr=[t1], rd=[s1]),
                 Ins(f"v_exp_f32 {t0}, {t0}", "trans", wr=[t0], rd=[t0]),
@@ -512,9 +512,10 @@ class Step:
         v = [f"v{VOTE + i}" for i in range(6)]
         pre = []
         if self.i8:
-            # int8: the maxima of the int32 scores, converted (exact: < 2^24)
-            pre = [Ins("v_cvt_f32_i32 %[tm0], %[tm0]", "valu"),
-                   Ins("v_cvt_f32_i32 %[tm1], %[tm1]", "valu")]
+            # int8: the maxima of the scores' bits, K0 + tm 2^-26, less K0
+            # (exact: same binade); the tile's multiplier carries the 2^26
+            pre = [Ins("v_subrev_f32 %[tm0], 0.15915494, %[tm0]", "valu"),
+                   Ins("v_subrev_f32 %[tm1], 0.15915494, %[tm1]", "valu")]
         if self.f8:
             # 8-bit scores are in code units: times q scale x k scale of the tile
             pre += [Ins("v_mul_f32 %[tm0], %[tm0], %[qa]", "valu"),
@@ -1068,7 +1069,8 @@ struct LoopArgs {{
 """
 LOOP_ARGS_F8_DOC = """
 // fp8 QK^T: ksp points at the K tile scales of this KV head (one fp32 per
-// 64-key tile), sqv is this wave's Q tile scale, nkbm1 the last key tile,
+// 64-key tile), sqv is this wave's Q tile scale (int8: times 2^26, the
+// unit of the scores as the loop reads them), nkbm1 the last key tile,
 // wlv the wave's LDS base for V tile copies (wl: for K)."""
 LOOP_ARGS_SAS_DOC = """
 // SAS exponential: c is 1 / sqrt(d) (not log2(e) / sqrt(d)), lazy is 0 (the
@@ -1119,7 +1121,7 @@ def loop_cxx(d, causal, budget, f8=False, sas=0, v8=False, i8=False):
         return slot_base("%[t0]", 0) + [f"s_add_u32 %[t0], %[t0], {tile_k}",
                 "v_add_u32 %[vb0], %[t0], %[tr0]", "v_add_u32 %[vb1], %[t0], %[tr1]"]
 
-    def nmc(x):
+    def nmc(x, full=False):
         if sas:  # mref / sqrt(d), the exponent input's offset
             return ["v_mul_f32 %[nm0], %[mr0], %[c]", "v_mul_f32 %[nm1], %[mr1], %[c]"]
         out = ["v_mul_f32 %[nm0], %[mr0], %[c]", "v_mul_f32 %[nm1], %[mr1], %[c]",
@@ -1127,6 +1129,11 @@ def loop_cxx(d, causal, budget, f8=False, sas=0, v8=False, i8=False):
         if f8:
             # the exponent input's multiplier for tile kb's code-unit scores
             out.append(f"v_mul_f32 %[ce], {QA[x]}, %[c]")
+        if i8 and full:
+            # a "full" step's scores are K0 + s 2^-26 (exp2_stream): the
+            # offset also takes off K0 times the multiplier
+            out += ["v_fma_f32 %[nm0], -%[ce], 0.15915494, %[nm0]",
+                    "v_fma_f32 %[nm1], -%[ce], 0.15915494, %[nm1]"]
         return out
 
     def rare(kbn):  # %[rare] = all ones when tile kbn needs the mask
@@ -1142,13 +1149,14 @@ def loop_cxx(d, causal, budget, f8=False, sas=0, v8=False, i8=False):
         if i8:
             # int8: the wave's last tile goes to a "pv" step (and, when it is
             # the causal diagonal or the ragged end, through the masked
-            # re-vote) with fp32 scores: convert its int32 scores in place.
-            # Every other tile's scores stay int32 for the next "full" step.
+            # re-vote) with the scores s 2^-26: K0 comes off each in place
+            # (exact), and the multiplier's 2^26 restores s. Every other
+            # tile's scores stay K0 + s 2^-26 for the next "full" step.
             regs = [SBUF[y] + 16 * (2 * a + nb) + r for a in range(2) for nb in range(2)
                     for r in range(16)]
             out += [f"s_add_u32 %[t3], {kbn}, 1", "s_cmp_eq_u32 %[t3], %[nkbw]",
                     f"s_cbranch_scc0 {lab('nc' + tag)}"]
-            out += [f"v_cvt_f32_i32 v{r}, v{r}" for r in regs]
+            out += [f"v_subrev_f32 v{r}, 0.15915494, v{r}" for r in regs]
             out += [f"{lab('nc' + tag)}:"]
         out += ["s_cmp_lg_u64 %[rare], 0", f"s_cbranch_scc0 {lab('nm' + tag)}",
                f"s_lshl_b32 %[t0], {kbn}, 6",
@@ -1236,7 +1244,7 @@ def loop_cxx(d, causal, budget, f8=False, sas=0, v8=False, i8=False):
         L += ["s_cmp_lg_u64 %[keep], 0", f"s_cbranch_scc0 {lab('skip' + t)}",
               "s_cmp_lg_u64 %[grow], 0", f"s_cbranch_scc0 {lab('nr' + t)}"]
         L += _rescale_lines(d, sas)
-        L += [f"{lab('nr' + t)}:"] + nmc(x) + vaddr()
+        L += [f"{lab('nr' + t)}:"] + nmc(x, full=True) + vaddr()
         L += _step_lines(d, "full", x, y, budget, f8=f8, sas=sas, v8=v8, i8=i8)
         L += [f"s_branch {lab('voted' + t)}", f"{lab('skip' + t)}:"]
         L += _step_lines(d, "qk", y, y, budget, f8=f8, v8=v8, i8=i8)

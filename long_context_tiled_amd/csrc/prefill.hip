@@ -201,7 +201,9 @@ template <> struct LoopArgsOf<64, true, 0, false, true> { using type = d64i8::Lo
 // I8 (with F8, whole-sequence only): Q and K are symmetric int8 codes with
 // the same tile scales; S^T runs on v_mfma_i32_32x32x32_i8 (two per fp8
 // MFMA: the contraction halves of the same operand registers), exact in
-// int32, and the scores are converted to fp32 before their row maxima.
+// int32. The sums start from the bits of 1/(2 pi), so each score s leaves
+// the MFMA as the exact float 1/(2 pi) + s 2^-26 with no conversion; the Q
+// scale carries the 2^26 back (sqv below).
 // F8: Q and K are fp8 (E4M3) codes with one fp32 scale per 64-row Q tile
 // (qsc, [B, Hq, ceil(Nq/64)]) and per 64-key K tile (ksc, [B, Hkv,
 // ceil(cap/64)]); S^T = K . Q^T runs on v_mfma_f32_32x32x64_f8f6f4 in code
@@ -438,7 +440,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(40))) void p
     if constexpr (F8) {
       const int nkbc = (cap + kTile - 1) / kTile;  // K scales per head
       la.ksp = (uint64_t)(uintptr_t)(ksc + (size_t)(b * Hkv + g) * nkbc);
-      la.sqv = wave_valid ? qsc[bh * nqb + qb] : 1.f;
+      // int8: times 2^26 (exact), the unit of the scores as the int8 key
+      // loops read them
+      la.sqv = (wave_valid ? qsc[bh * nqb + qb] : 1.f) * (I8 ? 0x1p26f : 1.f);
       la.nkbm1 = nkb - 1;
       la.wlv = smem_lds + (uint32_t)(T::kBytes + wave * IPW * 1024);
     } else if constexpr (V8) {
