@@ -108,3 +108,35 @@ def test_kernels_get_the_register_file_they_name(device_asm):
         assert desc["accum_offset"] == 256, name
         assert desc["next_free_vgpr"] == want, name
         assert desc["private_segment_fixed_size"] == 0, name
+
+
+def test_int8_scores_as_offset_floats():
+    # The int8 key loops start every S^T sum from the bits of the inline
+    # constant 1/(2 pi) and read the int32 result as fp32: for every score
+    # the int8 codes can give (|s| <= 127 * 127 * 128 at d = 128) the bits
+    # 0x3e22f983 + s are exactly the float K0 + s 2^-26, their int32 order
+    # is the order of s, and (bits - K0) * 2^26 gives s back exactly.
+    import numpy as np
+    k0_bits = 0x3E22F983
+    k0 = np.array([k0_bits], np.uint32).view(np.float32)[0]
+    assert k0 == np.float32(1.0 / (2.0 * np.pi))
+    smax = 127 * 127 * 128
+    assert smax < 2 ** 21
+    s = np.arange(-smax, smax + 1, dtype=np.int64)
+    f = (k0_bits + s).astype(np.uint32).view(np.float32)
+    assert np.array_equal(f.astype(np.float64), np.float64(k0) + s * 2.0 ** -26)
+    assert np.all(np.diff((k0_bits + s).astype(np.int32)) > 0)
+    back = (f - k0) * np.float32(2.0 ** 26)          # fp32 operations, as the loop does
+    assert np.array_equal(back.astype(np.int64), s)
+
+
+def test_int8_loops_start_from_the_offset_and_convert_nothing():
+    with open(os.path.join(CSRC, "prefill_steps.inc")) as f:
+        text = f.read()
+    for ns in ("d128i8", "d64i8"):
+        body = text[text.index(f"namespace {ns} {{"):text.index(f"}}  // namespace {ns}")]
+        mfma = re.findall(r"v_mfma_i32_32x32x32_i8 (v\[\d+:\d+\]), \S+, \S+, (\S+?)\\n", body)
+        assert mfma, ns
+        starts = [c for d, c in mfma if c != d]
+        assert starts and set(starts) == {"0.15915494"}, (ns, set(starts))
+        assert "v_cvt_f32_i32" not in body, ns
